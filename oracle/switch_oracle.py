@@ -1,0 +1,353 @@
+"""fp64 CPU oracle for the Switch Transformer sparse expert FFN layer (forward).
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path imports this module:
+only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg use it.
+It shares no code, tables or helpers with the HIP library and imports nothing
+from it.
+
+Every step is written out in plain NumPy float64, in the order and notation of
+the pages, with no blocking or fusion.  Inputs are the same bf16 / fp32 values
+the GPU receives, taken exactly into float64.
+
+Sources (page title, then the section or formula used):
+  [WQ]  "042 Switch Transformer: each token picks one expert"
+        (wq-win.github.io/llm/042-switch.html): sec. 1 problem setting
+        (router softmax, e* = argmax, y = p_e* f_e*, capacity C = (T/E)c,
+        overflow rides the residual); sec. 2 (aux loss
+        alpha*E*sum f_e P_e, f a hard count, P differentiable, worked example
+        2(0.72+0.02) = 1.48, the gate 0.7 must not be renormalised); sec. 3
+        (the layer as a step list: fp32 router, top-1, aux loss, capacity-
+        truncated dispatch/combine, expert FFN, gate-scaled combine back to the
+        original position, residual; the 100-token / 10-expert example).
+  [DMX] "Switch Transformers: Scaling to Trillion Parameter Models with Simple
+        and Efficient Sparsity" essay (dmxsf.com): "core structure" section
+        (experts replace the FFN sublayer).
+  [XZ]  paper card "Switch Transformers ..." (ai-papers.xuzou.cn): "bottleneck"
+        (fixed capacity, overflow skips the expert layer) and "method
+        adaptation" (fp32 router and softmax; dispatch/combine tensors over
+        [cores, tokens, experts, capacity]).
+  [LAP] "Mixture of experts" explainer (world.lapla.si/zh/moe/): "what is
+        inside an expert" (d -> d_ff ReLU -> d FFN); "a small penalty"
+        (alpha*N*sum f_i P_i, alpha = 0.01); "full means turned back"
+        (capacity, dropped tokens continue on the residual).
+  [ZF]  "MoE routing load collapse" reproduction note (zffjzz.top): "core idea
+        and formulas" (Z = XW, p = softmax(Z_t), a_t = argmax, f, P, L_bal,
+        C = ceil(cT/E), accept mask m_t, z-loss); "official code reading route"
+        (aux statistics computed before capacity masks, slots by cumulative
+        position along the sequence, argmax of a truncated mask sends dropped
+        rows to expert 0); "minimal experiment" (uniform rows: f = (1,0,0,0),
+        loss 1, C = 20, 68.75 % overflow; [28,12,12,12] -> [8,8,8,8]; +100
+        shift leaves p and a unchanged); "troubleshooting" (central finite
+        differences).
+
+Readings where the pages are silent or disagree (each one also listed in the
+design notes): argmax is taken over the logits, which equals the argmax of the
+exact probabilities because softmax is strictly increasing; ties go to the
+lowest index (NumPy's first-occurrence rule, [ZF] minimal experiment);
+C = ceil(c*T/E) on the exact binary value of c ([ZF] formulas; [WQ] sec. 1
+gives T/E*c without rounding); one routing group holds all T tokens; alpha sits
+inside the aux loss ([WQ] sec. 2; [ZF] places it outside, pins use alpha = 1);
+the gate is the raw p_e*, never renormalised ([WQ] sec. 2); experts carry no
+biases; empty capacity slots hold zeros.
+
+Pins: every function here is pinned by tests/test_oracle_pins.py against the
+pages' worked values, closed forms, library routines (scipy softmax /
+logsumexp, a dense torch MLP) and brute force on tiny inputs.
+"""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+from typing import NamedTuple, Optional
+
+import numpy as np
+
+
+# ------------------------------------------------------------------ O1 router
+def router_logits(x: np.ndarray, w_r: np.ndarray, b_r: Optional[np.ndarray] = None) -> np.ndarray:
+    """z_te = sum_i x_ti W_r[i, e] + b_r[e]  in float64.
+
+    [ZF] "core idea and formulas": Z = XW with W in R^{d x E}; [WQ] sec. 1:
+    p(x) = softmax(W_r x).  The bias is the constant-one input column of [ZF]
+    "core idea and formulas" written as a separate vector.
+    """
+    z = np.asarray(x, np.float64) @ np.asarray(w_r, np.float64)
+    if b_r is not None:
+        z = z + np.asarray(b_r, np.float64)[None, :]
+    return z
+
+
+# ------------------------------------------------------- O2, O3 softmax, top-1
+class Routing(NamedTuple):
+    p: np.ndarray        # [T, E] probabilities, rows sum to 1
+    lse: np.ndarray      # [T] log sum_j exp(z_tj)
+    expert: np.ndarray   # [T] int64, e*_t (lowest index among maximal logits)
+    gate: np.ndarray     # [T] p_{t, e*_t}
+
+
+def softmax_top1(z: np.ndarray) -> Routing:
+    """p_te = exp(z_te - m_t) / sum_j exp(z_tj - m_t), m_t = max_j z_tj;
+    e*_t = argmax_e z_te (first maximum); gate_t = p_{t,e*_t}.
+
+    [WQ] sec. 1: e*(x) = argmax_e p_e(x), y = p_e*(x) f_e*(x).
+    [ZF] "core idea and formulas": p_ti = softmax(Z_t)_i, a_t = argmax_i p_ti;
+    "minimal experiment": ties go to the first index.
+    """
+    z = np.asarray(z, np.float64)
+    if not np.all(np.isfinite(z)):
+        raise ValueError("non-finite logits are outside the layer's contract")
+    m = z.max(axis=1)
+    ez = np.exp(z - m[:, None])
+    s = ez.sum(axis=1)
+    p = ez / s[:, None]
+    lse = m + np.log(s)
+    expert = np.argmax(z, axis=1).astype(np.int64)
+    gate = p[np.arange(z.shape[0]), expert]
+    return Routing(p, lse, expert, gate)
+
+
+# ------------------------------------------------------------- O4 capacity
+def capacity(T: int, E: int, c: float) -> int:
+    """C = ceil(c * T / E), exact on the binary value of c.
+
+    [ZF] "core idea and formulas": C = ceil(cT/E) (rounding up is that page's
+    convention); [WQ] sec. 1: C = (T/E) c; [XZ] "bottleneck": tokens per batch
+    divided by the number of experts, times the capacity factor.
+    """
+    if T < 0 or E <= 0 or not (c >= 0) or math.isinf(c):
+        raise ValueError("capacity needs T >= 0, E > 0, finite c >= 0")
+    return math.ceil(Fraction(c) * T / E)
+
+
+# ------------------------------------------------------------- O5 slot scan
+class Slots(NamedTuple):
+    position: np.ndarray    # [T] int64: rank of t among earlier tokens with the same expert
+    keep: np.ndarray        # [T] bool: position < C
+    counts: np.ndarray      # [E] raw (pre-capacity) choices
+    accepted: np.ndarray    # [E] min(counts, C)
+    slot_token: np.ndarray  # [E, C] token in each slot, -1 if empty
+
+
+def slot_scan(expert: np.ndarray, E: int, C: int) -> Slots:
+    """One pass in token order: pos_t = cnt[e*_t]; cnt[e*_t] += 1; keep_t = pos_t < C.
+
+    [ZF] "official code reading route": positions are the cumulative count
+    along the sequence, not an ordering by probability; [WQ] sec. 3:
+    truncate the assignment by expert capacity.  Dropped tokens keep their
+    true expert id ([ZF] "official code reading route": recovering the id
+    from the truncated mask would send them to expert 0).
+    """
+    expert = np.asarray(expert, np.int64)
+    T = expert.shape[0]
+    cnt = [0] * E
+    position = np.empty(T, np.int64)
+    keep = np.empty(T, bool)
+    slot_token = np.full((E, C), -1, np.int64)
+    for t in range(T):
+        e = int(expert[t])
+        position[t] = cnt[e]
+        cnt[e] += 1
+        keep[t] = position[t] < C
+        if keep[t]:
+            slot_token[e, position[t]] = t
+    counts = np.array(cnt, np.int64)
+    return Slots(position, keep, counts, np.minimum(counts, C), slot_token)
+
+
+# ------------------------------------------------------------- O6 dispatch
+def dispatch(x: np.ndarray, slot_token: np.ndarray) -> np.ndarray:
+    """buf[e, s] = x[slot_token[e, s]] for filled slots, zero rows otherwise.
+
+    [WQ] sec. 3: build the dispatch tensor and send tokens to their expert;
+    [XZ] "method adaptation": dispatch/combine over [tokens, experts, capacity].
+    """
+    E, C = slot_token.shape
+    buf = np.zeros((E, C, x.shape[1]), np.float64)
+    filled = slot_token >= 0
+    buf[filled] = np.asarray(x, np.float64)[slot_token[filled]]
+    return buf
+
+
+# ------------------------------------------------------------- O7 experts
+def expert_rows(rows: np.ndarray, w1_e: np.ndarray, w2_e: np.ndarray) -> np.ndarray:
+    """One expert on a set of rows: max(0, rows W1_e^T) W2_e^T, fp64, no rounding.
+
+    [DMX] "core structure": experts take the place of the FFN sublayer;
+    [LAP] "what is inside an expert": d numbers -> d_ff with negatives set to
+    zero -> back to d.  W1_e is [d_ff, d] and W2_e is [d, d_ff] (out-features
+    major); no expert biases.
+    """
+    h = np.maximum(np.asarray(rows, np.float64) @ np.asarray(w1_e, np.float64).T, 0.0)
+    return h @ np.asarray(w2_e, np.float64).T
+
+
+def expert_ffn(buf: np.ndarray, accepted: np.ndarray, w1, w2) -> np.ndarray:
+    """y[e, s] = expert_e(buf[e, s]) for s < accepted[e]; other rows zero.
+
+    w1 and w2 are indexable by expert (arrays or callables returning a float
+    matrix), so experts can be materialised one at a time.
+    """
+    E, C, d = buf.shape
+    y = np.zeros((E, C, d), np.float64)
+    for e in range(E):
+        a = int(accepted[e])
+        if a == 0:
+            continue
+        w1e = w1(e) if callable(w1) else w1[e]
+        w2e = w2(e) if callable(w2) else w2[e]
+        y[e, :a] = expert_rows(buf[e, :a], w1e, w2e)
+    return y
+
+
+# ------------------------------------------------------------- O8 combine
+def combine(y: np.ndarray, expert: np.ndarray, position: np.ndarray, keep: np.ndarray,
+            gate: np.ndarray, residual: Optional[np.ndarray] = None) -> np.ndarray:
+    """branch_t = keep_t * gate_t * y[e*_t, pos_t] (0 if dropped); out_t = residual_t + branch_t.
+
+    [WQ] sec. 1: y = p_e*(x) f_e*(x), overflow tokens skip the expert branch
+    and continue on the residual; sec. 2: the selected probability (e.g. 0.7)
+    multiplies the expert output and is not renormalised to 1; sec. 3: multiply
+    by the routing probability, put back at the original position, add the
+    residual.  [ZF] "core idea and formulas": y_t = residual + m_t p_{t,a_t} (...).
+    """
+    T = expert.shape[0]
+    d = y.shape[2]
+    branch = np.zeros((T, d), np.float64)
+    k = np.flatnonzero(keep)
+    branch[k] = np.asarray(gate, np.float64)[k, None] * y[expert[k], position[k]]
+    if residual is None:
+        return branch
+    return np.asarray(residual, np.float64) + branch
+
+
+# ------------------------------------------------------------- O9 aux loss
+class Aux(NamedTuple):
+    f: np.ndarray        # [E] fraction of raw (pre-capacity) choices
+    P: np.ndarray        # [E] mean router probability
+    loss: float          # alpha * E * sum_e f_e P_e
+    dlogits: np.ndarray  # [T, E] dL/dz with f held constant
+
+
+def aux_loss(counts: np.ndarray, p: np.ndarray, alpha: float) -> Aux:
+    """f_e = counts_e / T, P_e = (1/T) sum_t p_te, L = alpha E sum_e f_e P_e,
+    dL/dz_tj = (alpha E / T) p_tj (f_j - sum_e f_e p_te).
+
+    [WQ] sec. 2: L_aux = alpha E sum_e f_e P_e, f from the hard choice and not
+    differentiated, P differentiable.  [ZF] "core idea and formulas": f counts
+    the choices before the capacity limit.  The gradient is the chain rule of
+    L through P_e = mean_t softmax(z_t)_e with d p_te / d z_tj = p_te (delta_ej - p_tj).
+    """
+    p = np.asarray(p, np.float64)
+    T, E = p.shape
+    f = np.asarray(counts, np.float64) / T
+    P = p.sum(axis=0) / T
+    loss = float(alpha * E * np.dot(f, P))
+    s = p @ f
+    dlogits = (alpha * E / T) * p * (f[None, :] - s[:, None])
+    return Aux(f, P, loss, dlogits)
+
+
+# ------------------------------------------------------------- the layer
+class LayerResult(NamedTuple):
+    z: np.ndarray
+    routing: Routing
+    C: int
+    slots: Slots
+    buf: np.ndarray
+    y: np.ndarray
+    branch: np.ndarray
+    out: np.ndarray
+    aux: Aux
+
+
+def layer_forward(x, w_r, b_r, w1, w2, c: float, alpha: float,
+                  logits: Optional[np.ndarray] = None,
+                  expert_override: Optional[np.ndarray] = None,
+                  C: Optional[int] = None) -> LayerResult:
+    """O1 .. O9 in the order of [WQ] sec. 3.
+
+    The aux statistics use the raw choices, before capacity truncates them
+    ([ZF] "official code reading route").  `logits` replaces O1 (dispatch-only
+    runs are fed identical fp32 logits).  `expert_override` substitutes a
+    given choice vector after O3 and re-runs O4..O9 from it; tests use it to
+    resolve near-tie tokens the same way the device did.
+    """
+    x = np.asarray(x, np.float64)
+    T = x.shape[0]
+    z = router_logits(x, w_r, b_r) if logits is None else np.asarray(logits, np.float64)
+    E = z.shape[1]
+    r = softmax_top1(z)
+    if expert_override is not None:
+        e = np.asarray(expert_override, np.int64)
+        r = Routing(r.p, r.lse, e, r.p[np.arange(T), e])
+    if C is None:
+        C = capacity(T, E, c)
+    aux = aux_loss(np.bincount(r.expert, minlength=E), r.p, alpha)
+    sl = slot_scan(r.expert, E, C)
+    buf = dispatch(x, sl.slot_token)
+    y = expert_ffn(buf, sl.accepted, w1, w2)
+    branch = combine(y, r.expert, sl.position, sl.keep, r.gate, None)
+    return LayerResult(z, r, C, sl, buf, y, branch, x + branch, aux)
+
+
+# ------------------------------------------------ O10 independent formulations
+def layer_dense_onehot(x, z, w1, w2, C: int):
+    """The dispatch/combine-tensor form, written from its description in [XZ]
+    "method adaptation" (dispatch and combine tensors over tokens x experts x
+    capacity; a one-hot dispatch, a gate-weighted combine).
+
+    Positions come from a cumulative sum of the one-hot choice matrix along
+    the token axis (no running counter), expert inputs from a contraction of
+    the dispatch tensor with x, and the output from a contraction of the
+    combine tensor with the expert outputs.  For tiny inputs only.
+    """
+    x = np.asarray(x, np.float64)
+    z = np.asarray(z, np.float64)
+    T, E = z.shape
+    p = np.exp(z - z.max(axis=1, keepdims=True))
+    p = p / p.sum(axis=1, keepdims=True)
+    onehot = (np.arange(E)[None, :] == np.argmax(z, axis=1)[:, None]).astype(np.float64)
+    pos_in_expert = (np.cumsum(onehot, axis=0) - 1.0) * onehot        # [T, E]
+    dispatch_t = np.zeros((T, E, C))
+    for s in range(C):
+        dispatch_t[:, :, s] = onehot * (pos_in_expert == s)
+    expert_in = np.einsum("tes,td->esd", dispatch_t, x)
+    expert_out = np.zeros_like(expert_in)
+    for e in range(E):
+        w1e = w1(e) if callable(w1) else w1[e]
+        w2e = w2(e) if callable(w2) else w2[e]
+        expert_out[e] = np.maximum(expert_in[e] @ np.asarray(w1e, np.float64).T, 0.0) @ np.asarray(w2e, np.float64).T
+    combine_t = dispatch_t * (p * onehot).sum(axis=1)[:, None, None]
+    branch = np.einsum("tes,esd->td", combine_t, expert_out)
+    return dispatch_t, expert_in, branch
+
+
+def layer_per_token(x, z, w1, w2, C: int):
+    """A per-token loop with no shared state: for each token, its expert by a
+    strict-greater scan over the logits, its slot by counting earlier tokens
+    with the same expert, and its branch by two matrix-vector products.
+    For tiny inputs only.
+    """
+    x = np.asarray(x, np.float64)
+    z = np.asarray(z, np.float64)
+    T, E = z.shape
+    experts = []
+    for t in range(T):
+        best = 0
+        for e in range(1, E):
+            if z[t, e] > z[t, best]:
+                best = e
+        experts.append(best)
+    branch = np.zeros_like(x)
+    positions = []
+    for t in range(T):
+        e = experts[t]
+        pos = sum(1 for s in range(t) if experts[s] == e)
+        positions.append(pos)
+        if pos < C:
+            g = math.exp(z[t, e]) / sum(math.exp(v) for v in z[t])
+            w1e = np.asarray(w1(e) if callable(w1) else w1[e], np.float64)
+            w2e = np.asarray(w2(e) if callable(w2) else w2[e], np.float64)
+            h = np.maximum(w1e @ x[t], 0.0)
+            branch[t] = g * (w2e @ h)
+    return np.array(experts), np.array(positions), branch

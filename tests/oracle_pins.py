@@ -1,0 +1,297 @@
+"""Pins for the fp64 oracle: each function checks the oracle module `so`
+against something other than itself (a value the pages print, a closed form,
+a library routine, brute force) and raises AssertionError on a mismatch.
+
+They take the oracle module as an argument so that tests/test_oracle_mutations.py
+can run the same pins against copies of the oracle with planted mistakes.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import scipy.special
+import torch
+
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pins.json")))
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _bf16_round(a):
+    return torch.from_numpy(np.asarray(a, np.float32)).to(torch.bfloat16).to(torch.float32).numpy()
+
+
+def pin_two_expert_balance(so):
+    """wq-win sec. 2: 2(0.72 + 0.02) = 1.48, balanced = 1 (alpha removed)."""
+    g = GOLDEN["two_expert_balance"]
+    # 9 tokens at (0.85, 0.15) and one at (0.35, 0.65): f = (0.9, 0.1), P = (0.8, 0.2)
+    p = np.array([[0.85, 0.15]] * 9 + [[0.35, 0.65]])
+    r = so.softmax_top1(np.log(p))
+    counts = np.bincount(r.expert, minlength=2)
+    aux = so.aux_loss(counts, r.p, g["alpha"])
+    np.testing.assert_allclose(aux.f, g["f"], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(aux.P, g["P"], rtol=1e-14)
+    assert abs(aux.loss - g["expected_loss"]) < 1e-12, aux.loss
+    pb = np.array([[0.75, 0.25]] * 5 + [[0.25, 0.75]] * 5)
+    rb = so.softmax_top1(np.log(pb))
+    auxb = so.aux_loss(np.bincount(rb.expert, minlength=2), rb.p, 1.0)
+    assert abs(auxb.loss - g["balanced_loss"]) < 1e-12, auxb.loss
+
+
+def pin_uniform_counterexample(so):
+    """zffjzz 'minimal experiment': uniform rows all pick expert 0, loss stays 1;
+    the gradient is the closed form (alpha E / T) p (f_j - sum_e f_e p_e)."""
+    g = GOLDEN["uniform_rows_counterexample"]
+    T, E = g["T"], g["E"]
+    r = so.softmax_top1(np.zeros((T, E)))
+    assert np.all(r.expert == g["expected_expert"])
+    aux = so.aux_loss(np.bincount(r.expert, minlength=E), r.p, g["alpha"])
+    np.testing.assert_array_equal(aux.f, g["expected_f"])
+    np.testing.assert_allclose(aux.P, [0.25] * 4, rtol=1e-15)
+    assert abs(aux.loss - g["expected_loss"]) < 1e-14
+    a = 0.37
+    aux = so.aux_loss(np.bincount(r.expert, minlength=E), r.p, a)
+    c = a * E / T
+    np.testing.assert_allclose(aux.dlogits[:, 0], c * 0.25 * 0.75, rtol=1e-13)
+    np.testing.assert_allclose(aux.dlogits[:, 1:], -c * 0.25 * 0.25, rtol=1e-13)
+
+
+def pin_uniform_capacity(so):
+    """zffjzz 'minimal experiment': C = 20 at c = 1.25, 20 kept, 68.75 % overflow."""
+    g = GOLDEN["uniform_rows_capacity"]
+    T, E = g["T"], g["E"]
+    C = so.capacity(T, E, g["c"])
+    assert C == g["expected_C"], C
+    r = so.softmax_top1(np.zeros((T, E)))
+    s = so.slot_scan(r.expert, E, C)
+    assert int(s.accepted.sum()) == g["expected_accepted_total"]
+    np.testing.assert_array_equal(s.accepted, [20, 0, 0, 0])
+    np.testing.assert_array_equal(s.keep, np.arange(T) < 20)
+    assert abs((T - s.keep.sum()) / T - g["expected_overflow"]) < 1e-15
+
+
+def pin_raw_load_capped(so):
+    """zffjzz 'minimal experiment': [28,12,12,12] capped at 8 -> [8,8,8,8]; f keeps the raw load."""
+    g = GOLDEN["raw_load_capped"]
+    raw = g["raw"]
+    expert = np.repeat(np.arange(4), raw)
+    _rng(5).shuffle(expert)
+    T = len(expert)
+    C = so.capacity(T, 4, 0.5)
+    assert C == g["C"]
+    s = so.slot_scan(expert, 4, C)
+    np.testing.assert_array_equal(s.accepted, g["expected_accepted"])
+    np.testing.assert_array_equal(s.counts, raw)
+    # the f statistic uses the raw choices, not the accepted ones
+    z = np.where(np.arange(4)[None, :] == expert[:, None], 1.0, 0.0)
+    r = so.softmax_top1(z)
+    layer = so.layer_forward(np.zeros((T, 2)), None, None, np.zeros((4, 2, 2)), np.zeros((4, 2, 2)),
+                             0.5, 1.0, logits=z)
+    np.testing.assert_allclose(layer.aux.f, np.array(raw) / T, rtol=0, atol=0)
+    assert np.all(r.expert == expert)
+
+
+def pin_shift_invariance(so):
+    """zffjzz 'minimal experiment': +100 on every score keeps p and the choice."""
+    sh = GOLDEN["shift_invariance"]["shift"]
+    z = _rng(1).standard_normal((257, 9))
+    a, b = so.softmax_top1(z), so.softmax_top1(z + sh)
+    np.testing.assert_array_equal(a.expert, b.expert)
+    np.testing.assert_allclose(a.p, b.p, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(b.lse - a.lse, sh, rtol=1e-13)
+
+
+def pin_softmax_library(so):
+    """Softmax and log-sum-exp against scipy.special on random rows, including huge logits."""
+    z = _rng(2).standard_normal((300, 17)) * 30.0
+    r = so.softmax_top1(z)
+    np.testing.assert_allclose(r.p, scipy.special.softmax(z, axis=1), rtol=1e-12, atol=1e-300)
+    np.testing.assert_allclose(r.lse, scipy.special.logsumexp(z, axis=1), rtol=1e-14)
+    np.testing.assert_allclose(r.p.sum(axis=1), 1.0, rtol=1e-14)
+    np.testing.assert_array_equal(r.gate, r.p.max(axis=1))
+    # lowest index among equal maxima
+    zt = np.array([[1.0, 3.0, 3.0, 0.0], [2.0, 2.0, 2.0, 2.0], [0.0, 0.0, 0.0, 5.0]])
+    np.testing.assert_array_equal(so.softmax_top1(zt).expert, [1, 0, 3])
+
+
+def pin_gate_not_renormalised(so):
+    """wq-win sec. 2: the selected probability 0.7 stays on the expert output."""
+    pg = GOLDEN["gate_not_renormalised"]["p_selected"]
+    rng = _rng(3)
+    T, d, F = 6, 8, 12
+    x = rng.standard_normal((T, d))
+    w1 = rng.standard_normal((2, F, d))
+    w2 = rng.standard_normal((2, d, F))
+    z = np.tile(np.log([pg, 1 - pg]), (T, 1))
+    layer = so.layer_forward(x, None, None, w1, w2, 2.0, 0.01, logits=z)
+    xt, w1t, w2t = (torch.from_numpy(a) for a in (x, w1[0], w2[0]))
+    ffn = (torch.relu(xt @ w1t.T) @ w2t.T).numpy()
+    np.testing.assert_allclose(layer.routing.gate, pg, rtol=1e-14)
+    np.testing.assert_allclose(layer.branch, pg * ffn, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(layer.out, x + pg * ffn, rtol=1e-12, atol=1e-12)
+
+
+def pin_local_overflow(so):
+    """wq-win sec. 3: 100 tokens, 10 experts, c = 1: 30 tokens on one expert drop 20."""
+    g = GOLDEN["local_overflow"]
+    T, E = g["T"], g["E"]
+    C = so.capacity(T, E, g["c"])
+    assert C == g["expected_C"]
+    others = np.repeat([0, 1, 2, 4, 5, 6, 7, 8, 9], [7, 8, 8, 8, 8, 8, 8, 8, 7])
+    expert = np.concatenate([others, np.full(g["hot_tokens"], 3)])
+    _rng(4).shuffle(expert)
+    s = so.slot_scan(expert, E, C)
+    assert int((~s.keep).sum()) == g["expected_dropped"]
+    hot = np.flatnonzero(expert == 3)
+    np.testing.assert_array_equal(s.keep[hot], np.arange(30) < 10)      # first ten in token order
+    np.testing.assert_array_equal(s.position[hot], np.arange(30))
+    assert s.accepted.sum() == 80 and s.counts.sum() == T
+
+
+def pin_capacity_values(so):
+    """C = ceil(c T / E) at the five layer shapes and at boundaries."""
+    assert so.capacity(512, 4, 1.25) == 160
+    assert so.capacity(16384, 128, 1.0) == 128
+    assert so.capacity(16384, 64, 2.0) == 512
+    assert so.capacity(32768, 128, 1.25) == 320
+    assert so.capacity(65536, 2048, 1.0) == 32
+    assert so.capacity(10, 3, 1.0) == 4           # 10/3 rounds up
+    assert so.capacity(9, 3, 1.0) == 3            # exact stays exact
+    assert so.capacity(64, 4, 0.0) == 0
+    assert so.capacity(0, 4, 1.0) == 0
+    assert so.capacity(30, 3, 0.1) == 2           # binary 0.1 is slightly above 1/10
+    assert so.capacity(30, 3, 0.09375) == 1       # 0.09375 = 3/32 is exact
+
+
+def pin_single_expert_is_dense_ffn(so):
+    """E = 1: nothing dropped, p = 1, loss = alpha, G = 0, branch = the dense FFN (torch)."""
+    rng = _rng(6)
+    T, d, F = 40, 16, 24
+    x = _bf16_round(rng.standard_normal((T, d)))
+    w_r = rng.standard_normal((d, 1)).astype(np.float32)
+    w1 = rng.standard_normal((1, F, d)) * 0.3
+    w2 = rng.standard_normal((1, d, F)) * 0.3
+    alpha = 0.01
+    L = so.layer_forward(x, w_r, None, w1, w2, 1.0, alpha)
+    assert L.C >= T and L.slots.keep.all()
+    np.testing.assert_allclose(L.routing.p, 1.0, rtol=0, atol=0)
+    assert abs(L.aux.loss - alpha) < 1e-15
+    np.testing.assert_array_equal(L.aux.dlogits, 0.0)
+    ref = torch.nn.functional.linear(torch.relu(torch.nn.functional.linear(
+        torch.from_numpy(np.asarray(x, np.float64)), torch.from_numpy(w1[0]))), torch.from_numpy(w2[0])).numpy()
+    np.testing.assert_allclose(L.branch, ref, rtol=1e-12, atol=1e-12)
+
+
+def _tiny_problem(seed, T, d, F, E):
+    rng = _rng(seed)
+    x = _bf16_round(rng.standard_normal((T, d)))
+    w_r = (rng.standard_normal((d, E)) * 0.5).astype(np.float32)
+    b_r = (rng.standard_normal(E) * 0.3).astype(np.float32)
+    w1 = _bf16_round(rng.standard_normal((E, F, d)) * 0.2)
+    w2 = _bf16_round(rng.standard_normal((E, d, F)) * 0.2)
+    return x, w_r, b_r, w1, w2
+
+
+def pin_no_drop_brute_force(so):
+    """c >= E so C >= T: every token kept; branch_t = p_{t,e*} FFN_{e*}(x_t) token by token."""
+    x, w_r, b_r, w1, w2 = _tiny_problem(7, 50, 12, 20, 5)
+    L = so.layer_forward(x, w_r, b_r, w1, w2, 5.0, 0.01)
+    assert L.C >= 50 and L.slots.keep.all()
+    z = x.astype(np.float64) @ w_r.astype(np.float64) + b_r
+    for t in range(50):
+        e = int(np.argmax(z[t]))
+        g = math.exp(z[t, e] - z[t].max()) / np.exp(z[t] - z[t].max()).sum()
+        h = np.maximum(w1[e].astype(np.float64) @ x[t], 0)
+        np.testing.assert_allclose(L.branch[t], g * (w2[e].astype(np.float64) @ h), rtol=1e-12, atol=1e-13)
+
+
+def pin_zero_capacity(so):
+    """c = 0: C = 0, every token dropped, out = x exactly, f and P as with c = 1."""
+    x, w_r, b_r, w1, w2 = _tiny_problem(8, 33, 8, 16, 3)
+    L0 = so.layer_forward(x, w_r, b_r, w1, w2, 0.0, 0.01)
+    L1 = so.layer_forward(x, w_r, b_r, w1, w2, 1.0, 0.01)
+    assert L0.C == 0 and not L0.slots.keep.any()
+    np.testing.assert_array_equal(L0.out, x.astype(np.float64))
+    np.testing.assert_array_equal(L0.branch, 0.0)
+    np.testing.assert_array_equal(L0.aux.f, L1.aux.f)
+    np.testing.assert_array_equal(L0.aux.P, L1.aux.P)
+    assert L0.buf.shape[1] == 0
+
+
+def pin_invariants(so):
+    """sum f = 1, sum P = 1, rows of G sum to 0, uniform f gives G = 0, slots are 0..accepted-1 in token order."""
+    x, w_r, b_r, w1, w2 = _tiny_problem(9, 97, 8, 16, 6)
+    for c in (0.5, 1.0, 1.7):
+        L = so.layer_forward(x, w_r, b_r, w1, w2, c, 0.3)
+        assert abs(L.aux.f.sum() - 1) < 1e-15 and abs(L.aux.P.sum() - 1) < 1e-14
+        np.testing.assert_allclose(L.aux.dlogits.sum(axis=1), 0.0, atol=1e-16)
+        E, C = L.slots.slot_token.shape
+        for e in range(E):
+            toks = np.flatnonzero((L.routing.expert == e) & L.slots.keep)
+            np.testing.assert_array_equal(L.slots.position[toks], np.arange(len(toks)))
+            np.testing.assert_array_equal(L.slots.slot_token[e, :len(toks)], toks)
+            assert np.all(L.slots.slot_token[e, len(toks):] == -1)
+            assert np.all(toks[:-1] < toks[1:])
+        assert L.slots.accepted.sum() <= min(97, E * C)
+        filled = L.slots.slot_token >= 0
+        np.testing.assert_array_equal(L.buf[filled], x[L.slots.slot_token[filled]])
+        np.testing.assert_array_equal(L.buf[~filled], 0.0)
+    # uniform f: each expert chosen twice
+    z = np.full((8, 4), -1.0)
+    z[np.arange(8), np.repeat(np.arange(4), 2)] = 1.0
+    z += _rng(10).standard_normal((8, 4)) * 0.1
+    r = so.softmax_top1(z)
+    aux = so.aux_loss(np.bincount(r.expert, minlength=4), r.p, 1.0)
+    np.testing.assert_allclose(aux.f, 0.25)
+    np.testing.assert_allclose(aux.dlogits, 0.0, atol=1e-17)
+
+
+def pin_finite_differences(so):
+    """zffjzz 'troubleshooting': central finite differences of L(z) with f held fixed."""
+    rng = _rng(11)
+    T, E, alpha = 7, 5, 0.7
+    z = rng.standard_normal((T, E))
+    r = so.softmax_top1(z)
+    counts = np.bincount(r.expert, minlength=E)
+    G = so.aux_loss(counts, r.p, alpha).dlogits
+    h = 1e-6
+    num = np.zeros_like(z)
+    for t in range(T):
+        for j in range(E):
+            zp, zm = z.copy(), z.copy()
+            zp[t, j] += h
+            zm[t, j] -= h
+            lp = so.aux_loss(counts, so.softmax_top1(zp).p, alpha).loss
+            lm = so.aux_loss(counts, so.softmax_top1(zm).p, alpha).loss
+            num[t, j] = (lp - lm) / (2 * h)
+    np.testing.assert_allclose(G, num, rtol=0, atol=2e-9)
+
+
+def pin_independent_forms(so, T=512, d=64, F=128, E=4, c=1.25, seed=12, bias0=2.0):
+    """The index form against the dense one-hot dispatch/combine form and a per-token loop."""
+    x, w_r, b_r, w1, w2 = _tiny_problem(seed, T, d, F, E)
+    b_r = b_r.copy()
+    b_r[0] += bias0
+    L = so.layer_forward(x, w_r, b_r, w1, w2, c, 0.01)
+    D, expert_in, branch_dense = so.layer_dense_onehot(x, L.z, w1, w2, L.C)
+    experts, positions, branch_loop = so.layer_per_token(x, L.z, w1, w2, L.C)
+    np.testing.assert_array_equal(L.routing.expert, experts)
+    np.testing.assert_array_equal(L.slots.position, positions)
+    np.testing.assert_array_equal(L.buf, expert_in)
+    np.testing.assert_allclose(L.branch, branch_dense, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(L.branch, branch_loop, rtol=1e-12, atol=1e-12)
+    return L
+
+
+ALL_PINS = [
+    pin_two_expert_balance, pin_uniform_counterexample, pin_uniform_capacity, pin_raw_load_capped,
+    pin_shift_invariance, pin_softmax_library, pin_gate_not_renormalised, pin_local_overflow,
+    pin_capacity_values, pin_single_expert_is_dense_ffn, pin_no_drop_brute_force, pin_zero_capacity,
+    pin_invariants, pin_finite_differences,
+    lambda so: pin_independent_forms(so, T=40, d=8, F=12, E=3, c=1.0, seed=13, bias0=0.5),
+]

@@ -1,0 +1,155 @@
+"""Plants plausible mistakes in copies of the oracle (on the CPU) and checks
+that the pins catch every one of them.  This is evidence that the pins fix
+each part of the oracle rather than restating it."""
+import inspect
+import math
+import types
+
+import numpy as np
+import pytest
+
+import oracle.switch_oracle as so_real
+from tests import oracle_pins as pins
+
+SRC = inspect.getsource(so_real)
+
+
+def fresh_oracle():
+    mod = types.ModuleType("oracle_mutant")
+    mod.__dict__["__name__"] = "oracle_mutant"
+    exec(compile(SRC, "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+def m_argmax_last(m):
+    orig = m.softmax_top1
+    def f(z):
+        r = orig(z)
+        z = np.asarray(z, np.float64)
+        e = (z.shape[1] - 1 - np.argmax(z[:, ::-1], axis=1)).astype(np.int64)
+        return m.Routing(r.p, r.lse, e, r.p[np.arange(len(e)), e])
+    m.softmax_top1 = f
+
+
+def m_capacity_floor(m):
+    m.capacity = lambda T, E, c: int(math.floor(c * T / E))
+
+
+def m_capacity_float(m):
+    m.capacity = lambda T, E, c: int(math.ceil(float(c) * T / E - 1e-9))
+
+
+def m_aux_no_E(m):
+    orig = m.aux_loss
+    def f(counts, p, alpha):
+        a = orig(counts, p, alpha)
+        E = np.asarray(p).shape[1]
+        return m.Aux(a.f, a.P, a.loss / E, a.dlogits / E)
+    m.aux_loss = f
+
+
+def m_aux_grad_sign(m):
+    orig = m.aux_loss
+    m.aux_loss = lambda counts, p, alpha: orig(counts, p, alpha)._replace(dlogits=-orig(counts, p, alpha).dlogits)
+
+
+def m_aux_grad_no_p(m):
+    orig = m.aux_loss
+    def f(counts, p, alpha):
+        a = orig(counts, p, alpha)
+        p = np.asarray(p, np.float64)
+        T, E = p.shape
+        return a._replace(dlogits=(alpha * E / T) * (a.f[None, :] - (p @ a.f)[:, None]))
+    m.aux_loss = f
+
+
+def m_f_after_capacity(m):
+    orig_layer = m.layer_forward
+    def f(x, w_r, b_r, w1, w2, c, alpha, logits=None, expert_override=None, C=None):
+        L = orig_layer(x, w_r, b_r, w1, w2, c, alpha, logits, expert_override, C)
+        return L._replace(aux=m.aux_loss(L.slots.accepted, L.routing.p, alpha))
+    m.layer_forward = f
+
+
+def m_gate_renormalised(m):
+    orig = m.combine
+    m.combine = lambda y, e, pos, keep, gate, residual=None: orig(y, e, pos, keep, np.ones_like(gate), residual)
+
+
+def m_scan_reverse(m):
+    orig = m.slot_scan
+    def f(expert, E, C):
+        expert = np.asarray(expert)
+        s = orig(expert[::-1], E, C)
+        T = len(expert)
+        st = np.where(s.slot_token >= 0, T - 1 - s.slot_token, -1)
+        return m.Slots(s.position[::-1], s.keep[::-1], s.counts, s.accepted, st)
+    m.slot_scan = f
+
+
+def m_no_relu(m):
+    m.expert_rows = lambda rows, w1, w2: (np.asarray(rows, np.float64) @ np.asarray(w1, np.float64).T) @ np.asarray(w2, np.float64).T
+
+
+def m_combine_wrong_row(m):
+    def f(y, expert, position, keep, gate, residual=None):
+        T = expert.shape[0]
+        branch = np.zeros((T, y.shape[2]))
+        k = np.flatnonzero(keep)
+        branch[k] = np.asarray(gate)[k, None] * y[expert[k], np.minimum(k, y.shape[1] - 1)]
+        return branch if residual is None else residual + branch
+    m.combine = f
+
+
+def m_lse_no_max(m):
+    orig = m.softmax_top1
+    def f(z):
+        r = orig(z)
+        z = np.asarray(z, np.float64)
+        return r._replace(lse=np.log(np.exp(z - z.max(axis=1, keepdims=True)).sum(axis=1)))
+    m.softmax_top1 = f
+
+
+def m_P_over_kept(m):
+    orig_layer = m.layer_forward
+    def f(x, w_r, b_r, w1, w2, c, alpha, logits=None, expert_override=None, C=None):
+        L = orig_layer(x, w_r, b_r, w1, w2, c, alpha, logits, expert_override, C)
+        p = L.routing.p * L.slots.keep[:, None]
+        return L._replace(aux=m.aux_loss(L.slots.counts, p, alpha))
+    m.layer_forward = f
+
+
+def m_dispatch_shift(m):
+    orig = m.dispatch
+    def f(x, slot_token):
+        b = orig(x, slot_token)
+        return np.roll(b, 1, axis=1)
+    m.dispatch = f
+
+
+def m_transposed_w2(m):
+    m.expert_rows = lambda rows, w1, w2: np.maximum(np.asarray(rows, np.float64) @ np.asarray(w1, np.float64).T, 0) @ np.asarray(w2, np.float64).reshape(np.asarray(w2).shape[::-1])
+
+
+MUTANTS = [m_argmax_last, m_capacity_floor, m_capacity_float, m_aux_no_E, m_aux_grad_sign, m_aux_grad_no_p,
+           m_f_after_capacity, m_gate_renormalised, m_scan_reverse, m_no_relu, m_combine_wrong_row,
+           m_lse_no_max, m_P_over_kept, m_dispatch_shift, m_transposed_w2]
+
+
+@pytest.mark.parametrize("mutate", MUTANTS, ids=lambda f: f.__name__)
+def test_pins_catch_mutant(mutate):
+    m = fresh_oracle()
+    mutate(m)
+    failed = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(m)
+        except Exception:  # an assertion, or a shape error caused by the mistake
+            failed.append(getattr(pin, "__name__", "independent_forms"))
+    assert failed, f"no pin caught {mutate.__name__}"
+
+
+def test_fresh_oracle_passes_all_pins():
+    m = fresh_oracle()
+    for pin in pins.ALL_PINS:
+        pin(m)
