@@ -1,0 +1,247 @@
+/*
+ * switch_moe.h -- C ABI of the Switch Transformer sparse expert FFN layer
+ * (forward pass) on one AMD MI355X (gfx950).
+ *
+ * The layer (sources: "042 Switch Transformer" teaching note, wq-win.github.io,
+ * sec. 1-3; "MoE routing load collapse" reproduction note, zffjzz.top,
+ * "core idea and formulas" and "official code reading route"; paper card
+ * "Switch Transformers", ai-papers.xuzou.cn, "bottleneck" and "method
+ * adaptation"; "Mixture of experts" explainer, world.lapla.si, "what is inside
+ * an expert" and "full means turned back"):
+ *
+ *   z_te     = sum_i x_ti W_r[i,e] + b_r[e]                  fp32 router
+ *   p_te     = softmax_e(z_t),  e*_t = argmax_e z_te (lowest index on ties)
+ *   C        = ceil(c T / E)                                 expert capacity
+ *   pos_t    = #{s < t : e*_s = e*_t},  keep_t = pos_t < C   slots in token order
+ *   buf[e,s] = x_t  for the token t in slot s of expert e    dispatch, bf16
+ *   y[e,s]   = ReLU(buf[e,s] W1_e^T) W2_e^T                  expert FFN
+ *   out_t    = x_t + keep_t p_{t,e*} y[e*_t, pos_t]          gate not renormalised
+ *   f_e = counts_e / T,  P_e = (1/T) sum_t p_te,  L = alpha E sum_e f_e P_e
+ *   dL/dz_tj = (alpha E / T) p_tj (f_j - sum_e f_e p_te)     (f held constant)
+ *
+ * Conventions for every device entry point
+ *   - Every pointer is a device pointer owned by the caller; the library keeps
+ *     no reference after the call returns.  All arrays are row-major and
+ *     contiguous.  bf16 arrays must be 16-byte aligned, others 4-byte aligned.
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *     stream).  No call synchronises the host, allocates device memory or
+ *     copies device data to the host.
+ *   - Arguments are validated before any HIP call: a bad argument returns
+ *     SWITCH_E_INVALID / SWITCH_E_UNSUPPORTED / SWITCH_E_WORKSPACE with a
+ *     message in switch_last_error() and nothing is enqueued.  A failed
+ *     launch returns SWITCH_E_HIP.  Faults while kernels run surface at the
+ *     caller's next synchronisation.  Nothing is thrown across the ABI.
+ *   - Results are bitwise reproducible run to run (fixed-order reductions,
+ *     no floating-point atomics).
+ *   - Scratch space is the caller's `ws` of `ws_bytes` bytes, 256-byte
+ *     aligned, sized by the matching *_workspace_bytes() helper; its contents
+ *     on entry do not matter.  Calls that share a workspace must not overlap.
+ *   - Non-finite inputs are outside the contract.
+ *   - Limits: 0 <= T < 2^31, 1 <= E <= 4096, 0 <= C, E*C < 2^31; d and d_ff
+ *     multiples of 64 (the router alone needs d a multiple of 32, dispatch
+ *     and combine need d a multiple of 8).
+ */
+#ifndef SWITCH_MOE_H
+#define SWITCH_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SWITCH_OK = 0,
+    SWITCH_E_INVALID = 1,      /* NULL required pointer, bad size, misaligned pointer */
+    SWITCH_E_UNSUPPORTED = 2,  /* sizes outside the limits above */
+    SWITCH_E_WORKSPACE = 3,    /* ws_bytes smaller than required */
+    SWITCH_E_HIP = 4           /* a HIP runtime call failed (text in switch_last_error) */
+} switch_status;
+
+typedef uint16_t switch_bf16;  /* raw bf16 bits (torch.bfloat16 storage) */
+
+/* ------------------------------------------------------------ host helpers */
+
+/* C = ceil(c * T / E), exact on the binary value of c (no float rounding).
+ * Sources: zffjzz.top note, "core idea and formulas" (C = ceil(cT/E));
+ * wq-win note sec. 1 (C = (T/E) c).  Returns SWITCH_E_INVALID for T < 0,
+ * E <= 0, c negative or not finite, or a result above 2^31 - 1. */
+switch_status switch_capacity(int64_t T, int32_t E, double c, int32_t *C_out);
+
+/* Workspace bytes for each entry point, and for switch_layer_fwd (which
+ * covers every other call with the same sizes).  Return 0 for invalid sizes. */
+size_t switch_route_workspace_bytes(int64_t T, int32_t d, int32_t E);
+size_t switch_dispatch_workspace_bytes(int64_t T, int32_t E);
+size_t switch_expert_ffn_workspace_bytes(int32_t E, int32_t C, int32_t d_ff);
+size_t switch_aux_loss_workspace_bytes(int64_t T, int32_t E);
+size_t switch_workspace_bytes(int64_t T, int32_t d, int32_t d_ff, int32_t E, int32_t C);
+
+const char *switch_status_string(switch_status s);
+/* Detail of the last failing call on this host thread ("" if none). */
+const char *switch_last_error(void);
+
+/* ------------------------------------------------------- device entry points */
+
+/* Router, softmax and top-1.  Sources: wq-win note sec. 1 (p = softmax(W_r x),
+ * e* = argmax p) and sec. 2 (fp32 inside the router); zffjzz.top note, "core
+ * idea and formulas" (Z = XW, p_ti = softmax(Z_t)_i, a_t = argmax, ties to the
+ * first index); ai-papers.xuzou.cn card, "method adaptation" (router input,
+ * logits and softmax in float32).
+ *
+ *   x         [T, d]  bf16   tokens                      (unused if logits_in)
+ *   w_r       [d, E]  fp32   router weights              (unused if logits_in)
+ *   b_r       [E]     fp32   router bias, may be NULL    (unused if logits_in)
+ *   logits_in [T, E]  fp32   if not NULL the GEMM is skipped and these logits
+ *                            are routed as given (dispatch-only runs)
+ *   logits_out[T, E]  fp32   may be NULL; receives z (in GEMM mode)
+ *   expert    [T]     int32  e*_t, the raw choice (also for dropped tokens)
+ *   gate      [T]     fp32   p_{t,e*_t}
+ *   lse       [T]     fp32   log sum_e exp(z_te)
+ *   prob_sum  [E]     fp32   sum_t p_te
+ *
+ * The logits equal an fp32 GEMM up to rounding order: W_r is split into three
+ * bf16 terms whose products with bf16 x are exact, accumulated in fp32 on MFMA.
+ * The argmax is taken over the logits (equal to the argmax of the exact
+ * probabilities).  Workspace: switch_route_workspace_bytes(T, d, E). */
+switch_status switch_route(const switch_bf16 *x, const float *w_r, const float *b_r,
+                           const float *logits_in, int64_t T, int32_t d, int32_t E,
+                           float *logits_out, int32_t *expert, float *gate, float *lse,
+                           float *prob_sum, void *ws, size_t ws_bytes, void *stream);
+
+/* Capacity-truncated dispatch in token order.  Sources: zffjzz.top note,
+ * "official code reading route" (positions are the cumulative count along the
+ * sequence; the raw choice must be kept apart from the capacity mask);
+ * wq-win note sec. 3 (truncate by capacity, build the dispatch tensor, cast
+ * to low precision and send tokens to their expert); ai-papers.xuzou.cn card,
+ * "bottleneck" (fixed capacity; overflow skips the expert layer).
+ *
+ *   x          [T, d]    bf16   tokens
+ *   expert     [T]       int32  e*_t in [0, E)
+ *   C                           capacity (switch_capacity); 0 drops every token
+ *   position   [T]       int32  pos_t = #{s < t : e*_s = e*_t}
+ *   keep       [T]       uint8  pos_t < C
+ *   counts     [E]       int32  raw choices per expert
+ *   accepted   [E]       int32  min(counts, C)
+ *   slot_token [E, C]    int32  token in each slot, -1 if empty; may be NULL
+ *   buf        [E, C, d] bf16   buf[e, pos_t] = x_t for kept t, zero rows in
+ *                               empty slots
+ * Workspace: switch_dispatch_workspace_bytes(T, E). */
+switch_status switch_dispatch(const switch_bf16 *x, const int32_t *expert, int64_t T, int32_t d,
+                              int32_t E, int32_t C, int32_t *position, uint8_t *keep,
+                              int32_t *counts, int32_t *accepted, int32_t *slot_token,
+                              switch_bf16 *buf, void *ws, size_t ws_bytes, void *stream);
+
+/* The experts: per expert e and row s < accepted[e],
+ *   y[e, s] = ReLU(buf[e, s] W1_e^T) W2_e^T
+ * Sources: dmxsf.com essay, "core structure" (experts replace the FFN
+ * sublayer); world.lapla.si explainer, "what is inside an expert"
+ * (d -> d_ff with ReLU -> d).  bf16 MFMA with fp32 accumulation; the hidden
+ * activation is rounded to bf16 once after the ReLU; no expert biases.
+ *
+ *   buf      [E, C, d]     bf16  expert inputs (switch_dispatch)
+ *   accepted [E]           int32 rows in use per expert (0 <= accepted <= C)
+ *   w1       [E, d_ff, d]  bf16  first layer, out-features major
+ *   w2       [E, d, d_ff]  bf16  second layer, out-features major
+ *   y        [E, C, d]     fp32  rows >= accepted[e] are left unwritten
+ * Workspace: switch_expert_ffn_workspace_bytes(E, C, d_ff) (the hidden
+ * activations, bf16 [E, C, d_ff]). */
+switch_status switch_expert_ffn(const switch_bf16 *buf, const int32_t *accepted,
+                                const switch_bf16 *w1, const switch_bf16 *w2, int32_t E,
+                                int32_t C, int32_t d, int32_t d_ff, float *y, void *ws,
+                                size_t ws_bytes, void *stream);
+
+/* Gate-scaled combine back to each token's row.  Sources: wq-win note sec. 1
+ * (y = p_e* f_e*(x); overflow tokens continue on the residual) and sec. 2
+ * (the selected probability, e.g. 0.7, stays on the output; no
+ * renormalisation to 1); sec. 3 (multiply by the routing probability, put
+ * back at the original position, add the residual).
+ *
+ *   out_t = residual_t + keep_t * gate_t * y[expert_t, position_t]
+ * computed in fp32 and rounded to bf16 once.  Dropped tokens get
+ * out_t = residual_t bit for bit.  residual == NULL gives the branch alone
+ * (zero rows for dropped tokens).  y rows are read only for kept tokens.
+ *   y [E, C, d] fp32; expert, position [T] int32; keep [T] uint8; gate [T] fp32;
+ *   residual [T, d] bf16 or NULL; out [T, d] bf16 (must not alias residual). */
+switch_status switch_combine(const float *y, const int32_t *expert, const int32_t *position,
+                             const uint8_t *keep, const float *gate, const switch_bf16 *residual,
+                             int64_t T, int32_t d, int32_t E, int32_t C, switch_bf16 *out,
+                             void *stream);
+
+/* Load-balancing statistics, aux loss and its gradient.  Sources: wq-win note
+ * sec. 2 (L = alpha E sum_e f_e P_e; f from the hard choice, not
+ * differentiated; P differentiable; alpha = 1e-2 in the paper's recipe);
+ * zffjzz.top note, "core idea and formulas" (f counts choices before the
+ * capacity limit) and "official code reading route" (the aux statistics are
+ * taken before capacity modifies the masks).
+ *
+ *   counts   [E]    int32 raw choices (switch_dispatch)
+ *   prob_sum [E]    fp32  sum_t p_te (switch_route)
+ *   logits   [T, E] fp32  needed only when dlogits != NULL
+ *   lse      [T]    fp32  needed only when dlogits != NULL
+ *   f [E], P [E], loss [1] fp32 outputs; dlogits [T, E] fp32 or NULL
+ * For T == 0: f = P = 0 and loss = 0.  loss is reduced in fp64 in a fixed
+ * order.  Workspace: switch_aux_loss_workspace_bytes(T, E). */
+switch_status switch_aux_loss(const int32_t *counts, const float *prob_sum, const float *logits,
+                              const float *lse, int64_t T, int32_t E, float alpha, float *f,
+                              float *P, float *loss, float *dlogits, void *ws, size_t ws_bytes,
+                              void *stream);
+
+/* The whole layer on one stream: route, dispatch, experts, combine, aux loss.
+ * Sources: wq-win note sec. 3 (the layer as a step list).  Required pointers
+ * are marked (R); optional outputs may be NULL, in which case intermediates
+ * live in the workspace (switch_workspace_bytes(T, d, d_ff, E, C)). */
+typedef struct switch_layer_args {
+    /* inputs */
+    const switch_bf16 *x;        /* (R) [T, d] */
+    const float *w_r;            /* (R) [d, E] */
+    const float *b_r;            /*     [E] or NULL */
+    const switch_bf16 *w1;       /* (R) [E, d_ff, d] */
+    const switch_bf16 *w2;       /* (R) [E, d, d_ff] */
+    /* outputs */
+    switch_bf16 *out;            /* (R) [T, d] */
+    int32_t *expert;             /* (R) [T] */
+    float *gate;                 /* (R) [T] */
+    int32_t *position;           /* (R) [T] */
+    uint8_t *keep;               /* (R) [T] */
+    int32_t *counts;             /* (R) [E] */
+    int32_t *accepted;           /* (R) [E] */
+    float *f;                    /* (R) [E] */
+    float *P;                    /* (R) [E] */
+    float *loss;                 /* (R) [1] */
+    float *logits;               /*     [T, E] */
+    float *lse;                  /*     [T] */
+    float *prob_sum;             /*     [E] */
+    float *dlogits;              /*     [T, E]; NULL = gradient not computed */
+    int32_t *slot_token;         /*     [E, C] */
+    switch_bf16 *buf;            /*     [E, C, d] */
+    float *y;                    /*     [E, C, d] */
+    /* sizes */
+    int64_t T;
+    int32_t d, d_ff, E, C;
+    float alpha;
+    int32_t residual;            /* 1: out = x + branch; 0: out = branch only */
+} switch_layer_args;
+
+switch_status switch_layer_fwd(const switch_layer_args *a, void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------- measurement */
+
+/* A plain device-to-device copy kernel (16-byte vectors); the reference
+ * point for bandwidth and hardware-counter calibration.  nbytes must be a
+ * multiple of 16 and both pointers 16-byte aligned. */
+switch_status switch_stream_copy(void *dst, const void *src, size_t nbytes, void *stream);
+
+/* Per-launch timing.  While enabled, every kernel launch made by this library
+ * is bracketed by two HIP events recorded on the launch's own stream.
+ * switch_profile_collect waits for the recorded events, writes up to `max`
+ * (kernel id, milliseconds) pairs in launch order, clears the record and
+ * returns how many were written (negative on a HIP error).  Not thread safe. */
+void switch_profile_enable(int on);
+int switch_profile_collect(int max, int32_t *kernel_ids, float *ms);
+const char *switch_kernel_name(int32_t kernel_id);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SWITCH_MOE_H */

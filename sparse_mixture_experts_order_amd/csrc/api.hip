@@ -1,0 +1,511 @@
+// C ABI of the Switch FFN layer: argument validation (before any HIP call),
+// workspace layout, kernel launches on the caller's stream, error text and
+// the optional per-launch event timing.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "../../include/switch_moe.h"
+#include "common.hpp"
+#include "kernels.hpp"
+
+using namespace swmoe;
+
+namespace {
+
+thread_local std::string g_err;
+
+switch_status fail(switch_status s, const char* fmt, ...) {
+    char b[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(b, sizeof b, fmt, ap);
+    va_end(ap);
+    g_err = b;
+    return s;
+}
+
+switch_status hip_fail(hipError_t e, const char* where) {
+    return fail(SWITCH_E_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+// ----------------------------------------------------------- launch timing
+enum KernelId {
+    K_SPLIT = 0, K_RGEMM, K_RSOFTMAX, K_RREDUCE, K_SCAN_LOCAL, K_SCAN_OFFSETS, K_GATHER,
+    K_GEMM1, K_GEMM2, K_COMBINE, K_AUX_STATS, K_AUX_GRAD, K_COPY, K_COUNT
+};
+const char* kKernelNames[K_COUNT] = {
+    "split_router_weights", "router_gemm", "router_softmax", "router_reduce", "scan_local", "scan_offsets",
+    "gather", "expert_gemm1", "expert_gemm2", "combine", "aux_stats", "aux_grad", "stream_copy"};
+
+struct ProfRec { int id; hipEvent_t a, b; };
+bool g_prof = false;
+std::vector<ProfRec> g_recs;
+std::vector<hipEvent_t> g_pool;
+
+hipEvent_t pool_get() {
+    if (!g_pool.empty()) { hipEvent_t e = g_pool.back(); g_pool.pop_back(); return e; }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+template <class F>
+hipError_t timed(int id, hipStream_t s, F&& launch) {
+    if (!g_prof) return launch();
+    ProfRec r{id, pool_get(), pool_get()};
+    if (r.a) (void)hipEventRecord(r.a, s);
+    hipError_t err = launch();
+    if (r.b) (void)hipEventRecord(r.b, s);
+    if (r.a && r.b) g_recs.push_back(r);
+    return err;
+}
+
+#define LAUNCH(id, where, stream, call)                                     \
+    do {                                                                    \
+        hipError_t _e = timed(id, stream, [&]() { return (call); });       \
+        if (_e != hipSuccess) return hip_fail(_e, where);                   \
+    } while (0)
+
+// ----------------------------------------------------------- workspace
+constexpr size_t kAlign = 256;
+size_t up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
+
+struct Carver {
+    char* base;
+    size_t off = 0;
+    template <class T> T* take(size_t count) {
+        T* p = reinterpret_cast<T*>(base + off);
+        off += up(count * sizeof(T));
+        return p;
+    }
+};
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t route_ws(int64_t T, int32_t d, int32_t E, bool need_logits) {
+    size_t n = up((size_t)3 * d * E * sizeof(bf16_t)) + up((size_t)router_softmax_blocks(T, E) * E * sizeof(float));
+    if (need_logits) n += up((size_t)T * E * sizeof(float));
+    return n;
+}
+size_t dispatch_ws(int64_t T, int32_t E) { return up((size_t)scan_tiles(T) * E * sizeof(int32_t)); }
+size_t ffn_ws(int32_t E, int32_t C, int32_t d_ff) { return up((size_t)E * C * d_ff * sizeof(bf16_t)); }
+
+// ----------------------------------------------------------- validation
+#define REQUIRE(cond, ...) \
+    do { if (!(cond)) return fail(SWITCH_E_INVALID, __VA_ARGS__); } while (0)
+#define SUPPORT(cond, ...) \
+    do { if (!(cond)) return fail(SWITCH_E_UNSUPPORTED, __VA_ARGS__); } while (0)
+
+switch_status check_TE(int64_t T, int32_t E) {
+    REQUIRE(T >= 0, "T must be >= 0 (got %lld)", (long long)T);
+    REQUIRE(E >= 1, "E must be >= 1 (got %d)", E);
+    SUPPORT(T < (int64_t(1) << 31), "T must be < 2^31 (got %lld)", (long long)T);
+    SUPPORT(E <= 4096, "E must be <= 4096 (got %d)", E);
+    SUPPORT((int64_t)T * E < (int64_t(1) << 40), "T*E too large");
+    return SWITCH_OK;
+}
+
+switch_status check_C(int32_t E, int32_t C) {
+    REQUIRE(C >= 0, "C must be >= 0 (got %d)", C);
+    SUPPORT((int64_t)E * C < (int64_t(1) << 31), "E*C must be < 2^31");
+    return SWITCH_OK;
+}
+
+#define CHECK(x) do { switch_status _s = (x); if (_s != SWITCH_OK) return _s; } while (0)
+#define NONNULL(p) REQUIRE((p) != nullptr, "%s must not be NULL", #p)
+// arrays with zero elements may be NULL (torch gives empty tensors a NULL data pointer)
+#define NONNULL_IF(cond, p) do { if (cond) NONNULL(p); } while (0)
+#define ALIGNED16(p) REQUIRE((p) == nullptr || aligned((p), 16), "%s must be 16-byte aligned", #p)
+#define ALIGNED4(p) REQUIRE((p) == nullptr || aligned((p), 4), "%s must be 4-byte aligned", #p)
+
+// ----------------------------------------------------------- the steps
+struct RouteArgs {
+    const bf16_t* x; const float* w_r; const float* b_r; const float* logits_in;
+    int64_t T; int32_t d, E;
+    float* logits_out; int32_t* expert; float* gate; float* lse; float* prob_sum;
+};
+
+switch_status validate_route(const RouteArgs& a, const void* ws, size_t ws_bytes) {
+    CHECK(check_TE(a.T, a.E));
+    const bool tok = a.T > 0;
+    NONNULL_IF(tok, a.expert); NONNULL_IF(tok, a.gate); NONNULL_IF(tok, a.lse); NONNULL(a.prob_sum);
+    ALIGNED4(a.expert); ALIGNED4(a.gate); ALIGNED4(a.lse); ALIGNED4(a.prob_sum); ALIGNED4(a.logits_out);
+    ALIGNED4(a.logits_in);
+    if (!a.logits_in) {
+        NONNULL_IF(tok, a.x); NONNULL(a.w_r);
+        ALIGNED16(a.x); ALIGNED4(a.w_r); ALIGNED4(a.b_r);
+        REQUIRE(a.d >= 1, "d must be >= 1 (got %d)", a.d);
+        SUPPORT(a.d % 32 == 0, "d must be a multiple of 32 for the router GEMM (got %d)", a.d);
+    }
+    REQUIRE(a.logits_in != nullptr || !tok || a.x != nullptr, "x must not be NULL");
+    const size_t need = a.logits_in ? route_ws(a.T, 0, a.E, false) : route_ws(a.T, a.d, a.E, a.logits_out == nullptr);
+    if (ws_bytes < need) return fail(SWITCH_E_WORKSPACE, "route needs %zu workspace bytes, got %zu", need, ws_bytes);
+    REQUIRE(need == 0 || ws != nullptr, "ws must not be NULL");
+    REQUIRE(aligned(ws, kAlign), "ws must be %zu-byte aligned", kAlign);
+    return SWITCH_OK;
+}
+
+switch_status run_route(const RouteArgs& a, void* ws, hipStream_t s) {
+    const int T = (int)a.T, E = a.E;
+    Carver c{(char*)ws};
+    const float* logits = a.logits_in;
+    if (!logits) {
+        bf16_t* wr3 = c.take<bf16_t>((size_t)3 * a.d * E);
+        float* z = a.logits_out ? a.logits_out : c.take<float>((size_t)T * E);
+        LAUNCH(K_SPLIT, "split_router_weights", s, launch_split_router_weights(a.w_r, wr3, a.d, E, s));
+        if (T > 0) LAUNCH(K_RGEMM, "router_gemm", s, launch_router_gemm(a.x, wr3, a.b_r, z, T, a.d, E, s));
+        logits = z;
+    }
+    const int nblk = router_softmax_blocks(T, E);
+    float* part = c.take<float>((size_t)nblk * E);
+    if (T > 0)
+        LAUNCH(K_RSOFTMAX, "router_softmax", s, launch_router_softmax(logits, T, E, a.expert, a.gate, a.lse, part, s));
+    LAUNCH(K_RREDUCE, "router_reduce", s, launch_router_reduce(part, nblk, E, a.prob_sum, s));
+    return SWITCH_OK;
+}
+
+struct DispatchArgs {
+    const bf16_t* x; const int32_t* expert; int64_t T; int32_t d, E, C;
+    int32_t* position; uint8_t* keep; int32_t* counts; int32_t* accepted; int32_t* slot_token; bf16_t* buf;
+};
+
+switch_status validate_dispatch(const DispatchArgs& a, const void* ws, size_t ws_bytes) {
+    CHECK(check_TE(a.T, a.E));
+    CHECK(check_C(a.E, a.C));
+    REQUIRE(a.d >= 1, "d must be >= 1 (got %d)", a.d);
+    SUPPORT(a.d % 8 == 0, "d must be a multiple of 8 (got %d)", a.d);
+    const bool tok = a.T > 0;
+    NONNULL_IF(tok, a.x); NONNULL_IF(tok, a.expert); NONNULL_IF(tok, a.position); NONNULL_IF(tok, a.keep);
+    NONNULL(a.counts); NONNULL(a.accepted);
+    NONNULL_IF(a.C > 0, a.buf);
+    ALIGNED16(a.x); ALIGNED16(a.buf); ALIGNED4(a.expert); ALIGNED4(a.position); ALIGNED4(a.counts);
+    ALIGNED4(a.accepted); ALIGNED4(a.slot_token);
+    const size_t need = dispatch_ws(a.T, a.E);
+    if (ws_bytes < need) return fail(SWITCH_E_WORKSPACE, "dispatch needs %zu workspace bytes, got %zu", need, ws_bytes);
+    REQUIRE(need == 0 || ws != nullptr, "ws must not be NULL");
+    REQUIRE(aligned(ws, kAlign), "ws must be %zu-byte aligned", kAlign);
+    return SWITCH_OK;
+}
+
+switch_status run_dispatch(const DispatchArgs& a, void* ws, hipStream_t s) {
+    const int T = (int)a.T;
+    Carver c{(char*)ws};
+    const int ntiles = scan_tiles(T);
+    int32_t* tile_counts = c.take<int32_t>((size_t)ntiles * a.E);
+    if (T > 0)
+        LAUNCH(K_SCAN_LOCAL, "scan_local", s, launch_scan_local(a.expert, T, a.E, a.position, tile_counts, s));
+    LAUNCH(K_SCAN_OFFSETS, "scan_offsets", s,
+           launch_scan_offsets(tile_counts, ntiles, a.E, a.C, a.counts, a.accepted, s));
+    LAUNCH(K_GATHER, "gather", s,
+           launch_gather(a.x, a.expert, tile_counts, a.accepted, T, a.d, a.E, a.C, a.position, a.keep,
+                         a.slot_token, a.buf, s));
+    return SWITCH_OK;
+}
+
+struct FfnArgs {
+    const bf16_t* buf; const int32_t* accepted; const bf16_t* w1; const bf16_t* w2;
+    int32_t E, C, d, d_ff; float* y;
+};
+
+switch_status validate_ffn(const FfnArgs& a, const void* ws, size_t ws_bytes) {
+    REQUIRE(a.E >= 1, "E must be >= 1 (got %d)", a.E);
+    SUPPORT(a.E <= 4096, "E must be <= 4096 (got %d)", a.E);
+    CHECK(check_C(a.E, a.C));
+    REQUIRE(a.d >= 1 && a.d_ff >= 1, "d and d_ff must be >= 1");
+    SUPPORT(a.d % 64 == 0 && a.d_ff % 64 == 0, "d and d_ff must be multiples of 64 (got %d, %d)", a.d, a.d_ff);
+    SUPPORT((int64_t)a.E * a.C * std::max(a.d, a.d_ff) < (int64_t(1) << 40), "E*C*max(d,d_ff) too large");
+    NONNULL(a.accepted); NONNULL(a.w1); NONNULL(a.w2);
+    if (a.C > 0) { NONNULL(a.buf); NONNULL(a.y); }
+    ALIGNED16(a.buf); ALIGNED16(a.w1); ALIGNED16(a.w2); ALIGNED16(a.y); ALIGNED4(a.accepted);
+    const size_t need = ffn_ws(a.E, a.C, a.d_ff);
+    if (ws_bytes < need) return fail(SWITCH_E_WORKSPACE, "expert_ffn needs %zu workspace bytes, got %zu", need, ws_bytes);
+    REQUIRE(need == 0 || ws != nullptr, "ws must not be NULL");
+    REQUIRE(aligned(ws, kAlign), "ws must be %zu-byte aligned", kAlign);
+    return SWITCH_OK;
+}
+
+switch_status run_ffn(const FfnArgs& a, void* ws, hipStream_t s) {
+    if (a.C == 0) return SWITCH_OK;
+    Carver c{(char*)ws};
+    bf16_t* h = c.take<bf16_t>((size_t)a.E * a.C * a.d_ff);
+    LAUNCH(K_GEMM1, "expert_gemm1", s, launch_expert_gemm1(a.buf, a.w1, a.accepted, h, a.E, a.C, a.d, a.d_ff, s));
+    LAUNCH(K_GEMM2, "expert_gemm2", s, launch_expert_gemm2(h, a.w2, a.accepted, a.y, a.E, a.C, a.d, a.d_ff, s));
+    return SWITCH_OK;
+}
+
+struct CombineArgs {
+    const float* y; const int32_t* expert; const int32_t* position; const uint8_t* keep; const float* gate;
+    const bf16_t* residual; int64_t T; int32_t d, E, C; bf16_t* out;
+};
+
+switch_status validate_combine(const CombineArgs& a) {
+    CHECK(check_TE(a.T, a.E));
+    CHECK(check_C(a.E, a.C));
+    REQUIRE(a.d >= 1, "d must be >= 1 (got %d)", a.d);
+    SUPPORT(a.d % 8 == 0, "d must be a multiple of 8 (got %d)", a.d);
+    const bool tok = a.T > 0;
+    NONNULL_IF(tok, a.expert); NONNULL_IF(tok, a.position); NONNULL_IF(tok, a.keep); NONNULL_IF(tok, a.gate);
+    NONNULL_IF(tok, a.out);
+    NONNULL_IF(tok && a.C > 0, a.y);
+    ALIGNED16(a.y); ALIGNED16(a.residual); ALIGNED16(a.out); ALIGNED4(a.expert); ALIGNED4(a.position);
+    ALIGNED4(a.gate);
+    REQUIRE(!tok || a.residual == nullptr || (const void*)a.residual != (const void*)a.out,
+            "out must not alias residual");
+    return SWITCH_OK;
+}
+
+switch_status run_combine(const CombineArgs& a, hipStream_t s) {
+    LAUNCH(K_COMBINE, "combine", s,
+           launch_combine(a.y, a.expert, a.position, a.keep, a.gate, a.residual, a.T, a.d, a.E, a.C, a.out, s));
+    return SWITCH_OK;
+}
+
+struct AuxArgs {
+    const int32_t* counts; const float* prob_sum; const float* logits; const float* lse;
+    int64_t T; int32_t E; float alpha; float* f; float* P; float* loss; float* dlogits;
+};
+
+switch_status validate_aux(const AuxArgs& a) {
+    CHECK(check_TE(a.T, a.E));
+    REQUIRE(std::isfinite(a.alpha), "alpha must be finite");
+    NONNULL(a.counts); NONNULL(a.prob_sum); NONNULL(a.f); NONNULL(a.P); NONNULL(a.loss);
+    if (a.dlogits && a.T > 0) { NONNULL(a.logits); NONNULL(a.lse); }
+    ALIGNED4(a.counts); ALIGNED4(a.prob_sum); ALIGNED4(a.logits); ALIGNED4(a.lse); ALIGNED4(a.f); ALIGNED4(a.P);
+    ALIGNED4(a.loss); ALIGNED4(a.dlogits);
+    return SWITCH_OK;
+}
+
+switch_status run_aux(const AuxArgs& a, hipStream_t s) {
+    LAUNCH(K_AUX_STATS, "aux_stats", s,
+           launch_aux_stats(a.counts, a.prob_sum, a.T, a.E, a.alpha, a.f, a.P, a.loss, s));
+    if (a.dlogits && a.T > 0)
+        LAUNCH(K_AUX_GRAD, "aux_grad", s, launch_aux_grad(a.logits, a.lse, a.f, a.T, a.E, a.alpha, a.dlogits, s));
+    return SWITCH_OK;
+}
+
+}  // namespace
+
+namespace swmoe {
+__global__ __launch_bounds__(256) void stream_copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                          size_t n) {
+    size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const size_t stride = (size_t)gridDim.x * 256;
+    for (; i < n; i += stride) dst[i] = src[i];
+}
+hipError_t launch_stream_copy(void* dst, const void* src, size_t nbytes, hipStream_t s) {
+    const size_t n = nbytes / 16;
+    if (n == 0) return hipSuccess;
+    const size_t blocks = std::min<size_t>((n + 255) / 256, 256 * 64);
+    hipLaunchKernelGGL(stream_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const uint4*)src, (uint4*)dst, n);
+    return hipGetLastError();
+}
+}  // namespace swmoe
+
+// =================================================================== C ABI
+extern "C" {
+
+switch_status switch_capacity(int64_t T, int32_t E, double c, int32_t* C_out) {
+    if (!C_out) return fail(SWITCH_E_INVALID, "C_out must not be NULL");
+    if (T < 0) return fail(SWITCH_E_INVALID, "T must be >= 0");
+    if (E <= 0) return fail(SWITCH_E_INVALID, "E must be > 0");
+    if (!std::isfinite(c) || c < 0) return fail(SWITCH_E_INVALID, "c must be finite and >= 0");
+    if (c == 0 || T == 0) { *C_out = 0; return SWITCH_OK; }
+    // c = m * 2^ex exactly, with m a 53-bit integer
+    int ex = 0;
+    const double fr = std::frexp(c, &ex);
+    const uint64_t m = (uint64_t)std::ldexp(fr, 53);
+    ex -= 53;
+    typedef unsigned __int128 u128;
+    const u128 num = (u128)m * (u128)(uint64_t)T;  // < 2^84
+    u128 q;
+    if (ex >= 0) {
+        if (ex > 40) return fail(SWITCH_E_INVALID, "capacity does not fit in int32");
+        const u128 n2 = num << ex;
+        q = (n2 + (u128)(uint32_t)E - 1) / (u128)(uint32_t)E;
+    } else {
+        const int sh = -ex;
+        if (sh >= 96) {
+            q = num > 0 ? 1 : 0;  // 0 < c T / E < 1
+        } else {
+            const u128 den = (u128)(uint32_t)E << sh;
+            q = (num + den - 1) / den;
+        }
+    }
+    if (q > (u128)INT32_MAX) return fail(SWITCH_E_INVALID, "capacity does not fit in int32");
+    *C_out = (int32_t)q;
+    return SWITCH_OK;
+}
+
+size_t switch_route_workspace_bytes(int64_t T, int32_t d, int32_t E) {
+    if (T < 0 || d < 0 || E < 1 || E > 4096 || T >= (int64_t(1) << 31)) return 0;
+    return route_ws(T, d, E, true);
+}
+size_t switch_dispatch_workspace_bytes(int64_t T, int32_t E) {
+    if (T < 0 || E < 1 || E > 4096 || T >= (int64_t(1) << 31)) return 0;
+    return dispatch_ws(T, E);
+}
+size_t switch_expert_ffn_workspace_bytes(int32_t E, int32_t C, int32_t d_ff) {
+    if (E < 1 || C < 0 || d_ff < 0) return 0;
+    return ffn_ws(E, C, d_ff);
+}
+size_t switch_aux_loss_workspace_bytes(int64_t, int32_t) { return 0; }
+
+static size_t layer_ws(int64_t T, int32_t d, int32_t d_ff, int32_t E, int32_t C) {
+    size_t n = route_ws(T, d, E, false) + dispatch_ws(T, E) + ffn_ws(E, C, d_ff);
+    n += up((size_t)T * E * sizeof(float));          // logits
+    n += up((size_t)T * sizeof(float));              // lse
+    n += up((size_t)E * sizeof(float));              // prob_sum
+    n += up((size_t)E * C * d * sizeof(bf16_t));     // buf
+    n += up((size_t)E * C * d * sizeof(float));      // y
+    return n;
+}
+
+size_t switch_workspace_bytes(int64_t T, int32_t d, int32_t d_ff, int32_t E, int32_t C) {
+    if (T < 0 || d < 0 || d_ff < 0 || E < 1 || E > 4096 || C < 0 || T >= (int64_t(1) << 31)) return 0;
+    return layer_ws(T, d, d_ff, E, C);
+}
+
+const char* switch_status_string(switch_status s) {
+    switch (s) {
+        case SWITCH_OK: return "ok";
+        case SWITCH_E_INVALID: return "invalid argument";
+        case SWITCH_E_UNSUPPORTED: return "unsupported size";
+        case SWITCH_E_WORKSPACE: return "workspace too small";
+        case SWITCH_E_HIP: return "HIP error";
+    }
+    return "unknown status";
+}
+
+const char* switch_last_error(void) { return g_err.c_str(); }
+
+switch_status switch_route(const switch_bf16* x, const float* w_r, const float* b_r, const float* logits_in,
+                           int64_t T, int32_t d, int32_t E, float* logits_out, int32_t* expert, float* gate,
+                           float* lse, float* prob_sum, void* ws, size_t ws_bytes, void* stream) {
+    g_err.clear();
+    RouteArgs a{x, w_r, b_r, logits_in, T, d, E, logits_out, expert, gate, lse, prob_sum};
+    CHECK(validate_route(a, ws, ws_bytes));
+    return run_route(a, ws, (hipStream_t)stream);
+}
+
+switch_status switch_dispatch(const switch_bf16* x, const int32_t* expert, int64_t T, int32_t d, int32_t E,
+                              int32_t C, int32_t* position, uint8_t* keep, int32_t* counts, int32_t* accepted,
+                              int32_t* slot_token, switch_bf16* buf, void* ws, size_t ws_bytes, void* stream) {
+    g_err.clear();
+    DispatchArgs a{x, expert, T, d, E, C, position, keep, counts, accepted, slot_token, buf};
+    CHECK(validate_dispatch(a, ws, ws_bytes));
+    return run_dispatch(a, ws, (hipStream_t)stream);
+}
+
+switch_status switch_expert_ffn(const switch_bf16* buf, const int32_t* accepted, const switch_bf16* w1,
+                                const switch_bf16* w2, int32_t E, int32_t C, int32_t d, int32_t d_ff, float* y,
+                                void* ws, size_t ws_bytes, void* stream) {
+    g_err.clear();
+    FfnArgs a{buf, accepted, w1, w2, E, C, d, d_ff, y};
+    CHECK(validate_ffn(a, ws, ws_bytes));
+    return run_ffn(a, ws, (hipStream_t)stream);
+}
+
+switch_status switch_combine(const float* y, const int32_t* expert, const int32_t* position, const uint8_t* keep,
+                             const float* gate, const switch_bf16* residual, int64_t T, int32_t d, int32_t E,
+                             int32_t C, switch_bf16* out, void* stream) {
+    g_err.clear();
+    CombineArgs a{y, expert, position, keep, gate, residual, T, d, E, C, out};
+    CHECK(validate_combine(a));
+    return run_combine(a, (hipStream_t)stream);
+}
+
+switch_status switch_aux_loss(const int32_t* counts, const float* prob_sum, const float* logits, const float* lse,
+                              int64_t T, int32_t E, float alpha, float* f, float* P, float* loss, float* dlogits,
+                              void* ws, size_t ws_bytes, void* stream) {
+    (void)ws; (void)ws_bytes;
+    g_err.clear();
+    AuxArgs a{counts, prob_sum, logits, lse, T, E, alpha, f, P, loss, dlogits};
+    CHECK(validate_aux(a));
+    return run_aux(a, (hipStream_t)stream);
+}
+
+switch_status switch_layer_fwd(const switch_layer_args* la, void* ws, size_t ws_bytes, void* stream) {
+    g_err.clear();
+    if (!la) return fail(SWITCH_E_INVALID, "args must not be NULL");
+    const switch_layer_args& L = *la;
+    hipStream_t s = (hipStream_t)stream;
+    CHECK(check_TE(L.T, L.E));
+    CHECK(check_C(L.E, L.C));
+    REQUIRE(L.d >= 1 && L.d_ff >= 1, "d and d_ff must be >= 1");
+    SUPPORT(L.d % 64 == 0 && L.d_ff % 64 == 0, "d and d_ff must be multiples of 64 (got %d, %d)", L.d, L.d_ff);
+    REQUIRE(L.residual == 0 || L.residual == 1, "residual must be 0 or 1");
+    const size_t need = layer_ws(L.T, L.d, L.d_ff, L.E, L.C);
+    if (ws_bytes < need) return fail(SWITCH_E_WORKSPACE, "layer needs %zu workspace bytes, got %zu", need, ws_bytes);
+    REQUIRE(ws != nullptr, "ws must not be NULL");
+    REQUIRE(aligned(ws, kAlign), "ws must be %zu-byte aligned", kAlign);
+    Carver c{(char*)ws};
+    char* route_space = c.take<char>(route_ws(L.T, L.d, L.E, false));
+    char* dispatch_space = c.take<char>(dispatch_ws(L.T, L.E));
+    char* ffn_space = c.take<char>(ffn_ws(L.E, L.C, L.d_ff));
+    float* logits = c.take<float>((size_t)L.T * L.E);
+    float* lse = c.take<float>((size_t)L.T);
+    float* prob_sum = c.take<float>((size_t)L.E);
+    bf16_t* buf = c.take<bf16_t>((size_t)L.E * L.C * L.d);
+    float* y = c.take<float>((size_t)L.E * L.C * L.d);
+    if (L.logits) logits = L.logits;
+    if (L.lse) lse = L.lse;
+    if (L.prob_sum) prob_sum = L.prob_sum;
+    if (L.buf) buf = L.buf;
+    if (L.y) y = L.y;
+
+    RouteArgs ra{L.x, L.w_r, L.b_r, nullptr, L.T, L.d, L.E, logits, L.expert, L.gate, lse, prob_sum};
+    DispatchArgs da{L.x, L.expert, L.T, L.d, L.E, L.C, L.position, L.keep, L.counts, L.accepted, L.slot_token, buf};
+    FfnArgs fa{buf, L.accepted, L.w1, L.w2, L.E, L.C, L.d, L.d_ff, y};
+    CombineArgs ca{y, L.expert, L.position, L.keep, L.gate, L.residual ? L.x : nullptr, L.T, L.d, L.E, L.C, L.out};
+    AuxArgs xa{L.counts, prob_sum, logits, lse, L.T, L.E, L.alpha, L.f, L.P, L.loss, L.dlogits};
+    // validate everything before the first launch
+    CHECK(validate_route(ra, route_space, route_ws(L.T, L.d, L.E, false)));
+    CHECK(validate_dispatch(da, dispatch_space, dispatch_ws(L.T, L.E)));
+    CHECK(validate_ffn(fa, ffn_space, ffn_ws(L.E, L.C, L.d_ff)));
+    CHECK(validate_combine(ca));
+    CHECK(validate_aux(xa));
+    CHECK(run_route(ra, route_space, s));
+    CHECK(run_dispatch(da, dispatch_space, s));
+    CHECK(run_ffn(fa, ffn_space, s));
+    CHECK(run_combine(ca, s));
+    CHECK(run_aux(xa, s));
+    return SWITCH_OK;
+}
+
+switch_status switch_stream_copy(void* dst, const void* src, size_t nbytes, void* stream) {
+    g_err.clear();
+    REQUIRE(dst && src, "dst and src must not be NULL");
+    REQUIRE(nbytes % 16 == 0, "nbytes must be a multiple of 16");
+    REQUIRE(aligned(dst, 16) && aligned(src, 16), "pointers must be 16-byte aligned");
+    hipStream_t s = (hipStream_t)stream;
+    LAUNCH(K_COPY, "stream_copy", s, launch_stream_copy(dst, src, nbytes, s));
+    return SWITCH_OK;
+}
+
+void switch_profile_enable(int on) { g_prof = on != 0; }
+
+int switch_profile_collect(int max, int32_t* kernel_ids, float* ms) {
+    int n = 0;
+    int status = 0;
+    for (const ProfRec& r : g_recs) {
+        if (hipEventSynchronize(r.b) != hipSuccess) status = -1;
+        if (n < max && status == 0) {
+            float t = 0.f;
+            if (hipEventElapsedTime(&t, r.a, r.b) != hipSuccess) status = -1;
+            if (kernel_ids) kernel_ids[n] = r.id;
+            if (ms) ms[n] = t;
+            ++n;
+        }
+        g_pool.push_back(r.a);
+        g_pool.push_back(r.b);
+    }
+    g_recs.clear();
+    return status ? status : n;
+}
+
+const char* switch_kernel_name(int32_t id) { return (id >= 0 && id < K_COUNT) ? kKernelNames[id] : "?"; }
+
+}  // extern "C"

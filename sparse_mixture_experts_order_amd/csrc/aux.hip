@@ -1,0 +1,89 @@
+// Load-balancing statistics, aux loss and its gradient with respect to the logits.
+//   f_e = counts_e / T,  P_e = prob_sum_e / T,  L = alpha E sum_e f_e P_e
+//   dL/dz_tj = (alpha E / T) p_tj (f_j - sum_e f_e p_te),  p_tj = exp(z_tj - lse_t)
+//
+// Sources: "042 Switch Transformer" (wq-win.github.io) sec. 2: the aux loss,
+// f from the hard choice (no gradient), P the differentiable mean probability;
+// "MoE routing load collapse" (zffjzz.top), "core idea and formulas": f counts
+// the choices before the capacity limit, the gradient flows through P only.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace swmoe {
+
+// One workgroup: f, P and the loss, reduced in fp64 in a fixed tree order.
+__global__ __launch_bounds__(1024) void aux_stats(const int32_t* __restrict__ counts,
+                                                  const float* __restrict__ prob_sum, int64_t T, int E,
+                                                  float alpha, float* __restrict__ f, float* __restrict__ P,
+                                                  float* __restrict__ loss) {
+    __shared__ double red[1024];
+    double acc = 0.0;
+    for (int e = threadIdx.x; e < E; e += 1024) {
+        const double fe = T > 0 ? (double)counts[e] / (double)T : 0.0;
+        const double pe = T > 0 ? (double)prob_sum[e] / (double)T : 0.0;
+        f[e] = (float)fe;
+        P[e] = (float)pe;
+        acc += fe * pe;
+    }
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    for (int s = 512; s > 0; s >>= 1) {
+        if ((int)threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) loss[0] = (float)((double)alpha * (double)E * red[0]);
+}
+
+// One wave per token row; lane j holds experts j, j+64, ...
+template <int NCH>
+__global__ __launch_bounds__(256) void aux_grad(const float* __restrict__ logits, const float* __restrict__ lse,
+                                                const float* __restrict__ f, int64_t T, int E, float scale,
+                                                float* __restrict__ dlogits) {
+    const int lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const float* row = logits + t * E;
+    const float l = lse[t];
+    float p[NCH], fr[NCH];
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+        const int e = lane + 64 * i;
+        p[i] = e < E ? expf(row[e] - l) : 0.f;
+        fr[i] = e < E ? f[e] : 0.f;
+        s = fmaf(fr[i], p[i], s);
+    }
+    s = wave_sum(s);
+    float* g = dlogits + t * E;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+        const int e = lane + 64 * i;
+        if (e < E) g[e] = scale * p[i] * (fr[i] - s);
+    }
+}
+
+hipError_t launch_aux_stats(const int32_t* counts, const float* prob_sum, int64_t T, int E, float alpha, float* f,
+                            float* P, float* loss, hipStream_t s) {
+    hipLaunchKernelGGL(aux_stats, dim3(1), dim3(1024), 0, s, counts, prob_sum, T, E, alpha, f, P, loss);
+    return hipGetLastError();
+}
+
+hipError_t launch_aux_grad(const float* logits, const float* lse, const float* f, int64_t T, int E, float alpha,
+                           float* dlogits, hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    const float scale = (float)((double)alpha * (double)E / (double)T);
+    const unsigned grid = (unsigned)((T + 3) / 4);
+    const int nch = (E + 63) / 64;
+#define SWMOE_GRAD(N) hipLaunchKernelGGL(aux_grad<N>, dim3(grid), dim3(256), 0, s, logits, lse, f, T, E, scale, dlogits)
+    if (nch <= 1) SWMOE_GRAD(1);
+    else if (nch <= 2) SWMOE_GRAD(2);
+    else if (nch <= 4) SWMOE_GRAD(4);
+    else if (nch <= 8) SWMOE_GRAD(8);
+    else if (nch <= 16) SWMOE_GRAD(16);
+    else if (nch <= 32) SWMOE_GRAD(32);
+    else SWMOE_GRAD(64);
+#undef SWMOE_GRAD
+    return hipGetLastError();
+}
+
+}  // namespace swmoe

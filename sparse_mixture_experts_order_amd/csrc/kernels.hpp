@@ -1,0 +1,50 @@
+// Host-side launchers of the device kernels (one per kernel; each enqueues on
+// the given stream and returns hipGetLastError()).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+namespace swmoe {
+typedef uint16_t bf16_t;
+
+// route.hip
+hipError_t launch_split_router_weights(const float* w_r, bf16_t* wr3, int d, int E, hipStream_t s);
+hipError_t launch_router_gemm(const bf16_t* x, const bf16_t* wr3, const float* b_r, float* logits, int T, int d,
+                              int E, hipStream_t s);
+int router_softmax_blocks(int64_t T, int E);
+hipError_t launch_router_softmax(const float* logits, int T, int E, int32_t* expert, float* gate, float* lse,
+                                 float* part, hipStream_t s);
+hipError_t launch_router_reduce(const float* part, int nblk, int E, float* prob_sum, hipStream_t s);
+
+// dispatch.hip
+int scan_tiles(int64_t T);
+hipError_t launch_scan_local(const int32_t* expert, int T, int E, int32_t* local_rank, int32_t* tile_counts,
+                             hipStream_t s);
+hipError_t launch_scan_offsets(int32_t* tile_counts, int ntiles, int E, int C, int32_t* counts, int32_t* accepted,
+                               hipStream_t s);
+hipError_t launch_gather(const bf16_t* x, const int32_t* expert, const int32_t* offsets, const int32_t* accepted,
+                         int T, int d, int E, int C, int32_t* position, uint8_t* keep, int32_t* slot_token,
+                         bf16_t* buf, hipStream_t s);
+
+// expert_ffn.hip
+hipError_t launch_expert_gemm1(const bf16_t* buf, const bf16_t* w1, const int32_t* accepted, bf16_t* h, int E,
+                               int C, int d, int d_ff, hipStream_t s);
+hipError_t launch_expert_gemm2(const bf16_t* h, const bf16_t* w2, const int32_t* accepted, float* y, int E, int C,
+                               int d, int d_ff, hipStream_t s);
+
+// combine.hip
+hipError_t launch_combine(const float* y, const int32_t* expert, const int32_t* position, const uint8_t* keep,
+                          const float* gate, const bf16_t* residual, int64_t T, int d, int E, int C, bf16_t* out,
+                          hipStream_t s);
+
+// aux.hip
+hipError_t launch_aux_stats(const int32_t* counts, const float* prob_sum, int64_t T, int E, float alpha, float* f,
+                            float* P, float* loss, hipStream_t s);
+hipError_t launch_aux_grad(const float* logits, const float* lse, const float* f, int64_t T, int E, float alpha,
+                           float* dlogits, hipStream_t s);
+
+// api.hip
+hipError_t launch_stream_copy(void* dst, const void* src, size_t nbytes, hipStream_t s);
+}  // namespace swmoe

@@ -1,0 +1,134 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol the header
+declares, sizes workspaces, computes capacities exactly, and rejects bad
+arguments before any HIP call (so none of these tests touches a GPU)."""
+import os
+import random
+import re
+
+import pytest
+
+import sparse_mixture_experts_order_amd as sw
+from oracle.switch_oracle import capacity as oracle_capacity
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "switch_moe.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(switch_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = sw.lib()
+    names = declared_functions()
+    assert len(names) >= 18
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(sw.EXPORTS) == names
+
+
+def test_capacity_matches_oracle():
+    cases = [(512, 4, 1.25), (16384, 128, 1.0), (16384, 64, 2.0), (32768, 128, 1.25), (65536, 2048, 1.0),
+             (64, 4, 1.25), (100, 10, 1.0), (30, 3, 0.1), (0, 5, 3.0), (7, 7, 0.0), (1, 4096, 1e-300),
+             (2**31 - 1, 1, 1.0), (1000, 3, 1 / 3), (999, 7, 0.7)]
+    rng = random.Random(0)
+    for _ in range(2000):
+        cases.append((rng.randrange(0, 1 << 20), rng.randrange(1, 5000), rng.choice([rng.random() * 4, rng.randrange(0, 9) / 4])))
+    for T, E, c in cases:
+        assert sw.switch_capacity(T, E, c) == oracle_capacity(T, E, c), (T, E, c)
+
+
+@pytest.mark.parametrize("args", [(-1, 4, 1.0), (10, 0, 1.0), (10, 4, -0.5), (10, 4, float("nan")),
+                                  (10, 4, float("inf")), (2**31 - 1, 1, 2.0)])
+def test_capacity_rejects(args):
+    with pytest.raises(sw.SwitchError) as ei:
+        sw.switch_capacity(*args)
+    assert ei.value.status == sw.SWITCH_E_INVALID
+
+
+def test_workspace_sizes():
+    assert sw.switch_workspace_bytes(16384, 768, 3072, 128, 128) >= 128 * 128 * 3072 * 2 + 128 * 128 * 768 * 6
+    assert sw.switch_expert_ffn_workspace_bytes(128, 128, 3072) >= 128 * 128 * 3072 * 2
+    assert sw.switch_dispatch_workspace_bytes(16384, 128) >= (16384 // 256) * 128 * 4
+    assert sw.switch_route_workspace_bytes(16384, 768, 128) >= 3 * 768 * 128 * 2 + 16384 * 128 * 4
+    assert sw.switch_aux_loss_workspace_bytes(10, 4) == 0
+    assert sw.switch_workspace_bytes(10, 64, 64, 0, 1) == 0      # E = 0 is invalid
+    assert sw.switch_workspace_bytes(10, 64, 64, 5000, 1) == 0   # E above the limit
+
+
+def _status(fn, *a):
+    with pytest.raises(sw.SwitchError) as ei:
+        fn(*a)
+    return ei.value.status
+
+
+FAKE = 1 << 20   # an aligned non-NULL address; never dereferenced because validation fails first
+
+
+def test_route_validation():
+    L = sw.lib()
+    st = L.switch_route(None, FAKE, None, None, 16, 64, 4, None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert st == sw.SWITCH_E_INVALID and b"x" in L.switch_last_error()
+    st = L.switch_route(FAKE, FAKE, None, None, 16, 48, 4, None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert st == sw.SWITCH_E_UNSUPPORTED
+    st = L.switch_route(FAKE, FAKE, None, None, 16, 64, 0, None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert st == sw.SWITCH_E_INVALID
+    st = L.switch_route(FAKE, FAKE, None, None, 16, 64, 4, None, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None)
+    assert st == sw.SWITCH_E_WORKSPACE
+    st = L.switch_route(FAKE + 2, FAKE, None, None, 16, 64, 4, None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert st == sw.SWITCH_E_INVALID and b"aligned" in L.switch_last_error()
+    st = L.switch_route(FAKE, FAKE, None, None, -1, 64, 4, None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert st == sw.SWITCH_E_INVALID
+    st = L.switch_route(FAKE, FAKE, None, None, 16, 64, 5000, None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert st == sw.SWITCH_E_UNSUPPORTED
+
+
+def test_dispatch_validation():
+    L = sw.lib()
+    ok = dict(x=FAKE, e=FAKE, T=16, d=64, E=4, C=4, pos=FAKE, keep=FAKE, cnt=FAKE, acc=FAKE, st=None, buf=FAKE,
+              ws=FAKE, wsn=1 << 20)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.switch_dispatch(a["x"], a["e"], a["T"], a["d"], a["E"], a["C"], a["pos"], a["keep"], a["cnt"],
+                                 a["acc"], a["st"], a["buf"], a["ws"], a["wsn"], None)
+    assert call(C=-1) == sw.SWITCH_E_INVALID
+    assert call(x=None) == sw.SWITCH_E_INVALID
+    assert call(buf=None) == sw.SWITCH_E_INVALID
+    assert call(d=12) == sw.SWITCH_E_UNSUPPORTED
+    assert call(wsn=0) == sw.SWITCH_E_WORKSPACE
+    assert call(E=1 << 16, C=1 << 16) == sw.SWITCH_E_UNSUPPORTED
+    assert call(ws=FAKE + 64) == sw.SWITCH_E_INVALID
+
+
+def test_ffn_combine_aux_validation():
+    L = sw.lib()
+    assert L.switch_expert_ffn(FAKE, FAKE, FAKE, FAKE, 4, 8, 96, 128, FAKE, FAKE, 1 << 30, None) == sw.SWITCH_E_UNSUPPORTED
+    assert L.switch_expert_ffn(FAKE, FAKE, None, FAKE, 4, 8, 64, 128, FAKE, FAKE, 1 << 30, None) == sw.SWITCH_E_INVALID
+    assert L.switch_expert_ffn(FAKE, FAKE, FAKE, FAKE, 4, 8, 64, 128, FAKE, FAKE, 64, None) == sw.SWITCH_E_WORKSPACE
+    assert L.switch_combine(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, 64, 4, 4, FAKE, None) == sw.SWITCH_E_INVALID  # alias
+    assert L.switch_combine(FAKE, None, FAKE, FAKE, FAKE, None, 16, 64, 4, 4, FAKE, None) == sw.SWITCH_E_INVALID
+    assert L.switch_aux_loss(FAKE, FAKE, None, None, 16, 4, float("nan"), FAKE, FAKE, FAKE, None, None, 0, None) == sw.SWITCH_E_INVALID
+    assert L.switch_aux_loss(FAKE, FAKE, None, FAKE, 16, 4, 0.01, FAKE, FAKE, FAKE, FAKE, None, 0, None) == sw.SWITCH_E_INVALID
+    assert L.switch_stream_copy(FAKE, FAKE, 15, None) == sw.SWITCH_E_INVALID
+
+
+def test_layer_validation():
+    L = sw.lib()
+    a = sw.LayerArgs()
+    a.T, a.d, a.d_ff, a.E, a.C, a.alpha, a.residual = 16, 64, 128, 4, 8, 0.01, 1
+    assert L.switch_layer_fwd(None, FAKE, 1 << 30, None) == sw.SWITCH_E_INVALID
+    import ctypes
+    assert L.switch_layer_fwd(ctypes.byref(a), FAKE, 1 << 30, None) == sw.SWITCH_E_INVALID   # NULL pointers
+    a.d = 96
+    assert L.switch_layer_fwd(ctypes.byref(a), FAKE, 1 << 30, None) == sw.SWITCH_E_UNSUPPORTED
+    a.d = 64
+    assert L.switch_layer_fwd(ctypes.byref(a), FAKE, 16, None) == sw.SWITCH_E_WORKSPACE
+
+
+def test_status_strings():
+    L = sw.lib()
+    for s in range(5):
+        assert L.switch_status_string(s)
+    assert L.switch_kernel_name(7) == b"expert_gemm1"
