@@ -8,6 +8,7 @@ namespace swmoe {
 typedef uint16_t bf16_t;                                        // raw bf16 bits
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));      // MFMA A/B operand (8 x bf16)
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 16-byte load/store unit (a native vector, kept in VGPRs)
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kWave = 64;
@@ -21,6 +22,10 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
+    return __builtin_bit_cast(bf16x8, v);
+}
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
     bf16x8 r;

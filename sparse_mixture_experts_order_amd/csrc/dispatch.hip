@@ -63,21 +63,33 @@ __global__ __launch_bounds__(256) void scan_local(const int32_t* __restrict__ ex
     for (int i = threadIdx.x; i < E; i += 256) tile_counts[(size_t)blockIdx.x * E + i] = hist[i];
 }
 
-// tile_counts[b][e] becomes the exclusive prefix over tiles b' < b.
+// tile_counts[b][e] becomes the exclusive prefix over tiles b' < b.  One wave
+// per expert: lanes take 64 tiles at a time, a wave prefix sum (shuffles)
+// ranks them and the running total carries into the next 64.
 __global__ __launch_bounds__(256) void scan_offsets(int32_t* __restrict__ tile_counts, int ntiles, int E,
                                                     int C, int32_t* __restrict__ counts,
                                                     int32_t* __restrict__ accepted) {
-    const int e = blockIdx.x * 256 + threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (e >= E) return;
     int run = 0;
-    for (int b = 0; b < ntiles; ++b) {
+    for (int b0 = 0; b0 < ntiles; b0 += 64) {
+        const int b = b0 + lane;
         const size_t o = (size_t)b * E + e;
-        const int c = tile_counts[o];
-        tile_counts[o] = run;
-        run += c;
+        const int c = b < ntiles ? tile_counts[o] : 0;
+        int incl = c;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int v = __shfl_up(incl, off);
+            if (lane >= off) incl += v;
+        }
+        if (b < ntiles) tile_counts[o] = run + incl - c;
+        run += __shfl(incl, 63);
     }
-    counts[e] = run;
-    accepted[e] = min(run, C);
+    if (lane == 0) {
+        counts[e] = run;
+        accepted[e] = min(run, C);
+    }
 }
 
 // Workgroups [0, ntok_blocks) handle GATHER_TOK tokens each; the rest zero the
@@ -149,7 +161,7 @@ hipError_t launch_scan_local(const int32_t* expert, int T, int E, int32_t* local
 
 hipError_t launch_scan_offsets(int32_t* tile_counts, int ntiles, int E, int C, int32_t* counts,
                                int32_t* accepted, hipStream_t s) {
-    hipLaunchKernelGGL(scan_offsets, dim3((E + 255) / 256), dim3(256), 0, s, tile_counts, ntiles, E, C, counts,
+    hipLaunchKernelGGL(scan_offsets, dim3((E + 3) / 4), dim3(256), 0, s, tile_counts, ntiles, E, C, counts,
                        accepted);
     return hipGetLastError();
 }

@@ -26,20 +26,35 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
+#include <type_traits>
+
 namespace swmoe {
 
 constexpr int FFN_LDS_STRIDE = 72;  // bf16 elements per LDS row (64 + 8 pad)
 
-template <int TOKB, int NBW, bool GEMM1>
-__global__ __launch_bounds__(256) void expert_gemm(const bf16_t* __restrict__ A,   // [E, C, K]
-                                                   const bf16_t* __restrict__ W,   // [E, N, K]
-                                                   const int32_t* __restrict__ accepted,
-                                                   void* __restrict__ out,         // [E, C, N]
-                                                   int C, int K, int N, int n_tiles, int tok_tiles,
-                                                   int ntiles, int grid_padded) {
+// TOKB: 32-row token blocks per tile; NBW: 32-row weight blocks per wave;
+// WAVES: waves per workgroup; R: depth of the register rings (R-1 chunks of
+// 64 K-elements in flight ahead of the MFMAs).
+template <int TOKB, int NBW, int WAVES, int R, bool GEMM1>
+__global__ __launch_bounds__(64 * WAVES) void expert_gemm(const bf16_t* __restrict__ A,   // [E, C, K]
+                                                          const bf16_t* __restrict__ W,   // [E, N, K]
+                                                          const int32_t* __restrict__ accepted,
+                                                          void* __restrict__ out,         // [E, C, N]
+                                                          int C, int K, int N, int n_tiles, int tok_tiles,
+                                                          int ntiles, int grid_padded) {
     constexpr int TOK = 32 * TOKB;
-    constexpr int NWG = 4 * 32 * NBW;
-    __shared__ __attribute__((aligned(16))) bf16_t lds[2][TOK * FFN_LDS_STRIDE];
+    constexpr int NWG = WAVES * 32 * NBW;
+    constexpr int NTHR = 64 * WAVES;
+    constexpr int PIECES = TOK * 8;                       // 16-byte pieces of one token chunk
+    constexpr int APT = (PIECES + NTHR - 1) / NTHR;       // pieces per thread
+    // output staging after the K loop reuses the same LDS: TOK rows of NWG
+    // values (bf16 for GEMM1, fp32 for GEMM2), rows padded by 16 bytes
+    constexpr int OUT_BYTES = GEMM1 ? 2 : 4;
+    constexpr int OSTRIDE = NWG * OUT_BYTES + 16;                     // bytes per staged row
+    constexpr int A_BYTES = 2 * TOK * FFN_LDS_STRIDE * 2;
+    constexpr int LDS_BYTES = A_BYTES > TOK * OSTRIDE ? A_BYTES : TOK * OSTRIDE;
+    __shared__ __attribute__((aligned(16))) char lds_raw[LDS_BYTES];
+    bf16_t (*lds)[TOK * FFN_LDS_STRIDE] = reinterpret_cast<bf16_t (*)[TOK * FFN_LDS_STRIDE]>(lds_raw);
 
     const int tile = xcd_swizzle(blockIdx.x, grid_padded);
     if (tile >= ntiles) return;
@@ -51,14 +66,16 @@ __global__ __launch_bounds__(256) void expert_gemm(const bf16_t* __restrict__ A,
     const int acc_e = min(max(accepted[e], 0), C);  // rows in use, never past the capacity
     if (tok_base >= acc_e) return;
     const int nv = min(TOK, acc_e - tok_base);  // valid rows in this tile
-    const int nvb = (nv + 31) >> 5;             // valid 32-row blocks
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
     const int half = lane >> 5, l32 = lane & 31;
     const int wrow0 = nt * NWG + wave * 32 * NBW;
     const bool wave_active = wrow0 < N;
 
-    const bf16_t* Ae = A + ((size_t)e * C + tok_base) * K;
+    // Weight rows: lane l reads row wrow0 + 32*nb + l%32, 64 contiguous bytes
+    // per chunk (its half of the 128-byte chunk).  Waves past the last row
+    // read row 0 and store nothing.
     const bf16_t* wptr[NBW];
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb) {
@@ -66,32 +83,26 @@ __global__ __launch_bounds__(256) void expert_gemm(const bf16_t* __restrict__ A,
         wptr[nb] = W + ((size_t)e * N + r) * K + half * 32;
     }
 
-    // token tile staging: thread -> (row = tid/8 + 32*j, 16-byte column tid%8)
-    const int srow = threadIdx.x >> 3, scol = (threadIdx.x & 7) * 8;
-    uint4 areg[TOKB];
-    auto load_a = [&](int kc) {
+    // Token-tile staging: piece q = tid + j*NTHR -> (row q/8, 16-byte column q%8).
+    // Pieces past the tile repeat the last piece and rows past the valid count
+    // re-load the last valid row, so every load is unconditional.
+    const bf16_t* Ae = A + ((size_t)e * C + tok_base) * K;
+    const bf16_t* aptr[APT];
+    int aoff[APT];
 #pragma unroll
-        for (int j = 0; j < TOKB; ++j) {
-            const int r = srow + 32 * j;
-            if (r < nv) areg[j] = *(const uint4*)(Ae + (size_t)r * K + kc * 64 + scol);
-        }
-    };
-    auto store_a = [&](int buf) {
-#pragma unroll
-        for (int j = 0; j < TOKB; ++j) {
-            const int r = srow + 32 * j;
-            if (r < nv) *(uint4*)(&lds[buf][r * FFN_LDS_STRIDE + scol]) = areg[j];
-        }
-    };
+    for (int j = 0; j < APT; ++j) {
+        const int q = min((int)threadIdx.x + j * NTHR, PIECES - 1);
+        const int row = q >> 3, c16 = (q & 7) * 8;
+        aptr[j] = Ae + (size_t)min(row, nv - 1) * K + c16;
+        aoff[j] = row * FFN_LDS_STRIDE + c16;
+    }
 
-    uint4 wreg[2][NBW][4];
-    auto load_w = [&](int kc, int buf) {
-        if (!wave_active) return;
-#pragma unroll
-        for (int nb = 0; nb < NBW; ++nb)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) wreg[buf][nb][j] = *(const uint4*)(wptr[nb] + kc * 64 + j * 8);
-    };
+    // Register rings.  At step k a wave issues the token chunk k+R-1 first
+    // and then the weight chunk k+R-1: vector-memory counters complete in
+    // issue order, so waiting for the token chunk k+1 never waits for a
+    // weight chunk that is still ahead of the MFMAs.
+    u32x4 areg[R][APT];
+    u32x4 wreg[R][NBW][4];
 
     f32x16 acc[NBW][TOKB];
 #pragma unroll
@@ -101,90 +112,120 @@ __global__ __launch_bounds__(256) void expert_gemm(const bf16_t* __restrict__ A,
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[nb][tb][i] = 0.f;
 
-    auto compute = [&](int buf) {
-        if (!wave_active) return;
+    const int nk = K >> 6;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            bf16x8 bt[TOKB];
+    for (int p = 0; p < R - 1; ++p) {
+        const int kc = min(p, nk - 1);
 #pragma unroll
-            for (int tb = 0; tb < TOKB; ++tb)
-                if (tb < nvb)
-                    bt[tb] = as_bf16x8(*(const uint4*)(&lds[buf][(tb * 32 + l32) * FFN_LDS_STRIDE + half * 32 + s * 8]));
+        for (int j = 0; j < APT; ++j) areg[p][j] = *(const u32x4*)(aptr[j] + kc * 64);
 #pragma unroll
-            for (int nb = 0; nb < NBW; ++nb) {
-                const bf16x8 wa = as_bf16x8(wreg[buf][nb][s]);
+        for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
-                for (int tb = 0; tb < TOKB; ++tb)
-                    if (tb < nvb) acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, bt[tb], acc[nb][tb], 0, 0, 0);
+            for (int j = 0; j < 4; ++j) wreg[p][nb][j] = *(const u32x4*)(wptr[nb] + kc * 64 + j * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < APT; ++j) *(u32x4*)(&lds[0][aoff[j]]) = areg[0][j];
+
+    for (int k0 = 0; k0 < nk; k0 += R) {
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+            const int k = k0 + u;
+            if (k < nk) {
+                const int kn = min(k + R - 1, nk - 1);   // chunk entering the rings (clamped)
+                const int slot_n = (u + R - 1) % R;      // a constant once the u loop is unrolled
+#pragma unroll
+                for (int j = 0; j < APT; ++j) areg[slot_n][j] = *(const u32x4*)(aptr[j] + kn * 64);
+#pragma unroll
+                for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        wreg[slot_n][nb][j] = *(const u32x4*)(wptr[nb] + kn * 64 + j * 8);
+                __syncthreads();
+                const bf16_t* lb = &lds[k & 1][0];
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    bf16x8 bt[TOKB];
+#pragma unroll
+                    for (int tb = 0; tb < TOKB; ++tb)
+                        bt[tb] = as_bf16x8(*(const u32x4*)(lb + (tb * 32 + l32) * FFN_LDS_STRIDE + half * 32 + s * 8));
+#pragma unroll
+                    for (int nb = 0; nb < NBW; ++nb) {
+                        const bf16x8 wa = as_bf16x8(wreg[u][nb][s]);
+#pragma unroll
+                        for (int tb = 0; tb < TOKB; ++tb)
+                            acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, bt[tb], acc[nb][tb], 0, 0, 0);
+                    }
+                }
+                // token chunk k+1 (ring slot u+1) into the other LDS buffer
+                const int slot_a = (u + 1) % R;
+                bf16_t* sb = &lds[(k + 1) & 1][0];
+#pragma unroll
+                for (int j = 0; j < APT; ++j) *(u32x4*)(sb + aoff[j]) = areg[slot_a][j];
             }
         }
-    };
-
-    const int nk = K >> 6;
-    load_a(0);
-    load_w(0, 0);
-    store_a(0);
-    for (int kc = 0; kc < nk; kc += 2) {
-        // even step: compute chunk kc from buffers 0
-        if (kc + 1 < nk) { load_a(kc + 1); load_w(kc + 1, 1); }
-        __syncthreads();
-        compute(0);
-        if (kc + 1 < nk) store_a(1);
-        if (kc + 1 >= nk) break;
-        // odd step: compute chunk kc+1 from buffers 1
-        if (kc + 2 < nk) { load_a(kc + 2); load_w(kc + 2, 0); }
-        __syncthreads();
-        compute(1);
-        if (kc + 2 < nk) store_a(0);
     }
 
-    if (!wave_active) return;
-    // lane holds token column l32 of block tb and weight rows 8*(i/4) + 4*half + i%4
+    // Epilogue: each wave parks its tile in LDS (lane: token column l32 of
+    // block tb, weight rows 8*(i/4) + 4*half + i%4, so 4 consecutive outputs
+    // per store), then the workgroup writes whole rows of NWG outputs per
+    // token with 16-byte stores, so every token row gets NWG*OUT_BYTES
+    // contiguous bytes instead of scattered 8/16-byte pieces.
+    __syncthreads();   // all waves are done reading the token tile
 #pragma unroll
     for (int tb = 0; tb < TOKB; ++tb) {
         const int r = tb * 32 + l32;
-        if (r >= nv) continue;
-        const size_t orow = ((size_t)e * C + tok_base + r) * N;
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int n = wrow0 + nb * 32 + q * 8 + half * 4;
+                const int c = wave * 32 * NBW + nb * 32 + q * 8 + half * 4;   // column within the tile
                 const f32x16& a = acc[nb][tb];
+                char* dst = lds_raw + r * OSTRIDE + c * OUT_BYTES;
                 if constexpr (GEMM1) {
                     const uint32_t b0 = bf16_rne(fmaxf(a[4 * q + 0], 0.f)), b1 = bf16_rne(fmaxf(a[4 * q + 1], 0.f));
                     const uint32_t b2 = bf16_rne(fmaxf(a[4 * q + 2], 0.f)), b3 = bf16_rne(fmaxf(a[4 * q + 3], 0.f));
-                    *(uint2*)((bf16_t*)out + orow + n) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+                    *(uint2*)dst = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
                 } else {
-                    *(f32x4*)((float*)out + orow + n) = f32x4{a[4 * q + 0], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+                    *(f32x4*)dst = f32x4{a[4 * q + 0], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
                 }
             }
+    }
+    __syncthreads();
+    constexpr int VPR = NWG * OUT_BYTES / 16;        // 16-byte vectors per staged row
+    const int ncols = min(NWG, N - nt * NWG);        // valid columns (a multiple of 32)
+    const int vpr_valid = ncols * OUT_BYTES / 16;
+    char* gout = (char*)out + (((size_t)e * C + tok_base) * N + (size_t)nt * NWG) * OUT_BYTES;
+    for (int i = threadIdx.x; i < TOK * VPR; i += NTHR) {
+        const int r = i / VPR, v = i - r * VPR;
+        if (r < nv && v < vpr_valid)
+            *(u32x4*)(gout + (size_t)r * N * OUT_BYTES + v * 16) = *(const u32x4*)(lds_raw + r * OSTRIDE + v * 16);
     }
 }
 
 // ------------------------------------------------------------------ launchers
-template <int TOKB, int NBW, bool GEMM1>
-static hipError_t launch_expert_gemm_t(const bf16_t* A, const bf16_t* W, const int32_t* accepted, void* out,
-                                       int E, int C, int K, int N, hipStream_t s) {
-    constexpr int TOK = 32 * TOKB, NWG = 128 * NBW;
+template <int TOKB, int NBW, int WAVES, int R, bool GEMM1>
+hipError_t launch_expert_gemm_t(const bf16_t* A, const bf16_t* W, const int32_t* accepted, void* out, int E, int C,
+                                int K, int N, hipStream_t s) {
+    constexpr int TOK = 32 * TOKB, NWG = WAVES * 32 * NBW;
     const int n_tiles = (N + NWG - 1) / NWG;
     const int tok_tiles = (C + TOK - 1) / TOK;
     const int64_t ntiles = (int64_t)E * n_tiles * tok_tiles;
     if (ntiles == 0) return hipSuccess;
     const int64_t grid = (ntiles + 7) / 8 * 8;
-    hipLaunchKernelGGL((expert_gemm<TOKB, NBW, GEMM1>), dim3((unsigned)grid), dim3(256), 0, s, A, W, accepted,
-                       out, C, K, N, n_tiles, tok_tiles, (int)ntiles, (int)grid);
+    hipLaunchKernelGGL((expert_gemm<TOKB, NBW, WAVES, R, GEMM1>), dim3((unsigned)grid), dim3(64 * WAVES), 0, s, A, W,
+                       accepted, out, C, K, N, n_tiles, tok_tiles, (int)ntiles, (int)grid);
     return hipGetLastError();
 }
 
+#ifndef SWMOE_FFN_CUSTOM_DISPATCH
 template <bool GEMM1>
 static hipError_t launch_expert_gemm(const bf16_t* A, const bf16_t* W, const int32_t* accepted, void* out, int E,
                                      int C, int K, int N, hipStream_t s) {
     // rows per tile: enough 32-row blocks for the capacity, at most 8
-    if (C > 128) return launch_expert_gemm_t<8, 1, GEMM1>(A, W, accepted, out, E, C, K, N, s);
-    if (C > 64) return launch_expert_gemm_t<4, 1, GEMM1>(A, W, accepted, out, E, C, K, N, s);
-    if (C > 32) return launch_expert_gemm_t<2, 2, GEMM1>(A, W, accepted, out, E, C, K, N, s);
-    return launch_expert_gemm_t<1, 2, GEMM1>(A, W, accepted, out, E, C, K, N, s);
+    if (C > 128) return launch_expert_gemm_t<8, 1, 4, 3, GEMM1>(A, W, accepted, out, E, C, K, N, s);
+    if (C > 64) return launch_expert_gemm_t<4, 1, 8, 5, GEMM1>(A, W, accepted, out, E, C, K, N, s);
+    if (C > 32) return launch_expert_gemm_t<2, 2, 4, 3, GEMM1>(A, W, accepted, out, E, C, K, N, s);
+    return launch_expert_gemm_t<1, 2, 4, 3, GEMM1>(A, W, accepted, out, E, C, K, N, s);
 }
 
 hipError_t launch_expert_gemm1(const bf16_t* buf, const bf16_t* w1, const int32_t* accepted, bf16_t* h, int E,
@@ -196,5 +237,6 @@ hipError_t launch_expert_gemm2(const bf16_t* h, const bf16_t* w2, const int32_t*
                                int d, int d_ff, hipStream_t s) {
     return launch_expert_gemm<false>(h, w2, accepted, y, E, C, d_ff, d, s);
 }
+#endif
 
 }  // namespace swmoe

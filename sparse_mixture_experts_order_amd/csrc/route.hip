@@ -174,14 +174,34 @@ __global__ __launch_bounds__(256) void router_softmax(const float* __restrict__ 
     for (int e = threadIdx.x; e < E; e += 256) part[(size_t)blockIdx.x * E + e] = red[e];
 }
 
-// prob_sum[e] = sum over workgroups of the partial sums, in fp64, in order.
-__global__ __launch_bounds__(256) void router_reduce(const float* __restrict__ part, int nblk, int E,
-                                                     float* __restrict__ prob_sum) {
-    int e = blockIdx.x * 256 + threadIdx.x;
-    if (e >= E) return;
+// prob_sum[e] = sum over workgroups of the partial sums, in fp64, in a fixed
+// order: a workgroup owns 64 experts; its 16 row groups take every 16th
+// partial row, then the row groups are added in order.
+__global__ __launch_bounds__(1024) void router_reduce(const float* __restrict__ part, int nblk, int E,
+                                                      float* __restrict__ prob_sum) {
+    __shared__ double red[16][64];
+    const int c = threadIdx.x & 63, rg = threadIdx.x >> 6;
+    const int e = blockIdx.x * 64 + c;
     double s = 0.0;
-    for (int b = 0; b < nblk; ++b) s += (double)part[(size_t)b * E + e];
-    prob_sum[e] = (float)s;
+    if (e < E) {
+        int b = rg;
+        for (; b + 48 < nblk; b += 64) {
+            const float v0 = part[(size_t)b * E + e], v1 = part[(size_t)(b + 16) * E + e];
+            const float v2 = part[(size_t)(b + 32) * E + e], v3 = part[(size_t)(b + 48) * E + e];
+            s += (double)v0;
+            s += (double)v1;
+            s += (double)v2;
+            s += (double)v3;
+        }
+        for (; b < nblk; b += 16) s += (double)part[(size_t)b * E + e];
+    }
+    red[rg][c] = s;
+    __syncthreads();
+    if (rg == 0 && e < E) {
+        double t = 0.0;
+        for (int r = 0; r < 16; ++r) t += red[r][c];
+        prob_sum[e] = (float)t;
+    }
 }
 
 // ------------------------------------------------------------------ launchers
@@ -200,7 +220,8 @@ hipError_t launch_router_gemm(const bf16_t* x, const bf16_t* wr3, const float* b
 
 int router_softmax_blocks(int64_t T, int E) {
     if (T <= 0) return 0;
-    int64_t nblk = std::min<int64_t>(2048, std::max<int64_t>(1, (int64_t(1) << 19) / E));
+    // about 64 tokens per workgroup, at most 4 MiB of partial sums
+    int64_t nblk = std::min<int64_t>((T + 63) / 64, std::max<int64_t>(1, (int64_t(1) << 20) / E));
     int64_t tpb = (T + nblk - 1) / nblk;
     return (int)((T + tpb - 1) / tpb);
 }
@@ -226,7 +247,7 @@ hipError_t launch_router_softmax(const float* logits, int T, int E, int32_t* exp
 }
 
 hipError_t launch_router_reduce(const float* part, int nblk, int E, float* prob_sum, hipStream_t s) {
-    hipLaunchKernelGGL(router_reduce, dim3((E + 255) / 256), dim3(256), 0, s, part, nblk, E, prob_sum);
+    hipLaunchKernelGGL(router_reduce, dim3((E + 63) / 64), dim3(1024), 0, s, part, nblk, E, prob_sum);
     return hipGetLastError();
 }
 
