@@ -34,11 +34,11 @@ switch_status hip_fail(hipError_t e, const char* where) {
 // ----------------------------------------------------------- launch timing
 enum KernelId {
     K_SPLIT = 0, K_RGEMM, K_RSOFTMAX, K_RREDUCE, K_SCAN_LOCAL, K_SCAN_OFFSETS, K_GATHER,
-    K_GEMM1, K_GEMM2, K_COMBINE, K_AUX_STATS, K_AUX_GRAD, K_COPY, K_COUNT
+    K_GEMM1, K_GEMM2, K_COMBINE, K_AUX_STATS, K_AUX_GRAD, K_COPY, K_FFN_TILES, K_COUNT
 };
 const char* kKernelNames[K_COUNT] = {
     "split_router_weights", "router_gemm", "router_softmax", "router_reduce", "scan_local", "scan_offsets",
-    "gather", "expert_gemm1", "expert_gemm2", "combine", "aux_stats", "aux_grad", "stream_copy"};
+    "gather", "expert_gemm1", "expert_gemm2", "combine", "aux_stats", "aux_grad", "stream_copy", "ffn_tile_prefix"};
 
 struct ProfRec { int id; hipEvent_t a, b; };
 bool g_prof = false;
@@ -91,7 +91,10 @@ size_t route_ws(int64_t T, int32_t d, int32_t E, bool need_logits) {
     return n;
 }
 size_t dispatch_ws(int64_t T, int32_t E) { return up((size_t)scan_tiles(T) * E * sizeof(int32_t)); }
-size_t ffn_ws(int32_t E, int32_t C, int32_t d_ff) { return up((size_t)E * C * d_ff * sizeof(bf16_t)); }
+size_t ffn_ws(int32_t E, int32_t C, int32_t d_ff) {
+    return up((size_t)E * C * d_ff * sizeof(bf16_t)) + up((size_t)(E + 1) * sizeof(int32_t)) +
+           up(ffn_tile_table_entries(E, C) * sizeof(int4));
+}
 
 // ----------------------------------------------------------- validation
 #define REQUIRE(cond, ...) \
@@ -231,8 +234,11 @@ switch_status run_ffn(const FfnArgs& a, void* ws, hipStream_t s) {
     if (a.C == 0) return SWITCH_OK;
     Carver c{(char*)ws};
     bf16_t* h = c.take<bf16_t>((size_t)a.E * a.C * a.d_ff);
-    LAUNCH(K_GEMM1, "expert_gemm1", s, launch_expert_gemm1(a.buf, a.w1, a.accepted, h, a.E, a.C, a.d, a.d_ff, s));
-    LAUNCH(K_GEMM2, "expert_gemm2", s, launch_expert_gemm2(h, a.w2, a.accepted, a.y, a.E, a.C, a.d, a.d_ff, s));
+    int32_t* pre = c.take<int32_t>((size_t)a.E + 1);
+    int4* ttab = c.take<int4>(ffn_tile_table_entries(a.E, a.C));
+    LAUNCH(K_FFN_TILES, "ffn_tile_prefix", s, launch_ffn_tile_prefix(a.accepted, a.E, a.C, pre, ttab, s));
+    LAUNCH(K_GEMM1, "expert_gemm1", s, launch_expert_gemm1(a.buf, a.w1, pre, ttab, h, a.E, a.C, a.d, a.d_ff, s));
+    LAUNCH(K_GEMM2, "expert_gemm2", s, launch_expert_gemm2(h, a.w2, pre, ttab, a.y, a.E, a.C, a.d, a.d_ff, s));
     return SWITCH_OK;
 }
 

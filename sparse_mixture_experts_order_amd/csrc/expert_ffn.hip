@@ -1,8 +1,9 @@
 // Grouped expert GEMM on bf16 MFMA (v_mfma_f32_32x32x16_bf16), used twice:
 //   H[e, s, :] = bf16(ReLU(buf[e, s, :] W1_e^T))     (N = d_ff, K = d)
 //   Y[e, s, :] = H[e, s, :] W2_e^T                   (N = d,    K = d_ff), fp32
-// for rows s < accepted[e]; the row counts are read on the device, so the
-// grid covers every possible tile and tiles past accepted[e] return at once.
+// for rows s < accepted[e].  The row counts stay on the device: a one-block
+// kernel turns them into a prefix over experts of valid token tiles, and the
+// GEMMs walk that list without any host synchronisation.
 //
 // Sources: "Switch Transformers ..." essay (dmxsf.com), "core structure":
 // experts replace the FFN sublayer; "Mixture of experts" (world.lapla.si),
@@ -11,99 +12,160 @@
 // Design for one MI355X.  At Switch-Base shapes an expert sees ~120 rows, so
 // the layer is bound by streaming every expert's weights from HBM once, not
 // by MFMA.  The kernel is organised around that stream:
-//   - a workgroup (4 waves) owns TOK = 32*TOKB rows of one expert and
-//     NWG = 4*32*NBW weight rows; each wave owns 32*NBW weight rows and
-//     computes them against all TOK rows (weights = MFMA A operand, tokens =
-//     MFMA B operand, so a lane's results are 4 consecutive outputs of one row);
-//   - weights never touch LDS: each lane loads 64 contiguous bytes of its
-//     weight row per 64-wide K chunk straight into registers, one chunk ahead
-//     of the MFMAs.  The K order inside a chunk is permuted identically for
-//     both operands (a reduction is order free), so the 32 lanes of a half
-//     wave read whole 64-byte runs;
-//   - the token tile is shared by the 4 waves through LDS, double buffered,
-//     rows padded to 144 bytes so the MFMA-layout reads are conflict free;
-//   - tile ids are dealt XCD-major so the tiles of one expert share an L2.
+//   - persistent workgroups (as many as fit on the chip) walk the tile list;
+//     a tile is (token block of TOK rows of one expert, weight-row block of
+//     NWG rows), ordered so the weight blocks of one token block are
+//     neighbours, and dealt XCD-major so neighbours share an L2;
+//   - each wave owns 32*NBW weight rows of the tile and computes them
+//     against all TOK token rows.  Weights never touch LDS: each lane loads
+//     64 contiguous bytes of its weight row per 64-wide K chunk straight into
+//     registers.  The K order inside a chunk is permuted identically for both
+//     operands (a reduction is order free), so a half wave reads whole
+//     64-byte runs;
+//   - weights and token tiles flow through rings of R register chunks, R-1
+//     of them in flight, and the ring runs across tile boundaries: the next
+//     tile's loads are in flight while a tile's results are written out, so
+//     the HBM stream never drains between tiles;
+//   - the token tile is shared by the waves through LDS, double buffered,
+//     rows padded to 144 bytes so the MFMA-layout reads are conflict free.
+//     Token loads are issued before weight loads of the same step: vector
+//     memory counters complete in issue order, so waiting for a token chunk
+//     never waits for a weight chunk still ahead of the MFMAs.
 #include "common.hpp"
 #include "kernels.hpp"
 
-#include <type_traits>
-
 namespace swmoe {
 
-constexpr int FFN_LDS_STRIDE = 72;  // bf16 elements per LDS row (64 + 8 pad)
+constexpr int FFN_LDS_STRIDE = 72;  // bf16 elements per token row in LDS (64 + 8 pad)
+
+// Token-tile list: pre[e] = number of valid TOK-row token tiles of experts < e
+// (pre[E] = total V), and ttab[v] = {expert, first row, valid rows, 0} for
+// v = pre[e] + tt, the token tiles of each expert in row order.
+__global__ __launch_bounds__(1024) void ffn_tile_prefix(const int32_t* __restrict__ accepted, int E, int C, int TOK,
+                                                        int32_t* __restrict__ pre, int4* __restrict__ ttab) {
+    __shared__ int wsum[16];
+    const int per = (E + 1023) / 1024;
+    const int e0 = threadIdx.x * per;
+    int local = 0;
+    for (int i = 0; i < per; ++i) {
+        const int e = e0 + i;
+        if (e < E) local += (min(max(accepted[e], 0), C) + TOK - 1) / TOK;
+    }
+    // exclusive scan of `local` over the block: waves, then wave totals in order
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int incl = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off);
+        if (lane >= off) incl += v;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int base = 0;
+    for (int w = 0; w < wave; ++w) base += wsum[w];
+    int run = base + incl - local;
+    for (int i = 0; i < per; ++i) {
+        const int e = e0 + i;
+        if (e < E) {
+            pre[e] = run;
+            const int a = min(max(accepted[e], 0), C);
+            for (int tt = 0; tt * TOK < a; ++tt) ttab[run + tt] = make_int4(e, tt * TOK, min(TOK, a - tt * TOK), 0);
+            run += (a + TOK - 1) / TOK;
+        }
+    }
+    if (threadIdx.x == 1023) pre[E] = base + incl;
+}
+
+struct FfnTile {
+    int e, nt, tok_base, nv;
+};
+
+// Tile i = v * n_tiles + nt: token tile v of the list, weight block nt.  The
+// tiles of one token tile are neighbours (they share the token rows in L2).
+// The table read is uniform, so it goes through the scalar cache and uses no
+// vector registers.
+__device__ __forceinline__ FfnTile decode_tile(int i, const int4* __restrict__ ttab, int n_tiles) {
+    const int v = i / n_tiles;
+    const int4 m = ttab[v];
+    FfnTile t;
+    t.e = __builtin_amdgcn_readfirstlane(m.x);
+    t.tok_base = __builtin_amdgcn_readfirstlane(m.y);
+    t.nv = __builtin_amdgcn_readfirstlane(m.z);
+    t.nt = i - v * n_tiles;
+    return t;
+}
 
 // TOKB: 32-row token blocks per tile; NBW: 32-row weight blocks per wave;
-// WAVES: waves per workgroup; R: depth of the register rings (R-1 chunks of
-// 64 K-elements in flight ahead of the MFMAs).
+// WAVES: waves per workgroup; R: depth of the register rings.  GEMM1 writes
+// bf16(ReLU(.)), GEMM2 writes fp32.
 template <int TOKB, int NBW, int WAVES, int R, bool GEMM1>
 __global__ __launch_bounds__(64 * WAVES) void expert_gemm(const bf16_t* __restrict__ A,   // [E, C, K]
                                                           const bf16_t* __restrict__ W,   // [E, N, K]
-                                                          const int32_t* __restrict__ accepted,
+                                                          const int32_t* __restrict__ pre,
+                                                          const int4* __restrict__ ttab,
                                                           void* __restrict__ out,         // [E, C, N]
-                                                          int C, int K, int N, int n_tiles, int tok_tiles,
-                                                          int ntiles, int grid_padded) {
+                                                          int E, int C, int K, int N, int n_tiles) {
     constexpr int TOK = 32 * TOKB;
     constexpr int NWG = WAVES * 32 * NBW;
     constexpr int NTHR = 64 * WAVES;
     constexpr int PIECES = TOK * 8;                       // 16-byte pieces of one token chunk
     constexpr int APT = (PIECES + NTHR - 1) / NTHR;       // pieces per thread
-    // output staging after the K loop reuses the same LDS: TOK rows of NWG
-    // values (bf16 for GEMM1, fp32 for GEMM2), rows padded by 16 bytes
     constexpr int OUT_BYTES = GEMM1 ? 2 : 4;
-    constexpr int OSTRIDE = NWG * OUT_BYTES + 16;                     // bytes per staged row
+    constexpr int ROW_BYTES = NWG * OUT_BYTES;                        // output bytes per token row
+    constexpr int PASS_BYTES = ROW_BYTES < 512 ? ROW_BYTES : 512;     // staged per pass
+    constexpr int NPASS = ROW_BYTES / PASS_BYTES;
+    constexpr int CPP = PASS_BYTES / OUT_BYTES;                       // columns per pass
+    constexpr int OSTRIDE = PASS_BYTES + 16;                          // bytes per staged row
     constexpr int A_BYTES = 2 * TOK * FFN_LDS_STRIDE * 2;
-    constexpr int LDS_BYTES = A_BYTES > TOK * OSTRIDE ? A_BYTES : TOK * OSTRIDE;
-    __shared__ __attribute__((aligned(16))) char lds_raw[LDS_BYTES];
-    bf16_t (*lds)[TOK * FFN_LDS_STRIDE] = reinterpret_cast<bf16_t (*)[TOK * FFN_LDS_STRIDE]>(lds_raw);
+    constexpr int O_BYTES = TOK * OSTRIDE;
+    __shared__ __attribute__((aligned(16))) char lds_raw[A_BYTES + O_BYTES];
+    bf16_t* const lds_a = reinterpret_cast<bf16_t*>(lds_raw);
+    char* const lds_o = lds_raw + A_BYTES;
 
-    const int tile = xcd_swizzle(blockIdx.x, grid_padded);
-    if (tile >= ntiles) return;
-    const int tt = tile % tok_tiles;
-    const int rest = tile / tok_tiles;
-    const int nt = rest % n_tiles;
-    const int e = rest / n_tiles;
-    const int tok_base = tt * TOK;
-    const int acc_e = min(max(accepted[e], 0), C);  // rows in use, never past the capacity
-    if (tok_base >= acc_e) return;
-    const int nv = min(TOK, acc_e - tok_base);  // valid rows in this tile
+    const int total = pre[E] * n_tiles;
+    const int G = gridDim.x;                                          // a multiple of 8
+    const int slot = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3); // XCD-major
+    if (slot >= total) return;
+    const int ntl = (total - slot + G - 1) / G;                       // tiles of this workgroup
+    const int nk = K >> 6;
+    const int P = ntl * nk;                                           // chunk positions
 
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int half = lane >> 5, l32 = lane & 31;
-    const int wrow0 = nt * NWG + wave * 32 * NBW;
-    const bool wave_active = wrow0 < N;
 
-    // Weight rows: lane l reads row wrow0 + 32*nb + l%32, 64 contiguous bytes
-    // per chunk (its half of the 128-byte chunk).  Waves past the last row
-    // read row 0 and store nothing.
-    const bf16_t* wptr[NBW];
+    // Frontier tile (the one whose chunks are being loaded).  Load addresses
+    // are a uniform 64-bit base (scalar registers) plus a 32-bit per-lane
+    // offset, so the loop computes no per-lane 64-bit addresses.
+    int f_tile = -1;
+    const char* wbase = nullptr;   // uniform: this wave's first weight row of the frontier tile
+    const char* abase = nullptr;   // uniform: the frontier tile's first token row
+    uint32_t woff[NBW];            // per lane: weight row nb*32 + l32, half-chunk `half`
+    uint32_t aoffg[APT];           // per lane: token row and 16-byte column of piece j
 #pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) {
-        const int r = wave_active ? wrow0 + nb * 32 + l32 : 0;
-        wptr[nb] = W + ((size_t)e * N + r) * K + half * 32;
-    }
-
-    // Token-tile staging: piece q = tid + j*NTHR -> (row q/8, 16-byte column q%8).
-    // Pieces past the tile repeat the last piece and rows past the valid count
-    // re-load the last valid row, so every load is unconditional.
-    const bf16_t* Ae = A + ((size_t)e * C + tok_base) * K;
-    const bf16_t* aptr[APT];
+    for (int nb = 0; nb < NBW; ++nb) woff[nb] = ((uint32_t)(nb * 32 + l32) * K + half * 32) * 2;
+    auto set_frontier = [&](int j) {
+        f_tile = j;
+        const FfnTile t = decode_tile(j * G + slot, ttab, n_tiles);
+        int wr0 = t.nt * NWG + wave * 32 * NBW;
+        if (wr0 >= N) wr0 = 0;     // waves past the last weight row read rows 0.. and store nothing
+        wbase = (const char*)W + ((size_t)t.e * N + wr0) * K * 2;
+        abase = (const char*)A + ((size_t)t.e * C + t.tok_base) * K * 2;
+#pragma unroll
+        for (int j2 = 0; j2 < APT; ++j2) {
+            const int q = min((int)threadIdx.x + j2 * NTHR, PIECES - 1);
+            aoffg[j2] = ((uint32_t)min(q >> 3, t.nv - 1) * K + (q & 7) * 8) * 2;
+        }
+    };
     int aoff[APT];
 #pragma unroll
-    for (int j = 0; j < APT; ++j) {
-        const int q = min((int)threadIdx.x + j * NTHR, PIECES - 1);
-        const int row = q >> 3, c16 = (q & 7) * 8;
-        aptr[j] = Ae + (size_t)min(row, nv - 1) * K + c16;
-        aoff[j] = row * FFN_LDS_STRIDE + c16;
+    for (int j2 = 0; j2 < APT; ++j2) {
+        const int q = min((int)threadIdx.x + j2 * NTHR, PIECES - 1);
+        aoff[j2] = (q >> 3) * FFN_LDS_STRIDE + (q & 7) * 8;
     }
 
-    // Register rings.  At step k a wave issues the token chunk k+R-1 first
-    // and then the weight chunk k+R-1: vector-memory counters complete in
-    // issue order, so waiting for the token chunk k+1 never waits for a
-    // weight chunk that is still ahead of the MFMAs.
     u32x4 areg[R][APT];
     u32x4 wreg[R][NBW][4];
-
     f32x16 acc[NBW][TOKB];
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb)
@@ -112,36 +174,35 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm(const bf16_t* __restri
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[nb][tb][i] = 0.f;
 
-    const int nk = K >> 6;
+    // loads of position f (clamped to the last position) into one ring slot
+    auto load_pos = [&](int f, u32x4 (&ar)[APT], u32x4 (&wr)[NBW][4]) {
+        f = min(f, P - 1);
+        const int jf = f / nk, kf = f - jf * nk;
+        if (jf != f_tile) set_frontier(jf);
+        const char* ak = abase + kf * 128;
+        const char* wk = wbase + kf * 128;
 #pragma unroll
-    for (int p = 0; p < R - 1; ++p) {
-        const int kc = min(p, nk - 1);
-#pragma unroll
-        for (int j = 0; j < APT; ++j) areg[p][j] = *(const u32x4*)(aptr[j] + kc * 64);
+        for (int j2 = 0; j2 < APT; ++j2) ar[j2] = *(const u32x4*)(ak + aoffg[j2]);
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) wreg[p][nb][j] = *(const u32x4*)(wptr[nb] + kc * 64 + j * 8);
-    }
-#pragma unroll
-    for (int j = 0; j < APT; ++j) *(u32x4*)(&lds[0][aoff[j]]) = areg[0][j];
+            for (int j2 = 0; j2 < 4; ++j2) wr[nb][j2] = *(const u32x4*)(wk + woff[nb] + j2 * 16);
+    };
 
-    for (int k0 = 0; k0 < nk; k0 += R) {
+#pragma unroll
+    for (int p = 0; p < R - 1; ++p) load_pos(p, areg[p], wreg[p]);
+#pragma unroll
+    for (int j2 = 0; j2 < APT; ++j2) *(u32x4*)(lds_a + aoff[j2]) = areg[0][j2];
+
+    for (int p0 = 0; p0 < P; p0 += R) {
 #pragma unroll
         for (int u = 0; u < R; ++u) {
-            const int k = k0 + u;
-            if (k < nk) {
-                const int kn = min(k + R - 1, nk - 1);   // chunk entering the rings (clamped)
-                const int slot_n = (u + R - 1) % R;      // a constant once the u loop is unrolled
-#pragma unroll
-                for (int j = 0; j < APT; ++j) areg[slot_n][j] = *(const u32x4*)(aptr[j] + kn * 64);
-#pragma unroll
-                for (int nb = 0; nb < NBW; ++nb)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        wreg[slot_n][nb][j] = *(const u32x4*)(wptr[nb] + kn * 64 + j * 8);
+            const int p = p0 + u;
+            if (p < P) {
+                const int slot_n = (u + R - 1) % R;   // constant once the u loop is unrolled
+                load_pos(p + R - 1, areg[slot_n], wreg[slot_n]);
                 __syncthreads();
-                const bf16_t* lb = &lds[k & 1][0];
+                const bf16_t* lb = lds_a + (p & 1) * (TOK * FFN_LDS_STRIDE);
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     bf16x8 bt[TOKB];
@@ -156,86 +217,137 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm(const bf16_t* __restri
                             acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, bt[tb], acc[nb][tb], 0, 0, 0);
                     }
                 }
-                // token chunk k+1 (ring slot u+1) into the other LDS buffer
+                // token chunk of position p+1 into the other LDS buffer
                 const int slot_a = (u + 1) % R;
-                bf16_t* sb = &lds[(k + 1) & 1][0];
+                bf16_t* sb = lds_a + ((p + 1) & 1) * (TOK * FFN_LDS_STRIDE);
 #pragma unroll
-                for (int j = 0; j < APT; ++j) *(u32x4*)(sb + aoff[j]) = areg[slot_a][j];
-            }
-        }
-    }
+                for (int j2 = 0; j2 < APT; ++j2) *(u32x4*)(sb + aoff[j2]) = areg[slot_a][j2];
 
-    // Epilogue: each wave parks its tile in LDS (lane: token column l32 of
-    // block tb, weight rows 8*(i/4) + 4*half + i%4, so 4 consecutive outputs
-    // per store), then the workgroup writes whole rows of NWG outputs per
-    // token with 16-byte stores, so every token row gets NWG*OUT_BYTES
-    // contiguous bytes instead of scattered 8/16-byte pieces.
-    __syncthreads();   // all waves are done reading the token tile
+                const int j = p / nk;
+                if (p - j * nk == nk - 1) {
+                    // ------------------------------------------------ tile epilogue
+                    const FfnTile t = decode_tile(j * G + slot, ttab, n_tiles);
+                    // Output rows go out through LDS in passes of CPP columns:
+                    // the waves owning a pass park their results (lane: token
+                    // column l32 of block tb, weight rows 8*(i/4) + 4*half + i%4),
+                    // then the workgroup writes whole row segments with
+                    // 16-byte stores.
+                    const int ncols = min(NWG, N - t.nt * NWG);
 #pragma unroll
-    for (int tb = 0; tb < TOKB; ++tb) {
-        const int r = tb * 32 + l32;
+                    for (int pass = 0; pass < NPASS; ++pass) {
+                        if (pass > 0) __syncthreads();
+                        const int c0 = wave * 32 * NBW - pass * CPP;
+                        if (c0 >= 0 && c0 < CPP) {
 #pragma unroll
-        for (int nb = 0; nb < NBW; ++nb)
+                            for (int tb = 0; tb < TOKB; ++tb)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int c = wave * 32 * NBW + nb * 32 + q * 8 + half * 4;   // column within the tile
-                const f32x16& a = acc[nb][tb];
-                char* dst = lds_raw + r * OSTRIDE + c * OUT_BYTES;
-                if constexpr (GEMM1) {
-                    const uint32_t b0 = bf16_rne(fmaxf(a[4 * q + 0], 0.f)), b1 = bf16_rne(fmaxf(a[4 * q + 1], 0.f));
-                    const uint32_t b2 = bf16_rne(fmaxf(a[4 * q + 2], 0.f)), b3 = bf16_rne(fmaxf(a[4 * q + 3], 0.f));
-                    *(uint2*)dst = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
-                } else {
-                    *(f32x4*)dst = f32x4{a[4 * q + 0], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+                                for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+                                    for (int q = 0; q < 4; ++q) {
+                                        const int c = c0 + nb * 32 + q * 8 + half * 4;
+                                        const f32x16& a = acc[nb][tb];
+                                        char* dst = lds_o + (tb * 32 + l32) * OSTRIDE + c * OUT_BYTES;
+                                        if constexpr (GEMM1) {
+                                            const uint32_t b0 = bf16_rne(fmaxf(a[4 * q + 0], 0.f));
+                                            const uint32_t b1 = bf16_rne(fmaxf(a[4 * q + 1], 0.f));
+                                            const uint32_t b2 = bf16_rne(fmaxf(a[4 * q + 2], 0.f));
+                                            const uint32_t b3 = bf16_rne(fmaxf(a[4 * q + 3], 0.f));
+                                            *(uint2*)dst = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+                                        } else {
+                                            *(f32x4*)dst = f32x4{a[4 * q + 0], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+                                        }
+                                    }
+                        }
+                        __syncthreads();
+                        constexpr int VPR = PASS_BYTES / 16;           // 16-byte vectors per staged row
+                        const int vpr_valid = max(0, min(CPP, ncols - pass * CPP)) * OUT_BYTES / 16;
+                        char* gout = (char*)out + (((size_t)t.e * C + t.tok_base) * N + (size_t)t.nt * NWG + pass * CPP) * OUT_BYTES;
+                        static_assert((TOK * VPR) % NTHR == 0, "whole store passes");
+#pragma unroll
+                        for (int it = 0; it < TOK * VPR / NTHR; ++it) {
+                            const int i = threadIdx.x + it * NTHR;
+                            const int r = i / VPR, v = i - r * VPR;
+                            if (r < t.nv && v < vpr_valid)
+                                *(u32x4*)(gout + (size_t)r * N * OUT_BYTES + v * 16) = *(const u32x4*)(lds_o + r * OSTRIDE + v * 16);
+                        }
+                    }
+#pragma unroll
+                    for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+                        for (int tb = 0; tb < TOKB; ++tb)
+#pragma unroll
+                            for (int i = 0; i < 16; ++i) acc[nb][tb][i] = 0.f;
                 }
             }
-    }
-    __syncthreads();
-    constexpr int VPR = NWG * OUT_BYTES / 16;        // 16-byte vectors per staged row
-    const int ncols = min(NWG, N - nt * NWG);        // valid columns (a multiple of 32)
-    const int vpr_valid = ncols * OUT_BYTES / 16;
-    char* gout = (char*)out + (((size_t)e * C + tok_base) * N + (size_t)nt * NWG) * OUT_BYTES;
-    for (int i = threadIdx.x; i < TOK * VPR; i += NTHR) {
-        const int r = i / VPR, v = i - r * VPR;
-        if (r < nv && v < vpr_valid)
-            *(u32x4*)(gout + (size_t)r * N * OUT_BYTES + v * 16) = *(const u32x4*)(lds_raw + r * OSTRIDE + v * 16);
+        }
     }
 }
 
 // ------------------------------------------------------------------ launchers
+static int device_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cus[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
 template <int TOKB, int NBW, int WAVES, int R, bool GEMM1>
-hipError_t launch_expert_gemm_t(const bf16_t* A, const bf16_t* W, const int32_t* accepted, void* out, int E, int C,
-                                int K, int N, hipStream_t s) {
-    constexpr int TOK = 32 * TOKB, NWG = WAVES * 32 * NBW;
+hipError_t launch_expert_gemm_t(const bf16_t* A, const bf16_t* W, const int32_t* pre, const int4* ttab, void* out,
+                                int E, int C, int K, int N, hipStream_t s) {
+    constexpr int NWG = WAVES * 32 * NBW;
     const int n_tiles = (N + NWG - 1) / NWG;
-    const int tok_tiles = (C + TOK - 1) / TOK;
-    const int64_t ntiles = (int64_t)E * n_tiles * tok_tiles;
-    if (ntiles == 0) return hipSuccess;
-    const int64_t grid = (ntiles + 7) / 8 * 8;
+    static int per_cu = 0;   // resident workgroups per CU for this kernel
+    if (!per_cu) {
+        int b = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, expert_gemm<TOKB, NBW, WAVES, R, GEMM1>, 64 * WAVES, 0) !=
+                hipSuccess || b <= 0)
+            b = 1;
+        per_cu = b;
+    }
+    const int tok_tiles = (C + 32 * TOKB - 1) / (32 * TOKB);
+    const int64_t max_tiles = (int64_t)E * n_tiles * tok_tiles;
+    int64_t grid = std::min<int64_t>((int64_t)device_cus() * per_cu, (max_tiles + 7) / 8 * 8);
+    grid = std::max<int64_t>(8, grid / 8 * 8);
     hipLaunchKernelGGL((expert_gemm<TOKB, NBW, WAVES, R, GEMM1>), dim3((unsigned)grid), dim3(64 * WAVES), 0, s, A, W,
-                       accepted, out, C, K, N, n_tiles, tok_tiles, (int)ntiles, (int)grid);
+                       pre, ttab, out, E, C, K, N, n_tiles);
+    return hipGetLastError();
+}
+
+int ffn_token_tile(int C) { return C > 64 ? 128 : (C > 32 ? 64 : 32); }
+
+size_t ffn_tile_table_entries(int E, int C) {
+    const int tok = ffn_token_tile(C);
+    return (size_t)E * ((C + tok - 1) / tok);
+}
+
+hipError_t launch_ffn_tile_prefix(const int32_t* accepted, int E, int C, int32_t* pre, int4* ttab, hipStream_t s) {
+    hipLaunchKernelGGL(ffn_tile_prefix, dim3(1), dim3(1024), 0, s, accepted, E, C, ffn_token_tile(C), pre, ttab);
     return hipGetLastError();
 }
 
 #ifndef SWMOE_FFN_CUSTOM_DISPATCH
 template <bool GEMM1>
-static hipError_t launch_expert_gemm(const bf16_t* A, const bf16_t* W, const int32_t* accepted, void* out, int E,
-                                     int C, int K, int N, hipStream_t s) {
-    // rows per tile: enough 32-row blocks for the capacity, at most 8
-    if (C > 128) return launch_expert_gemm_t<8, 1, 4, 3, GEMM1>(A, W, accepted, out, E, C, K, N, s);
-    if (C > 64) return launch_expert_gemm_t<4, 1, 8, 5, GEMM1>(A, W, accepted, out, E, C, K, N, s);
-    if (C > 32) return launch_expert_gemm_t<2, 2, 4, 3, GEMM1>(A, W, accepted, out, E, C, K, N, s);
-    return launch_expert_gemm_t<1, 2, 4, 3, GEMM1>(A, W, accepted, out, E, C, K, N, s);
+static hipError_t launch_expert_gemm(const bf16_t* A, const bf16_t* W, const int32_t* pre, const int4* ttab, void* out,
+                                     int E, int C, int K, int N, hipStream_t s) {
+    // the token tile must be ffn_token_tile(C) rows: the prefix kernel lists tiles of that size
+    if (C > 64) return launch_expert_gemm_t<4, 1, 8, 4, GEMM1>(A, W, pre, ttab, out, E, C, K, N, s);
+    if (C > 32) return launch_expert_gemm_t<2, 2, 4, 3, GEMM1>(A, W, pre, ttab, out, E, C, K, N, s);
+    return launch_expert_gemm_t<1, 2, 4, 4, GEMM1>(A, W, pre, ttab, out, E, C, K, N, s);
 }
 
-hipError_t launch_expert_gemm1(const bf16_t* buf, const bf16_t* w1, const int32_t* accepted, bf16_t* h, int E,
-                               int C, int d, int d_ff, hipStream_t s) {
-    return launch_expert_gemm<true>(buf, w1, accepted, h, E, C, d, d_ff, s);
+hipError_t launch_expert_gemm1(const bf16_t* buf, const bf16_t* w1, const int32_t* pre, const int4* ttab, bf16_t* h,
+                               int E, int C, int d, int d_ff, hipStream_t s) {
+    return launch_expert_gemm<true>(buf, w1, pre, ttab, h, E, C, d, d_ff, s);
 }
 
-hipError_t launch_expert_gemm2(const bf16_t* h, const bf16_t* w2, const int32_t* accepted, float* y, int E, int C,
-                               int d, int d_ff, hipStream_t s) {
-    return launch_expert_gemm<false>(h, w2, accepted, y, E, C, d_ff, d, s);
+hipError_t launch_expert_gemm2(const bf16_t* h, const bf16_t* w2, const int32_t* pre, const int4* ttab, float* y,
+                               int E, int C, int d, int d_ff, hipStream_t s) {
+    return launch_expert_gemm<false>(h, w2, pre, ttab, y, E, C, d_ff, d, s);
 }
 #endif
 

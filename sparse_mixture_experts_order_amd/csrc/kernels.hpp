@@ -29,10 +29,13 @@ hipError_t launch_gather(const bf16_t* x, const int32_t* expert, const int32_t* 
                          bf16_t* buf, hipStream_t s);
 
 // expert_ffn.hip
-hipError_t launch_expert_gemm1(const bf16_t* buf, const bf16_t* w1, const int32_t* accepted, bf16_t* h, int E,
-                               int C, int d, int d_ff, hipStream_t s);
-hipError_t launch_expert_gemm2(const bf16_t* h, const bf16_t* w2, const int32_t* accepted, float* y, int E, int C,
-                               int d, int d_ff, hipStream_t s);
+int ffn_token_tile(int C);
+size_t ffn_tile_table_entries(int E, int C);
+hipError_t launch_ffn_tile_prefix(const int32_t* accepted, int E, int C, int32_t* pre, int4* ttab, hipStream_t s);
+hipError_t launch_expert_gemm1(const bf16_t* buf, const bf16_t* w1, const int32_t* pre, const int4* ttab, bf16_t* h,
+                               int E, int C, int d, int d_ff, hipStream_t s);
+hipError_t launch_expert_gemm2(const bf16_t* h, const bf16_t* w2, const int32_t* pre, const int4* ttab, float* y,
+                               int E, int C, int d, int d_ff, hipStream_t s);
 
 // combine.hip
 hipError_t launch_combine(const float* y, const int32_t* expert, const int32_t* position, const uint8_t* keep,
