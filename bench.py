@@ -26,7 +26,7 @@ sys.path.insert(0, ROOT)
 METRIC = "Switch FFN layer fwd tokens/s (E=128,d=768) + % bf16 MFMA peak + dispatch GB/s"
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_switch_base.txt")
+PROFILES = os.path.join(ROOT, "profiles")
 
 
 def parse():
@@ -68,20 +68,23 @@ def kernel_source_sha() -> str:
     return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
 
 
-def read_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` from the committed counter summary, or
-    None when the summary is missing or was taken on a different kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+def read_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` (FETCH_SIZE + WRITE_SIZE, each scaled by
+    the same counter's reading on a plain copy of known size) from the committed
+    counter summary, or None when the summary is missing or was taken on a
+    different expert-kernel source."""
+    path = os.path.join(PROFILES, f"traffic_{workload}.txt")
+    if not os.path.exists(path):
         return None
     vals = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
     if vals.get("source_sha256_16") != kernel_source_sha():
         return None
-    v = vals.get(f"{kernel}_hbm_bytes_per_launch")
-    return float(v) if v else None
+    f, w = vals.get(f"{kernel}_fetch_bytes_per_launch"), vals.get(f"{kernel}_write_bytes_per_launch")
+    return float(f) + float(w) if f and w else None
 
 
 def cpu_baseline(inp, cfg, sample_tokens):
@@ -182,7 +185,7 @@ def main():
     ffn_flops = 4 * A * d * F
     ffn_bytes = alg["expert_gemm1"]["bytes"] + alg["expert_gemm2"]["bytes"]
     dispatch_us = sum(kern_us.get(k, 0) for k in ("scan_local", "scan_offsets", "gather"))
-    traffic = read_traffic(dominant)
+    traffic = read_traffic(dominant, cfg.name)
 
     result = {
         "metric": METRIC,
