@@ -187,6 +187,22 @@ switch_status switch_aux_loss(const int32_t *counts, const float *prob_sum, cons
                               float *P, float *loss, float *dlogits, void *ws, size_t ws_bytes,
                               void *stream);
 
+/* Router z-loss (a NEXT row beyond the forward layer).  Source: "MoE routing
+ * load collapse" (zffjzz.top), "core idea and formulas": the ST-MoE z-loss
+ * L_z = (1/T) sum_t (log sum_i exp z_ti)^2 penalises the log normaliser of the
+ * scores; "minimal experiment": a +100 shift of all scores changes it while
+ * the probabilities and choices stay the same.
+ *
+ *   lse      [T]    fp32  log-sum-exp per token (switch_route)
+ *   logits   [T, E] fp32  needed only when dlogits != NULL
+ *   beta            coefficient, applied to both outputs (z_loss = beta L_z)
+ *   z_loss   [1]    fp32  beta (1/T) sum_t lse_t^2, reduced in fp64 in a fixed order
+ *   dlogits  [T, E] fp32  or NULL: beta (2/T) lse_t p_tj, written (accumulate = 0)
+ *                         or added to the array's contents (accumulate = 1)
+ * For T == 0: z_loss = 0. */
+switch_status switch_router_z_loss(const float *lse, const float *logits, int64_t T, int32_t E, float beta,
+                                   float *z_loss, float *dlogits, int32_t accumulate, void *stream);
+
 /* The whole layer on one stream: route, dispatch, experts, combine, aux loss.
  * Sources: wq-win note sec. 3 (the layer as a step list).  Required pointers
  * are marked (R); optional outputs may be NULL, in which case intermediates
@@ -212,14 +228,17 @@ typedef struct switch_layer_args {
     float *logits;               /*     [T, E] */
     float *lse;                  /*     [T] */
     float *prob_sum;             /*     [E] */
-    float *dlogits;              /*     [T, E]; NULL = gradient not computed */
+    float *dlogits;              /*     [T, E]; NULL = gradient not computed.  With z_loss
+                                  *     set it is the gradient of aux loss + z-loss */
     int32_t *slot_token;         /*     [E, C] */
     switch_bf16 *buf;            /*     [E, C, d] */
     float *y;                    /*     [E, C, d] */
+    float *z_loss;               /*     [1]: beta-weighted router z-loss; NULL = not computed */
     /* sizes */
     int64_t T;
     int32_t d, d_ff, E, C;
     float alpha;
+    float z_beta;                /* z-loss coefficient (used when z_loss != NULL) */
     int32_t residual;            /* 1: out = x + branch; 0: out = branch only */
 } switch_layer_args;
 

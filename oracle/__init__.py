@@ -6,5 +6,5 @@ cpu_baseline leg may import it; the library never does.
 from .switch_oracle import (  # noqa: F401
     Aux, LayerResult, Routing, Slots, aux_loss, capacity, combine, dispatch,
     expert_ffn, expert_rows, layer_dense_onehot, layer_forward, layer_per_token,
-    router_logits, slot_scan, softmax_top1,
+    router_logits, router_z_loss, slot_scan, softmax_top1, ZLoss,
 )

@@ -239,6 +239,8 @@ def aux_loss(counts: np.ndarray, p: np.ndarray, alpha: float) -> Aux:
     """
     p = np.asarray(p, np.float64)
     T, E = p.shape
+    if T == 0:   # empty batch: no load, no probability mass, no loss
+        return Aux(np.zeros(E), np.zeros(E), 0.0, np.zeros((0, E)))
     f = np.asarray(counts, np.float64) / T
     P = p.sum(axis=0) / T
     loss = float(alpha * E * np.dot(f, P))
@@ -351,3 +353,29 @@ def layer_per_token(x, z, w1, w2, C: int):
             h = np.maximum(w1e @ x[t], 0.0)
             branch[t] = g * (w2e @ h)
     return np.array(experts), np.array(positions), branch
+
+
+# ------------------------------------------------ NEXT f-1: router z-loss
+class ZLoss(NamedTuple):
+    loss: float          # beta * (1/T) sum_t lse_t^2
+    dlogits: np.ndarray  # [T, E] d loss / d z = beta * (2/T) lse_t p_tj
+
+
+def router_z_loss(z: np.ndarray, beta: float) -> ZLoss:
+    """L_z = beta * (1/T) sum_t (log sum_i exp(z_ti))^2 and its gradient.
+
+    [ZF] "core idea and formulas": the router z-loss of ST-MoE penalises the
+    log normaliser of every token's scores (it is not a balance measure);
+    "minimal experiment": adding 100 to every score changes it while p and
+    the choice do not.  beta is the coefficient the caller puts on it, kept
+    inside like alpha (ZF trains with 0.001).  d lse_t / d z_tj = p_tj.
+    For T = 0 the loss is 0.
+    """
+    z = np.asarray(z, np.float64)
+    T = z.shape[0]
+    if T == 0:
+        return ZLoss(0.0, np.zeros_like(z))
+    r = softmax_top1(z)
+    loss = float(beta * np.mean(r.lse ** 2))
+    dlogits = beta * (2.0 / T) * r.lse[:, None] * r.p
+    return ZLoss(loss, dlogits)

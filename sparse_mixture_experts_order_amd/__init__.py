@@ -25,7 +25,7 @@ EXPORTS = [
     "switch_expert_ffn_workspace_bytes", "switch_aux_loss_workspace_bytes", "switch_workspace_bytes",
     "switch_status_string", "switch_last_error", "switch_route", "switch_dispatch", "switch_expert_ffn",
     "switch_combine", "switch_aux_loss", "switch_layer_fwd", "switch_stream_copy", "switch_profile_enable",
-    "switch_profile_collect", "switch_kernel_name",
+    "switch_profile_collect", "switch_kernel_name", "switch_router_z_loss",
 ]
 
 
@@ -39,9 +39,9 @@ class LayerArgs(ctypes.Structure):
     """Mirror of switch_layer_args."""
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "x", "w_r", "b_r", "w1", "w2", "out", "expert", "gate", "position", "keep", "counts", "accepted",
-        "f", "P", "loss", "logits", "lse", "prob_sum", "dlogits", "slot_token", "buf", "y")] + [
+        "f", "P", "loss", "logits", "lse", "prob_sum", "dlogits", "slot_token", "buf", "y", "z_loss")] + [
         ("T", ctypes.c_int64), ("d", ctypes.c_int32), ("d_ff", ctypes.c_int32), ("E", ctypes.c_int32),
-        ("C", ctypes.c_int32), ("alpha", ctypes.c_float), ("residual", ctypes.c_int32)]
+        ("C", ctypes.c_int32), ("alpha", ctypes.c_float), ("z_beta", ctypes.c_float), ("residual", ctypes.c_int32)]
 
 
 def lib():
@@ -72,6 +72,7 @@ def lib():
             "switch_profile_enable": (None, [I32]),
             "switch_profile_collect": (I32, [I32, P, P]),
             "switch_kernel_name": (ctypes.c_char_p, [I32]),
+            "switch_router_z_loss": (I32, [P, P, I64, I32, F32, P, P, I32, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -170,6 +171,11 @@ def switch_aux_loss(counts, prob_sum, logits, lse, T, E, alpha, f, P, loss, dlog
                                  _ptr(P), _ptr(loss), _ptr(dlogits), wp, wn, _stream(stream)), "switch_aux_loss")
 
 
+def switch_router_z_loss(lse, logits, T, E, beta, z_loss, dlogits=None, accumulate=False, stream=None):
+    _check(lib().switch_router_z_loss(_ptr(lse), _ptr(logits), T, E, beta, _ptr(z_loss), _ptr(dlogits),
+                                      1 if accumulate else 0, _stream(stream)), "switch_router_z_loss")
+
+
 def switch_layer_fwd(args: LayerArgs, ws, stream=None):
     wp, wn = _ws(ws)
     _check(lib().switch_layer_fwd(ctypes.byref(args), wp, wn, _stream(stream)), "switch_layer_fwd")
@@ -194,7 +200,7 @@ def switch_profile_collect(max_records: int = 1 << 16):
 
 
 # ------------------------------------------------------------ allocation helpers
-def layer_tensors(T, d, d_ff, E, C, device="cuda", logits=False, dlogits=False, inspect=False):
+def layer_tensors(T, d, d_ff, E, C, device="cuda", logits=False, dlogits=False, inspect=False, z_loss=False):
     """Output tensors of switch_layer_fwd (plus a workspace), allocated with torch."""
     import torch
     dev = torch.device(device)
@@ -216,6 +222,8 @@ def layer_tensors(T, d, d_ff, E, C, device="cuda", logits=False, dlogits=False, 
         o["logits"] = torch.empty((T, E), dtype=torch.float32, device=dev)
     if dlogits:
         o["dlogits"] = torch.empty((T, E), dtype=torch.float32, device=dev)
+    if z_loss:
+        o["z_loss"] = torch.empty(1, dtype=torch.float32, device=dev)
     if inspect:
         o["slot_token"] = torch.empty((E, C), dtype=torch.int32, device=dev)
         o["buf"] = torch.empty((E, C, d), dtype=torch.bfloat16, device=dev)
@@ -224,12 +232,13 @@ def layer_tensors(T, d, d_ff, E, C, device="cuda", logits=False, dlogits=False, 
     return o
 
 
-def make_layer_args(x, w_r, b_r, w1, w2, t: dict, T, d, d_ff, E, C, alpha, residual=True) -> LayerArgs:
+def make_layer_args(x, w_r, b_r, w1, w2, t: dict, T, d, d_ff, E, C, alpha, residual=True, z_beta=0.0) -> LayerArgs:
     a = LayerArgs()
     for name, v in (("x", x), ("w_r", w_r), ("b_r", b_r), ("w1", w1), ("w2", w2)):
         setattr(a, name, _ptr(v))
     for name in ("out", "expert", "gate", "position", "keep", "counts", "accepted", "f", "P", "loss", "logits",
-                 "lse", "prob_sum", "dlogits", "slot_token", "buf", "y"):
+                 "lse", "prob_sum", "dlogits", "slot_token", "buf", "y", "z_loss"):
         setattr(a, name, _ptr(t.get(name)))
     a.T, a.d, a.d_ff, a.E, a.C, a.alpha, a.residual = T, d, d_ff, E, C, alpha, 1 if residual else 0
+    a.z_beta = z_beta
     return a

@@ -34,11 +34,11 @@ switch_status hip_fail(hipError_t e, const char* where) {
 // ----------------------------------------------------------- launch timing
 enum KernelId {
     K_SPLIT = 0, K_RGEMM, K_RSOFTMAX, K_RREDUCE, K_SCAN_LOCAL, K_SCAN_OFFSETS, K_GATHER,
-    K_GEMM1, K_GEMM2, K_COMBINE, K_AUX_STATS, K_AUX_GRAD, K_COPY, K_FFN_TILES, K_COUNT
+    K_GEMM1, K_GEMM2, K_COMBINE, K_AUX_STATS, K_AUX_GRAD, K_COPY, K_FFN_TILES, K_Z_LOSS, K_COUNT
 };
 const char* kKernelNames[K_COUNT] = {
     "split_router_weights", "router_gemm", "router_softmax", "router_reduce", "scan_local", "scan_offsets",
-    "gather", "expert_gemm1", "expert_gemm2", "combine", "aux_stats", "aux_grad", "stream_copy", "ffn_tile_prefix"};
+    "gather", "expert_gemm1", "expert_gemm2", "combine", "aux_stats", "aux_grad", "stream_copy", "ffn_tile_prefix", "z_loss"};
 
 struct ProfRec { int id; hipEvent_t a, b; };
 bool g_prof = false;
@@ -272,6 +272,7 @@ switch_status run_combine(const CombineArgs& a, hipStream_t s) {
 struct AuxArgs {
     const int32_t* counts; const float* prob_sum; const float* logits; const float* lse;
     int64_t T; int32_t E; float alpha; float* f; float* P; float* loss; float* dlogits;
+    float beta; float* z_loss;   // router z-loss (optional, z_loss == NULL: not computed)
 };
 
 switch_status validate_aux(const AuxArgs& a) {
@@ -279,6 +280,9 @@ switch_status validate_aux(const AuxArgs& a) {
     REQUIRE(std::isfinite(a.alpha), "alpha must be finite");
     NONNULL(a.counts); NONNULL(a.prob_sum); NONNULL(a.f); NONNULL(a.P); NONNULL(a.loss);
     if (a.dlogits && a.T > 0) { NONNULL(a.logits); NONNULL(a.lse); }
+    if (a.z_loss && a.T > 0) NONNULL(a.lse);
+    REQUIRE(std::isfinite(a.beta), "beta must be finite");
+    ALIGNED4(a.z_loss);
     ALIGNED4(a.counts); ALIGNED4(a.prob_sum); ALIGNED4(a.logits); ALIGNED4(a.lse); ALIGNED4(a.f); ALIGNED4(a.P);
     ALIGNED4(a.loss); ALIGNED4(a.dlogits);
     return SWITCH_OK;
@@ -287,8 +291,10 @@ switch_status validate_aux(const AuxArgs& a) {
 switch_status run_aux(const AuxArgs& a, hipStream_t s) {
     LAUNCH(K_AUX_STATS, "aux_stats", s,
            launch_aux_stats(a.counts, a.prob_sum, a.T, a.E, a.alpha, a.f, a.P, a.loss, s));
+    if (a.z_loss) LAUNCH(K_Z_LOSS, "z_loss", s, launch_z_loss(a.lse, a.T, a.beta, a.z_loss, s));
     if (a.dlogits && a.T > 0)
-        LAUNCH(K_AUX_GRAD, "aux_grad", s, launch_aux_grad(a.logits, a.lse, a.f, a.T, a.E, a.alpha, a.dlogits, s));
+        LAUNCH(K_AUX_GRAD, "aux_grad", s,
+               launch_aux_grad(a.logits, a.lse, a.f, a.T, a.E, a.alpha, a.z_loss ? a.beta : 0.f, 0, a.dlogits, s));
     return SWITCH_OK;
 }
 
@@ -428,9 +434,26 @@ switch_status switch_aux_loss(const int32_t* counts, const float* prob_sum, cons
                               void* ws, size_t ws_bytes, void* stream) {
     (void)ws; (void)ws_bytes;
     g_err.clear();
-    AuxArgs a{counts, prob_sum, logits, lse, T, E, alpha, f, P, loss, dlogits};
+    AuxArgs a{counts, prob_sum, logits, lse, T, E, alpha, f, P, loss, dlogits, 0.f, nullptr};
     CHECK(validate_aux(a));
     return run_aux(a, (hipStream_t)stream);
+}
+
+switch_status switch_router_z_loss(const float* lse, const float* logits, int64_t T, int32_t E, float beta,
+                                   float* z_loss, float* dlogits, int32_t accumulate, void* stream) {
+    g_err.clear();
+    CHECK(check_TE(T, E));
+    REQUIRE(std::isfinite(beta), "beta must be finite");
+    NONNULL(z_loss);
+    NONNULL_IF(T > 0, lse);
+    if (dlogits && T > 0) NONNULL(logits);
+    REQUIRE(accumulate == 0 || accumulate == 1, "accumulate must be 0 or 1");
+    ALIGNED4(lse); ALIGNED4(logits); ALIGNED4(z_loss); ALIGNED4(dlogits);
+    hipStream_t s = (hipStream_t)stream;
+    LAUNCH(K_Z_LOSS, "z_loss", s, launch_z_loss(lse, T, beta, z_loss, s));
+    if (dlogits && T > 0)
+        LAUNCH(K_AUX_GRAD, "aux_grad", s, launch_aux_grad(logits, lse, nullptr, T, E, 0.f, beta, accumulate, dlogits, s));
+    return SWITCH_OK;
 }
 
 switch_status switch_layer_fwd(const switch_layer_args* la, void* ws, size_t ws_bytes, void* stream) {
@@ -466,7 +489,7 @@ switch_status switch_layer_fwd(const switch_layer_args* la, void* ws, size_t ws_
     DispatchArgs da{L.x, L.expert, L.T, L.d, L.E, L.C, L.position, L.keep, L.counts, L.accepted, L.slot_token, buf};
     FfnArgs fa{buf, L.accepted, L.w1, L.w2, L.E, L.C, L.d, L.d_ff, y};
     CombineArgs ca{y, L.expert, L.position, L.keep, L.gate, L.residual ? L.x : nullptr, L.T, L.d, L.E, L.C, L.out};
-    AuxArgs xa{L.counts, prob_sum, logits, lse, L.T, L.E, L.alpha, L.f, L.P, L.loss, L.dlogits};
+    AuxArgs xa{L.counts, prob_sum, logits, lse, L.T, L.E, L.alpha, L.f, L.P, L.loss, L.dlogits, L.z_beta, L.z_loss};
     // validate everything before the first launch
     CHECK(validate_route(ra, route_space, route_ws(L.T, L.d, L.E, false)));
     CHECK(validate_dispatch(da, dispatch_space, dispatch_ws(L.T, L.E)));

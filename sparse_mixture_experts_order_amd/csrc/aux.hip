@@ -34,11 +34,36 @@ __global__ __launch_bounds__(1024) void aux_stats(const int32_t* __restrict__ co
     if (threadIdx.x == 0) loss[0] = (float)((double)alpha * (double)E * red[0]);
 }
 
-// One wave per token row; lane j holds experts j, j+64, ...
+// Router z-loss (ST-MoE, as restated in "MoE routing load collapse",
+// zffjzz.top, "core idea and formulas"): L_z = beta (1/T) sum_t lse_t^2.
+// One workgroup, fp64, fixed tree order.
+__global__ __launch_bounds__(1024) void z_loss_reduce(const float* __restrict__ lse, int64_t T, float beta,
+                                                      float* __restrict__ z_loss) {
+    __shared__ double red[1024];
+    double acc = 0.0;
+    for (int64_t t = threadIdx.x; t < T; t += 1024) {
+        const double l = (double)lse[t];
+        acc += l * l;
+    }
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    for (int s = 512; s > 0; s >>= 1) {
+        if ((int)threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) z_loss[0] = T > 0 ? (float)((double)beta * red[0] / (double)T) : 0.f;
+}
+
+// Gradient with respect to the logits of  c_aux-weighted aux loss and
+// c_z-weighted z-loss, with p_tj = exp(z_tj - lse_t):
+//   G_tj = p_tj * (c_aux (f_j - sum_e f_e p_te) + c_z lse_t)
+// c_aux = alpha E / T (aux, f held constant), c_z = 2 beta / T (z-loss).
+// One wave per token row; lane j holds experts j, j+64, ...  With
+// `accumulate` the result is added to dlogits instead of stored.
 template <int NCH>
 __global__ __launch_bounds__(256) void aux_grad(const float* __restrict__ logits, const float* __restrict__ lse,
-                                                const float* __restrict__ f, int64_t T, int E, float scale,
-                                                float* __restrict__ dlogits) {
+                                                const float* __restrict__ f, int64_t T, int E, float c_aux,
+                                                float c_z, int accumulate, float* __restrict__ dlogits) {
     const int lane = threadIdx.x & 63;
     const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
@@ -50,15 +75,19 @@ __global__ __launch_bounds__(256) void aux_grad(const float* __restrict__ logits
     for (int i = 0; i < NCH; ++i) {
         const int e = lane + 64 * i;
         p[i] = e < E ? expf(row[e] - l) : 0.f;
-        fr[i] = e < E ? f[e] : 0.f;
+        fr[i] = (e < E && f) ? f[e] : 0.f;
         s = fmaf(fr[i], p[i], s);
     }
     s = wave_sum(s);
+    const float zt = c_z * l;
     float* g = dlogits + t * E;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
         const int e = lane + 64 * i;
-        if (e < E) g[e] = scale * p[i] * (fr[i] - s);
+        if (e < E) {
+            const float v = p[i] * (c_aux * (fr[i] - s) + zt);
+            g[e] = accumulate ? g[e] + v : v;
+        }
     }
 }
 
@@ -68,13 +97,21 @@ hipError_t launch_aux_stats(const int32_t* counts, const float* prob_sum, int64_
     return hipGetLastError();
 }
 
+hipError_t launch_z_loss(const float* lse, int64_t T, float beta, float* z_loss, hipStream_t s) {
+    hipLaunchKernelGGL(z_loss_reduce, dim3(1), dim3(1024), 0, s, lse, T, beta, z_loss);
+    return hipGetLastError();
+}
+
 hipError_t launch_aux_grad(const float* logits, const float* lse, const float* f, int64_t T, int E, float alpha,
-                           float* dlogits, hipStream_t s) {
+                           float beta, int accumulate, float* dlogits, hipStream_t s) {
     if (T == 0) return hipSuccess;
-    const float scale = (float)((double)alpha * (double)E / (double)T);
+    const float c_aux = f ? (float)((double)alpha * (double)E / (double)T) : 0.f;
+    const float c_z = (float)(2.0 * (double)beta / (double)T);
     const unsigned grid = (unsigned)((T + 3) / 4);
     const int nch = (E + 63) / 64;
-#define SWMOE_GRAD(N) hipLaunchKernelGGL(aux_grad<N>, dim3(grid), dim3(256), 0, s, logits, lse, f, T, E, scale, dlogits)
+#define SWMOE_GRAD(N)                                                                                          \
+    hipLaunchKernelGGL(aux_grad<N>, dim3(grid), dim3(256), 0, s, logits, lse, f, T, E, c_aux, c_z, accumulate, \
+                       dlogits)
     if (nch <= 1) SWMOE_GRAD(1);
     else if (nch <= 2) SWMOE_GRAD(2);
     else if (nch <= 4) SWMOE_GRAD(4);

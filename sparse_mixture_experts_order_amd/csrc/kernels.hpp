@@ -45,8 +45,9 @@ hipError_t launch_combine(const float* y, const int32_t* expert, const int32_t* 
 // aux.hip
 hipError_t launch_aux_stats(const int32_t* counts, const float* prob_sum, int64_t T, int E, float alpha, float* f,
                             float* P, float* loss, hipStream_t s);
+hipError_t launch_z_loss(const float* lse, int64_t T, float beta, float* z_loss, hipStream_t s);
 hipError_t launch_aux_grad(const float* logits, const float* lse, const float* f, int64_t T, int E, float alpha,
-                           float* dlogits, hipStream_t s);
+                           float beta, int accumulate, float* dlogits, hipStream_t s);
 
 // api.hip
 hipError_t launch_stream_copy(void* dst, const void* src, size_t nbytes, hipStream_t s);

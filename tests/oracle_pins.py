@@ -295,3 +295,37 @@ ALL_PINS = [
     pin_invariants, pin_finite_differences,
     lambda so: pin_independent_forms(so, T=40, d=8, F=12, E=3, c=1.0, seed=13, bias0=0.5),
 ]
+
+
+# ------------------------------------------------ NEXT f-1: router z-loss
+def pin_z_loss(so):
+    """zffjzz 'core idea and formulas' / 'minimal experiment': L_z = mean lse^2;
+    +100 on every score moves lse by exactly 100 (L_z changes, p does not);
+    uniform rows give (log E)^2; gradient by central finite differences;
+    rows of the gradient sum to beta * 2 lse_t / T."""
+    sh = GOLDEN["z_loss_shift"]["shift"]
+    rng = _rng(21)
+    z = rng.standard_normal((33, 7))
+    beta = 0.37
+    a, b = so.router_z_loss(z, beta), so.router_z_loss(z + sh, beta)
+    lse = scipy.special.logsumexp(z, axis=1)
+    assert abs(a.loss - beta * np.mean(lse ** 2)) <= 1e-13 * a.loss
+    assert abs(b.loss - beta * np.mean((lse + sh) ** 2)) <= 1e-12 * b.loss
+    assert b.loss > a.loss
+    np.testing.assert_allclose(so.softmax_top1(z + sh).p, so.softmax_top1(z).p, rtol=1e-12, atol=1e-15)
+    u = so.router_z_loss(np.zeros((10, 8)), 1.0)
+    assert abs(u.loss - math.log(8) ** 2) < 1e-14
+    np.testing.assert_allclose(a.dlogits.sum(axis=1), beta * 2 * lse / z.shape[0], rtol=1e-12)
+    h = 1e-6
+    num = np.zeros_like(z)
+    for t in range(0, 33, 4):
+        for j in range(7):
+            zp, zm = z.copy(), z.copy()
+            zp[t, j] += h
+            zm[t, j] -= h
+            num[t, j] = (so.router_z_loss(zp, beta).loss - so.router_z_loss(zm, beta).loss) / (2 * h)
+    np.testing.assert_allclose(a.dlogits[::4], num[::4], rtol=0, atol=1e-9)
+    assert so.router_z_loss(np.zeros((0, 3)), 1.0).loss == 0.0
+
+
+ALL_PINS.append(pin_z_loss)

@@ -411,3 +411,68 @@ def test_extreme_logits_are_stable():
     assert torch.isfinite(t["gate"]).all() and torch.isfinite(t["lse"]).all()
     np.testing.assert_allclose(t["lse"].cpu().numpy(), r.lse, rtol=1e-6)
     np.testing.assert_allclose(t["prob_sum"].cpu().numpy(), r.p.sum(axis=0), rtol=AUX_REL, atol=1e-5)
+
+
+# ------------------------------------------------------------ NEXT f-1: router z-loss
+def test_router_z_loss(D):
+    """z-loss and its gradient against the oracle, alone and accumulated onto the aux gradient."""
+    cfg = D.cfg
+    say(f"z-loss cfg{cfg.index}")
+    z32 = D.z.astype(np.float32)
+    t = run_route(None, None, None, f32_dev(z32), cfg.T, cfg.d, cfg.E)
+    beta = 1e-3
+    ref = so.router_z_loss(z32, beta)
+    zl = torch.empty(1, dtype=torch.float32, device="cuda")
+    want_g = cfg.T * cfg.E <= (1 << 25)
+    G = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device="cuda") if want_g else None
+    sw.switch_router_z_loss(t["lse"], f32_dev(z32), cfg.T, cfg.E, beta, zl, G)
+    assert abs(zl.item() - ref.loss) <= AUX_REL * abs(ref.loss), (zl.item(), ref.loss)
+    if want_g:
+        g = G.cpu().numpy()
+        assert rel_fro(g, ref.dlogits) <= GRAD_REL
+        assert np.abs(g - ref.dlogits).max() <= GRAD_REL * np.abs(ref.dlogits).max()
+        # accumulate onto the aux gradient: the sum of both gradients
+        r = so.softmax_top1(z32)
+        aux = so.aux_loss(np.bincount(r.expert, minlength=cfg.E), r.p, cfg.alpha)
+        f = torch.empty(cfg.E, dtype=torch.float32, device="cuda")
+        P, loss = torch.empty_like(f), torch.empty(1, dtype=torch.float32, device="cuda")
+        sw.switch_aux_loss(i32_dev(np.bincount(r.expert, minlength=cfg.E)), t["prob_sum"], f32_dev(z32), t["lse"],
+                           cfg.T, cfg.E, cfg.alpha, f, P, loss, G)
+        sw.switch_router_z_loss(t["lse"], f32_dev(z32), cfg.T, cfg.E, beta, zl, G, accumulate=True)
+        both = aux.dlogits + ref.dlogits
+        g = G.cpu().numpy()
+        assert rel_fro(g, both) <= GRAD_REL
+        assert np.abs(g - both).max() <= GRAD_REL * np.abs(both).max()
+
+
+def test_z_loss_shift_and_layer():
+    """+100 on every logit moves L_z as the oracle says while ids and gates stay;
+    the layer's fused gradient equals aux + z-loss gradients."""
+    T, E = 2048, 16
+    rng = np.random.default_rng(17)
+    z = (rng.standard_normal((T, E)) * 0.5).astype(np.float32)
+    zl = torch.empty(2, dtype=torch.float32, device="cuda")
+    for i, zz in enumerate((z, z + np.float32(100))):
+        t = run_route(None, None, None, f32_dev(zz), T, 64, E)
+        sw.switch_router_z_loss(t["lse"], None, T, E, 0.5, zl[i:i + 1])
+        ref = so.router_z_loss(zz, 0.5).loss
+        assert abs(zl[i].item() - ref) <= AUX_REL * ref
+    assert zl[1].item() > zl[0].item()
+    # fused in the layer
+    cfg = workloads.CONFIGS[1]
+    Dv = DeviceInputs(cfg)
+    tt = sw.layer_tensors(cfg.T, cfg.d, cfg.d_ff, cfg.E, Dv.C, dlogits=True, z_loss=True)
+    args = sw.make_layer_args(Dv.x, Dv.w_r, Dv.b_r, Dv.w1, Dv.w2, tt, cfg.T, cfg.d, cfg.d_ff, cfg.E, Dv.C, cfg.alpha,
+                              z_beta=1e-3)
+    sw.switch_layer_fwd(args, tt["ws"])
+    torch.cuda.synchronize()
+    z64 = Dv.z
+    r = so.softmax_top1(z64)
+    assert np.array_equal(tt["expert"].cpu().numpy(), r.expert)
+    aux = so.aux_loss(np.bincount(r.expert, minlength=cfg.E), r.p, cfg.alpha)
+    zr = so.router_z_loss(z64, 1e-3)
+    assert abs(tt["z_loss"].item() - zr.loss) <= AUX_REL * zr.loss
+    both = aux.dlogits + zr.dlogits
+    g = tt["dlogits"].cpu().numpy()
+    assert rel_fro(g, both) <= GRAD_REL
+    assert np.abs(g - both).max() <= GRAD_REL * np.abs(both).max()

@@ -153,3 +153,29 @@ def test_fresh_oracle_passes_all_pins():
     m = fresh_oracle()
     for pin in pins.ALL_PINS:
         pin(m)
+
+
+def m_zloss_no_square(m):
+    orig = m.router_z_loss
+    def f(z, beta):
+        r = orig(z, beta)
+        lse = m.softmax_top1(z).lse if np.asarray(z).shape[0] else np.zeros(0)
+        return r._replace(loss=float(beta * np.mean(np.abs(lse))) if lse.size else 0.0)
+    m.router_z_loss = f
+
+
+def m_zloss_grad_no_lse(m):
+    orig = m.router_z_loss
+    def f(z, beta):
+        r = orig(z, beta)
+        T = np.asarray(z).shape[0]
+        return r._replace(dlogits=beta * (2.0 / max(T, 1)) * m.softmax_top1(z).p if T else r.dlogits)
+    m.router_z_loss = f
+
+
+@pytest.mark.parametrize("mutate", [m_zloss_no_square, m_zloss_grad_no_lse], ids=lambda f: f.__name__)
+def test_z_loss_pin_catches_mutant(mutate):
+    m = fresh_oracle()
+    mutate(m)
+    with pytest.raises(Exception):
+        pins.pin_z_loss(m)
