@@ -34,11 +34,11 @@ switch_status hip_fail(hipError_t e, const char* where) {
 // ----------------------------------------------------------- launch timing
 enum KernelId {
     K_SPLIT = 0, K_RGEMM, K_RSOFTMAX, K_RREDUCE, K_SCAN_LOCAL, K_SCAN_OFFSETS, K_GATHER,
-    K_GEMM1, K_GEMM2, K_COMBINE, K_AUX_STATS, K_AUX_GRAD, K_COPY, K_FFN_TILES, K_Z_LOSS, K_COUNT
+    K_GEMM1, K_GEMM2, K_COMBINE, K_AUX_STATS, K_AUX_GRAD, K_COPY, K_FFN_TILES, K_Z_LOSS, K_RFUSED, K_COUNT
 };
 const char* kKernelNames[K_COUNT] = {
     "split_router_weights", "router_gemm", "router_softmax", "router_reduce", "scan_local", "scan_offsets",
-    "gather", "expert_gemm1", "expert_gemm2", "combine", "aux_stats", "aux_grad", "stream_copy", "ffn_tile_prefix", "z_loss"};
+    "gather", "expert_gemm1", "expert_gemm2", "combine", "aux_stats", "aux_grad", "stream_copy", "ffn_tile_prefix", "z_loss", "router_fused"};
 
 struct ProfRec { int id; hipEvent_t a, b; };
 bool g_prof = false;
@@ -85,9 +85,15 @@ struct Carver {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-size_t route_ws(int64_t T, int32_t d, int32_t E, bool need_logits) {
-    size_t n = up((size_t)3 * d * E * sizeof(bf16_t)) + up((size_t)router_softmax_blocks(T, E) * E * sizeof(float));
-    if (need_logits) n += up((size_t)T * E * sizeof(float));
+// GEMM mode with E <= kRouterFusedMaxE runs the fused router (no logits
+// round trip); wider routers write the logits and run the softmax pass.
+bool route_fused(int32_t E) { return E <= kRouterFusedMaxE; }
+size_t route_parts(int64_t T, int32_t E) {
+    return (size_t)std::max(router_softmax_blocks(T, E), router_fused_blocks(T)) * E;
+}
+size_t route_ws(int64_t T, int32_t d, int32_t E, bool logits_out_given) {
+    size_t n = up((size_t)3 * d * E * sizeof(bf16_t)) + up(route_parts(T, E) * sizeof(float));
+    if (!logits_out_given && !route_fused(E)) n += up((size_t)T * E * sizeof(float));
     return n;
 }
 size_t dispatch_ws(int64_t T, int32_t E) { return up((size_t)scan_tiles(T) * E * sizeof(int32_t)); }
@@ -144,7 +150,7 @@ switch_status validate_route(const RouteArgs& a, const void* ws, size_t ws_bytes
         SUPPORT(a.d % 32 == 0, "d must be a multiple of 32 for the router GEMM (got %d)", a.d);
     }
     REQUIRE(a.logits_in != nullptr || !tok || a.x != nullptr, "x must not be NULL");
-    const size_t need = a.logits_in ? route_ws(a.T, 0, a.E, false) : route_ws(a.T, a.d, a.E, a.logits_out == nullptr);
+    const size_t need = a.logits_in ? route_ws(a.T, 0, a.E, true) : route_ws(a.T, a.d, a.E, a.logits_out != nullptr);
     if (ws_bytes < need) return fail(SWITCH_E_WORKSPACE, "route needs %zu workspace bytes, got %zu", need, ws_bytes);
     REQUIRE(need == 0 || ws != nullptr, "ws must not be NULL");
     REQUIRE(aligned(ws, kAlign), "ws must be %zu-byte aligned", kAlign);
@@ -157,13 +163,22 @@ switch_status run_route(const RouteArgs& a, void* ws, hipStream_t s) {
     const float* logits = a.logits_in;
     if (!logits) {
         bf16_t* wr3 = c.take<bf16_t>((size_t)3 * a.d * E);
-        float* z = a.logits_out ? a.logits_out : c.take<float>((size_t)T * E);
         LAUNCH(K_SPLIT, "split_router_weights", s, launch_split_router_weights(a.w_r, wr3, a.d, E, s));
+        if (route_fused(E)) {
+            float* part = c.take<float>(route_parts(T, E));
+            const int nblk = T > 0 ? router_fused_blocks(T) : 0;
+            if (T > 0)
+                LAUNCH(K_RFUSED, "router_fused", s,
+                       launch_router_fused(a.x, wr3, a.b_r, T, a.d, E, a.logits_out, a.expert, a.gate, a.lse, part, s));
+            LAUNCH(K_RREDUCE, "router_reduce", s, launch_router_reduce(part, nblk, E, a.prob_sum, s));
+            return SWITCH_OK;
+        }
+        float* z = a.logits_out ? a.logits_out : c.take<float>((size_t)T * E);
         if (T > 0) LAUNCH(K_RGEMM, "router_gemm", s, launch_router_gemm(a.x, wr3, a.b_r, z, T, a.d, E, s));
         logits = z;
     }
     const int nblk = router_softmax_blocks(T, E);
-    float* part = c.take<float>((size_t)nblk * E);
+    float* part = c.take<float>(route_parts(T, E));
     if (T > 0)
         LAUNCH(K_RSOFTMAX, "router_softmax", s, launch_router_softmax(logits, T, E, a.expert, a.gate, a.lse, part, s));
     LAUNCH(K_RREDUCE, "router_reduce", s, launch_router_reduce(part, nblk, E, a.prob_sum, s));
@@ -353,7 +368,7 @@ switch_status switch_capacity(int64_t T, int32_t E, double c, int32_t* C_out) {
 
 size_t switch_route_workspace_bytes(int64_t T, int32_t d, int32_t E) {
     if (T < 0 || d < 0 || E < 1 || E > 4096 || T >= (int64_t(1) << 31)) return 0;
-    return route_ws(T, d, E, true);
+    return route_ws(T, d, E, false);
 }
 size_t switch_dispatch_workspace_bytes(int64_t T, int32_t E) {
     if (T < 0 || E < 1 || E > 4096 || T >= (int64_t(1) << 31)) return 0;
@@ -366,7 +381,7 @@ size_t switch_expert_ffn_workspace_bytes(int32_t E, int32_t C, int32_t d_ff) {
 size_t switch_aux_loss_workspace_bytes(int64_t, int32_t) { return 0; }
 
 static size_t layer_ws(int64_t T, int32_t d, int32_t d_ff, int32_t E, int32_t C) {
-    size_t n = route_ws(T, d, E, false) + dispatch_ws(T, E) + ffn_ws(E, C, d_ff);
+    size_t n = route_ws(T, d, E, true) + dispatch_ws(T, E) + ffn_ws(E, C, d_ff);
     n += up((size_t)T * E * sizeof(float));          // logits
     n += up((size_t)T * sizeof(float));              // lse
     n += up((size_t)E * sizeof(float));              // prob_sum
@@ -471,7 +486,7 @@ switch_status switch_layer_fwd(const switch_layer_args* la, void* ws, size_t ws_
     REQUIRE(ws != nullptr, "ws must not be NULL");
     REQUIRE(aligned(ws, kAlign), "ws must be %zu-byte aligned", kAlign);
     Carver c{(char*)ws};
-    char* route_space = c.take<char>(route_ws(L.T, L.d, L.E, false));
+    char* route_space = c.take<char>(route_ws(L.T, L.d, L.E, true));
     char* dispatch_space = c.take<char>(dispatch_ws(L.T, L.E));
     char* ffn_space = c.take<char>(ffn_ws(L.E, L.C, L.d_ff));
     float* logits = c.take<float>((size_t)L.T * L.E);
@@ -480,6 +495,7 @@ switch_status switch_layer_fwd(const switch_layer_args* la, void* ws, size_t ws_
     bf16_t* buf = c.take<bf16_t>((size_t)L.E * L.C * L.d);
     float* y = c.take<float>((size_t)L.E * L.C * L.d);
     if (L.logits) logits = L.logits;
+    else if (!L.dlogits && route_fused(L.E)) logits = nullptr;   // the fused router needs no logits array
     if (L.lse) lse = L.lse;
     if (L.prob_sum) prob_sum = L.prob_sum;
     if (L.buf) buf = L.buf;
@@ -491,7 +507,7 @@ switch_status switch_layer_fwd(const switch_layer_args* la, void* ws, size_t ws_
     CombineArgs ca{y, L.expert, L.position, L.keep, L.gate, L.residual ? L.x : nullptr, L.T, L.d, L.E, L.C, L.out};
     AuxArgs xa{L.counts, prob_sum, logits, lse, L.T, L.E, L.alpha, L.f, L.P, L.loss, L.dlogits, L.z_beta, L.z_loss};
     // validate everything before the first launch
-    CHECK(validate_route(ra, route_space, route_ws(L.T, L.d, L.E, false)));
+    CHECK(validate_route(ra, route_space, route_ws(L.T, L.d, L.E, logits != nullptr)));
     CHECK(validate_dispatch(da, dispatch_space, dispatch_ws(L.T, L.E)));
     CHECK(validate_ffn(fa, ffn_space, ffn_ws(L.E, L.C, L.d_ff)));
     CHECK(validate_combine(ca));

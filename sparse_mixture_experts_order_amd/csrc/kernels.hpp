@@ -17,6 +17,11 @@ int router_softmax_blocks(int64_t T, int E);
 hipError_t launch_router_softmax(const float* logits, int T, int E, int32_t* expert, float* gate, float* lse,
                                  float* part, hipStream_t s);
 hipError_t launch_router_reduce(const float* part, int nblk, int E, float* prob_sum, hipStream_t s);
+constexpr int kRouterFusedMaxE = 256;
+int router_fused_blocks(int64_t T);
+hipError_t launch_router_fused(const bf16_t* x, const bf16_t* wr3, const float* b_r, int T, int d, int E,
+                               float* logits_out, int32_t* expert, float* gate, float* lse, float* part,
+                               hipStream_t s);
 
 // dispatch.hip
 int scan_tiles(int64_t T);

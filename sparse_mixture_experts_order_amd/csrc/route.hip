@@ -251,4 +251,209 @@ hipError_t launch_router_reduce(const float* part, int nblk, int E, float* prob_
     return hipGetLastError();
 }
 
+
+// ---------------------------------------------------------------------------
+// Fused router for E <= 256: logits, softmax statistics and top-1 in one pass.
+// A workgroup owns RF_TOK tokens and all experts; wave w owns 16*RF_TB of the
+// tokens (RF_TB 16-token MFMA blocks) against every expert, so a token's whole
+// logit row lives in one wave.  The three bf16 terms of W_r stream through LDS
+// (shared by the 4 waves) in 32-wide K stages; the token fragments stream
+// straight into registers.  Both go through register rings R stages deep.
+// Epilogue per token: bias, row max with the lowest index on ties, sum of
+// exp, lse, gate = 1/sum, optional logits store, and the workgroup's partial
+// sums of p_te over its tokens (shuffles over the 16 tokens of a block, the
+// two blocks in turn, then the waves in turn through LDS: a fixed order).
+constexpr int RF_TB = 1;                 // 16-token MFMA blocks per wave
+constexpr int RF_TOK = 4 * 16 * RF_TB;   // tokens per workgroup
+constexpr int RF_ROW = 40;     // bf16 per staged W row: 32 + 8 pad (80 bytes)
+
+int router_fused_blocks(int64_t T) { return (int)((T + RF_TOK - 1) / RF_TOK); }
+
+template <int EB, int R>
+__global__ __launch_bounds__(256) void router_fused(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wr3,
+                                                    const float* __restrict__ b_r, int T, int d, int E,
+                                                    float* __restrict__ logits_out, int32_t* __restrict__ expert,
+                                                    float* __restrict__ gate, float* __restrict__ lse,
+                                                    float* __restrict__ part) {
+    constexpr int EP = EB * 16;                 // experts padded to whole 16-row blocks
+    constexpr int PIECES = 3 * EP * 4;          // 16-byte pieces of one stage (3 terms x EP rows x 64 B)
+    constexpr int PPT = (PIECES + 255) / 256;
+    __shared__ __attribute__((aligned(16))) bf16_t wl[2][3 * EP * RF_ROW];
+    __shared__ float red[EP];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r16 = lane & 15, kq = (lane >> 4) * 8;
+    const int tbase = blockIdx.x * RF_TOK + wave * 16 * RF_TB;
+    const size_t plane = (size_t)E * d;
+
+    // token fragments: block tb, token tbase + 16 tb + r16 (clamped), k offset kq
+    uint32_t xoff[RF_TB];
+#pragma unroll
+    for (int tb = 0; tb < RF_TB; ++tb) xoff[tb] = ((uint32_t)min(tbase + tb * 16 + r16, T - 1) * d + kq) * 2;
+    // W pieces: q -> (row = q/4 in [3][EP], 16-byte column q%4); rows past E repeat row E-1
+    uint32_t woff[PPT];
+    int wlds[PPT];
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+        const int q = min((int)threadIdx.x + j * 256, PIECES - 1);
+        const int row = q >> 2, c = q & 3;
+        const int term = row / EP, e = min(row - term * EP, E - 1);
+        woff[j] = (uint32_t)(((size_t)term * plane + (size_t)e * d + c * 8) * 2);
+        wlds[j] = row * RF_ROW + c * 8;
+    }
+    const char* xb8 = (const char*)x;
+    const char* wb8 = (const char*)wr3;
+
+    u32x4 wreg[R][PPT];
+    u32x4 xreg[R][RF_TB];
+    f32x4 acc[RF_TB][EB];
+#pragma unroll
+    for (int tb = 0; tb < RF_TB; ++tb)
+#pragma unroll
+        for (int eb = 0; eb < EB; ++eb) acc[tb][eb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nk = d >> 5;
+    auto load_stage = [&](int k, u32x4 (&wr)[PPT], u32x4 (&xr)[RF_TB]) {
+        k = min(k, nk - 1);
+        const char* wk = wb8 + k * 64;
+        const char* xk = xb8 + k * 64;
+#pragma unroll
+        for (int j = 0; j < PPT; ++j) wr[j] = *(const u32x4*)(wk + woff[j]);
+#pragma unroll
+        for (int tb = 0; tb < RF_TB; ++tb) xr[tb] = *(const u32x4*)(xk + xoff[tb]);
+    };
+#pragma unroll
+    for (int p = 0; p < R - 1; ++p) load_stage(p, wreg[p], xreg[p]);
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) *(u32x4*)(&wl[0][wlds[j]]) = wreg[0][j];
+
+    for (int k0 = 0; k0 < nk; k0 += R) {
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+            const int k = k0 + u;
+            if (k < nk) {
+                const int slot_n = (u + R - 1) % R;
+                load_stage(k + R - 1, wreg[slot_n], xreg[slot_n]);
+                __syncthreads();
+                const bf16_t* lb = &wl[k & 1][0];
+                bf16x8 xb[RF_TB];
+#pragma unroll
+                for (int tb = 0; tb < RF_TB; ++tb) xb[tb] = as_bf16x8(xreg[u][tb]);
+                // small terms first: lo (plane 2), mid (1), hi (0)
+#pragma unroll
+                for (int jj = 0; jj < 3; ++jj) {
+                    const int term = 2 - jj;
+#pragma unroll
+                    for (int eb = 0; eb < EB; ++eb) {
+                        const bf16x8 a = as_bf16x8(*(const u32x4*)(lb + (term * EP + eb * 16 + r16) * RF_ROW + kq));
+#pragma unroll
+                        for (int tb = 0; tb < RF_TB; ++tb)
+                            acc[tb][eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xb[tb], acc[tb][eb], 0, 0, 0);
+                    }
+                }
+                const int slot_a = (u + 1) % R;
+                bf16_t* sb = &wl[(k + 1) & 1][0];
+#pragma unroll
+                for (int j = 0; j < PPT; ++j) *(u32x4*)(sb + wlds[j]) = wreg[slot_a][j];
+            }
+        }
+    }
+
+    // ------------------------------------------------------------ epilogue
+    // lane holds token r16 of block tb and experts 16 eb + 4 (lane >> 4) + i
+    float psum[EB][4];
+#pragma unroll
+    for (int eb = 0; eb < EB; ++eb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) psum[eb][i] = 0.f;
+#pragma unroll
+    for (int tb = 0; tb < RF_TB; ++tb) {
+        const int t = tbase + tb * 16 + r16;
+        float v[EB][4];
+        float m = -INFINITY;
+        int mi = 0x7fffffff;
+#pragma unroll
+        for (int eb = 0; eb < EB; ++eb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int e = eb * 16 + (lane >> 4) * 4 + i;
+                v[eb][i] = e < E ? acc[tb][eb][i] + (b_r ? b_r[e] : 0.f) : -INFINITY;
+                if (v[eb][i] > m) { m = v[eb][i]; mi = e; }
+            }
+        // the 4 lane groups (lane >> 4) hold the other experts of the same token
+#pragma unroll
+        for (int off = 16; off <= 32; off <<= 1) {
+            const float om = __shfl_xor(m, off);
+            const int oi = __shfl_xor(mi, off);
+            if (om > m || (om == m && oi < mi)) { m = om; mi = oi; }
+        }
+        float ssum = 0.f;
+#pragma unroll
+        for (int eb = 0; eb < EB; ++eb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int e = eb * 16 + (lane >> 4) * 4 + i;
+                const float z = v[eb][i];
+                v[eb][i] = e < E ? expf(z - m) : 0.f;
+                ssum += v[eb][i];
+                if (logits_out && t < T && e < E) logits_out[(size_t)t * E + e] = z;
+            }
+        ssum += __shfl_xor(ssum, 16);
+        ssum += __shfl_xor(ssum, 32);
+        const float inv = 1.0f / ssum;
+        if (t < T && lane < 16) {
+            expert[t] = mi;
+            gate[t] = inv;
+            lse[t] = m + logf(ssum);
+        }
+        const float w = t < T ? inv : 0.f;
+#pragma unroll
+        for (int eb = 0; eb < EB; ++eb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) psum[eb][i] += v[eb][i] * w;
+    }
+    // sum over the 16 tokens of a lane group, then waves in order
+#pragma unroll
+    for (int eb = 0; eb < EB; ++eb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float q = psum[eb][i];
+            q += __shfl_xor(q, 1);
+            q += __shfl_xor(q, 2);
+            q += __shfl_xor(q, 4);
+            q += __shfl_xor(q, 8);
+            psum[eb][i] = q;
+        }
+    for (int w = 0; w < 4; ++w) {
+        if (wave == w && r16 == 0) {
+#pragma unroll
+            for (int eb = 0; eb < EB; ++eb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int e = eb * 16 + (lane >> 4) * 4 + i;
+                    red[e] = (w == 0) ? psum[eb][i] : red[e] + psum[eb][i];
+                }
+        }
+        __syncthreads();
+    }
+    for (int e = threadIdx.x; e < E; e += 256) part[(size_t)blockIdx.x * E + e] = red[e];
+}
+
+hipError_t launch_router_fused(const bf16_t* x, const bf16_t* wr3, const float* b_r, int T, int d, int E,
+                               float* logits_out, int32_t* expert, float* gate, float* lse, float* part,
+                               hipStream_t s) {
+    const dim3 grid(router_fused_blocks(T));
+#define SWMOE_RF(EB, R)                                                                                             \
+    hipLaunchKernelGGL((router_fused<EB, R>), grid, dim3(256), 0, s, x, wr3, b_r, T, d, E, logits_out, expert, gate, \
+                       lse, part)
+    if (E <= 16) SWMOE_RF(1, 4);
+    else if (E <= 32) SWMOE_RF(2, 4);
+    else if (E <= 64) SWMOE_RF(4, 4);
+    else if (E <= 128) SWMOE_RF(8, 4);
+    else SWMOE_RF(16, 2);
+#undef SWMOE_RF
+    return hipGetLastError();
+}
+
 }  // namespace swmoe

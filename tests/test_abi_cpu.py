@@ -51,7 +51,10 @@ def test_workspace_sizes():
     assert sw.switch_workspace_bytes(16384, 768, 3072, 128, 128) >= 128 * 128 * 3072 * 2 + 128 * 128 * 768 * 6
     assert sw.switch_expert_ffn_workspace_bytes(128, 128, 3072) >= 128 * 128 * 3072 * 2
     assert sw.switch_dispatch_workspace_bytes(16384, 128) >= (16384 // 256) * 128 * 4
-    assert sw.switch_route_workspace_bytes(16384, 768, 128) >= 3 * 768 * 128 * 2 + 16384 * 128 * 4
+    # E <= 256: the fused router needs only the split weights and partial sums
+    assert sw.switch_route_workspace_bytes(16384, 768, 128) >= 3 * 768 * 128 * 2
+    # wider routers keep the logits in the workspace when the caller gives no logits array
+    assert sw.switch_route_workspace_bytes(65536, 1024, 2048) >= 3 * 1024 * 2048 * 2 + 65536 * 2048 * 4
     assert sw.switch_aux_loss_workspace_bytes(10, 4) == 0
     assert sw.switch_workspace_bytes(10, 64, 64, 0, 1) == 0      # E = 0 is invalid
     assert sw.switch_workspace_bytes(10, 64, 64, 5000, 1) == 0   # E above the limit
