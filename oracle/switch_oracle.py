@@ -379,3 +379,250 @@ def router_z_loss(z: np.ndarray, beta: float) -> ZLoss:
     loss = float(beta * np.mean(r.lse ** 2))
     dlogits = beta * (2.0 / T) * r.lse[:, None] * r.p
     return ZLoss(loss, dlogits)
+
+
+# ------------------------------------ NEXT f-3 / f-4: routing groups and top-k
+#
+# Routing groups ([XZ] "method adaptation": the input is reshaped to
+# cores x tokens per core x d and dispatch/combine carry a group axis;
+# [ZF] "evaluation protocol": every 64 rows apply the capacity limit on their
+# own and the batch metrics are averaged over those batches; "follow-up
+# questions": compare per-group and merged statistics).  Group g holds the
+# G consecutive tokens g*G .. g*G+G-1 (T must be a multiple of G); each group
+# has its own capacity per expert and its own slot counters.
+#
+# Top-k ([LAP] "full means turned back": capacity = tokens per batch / experts
+# x choices per token x capacity factor; [XZ] "method adaptation": Switch is
+# the k = 1 case of the earlier top-2 MoE).  A token's k choices are its k
+# largest logits, ties to the lower index; each choice keeps its raw softmax
+# probability as its gate (no renormalisation over the k, as for Switch in
+# [WQ] sec. 2).
+#
+# Order of the assignments inside a group, for the slot counters:
+#   "token": (token, rank) in lexicographic order - every slot of an expert
+#            goes to earlier tokens first, whatever the rank of the choice;
+#   "rank":  (rank, token) - all first choices of the group before any second
+#            choice (the priority of the earlier top-2 MoE).
+# Both equal the hot path's token order when k = 1.
+#
+# Buffer rows: an expert's kept assignments are packed in (group, order)
+# order, so row = (kept assignments of that expert in earlier groups) + the
+# in-group position; the buffer has n_groups * C_g rows per expert and the
+# filled rows of expert e are 0 .. accepted_total[e]-1.  With one group the row
+# is the position, as in the hot path.
+
+class RoutingK(NamedTuple):
+    p: np.ndarray        # [T, E]
+    lse: np.ndarray      # [T]
+    expert: np.ndarray   # [T, k] int64, choices in decreasing logit order
+    gate: np.ndarray     # [T, k] raw probabilities of the choices
+
+
+def softmax_topk(z: np.ndarray, k: int) -> RoutingK:
+    """The k largest logits of each token, ties to the lower index, with their
+    raw softmax probabilities.  k = 1 is softmax_top1."""
+    z = np.asarray(z, np.float64)
+    T, E = z.shape
+    if not 1 <= k <= E:
+        raise ValueError("need 1 <= k <= E")
+    r = softmax_top1(z)
+    # a stable sort of -z keeps equal logits in index order
+    order = np.argsort(-z, axis=1, kind="stable")[:, :k].astype(np.int64)
+    gate = np.take_along_axis(r.p, order, axis=1)
+    return RoutingK(r.p, r.lse, order, gate)
+
+
+def group_capacity(G: int, E: int, c: float, k: int = 1) -> int:
+    """Per-group, per-expert capacity ceil(c * k * G / E) ([LAP] "full means
+    turned back"; the rounding up follows [ZF] "core idea and formulas")."""
+    return capacity(k * G, E, c)
+
+
+class SlotsG(NamedTuple):
+    position: np.ndarray        # [T, k] in-group position of each assignment
+    keep: np.ndarray            # [T, k] position < C_g
+    slot: np.ndarray            # [T, k] buffer row within its expert, -1 if dropped
+    counts: np.ndarray          # [n_groups, E] raw assignments per group
+    accepted: np.ndarray        # [n_groups, E] min(counts, C_g)
+    accepted_total: np.ndarray  # [E] sum over groups of accepted
+    slot_token: np.ndarray      # [E, n_groups * C_g] token in each row, -1 if empty
+
+
+def assignment_order(G: int, k: int, priority: str):
+    """(local token, rank) pairs of one group in slot-counter order."""
+    if priority == "token":
+        return [(u, i) for u in range(G) for i in range(k)]
+    if priority == "rank":
+        return [(u, i) for i in range(k) for u in range(G)]
+    raise ValueError("priority must be 'token' or 'rank'")
+
+
+def slot_scan_grouped(expert: np.ndarray, E: int, G: int, Cg: int, priority: str = "token") -> SlotsG:
+    """Per group: one pass over its assignments in the chosen order with a
+    counter per expert; keep = position < C_g.  Rows packed per expert."""
+    expert = np.asarray(expert, np.int64)
+    if expert.ndim == 1:
+        expert = expert[:, None]
+    T, k = expert.shape
+    if G <= 0 or T % G != 0:
+        raise ValueError("T must be a multiple of the group size")
+    ng = T // G
+    position = np.empty((T, k), np.int64)
+    keep = np.empty((T, k), bool)
+    slot = np.full((T, k), -1, np.int64)
+    counts = np.zeros((ng, E), np.int64)
+    accepted = np.zeros((ng, E), np.int64)
+    slot_token = np.full((E, ng * Cg), -1, np.int64)
+    rows_used = [0] * E
+    order = assignment_order(G, k, priority)
+    for g in range(ng):
+        cnt = [0] * E
+        for u, i in order:
+            t = g * G + u
+            e = int(expert[t, i])
+            position[t, i] = cnt[e]
+            cnt[e] += 1
+            keep[t, i] = position[t, i] < Cg
+        for e in range(E):
+            counts[g, e] = cnt[e]
+            accepted[g, e] = min(cnt[e], Cg)
+        # rows: this group's kept assignments of each expert follow the
+        # earlier groups', in in-group position order
+        for u, i in order:
+            t = g * G + u
+            if keep[t, i]:
+                e = int(expert[t, i])
+                slot[t, i] = rows_used[e] + position[t, i]
+                slot_token[e, slot[t, i]] = t
+        for e in range(E):
+            rows_used[e] += int(accepted[g, e])
+    return SlotsG(position, keep, slot, counts, accepted, np.array(rows_used, np.int64), slot_token)
+
+
+def combine_topk(y: np.ndarray, expert: np.ndarray, slot: np.ndarray, keep: np.ndarray, gate: np.ndarray,
+                 residual: Optional[np.ndarray] = None) -> np.ndarray:
+    """branch_t = sum over the token's kept choices i of gate_ti * y[e_ti, slot_ti]
+    ([WQ] sec. 1/3 for one choice; the k choices are added with their raw
+    probabilities).  Dropped choices add nothing."""
+    expert = np.asarray(expert, np.int64).reshape(len(expert), -1)
+    slot = np.asarray(slot, np.int64).reshape(expert.shape)
+    keep = np.asarray(keep, bool).reshape(expert.shape)
+    gate = np.asarray(gate, np.float64).reshape(expert.shape)
+    T, k = expert.shape
+    branch = np.zeros((T, y.shape[2]), np.float64)
+    for i in range(k):
+        m = np.flatnonzero(keep[:, i])
+        branch[m] += gate[m, i, None] * y[expert[m, i], slot[m, i]]
+    if residual is None:
+        return branch
+    return np.asarray(residual, np.float64) + branch
+
+
+class AuxG(NamedTuple):
+    f: np.ndarray        # [n_groups, E] counts / (k G)
+    P: np.ndarray        # [n_groups, E] mean probability over the group
+    loss: float          # alpha E mean_g sum_e f_ge P_ge
+    dlogits: np.ndarray  # [T, E] with f held constant
+
+
+def aux_loss_grouped(counts: np.ndarray, p: np.ndarray, G: int, k: int, alpha: float) -> AuxG:
+    """The balance loss of [WQ] sec. 2 per routing group, averaged over the
+    groups ([ZF] "evaluation protocol": metrics per 64-row batch, then the
+    mean).  With k choices f counts the assignments and is divided by k G so
+    that it sums to 1 over the experts and the balanced loss stays alpha.
+    dL/dz_tj = (alpha E / T) p_tj (f_{g(t) j} - sum_e f_{g(t) e} p_te)."""
+    p = np.asarray(p, np.float64)
+    T, E = p.shape
+    counts = np.asarray(counts, np.float64).reshape(-1, E)
+    ng = counts.shape[0]
+    if T == 0:
+        return AuxG(np.zeros((ng, E)), np.zeros((ng, E)), 0.0, np.zeros((0, E)))
+    f = counts / (k * G)
+    P = p.reshape(ng, G, E).sum(axis=1) / G
+    loss = float(alpha * E * np.mean(np.sum(f * P, axis=1)))
+    fg = np.repeat(f, G, axis=0)                      # f of each token's group
+    s = np.sum(fg * p, axis=1)
+    dlogits = (alpha * E / T) * p * (fg - s[:, None])
+    return AuxG(f, P, loss, dlogits)
+
+
+class LayerResultG(NamedTuple):
+    z: np.ndarray
+    routing: RoutingK
+    G: int
+    Cg: int
+    slots: SlotsG
+    buf: np.ndarray
+    y: np.ndarray
+    branch: np.ndarray
+    out: np.ndarray
+    aux: AuxG
+
+
+def layer_forward_grouped(x, w_r, b_r, w1, w2, c: float, alpha: float, k: int = 1, G: Optional[int] = None,
+                          priority: str = "token", logits: Optional[np.ndarray] = None,
+                          expert_override: Optional[np.ndarray] = None, Cg: Optional[int] = None) -> LayerResultG:
+    """The layer with routing groups of G tokens (default: one group of T) and
+    top-k choices, in the step order of [WQ] sec. 3."""
+    x = np.asarray(x, np.float64)
+    T = x.shape[0]
+    z = router_logits(x, w_r, b_r) if logits is None else np.asarray(logits, np.float64)
+    E = z.shape[1]
+    G = T if G is None else int(G)
+    r = softmax_topk(z, k)
+    if expert_override is not None:
+        e = np.asarray(expert_override, np.int64).reshape(T, k)
+        r = RoutingK(r.p, r.lse, e, np.take_along_axis(r.p, e, axis=1))
+    if Cg is None:
+        Cg = group_capacity(G, E, c, k)
+    G = max(G, 1)   # an empty batch is zero groups of any size
+    sl = slot_scan_grouped(r.expert, E, G, Cg, priority)
+    aux = aux_loss_grouped(sl.counts, r.p, G, k, alpha)
+    buf = dispatch(x, sl.slot_token)
+    y = expert_ffn(buf, sl.accepted_total, w1, w2)
+    branch = combine_topk(y, r.expert, sl.slot, sl.keep, r.gate, None)
+    return LayerResultG(z, r, G, Cg, sl, buf, y, branch, x + branch, aux)
+
+
+def layer_per_token_topk(x, z, w1, w2, k: int, G: int, Cg: int, priority: str = "token"):
+    """Brute force for tiny inputs, with no shared state between tokens: each
+    token's choices by repeated strict-greater scans over the logits that skip
+    the experts already chosen, each choice's in-group position by counting
+    the group's assignments that come before it in the chosen order and pick
+    the same expert, and its branch by matrix-vector products."""
+    x = np.asarray(x, np.float64)
+    z = np.asarray(z, np.float64)
+    T, E = z.shape
+    choices = []
+    for t in range(T):
+        taken = []
+        for _ in range(k):
+            best = -1
+            for e in range(E):
+                if e in taken:
+                    continue
+                if best < 0 or z[t, e] > z[t, best]:
+                    best = e
+            taken.append(best)
+        choices.append(taken)
+
+    def before(a, b):  # does assignment a = (t, i) precede b in its group's order?
+        (ta, ia), (tb, ib) = a, b
+        return (ta, ia) < (tb, ib) if priority == "token" else (ia, ta) < (ib, tb)
+
+    positions = np.zeros((T, k), np.int64)
+    branch = np.zeros_like(x)
+    for t in range(T):
+        g0 = (t // G) * G
+        denom = sum(math.exp(v) for v in z[t])
+        for i in range(k):
+            e = choices[t][i]
+            pos = sum(1 for s in range(g0, g0 + G) for j in range(k)
+                      if choices[s][j] == e and before((s, j), (t, i)))
+            positions[t, i] = pos
+            if pos < Cg:
+                gte = math.exp(z[t, e]) / denom
+                w1e = np.asarray(w1(e) if callable(w1) else w1[e], np.float64)
+                w2e = np.asarray(w2(e) if callable(w2) else w2[e], np.float64)
+                branch[t] += gte * (w2e @ np.maximum(w1e @ x[t], 0.0))
+    return np.array(choices, np.int64), positions, branch

@@ -329,3 +329,206 @@ def pin_z_loss(so):
 
 
 ALL_PINS.append(pin_z_loss)
+
+
+# ------------------------------------ NEXT f-3 / f-4: routing groups and top-k
+def pin_groups_reduce_to_hot_path(so):
+    """One group of all T tokens and k = 1 is the hot-path layer, field by field."""
+    x, w_r, b_r, w1, w2 = _tiny_problem(31, 60, 8, 12, 5)
+    for c in (0.5, 1.0, 1.5):
+        A = so.layer_forward(x, w_r, b_r, w1, w2, c, 0.2)
+        B = so.layer_forward_grouped(x, w_r, b_r, w1, w2, c, 0.2, k=1, G=None)
+        assert B.Cg == A.C
+        np.testing.assert_array_equal(B.routing.expert[:, 0], A.routing.expert)
+        np.testing.assert_array_equal(B.slots.position[:, 0], A.slots.position)
+        np.testing.assert_array_equal(B.slots.keep[:, 0], A.slots.keep)
+        np.testing.assert_array_equal(B.slots.slot[:, 0], np.where(A.slots.keep, A.slots.position, -1))
+        np.testing.assert_array_equal(B.slots.counts[0], A.slots.counts)
+        np.testing.assert_array_equal(B.slots.accepted_total, A.slots.accepted)
+        np.testing.assert_array_equal(B.slots.slot_token, A.slots.slot_token)
+        np.testing.assert_array_equal(B.branch, A.branch)
+        np.testing.assert_array_equal(B.aux.f[0], A.aux.f)
+        np.testing.assert_array_equal(B.aux.P[0], A.aux.P)
+        assert abs(B.aux.loss - A.aux.loss) <= 1e-14 * abs(A.aux.loss)
+        np.testing.assert_allclose(B.aux.dlogits, A.aux.dlogits, rtol=1e-12, atol=1e-18)
+
+
+def pin_groups_are_separate_batches(so):
+    """zffjzz 'evaluation protocol': each group is its own batch.  The hot-path
+    layer run on every group's slice with C = C_g gives the grouped result:
+    positions, masks, counts, branch, f and P per group; the grouped loss is the
+    mean of the per-group losses and the grouped gradient is the per-group one
+    over the number of groups.  Buffer rows pack the groups in order."""
+    x, w_r, b_r, w1, w2 = _tiny_problem(32, 96, 8, 12, 4)
+    b_r = b_r.copy()
+    b_r[1] += 1.0
+    G = 24
+    for c in (0.5, 1.25):
+        L = so.layer_forward_grouped(x, w_r, b_r, w1, w2, c, 0.3, k=1, G=G)
+        Cg = so.capacity(G, 4, c)
+        assert L.Cg == Cg
+        rows = np.zeros(4, np.int64)
+        losses = []
+        for g in range(96 // G):
+            s = slice(g * G, (g + 1) * G)
+            A = so.layer_forward(x[s], w_r, b_r, w1, w2, c, 0.3, C=Cg)
+            np.testing.assert_array_equal(L.slots.position[s, 0], A.slots.position)
+            np.testing.assert_array_equal(L.slots.keep[s, 0], A.slots.keep)
+            np.testing.assert_array_equal(L.slots.counts[g], A.slots.counts)
+            np.testing.assert_array_equal(L.slots.accepted[g], A.slots.accepted)
+            kept = A.slots.keep
+            e = A.routing.expert
+            np.testing.assert_array_equal(L.slots.slot[s, 0][kept], rows[e[kept]] + A.slots.position[kept])
+            rows += A.slots.accepted
+            np.testing.assert_allclose(L.branch[s], A.branch, rtol=1e-13, atol=1e-14)
+            np.testing.assert_allclose(L.aux.f[g], A.aux.f, rtol=1e-15)
+            np.testing.assert_allclose(L.aux.P[g], A.aux.P, rtol=1e-13)
+            np.testing.assert_allclose(L.aux.dlogits[s], A.aux.dlogits / (96 // G), rtol=1e-12, atol=1e-17)
+            losses.append(A.aux.loss)
+        np.testing.assert_array_equal(L.slots.accepted_total, rows)
+        assert abs(L.aux.loss - np.mean(losses)) <= 1e-14 * abs(L.aux.loss) + 1e-17
+
+
+def _logits_for_choices(choices, E, rng):
+    """Tie-free logits whose top choices are the given expert lists."""
+    T = len(choices)
+    z = rng.uniform(-1.0, 0.0, (T, E))
+    for t, ch in enumerate(choices):
+        for i, e in enumerate(ch):
+            z[t, e] = 3.0 - i
+    return z
+
+
+def pin_batch_capacity_overflow(so):
+    """zffjzz: per-64-row capacity; test counts [32,2,116,106] give 24.22 %
+    overflow at c = 1.25 and none at c = 4.  A split with the hot experts
+    uneven across batches overflows more under groups than under one group
+    of all rows (local vs merged balance)."""
+    g = GOLDEN["batch_capacity_overflow"]
+    G, E = g["G"], g["E"]
+    rng = _rng(33)
+
+    def run(split, c, group):
+        choices = []
+        for b in range(4):
+            blk = [e for e in range(E) for _ in range(split[e][b])]
+            rng.shuffle(blk)
+            choices += [[e] for e in blk]
+        z = _logits_for_choices(choices, E, rng)
+        r = so.softmax_topk(z, 1)
+        T = len(choices)
+        Gs = group if group else T
+        sl = so.slot_scan_grouped(r.expert, E, Gs, so.group_capacity(Gs, E, c, 1))
+        assert sl.counts.sum(axis=0).tolist() == g["test_counts"]
+        return 1.0 - sl.keep.mean(), so.group_capacity(Gs, E, c, 1)
+
+    even = [[8] * 4, [1, 1, 0, 0], [29] * 4, [26, 26, 27, 27]]
+    ov, Cg = run(even, g["c_low"], G)
+    assert Cg == g["expected_Cg_low"]
+    assert round(100 * ov, 2) == g["expected_overflow_low_pct"] and ov == 62 / 256
+    assert run(even, g["c_high"], G)[0] == g["expected_overflow_high"]
+    assert run(even, g["c_low"], None)[0] == 62 / 256          # one group of 256 rows, C = 80
+    uneven = [[8] * 4, [1, 1, 0, 0], [44, 44, 14, 14], [11, 11, 42, 42]]
+    assert run(uneven, g["c_low"], G)[0] == 92 / 256
+    assert run(uneven, g["c_low"], None)[0] == 62 / 256
+
+
+def pin_topk_capacity(so):
+    """lapla.si 'full means turned back': 32 per batch, 16 experts, 2 choices, c = 1 -> 4."""
+    g = GOLDEN["topk_batch_capacity"]
+    assert so.group_capacity(g["G"], g["E"], g["c"], g["k"]) == g["expected_C"]
+    assert so.group_capacity(32, 16, 1.25, 2) == 5 and so.group_capacity(32, 16, 2.0, 2) == 8
+    assert so.group_capacity(64, 4, 1.25, 1) == 20
+
+
+def pin_priority_hand_example(so):
+    """A hand-worked case where the two assignment orders differ: E = 3, k = 2,
+    one group of 3 tokens, C_g = ceil(0.5 * 2 * 3 / 3) = 1; choices
+    t0 -> (1, 0), t1 -> (0, 2), t2 -> (0, 1).
+    Token order: t0's second choice takes expert 0's slot, t1's first choice drops.
+    Rank order: t1's first choice takes it and t0's second choice drops."""
+    z = np.array([[1.0, 2.0, 0.0], [2.0, 0.0, 1.0], [2.0, 1.0, 0.0]])
+    r = so.softmax_topk(z, 2)
+    np.testing.assert_array_equal(r.expert, [[1, 0], [0, 2], [0, 1]])
+    Cg = so.group_capacity(3, 3, 0.5, 2)
+    assert Cg == 1
+    a = so.slot_scan_grouped(r.expert, 3, 3, Cg, "token")
+    np.testing.assert_array_equal(a.position, [[0, 0], [1, 0], [2, 1]])
+    np.testing.assert_array_equal(a.keep, [[1, 1], [0, 1], [0, 0]])
+    np.testing.assert_array_equal(a.slot_token, [[0], [0], [1]])
+    b = so.slot_scan_grouped(r.expert, 3, 3, Cg, "rank")
+    np.testing.assert_array_equal(b.position, [[0, 2], [0, 0], [1, 1]])
+    np.testing.assert_array_equal(b.keep, [[1, 0], [1, 1], [0, 0]])
+    np.testing.assert_array_equal(b.slot_token, [[1], [0], [1]])
+    np.testing.assert_array_equal(a.counts, [[3, 2, 1]])
+    np.testing.assert_array_equal(b.counts, [[3, 2, 1]])
+
+
+def pin_topk_brute_force(so):
+    """Top-k with groups against a per-token brute force (repeated strict-greater
+    scans, counting earlier assignments), both orders, with and without ties."""
+    x, w_r, b_r, w1, w2 = _tiny_problem(34, 48, 8, 12, 5)
+    z_rand = x.astype(np.float64) @ w_r.astype(np.float64) + b_r
+    z_ties = _rng(35).integers(-2, 3, (48, 5)).astype(np.float64) / 4
+    for z in (z_rand, z_ties):
+        for k in (1, 2, 3):
+            for G in (48, 12):
+                for pr in ("token", "rank"):
+                    for c in (0.5, 1.0):
+                        L = so.layer_forward_grouped(x, w_r, b_r, w1, w2, c, 0.1, k=k, G=G, priority=pr, logits=z)
+                        ch, pos, br = so.layer_per_token_topk(x, z, w1, w2, k, G, L.Cg, pr)
+                        np.testing.assert_array_equal(L.routing.expert, ch)
+                        np.testing.assert_array_equal(L.slots.position, pos)
+                        np.testing.assert_array_equal(L.slots.keep, pos < L.Cg)
+                        np.testing.assert_allclose(L.branch, br, rtol=1e-12, atol=1e-13)
+
+
+def pin_topk_all_experts_is_soft_mixture(so):
+    """k = E and c = 1: C_g = G, nothing dropped, and the branch is the dense
+    probability-weighted sum of every expert's FFN (torch einsum)."""
+    x, w_r, b_r, w1, w2 = _tiny_problem(36, 20, 8, 12, 3)
+    L = so.layer_forward_grouped(x, w_r, b_r, w1, w2, 1.0, 0.1, k=3, G=10)
+    assert L.Cg == 10 and L.slots.keep.all()
+    X = torch.from_numpy(x.astype(np.float64))
+    H = torch.relu(torch.einsum("td,efd->tef", X, torch.from_numpy(w1.astype(np.float64))))
+    Y = torch.einsum("tef,edf->ted", H, torch.from_numpy(w2.astype(np.float64)))
+    p = torch.softmax(torch.from_numpy(L.z), dim=1)
+    ref = torch.einsum("te,ted->td", p, Y).numpy()
+    np.testing.assert_allclose(L.branch, ref, rtol=1e-12, atol=1e-13)
+
+
+def pin_grouped_aux(so):
+    """Grouped / top-k balance loss: uniform rows give 1 for k = 1 and 2
+    (f sums to 1 over the assignments); f of each group sums to 1; gradient
+    rows sum to 0; central finite differences of the grouped loss."""
+    for k in (1, 2):
+        r = so.softmax_topk(np.zeros((64, 4)), k)
+        sl = so.slot_scan_grouped(r.expert, 4, 16, 100)
+        a = so.aux_loss_grouped(sl.counts, r.p, 16, k, 1.0)
+        assert abs(a.loss - 1.0) < 1e-14
+        np.testing.assert_allclose(a.f.sum(axis=1), 1.0, rtol=1e-15)
+    rng = _rng(37)
+    T, E, G, k, alpha = 12, 4, 4, 2, 0.7
+    z = rng.standard_normal((T, E))
+    r = so.softmax_topk(z, k)
+    counts = so.slot_scan_grouped(r.expert, E, G, 100).counts
+    A = so.aux_loss_grouped(counts, r.p, G, k, alpha)
+    np.testing.assert_allclose(A.dlogits.sum(axis=1), 0.0, atol=1e-16)
+    h = 1e-6
+    num = np.zeros_like(z)
+    for t in range(T):
+        for j in range(E):
+            zp, zm = z.copy(), z.copy()
+            zp[t, j] += h
+            zm[t, j] -= h
+            num[t, j] = (so.aux_loss_grouped(counts, so.softmax_top1(zp).p, G, k, alpha).loss -
+                         so.aux_loss_grouped(counts, so.softmax_top1(zm).p, G, k, alpha).loss) / (2 * h)
+    np.testing.assert_allclose(A.dlogits, num, rtol=0, atol=2e-9)
+
+
+GROUP_TOPK_PINS = [
+    pin_groups_reduce_to_hot_path, pin_groups_are_separate_batches, pin_batch_capacity_overflow,
+    pin_topk_capacity, pin_priority_hand_example, pin_topk_brute_force, pin_topk_all_experts_is_soft_mixture,
+    pin_grouped_aux,
+]
+ALL_PINS.extend(GROUP_TOPK_PINS)

@@ -179,3 +179,121 @@ def test_z_loss_pin_catches_mutant(mutate):
     mutate(m)
     with pytest.raises(Exception):
         pins.pin_z_loss(m)
+
+
+# ------------------------------------ routing groups and top-k
+def m_group_capacity_no_k(m):
+    cap = m.capacity
+    m.group_capacity = lambda G, E, c, k=1: cap(G, E, c)
+
+
+def m_priority_swapped(m):
+    orig = m.assignment_order
+    m.assignment_order = lambda G, k, priority: orig(G, k, "rank" if priority == "token" else "token")
+
+
+def m_rows_not_packed(m):
+    orig = m.slot_scan_grouped
+    def f(expert, E, G, Cg, priority="token"):
+        s = orig(expert, E, G, Cg, priority)
+        slot = np.where(s.keep, s.position, -1)
+        st = np.full_like(s.slot_token, -1)
+        T, k = slot.shape
+        for t in range(T):
+            for i in range(k):
+                if slot[t, i] >= 0:
+                    st[int(np.asarray(expert).reshape(T, -1)[t, i]), slot[t, i]] = t
+        return s._replace(slot=slot, slot_token=st)
+    m.slot_scan_grouped = f
+
+
+def m_counters_not_reset(m):
+    def f(expert, E, G, Cg, priority="token"):
+        expert = np.asarray(expert, np.int64).reshape(len(expert), -1)
+        T, k = expert.shape
+        one = m.slot_scan(expert[:, 0], E, Cg) if k == 1 else None
+        if one is None:
+            raise AssertionError("k > 1 path not mutated")
+        ng = T // G
+        counts = np.stack([np.bincount(expert[g * G:(g + 1) * G, 0], minlength=E) for g in range(ng)])
+        slot = np.where(one.keep, one.position, -1)[:, None]
+        st = np.full((E, ng * Cg), -1, np.int64)
+        st[:, :Cg] = one.slot_token
+        return m.SlotsG(one.position[:, None], one.keep[:, None], slot, counts, np.minimum(counts, Cg),
+                        one.accepted, st)
+    m.slot_scan_grouped = f
+
+
+def m_grouped_f_over_G(m):
+    orig = m.aux_loss_grouped
+    m.aux_loss_grouped = lambda counts, p, G, k, alpha: orig(np.asarray(counts) * k, p, G, k, alpha)
+
+
+def m_grouped_loss_sum(m):
+    orig = m.aux_loss_grouped
+    def f(counts, p, G, k, alpha):
+        a = orig(counts, p, G, k, alpha)
+        ng = np.asarray(counts).reshape(-1, np.asarray(p).shape[1]).shape[0]
+        return a._replace(loss=a.loss * ng)
+    m.aux_loss_grouped = f
+
+
+def m_grouped_grad_global_f(m):
+    orig = m.aux_loss_grouped
+    def f(counts, p, G, k, alpha):
+        a = orig(counts, p, G, k, alpha)
+        p = np.asarray(p, np.float64)
+        T, E = p.shape
+        if T == 0:
+            return a
+        fm = a.f.mean(axis=0)
+        return a._replace(dlogits=(alpha * E / T) * p * (fm[None, :] - (p @ fm)[:, None]))
+    m.aux_loss_grouped = f
+
+
+def m_topk_ties_high(m):
+    orig = m.softmax_topk
+    def f(z, k):
+        r = orig(z, k)
+        z = np.asarray(z, np.float64)
+        E = z.shape[1]
+        order = (E - 1 - np.argsort(-z[:, ::-1], axis=1, kind="stable"))[:, :k]
+        return r._replace(expert=order, gate=np.take_along_axis(r.p, order, axis=1))
+    m.softmax_topk = f
+
+
+def m_topk_renormalised(m):
+    orig = m.softmax_topk
+    def f(z, k):
+        r = orig(z, k)
+        return r._replace(gate=r.gate / r.gate.sum(axis=1, keepdims=True))
+    m.softmax_topk = f
+
+
+def m_combine_first_choice_only(m):
+    orig = m.combine_topk
+    def f(y, expert, slot, keep, gate, residual=None):
+        keep = np.asarray(keep, bool).reshape(len(expert), -1).copy()
+        keep[:, 1:] = False
+        return orig(y, expert, slot, keep, gate, residual)
+    m.combine_topk = f
+
+
+GROUP_MUTANTS = [m_group_capacity_no_k, m_priority_swapped, m_rows_not_packed, m_counters_not_reset,
+                 m_grouped_f_over_G, m_grouped_loss_sum, m_grouped_grad_global_f, m_topk_ties_high,
+                 m_topk_renormalised, m_combine_first_choice_only]
+
+
+@pytest.mark.parametrize("mutate", GROUP_MUTANTS, ids=lambda f: f.__name__)
+def test_group_topk_pins_catch_mutant(mutate):
+    """Each planted mistake in the grouped / top-k oracle fails one of the pins
+    written for it (not only a pin of the hot path)."""
+    m = fresh_oracle()
+    mutate(m)
+    failed = []
+    for pin in pins.GROUP_TOPK_PINS:
+        try:
+            pin(m)
+        except Exception:
+            failed.append(pin.__name__)
+    assert failed, f"no grouped/top-k pin caught {mutate.__name__}"
