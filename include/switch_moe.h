@@ -240,9 +240,86 @@ typedef struct switch_layer_args {
     float alpha;
     float z_beta;                /* z-loss coefficient (used when z_loss != NULL) */
     int32_t residual;            /* 1: out = x + branch; 0: out = branch only */
+    /* routing groups and top-k (see the extended entry points below); zero
+     * selects the Switch layer: k = 0 means 1, group = 0 one group of T tokens.
+     * With k > 1, expert/gate/position/keep are [T, k]; with several groups,
+     * counts/accepted/f/P/prob_sum are [T / group, E], C is the capacity of one
+     * group and the buffer has (T / group) * C rows per expert. */
+    int32_t k;                   /* choices per token, 1 .. 4 */
+    int32_t priority;            /* slot order inside a group: 0 token, 1 rank */
+    int64_t group;               /* tokens per routing group */
+    int32_t *slot;               /*     [T, k] buffer row of each kept choice, -1 if dropped */
+    int32_t *accepted_total;     /*     [E] filled buffer rows per expert */
 } switch_layer_args;
 
 switch_status switch_layer_fwd(const switch_layer_args *a, void *ws, size_t ws_bytes, void *stream);
+size_t switch_workspace_bytes_ex(int64_t T, int32_t d, int32_t d_ff, int32_t E, int32_t C, int32_t k,
+                                 int64_t group);
+
+/* ------------------------------------------- routing groups and top-k choices
+ *
+ * Routing groups.  Sources: paper card "Switch Transformers" (xuzou.cn),
+ * "method adaptation": the input is reshaped to cores x tokens per core and
+ * the dispatch/combine tensors carry that group axis; "MoE routing load
+ * collapse" (zffjzz.top), "evaluation protocol": every 64 rows apply the
+ * capacity limit on their own and the batch metrics are averaged, and
+ * "follow-up questions": per-group against merged statistics.  Group g is the
+ * `group` consecutive tokens g*group ..; T must be a multiple of `group`, and
+ * with more than one group `group` must be a multiple of 64.  Every group has
+ * its own capacity C per expert and its own slot counters.
+ *
+ * Top-k.  Sources: "Mixture of experts" (world.lapla.si), "full means turned
+ * back": capacity = tokens per batch / experts x choices per token x capacity
+ * factor (so C = switch_capacity(k * group, E, c)); the card's "method
+ * adaptation": Switch is the k = 1 case of the earlier top-2 MoE.  A token's
+ * choices are its k largest logits in decreasing order, ties to the lower
+ * index; each keeps its raw probability as its gate (no renormalisation).
+ *
+ * Slot order inside a group (priority): 0 = (token, choice) in lexicographic
+ * order; 1 = (choice, token), all first choices before any second choice.
+ * Buffer rows: each expert's kept choices are packed group after group, so
+ * row = (kept choices of that expert in earlier groups) + in-group position,
+ * the buffer has groups * C rows per expert and rows 0 .. accepted_total[e]-1
+ * of expert e are filled.  One group and k = 1 give the Switch layer exactly.
+ */
+
+/* switch_route with k choices per token and per-group probability sums.
+ *   expert, gate [T, k]; lse [T]; prob_sum [T / group, E] (one row for one group)
+ * Workspace: switch_route_workspace_bytes(T, d, E). */
+switch_status switch_route_ex(const switch_bf16 *x, const float *w_r, const float *b_r,
+                              const float *logits_in, int64_t T, int32_t d, int32_t E, int32_t k,
+                              int64_t group, float *logits_out, int32_t *expert, float *gate,
+                              float *lse, float *prob_sum, void *ws, size_t ws_bytes, void *stream);
+
+/* switch_dispatch over the T*k choices with routing groups.
+ *   expert [T, k] int32; C capacity of one group per expert;
+ *   position [T, k] in-group rank (-1 for ids outside [0, E)); keep [T, k];
+ *   slot [T, k] buffer row or -1 (may be NULL with one group);
+ *   counts, accepted [T / group, E]; accepted_total [E] (may be NULL with one group);
+ *   slot_token [E, groups * C] or NULL; buf [E, groups * C, d] bf16, empty rows zero.
+ * Workspace: switch_dispatch_workspace_bytes_ex(T, E, k, group). */
+size_t switch_dispatch_workspace_bytes_ex(int64_t T, int32_t E, int32_t k, int64_t group);
+switch_status switch_dispatch_ex(const switch_bf16 *x, const int32_t *expert, int64_t T, int32_t d, int32_t E,
+                                 int32_t k, int64_t group, int32_t C, int32_t priority, int32_t *position,
+                                 uint8_t *keep, int32_t *slot, int32_t *counts, int32_t *accepted,
+                                 int32_t *accepted_total, int32_t *slot_token, switch_bf16 *buf, void *ws,
+                                 size_t ws_bytes, void *stream);
+
+/* switch_combine over k choices: out_t = residual_t + sum_i keep_ti gate_ti
+ * y[expert_ti, slot_ti], the choices added in rank order in fp32, one bf16
+ * rounding; a token with every choice dropped gets its residual bit for bit.
+ *   y [E, rows, d] fp32; expert, slot [T, k]; keep [T, k]; gate [T, k]. */
+switch_status switch_combine_ex(const float *y, const int32_t *expert, const int32_t *slot, const uint8_t *keep,
+                                const float *gate, const switch_bf16 *residual, int64_t T, int32_t d, int32_t E,
+                                int32_t k, int32_t rows, switch_bf16 *out, void *stream);
+
+/* switch_aux_loss per routing group: f_ge = counts_ge / (k group),
+ * P_ge = prob_sum_ge / group, loss = alpha E (1 / groups) sum_g sum_e f_ge P_ge;
+ * dlogits_tj = (alpha E / T) p_tj (f_{g(t) j} - sum_e f_{g(t) e} p_te).
+ *   counts, prob_sum, f, P [T / group, E]. */
+switch_status switch_aux_loss_ex(const int32_t *counts, const float *prob_sum, const float *logits,
+                                 const float *lse, int64_t T, int32_t E, int32_t k, int64_t group, float alpha,
+                                 float *f, float *P, float *loss, float *dlogits, void *stream);
 
 /* ------------------------------------------------------------- measurement */
 

@@ -26,6 +26,8 @@ EXPORTS = [
     "switch_status_string", "switch_last_error", "switch_route", "switch_dispatch", "switch_expert_ffn",
     "switch_combine", "switch_aux_loss", "switch_layer_fwd", "switch_stream_copy", "switch_profile_enable",
     "switch_profile_collect", "switch_kernel_name", "switch_router_z_loss",
+    "switch_route_ex", "switch_dispatch_ex", "switch_dispatch_workspace_bytes_ex", "switch_combine_ex",
+    "switch_aux_loss_ex", "switch_workspace_bytes_ex",
 ]
 
 
@@ -41,7 +43,9 @@ class LayerArgs(ctypes.Structure):
         "x", "w_r", "b_r", "w1", "w2", "out", "expert", "gate", "position", "keep", "counts", "accepted",
         "f", "P", "loss", "logits", "lse", "prob_sum", "dlogits", "slot_token", "buf", "y", "z_loss")] + [
         ("T", ctypes.c_int64), ("d", ctypes.c_int32), ("d_ff", ctypes.c_int32), ("E", ctypes.c_int32),
-        ("C", ctypes.c_int32), ("alpha", ctypes.c_float), ("z_beta", ctypes.c_float), ("residual", ctypes.c_int32)]
+        ("C", ctypes.c_int32), ("alpha", ctypes.c_float), ("z_beta", ctypes.c_float), ("residual", ctypes.c_int32),
+        ("k", ctypes.c_int32), ("priority", ctypes.c_int32), ("group", ctypes.c_int64),
+        ("slot", ctypes.c_void_p), ("accepted_total", ctypes.c_void_p)]
 
 
 def lib():
@@ -73,6 +77,12 @@ def lib():
             "switch_profile_collect": (I32, [I32, P, P]),
             "switch_kernel_name": (ctypes.c_char_p, [I32]),
             "switch_router_z_loss": (I32, [P, P, I64, I32, F32, P, P, I32, P]),
+            "switch_route_ex": (I32, [P, P, P, P, I64, I32, I32, I32, I64, P, P, P, P, P, P, SZ, P]),
+            "switch_dispatch_workspace_bytes_ex": (SZ, [I64, I32, I32, I64]),
+            "switch_dispatch_ex": (I32, [P, P, I64, I32, I32, I32, I64, I32, I32, P, P, P, P, P, P, P, P, P, SZ, P]),
+            "switch_combine_ex": (I32, [P, P, P, P, P, P, I64, I32, I32, I32, I32, P, P]),
+            "switch_aux_loss_ex": (I32, [P, P, P, P, I64, I32, I32, I64, F32, P, P, P, P, P]),
+            "switch_workspace_bytes_ex": (SZ, [I64, I32, I32, I32, I32, I32, I64]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -137,6 +147,14 @@ def switch_workspace_bytes(T, d, d_ff, E, C):
     return lib().switch_workspace_bytes(T, d, d_ff, E, C)
 
 
+def switch_dispatch_workspace_bytes_ex(T, E, k, group):
+    return lib().switch_dispatch_workspace_bytes_ex(T, E, k, group)
+
+
+def switch_workspace_bytes_ex(T, d, d_ff, E, C, k, group):
+    return lib().switch_workspace_bytes_ex(T, d, d_ff, E, C, k, group)
+
+
 # ------------------------------------------------------------ device calls
 # Tensors: bf16 arrays are torch.bfloat16, int32 arrays torch.int32, keep is
 # torch.uint8, floats torch.float32; all contiguous on the current device.
@@ -176,6 +194,33 @@ def switch_router_z_loss(lse, logits, T, E, beta, z_loss, dlogits=None, accumula
                                       1 if accumulate else 0, _stream(stream)), "switch_router_z_loss")
 
 
+def switch_route_ex(x, w_r, b_r, logits_in, T, d, E, k, group, logits_out, expert, gate, lse, prob_sum, ws,
+                    stream=None):
+    wp, wn = _ws(ws)
+    _check(lib().switch_route_ex(_ptr(x), _ptr(w_r), _ptr(b_r), _ptr(logits_in), T, d, E, k, group, _ptr(logits_out),
+                                 _ptr(expert), _ptr(gate), _ptr(lse), _ptr(prob_sum), wp, wn, _stream(stream)),
+           "switch_route_ex")
+
+
+def switch_dispatch_ex(x, expert, T, d, E, k, group, C, priority, position, keep, slot, counts, accepted,
+                       accepted_total, slot_token, buf, ws, stream=None):
+    wp, wn = _ws(ws)
+    _check(lib().switch_dispatch_ex(_ptr(x), _ptr(expert), T, d, E, k, group, C, priority, _ptr(position), _ptr(keep),
+                                    _ptr(slot), _ptr(counts), _ptr(accepted), _ptr(accepted_total), _ptr(slot_token),
+                                    _ptr(buf), wp, wn, _stream(stream)), "switch_dispatch_ex")
+
+
+def switch_combine_ex(y, expert, slot, keep, gate, residual, T, d, E, k, rows, out, stream=None):
+    _check(lib().switch_combine_ex(_ptr(y), _ptr(expert), _ptr(slot), _ptr(keep), _ptr(gate), _ptr(residual),
+                                   T, d, E, k, rows, _ptr(out), _stream(stream)), "switch_combine_ex")
+
+
+def switch_aux_loss_ex(counts, prob_sum, logits, lse, T, E, k, group, alpha, f, P, loss, dlogits, stream=None):
+    _check(lib().switch_aux_loss_ex(_ptr(counts), _ptr(prob_sum), _ptr(logits), _ptr(lse), T, E, k, group, alpha,
+                                    _ptr(f), _ptr(P), _ptr(loss), _ptr(dlogits), _stream(stream)),
+           "switch_aux_loss_ex")
+
+
 def switch_layer_fwd(args: LayerArgs, ws, stream=None):
     wp, wn = _ws(ws)
     _check(lib().switch_layer_fwd(ctypes.byref(args), wp, wn, _stream(stream)), "switch_layer_fwd")
@@ -200,24 +245,34 @@ def switch_profile_collect(max_records: int = 1 << 16):
 
 
 # ------------------------------------------------------------ allocation helpers
-def layer_tensors(T, d, d_ff, E, C, device="cuda", logits=False, dlogits=False, inspect=False, z_loss=False):
-    """Output tensors of switch_layer_fwd (plus a workspace), allocated with torch."""
+def layer_tensors(T, d, d_ff, E, C, device="cuda", logits=False, dlogits=False, inspect=False, z_loss=False,
+                  k=1, group=0):
+    """Output tensors of switch_layer_fwd (plus a workspace), allocated with torch.
+    With k choices the per-choice arrays are [T, k]; with several routing groups
+    of `group` tokens the per-expert statistics are [T // group, E], C is the
+    capacity of one group and the buffer has (T // group) * C rows per expert."""
     import torch
     dev = torch.device(device)
+    ng = 1 if group in (0, T) else T // group
+    rows = ng * C
+    kk = () if k == 1 else (k,)
     o = {
         "out": torch.empty((T, d), dtype=torch.bfloat16, device=dev),
-        "expert": torch.empty(T, dtype=torch.int32, device=dev),
-        "gate": torch.empty(T, dtype=torch.float32, device=dev),
-        "position": torch.empty(T, dtype=torch.int32, device=dev),
-        "keep": torch.empty(T, dtype=torch.uint8, device=dev),
-        "counts": torch.empty(E, dtype=torch.int32, device=dev),
-        "accepted": torch.empty(E, dtype=torch.int32, device=dev),
-        "f": torch.empty(E, dtype=torch.float32, device=dev),
-        "P": torch.empty(E, dtype=torch.float32, device=dev),
+        "expert": torch.empty((T,) + kk, dtype=torch.int32, device=dev),
+        "gate": torch.empty((T,) + kk, dtype=torch.float32, device=dev),
+        "position": torch.empty((T,) + kk, dtype=torch.int32, device=dev),
+        "keep": torch.empty((T,) + kk, dtype=torch.uint8, device=dev),
+        "counts": torch.empty((ng, E) if ng != 1 else E, dtype=torch.int32, device=dev),
+        "accepted": torch.empty((ng, E) if ng != 1 else E, dtype=torch.int32, device=dev),
+        "f": torch.empty((ng, E) if ng != 1 else E, dtype=torch.float32, device=dev),
+        "P": torch.empty((ng, E) if ng != 1 else E, dtype=torch.float32, device=dev),
         "loss": torch.empty(1, dtype=torch.float32, device=dev),
         "lse": torch.empty(T, dtype=torch.float32, device=dev),
-        "prob_sum": torch.empty(E, dtype=torch.float32, device=dev),
+        "prob_sum": torch.empty((ng, E) if ng != 1 else E, dtype=torch.float32, device=dev),
     }
+    if ng != 1:
+        o["slot"] = torch.empty((T,) + kk, dtype=torch.int32, device=dev)
+        o["accepted_total"] = torch.empty(E, dtype=torch.int32, device=dev)
     if logits or dlogits:
         o["logits"] = torch.empty((T, E), dtype=torch.float32, device=dev)
     if dlogits:
@@ -225,20 +280,23 @@ def layer_tensors(T, d, d_ff, E, C, device="cuda", logits=False, dlogits=False, 
     if z_loss:
         o["z_loss"] = torch.empty(1, dtype=torch.float32, device=dev)
     if inspect:
-        o["slot_token"] = torch.empty((E, C), dtype=torch.int32, device=dev)
-        o["buf"] = torch.empty((E, C, d), dtype=torch.bfloat16, device=dev)
-        o["y"] = torch.empty((E, C, d), dtype=torch.float32, device=dev)
-    o["ws"] = torch.empty(max(256, switch_workspace_bytes(T, d, d_ff, E, C)), dtype=torch.uint8, device=dev)
+        o["slot_token"] = torch.empty((E, rows), dtype=torch.int32, device=dev)
+        o["buf"] = torch.empty((E, rows, d), dtype=torch.bfloat16, device=dev)
+        o["y"] = torch.empty((E, rows, d), dtype=torch.float32, device=dev)
+    nbytes = switch_workspace_bytes_ex(T, d, d_ff, E, C, k, group)
+    o["ws"] = torch.empty(max(256, nbytes), dtype=torch.uint8, device=dev)
     return o
 
 
-def make_layer_args(x, w_r, b_r, w1, w2, t: dict, T, d, d_ff, E, C, alpha, residual=True, z_beta=0.0) -> LayerArgs:
+def make_layer_args(x, w_r, b_r, w1, w2, t: dict, T, d, d_ff, E, C, alpha, residual=True, z_beta=0.0,
+                    k=1, group=0, priority=0) -> LayerArgs:
     a = LayerArgs()
     for name, v in (("x", x), ("w_r", w_r), ("b_r", b_r), ("w1", w1), ("w2", w2)):
         setattr(a, name, _ptr(v))
     for name in ("out", "expert", "gate", "position", "keep", "counts", "accepted", "f", "P", "loss", "logits",
-                 "lse", "prob_sum", "dlogits", "slot_token", "buf", "y", "z_loss"):
+                 "lse", "prob_sum", "dlogits", "slot_token", "buf", "y", "z_loss", "slot", "accepted_total"):
         setattr(a, name, _ptr(t.get(name)))
     a.T, a.d, a.d_ff, a.E, a.C, a.alpha, a.residual = T, d, d_ff, E, C, alpha, 1 if residual else 0
     a.z_beta = z_beta
+    a.k, a.group, a.priority = k, group, priority
     return a

@@ -96,7 +96,20 @@ size_t route_ws(int64_t T, int32_t d, int32_t E, bool logits_out_given) {
     if (!logits_out_given && !route_fused(E)) n += up((size_t)T * E * sizeof(float));
     return n;
 }
-size_t dispatch_ws(int64_t T, int32_t E) { return up((size_t)scan_tiles(T) * E * sizeof(int32_t)); }
+// Routing groups: group == 0 (or == T) is one group of all T tokens.
+bool one_group(int64_t T, int64_t G) { return G == 0 || G == T; }
+int64_t group_count(int64_t T, int64_t G) { return one_group(T, G) ? 1 : T / G; }
+int64_t group_tokens(int64_t T, int64_t G) { return one_group(T, G) ? T : G; }
+// buffer rows per expert: C per group, groups packed one after the other
+int64_t buffer_rows(int64_t T, int64_t G, int32_t C) { return group_count(T, G) * C; }
+
+size_t dispatch_ws(int64_t T, int32_t E, int32_t k, int64_t G) {
+    const bool one = one_group(T, G);
+    const int tile = scan_tile(group_tokens(T, G) * k, one);
+    size_t n = up((size_t)scan_tiles(T * k, tile) * E * sizeof(int32_t));
+    if (!one) n += up((size_t)group_count(T, G) * E * sizeof(int32_t)) + up((size_t)E * sizeof(int32_t));
+    return n;
+}
 size_t ffn_ws(int32_t E, int32_t C, int32_t d_ff) {
     return up((size_t)E * C * d_ff * sizeof(bf16_t)) + up((size_t)(E + 1) * sizeof(int32_t)) +
            up(ffn_tile_table_entries(E, C) * sizeof(int4));
@@ -123,6 +136,19 @@ switch_status check_C(int32_t E, int32_t C) {
     return SWITCH_OK;
 }
 
+// k choices per token and routing groups of G tokens
+switch_status check_kG(int64_t T, int32_t E, int32_t k, int64_t G) {
+    REQUIRE(k >= 1 && k <= E, "k must be in [1, E] (got %d)", k);
+    SUPPORT(k <= kMaxTopK, "k must be <= %d (got %d)", kMaxTopK, k);
+    SUPPORT(T * k < (int64_t(1) << 31), "T*k must be < 2^31");
+    REQUIRE(G >= 0, "group must be >= 0 (got %lld)", (long long)G);
+    if (!one_group(T, G)) {
+        REQUIRE(T % G == 0, "T (%lld) must be a multiple of the group size (%lld)", (long long)T, (long long)G);
+        SUPPORT(G % 64 == 0, "the group size must be a multiple of 64 (got %lld)", (long long)G);
+    }
+    return SWITCH_OK;
+}
+
 #define CHECK(x) do { switch_status _s = (x); if (_s != SWITCH_OK) return _s; } while (0)
 #define NONNULL(p) REQUIRE((p) != nullptr, "%s must not be NULL", #p)
 // arrays with zero elements may be NULL (torch gives empty tensors a NULL data pointer)
@@ -135,12 +161,15 @@ struct RouteArgs {
     const bf16_t* x; const float* w_r; const float* b_r; const float* logits_in;
     int64_t T; int32_t d, E;
     float* logits_out; int32_t* expert; float* gate; float* lse; float* prob_sum;
+    int32_t k = 1; int64_t G = 0;   // choices per token; tokens per routing group (0: one group)
 };
 
 switch_status validate_route(const RouteArgs& a, const void* ws, size_t ws_bytes) {
     CHECK(check_TE(a.T, a.E));
+    CHECK(check_kG(a.T, a.E, a.k, a.G));
     const bool tok = a.T > 0;
-    NONNULL_IF(tok, a.expert); NONNULL_IF(tok, a.gate); NONNULL_IF(tok, a.lse); NONNULL(a.prob_sum);
+    NONNULL_IF(tok, a.expert); NONNULL_IF(tok, a.gate); NONNULL_IF(tok, a.lse);
+    NONNULL_IF(group_count(a.T, a.G) > 0, a.prob_sum);
     ALIGNED4(a.expert); ALIGNED4(a.gate); ALIGNED4(a.lse); ALIGNED4(a.prob_sum); ALIGNED4(a.logits_out);
     ALIGNED4(a.logits_in);
     if (!a.logits_in) {
@@ -159,6 +188,10 @@ switch_status validate_route(const RouteArgs& a, const void* ws, size_t ws_bytes
 
 switch_status run_route(const RouteArgs& a, void* ws, hipStream_t s) {
     const int T = (int)a.T, E = a.E;
+    // with routing groups the partial rows cover 64 tokens each and are summed per group
+    const bool one = one_group(a.T, a.G);
+    const int ng = (int)group_count(a.T, a.G);
+    const int rows_per_group = one ? 0 : (int)(a.G / 64);
     Carver c{(char*)ws};
     const float* logits = a.logits_in;
     if (!logits) {
@@ -169,39 +202,50 @@ switch_status run_route(const RouteArgs& a, void* ws, hipStream_t s) {
             const int nblk = T > 0 ? router_fused_blocks(T) : 0;
             if (T > 0)
                 LAUNCH(K_RFUSED, "router_fused", s,
-                       launch_router_fused(a.x, wr3, a.b_r, T, a.d, E, a.logits_out, a.expert, a.gate, a.lse, part, s));
-            LAUNCH(K_RREDUCE, "router_reduce", s, launch_router_reduce(part, nblk, E, a.prob_sum, s));
+                       launch_router_fused(a.x, wr3, a.b_r, T, a.d, E, a.k, a.logits_out, a.expert, a.gate, a.lse,
+                                           part, s));
+            LAUNCH(K_RREDUCE, "router_reduce", s,
+                   launch_router_reduce(part, one ? nblk : rows_per_group, ng, E, a.prob_sum, s));
             return SWITCH_OK;
         }
         float* z = a.logits_out ? a.logits_out : c.take<float>((size_t)T * E);
         if (T > 0) LAUNCH(K_RGEMM, "router_gemm", s, launch_router_gemm(a.x, wr3, a.b_r, z, T, a.d, E, s));
         logits = z;
     }
-    const int nblk = router_softmax_blocks(T, E);
+    const int nblk = one ? router_softmax_blocks(T, E) : router_softmax_blocks_grouped(T);
     float* part = c.take<float>(route_parts(T, E));
     if (T > 0)
-        LAUNCH(K_RSOFTMAX, "router_softmax", s, launch_router_softmax(logits, T, E, a.expert, a.gate, a.lse, part, s));
-    LAUNCH(K_RREDUCE, "router_reduce", s, launch_router_reduce(part, nblk, E, a.prob_sum, s));
+        LAUNCH(K_RSOFTMAX, "router_softmax", s,
+               launch_router_softmax(logits, T, E, a.k, !one, a.expert, a.gate, a.lse, part, s));
+    LAUNCH(K_RREDUCE, "router_reduce", s,
+           launch_router_reduce(part, one ? nblk : rows_per_group, ng, E, a.prob_sum, s));
     return SWITCH_OK;
 }
 
 struct DispatchArgs {
     const bf16_t* x; const int32_t* expert; int64_t T; int32_t d, E, C;
     int32_t* position; uint8_t* keep; int32_t* counts; int32_t* accepted; int32_t* slot_token; bf16_t* buf;
+    int32_t k = 1; int64_t G = 0; int32_t priority = 0;   // C is the capacity of one group
+    int32_t* slot = nullptr; int32_t* rows_total = nullptr;
 };
 
 switch_status validate_dispatch(const DispatchArgs& a, const void* ws, size_t ws_bytes) {
     CHECK(check_TE(a.T, a.E));
     CHECK(check_C(a.E, a.C));
+    CHECK(check_kG(a.T, a.E, a.k, a.G));
+    REQUIRE(a.priority == 0 || a.priority == 1, "priority must be 0 (token) or 1 (rank)");
+    const int64_t rows = buffer_rows(a.T, a.G, a.C);
+    SUPPORT((int64_t)a.E * rows < (int64_t(1) << 31), "E * groups * C must be < 2^31");
+    const bool grouped = group_count(a.T, a.G) > 0;
     REQUIRE(a.d >= 1, "d must be >= 1 (got %d)", a.d);
     SUPPORT(a.d % 8 == 0, "d must be a multiple of 8 (got %d)", a.d);
     const bool tok = a.T > 0;
     NONNULL_IF(tok, a.x); NONNULL_IF(tok, a.expert); NONNULL_IF(tok, a.position); NONNULL_IF(tok, a.keep);
-    NONNULL(a.counts); NONNULL(a.accepted);
-    NONNULL_IF(a.C > 0, a.buf);
+    NONNULL_IF(grouped, a.counts); NONNULL_IF(grouped, a.accepted);
+    NONNULL_IF(rows > 0, a.buf);
     ALIGNED16(a.x); ALIGNED16(a.buf); ALIGNED4(a.expert); ALIGNED4(a.position); ALIGNED4(a.counts);
-    ALIGNED4(a.accepted); ALIGNED4(a.slot_token);
-    const size_t need = dispatch_ws(a.T, a.E);
+    ALIGNED4(a.accepted); ALIGNED4(a.slot_token); ALIGNED4(a.slot); ALIGNED4(a.rows_total);
+    const size_t need = dispatch_ws(a.T, a.E, a.k, a.G);
     if (ws_bytes < need) return fail(SWITCH_E_WORKSPACE, "dispatch needs %zu workspace bytes, got %zu", need, ws_bytes);
     REQUIRE(need == 0 || ws != nullptr, "ws must not be NULL");
     REQUIRE(aligned(ws, kAlign), "ws must be %zu-byte aligned", kAlign);
@@ -209,17 +253,31 @@ switch_status validate_dispatch(const DispatchArgs& a, const void* ws, size_t ws
 }
 
 switch_status run_dispatch(const DispatchArgs& a, void* ws, hipStream_t s) {
-    const int T = (int)a.T;
+    const bool one = one_group(a.T, a.G);
+    const int N = (int)(a.T * a.k);
+    const int G = (int)std::max<int64_t>(group_tokens(a.T, a.G), 1);
+    const int ng = (int)group_count(a.T, a.G);
+    const int tile = scan_tile((int64_t)G * a.k, one);
+    const int ntiles = scan_tiles(N, tile);
+    const int tpg = one ? ntiles : G * a.k / tile;
+    const int rows = (int)buffer_rows(a.T, a.G, a.C);
     Carver c{(char*)ws};
-    const int ntiles = scan_tiles(T);
     int32_t* tile_counts = c.take<int32_t>((size_t)ntiles * a.E);
-    if (T > 0)
-        LAUNCH(K_SCAN_LOCAL, "scan_local", s, launch_scan_local(a.expert, T, a.E, a.position, tile_counts, s));
+    int32_t* group_base = one ? nullptr : c.take<int32_t>((size_t)ng * a.E);
+    int32_t* rows_total = a.rows_total;
+    if (!one) {
+        int32_t* own = c.take<int32_t>((size_t)a.E);
+        if (!rows_total) rows_total = own;
+    }
+    if (N > 0)
+        LAUNCH(K_SCAN_LOCAL, "scan_local", s,
+               launch_scan_local(a.expert, N, a.E, a.k, G, a.priority, tile, a.position, tile_counts, s));
     LAUNCH(K_SCAN_OFFSETS, "scan_offsets", s,
-           launch_scan_offsets(tile_counts, ntiles, a.E, a.C, a.counts, a.accepted, s));
+           launch_scan_offsets(tile_counts, ntiles, tpg, ng, a.E, a.C, a.counts, a.accepted, group_base, rows_total,
+                               s));
     LAUNCH(K_GATHER, "gather", s,
-           launch_gather(a.x, a.expert, tile_counts, a.accepted, T, a.d, a.E, a.C, a.position, a.keep,
-                         a.slot_token, a.buf, s));
+           launch_gather(a.x, a.expert, tile_counts, group_base, one ? a.accepted : rows_total, N, a.d, a.E, a.k, G,
+                         a.priority, tile, a.C, rows, a.position, a.keep, a.slot, a.slot_token, a.buf, s));
     return SWITCH_OK;
 }
 
@@ -260,11 +318,13 @@ switch_status run_ffn(const FfnArgs& a, void* ws, hipStream_t s) {
 struct CombineArgs {
     const float* y; const int32_t* expert; const int32_t* position; const uint8_t* keep; const float* gate;
     const bf16_t* residual; int64_t T; int32_t d, E, C; bf16_t* out;
+    int32_t k = 1;   // choices per token; `position` holds buffer rows, C the rows per expert
 };
 
 switch_status validate_combine(const CombineArgs& a) {
     CHECK(check_TE(a.T, a.E));
     CHECK(check_C(a.E, a.C));
+    CHECK(check_kG(a.T, a.E, a.k, 0));
     REQUIRE(a.d >= 1, "d must be >= 1 (got %d)", a.d);
     SUPPORT(a.d % 8 == 0, "d must be a multiple of 8 (got %d)", a.d);
     const bool tok = a.T > 0;
@@ -280,7 +340,7 @@ switch_status validate_combine(const CombineArgs& a) {
 
 switch_status run_combine(const CombineArgs& a, hipStream_t s) {
     LAUNCH(K_COMBINE, "combine", s,
-           launch_combine(a.y, a.expert, a.position, a.keep, a.gate, a.residual, a.T, a.d, a.E, a.C, a.out, s));
+           launch_combine(a.y, a.expert, a.position, a.keep, a.gate, a.residual, a.T, a.d, a.E, a.k, a.C, a.out, s));
     return SWITCH_OK;
 }
 
@@ -288,12 +348,16 @@ struct AuxArgs {
     const int32_t* counts; const float* prob_sum; const float* logits; const float* lse;
     int64_t T; int32_t E; float alpha; float* f; float* P; float* loss; float* dlogits;
     float beta; float* z_loss;   // router z-loss (optional, z_loss == NULL: not computed)
+    int32_t k = 1; int64_t G = 0;   // counts, prob_sum, f, P are [groups, E]
 };
 
 switch_status validate_aux(const AuxArgs& a) {
     CHECK(check_TE(a.T, a.E));
+    CHECK(check_kG(a.T, a.E, a.k, a.G));
     REQUIRE(std::isfinite(a.alpha), "alpha must be finite");
-    NONNULL(a.counts); NONNULL(a.prob_sum); NONNULL(a.f); NONNULL(a.P); NONNULL(a.loss);
+    const bool grouped = group_count(a.T, a.G) > 0;
+    NONNULL_IF(grouped, a.counts); NONNULL_IF(grouped, a.prob_sum); NONNULL_IF(grouped, a.f);
+    NONNULL_IF(grouped, a.P); NONNULL(a.loss);
     if (a.dlogits && a.T > 0) { NONNULL(a.logits); NONNULL(a.lse); }
     if (a.z_loss && a.T > 0) NONNULL(a.lse);
     REQUIRE(std::isfinite(a.beta), "beta must be finite");
@@ -304,12 +368,15 @@ switch_status validate_aux(const AuxArgs& a) {
 }
 
 switch_status run_aux(const AuxArgs& a, hipStream_t s) {
+    const int64_t Gt = group_tokens(a.T, a.G);
     LAUNCH(K_AUX_STATS, "aux_stats", s,
-           launch_aux_stats(a.counts, a.prob_sum, a.T, a.E, a.alpha, a.f, a.P, a.loss, s));
+           launch_aux_stats(a.counts, a.prob_sum, Gt, (int)group_count(a.T, a.G), a.E, a.k, a.alpha, a.f, a.P,
+                            a.loss, s));
     if (a.z_loss) LAUNCH(K_Z_LOSS, "z_loss", s, launch_z_loss(a.lse, a.T, a.beta, a.z_loss, s));
     if (a.dlogits && a.T > 0)
         LAUNCH(K_AUX_GRAD, "aux_grad", s,
-               launch_aux_grad(a.logits, a.lse, a.f, a.T, a.E, a.alpha, a.z_loss ? a.beta : 0.f, 0, a.dlogits, s));
+               launch_aux_grad(a.logits, a.lse, a.f, a.T, Gt, a.E, a.alpha, a.z_loss ? a.beta : 0.f, 0, a.dlogits,
+                               s));
     return SWITCH_OK;
 }
 
@@ -372,7 +439,12 @@ size_t switch_route_workspace_bytes(int64_t T, int32_t d, int32_t E) {
 }
 size_t switch_dispatch_workspace_bytes(int64_t T, int32_t E) {
     if (T < 0 || E < 1 || E > 4096 || T >= (int64_t(1) << 31)) return 0;
-    return dispatch_ws(T, E);
+    return dispatch_ws(T, E, 1, 0);
+}
+size_t switch_dispatch_workspace_bytes_ex(int64_t T, int32_t E, int32_t k, int64_t group) {
+    if (T < 0 || E < 1 || E > 4096 || k < 1 || k > kMaxTopK || group < 0 || T * k >= (int64_t(1) << 31)) return 0;
+    if (!one_group(T, group) && (T % group != 0)) return 0;
+    return dispatch_ws(T, E, k, group);
 }
 size_t switch_expert_ffn_workspace_bytes(int32_t E, int32_t C, int32_t d_ff) {
     if (E < 1 || C < 0 || d_ff < 0) return 0;
@@ -380,19 +452,34 @@ size_t switch_expert_ffn_workspace_bytes(int32_t E, int32_t C, int32_t d_ff) {
 }
 size_t switch_aux_loss_workspace_bytes(int64_t, int32_t) { return 0; }
 
-static size_t layer_ws(int64_t T, int32_t d, int32_t d_ff, int32_t E, int32_t C) {
-    size_t n = route_ws(T, d, E, true) + dispatch_ws(T, E) + ffn_ws(E, C, d_ff);
+static size_t layer_ws(int64_t T, int32_t d, int32_t d_ff, int32_t E, int32_t C, int32_t k, int64_t G) {
+    const int64_t rows = buffer_rows(T, G, C);
+    const int64_t ng = group_count(T, G);
+    size_t n = route_ws(T, d, E, true) + dispatch_ws(T, E, k, G) + ffn_ws(E, (int32_t)rows, d_ff);
     n += up((size_t)T * E * sizeof(float));          // logits
     n += up((size_t)T * sizeof(float));              // lse
-    n += up((size_t)E * sizeof(float));              // prob_sum
-    n += up((size_t)E * C * d * sizeof(bf16_t));     // buf
-    n += up((size_t)E * C * d * sizeof(float));      // y
+    n += up((size_t)ng * E * sizeof(float));         // prob_sum
+    n += up((size_t)E * rows * d * sizeof(bf16_t));  // buf
+    n += up((size_t)E * rows * d * sizeof(float));   // y
+    if (!one_group(T, G)) {
+        n += up((size_t)T * k * sizeof(int32_t));    // slot
+        n += up((size_t)E * sizeof(int32_t));        // accepted rows per expert
+    }
     return n;
 }
 
 size_t switch_workspace_bytes(int64_t T, int32_t d, int32_t d_ff, int32_t E, int32_t C) {
     if (T < 0 || d < 0 || d_ff < 0 || E < 1 || E > 4096 || C < 0 || T >= (int64_t(1) << 31)) return 0;
-    return layer_ws(T, d, d_ff, E, C);
+    return layer_ws(T, d, d_ff, E, C, 1, 0);
+}
+
+size_t switch_workspace_bytes_ex(int64_t T, int32_t d, int32_t d_ff, int32_t E, int32_t C, int32_t k,
+                                 int64_t group) {
+    if (T < 0 || d < 0 || d_ff < 0 || E < 1 || E > 4096 || C < 0 || T >= (int64_t(1) << 31)) return 0;
+    if (k < 1 || k > kMaxTopK || group < 0 || T * k >= (int64_t(1) << 31)) return 0;
+    if (!one_group(T, group) && T % group != 0) return 0;
+    if ((int64_t)E * buffer_rows(T, group, C) >= (int64_t(1) << 31)) return 0;
+    return layer_ws(T, d, d_ff, E, C, k, group);
 }
 
 const char* switch_status_string(switch_status s) {
@@ -415,6 +502,49 @@ switch_status switch_route(const switch_bf16* x, const float* w_r, const float* 
     RouteArgs a{x, w_r, b_r, logits_in, T, d, E, logits_out, expert, gate, lse, prob_sum};
     CHECK(validate_route(a, ws, ws_bytes));
     return run_route(a, ws, (hipStream_t)stream);
+}
+
+switch_status switch_route_ex(const switch_bf16* x, const float* w_r, const float* b_r, const float* logits_in,
+                              int64_t T, int32_t d, int32_t E, int32_t k, int64_t group, float* logits_out,
+                              int32_t* expert, float* gate, float* lse, float* prob_sum, void* ws, size_t ws_bytes,
+                              void* stream) {
+    g_err.clear();
+    RouteArgs a{x, w_r, b_r, logits_in, T, d, E, logits_out, expert, gate, lse, prob_sum, k, group};
+    CHECK(validate_route(a, ws, ws_bytes));
+    return run_route(a, ws, (hipStream_t)stream);
+}
+
+switch_status switch_dispatch_ex(const switch_bf16* x, const int32_t* expert, int64_t T, int32_t d, int32_t E,
+                                 int32_t k, int64_t group, int32_t C, int32_t priority, int32_t* position,
+                                 uint8_t* keep, int32_t* slot, int32_t* counts, int32_t* accepted,
+                                 int32_t* accepted_total, int32_t* slot_token, switch_bf16* buf, void* ws,
+                                 size_t ws_bytes, void* stream) {
+    g_err.clear();
+    DispatchArgs a{x, expert, T, d, E, C, position, keep, counts, accepted, slot_token, buf,
+                   k, group, priority, slot, accepted_total};
+    CHECK(validate_dispatch(a, ws, ws_bytes));
+    REQUIRE(one_group(T, group) || accepted_total != nullptr || group_count(T, group) == 0,
+            "accepted_total must not be NULL with several routing groups");
+    NONNULL_IF(T > 0 && !one_group(T, group), slot);
+    return run_dispatch(a, ws, (hipStream_t)stream);
+}
+
+switch_status switch_combine_ex(const float* y, const int32_t* expert, const int32_t* slot, const uint8_t* keep,
+                                const float* gate, const switch_bf16* residual, int64_t T, int32_t d, int32_t E,
+                                int32_t k, int32_t rows, switch_bf16* out, void* stream) {
+    g_err.clear();
+    CombineArgs a{y, expert, slot, keep, gate, residual, T, d, E, rows, out, k};
+    CHECK(validate_combine(a));
+    return run_combine(a, (hipStream_t)stream);
+}
+
+switch_status switch_aux_loss_ex(const int32_t* counts, const float* prob_sum, const float* logits, const float* lse,
+                                 int64_t T, int32_t E, int32_t k, int64_t group, float alpha, float* f, float* P,
+                                 float* loss, float* dlogits, void* stream) {
+    g_err.clear();
+    AuxArgs a{counts, prob_sum, logits, lse, T, E, alpha, f, P, loss, dlogits, 0.f, nullptr, k, group};
+    CHECK(validate_aux(a));
+    return run_aux(a, (hipStream_t)stream);
 }
 
 switch_status switch_dispatch(const switch_bf16* x, const int32_t* expert, int64_t T, int32_t d, int32_t E,
@@ -467,7 +597,8 @@ switch_status switch_router_z_loss(const float* lse, const float* logits, int64_
     hipStream_t s = (hipStream_t)stream;
     LAUNCH(K_Z_LOSS, "z_loss", s, launch_z_loss(lse, T, beta, z_loss, s));
     if (dlogits && T > 0)
-        LAUNCH(K_AUX_GRAD, "aux_grad", s, launch_aux_grad(logits, lse, nullptr, T, E, 0.f, beta, accumulate, dlogits, s));
+        LAUNCH(K_AUX_GRAD, "aux_grad", s,
+               launch_aux_grad(logits, lse, nullptr, T, T, E, 0.f, beta, accumulate, dlogits, s));
     return SWITCH_OK;
 }
 
@@ -476,40 +607,61 @@ switch_status switch_layer_fwd(const switch_layer_args* la, void* ws, size_t ws_
     if (!la) return fail(SWITCH_E_INVALID, "args must not be NULL");
     const switch_layer_args& L = *la;
     hipStream_t s = (hipStream_t)stream;
+    const int32_t k = L.k == 0 ? 1 : L.k;
+    const int64_t G = L.group;
     CHECK(check_TE(L.T, L.E));
     CHECK(check_C(L.E, L.C));
+    CHECK(check_kG(L.T, L.E, k, G));
     REQUIRE(L.d >= 1 && L.d_ff >= 1, "d and d_ff must be >= 1");
     SUPPORT(L.d % 64 == 0 && L.d_ff % 64 == 0, "d and d_ff must be multiples of 64 (got %d, %d)", L.d, L.d_ff);
     REQUIRE(L.residual == 0 || L.residual == 1, "residual must be 0 or 1");
-    const size_t need = layer_ws(L.T, L.d, L.d_ff, L.E, L.C);
+    const int64_t rows64 = buffer_rows(L.T, G, L.C);
+    SUPPORT((int64_t)L.E * rows64 < (int64_t(1) << 31), "E * groups * C must be < 2^31");
+    const int32_t rows = (int32_t)rows64;
+    const bool one = one_group(L.T, G);
+    const size_t need = layer_ws(L.T, L.d, L.d_ff, L.E, L.C, k, G);
     if (ws_bytes < need) return fail(SWITCH_E_WORKSPACE, "layer needs %zu workspace bytes, got %zu", need, ws_bytes);
     REQUIRE(ws != nullptr, "ws must not be NULL");
     REQUIRE(aligned(ws, kAlign), "ws must be %zu-byte aligned", kAlign);
     Carver c{(char*)ws};
     char* route_space = c.take<char>(route_ws(L.T, L.d, L.E, true));
-    char* dispatch_space = c.take<char>(dispatch_ws(L.T, L.E));
-    char* ffn_space = c.take<char>(ffn_ws(L.E, L.C, L.d_ff));
+    char* dispatch_space = c.take<char>(dispatch_ws(L.T, L.E, k, G));
+    char* ffn_space = c.take<char>(ffn_ws(L.E, rows, L.d_ff));
     float* logits = c.take<float>((size_t)L.T * L.E);
     float* lse = c.take<float>((size_t)L.T);
-    float* prob_sum = c.take<float>((size_t)L.E);
-    bf16_t* buf = c.take<bf16_t>((size_t)L.E * L.C * L.d);
-    float* y = c.take<float>((size_t)L.E * L.C * L.d);
+    float* prob_sum = c.take<float>((size_t)group_count(L.T, G) * L.E);
+    bf16_t* buf = c.take<bf16_t>((size_t)L.E * rows * L.d);
+    float* y = c.take<float>((size_t)L.E * rows * L.d);
+    int32_t* slot = nullptr;
+    int32_t* acc_total = nullptr;
+    if (!one) {
+        slot = c.take<int32_t>((size_t)L.T * k);
+        acc_total = c.take<int32_t>((size_t)L.E);
+    }
     if (L.logits) logits = L.logits;
     else if (!L.dlogits && route_fused(L.E)) logits = nullptr;   // the fused router needs no logits array
     if (L.lse) lse = L.lse;
     if (L.prob_sum) prob_sum = L.prob_sum;
     if (L.buf) buf = L.buf;
     if (L.y) y = L.y;
+    if (L.slot) slot = L.slot;
+    if (L.accepted_total) acc_total = L.accepted_total;
+    // one group: the buffer row is the position, and accepted is per expert
+    const int32_t* rows_of = one ? L.position : slot;
+    const int32_t* filled = one ? L.accepted : acc_total;
 
-    RouteArgs ra{L.x, L.w_r, L.b_r, nullptr, L.T, L.d, L.E, logits, L.expert, L.gate, lse, prob_sum};
-    DispatchArgs da{L.x, L.expert, L.T, L.d, L.E, L.C, L.position, L.keep, L.counts, L.accepted, L.slot_token, buf};
-    FfnArgs fa{buf, L.accepted, L.w1, L.w2, L.E, L.C, L.d, L.d_ff, y};
-    CombineArgs ca{y, L.expert, L.position, L.keep, L.gate, L.residual ? L.x : nullptr, L.T, L.d, L.E, L.C, L.out};
-    AuxArgs xa{L.counts, prob_sum, logits, lse, L.T, L.E, L.alpha, L.f, L.P, L.loss, L.dlogits, L.z_beta, L.z_loss};
+    RouteArgs ra{L.x, L.w_r, L.b_r, nullptr, L.T, L.d, L.E, logits, L.expert, L.gate, lse, prob_sum, k, G};
+    DispatchArgs da{L.x, L.expert, L.T, L.d, L.E, L.C, L.position, L.keep, L.counts, L.accepted, L.slot_token, buf,
+                    k, G, L.priority, slot, acc_total};
+    FfnArgs fa{buf, filled, L.w1, L.w2, L.E, rows, L.d, L.d_ff, y};
+    CombineArgs ca{y, L.expert, rows_of, L.keep, L.gate, L.residual ? L.x : nullptr, L.T, L.d, L.E, rows, L.out, k};
+    AuxArgs xa{L.counts, prob_sum, logits, lse, L.T, L.E, L.alpha, L.f, L.P, L.loss, L.dlogits, L.z_beta, L.z_loss,
+               k, G};
     // validate everything before the first launch
     CHECK(validate_route(ra, route_space, route_ws(L.T, L.d, L.E, logits != nullptr)));
-    CHECK(validate_dispatch(da, dispatch_space, dispatch_ws(L.T, L.E)));
-    CHECK(validate_ffn(fa, ffn_space, ffn_ws(L.E, L.C, L.d_ff)));
+    CHECK(validate_dispatch(da, dispatch_space, dispatch_ws(L.T, L.E, k, G)));
+    if (L.T > 0 && group_count(L.T, G) > 0) NONNULL(filled);
+    CHECK(validate_ffn(fa, ffn_space, ffn_ws(L.E, rows, L.d_ff)));
     CHECK(validate_combine(ca));
     CHECK(validate_aux(xa));
     CHECK(run_route(ra, route_space, s));

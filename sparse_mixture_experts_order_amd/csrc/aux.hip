@@ -12,17 +12,22 @@
 namespace swmoe {
 
 // One workgroup: f, P and the loss, reduced in fp64 in a fixed tree order.
+// Routing groups: counts and prob_sum are [ngroups, E]; group g has G tokens
+// and k choices per token, f_ge = counts_ge / (k G), P_ge = prob_sum_ge / G and
+// the loss is alpha E times the mean over groups of sum_e f_ge P_ge.  One
+// group of T tokens with k = 1 is the Switch layer's loss.
 __global__ __launch_bounds__(1024) void aux_stats(const int32_t* __restrict__ counts,
-                                                  const float* __restrict__ prob_sum, int64_t T, int E,
-                                                  float alpha, float* __restrict__ f, float* __restrict__ P,
+                                                  const float* __restrict__ prob_sum, int64_t G, int ngroups, int E,
+                                                  int k, float alpha, float* __restrict__ f, float* __restrict__ P,
                                                   float* __restrict__ loss) {
     __shared__ double red[1024];
     double acc = 0.0;
-    for (int e = threadIdx.x; e < E; e += 1024) {
-        const double fe = T > 0 ? (double)counts[e] / (double)T : 0.0;
-        const double pe = T > 0 ? (double)prob_sum[e] / (double)T : 0.0;
-        f[e] = (float)fe;
-        P[e] = (float)pe;
+    const int64_t n = (int64_t)ngroups * E;
+    for (int64_t i = threadIdx.x; i < n; i += 1024) {
+        const double fe = G > 0 ? (double)counts[i] / ((double)k * (double)G) : 0.0;
+        const double pe = G > 0 ? (double)prob_sum[i] / (double)G : 0.0;
+        f[i] = (float)fe;
+        P[i] = (float)pe;
         acc += fe * pe;
     }
     red[threadIdx.x] = acc;
@@ -31,7 +36,7 @@ __global__ __launch_bounds__(1024) void aux_stats(const int32_t* __restrict__ co
         if ((int)threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
         __syncthreads();
     }
-    if (threadIdx.x == 0) loss[0] = (float)((double)alpha * (double)E * red[0]);
+    if (threadIdx.x == 0) loss[0] = ngroups > 0 ? (float)((double)alpha * (double)E * red[0] / (double)ngroups) : 0.f;
 }
 
 // Router z-loss (ST-MoE, as restated in "MoE routing load collapse",
@@ -57,16 +62,18 @@ __global__ __launch_bounds__(1024) void z_loss_reduce(const float* __restrict__ 
 // Gradient with respect to the logits of  c_aux-weighted aux loss and
 // c_z-weighted z-loss, with p_tj = exp(z_tj - lse_t):
 //   G_tj = p_tj * (c_aux (f_j - sum_e f_e p_te) + c_z lse_t)
-// c_aux = alpha E / T (aux, f held constant), c_z = 2 beta / T (z-loss).
+// c_aux = alpha E / T (aux, f held constant; f is the row of the token's
+// routing group of G tokens), c_z = 2 beta / T (z-loss).
 // One wave per token row; lane j holds experts j, j+64, ...  With
 // `accumulate` the result is added to dlogits instead of stored.
 template <int NCH>
 __global__ __launch_bounds__(256) void aux_grad(const float* __restrict__ logits, const float* __restrict__ lse,
-                                                const float* __restrict__ f, int64_t T, int E, float c_aux,
+                                                const float* __restrict__ f, int64_t T, int64_t G, int E, float c_aux,
                                                 float c_z, int accumulate, float* __restrict__ dlogits) {
     const int lane = threadIdx.x & 63;
     const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
+    if (f) f += (t / G) * E;
     const float* row = logits + t * E;
     const float l = lse[t];
     float p[NCH], fr[NCH];
@@ -91,9 +98,9 @@ __global__ __launch_bounds__(256) void aux_grad(const float* __restrict__ logits
     }
 }
 
-hipError_t launch_aux_stats(const int32_t* counts, const float* prob_sum, int64_t T, int E, float alpha, float* f,
-                            float* P, float* loss, hipStream_t s) {
-    hipLaunchKernelGGL(aux_stats, dim3(1), dim3(1024), 0, s, counts, prob_sum, T, E, alpha, f, P, loss);
+hipError_t launch_aux_stats(const int32_t* counts, const float* prob_sum, int64_t G, int ngroups, int E, int k,
+                            float alpha, float* f, float* P, float* loss, hipStream_t s) {
+    hipLaunchKernelGGL(aux_stats, dim3(1), dim3(1024), 0, s, counts, prob_sum, G, ngroups, E, k, alpha, f, P, loss);
     return hipGetLastError();
 }
 
@@ -102,16 +109,16 @@ hipError_t launch_z_loss(const float* lse, int64_t T, float beta, float* z_loss,
     return hipGetLastError();
 }
 
-hipError_t launch_aux_grad(const float* logits, const float* lse, const float* f, int64_t T, int E, float alpha,
-                           float beta, int accumulate, float* dlogits, hipStream_t s) {
+hipError_t launch_aux_grad(const float* logits, const float* lse, const float* f, int64_t T, int64_t G, int E,
+                           float alpha, float beta, int accumulate, float* dlogits, hipStream_t s) {
     if (T == 0) return hipSuccess;
     const float c_aux = f ? (float)((double)alpha * (double)E / (double)T) : 0.f;
     const float c_z = (float)(2.0 * (double)beta / (double)T);
     const unsigned grid = (unsigned)((T + 3) / 4);
     const int nch = (E + 63) / 64;
 #define SWMOE_GRAD(N)                                                                                          \
-    hipLaunchKernelGGL(aux_grad<N>, dim3(grid), dim3(256), 0, s, logits, lse, f, T, E, c_aux, c_z, accumulate, \
-                       dlogits)
+    hipLaunchKernelGGL(aux_grad<N>, dim3(grid), dim3(256), 0, s, logits, lse, f, T, std::max<int64_t>(G, 1), E, \
+                       c_aux, c_z, accumulate, dlogits)
     if (nch <= 1) SWMOE_GRAD(1);
     else if (nch <= 2) SWMOE_GRAD(2);
     else if (nch <= 4) SWMOE_GRAD(4);

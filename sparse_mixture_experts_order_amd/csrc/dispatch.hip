@@ -1,41 +1,68 @@
-// Token-order slot scan and dispatch gather.
+// Token-order slot scan and dispatch gather, with routing groups and top-k.
 //
 // Sources: "MoE routing load collapse" (zffjzz.top), "official code reading
 // route": a token's slot is the running count of earlier tokens that chose the
 // same expert (a cumulative sum along the sequence, not an ordering by
 // probability), and the raw choice is kept apart from the capacity mask;
-// "042 Switch Transformer" (wq-win.github.io) sec. 3: truncate the assignment
-// by expert capacity, build the dispatch tensor, cast to bf16 and send tokens
-// to their expert.
+// "evaluation protocol": the capacity limit applies to each 64-row batch on
+// its own.  "042 Switch Transformer" (wq-win.github.io) sec. 3: truncate the
+// assignment by expert capacity, build the dispatch tensor, cast to bf16 and
+// send tokens to their expert.  "Mixture of experts" (world.lapla.si), "full
+// means turned back": with k choices per token the capacity scales with k.
+//
+// The scan runs over the T*k assignments (token t, choice i) in scan order:
+// inside each routing group of G tokens either (t, i) lexicographic ("token"
+// priority, the same as the [T, k] output layout) or (i, t) ("rank" priority:
+// all first choices of the group before any second choice).  With k = 1 and
+// one group this is the plain token order of the Switch layer.
 //
 // Three launches, no host synchronisation:
-//   scan_local   per tile of 256 tokens: each token's rank among the earlier
-//                tokens of its tile with the same expert (wave ballots for
-//                the match, then the tile's waves in order through an LDS
-//                histogram), and the tile's per-expert counts.
-//   scan_offsets per expert: exclusive prefix of the tile counts over tiles;
-//                raw counts and accepted = min(counts, C).
-//   gather       per token: final position and keep flag, slot_token, and the
-//                row copy x[t] -> buf[e, pos]; extra workgroups zero the empty
-//                slots.
+//   scan_local   per tile of 64*W assignments in scan order: each one's rank
+//                among the earlier assignments of its tile with the same
+//                expert (wave ballots for the match, then the tile's waves in
+//                order through an LDS histogram), and the tile's per-expert
+//                counts.  Tiles never straddle a group.
+//   scan_offsets per expert: exclusive prefix of the tile counts over the
+//                tiles of each group (a segmented scan); per group the raw
+//                counts, accepted = min(counts, C), and the first buffer row
+//                of the group (accepted rows of the earlier groups).
+//   gather       per assignment: in-group position, keep flag, buffer row,
+//                slot_token and the row copy x[t] -> buf[e, row]; extra
+//                workgroups zero the empty rows.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace swmoe {
 
-constexpr int SCAN_TILE = 256;
+// scan index j -> [T, k] output index, and back.  G: tokens per group, k:
+// choices per token, rank: 1 for (i, t) order inside a group.
+__device__ __forceinline__ int out_of_scan(int j, int k, int G, int rank) {
+    if (!rank || k == 1) return j;
+    const int Gk = G * k;
+    const int g = j / Gk, r = j - g * Gk;
+    const int i = r / G, u = r - i * G;
+    return (g * G + u) * k + i;
+}
+__device__ __forceinline__ int scan_of_out(int o, int k, int G, int rank) {
+    if (!rank || k == 1) return o;
+    const int t = o / k, i = o - t * k;
+    const int g = t / G, u = t - g * G;
+    return g * G * k + i * G + u;
+}
 
-__global__ __launch_bounds__(256) void scan_local(const int32_t* __restrict__ expert, int T, int E,
-                                                  int nbits, int32_t* __restrict__ local_rank,
-                                                  int32_t* __restrict__ tile_counts) {
+template <int W>
+__global__ __launch_bounds__(64 * W) void scan_local(const int32_t* __restrict__ expert, int N, int E, int nbits,
+                                                     int k, int G, int rank, int32_t* __restrict__ local_rank,
+                                                     int32_t* __restrict__ tile_counts) {
     extern __shared__ int32_t hist[];  // [E]
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int t = blockIdx.x * SCAN_TILE + threadIdx.x;
-    for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
+    const int j = blockIdx.x * (64 * W) + threadIdx.x;
+    for (int e = threadIdx.x; e < E; e += 64 * W) hist[e] = 0;
 
-    // ids outside [0, E) are outside the contract: such tokens are not counted
-    // and never dispatched (gather marks them dropped with position -1)
-    const int eid = t < T ? expert[t] : -1;
+    // ids outside [0, E) are outside the contract: such assignments are not
+    // counted and never dispatched (gather marks them dropped with position -1)
+    const int o = j < N ? out_of_scan(j, k, G, rank) : 0;
+    const int eid = j < N ? expert[o] : -1;
     const bool valid = eid >= 0 && eid < E;
     const int e = valid ? eid : 0;
     // lanes of this wave holding the same expert id ("match any")
@@ -50,87 +77,126 @@ __global__ __launch_bounds__(256) void scan_local(const int32_t* __restrict__ ex
     const int group = __popcll(peers);
     const bool leader = valid && rank_in_wave == 0;
     __syncthreads();
-    // waves in token order: read the running count, then the group leader adds the group size
-    for (int w = 0; w < 4; ++w) {
-        if (wave == w && valid) {
-            const int base = hist[e];
-            local_rank[t] = base + rank_in_wave;
-        }
-        __syncthreads();
+    // waves in scan order: read the running count, then the group leader adds the group size
+    for (int w = 0; w < W; ++w) {
+        if (wave == w && valid) local_rank[o] = hist[e] + rank_in_wave;
+        if constexpr (W > 1) __syncthreads();
         if (wave == w && leader) hist[e] += group;
-        __syncthreads();
+        if constexpr (W > 1) __syncthreads();
     }
-    for (int i = threadIdx.x; i < E; i += 256) tile_counts[(size_t)blockIdx.x * E + i] = hist[i];
+    if constexpr (W == 1) __syncthreads();
+    for (int i = threadIdx.x; i < E; i += 64 * W) tile_counts[(size_t)blockIdx.x * E + i] = hist[i];
 }
 
-// tile_counts[b][e] becomes the exclusive prefix over tiles b' < b.  One wave
-// per expert: lanes take 64 tiles at a time, a wave prefix sum (shuffles)
-// ranks them and the running total carries into the next 64.
-__global__ __launch_bounds__(256) void scan_offsets(int32_t* __restrict__ tile_counts, int ntiles, int E,
-                                                    int C, int32_t* __restrict__ counts,
-                                                    int32_t* __restrict__ accepted) {
+// tile_counts[b][e] becomes the exclusive prefix over the earlier tiles of
+// b's group (tpg tiles per group).  One wave per expert: lanes take 64 tiles
+// at a time; a segmented wave scan (shuffles, restarting at each group's
+// first tile) ranks them and the open group's total carries into the next 64.
+// At each group's last tile: counts, accepted = min(counts, C) and, with
+// group_base, the group's first buffer row (a plain wave scan over the
+// accepted counts of the groups that end in these 64 tiles).  rows_total[e]
+// (optional) gets the accepted rows over all groups.
+__global__ __launch_bounds__(256) void scan_offsets(int32_t* __restrict__ tile_counts, int ntiles, int tpg,
+                                                    int ngroups, int E, int C, int32_t* __restrict__ counts,
+                                                    int32_t* __restrict__ accepted, int32_t* __restrict__ group_base,
+                                                    int32_t* __restrict__ rows_total) {
     const int lane = threadIdx.x & 63;
     const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (e >= E) return;
-    int run = 0;
+    int run = 0;    // count of the open group over the earlier chunks
+    int rows = 0;   // accepted rows of the finished groups
     for (int b0 = 0; b0 < ntiles; b0 += 64) {
         const int b = b0 + lane;
+        const bool in = b < ntiles;
         const size_t o = (size_t)b * E + e;
-        const int c = b < ntiles ? tile_counts[o] : 0;
-        int incl = c;
+        const int c = in ? tile_counts[o] : 0;
+        const int gi = b / tpg;
+        const int head = (b - gi * tpg) == 0;
+        const bool tail = in && ((b - gi * tpg) == tpg - 1 || b == ntiles - 1);
+        int v = c, f = head;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
-            const int v = __shfl_up(incl, off);
-            if (lane >= off) incl += v;
+            const int vu = __shfl_up(v, off);
+            const int fu = __shfl_up(f, off);
+            if (lane >= off && !f) { v += vu; f |= fu; }
         }
-        if (b < ntiles) tile_counts[o] = run + incl - c;
-        run += __shfl(incl, 63);
+        const int incl = v + (f ? 0 : run);
+        if (in) tile_counts[o] = incl - c;
+        const int acc = tail ? min(incl, C) : 0;
+        int a = acc;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int au = __shfl_up(a, off);
+            if (lane >= off) a += au;
+        }
+        if (tail) {
+            counts[(size_t)gi * E + e] = incl;
+            accepted[(size_t)gi * E + e] = acc;
+            if (group_base) group_base[(size_t)gi * E + e] = rows + a - acc;
+        }
+        rows += __shfl(a, 63);
+        run = __shfl((int)tail, 63) ? 0 : __shfl(incl, 63);
     }
-    if (lane == 0) {
-        counts[e] = run;
-        accepted[e] = min(run, C);
+    if (ntiles == 0 && lane == 0 && ngroups == 1) {   // no tokens, one group
+        counts[e] = 0;
+        accepted[e] = 0;
+        if (group_base) group_base[e] = 0;
     }
+    if (rows_total && lane == 0) rows_total[e] = rows;
 }
 
-// Workgroups [0, ntok_blocks) handle GATHER_TOK tokens each; the rest zero the
-// empty slots, GATHER_ROWS slot rows each.
+// Workgroups [0, ntok_blocks) handle GATHER_TOK assignments each (in [T, k]
+// order); the rest zero the empty rows, GATHER_ROWS rows each.  Buffer row of a
+// kept assignment: group_base[g][e] + position (position alone with one group).
 constexpr int GATHER_TOK = 16, GATHER_ROWS = 16;
 
 __global__ __launch_bounds__(256) void gather(const bf16_t* __restrict__ x, const int32_t* __restrict__ expert,
                                               const int32_t* __restrict__ offsets,
-                                              const int32_t* __restrict__ accepted, int T, int d, int E, int C,
-                                              int ntok_blocks, int32_t* __restrict__ position,
-                                              uint8_t* __restrict__ keep, int32_t* __restrict__ slot_token,
+                                              const int32_t* __restrict__ group_base,
+                                              const int32_t* __restrict__ rows_filled, int N, int d, int E, int k,
+                                              int G, int rank, int tile, int C, int rows, int ntok_blocks,
+                                              int32_t* __restrict__ position, uint8_t* __restrict__ keep,
+                                              int32_t* __restrict__ slot, int32_t* __restrict__ slot_token,
                                               bf16_t* __restrict__ buf) {
     __shared__ int s_dst[GATHER_TOK];
+    __shared__ int s_tok[GATHER_TOK];
     const int vpr = d >> 3;  // 16-byte vectors per row
     if ((int)blockIdx.x < ntok_blocks) {
-        const int t0 = blockIdx.x * GATHER_TOK;
+        const int o0 = blockIdx.x * GATHER_TOK;
         if (threadIdx.x < GATHER_TOK) {
-            const int t = t0 + threadIdx.x;
-            int dst = -1;
-            if (t < T && (expert[t] < 0 || expert[t] >= E)) {
-                position[t] = -1;
-                keep[t] = 0;
-            } else if (t < T) {
-                const int e = expert[t];
-                const int pos = offsets[(size_t)(t / SCAN_TILE) * E + e] + position[t];
-                const bool k = pos < C;
-                position[t] = pos;
-                keep[t] = k;
-                if (k) {
-                    dst = e * C + pos;
-                    if (slot_token) slot_token[dst] = t;
+            const int o = o0 + threadIdx.x;
+            int dst = -1, tok = 0;
+            if (o < N) {
+                const int e = expert[o];
+                tok = o / k;
+                if (e < 0 || e >= E) {
+                    position[o] = -1;
+                    keep[o] = 0;
+                    if (slot) slot[o] = -1;
+                } else {
+                    const int j = scan_of_out(o, k, G, rank);
+                    const int pos = offsets[(size_t)(j / tile) * E + e] + position[o];
+                    const bool kp = pos < C;
+                    int row = -1;
+                    position[o] = pos;
+                    keep[o] = kp;
+                    if (kp) {
+                        row = group_base ? group_base[(size_t)(tok / G) * E + e] + pos : pos;
+                        dst = e * rows + row;
+                        if (slot_token) slot_token[dst] = tok;
+                    }
+                    if (slot) slot[o] = row;
                 }
             }
             s_dst[threadIdx.x] = dst;
+            s_tok[threadIdx.x] = tok;
         }
         __syncthreads();
         for (int i = threadIdx.x; i < GATHER_TOK * vpr; i += 256) {
             const int r = i / vpr, v = i - r * vpr;
             const int dst = s_dst[r];
             if (dst < 0) continue;
-            const uint4 val = ((const uint4*)(x + (size_t)(t0 + r) * d))[v];
+            const uint4 val = ((const uint4*)(x + (size_t)s_tok[r] * d))[v];
             ((uint4*)(buf + (size_t)dst * d))[v] = val;
         }
     } else {
@@ -138,9 +204,9 @@ __global__ __launch_bounds__(256) void gather(const bf16_t* __restrict__ x, cons
         for (int i = threadIdx.x; i < GATHER_ROWS * vpr; i += 256) {
             const int r = i / vpr, v = i - r * vpr;
             const int row = row0 + r;
-            if (row >= E * C) break;
-            const int e = row / C, s = row - e * C;
-            if (s < accepted[e]) continue;
+            if (row >= E * rows) break;
+            const int e = row / rows, s = row - e * rows;
+            if (s < rows_filled[e]) continue;
             ((uint4*)(buf + (size_t)row * d))[v] = make_uint4(0, 0, 0, 0);
             if (v == 0 && slot_token) slot_token[row] = -1;
         }
@@ -148,33 +214,48 @@ __global__ __launch_bounds__(256) void gather(const bf16_t* __restrict__ x, cons
 }
 
 // ------------------------------------------------------------------ launchers
-int scan_tiles(int64_t T) { return (int)((T + SCAN_TILE - 1) / SCAN_TILE); }
+int scan_tile(int64_t group_assignments, bool one_group) {
+    if (one_group || group_assignments % 256 == 0) return 256;
+    return group_assignments % 128 == 0 ? 128 : 64;
+}
+int scan_tiles(int64_t N, int tile) { return (int)((N + tile - 1) / tile); }
 
-hipError_t launch_scan_local(const int32_t* expert, int T, int E, int32_t* local_rank, int32_t* tile_counts,
-                             hipStream_t s) {
+hipError_t launch_scan_local(const int32_t* expert, int N, int E, int k, int G, int rank, int tile,
+                             int32_t* local_rank, int32_t* tile_counts, hipStream_t s) {
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
-    hipLaunchKernelGGL(scan_local, dim3(scan_tiles(T)), dim3(256), (size_t)E * sizeof(int32_t), s, expert, T,
-                       E, nbits, local_rank, tile_counts);
+    const dim3 grid(scan_tiles(N, tile));
+    const size_t shm = (size_t)E * sizeof(int32_t);
+    if (tile == 256)
+        hipLaunchKernelGGL(scan_local<4>, grid, dim3(256), shm, s, expert, N, E, nbits, k, G, rank, local_rank,
+                           tile_counts);
+    else if (tile == 128)
+        hipLaunchKernelGGL(scan_local<2>, grid, dim3(128), shm, s, expert, N, E, nbits, k, G, rank, local_rank,
+                           tile_counts);
+    else
+        hipLaunchKernelGGL(scan_local<1>, grid, dim3(64), shm, s, expert, N, E, nbits, k, G, rank, local_rank,
+                           tile_counts);
     return hipGetLastError();
 }
 
-hipError_t launch_scan_offsets(int32_t* tile_counts, int ntiles, int E, int C, int32_t* counts,
-                               int32_t* accepted, hipStream_t s) {
-    hipLaunchKernelGGL(scan_offsets, dim3((E + 3) / 4), dim3(256), 0, s, tile_counts, ntiles, E, C, counts,
-                       accepted);
+hipError_t launch_scan_offsets(int32_t* tile_counts, int ntiles, int tiles_per_group, int ngroups, int E, int C,
+                               int32_t* counts, int32_t* accepted, int32_t* group_base, int32_t* rows_total,
+                               hipStream_t s) {
+    hipLaunchKernelGGL(scan_offsets, dim3((E + 3) / 4), dim3(256), 0, s, tile_counts, ntiles,
+                       std::max(tiles_per_group, 1), ngroups, E, C, counts, accepted, group_base, rows_total);
     return hipGetLastError();
 }
 
-hipError_t launch_gather(const bf16_t* x, const int32_t* expert, const int32_t* offsets, const int32_t* accepted,
-                         int T, int d, int E, int C, int32_t* position, uint8_t* keep, int32_t* slot_token,
-                         bf16_t* buf, hipStream_t s) {
-    const int ntok = (T + GATHER_TOK - 1) / GATHER_TOK;
-    const int64_t rows = (int64_t)E * C;
-    const int nzero = (int)((rows + GATHER_ROWS - 1) / GATHER_ROWS);
+hipError_t launch_gather(const bf16_t* x, const int32_t* expert, const int32_t* offsets, const int32_t* group_base,
+                         const int32_t* rows_filled, int N, int d, int E, int k, int G, int rank, int tile, int C,
+                         int rows, int32_t* position, uint8_t* keep, int32_t* slot, int32_t* slot_token, bf16_t* buf,
+                         hipStream_t s) {
+    const int ntok = (N + GATHER_TOK - 1) / GATHER_TOK;
+    const int64_t nrows = (int64_t)E * rows;
+    const int nzero = (int)((nrows + GATHER_ROWS - 1) / GATHER_ROWS);
     if (ntok + nzero == 0) return hipSuccess;
-    hipLaunchKernelGGL(gather, dim3(ntok + nzero), dim3(256), 0, s, x, expert, offsets, accepted, T, d, E, C,
-                       ntok, position, keep, slot_token, buf);
+    hipLaunchKernelGGL(gather, dim3(ntok + nzero), dim3(256), 0, s, x, expert, offsets, group_base, rows_filled, N, d,
+                       E, k, std::max(G, 1), rank, tile, C, rows, ntok, position, keep, slot, slot_token, buf);
     return hipGetLastError();
 }
 

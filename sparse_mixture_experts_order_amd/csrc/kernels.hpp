@@ -13,25 +13,30 @@ typedef uint16_t bf16_t;
 hipError_t launch_split_router_weights(const float* w_r, bf16_t* wr3, int d, int E, hipStream_t s);
 hipError_t launch_router_gemm(const bf16_t* x, const bf16_t* wr3, const float* b_r, float* logits, int T, int d,
                               int E, hipStream_t s);
+constexpr int kMaxTopK = 4;             // largest k the routers support
 int router_softmax_blocks(int64_t T, int E);
-hipError_t launch_router_softmax(const float* logits, int T, int E, int32_t* expert, float* gate, float* lse,
-                                 float* part, hipStream_t s);
-hipError_t launch_router_reduce(const float* part, int nblk, int E, float* prob_sum, hipStream_t s);
+int router_softmax_blocks_grouped(int64_t T);   // one partial row per 64 tokens
+hipError_t launch_router_softmax(const float* logits, int T, int E, int k, bool rows_of_64, int32_t* expert,
+                                 float* gate, float* lse, float* part, hipStream_t s);
+hipError_t launch_router_reduce(const float* part, int nblk, int ngroups, int E, float* prob_sum, hipStream_t s);
 constexpr int kRouterFusedMaxE = 256;
-int router_fused_blocks(int64_t T);
-hipError_t launch_router_fused(const bf16_t* x, const bf16_t* wr3, const float* b_r, int T, int d, int E,
+int router_fused_blocks(int64_t T);     // one partial row per 64 tokens
+hipError_t launch_router_fused(const bf16_t* x, const bf16_t* wr3, const float* b_r, int T, int d, int E, int k,
                                float* logits_out, int32_t* expert, float* gate, float* lse, float* part,
                                hipStream_t s);
 
 // dispatch.hip
-int scan_tiles(int64_t T);
-hipError_t launch_scan_local(const int32_t* expert, int T, int E, int32_t* local_rank, int32_t* tile_counts,
-                             hipStream_t s);
-hipError_t launch_scan_offsets(int32_t* tile_counts, int ntiles, int E, int C, int32_t* counts, int32_t* accepted,
+int scan_tile(int64_t group_assignments, bool one_group);   // 256, 128 or 64 assignments
+int scan_tiles(int64_t N, int tile);
+hipError_t launch_scan_local(const int32_t* expert, int N, int E, int k, int G, int rank, int tile,
+                             int32_t* local_rank, int32_t* tile_counts, hipStream_t s);
+hipError_t launch_scan_offsets(int32_t* tile_counts, int ntiles, int tiles_per_group, int ngroups, int E, int C,
+                               int32_t* counts, int32_t* accepted, int32_t* group_base, int32_t* rows_total,
                                hipStream_t s);
-hipError_t launch_gather(const bf16_t* x, const int32_t* expert, const int32_t* offsets, const int32_t* accepted,
-                         int T, int d, int E, int C, int32_t* position, uint8_t* keep, int32_t* slot_token,
-                         bf16_t* buf, hipStream_t s);
+hipError_t launch_gather(const bf16_t* x, const int32_t* expert, const int32_t* offsets, const int32_t* group_base,
+                         const int32_t* rows_filled, int N, int d, int E, int k, int G, int rank, int tile, int C,
+                         int rows, int32_t* position, uint8_t* keep, int32_t* slot, int32_t* slot_token, bf16_t* buf,
+                         hipStream_t s);
 
 // expert_ffn.hip
 int ffn_token_tile(int C);
@@ -43,16 +48,16 @@ hipError_t launch_expert_gemm2(const bf16_t* h, const bf16_t* w2, const int32_t*
                                int E, int C, int d, int d_ff, hipStream_t s);
 
 // combine.hip
-hipError_t launch_combine(const float* y, const int32_t* expert, const int32_t* position, const uint8_t* keep,
-                          const float* gate, const bf16_t* residual, int64_t T, int d, int E, int C, bf16_t* out,
-                          hipStream_t s);
+hipError_t launch_combine(const float* y, const int32_t* expert, const int32_t* slot, const uint8_t* keep,
+                          const float* gate, const bf16_t* residual, int64_t T, int d, int E, int k, int C,
+                          bf16_t* out, hipStream_t s);
 
 // aux.hip
-hipError_t launch_aux_stats(const int32_t* counts, const float* prob_sum, int64_t T, int E, float alpha, float* f,
-                            float* P, float* loss, hipStream_t s);
+hipError_t launch_aux_stats(const int32_t* counts, const float* prob_sum, int64_t G, int ngroups, int E, int k,
+                            float alpha, float* f, float* P, float* loss, hipStream_t s);
 hipError_t launch_z_loss(const float* lse, int64_t T, float beta, float* z_loss, hipStream_t s);
-hipError_t launch_aux_grad(const float* logits, const float* lse, const float* f, int64_t T, int E, float alpha,
-                           float beta, int accumulate, float* dlogits, hipStream_t s);
+hipError_t launch_aux_grad(const float* logits, const float* lse, const float* f, int64_t T, int64_t G, int E,
+                           float alpha, float beta, int accumulate, float* dlogits, hipStream_t s);
 
 // api.hip
 hipError_t launch_stream_copy(void* dst, const void* src, size_t nbytes, hipStream_t s);

@@ -119,10 +119,12 @@ __global__ __launch_bounds__(256) void router_gemm(const bf16_t* __restrict__ x,
 
 // Softmax statistics per token.  A workgroup (4 waves) owns `tpb` consecutive
 // tokens; a wave handles one token at a time with lane j holding experts
-// j, j+64, ...  Writes expert, gate, lse and the workgroup's partial sums of
-// p_te over its tokens (fixed order: lanes in registers, waves in turn).
-template <int NCH>
-__global__ __launch_bounds__(256) void router_softmax(const float* __restrict__ logits, int T, int E,
+// j, j+64, ...  Writes the k choices and their gates ([T, k], choices in
+// decreasing logit order, ties to the lower index), lse and the workgroup's
+// partial sums of p_te over its tokens (fixed order: lanes in registers,
+// waves in turn).  KMAX bounds k at compile time.
+template <int NCH, int KMAX>
+__global__ __launch_bounds__(256) void router_softmax(const float* __restrict__ logits, int T, int E, int k,
                                                       int tpb, int32_t* __restrict__ expert,
                                                       float* __restrict__ gate, float* __restrict__ lse,
                                                       float* __restrict__ part) {
@@ -136,12 +138,14 @@ __global__ __launch_bounds__(256) void router_softmax(const float* __restrict__ 
     for (int t = t0 + wave; t < t1; t += 4) {
         const float* row = logits + (size_t)t * E;
         float v[NCH];
+        float zc[KMAX > 1 ? NCH : 1];
         float m = -INFINITY;
         int mi = 0x7fffffff;
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
             int e = lane + 64 * i;
             v[i] = e < E ? row[e] : -INFINITY;
+            if constexpr (KMAX > 1) zc[i] = v[i];
             if (v[i] > m) { m = v[i]; mi = e; }   // strict: first (lowest) index per lane
         }
         wave_argmax(m, mi);
@@ -156,9 +160,34 @@ __global__ __launch_bounds__(256) void router_softmax(const float* __restrict__ 
 #pragma unroll
         for (int i = 0; i < NCH; ++i) acc[i] += v[i] * inv;
         if (lane == 0) {
-            expert[t] = mi;
-            gate[t] = inv;           // p_{e*} = exp(z_e* - m) / s = 1 / s
+            expert[(size_t)t * k] = mi;
+            gate[(size_t)t * k] = inv;    // p_{e*} = exp(z_e* - m) / s = 1 / s
             lse[t] = m + logf(s);
+        }
+        if constexpr (KMAX > 1) {
+            // choice r: the largest logit among the experts not yet chosen
+            int ch[KMAX];
+            ch[0] = mi;
+#pragma unroll
+            for (int r = 1; r < KMAX; ++r) {
+                if (r >= k) break;
+                float mr = -INFINITY;
+                int ir = 0x7fffffff;
+#pragma unroll
+                for (int i = 0; i < NCH; ++i) {
+                    const int e = lane + 64 * i;
+                    bool taken = e >= E;
+#pragma unroll
+                    for (int q = 0; q < r; ++q) taken |= e == ch[q];
+                    if (!taken && zc[i] > mr) { mr = zc[i]; ir = e; }
+                }
+                wave_argmax(mr, ir);
+                ch[r] = ir;
+                if (lane == 0) {
+                    expert[(size_t)t * k + r] = ir;
+                    gate[(size_t)t * k + r] = expf(mr - m) * inv;
+                }
+            }
         }
     }
     for (int w = 0; w < 4; ++w) {
@@ -174,14 +203,17 @@ __global__ __launch_bounds__(256) void router_softmax(const float* __restrict__ 
     for (int e = threadIdx.x; e < E; e += 256) part[(size_t)blockIdx.x * E + e] = red[e];
 }
 
-// prob_sum[e] = sum over workgroups of the partial sums, in fp64, in a fixed
-// order: a workgroup owns 64 experts; its 16 row groups take every 16th
-// partial row, then the row groups are added in order.
+// prob_sum[g][e] = sum over the partial rows of routing group g (rows
+// g*nblk .. g*nblk+nblk-1), in fp64, in a fixed order: a workgroup owns 64
+// experts of one group; its 16 row groups take every 16th partial row, then
+// the row groups are added in order.  One group: prob_sum[e] over all rows.
 __global__ __launch_bounds__(1024) void router_reduce(const float* __restrict__ part, int nblk, int E,
                                                       float* __restrict__ prob_sum) {
     __shared__ double red[16][64];
     const int c = threadIdx.x & 63, rg = threadIdx.x >> 6;
     const int e = blockIdx.x * 64 + c;
+    part += (size_t)blockIdx.y * nblk * E;
+    prob_sum += (size_t)blockIdx.y * E;
     double s = 0.0;
     if (e < E) {
         int b = rg;
@@ -226,14 +258,15 @@ int router_softmax_blocks(int64_t T, int E) {
     return (int)((T + tpb - 1) / tpb);
 }
 
-hipError_t launch_router_softmax(const float* logits, int T, int E, int32_t* expert, float* gate,
-                                 float* lse, float* part, hipStream_t s) {
-    int nblk = router_softmax_blocks(T, E);
-    int tpb = (T + nblk - 1) / nblk;
-    size_t shm = (size_t)E * sizeof(float);
-    int nch = (E + 63) / 64;
-#define SWMOE_SOFTMAX(N)                                                                          \
-    hipLaunchKernelGGL(router_softmax<N>, dim3(nblk), dim3(256), shm, s, logits, T, E, tpb, expert, \
+int router_softmax_blocks_grouped(int64_t T) { return (int)((T + 63) / 64); }
+
+template <int KMAX>
+static void softmax_by_width(int nblk, int tpb, const float* logits, int T, int E, int k, int32_t* expert,
+                             float* gate, float* lse, float* part, hipStream_t s) {
+    const size_t shm = (size_t)E * sizeof(float);
+    const int nch = (E + 63) / 64;
+#define SWMOE_SOFTMAX(N)                                                                                  \
+    hipLaunchKernelGGL((router_softmax<N, KMAX>), dim3(nblk), dim3(256), shm, s, logits, T, E, k, tpb, expert, \
                        gate, lse, part)
     if (nch <= 1) SWMOE_SOFTMAX(1);
     else if (nch <= 2) SWMOE_SOFTMAX(2);
@@ -243,11 +276,21 @@ hipError_t launch_router_softmax(const float* logits, int T, int E, int32_t* exp
     else if (nch <= 32) SWMOE_SOFTMAX(32);
     else SWMOE_SOFTMAX(64);
 #undef SWMOE_SOFTMAX
+}
+
+hipError_t launch_router_softmax(const float* logits, int T, int E, int k, bool rows_of_64, int32_t* expert,
+                                 float* gate, float* lse, float* part, hipStream_t s) {
+    const int nblk = rows_of_64 ? router_softmax_blocks_grouped(T) : router_softmax_blocks(T, E);
+    const int tpb = rows_of_64 ? 64 : (T + nblk - 1) / nblk;
+    if (k <= 1) softmax_by_width<1>(nblk, tpb, logits, T, E, k, expert, gate, lse, part, s);
+    else if (k <= 2) softmax_by_width<2>(nblk, tpb, logits, T, E, k, expert, gate, lse, part, s);
+    else softmax_by_width<kMaxTopK>(nblk, tpb, logits, T, E, k, expert, gate, lse, part, s);
     return hipGetLastError();
 }
 
-hipError_t launch_router_reduce(const float* part, int nblk, int E, float* prob_sum, hipStream_t s) {
-    hipLaunchKernelGGL(router_reduce, dim3((E + 63) / 64), dim3(1024), 0, s, part, nblk, E, prob_sum);
+hipError_t launch_router_reduce(const float* part, int nblk, int ngroups, int E, float* prob_sum, hipStream_t s) {
+    if (ngroups == 0) return hipSuccess;
+    hipLaunchKernelGGL(router_reduce, dim3((E + 63) / 64, ngroups), dim3(1024), 0, s, part, nblk, E, prob_sum);
     return hipGetLastError();
 }
 
@@ -267,11 +310,13 @@ constexpr int RF_TB = 1;                 // 16-token MFMA blocks per wave
 constexpr int RF_TOK = 4 * 16 * RF_TB;   // tokens per workgroup
 constexpr int RF_ROW = 40;     // bf16 per staged W row: 32 + 8 pad (80 bytes)
 
+// routing groups reduce whole 64-token partial rows (router_reduce)
+static_assert(RF_TOK == 64, "the fused router writes one partial row per 64 tokens");
 int router_fused_blocks(int64_t T) { return (int)((T + RF_TOK - 1) / RF_TOK); }
 
-template <int EB, int R>
+template <int EB, int R, int KMAX>
 __global__ __launch_bounds__(256) void router_fused(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wr3,
-                                                    const float* __restrict__ b_r, int T, int d, int E,
+                                                    const float* __restrict__ b_r, int T, int d, int E, int k,
                                                     float* __restrict__ logits_out, int32_t* __restrict__ expert,
                                                     float* __restrict__ gate, float* __restrict__ lse,
                                                     float* __restrict__ part) {
@@ -371,6 +416,7 @@ __global__ __launch_bounds__(256) void router_fused(const bf16_t* __restrict__ x
     for (int tb = 0; tb < RF_TB; ++tb) {
         const int t = tbase + tb * 16 + r16;
         float v[EB][4];
+        float zc[KMAX > 1 ? EB : 1][4];
         float m = -INFINITY;
         int mi = 0x7fffffff;
 #pragma unroll
@@ -379,6 +425,7 @@ __global__ __launch_bounds__(256) void router_fused(const bf16_t* __restrict__ x
             for (int i = 0; i < 4; ++i) {
                 const int e = eb * 16 + (lane >> 4) * 4 + i;
                 v[eb][i] = e < E ? acc[tb][eb][i] + (b_r ? b_r[e] : 0.f) : -INFINITY;
+                if constexpr (KMAX > 1) zc[eb][i] = v[eb][i];
                 if (v[eb][i] > m) { m = v[eb][i]; mi = e; }
             }
         // the 4 lane groups (lane >> 4) hold the other experts of the same token
@@ -403,9 +450,42 @@ __global__ __launch_bounds__(256) void router_fused(const bf16_t* __restrict__ x
         ssum += __shfl_xor(ssum, 32);
         const float inv = 1.0f / ssum;
         if (t < T && lane < 16) {
-            expert[t] = mi;
-            gate[t] = inv;
+            expert[(size_t)t * k] = mi;
+            gate[(size_t)t * k] = inv;
             lse[t] = m + logf(ssum);
+        }
+        if constexpr (KMAX > 1) {
+            // choice r: the largest logit among the experts not yet chosen
+            // (zc keeps the logits; v now holds the exponentials)
+            int ch[KMAX];
+            ch[0] = mi;
+#pragma unroll
+            for (int r = 1; r < KMAX; ++r) {
+                if (r >= k) break;
+                float mr = -INFINITY;
+                int ir = 0x7fffffff;
+#pragma unroll
+                for (int eb = 0; eb < EB; ++eb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int e = eb * 16 + (lane >> 4) * 4 + i;
+                        bool taken = e >= E;
+#pragma unroll
+                        for (int q = 0; q < r; ++q) taken |= e == ch[q];
+                        if (!taken && zc[eb][i] > mr) { mr = zc[eb][i]; ir = e; }
+                    }
+#pragma unroll
+                for (int off = 16; off <= 32; off <<= 1) {
+                    const float om = __shfl_xor(mr, off);
+                    const int oi = __shfl_xor(ir, off);
+                    if (om > mr || (om == mr && oi < ir)) { mr = om; ir = oi; }
+                }
+                ch[r] = ir;
+                if (t < T && lane < 16) {
+                    expert[(size_t)t * k + r] = ir;
+                    gate[(size_t)t * k + r] = expf(mr - m) * inv;
+                }
+            }
         }
         const float w = t < T ? inv : 0.f;
 #pragma unroll
@@ -440,19 +520,27 @@ __global__ __launch_bounds__(256) void router_fused(const bf16_t* __restrict__ x
     for (int e = threadIdx.x; e < E; e += 256) part[(size_t)blockIdx.x * E + e] = red[e];
 }
 
-hipError_t launch_router_fused(const bf16_t* x, const bf16_t* wr3, const float* b_r, int T, int d, int E,
-                               float* logits_out, int32_t* expert, float* gate, float* lse, float* part,
-                               hipStream_t s) {
+template <int KMAX>
+static void fused_by_width(const bf16_t* x, const bf16_t* wr3, const float* b_r, int T, int d, int E, int k,
+                           float* logits_out, int32_t* expert, float* gate, float* lse, float* part, hipStream_t s) {
     const dim3 grid(router_fused_blocks(T));
-#define SWMOE_RF(EB, R)                                                                                             \
-    hipLaunchKernelGGL((router_fused<EB, R>), grid, dim3(256), 0, s, x, wr3, b_r, T, d, E, logits_out, expert, gate, \
-                       lse, part)
+#define SWMOE_RF(EB, R)                                                                                    \
+    hipLaunchKernelGGL((router_fused<EB, R, KMAX>), grid, dim3(256), 0, s, x, wr3, b_r, T, d, E, k, logits_out, \
+                       expert, gate, lse, part)
     if (E <= 16) SWMOE_RF(1, 4);
     else if (E <= 32) SWMOE_RF(2, 4);
     else if (E <= 64) SWMOE_RF(4, 4);
     else if (E <= 128) SWMOE_RF(8, 4);
     else SWMOE_RF(16, 2);
 #undef SWMOE_RF
+}
+
+hipError_t launch_router_fused(const bf16_t* x, const bf16_t* wr3, const float* b_r, int T, int d, int E, int k,
+                               float* logits_out, int32_t* expert, float* gate, float* lse, float* part,
+                               hipStream_t s) {
+    if (k <= 1) fused_by_width<1>(x, wr3, b_r, T, d, E, k, logits_out, expert, gate, lse, part, s);
+    else if (k <= 2) fused_by_width<2>(x, wr3, b_r, T, d, E, k, logits_out, expert, gate, lse, part, s);
+    else fused_by_width<kMaxTopK>(x, wr3, b_r, T, d, E, k, logits_out, expert, gate, lse, part, s);
     return hipGetLastError();
 }
 

@@ -135,3 +135,54 @@ def test_status_strings():
     for s in range(5):
         assert L.switch_status_string(s)
     assert L.switch_kernel_name(7) == b"expert_gemm1"
+
+
+def test_group_topk_validation():
+    """Routing groups and top-k: k in [1, min(E, 4)], T a multiple of the
+    group size, group sizes that are multiples of 64, priority 0 or 1."""
+    L = sw.lib()
+    ok = dict(x=FAKE, e=FAKE, T=256, d=64, E=4, k=2, G=128, C=64, pr=0, pos=FAKE, keep=FAKE, slot=FAKE, cnt=FAKE,
+              acc=FAKE, tot=FAKE, st=None, buf=FAKE, ws=FAKE, wsn=1 << 20)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.switch_dispatch_ex(a["x"], a["e"], a["T"], a["d"], a["E"], a["k"], a["G"], a["C"], a["pr"],
+                                    a["pos"], a["keep"], a["slot"], a["cnt"], a["acc"], a["tot"], a["st"], a["buf"],
+                                    a["ws"], a["wsn"], None)
+    assert call(k=0) == sw.SWITCH_E_INVALID
+    assert call(k=5, E=8) == sw.SWITCH_E_UNSUPPORTED
+    assert call(k=5) == sw.SWITCH_E_INVALID                 # k > E
+    assert call(G=96) == sw.SWITCH_E_INVALID                # 256 % 96 != 0
+    assert call(T=96, G=32) == sw.SWITCH_E_UNSUPPORTED      # 32 is not a multiple of 64
+    assert call(pr=2) == sw.SWITCH_E_INVALID
+    assert call(G=-1) == sw.SWITCH_E_INVALID
+    assert call(tot=None) == sw.SWITCH_E_INVALID            # several groups need accepted_total
+    assert call(slot=None) == sw.SWITCH_E_INVALID
+    assert call(wsn=0) == sw.SWITCH_E_WORKSPACE
+    # one group (group = 0 or T) needs neither slot nor accepted_total; the
+    # failure left is the workspace, reached only after every other check
+    assert call(G=0, slot=None, tot=None, wsn=0) == sw.SWITCH_E_WORKSPACE
+    assert call(G=256, slot=None, tot=None, wsn=0) == sw.SWITCH_E_WORKSPACE
+    st = L.switch_route_ex(FAKE, FAKE, None, None, 256, 64, 4, 3, 96, None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                           None)
+    assert st == sw.SWITCH_E_INVALID
+    st = L.switch_aux_loss_ex(FAKE, FAKE, None, None, 256, 4, 5, 64, 0.01, FAKE, FAKE, FAKE, None, None)
+    assert st == sw.SWITCH_E_INVALID
+    assert L.switch_combine_ex(FAKE, FAKE, FAKE, FAKE, FAKE, None, 16, 64, 4, 0, 4, FAKE, None) == sw.SWITCH_E_INVALID
+
+
+def test_group_topk_workspace_sizes():
+    # one group and k = 1 give the Switch layer's sizes exactly
+    for T, d, F, E, C in [(16384, 768, 3072, 128, 128), (512, 64, 128, 4, 160), (65536, 1024, 1024, 2048, 32)]:
+        assert sw.switch_workspace_bytes_ex(T, d, F, E, C, 1, 0) == sw.switch_workspace_bytes(T, d, F, E, C)
+        assert sw.switch_workspace_bytes_ex(T, d, F, E, C, 1, T) == sw.switch_workspace_bytes(T, d, F, E, C)
+        assert sw.switch_dispatch_workspace_bytes_ex(T, E, 1, 0) == sw.switch_dispatch_workspace_bytes(T, E)
+    # groups of 64 with top-2: scan tiles of 128 choices, per-group bases, rows = groups * C
+    T, E, G, k = 16384, 128, 64, 2
+    ng = T // G
+    assert sw.switch_dispatch_workspace_bytes_ex(T, E, k, G) >= (T * k // 128) * E * 4 + ng * E * 4 + E * 4
+    C = sw.switch_capacity(k * G, E, 1.0)
+    assert C == 1
+    assert sw.switch_workspace_bytes_ex(T, 768, 3072, E, C, k, G) >= E * ng * C * 768 * 6 + T * k * 4
+    assert sw.switch_workspace_bytes_ex(T, 768, 3072, E, C, k, 100) == 0     # T % 100 != 0
+    assert sw.switch_workspace_bytes_ex(T, 768, 3072, E, C, 5, G) == 0       # k above the limit
