@@ -36,6 +36,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--config", type=int, default=2, help="layer configuration 1..5 (2 = Switch-Base shape)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-variants", action="store_true",
+                   help="skip the timing of the layer variants (z-loss, routing groups, top-2)")
     p.add_argument("--cpu-sample-tokens", type=int, default=0,
                    help="tokens in the oracle's timed sample (0 = the whole batch)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -104,6 +106,44 @@ def cpu_baseline(inp, cfg, sample_tokens):
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     del L
     return n / dt, dt, threads, n
+
+
+def time_variants(sw, torch, cfg, x, w_r, b_r, w1, w2, stream, steps, warmup):
+    """The same layer with the rows beyond the Switch forward switched on: the
+    router z-loss, routing groups of 64 tokens (capacity per group), and top-2
+    choices in groups of 2048 tokens.  Each variant: warm-up, then `steps`
+    timed steps between events on the launch stream."""
+    out = {}
+    variants = [
+        ("z_loss", dict(k=1, group=0, z=True)),
+        ("groups_of_64", dict(k=1, group=64, z=False)),
+        ("top2_groups_of_2048", dict(k=2, group=2048, z=False)),
+        ("top2_one_group", dict(k=2, group=0, z=False)),
+    ]
+    for name, v in variants:
+        G = v["group"] or cfg.T
+        if cfg.T % G:
+            continue
+        C = sw.switch_capacity(v["k"] * G, cfg.E, cfg.c)
+        t = sw.layer_tensors(cfg.T, cfg.d, cfg.d_ff, cfg.E, C, dlogits=cfg.want_grad, z_loss=v["z"], k=v["k"],
+                             group=v["group"])
+        la = sw.make_layer_args(x, w_r, b_r, w1, w2, t, cfg.T, cfg.d, cfg.d_ff, cfg.E, C, cfg.alpha, residual=True,
+                                z_beta=1e-3 if v["z"] else 0.0, k=v["k"], group=v["group"])
+        for _ in range(warmup):
+            sw.switch_layer_fwd(la, t["ws"], stream)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(steps):
+            sw.switch_layer_fwd(la, t["ws"], stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / steps
+        keep = t["keep"].cpu().numpy()
+        out[name] = {"k": v["k"], "group": G, "C_per_group": C, "ms_per_step": ms,
+                     "tokens_per_s": cfg.T / (ms / 1000.0), "kept_choices": float(keep.mean())}
+        del t, la
+    return out
 
 
 def main():
@@ -177,6 +217,7 @@ def main():
         "gather": dict(bytes=2 * A * d + 2 * E * C * d + 9 * T + 8 * E + 4 * E * C, flops=0),
         "combine": dict(bytes=4 * A * d + 2 * T * d + 2 * T * d + 13 * T, flops=0),
         "router_gemm": dict(bytes=2 * T * d + 6 * d * E + 4 * T * E, flops=2 * T * d * E),
+        "router_fused": dict(bytes=2 * T * d + 6 * d * E + 12 * T + 4 * E * ((T + 63) // 64), flops=2 * T * d * E),
     }
     dominant = max((k for k in kern_us if k in alg), key=lambda k: kern_us[k])
     dur_s = kern_us[dominant] * 1e-6
@@ -231,6 +272,10 @@ def main():
                     "empty_slot_ratio": 1 - A / (E * C) if C else None},
         "wall_s_timed": wall,
     }
+
+    if not args.no_variants:
+        result["variants"] = time_variants(sw, torch, cfg, x, w_r, b_r, w1, w2, stream, min(args.steps, 20),
+                                           min(args.warmup, 5))
 
     if not args.no_cpu_baseline:
         rate, dt, threads, n = cpu_baseline(inp, cfg, args.cpu_sample_tokens)

@@ -17,12 +17,15 @@ namespace swmoe {
 // residual, 2 x 16-byte fp32 loads of y per kept choice, one 16-byte store.
 // The k choices of a token are added in rank order into the fp32 residual,
 // then rounded once.  `slot` indexes the expert's buffer rows (the position
-// itself when there is one routing group).
+// itself when there is one routing group).  KC = k at compile time (1, the
+// Switch layer), or 0 for a run-time k.
+template <int KC>
 __global__ __launch_bounds__(256) void combine(const float* __restrict__ y, const int32_t* __restrict__ expert,
                                                const int32_t* __restrict__ slot,
                                                const uint8_t* __restrict__ keep, const float* __restrict__ gate,
-                                               const bf16_t* __restrict__ residual, int64_t T, int d, int E, int k,
+                                               const bf16_t* __restrict__ residual, int64_t T, int d, int E, int kr,
                                                int C, bf16_t* __restrict__ out) {
+    const int k = KC > 0 ? KC : kr;
     const int vpr = d >> 3;
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= T * vpr) return;
@@ -66,8 +69,13 @@ hipError_t launch_combine(const float* y, const int32_t* expert, const int32_t* 
                           bf16_t* out, hipStream_t s) {
     const int64_t n = T * (d >> 3);
     if (n == 0) return hipSuccess;
-    hipLaunchKernelGGL(combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, y, expert, slot, keep, gate,
-                       residual, T, d, E, k, C, out);
+    const dim3 grid((unsigned)((n + 255) / 256));
+    if (k == 1)
+        hipLaunchKernelGGL(combine<1>, grid, dim3(256), 0, s, y, expert, slot, keep, gate, residual, T, d, E, k, C,
+                           out);
+    else
+        hipLaunchKernelGGL(combine<0>, grid, dim3(256), 0, s, y, expert, slot, keep, gate, residual, T, d, E, k, C,
+                           out);
     return hipGetLastError();
 }
 
