@@ -96,9 +96,10 @@ __device__ __forceinline__ FfnTile decode_tile(int i, const int4* __restrict__ t
 }
 
 // TOKB: 32-row token blocks per tile; NBW: 32-row weight blocks per wave;
-// WAVES: waves per workgroup; R: depth of the register rings.  GEMM1 writes
-// bf16(ReLU(.)), GEMM2 writes fp32.
-template <int TOKB, int NBW, int WAVES, int R, bool GEMM1>
+// WAVES: waves per workgroup; R: depth of the register rings; PB: bytes of an
+// output row staged through LDS per pass.  GEMM1 writes bf16(ReLU(.)), GEMM2
+// writes fp32.
+template <int TOKB, int NBW, int WAVES, int R, bool GEMM1, int PB>
 __global__ __launch_bounds__(64 * WAVES) void expert_gemm(const bf16_t* __restrict__ A,   // [E, C, K]
                                                           const bf16_t* __restrict__ W,   // [E, N, K]
                                                           const int32_t* __restrict__ pre,
@@ -112,7 +113,9 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm(const bf16_t* __restri
     constexpr int APT = (PIECES + NTHR - 1) / NTHR;       // pieces per thread
     constexpr int OUT_BYTES = GEMM1 ? 2 : 4;
     constexpr int ROW_BYTES = NWG * OUT_BYTES;                        // output bytes per token row
-    constexpr int PASS_BYTES = ROW_BYTES < 512 ? ROW_BYTES : 512;     // staged per pass
+    constexpr int PASS_BYTES = ROW_BYTES <= PB ? ROW_BYTES
+                               : (ROW_BYTES % PB == 0 ? PB : (ROW_BYTES % (PB / 2) == 0 ? PB / 2 : PB / 4));
+    static_assert(ROW_BYTES % PASS_BYTES == 0 && PASS_BYTES % 16 == 0, "whole 16-byte passes");
     constexpr int NPASS = ROW_BYTES / PASS_BYTES;
     constexpr int CPP = PASS_BYTES / OUT_BYTES;                       // columns per pass
     constexpr int OSTRIDE = PASS_BYTES + 16;                          // bytes per staged row
@@ -262,12 +265,11 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm(const bf16_t* __restri
                         constexpr int VPR = PASS_BYTES / 16;           // 16-byte vectors per staged row
                         const int vpr_valid = max(0, min(CPP, ncols - pass * CPP)) * OUT_BYTES / 16;
                         char* gout = (char*)out + (((size_t)t.e * C + t.tok_base) * N + (size_t)t.nt * NWG + pass * CPP) * OUT_BYTES;
-                        static_assert((TOK * VPR) % NTHR == 0, "whole store passes");
 #pragma unroll
-                        for (int it = 0; it < TOK * VPR / NTHR; ++it) {
+                        for (int it = 0; it < (TOK * VPR + NTHR - 1) / NTHR; ++it) {
                             const int i = threadIdx.x + it * NTHR;
                             const int r = i / VPR, v = i - r * VPR;
-                            if (r < t.nv && v < vpr_valid)
+                            if (i < TOK * VPR && r < t.nv && v < vpr_valid)
                                 *(u32x4*)(gout + (size_t)r * N * OUT_BYTES + v * 16) = *(const u32x4*)(lds_o + r * OSTRIDE + v * 16);
                         }
                     }
@@ -296,7 +298,7 @@ static int device_cus() {
     return cus[dev];
 }
 
-template <int TOKB, int NBW, int WAVES, int R, bool GEMM1>
+template <int TOKB, int NBW, int WAVES, int R, bool GEMM1, int PB>
 hipError_t launch_expert_gemm_t(const bf16_t* A, const bf16_t* W, const int32_t* pre, const int4* ttab, void* out,
                                 int E, int C, int K, int N, hipStream_t s) {
     constexpr int NWG = WAVES * 32 * NBW;
@@ -304,7 +306,7 @@ hipError_t launch_expert_gemm_t(const bf16_t* A, const bf16_t* W, const int32_t*
     static int per_cu = 0;   // resident workgroups per CU for this kernel
     if (!per_cu) {
         int b = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, expert_gemm<TOKB, NBW, WAVES, R, GEMM1>, 64 * WAVES, 0) !=
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, expert_gemm<TOKB, NBW, WAVES, R, GEMM1, PB>, 64 * WAVES, 0) !=
                 hipSuccess || b <= 0)
             b = 1;
         per_cu = b;
@@ -313,7 +315,7 @@ hipError_t launch_expert_gemm_t(const bf16_t* A, const bf16_t* W, const int32_t*
     const int64_t max_tiles = (int64_t)E * n_tiles * tok_tiles;
     int64_t grid = std::min<int64_t>((int64_t)device_cus() * per_cu, (max_tiles + 7) / 8 * 8);
     grid = std::max<int64_t>(8, grid / 8 * 8);
-    hipLaunchKernelGGL((expert_gemm<TOKB, NBW, WAVES, R, GEMM1>), dim3((unsigned)grid), dim3(64 * WAVES), 0, s, A, W,
+    hipLaunchKernelGGL((expert_gemm<TOKB, NBW, WAVES, R, GEMM1, PB>), dim3((unsigned)grid), dim3(64 * WAVES), 0, s, A, W,
                        pre, ttab, out, E, C, K, N, n_tiles);
     return hipGetLastError();
 }
@@ -331,13 +333,32 @@ hipError_t launch_ffn_tile_prefix(const int32_t* accepted, int E, int C, int32_t
 }
 
 #ifndef SWMOE_FFN_CUSTOM_DISPATCH
+// Tile width for 128-row token tiles.  Every workgroup streams NWG weight rows
+// per tile, so a round of tiles over the persistent grid costs about NWG; the
+// kernel takes ceil(tiles / grid) rounds.  Choose the width with the smaller
+// rounds * NWG (the wider one on a tie), counting every expert's token tiles
+// as full: e.g. N = 768 at 128 experts gives 384 tiles of 256 columns (two
+// rounds, the second half empty) against 512 tiles of 192 (two full rounds).
+static bool narrow_tiles(int E, int C, int N) {
+    const int64_t tok_tiles = (int64_t)E * ((C + 127) / 128);
+    const int64_t grid = device_cus();          // one 6- or 8-wave workgroup per CU
+    auto cost = [&](int nwg) {
+        const int64_t tiles = tok_tiles * ((N + nwg - 1) / nwg);
+        return (tiles + grid - 1) / grid * nwg;
+    };
+    return cost(192) < cost(256);
+}
+
 template <bool GEMM1>
 static hipError_t launch_expert_gemm(const bf16_t* A, const bf16_t* W, const int32_t* pre, const int4* ttab, void* out,
                                      int E, int C, int K, int N, hipStream_t s) {
     // the token tile must be ffn_token_tile(C) rows: the prefix kernel lists tiles of that size
-    if (C > 64) return launch_expert_gemm_t<4, 1, 8, 4, GEMM1>(A, W, pre, ttab, out, E, C, K, N, s);
-    if (C > 32) return launch_expert_gemm_t<2, 2, 4, 3, GEMM1>(A, W, pre, ttab, out, E, C, K, N, s);
-    return launch_expert_gemm_t<1, 2, 4, 4, GEMM1>(A, W, pre, ttab, out, E, C, K, N, s);
+    if (C > 64) {
+        if (narrow_tiles(E, C, N)) return launch_expert_gemm_t<4, 1, 6, 3, GEMM1, 256>(A, W, pre, ttab, out, E, C, K, N, s);
+        return launch_expert_gemm_t<4, 1, 8, 4, GEMM1, 512>(A, W, pre, ttab, out, E, C, K, N, s);
+    }
+    if (C > 32) return launch_expert_gemm_t<2, 2, 4, 3, GEMM1, 512>(A, W, pre, ttab, out, E, C, K, N, s);
+    return launch_expert_gemm_t<1, 2, 4, 4, GEMM1, 512>(A, W, pre, ttab, out, E, C, K, N, s);
 }
 
 hipError_t launch_expert_gemm1(const bf16_t* buf, const bf16_t* w1, const int32_t* pre, const int4* ttab, bf16_t* h,
