@@ -9,4 +9,5 @@ from .switch_oracle import (  # noqa: F401
     router_logits, router_z_loss, slot_scan, softmax_top1, ZLoss,
     AuxG, LayerResultG, RoutingK, SlotsG, aux_loss_grouped, assignment_order, combine_topk,
     group_capacity, layer_forward_grouped, layer_per_token_topk, slot_scan_grouped, softmax_topk,
+    LayerGrads, layer_backward, layer_objective,
 )

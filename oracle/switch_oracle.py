@@ -626,3 +626,92 @@ def layer_per_token_topk(x, z, w1, w2, k: int, G: int, Cg: int, priority: str = 
                 w2e = np.asarray(w2(e) if callable(w2) else w2[e], np.float64)
                 branch[t] += gte * (w2e @ np.maximum(w1e @ x[t], 0.0))
     return np.array(choices, np.int64), positions, branch
+
+
+# ------------------------------------------------ NEXT f-2: layer backward
+#
+# The objective whose gradient is taken:  J = sum_t <dout_t, out_t> + L_aux
+# (+ L_z when beta > 0), i.e. dout is the gradient flowing into the layer's
+# output and the aux (and z) losses are added to the training loss with the
+# weights they carry inside ([WQ] sec. 2: the total loss adds the balance
+# term; the router stays differentiable through the selected gate).  The
+# choices, positions and masks are held fixed: argmax has no gradient ([WQ]
+# sec. 2; [ZF] "troubleshooting": finite differences that leave the discrete
+# choices and capacity masks unchanged).
+#
+# Chain rule for a kept token t with expert e = e*_t, slot s = pos_t:
+#   out_t = x_t + g_t y_t,  y_t = W2_e relu(a_t),  a_t = W1_e x_t,  g_t = p_{t,e}
+#   dy_t = g_t dout_t                       dg_t = <dout_t, y_t>
+#   dW2_e += dy_t relu(a_t)^T               dh_t = W2_e^T dy_t
+#   da_t = dh_t * [a_t > 0]                 dW1_e += da_t x_t^T
+#   dx_t = dout_t + W1_e^T da_t   (dropped tokens: dx_t = dout_t)
+# Router, with p_tj = softmax(z_t)_j and d p_te / d z_tj = p_te (delta_ej - p_tj):
+#   dz_tj = dg_t g_t (delta_{j e} - p_tj) + dL_aux/dz_tj (+ dL_z/dz_tj)
+#   dW_r = x^T dz,  db_r = sum_t dz_t,  dx_t += W_r dz_t.
+
+class LayerGrads(NamedTuple):
+    dx: np.ndarray      # [T, d]
+    dw_r: np.ndarray    # [d, E]
+    db_r: np.ndarray    # [E]
+    dw1: np.ndarray     # [E, d_ff, d]
+    dw2: np.ndarray     # [E, d, d_ff]
+    dz: np.ndarray      # [T, E] total gradient at the logits
+    dgate: np.ndarray   # [T] <dout_t, y_t> for kept tokens, 0 for dropped ones
+
+
+def layer_backward(x, w_r, b_r, w1, w2, c: float, alpha: float, dout, beta: float = 0.0,
+                   C: Optional[int] = None, expert_override: Optional[np.ndarray] = None,
+                   forward: Optional[LayerResult] = None) -> LayerGrads:
+    """Gradients of J = sum_t <dout_t, out_t> + L_aux (+ L_z) for the Switch
+    layer (one routing group, k = 1), in float64, expert by expert."""
+    x = np.asarray(x, np.float64)
+    dout = np.asarray(dout, np.float64)
+    L = forward if forward is not None else layer_forward(x, w_r, b_r, w1, w2, c, alpha, C=C,
+                                                          expert_override=expert_override)
+    T, d = x.shape
+    E = L.z.shape[1]
+    r, sl = L.routing, L.slots
+    w1e = (lambda e: np.asarray(w1(e) if callable(w1) else w1[e], np.float64))
+    w2e = (lambda e: np.asarray(w2(e) if callable(w2) else w2[e], np.float64))
+    F = w1e(0).shape[0]
+    dx = dout.copy()
+    dw1 = np.zeros((E, F, d))
+    dw2 = np.zeros((E, d, F))
+    dgate = np.zeros(T)
+    for e in range(E):
+        toks = np.flatnonzero((r.expert == e) & sl.keep)
+        if toks.size == 0:
+            continue
+        W1, W2 = w1e(e), w2e(e)
+        xe = x[toks]
+        a = xe @ W1.T                       # pre-activations [n, F]
+        h = np.maximum(a, 0.0)
+        y = h @ W2.T                        # [n, d]
+        g = r.gate[toks]
+        dgate[toks] = np.sum(dout[toks] * y, axis=1)
+        dy = g[:, None] * dout[toks]
+        dw2[e] = dy.T @ h
+        da = (dy @ W2) * (a > 0)
+        dw1[e] = da.T @ xe
+        dx[toks] += da @ W1
+    onehot = np.zeros((T, E))
+    onehot[np.arange(T), r.expert] = 1.0
+    dz = (dgate * r.gate)[:, None] * (onehot - r.p)
+    dz = dz + L.aux.dlogits
+    if beta:
+        dz = dz + router_z_loss(L.z, beta).dlogits
+    w_r64 = np.asarray(w_r, np.float64)
+    dw_r = x.T @ dz
+    db_r = dz.sum(axis=0)
+    dx = dx + dz @ w_r64.T
+    return LayerGrads(dx, dw_r, db_r, dw1, dw2, dz, dgate)
+
+
+def layer_objective(x, w_r, b_r, w1, w2, c, alpha, dout, beta, expert, C):
+    """J = sum <dout, out> + L_aux(f fixed from `expert`) + L_z at fixed
+    choices `expert` and capacity C; used by the finite-difference pins."""
+    L = layer_forward(x, w_r, b_r, w1, w2, c, alpha, C=C, expert_override=expert)
+    J = float(np.sum(np.asarray(dout, np.float64) * L.out)) + L.aux.loss
+    if beta:
+        J += router_z_loss(L.z, beta).loss
+    return J

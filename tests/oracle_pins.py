@@ -532,3 +532,98 @@ GROUP_TOPK_PINS = [
     pin_grouped_aux,
 ]
 ALL_PINS.extend(GROUP_TOPK_PINS)
+
+
+# ------------------------------------------------ NEXT f-2: layer backward
+def _fd_problem(seed, T=24, d=8, F=12, E=3):
+    """A tiny layer whose kept tokens have every pre-activation away from the
+    ReLU kink and every top-2 logit margin away from a tie, so that a 1e-6
+    step changes neither the choices nor the ReLU pattern."""
+    for s in range(seed, seed + 50):
+        x, w_r, b_r, w1, w2 = _tiny_problem(s, T, d, F, E)
+        x = x.astype(np.float64)
+        z = x @ w_r.astype(np.float64) + b_r
+        srt = np.sort(z, axis=1)
+        if np.min(srt[:, -1] - srt[:, -2]) < 1e-3:
+            continue
+        a = np.einsum("td,efd->tef", x, w1.astype(np.float64))
+        if np.min(np.abs(a)) < 1e-4:
+            continue
+        return x, w_r.astype(np.float64), b_r.astype(np.float64), w1.astype(np.float64), w2.astype(np.float64)
+    raise AssertionError("no suitable tiny problem")
+
+
+def pin_backward_finite_differences(so):
+    """zffjzz 'troubleshooting': central finite differences of
+    J = sum <dout, out> + L_aux (+ L_z) over every entry of x, W_r, b_r, W1
+    and W2, with the choices and masks held fixed; some tokens are dropped."""
+    x, w_r, b_r, w1, w2 = _fd_problem(41)
+    T, d = x.shape
+    E = w_r.shape[1]
+    c, alpha = 1.0, 0.3
+    dout = _rng(42).standard_normal((T, d))
+    for beta in (0.0, 0.05):
+        L = so.layer_forward(x, w_r, b_r, w1, w2, c, alpha)
+        assert (~L.slots.keep).any() and L.slots.keep.any()
+        g = so.layer_backward(x, w_r, b_r, w1, w2, c, alpha, dout, beta=beta)
+        e_fix, C = L.routing.expert, L.C
+        h = 1e-6
+
+        def J(**kw):
+            a = dict(x=x, w_r=w_r, b_r=b_r, w1=w1, w2=w2)
+            a.update(kw)
+            return so.layer_objective(a["x"], a["w_r"], a["b_r"], a["w1"], a["w2"], c, alpha, dout, beta, e_fix, C)
+
+        for name, arr, grad in (("x", x, g.dx), ("w_r", w_r, g.dw_r), ("b_r", b_r, g.db_r),
+                                ("w1", w1, g.dw1), ("w2", w2, g.dw2)):
+            num = np.zeros_like(arr)
+            for idx in np.ndindex(arr.shape):
+                p, m = arr.copy(), arr.copy()
+                p[idx] += h
+                m[idx] -= h
+                num[idx] = (J(**{name: p}) - J(**{name: m})) / (2 * h)
+            np.testing.assert_allclose(grad, num, rtol=1e-6, atol=2e-8, err_msg=f"d{name} (beta={beta})")
+
+
+def pin_backward_single_expert_is_dense_mlp(so):
+    """E = 1: p = 1, nothing dropped at c = 1, so the layer is x + relu(x W1^T) W2^T
+    and its gradients are torch autograd's for that MLP; the router gets no
+    gradient (the softmax of one logit is constant and the aux loss is alpha)."""
+    rng = _rng(43)
+    T, d, F = 20, 8, 12
+    x = rng.standard_normal((T, d))
+    w_r = rng.standard_normal((d, 1))
+    w1 = rng.standard_normal((1, F, d)) * 0.3
+    w2 = rng.standard_normal((1, d, F)) * 0.3
+    dout = rng.standard_normal((T, d))
+    g = so.layer_backward(x, w_r, None, w1, w2, 1.0, 0.01, dout)
+    X = torch.tensor(x, requires_grad=True)
+    W1 = torch.tensor(w1[0], requires_grad=True)
+    W2 = torch.tensor(w2[0], requires_grad=True)
+    out = X + torch.nn.functional.linear(torch.relu(torch.nn.functional.linear(X, W1)), W2)
+    out.backward(torch.tensor(dout))
+    np.testing.assert_allclose(g.dx, X.grad.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(g.dw1[0], W1.grad.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(g.dw2[0], W2.grad.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(g.dw_r, 0.0)
+    np.testing.assert_array_equal(g.db_r, 0.0)
+
+
+def pin_backward_everything_dropped(so):
+    """c = 0: every token rides the residual, so the experts get no gradient,
+    the gate gets none, and the input gradient is dout plus the aux loss's
+    path through the router (dz = dL_aux/dz)."""
+    x, w_r, b_r, w1, w2 = _fd_problem(44)
+    dout = _rng(45).standard_normal(x.shape)
+    g = so.layer_backward(x, w_r, b_r, w1, w2, 0.0, 0.2, dout)
+    np.testing.assert_array_equal(g.dw1, 0.0)
+    np.testing.assert_array_equal(g.dw2, 0.0)
+    np.testing.assert_array_equal(g.dgate, 0.0)
+    L = so.layer_forward(x, w_r, b_r, w1, w2, 0.0, 0.2)
+    np.testing.assert_allclose(g.dz, L.aux.dlogits, rtol=1e-15, atol=0)
+    np.testing.assert_allclose(g.dx, dout + L.aux.dlogits @ w_r.T, rtol=1e-13, atol=1e-15)
+
+
+BACKWARD_PINS = [pin_backward_finite_differences, pin_backward_single_expert_is_dense_mlp,
+                 pin_backward_everything_dropped]
+ALL_PINS.extend(BACKWARD_PINS)

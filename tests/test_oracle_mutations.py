@@ -297,3 +297,31 @@ def test_group_topk_pins_catch_mutant(mutate):
         except Exception:
             failed.append(pin.__name__)
     assert failed, f"no grouped/top-k pin caught {mutate.__name__}"
+
+
+# ------------------------------------ layer backward: mistakes planted in the source text
+BACKWARD_EDITS = [
+    ("da = (dy @ W2) * (a > 0)", "da = dy @ W2"),                                   # no ReLU mask
+    ("dy = g[:, None] * dout[toks]", "dy = dout[toks]"),                             # gate dropped
+    ("dz = (dgate * r.gate)[:, None] * (onehot - r.p)",
+     "dz = (dgate * r.gate)[:, None] * (r.p - onehot)"),                             # softmax sign
+    ("dx = dx + dz @ w_r64.T", "dx = dx"),                                           # no router path
+    ("dw2[e] = dy.T @ h", "dw2[e] = dy.T @ a"),                                      # pre-activation
+    ("dz = dz + L.aux.dlogits", "dz = dz"),                                          # aux gradient lost
+    ("dgate[toks] = np.sum(dout[toks] * y, axis=1)", "dgate[toks] = np.sum(dout[toks] * h @ W2.T * g[:, None], axis=1)"),
+]
+
+
+@pytest.mark.parametrize("edit", BACKWARD_EDITS, ids=lambda e: e[1][:30])
+def test_backward_pins_catch_mutant(edit):
+    old, new = edit
+    assert SRC.count(old) == 1, old
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(SRC.replace(old, new), "oracle_mutant", "exec"), mod.__dict__)
+    failed = []
+    for pin in pins.BACKWARD_PINS:
+        try:
+            pin(mod)
+        except Exception:
+            failed.append(pin.__name__)
+    assert failed, f"no backward pin caught {new}"
