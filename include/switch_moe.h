@@ -250,6 +250,8 @@ typedef struct switch_layer_args {
     int64_t group;               /* tokens per routing group */
     int32_t *slot;               /*     [T, k] buffer row of each kept choice, -1 if dropped */
     int32_t *accepted_total;     /*     [E] filled buffer rows per expert */
+    switch_bf16 *h;              /*     [E, rows, d_ff] hidden activations relu(buf W1^T) in bf16,
+                                  *     kept for switch_layer_bwd */
 } switch_layer_args;
 
 switch_status switch_layer_fwd(const switch_layer_args *a, void *ws, size_t ws_bytes, void *stream);
@@ -320,6 +322,63 @@ switch_status switch_combine_ex(const float *y, const int32_t *expert, const int
 switch_status switch_aux_loss_ex(const int32_t *counts, const float *prob_sum, const float *logits,
                                  const float *lse, int64_t T, int32_t E, int32_t k, int64_t group, float alpha,
                                  float *f, float *P, float *loss, float *dlogits, void *stream);
+
+/* ------------------------------------------------------------- backward
+ *
+ * Gradients of  J = sum_t <dout_t, out_t> + L_aux (+ L_z)  for the Switch
+ * layer (one routing group, k = 1), with the choices and capacity masks of
+ * the forward held fixed: argmax has no gradient and the router learns
+ * through the selected gate.  Sources: wq-win note sec. 2 (the router stays
+ * differentiable through p_e*; the balance loss is added to the training
+ * loss); zffjzz.top note, "troubleshooting" (finite differences that keep the
+ * discrete choices and masks).
+ *
+ * For a kept token t with expert e and slot s, a_t = W1_e x_t, g_t = gate_t:
+ *   dgate_t = <dout_t, y[e, s]>;  dy = g_t dout_t;  dA = (dy W2_e) * [a_t > 0]
+ *   dW2_e = sum dy relu(a)^T;  dW1_e = sum dA x^T;  dx_t = dout_t + dA W1_e
+ *   dz_tj = dgate_t g_t (delta_{j e} - p_tj) + dL_aux/dz_tj (+ dL_z/dz_tj)
+ *   dW_r = x^T dz;  db_r = sum_t dz_t;  dx_t += W_r dz_t
+ * Dropped tokens: dx_t = dout_t + W_r dz_t.
+ *
+ * Precision: dy and dA are rounded to bf16 (the MFMA inputs), the GEMMs
+ * accumulate in fp32, weight and router gradients are fp32, dx is rounded to
+ * bf16 once.  dz, dgate and the reductions over tokens (db_r, dW_r) are fp32
+ * with fp64 sums in a fixed order.  The aux gradient treats f as constant. */
+typedef struct switch_layer_bwd_args {
+    /* saved by switch_layer_fwd (with logits and h requested) */
+    const switch_bf16 *x;        /* [T, d] */
+    const float *w_r;            /* [d, E] */
+    const switch_bf16 *w1;       /* [E, d_ff, d] */
+    const switch_bf16 *w2;       /* [E, d, d_ff] */
+    const int32_t *expert;       /* [T] */
+    const float *gate;           /* [T] */
+    const int32_t *position;     /* [T] */
+    const uint8_t *keep;         /* [T] */
+    const int32_t *accepted;     /* [E] */
+    const float *f;              /* [E] load fractions of the aux loss */
+    const float *logits;         /* [T, E] */
+    const float *lse;            /* [T] */
+    const switch_bf16 *buf;      /* [E, C, d] */
+    const switch_bf16 *h;        /* [E, C, d_ff] */
+    const float *y;              /* [E, C, d] */
+    const switch_bf16 *dout;     /* [T, d] gradient at the layer output */
+    /* outputs */
+    switch_bf16 *dx;             /* [T, d] */
+    float *dw_r;                 /* [d, E] */
+    float *db_r;                 /* [E] */
+    float *dw1;                  /* [E, d_ff, d] */
+    float *dw2;                  /* [E, d, d_ff] */
+    float *dz;                   /*     [T, E] total gradient at the logits, or NULL */
+    float *dgate;                /*     [T] <dout_t, y_t> for kept tokens (0 if dropped), or NULL */
+    /* sizes */
+    int64_t T;
+    int32_t d, d_ff, E, C;
+    float alpha;                 /* aux-loss weight of the forward */
+    float z_beta;                /* z-loss weight (0: no z-loss term) */
+} switch_layer_bwd_args;
+
+size_t switch_layer_bwd_workspace_bytes(int64_t T, int32_t d, int32_t d_ff, int32_t E, int32_t C);
+switch_status switch_layer_bwd(const switch_layer_bwd_args *a, void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------- measurement */
 

@@ -661,9 +661,14 @@ class LayerGrads(NamedTuple):
 
 def layer_backward(x, w_r, b_r, w1, w2, c: float, alpha: float, dout, beta: float = 0.0,
                    C: Optional[int] = None, expert_override: Optional[np.ndarray] = None,
-                   forward: Optional[LayerResult] = None) -> LayerGrads:
+                   forward: Optional[LayerResult] = None, relu_active=None) -> LayerGrads:
     """Gradients of J = sum_t <dout_t, out_t> + L_aux (+ L_z) for the Switch
-    layer (one routing group, k = 1), in float64, expert by expert."""
+    layer (one routing group, k = 1), in float64, expert by expert.
+
+    relu_active(e, a) may replace the ReLU derivative [a > 0] of expert e's
+    kept rows (a: their pre-activations, tokens in order); tests use it to
+    take the device's decision on pre-activations within rounding of zero,
+    as `expert_override` does for near-tie choices."""
     x = np.asarray(x, np.float64)
     dout = np.asarray(dout, np.float64)
     L = forward if forward is not None else layer_forward(x, w_r, b_r, w1, w2, c, alpha, C=C,
@@ -691,7 +696,8 @@ def layer_backward(x, w_r, b_r, w1, w2, c: float, alpha: float, dout, beta: floa
         dgate[toks] = np.sum(dout[toks] * y, axis=1)
         dy = g[:, None] * dout[toks]
         dw2[e] = dy.T @ h
-        da = (dy @ W2) * (a > 0)
+        active = (a > 0) if relu_active is None else relu_active(e, a)
+        da = (dy @ W2) * active
         dw1[e] = da.T @ xe
         dx[toks] += da @ W1
     onehot = np.zeros((T, E))

@@ -27,7 +27,7 @@ EXPORTS = [
     "switch_combine", "switch_aux_loss", "switch_layer_fwd", "switch_stream_copy", "switch_profile_enable",
     "switch_profile_collect", "switch_kernel_name", "switch_router_z_loss",
     "switch_route_ex", "switch_dispatch_ex", "switch_dispatch_workspace_bytes_ex", "switch_combine_ex",
-    "switch_aux_loss_ex", "switch_workspace_bytes_ex",
+    "switch_aux_loss_ex", "switch_workspace_bytes_ex", "switch_layer_bwd", "switch_layer_bwd_workspace_bytes",
 ]
 
 
@@ -45,7 +45,16 @@ class LayerArgs(ctypes.Structure):
         ("T", ctypes.c_int64), ("d", ctypes.c_int32), ("d_ff", ctypes.c_int32), ("E", ctypes.c_int32),
         ("C", ctypes.c_int32), ("alpha", ctypes.c_float), ("z_beta", ctypes.c_float), ("residual", ctypes.c_int32),
         ("k", ctypes.c_int32), ("priority", ctypes.c_int32), ("group", ctypes.c_int64),
-        ("slot", ctypes.c_void_p), ("accepted_total", ctypes.c_void_p)]
+        ("slot", ctypes.c_void_p), ("accepted_total", ctypes.c_void_p), ("h", ctypes.c_void_p)]
+
+
+class LayerBwdArgs(ctypes.Structure):
+    """Mirror of switch_layer_bwd_args."""
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "x", "w_r", "w1", "w2", "expert", "gate", "position", "keep", "accepted", "f", "logits", "lse", "buf", "h",
+        "y", "dout", "dx", "dw_r", "db_r", "dw1", "dw2", "dz", "dgate")] + [
+        ("T", ctypes.c_int64), ("d", ctypes.c_int32), ("d_ff", ctypes.c_int32), ("E", ctypes.c_int32),
+        ("C", ctypes.c_int32), ("alpha", ctypes.c_float), ("z_beta", ctypes.c_float)]
 
 
 def lib():
@@ -83,6 +92,8 @@ def lib():
             "switch_combine_ex": (I32, [P, P, P, P, P, P, I64, I32, I32, I32, I32, P, P]),
             "switch_aux_loss_ex": (I32, [P, P, P, P, I64, I32, I32, I64, F32, P, P, P, P, P]),
             "switch_workspace_bytes_ex": (SZ, [I64, I32, I32, I32, I32, I32, I64]),
+            "switch_layer_bwd_workspace_bytes": (SZ, [I64, I32, I32, I32, I32]),
+            "switch_layer_bwd": (I32, [ctypes.POINTER(LayerBwdArgs), P, SZ, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -226,6 +237,50 @@ def switch_layer_fwd(args: LayerArgs, ws, stream=None):
     _check(lib().switch_layer_fwd(ctypes.byref(args), wp, wn, _stream(stream)), "switch_layer_fwd")
 
 
+def switch_layer_bwd_workspace_bytes(T, d, d_ff, E, C):
+    return lib().switch_layer_bwd_workspace_bytes(T, d, d_ff, E, C)
+
+
+def switch_layer_bwd(args: LayerBwdArgs, ws, stream=None):
+    wp, wn = _ws(ws)
+    _check(lib().switch_layer_bwd(ctypes.byref(args), wp, wn, _stream(stream)), "switch_layer_bwd")
+
+
+def make_layer_bwd_args(fwd: dict, x, w_r, w1, w2, dout, grads: dict, T, d, d_ff, E, C, alpha,
+                        z_beta=0.0) -> LayerBwdArgs:
+    """fwd: the forward's tensors (expert, gate, position, keep, accepted, f,
+    logits, lse, buf, h, y); grads: dx, dw_r, db_r, dw1, dw2 and optionally
+    dz, dgate."""
+    a = LayerBwdArgs()
+    for name, v in (("x", x), ("w_r", w_r), ("w1", w1), ("w2", w2), ("dout", dout)):
+        setattr(a, name, _ptr(v))
+    for name in ("expert", "gate", "position", "keep", "accepted", "f", "logits", "lse", "buf", "h", "y"):
+        setattr(a, name, _ptr(fwd.get(name)))
+    for name in ("dx", "dw_r", "db_r", "dw1", "dw2", "dz", "dgate"):
+        setattr(a, name, _ptr(grads.get(name)))
+    a.T, a.d, a.d_ff, a.E, a.C, a.alpha, a.z_beta = T, d, d_ff, E, C, alpha, z_beta
+    return a
+
+
+def layer_bwd_tensors(T, d, d_ff, E, C, device="cuda", inspect=False):
+    """Gradient tensors of switch_layer_bwd (plus its workspace)."""
+    import torch
+    dev = torch.device(device)
+    g = {
+        "dx": torch.empty((T, d), dtype=torch.bfloat16, device=dev),
+        "dw_r": torch.empty((d, E), dtype=torch.float32, device=dev),
+        "db_r": torch.empty(E, dtype=torch.float32, device=dev),
+        "dw1": torch.empty((E, d_ff, d), dtype=torch.float32, device=dev),
+        "dw2": torch.empty((E, d, d_ff), dtype=torch.float32, device=dev),
+    }
+    if inspect:
+        g["dz"] = torch.empty((T, E), dtype=torch.float32, device=dev)
+        g["dgate"] = torch.empty(T, dtype=torch.float32, device=dev)
+    g["ws"] = torch.empty(max(256, switch_layer_bwd_workspace_bytes(T, d, d_ff, E, C)), dtype=torch.uint8,
+                          device=dev)
+    return g
+
+
 def switch_stream_copy(dst, src, nbytes: int, stream=None):
     _check(lib().switch_stream_copy(_ptr(dst), _ptr(src), nbytes, _stream(stream)), "switch_stream_copy")
 
@@ -246,7 +301,7 @@ def switch_profile_collect(max_records: int = 1 << 16):
 
 # ------------------------------------------------------------ allocation helpers
 def layer_tensors(T, d, d_ff, E, C, device="cuda", logits=False, dlogits=False, inspect=False, z_loss=False,
-                  k=1, group=0):
+                  k=1, group=0, for_backward=False):
     """Output tensors of switch_layer_fwd (plus a workspace), allocated with torch.
     With k choices the per-choice arrays are [T, k]; with several routing groups
     of `group` tokens the per-expert statistics are [T // group, E], C is the
@@ -273,6 +328,9 @@ def layer_tensors(T, d, d_ff, E, C, device="cuda", logits=False, dlogits=False, 
     if ng != 1:
         o["slot"] = torch.empty((T,) + kk, dtype=torch.int32, device=dev)
         o["accepted_total"] = torch.empty(E, dtype=torch.int32, device=dev)
+    if for_backward:   # what switch_layer_bwd reads besides the inputs
+        logits = inspect = True
+        o["h"] = torch.empty((E, rows, d_ff), dtype=torch.bfloat16, device=dev)
     if logits or dlogits:
         o["logits"] = torch.empty((T, E), dtype=torch.float32, device=dev)
     if dlogits:
@@ -294,7 +352,7 @@ def make_layer_args(x, w_r, b_r, w1, w2, t: dict, T, d, d_ff, E, C, alpha, resid
     for name, v in (("x", x), ("w_r", w_r), ("b_r", b_r), ("w1", w1), ("w2", w2)):
         setattr(a, name, _ptr(v))
     for name in ("out", "expert", "gate", "position", "keep", "counts", "accepted", "f", "P", "loss", "logits",
-                 "lse", "prob_sum", "dlogits", "slot_token", "buf", "y", "z_loss", "slot", "accepted_total"):
+                 "lse", "prob_sum", "dlogits", "slot_token", "buf", "y", "z_loss", "slot", "accepted_total", "h"):
         setattr(a, name, _ptr(t.get(name)))
     a.T, a.d, a.d_ff, a.E, a.C, a.alpha, a.residual = T, d, d_ff, E, C, alpha, 1 if residual else 0
     a.z_beta = z_beta

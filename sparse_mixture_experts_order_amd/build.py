@@ -14,7 +14,7 @@ CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libswitch_moe.so")
 OBJ = os.path.join(PKG, "_build")
-SOURCES = ["route.hip", "dispatch.hip", "expert_ffn.hip", "combine.hip", "aux.hip", "api.hip"]
+SOURCES = ["route.hip", "dispatch.hip", "expert_ffn.hip", "combine.hip", "aux.hip", "backward.hip", "api.hip"]
 ARCH = os.environ.get("SWITCH_MOE_ARCH", "gfx950")
 
 

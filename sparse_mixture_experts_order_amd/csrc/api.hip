@@ -34,11 +34,15 @@ switch_status hip_fail(hipError_t e, const char* where) {
 // ----------------------------------------------------------- launch timing
 enum KernelId {
     K_SPLIT = 0, K_RGEMM, K_RSOFTMAX, K_RREDUCE, K_SCAN_LOCAL, K_SCAN_OFFSETS, K_GATHER,
-    K_GEMM1, K_GEMM2, K_COMBINE, K_AUX_STATS, K_AUX_GRAD, K_COPY, K_FFN_TILES, K_Z_LOSS, K_RFUSED, K_COUNT
+    K_GEMM1, K_GEMM2, K_COMBINE, K_AUX_STATS, K_AUX_GRAD, K_COPY, K_FFN_TILES, K_Z_LOSS, K_RFUSED,
+    K_COMBINE_BWD, K_ROUTER_DZ, K_ROUTER_DB, K_ROUTER_WGRAD, K_TRANSPOSE, K_GEMM_DA, K_GEMM_DBUF, K_GEMM_DW2,
+    K_GEMM_DW1, K_DX, K_COUNT
 };
 const char* kKernelNames[K_COUNT] = {
     "split_router_weights", "router_gemm", "router_softmax", "router_reduce", "scan_local", "scan_offsets",
-    "gather", "expert_gemm1", "expert_gemm2", "combine", "aux_stats", "aux_grad", "stream_copy", "ffn_tile_prefix", "z_loss", "router_fused"};
+    "gather", "expert_gemm1", "expert_gemm2", "combine", "aux_stats", "aux_grad", "stream_copy", "ffn_tile_prefix", "z_loss", "router_fused",
+    "combine_bwd", "router_dz", "router_db", "router_wgrad", "transpose_rows", "gemm_dA", "gemm_dbuf", "gemm_dW2",
+    "gemm_dW1", "dx_assemble"};
 
 struct ProfRec { int id; hipEvent_t a, b; };
 bool g_prof = false;
@@ -284,6 +288,7 @@ switch_status run_dispatch(const DispatchArgs& a, void* ws, hipStream_t s) {
 struct FfnArgs {
     const bf16_t* buf; const int32_t* accepted; const bf16_t* w1; const bf16_t* w2;
     int32_t E, C, d, d_ff; float* y;
+    bf16_t* h = nullptr;   // [E, C, d_ff] hidden activations; NULL: workspace only
 };
 
 switch_status validate_ffn(const FfnArgs& a, const void* ws, size_t ws_bytes) {
@@ -295,7 +300,7 @@ switch_status validate_ffn(const FfnArgs& a, const void* ws, size_t ws_bytes) {
     SUPPORT((int64_t)a.E * a.C * std::max(a.d, a.d_ff) < (int64_t(1) << 40), "E*C*max(d,d_ff) too large");
     NONNULL(a.accepted); NONNULL(a.w1); NONNULL(a.w2);
     if (a.C > 0) { NONNULL(a.buf); NONNULL(a.y); }
-    ALIGNED16(a.buf); ALIGNED16(a.w1); ALIGNED16(a.w2); ALIGNED16(a.y); ALIGNED4(a.accepted);
+    ALIGNED16(a.buf); ALIGNED16(a.w1); ALIGNED16(a.w2); ALIGNED16(a.y); ALIGNED4(a.accepted); ALIGNED16(a.h);
     const size_t need = ffn_ws(a.E, a.C, a.d_ff);
     if (ws_bytes < need) return fail(SWITCH_E_WORKSPACE, "expert_ffn needs %zu workspace bytes, got %zu", need, ws_bytes);
     REQUIRE(need == 0 || ws != nullptr, "ws must not be NULL");
@@ -307,6 +312,7 @@ switch_status run_ffn(const FfnArgs& a, void* ws, hipStream_t s) {
     if (a.C == 0) return SWITCH_OK;
     Carver c{(char*)ws};
     bf16_t* h = c.take<bf16_t>((size_t)a.E * a.C * a.d_ff);
+    if (a.h) h = a.h;
     int32_t* pre = c.take<int32_t>((size_t)a.E + 1);
     int4* ttab = c.take<int4>(ffn_tile_table_entries(a.E, a.C));
     LAUNCH(K_FFN_TILES, "ffn_tile_prefix", s, launch_ffn_tile_prefix(a.accepted, a.E, a.C, pre, ttab, s));
@@ -375,7 +381,8 @@ switch_status run_aux(const AuxArgs& a, hipStream_t s) {
     if (a.z_loss) LAUNCH(K_Z_LOSS, "z_loss", s, launch_z_loss(a.lse, a.T, a.beta, a.z_loss, s));
     if (a.dlogits && a.T > 0)
         LAUNCH(K_AUX_GRAD, "aux_grad", s,
-               launch_aux_grad(a.logits, a.lse, a.f, a.T, Gt, a.E, a.alpha, a.z_loss ? a.beta : 0.f, 0, a.dlogits,
+               launch_aux_grad(a.logits, a.lse, a.f, a.T, Gt, a.E, a.alpha, a.z_loss ? a.beta : 0.f, nullptr, nullptr,
+                               nullptr, 0, a.dlogits,
                                s));
     return SWITCH_OK;
 }
@@ -466,6 +473,128 @@ static size_t layer_ws(int64_t T, int32_t d, int32_t d_ff, int32_t E, int32_t C,
         n += up((size_t)E * sizeof(int32_t));        // accepted rows per expert
     }
     return n;
+}
+
+// ----------------------------------------------------------- layer backward
+static int64_t pad64(int64_t n) { return (n + 63) / 64 * 64; }
+
+static size_t layer_bwd_ws(int64_t T, int32_t d, int32_t d_ff, int32_t E, int32_t C) {
+    const size_t Cp = (size_t)pad64(C), e = (size_t)E;
+    size_t n = 0;
+    n += up(e * C * d * sizeof(bf16_t));          // dy
+    n += up(e * d * Cp * sizeof(bf16_t));         // dy^T
+    n += up(e * d_ff * Cp * sizeof(bf16_t));      // H^T
+    n += up(e * C * d_ff * sizeof(bf16_t));       // dA
+    n += up(e * d_ff * Cp * sizeof(bf16_t));      // dA^T
+    n += up(e * d * Cp * sizeof(bf16_t));         // buf^T
+    n += 2 * up(e * d * d_ff * sizeof(bf16_t));   // W1^T, W2^T
+    n += up(e * C * d * sizeof(float));           // dbuf
+    n += up((size_t)T * E * sizeof(float));       // dz
+    n += up((size_t)T * sizeof(float));           // dgate
+    n += up((size_t)std::max(router_wgrad_slices(T, d, E), 1) * d * E * sizeof(float));   // dW_r slices
+    n += 3 * up((e + 1) * sizeof(int32_t));       // tile prefixes: token rows, d rows, d_ff rows
+    n += up(ffn_tile_table_entries(E, C) * sizeof(int4)) + up(ffn_tile_table_entries(E, d) * sizeof(int4)) +
+         up(ffn_tile_table_entries(E, d_ff) * sizeof(int4));
+    return n;
+}
+
+size_t switch_layer_bwd_workspace_bytes(int64_t T, int32_t d, int32_t d_ff, int32_t E, int32_t C) {
+    if (T < 0 || d < 1 || d_ff < 1 || E < 1 || E > 4096 || C < 0 || T >= (int64_t(1) << 31)) return 0;
+    return layer_bwd_ws(T, d, d_ff, E, C);
+}
+
+switch_status switch_layer_bwd(const switch_layer_bwd_args* ba, void* ws, size_t ws_bytes, void* stream) {
+    g_err.clear();
+    if (!ba) return fail(SWITCH_E_INVALID, "args must not be NULL");
+    const switch_layer_bwd_args& B = *ba;
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t T = B.T;
+    const int32_t d = B.d, F = B.d_ff, E = B.E, C = B.C;
+    CHECK(check_TE(T, E));
+    CHECK(check_C(E, C));
+    REQUIRE(d >= 1 && F >= 1, "d and d_ff must be >= 1");
+    SUPPORT(d % 64 == 0 && F % 64 == 0, "d and d_ff must be multiples of 64 (got %d, %d)", d, F);
+    SUPPORT((int64_t)E * std::max<int64_t>(pad64(C), std::max(d, F)) * std::max(d, F) < (int64_t(1) << 40),
+            "E*C*max(d,d_ff) too large");
+    REQUIRE(std::isfinite(B.alpha) && std::isfinite(B.z_beta), "alpha and z_beta must be finite");
+    const bool tok = T > 0;
+    NONNULL_IF(tok, B.x); NONNULL(B.w_r); NONNULL(B.w1); NONNULL(B.w2);
+    NONNULL_IF(tok, B.expert); NONNULL_IF(tok, B.gate); NONNULL_IF(tok, B.position); NONNULL_IF(tok, B.keep);
+    NONNULL(B.accepted); NONNULL(B.f); NONNULL_IF(tok, B.logits); NONNULL_IF(tok, B.lse);
+    NONNULL_IF(C > 0, B.buf); NONNULL_IF(C > 0, B.h); NONNULL_IF(C > 0, B.y); NONNULL_IF(tok, B.dout);
+    NONNULL_IF(tok, B.dx); NONNULL(B.dw_r); NONNULL(B.db_r); NONNULL(B.dw1); NONNULL(B.dw2);
+    ALIGNED16(B.x); ALIGNED16(B.w1); ALIGNED16(B.w2); ALIGNED16(B.buf); ALIGNED16(B.h); ALIGNED16(B.y);
+    ALIGNED16(B.dout); ALIGNED16(B.dx); ALIGNED16(B.dw1); ALIGNED16(B.dw2);
+    ALIGNED4(B.w_r); ALIGNED4(B.expert); ALIGNED4(B.gate); ALIGNED4(B.position); ALIGNED4(B.accepted);
+    ALIGNED4(B.f); ALIGNED4(B.logits); ALIGNED4(B.lse); ALIGNED4(B.dw_r); ALIGNED4(B.db_r); ALIGNED4(B.dz);
+    ALIGNED4(B.dgate);
+    const size_t need = layer_bwd_ws(T, d, F, E, C);
+    if (ws_bytes < need) return fail(SWITCH_E_WORKSPACE, "layer backward needs %zu workspace bytes, got %zu", need, ws_bytes);
+    REQUIRE(ws != nullptr, "ws must not be NULL");
+    REQUIRE(aligned(ws, kAlign), "ws must be %zu-byte aligned", kAlign);
+
+    const int Cp = (int)pad64(C);
+    Carver c{(char*)ws};
+    bf16_t* dy = c.take<bf16_t>((size_t)E * C * d);
+    bf16_t* dyT = c.take<bf16_t>((size_t)E * d * Cp);
+    bf16_t* hT = c.take<bf16_t>((size_t)E * F * Cp);
+    bf16_t* dA = c.take<bf16_t>((size_t)E * C * F);
+    bf16_t* dAT = c.take<bf16_t>((size_t)E * F * Cp);
+    bf16_t* bufT = c.take<bf16_t>((size_t)E * d * Cp);
+    bf16_t* w1T = c.take<bf16_t>((size_t)E * d * F);
+    bf16_t* w2T = c.take<bf16_t>((size_t)E * d * F);
+    float* dbuf = c.take<float>((size_t)E * C * d);
+    float* dz = c.take<float>((size_t)T * E);
+    float* dgate = c.take<float>((size_t)T);
+    float* part = c.take<float>((size_t)std::max(router_wgrad_slices(T, d, E), 1) * d * E);
+    int32_t* pre_c = c.take<int32_t>((size_t)E + 1);
+    int32_t* pre_d = c.take<int32_t>((size_t)E + 1);
+    int32_t* pre_f = c.take<int32_t>((size_t)E + 1);
+    int4* tt_c = c.take<int4>(ffn_tile_table_entries(E, C));
+    int4* tt_d = c.take<int4>(ffn_tile_table_entries(E, d));
+    int4* tt_f = c.take<int4>(ffn_tile_table_entries(E, F));
+    if (B.dz) dz = B.dz;
+    if (B.dgate) dgate = B.dgate;
+    const bf16_t* x = B.x;
+
+    // gate and router: dgate, then dz = task + aux (+ z) gradient, db_r, dW_r
+    LAUNCH(K_COMBINE_BWD, "combine_bwd", s,
+           launch_combine_bwd(B.dout, B.y, B.expert, B.position, B.keep, B.gate, T, d, E, C, dy, dgate, s));
+    if (tok)
+        LAUNCH(K_ROUTER_DZ, "router_dz", s,
+               launch_aux_grad(B.logits, B.lse, B.f, T, T, E, B.alpha, B.z_beta, B.expert, B.gate, dgate, 0, dz, s));
+    LAUNCH(K_ROUTER_DB, "router_db", s, launch_router_reduce(dz, (int)T, 1, E, B.db_r, s));
+    LAUNCH(K_ROUTER_WGRAD, "router_wgrad", s, launch_router_wgrad(x, dz, T, d, E, part, B.dw_r, s));
+    // experts: transposed operands, then the four grouped GEMMs
+    LAUNCH(K_TRANSPOSE, "transpose_rows", s, launch_transpose_rows(B.w2, w2T, E, d, F, d, nullptr, s));
+    LAUNCH(K_TRANSPOSE, "transpose_rows", s, launch_transpose_rows(B.w1, w1T, E, F, d, F, nullptr, s));
+    if (C > 0) {
+        LAUNCH(K_TRANSPOSE, "transpose_rows", s, launch_transpose_rows(dy, dyT, E, C, d, Cp, B.accepted, s));
+        LAUNCH(K_TRANSPOSE, "transpose_rows", s, launch_transpose_rows(B.h, hT, E, C, F, Cp, B.accepted, s));
+        LAUNCH(K_TRANSPOSE, "transpose_rows", s, launch_transpose_rows(B.buf, bufT, E, C, d, Cp, B.accepted, s));
+        LAUNCH(K_FFN_TILES, "ffn_tile_prefix", s, launch_ffn_tile_prefix(B.accepted, E, C, pre_c, tt_c, s));
+        // dA = (dy W2) * [H > 0]          rows: tokens, K = d, N = d_ff
+        LAUNCH(K_GEMM_DA, "gemm_dA", s, launch_grouped_gemm_masked(dy, w2T, pre_c, tt_c, dA, B.h, E, C, d, F, s));
+        // dbuf = dA W1                    rows: tokens, K = d_ff, N = d
+        LAUNCH(K_GEMM_DBUF, "gemm_dbuf", s, launch_grouped_gemm_f32(dA, w1T, pre_c, tt_c, dbuf, E, C, F, d, s));
+        LAUNCH(K_TRANSPOSE, "transpose_rows", s, launch_transpose_rows(dA, dAT, E, C, F, Cp, B.accepted, s));
+    }
+    // weight gradients: K = the (zero-padded) token axis
+    LAUNCH(K_FFN_TILES, "ffn_tile_prefix", s, launch_ffn_tile_prefix(nullptr, E, d, pre_d, tt_d, s));
+    LAUNCH(K_FFN_TILES, "ffn_tile_prefix", s, launch_ffn_tile_prefix(nullptr, E, F, pre_f, tt_f, s));
+    if (C > 0) {
+        // dW2[e] = dy^T H                 rows: d, K = tokens, N = d_ff
+        LAUNCH(K_GEMM_DW2, "gemm_dW2", s, launch_grouped_gemm_f32(dyT, hT, pre_d, tt_d, B.dw2, E, d, Cp, F, s));
+        // dW1[e] = dA^T buf               rows: d_ff, K = tokens, N = d
+        LAUNCH(K_GEMM_DW1, "gemm_dW1", s, launch_grouped_gemm_f32(dAT, bufT, pre_f, tt_f, B.dw1, E, F, Cp, d, s));
+    } else {
+        LAUNCH(K_GEMM_DW2, "zero", s, launch_fill_zero(B.dw2, (int64_t)E * d * F, s));
+        LAUNCH(K_GEMM_DW1, "zero", s, launch_fill_zero(B.dw1, (int64_t)E * d * F, s));
+    }
+    // dx = dout + dbuf (kept tokens) + dz W_r^T
+    LAUNCH(K_DX, "dx_assemble", s,
+           launch_dx_assemble(B.dout, dbuf, B.expert, B.position, B.keep, dz, B.w_r, T, d, E, C, B.dx, s));
+    return SWITCH_OK;
 }
 
 size_t switch_workspace_bytes(int64_t T, int32_t d, int32_t d_ff, int32_t E, int32_t C) {
@@ -598,7 +727,8 @@ switch_status switch_router_z_loss(const float* lse, const float* logits, int64_
     LAUNCH(K_Z_LOSS, "z_loss", s, launch_z_loss(lse, T, beta, z_loss, s));
     if (dlogits && T > 0)
         LAUNCH(K_AUX_GRAD, "aux_grad", s,
-               launch_aux_grad(logits, lse, nullptr, T, T, E, 0.f, beta, accumulate, dlogits, s));
+               launch_aux_grad(logits, lse, nullptr, T, T, E, 0.f, beta, nullptr, nullptr, nullptr, accumulate,
+                               dlogits, s));
     return SWITCH_OK;
 }
 
@@ -653,7 +783,7 @@ switch_status switch_layer_fwd(const switch_layer_args* la, void* ws, size_t ws_
     RouteArgs ra{L.x, L.w_r, L.b_r, nullptr, L.T, L.d, L.E, logits, L.expert, L.gate, lse, prob_sum, k, G};
     DispatchArgs da{L.x, L.expert, L.T, L.d, L.E, L.C, L.position, L.keep, L.counts, L.accepted, L.slot_token, buf,
                     k, G, L.priority, slot, acc_total};
-    FfnArgs fa{buf, filled, L.w1, L.w2, L.E, rows, L.d, L.d_ff, y};
+    FfnArgs fa{buf, filled, L.w1, L.w2, L.E, rows, L.d, L.d_ff, y, L.h};
     CombineArgs ca{y, L.expert, rows_of, L.keep, L.gate, L.residual ? L.x : nullptr, L.T, L.d, L.E, rows, L.out, k};
     AuxArgs xa{L.counts, prob_sum, logits, lse, L.T, L.E, L.alpha, L.f, L.P, L.loss, L.dlogits, L.z_beta, L.z_loss,
                k, G};

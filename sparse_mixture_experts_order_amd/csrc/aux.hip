@@ -64,12 +64,17 @@ __global__ __launch_bounds__(1024) void z_loss_reduce(const float* __restrict__ 
 //   G_tj = p_tj * (c_aux (f_j - sum_e f_e p_te) + c_z lse_t)
 // c_aux = alpha E / T (aux, f held constant; f is the row of the token's
 // routing group of G tokens), c_z = 2 beta / T (z-loss).
+// With dgate (the layer backward) the task gradient through the selected gate
+// is added:  + dgate_t gate_t (delta_{j e*_t} - p_tj)  (d p_te / d z_tj =
+// p_te (delta_ej - p_tj)).
 // One wave per token row; lane j holds experts j, j+64, ...  With
 // `accumulate` the result is added to dlogits instead of stored.
 template <int NCH>
 __global__ __launch_bounds__(256) void aux_grad(const float* __restrict__ logits, const float* __restrict__ lse,
                                                 const float* __restrict__ f, int64_t T, int64_t G, int E, float c_aux,
-                                                float c_z, int accumulate, float* __restrict__ dlogits) {
+                                                float c_z, const int32_t* __restrict__ expert,
+                                                const float* __restrict__ gate, const float* __restrict__ dgate,
+                                                int accumulate, float* __restrict__ dlogits) {
     const int lane = threadIdx.x & 63;
     const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
@@ -87,12 +92,14 @@ __global__ __launch_bounds__(256) void aux_grad(const float* __restrict__ logits
     }
     s = wave_sum(s);
     const float zt = c_z * l;
+    const float dg = dgate ? dgate[t] * gate[t] : 0.f;
+    const int es = dgate ? expert[t] : -1;
     float* g = dlogits + t * E;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
         const int e = lane + 64 * i;
         if (e < E) {
-            const float v = p[i] * (c_aux * (fr[i] - s) + zt);
+            const float v = p[i] * (c_aux * (fr[i] - s) + zt - dg) + (e == es ? dg : 0.f);
             g[e] = accumulate ? g[e] + v : v;
         }
     }
@@ -110,7 +117,8 @@ hipError_t launch_z_loss(const float* lse, int64_t T, float beta, float* z_loss,
 }
 
 hipError_t launch_aux_grad(const float* logits, const float* lse, const float* f, int64_t T, int64_t G, int E,
-                           float alpha, float beta, int accumulate, float* dlogits, hipStream_t s) {
+                           float alpha, float beta, const int32_t* expert, const float* gate, const float* dgate,
+                           int accumulate, float* dlogits, hipStream_t s) {
     if (T == 0) return hipSuccess;
     const float c_aux = f ? (float)((double)alpha * (double)E / (double)T) : 0.f;
     const float c_z = (float)(2.0 * (double)beta / (double)T);
@@ -118,7 +126,7 @@ hipError_t launch_aux_grad(const float* logits, const float* lse, const float* f
     const int nch = (E + 63) / 64;
 #define SWMOE_GRAD(N)                                                                                          \
     hipLaunchKernelGGL(aux_grad<N>, dim3(grid), dim3(256), 0, s, logits, lse, f, T, std::max<int64_t>(G, 1), E, \
-                       c_aux, c_z, accumulate, dlogits)
+                       c_aux, c_z, expert, gate, dgate, accumulate, dlogits)
     if (nch <= 1) SWMOE_GRAD(1);
     else if (nch <= 2) SWMOE_GRAD(2);
     else if (nch <= 4) SWMOE_GRAD(4);

@@ -40,7 +40,8 @@ constexpr int FFN_LDS_STRIDE = 72;  // bf16 elements per token row in LDS (64 + 
 
 // Token-tile list: pre[e] = number of valid TOK-row token tiles of experts < e
 // (pre[E] = total V), and ttab[v] = {expert, first row, valid rows, 0} for
-// v = pre[e] + tt, the token tiles of each expert in row order.
+// v = pre[e] + tt, the token tiles of each expert in row order.  accepted ==
+// NULL means every expert has all C rows.
 __global__ __launch_bounds__(1024) void ffn_tile_prefix(const int32_t* __restrict__ accepted, int E, int C, int TOK,
                                                         int32_t* __restrict__ pre, int4* __restrict__ ttab) {
     __shared__ int wsum[16];
@@ -49,7 +50,7 @@ __global__ __launch_bounds__(1024) void ffn_tile_prefix(const int32_t* __restric
     int local = 0;
     for (int i = 0; i < per; ++i) {
         const int e = e0 + i;
-        if (e < E) local += (min(max(accepted[e], 0), C) + TOK - 1) / TOK;
+        if (e < E) local += (min(max(accepted ? accepted[e] : C, 0), C) + TOK - 1) / TOK;
     }
     // exclusive scan of `local` over the block: waves, then wave totals in order
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -68,7 +69,7 @@ __global__ __launch_bounds__(1024) void ffn_tile_prefix(const int32_t* __restric
         const int e = e0 + i;
         if (e < E) {
             pre[e] = run;
-            const int a = min(max(accepted[e], 0), C);
+            const int a = min(max(accepted ? accepted[e] : C, 0), C);
             for (int tt = 0; tt * TOK < a; ++tt) ttab[run + tt] = make_int4(e, tt * TOK, min(TOK, a - tt * TOK), 0);
             run += (a + TOK - 1) / TOK;
         }
@@ -95,23 +96,29 @@ __device__ __forceinline__ FfnTile decode_tile(int i, const int4* __restrict__ t
     return t;
 }
 
+// Output modes: bf16(ReLU(.)) (the first expert GEMM), fp32 (the second one,
+// and the gradients that reuse this kernel), and bf16 masked by a second
+// array (the backward of the ReLU: zero wherever the saved activation is 0).
+enum FfnOut { OUT_RELU_BF16 = 0, OUT_F32 = 1, OUT_MASK_BF16 = 2 };
+
 // TOKB: 32-row token blocks per tile; NBW: 32-row weight blocks per wave;
 // WAVES: waves per workgroup; R: depth of the register rings; PB: bytes of an
-// output row staged through LDS per pass.  GEMM1 writes bf16(ReLU(.)), GEMM2
-// writes fp32.
-template <int TOKB, int NBW, int WAVES, int R, bool GEMM1, int PB>
+// output row staged through LDS per pass; MODE: an FfnOut.
+template <int TOKB, int NBW, int WAVES, int R, int MODE, int PB>
 __global__ __launch_bounds__(64 * WAVES) void expert_gemm(const bf16_t* __restrict__ A,   // [E, C, K]
                                                           const bf16_t* __restrict__ W,   // [E, N, K]
                                                           const int32_t* __restrict__ pre,
                                                           const int4* __restrict__ ttab,
                                                           void* __restrict__ out,         // [E, C, N]
+                                                          const bf16_t* __restrict__ mask, // [E, C, N] (OUT_MASK_BF16)
                                                           int E, int C, int K, int N, int n_tiles) {
+    constexpr bool BF16_OUT = MODE != OUT_F32;
     constexpr int TOK = 32 * TOKB;
     constexpr int NWG = WAVES * 32 * NBW;
     constexpr int NTHR = 64 * WAVES;
     constexpr int PIECES = TOK * 8;                       // 16-byte pieces of one token chunk
     constexpr int APT = (PIECES + NTHR - 1) / NTHR;       // pieces per thread
-    constexpr int OUT_BYTES = GEMM1 ? 2 : 4;
+    constexpr int OUT_BYTES = BF16_OUT ? 2 : 4;
     constexpr int ROW_BYTES = NWG * OUT_BYTES;                        // output bytes per token row
     constexpr int PASS_BYTES = ROW_BYTES <= PB ? ROW_BYTES
                                : (ROW_BYTES % PB == 0 ? PB : (ROW_BYTES % (PB / 2) == 0 ? PB / 2 : PB / 4));
@@ -250,11 +257,15 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm(const bf16_t* __restri
                                         const int c = c0 + nb * 32 + q * 8 + half * 4;
                                         const f32x16& a = acc[nb][tb];
                                         char* dst = lds_o + (tb * 32 + l32) * OSTRIDE + c * OUT_BYTES;
-                                        if constexpr (GEMM1) {
+                                        if constexpr (MODE == OUT_RELU_BF16) {
                                             const uint32_t b0 = bf16_rne(fmaxf(a[4 * q + 0], 0.f));
                                             const uint32_t b1 = bf16_rne(fmaxf(a[4 * q + 1], 0.f));
                                             const uint32_t b2 = bf16_rne(fmaxf(a[4 * q + 2], 0.f));
                                             const uint32_t b3 = bf16_rne(fmaxf(a[4 * q + 3], 0.f));
+                                            *(uint2*)dst = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+                                        } else if constexpr (MODE == OUT_MASK_BF16) {
+                                            const uint32_t b0 = bf16_rne(a[4 * q + 0]), b1 = bf16_rne(a[4 * q + 1]);
+                                            const uint32_t b2 = bf16_rne(a[4 * q + 2]), b3 = bf16_rne(a[4 * q + 3]);
                                             *(uint2*)dst = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
                                         } else {
                                             *(f32x4*)dst = f32x4{a[4 * q + 0], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
@@ -269,8 +280,21 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm(const bf16_t* __restri
                         for (int it = 0; it < (TOK * VPR + NTHR - 1) / NTHR; ++it) {
                             const int i = threadIdx.x + it * NTHR;
                             const int r = i / VPR, v = i - r * VPR;
-                            if (i < TOK * VPR && r < t.nv && v < vpr_valid)
-                                *(u32x4*)(gout + (size_t)r * N * OUT_BYTES + v * 16) = *(const u32x4*)(lds_o + r * OSTRIDE + v * 16);
+                            if (i < TOK * VPR && r < t.nv && v < vpr_valid) {
+                                u32x4 val = *(const u32x4*)(lds_o + r * OSTRIDE + v * 16);
+                                if constexpr (MODE == OUT_MASK_BF16) {
+                                    // keep the elements whose saved activation is non-zero
+                                    const size_t off = (size_t)(gout - (char*)out) + (size_t)r * N * OUT_BYTES + v * 16;
+                                    const u32x4 m = *(const u32x4*)((const char*)mask + off);
+#pragma unroll
+                                    for (int w = 0; w < 4; ++w) {
+                                        const uint32_t keep_lo = (m[w] & 0x7fffu) ? 0xffffu : 0u;
+                                        const uint32_t keep_hi = (m[w] & 0x7fff0000u) ? 0xffff0000u : 0u;
+                                        val[w] &= keep_lo | keep_hi;
+                                    }
+                                }
+                                *(u32x4*)(gout + (size_t)r * N * OUT_BYTES + v * 16) = val;
+                            }
                         }
                     }
 #pragma unroll
@@ -298,15 +322,15 @@ static int device_cus() {
     return cus[dev];
 }
 
-template <int TOKB, int NBW, int WAVES, int R, bool GEMM1, int PB>
+template <int TOKB, int NBW, int WAVES, int R, int MODE, int PB>
 hipError_t launch_expert_gemm_t(const bf16_t* A, const bf16_t* W, const int32_t* pre, const int4* ttab, void* out,
-                                int E, int C, int K, int N, hipStream_t s) {
+                                const bf16_t* mask, int E, int C, int K, int N, hipStream_t s) {
     constexpr int NWG = WAVES * 32 * NBW;
     const int n_tiles = (N + NWG - 1) / NWG;
     static int per_cu = 0;   // resident workgroups per CU for this kernel
     if (!per_cu) {
         int b = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, expert_gemm<TOKB, NBW, WAVES, R, GEMM1, PB>, 64 * WAVES, 0) !=
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, expert_gemm<TOKB, NBW, WAVES, R, MODE, PB>, 64 * WAVES, 0) !=
                 hipSuccess || b <= 0)
             b = 1;
         per_cu = b;
@@ -315,8 +339,8 @@ hipError_t launch_expert_gemm_t(const bf16_t* A, const bf16_t* W, const int32_t*
     const int64_t max_tiles = (int64_t)E * n_tiles * tok_tiles;
     int64_t grid = std::min<int64_t>((int64_t)device_cus() * per_cu, (max_tiles + 7) / 8 * 8);
     grid = std::max<int64_t>(8, grid / 8 * 8);
-    hipLaunchKernelGGL((expert_gemm<TOKB, NBW, WAVES, R, GEMM1, PB>), dim3((unsigned)grid), dim3(64 * WAVES), 0, s, A, W,
-                       pre, ttab, out, E, C, K, N, n_tiles);
+    hipLaunchKernelGGL((expert_gemm<TOKB, NBW, WAVES, R, MODE, PB>), dim3((unsigned)grid), dim3(64 * WAVES), 0, s, A, W,
+                       pre, ttab, out, mask, E, C, K, N, n_tiles);
     return hipGetLastError();
 }
 
@@ -349,26 +373,37 @@ static bool narrow_tiles(int E, int C, int N) {
     return cost(192) < cost(256);
 }
 
-template <bool GEMM1>
+template <int MODE>
 static hipError_t launch_expert_gemm(const bf16_t* A, const bf16_t* W, const int32_t* pre, const int4* ttab, void* out,
-                                     int E, int C, int K, int N, hipStream_t s) {
+                                     const bf16_t* mask, int E, int C, int K, int N, hipStream_t s) {
     // the token tile must be ffn_token_tile(C) rows: the prefix kernel lists tiles of that size
     if (C > 64) {
-        if (narrow_tiles(E, C, N)) return launch_expert_gemm_t<4, 1, 6, 3, GEMM1, 256>(A, W, pre, ttab, out, E, C, K, N, s);
-        return launch_expert_gemm_t<4, 1, 8, 4, GEMM1, 512>(A, W, pre, ttab, out, E, C, K, N, s);
+        if (narrow_tiles(E, C, N))
+            return launch_expert_gemm_t<4, 1, 6, 3, MODE, 256>(A, W, pre, ttab, out, mask, E, C, K, N, s);
+        return launch_expert_gemm_t<4, 1, 8, 4, MODE, 512>(A, W, pre, ttab, out, mask, E, C, K, N, s);
     }
-    if (C > 32) return launch_expert_gemm_t<2, 2, 4, 3, GEMM1, 512>(A, W, pre, ttab, out, E, C, K, N, s);
-    return launch_expert_gemm_t<1, 2, 4, 4, GEMM1, 512>(A, W, pre, ttab, out, E, C, K, N, s);
+    if (C > 32) return launch_expert_gemm_t<2, 2, 4, 3, MODE, 512>(A, W, pre, ttab, out, mask, E, C, K, N, s);
+    return launch_expert_gemm_t<1, 2, 4, 4, MODE, 512>(A, W, pre, ttab, out, mask, E, C, K, N, s);
 }
 
 hipError_t launch_expert_gemm1(const bf16_t* buf, const bf16_t* w1, const int32_t* pre, const int4* ttab, bf16_t* h,
                                int E, int C, int d, int d_ff, hipStream_t s) {
-    return launch_expert_gemm<true>(buf, w1, pre, ttab, h, E, C, d, d_ff, s);
+    return launch_expert_gemm<OUT_RELU_BF16>(buf, w1, pre, ttab, h, nullptr, E, C, d, d_ff, s);
 }
 
 hipError_t launch_expert_gemm2(const bf16_t* h, const bf16_t* w2, const int32_t* pre, const int4* ttab, float* y,
                                int E, int C, int d, int d_ff, hipStream_t s) {
-    return launch_expert_gemm<false>(h, w2, pre, ttab, y, E, C, d_ff, d, s);
+    return launch_expert_gemm<OUT_F32>(h, w2, pre, ttab, y, nullptr, E, C, d_ff, d, s);
+}
+
+hipError_t launch_grouped_gemm_f32(const bf16_t* A, const bf16_t* W, const int32_t* pre, const int4* ttab, float* out,
+                                   int E, int rows, int K, int N, hipStream_t s) {
+    return launch_expert_gemm<OUT_F32>(A, W, pre, ttab, out, nullptr, E, rows, K, N, s);
+}
+
+hipError_t launch_grouped_gemm_masked(const bf16_t* A, const bf16_t* W, const int32_t* pre, const int4* ttab,
+                                      bf16_t* out, const bf16_t* mask, int E, int rows, int K, int N, hipStream_t s) {
+    return launch_expert_gemm<OUT_MASK_BF16>(A, W, pre, ttab, out, mask, E, rows, K, N, s);
 }
 #endif
 

@@ -46,6 +46,12 @@ hipError_t launch_expert_gemm1(const bf16_t* buf, const bf16_t* w1, const int32_
                                int E, int C, int d, int d_ff, hipStream_t s);
 hipError_t launch_expert_gemm2(const bf16_t* h, const bf16_t* w2, const int32_t* pre, const int4* ttab, float* y,
                                int E, int C, int d, int d_ff, hipStream_t s);
+// the same kernel on other operands: out[e, r, n] = sum_k A[e, r, k] W[e, n, k]
+// for the rows listed in (pre, ttab), fp32 out; or bf16 out zeroed where mask == 0
+hipError_t launch_grouped_gemm_f32(const bf16_t* A, const bf16_t* W, const int32_t* pre, const int4* ttab, float* out,
+                                   int E, int rows, int K, int N, hipStream_t s);
+hipError_t launch_grouped_gemm_masked(const bf16_t* A, const bf16_t* W, const int32_t* pre, const int4* ttab,
+                                      bf16_t* out, const bf16_t* mask, int E, int rows, int K, int N, hipStream_t s);
 
 // combine.hip
 hipError_t launch_combine(const float* y, const int32_t* expert, const int32_t* slot, const uint8_t* keep,
@@ -57,7 +63,22 @@ hipError_t launch_aux_stats(const int32_t* counts, const float* prob_sum, int64_
                             float alpha, float* f, float* P, float* loss, hipStream_t s);
 hipError_t launch_z_loss(const float* lse, int64_t T, float beta, float* z_loss, hipStream_t s);
 hipError_t launch_aux_grad(const float* logits, const float* lse, const float* f, int64_t T, int64_t G, int E,
-                           float alpha, float beta, int accumulate, float* dlogits, hipStream_t s);
+                           float alpha, float beta, const int32_t* expert, const float* gate, const float* dgate,
+                           int accumulate, float* dlogits, hipStream_t s);
+
+// backward.hip
+hipError_t launch_combine_bwd(const bf16_t* dout, const float* y, const int32_t* expert, const int32_t* position,
+                              const uint8_t* keep, const float* gate, int64_t T, int d, int E, int C, bf16_t* dy,
+                              float* dgate, hipStream_t s);
+hipError_t launch_transpose_rows(const bf16_t* src, bf16_t* dst, int E, int R, int S, int Rp, const int32_t* valid,
+                                 hipStream_t s);
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
+int router_wgrad_slices(int64_t T, int d, int E);
+hipError_t launch_router_wgrad(const bf16_t* x, const float* dz, int64_t T, int d, int E, float* part, float* dw_r,
+                               hipStream_t s);
+hipError_t launch_dx_assemble(const bf16_t* dout, const float* dbuf, const int32_t* expert, const int32_t* position,
+                              const uint8_t* keep, const float* dz, const float* w_r, int64_t T, int d, int E, int C,
+                              bf16_t* dx, hipStream_t s);
 
 // api.hip
 hipError_t launch_stream_copy(void* dst, const void* src, size_t nbytes, hipStream_t s);

@@ -76,6 +76,27 @@ def assert_branch_close(got, ref, what="branch"):
     return rf, mx / rms if rms else 0.0
 
 
+# Gradients of the layer backward: relative Frobenius <= REL_FRO, and per
+# element |got - ref| <= GRAD_ELEM_REL |ref| + MAX_ABS_RMS rms(ref).  The
+# proportional term covers the large entries of heavy-tailed gradients, whose
+# error scales with their own size (bf16 operands of the MFMA: 2^-9 relative).
+GRAD_ELEM_REL = 1e-2
+
+
+def assert_grad_close(got, ref, what="gradient"):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    rf = rel_fro(got, ref)
+    assert rf <= REL_FRO, f"{what}: relative Frobenius {rf:.3e} > {REL_FRO}"
+    if ref.size:
+        rms = np.sqrt(np.mean(ref ** 2))
+        err = np.abs(got - ref)
+        bad = err > GRAD_ELEM_REL * np.abs(ref) + MAX_ABS_RMS * rms + 1e-30
+        assert not bad.any(), (f"{what}: {int(bad.sum())} elements off, worst {err.max():.3e} "
+                               f"(rms {rms:.3e})")
+    return rf
+
+
 def assert_residual_close(out_bits, x, branch_ref, what="out"):
     """Residual mode: out = bf16(x + branch).  Allowed error per element: one
     bf16 ulp of the exact result plus the branch tolerance (MAX_ABS_RMS times

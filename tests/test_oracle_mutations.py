@@ -301,7 +301,7 @@ def test_group_topk_pins_catch_mutant(mutate):
 
 # ------------------------------------ layer backward: mistakes planted in the source text
 BACKWARD_EDITS = [
-    ("da = (dy @ W2) * (a > 0)", "da = dy @ W2"),                                   # no ReLU mask
+    ("active = (a > 0) if relu_active", "active = 1.0 if relu_active"),            # no ReLU mask
     ("dy = g[:, None] * dout[toks]", "dy = dout[toks]"),                             # gate dropped
     ("dz = (dgate * r.gate)[:, None] * (onehot - r.p)",
      "dz = (dgate * r.gate)[:, None] * (r.p - onehot)"),                             # softmax sign
