@@ -143,7 +143,46 @@ def time_variants(sw, torch, cfg, x, w_r, b_r, w1, w2, stream, steps, warmup):
         out[name] = {"k": v["k"], "group": G, "C_per_group": C, "ms_per_step": ms,
                      "tokens_per_s": cfg.T / (ms / 1000.0), "kept_choices": float(keep.mean())}
         del t, la
+    out["backward"] = time_backward(sw, torch, cfg, x, w_r, b_r, w1, w2, stream, steps, warmup)
     return out
+
+
+def time_backward(sw, torch, cfg, x, w_r, b_r, w1, w2, stream, steps, warmup):
+    """The layer backward (switch_layer_bwd) after a forward that keeps what it
+    needs (logits, hidden activations, dispatch buffer, expert outputs); a
+    step is one backward.  Per-kernel times from the library's events."""
+    T, d, F, E = cfg.T, cfg.d, cfg.d_ff, cfg.E
+    C = sw.switch_capacity(T, E, cfg.c)
+    t = sw.layer_tensors(T, d, F, E, C, for_backward=True)
+    la = sw.make_layer_args(x, w_r, b_r, w1, w2, t, T, d, F, E, C, cfg.alpha, residual=True)
+    sw.switch_layer_fwd(la, t["ws"], stream)
+    dout = torch.randn((T, d), device=x.device, generator=torch.Generator(device=x.device).manual_seed(7)).to(
+        torch.bfloat16)
+    g = sw.layer_bwd_tensors(T, d, F, E, C)
+    ba = sw.make_layer_bwd_args(t, x, w_r, w1, w2, dout, g, T, d, F, E, C, cfg.alpha)
+    for _ in range(warmup):
+        sw.switch_layer_bwd(ba, g["ws"], stream)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(steps):
+        sw.switch_layer_bwd(ba, g["ws"], stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    sw.switch_profile_enable(True)
+    for _ in range(steps):
+        sw.switch_layer_bwd(ba, g["ws"], stream)
+    torch.cuda.synchronize()
+    recs = sw.switch_profile_collect()
+    sw.switch_profile_enable(False)
+    per = {}
+    for name, kms in recs:
+        per[name] = per.get(name, 0.0) + kms
+    kern = {k: round(1000.0 * v / steps, 2) for k, v in sorted(per.items(), key=lambda kv: -kv[1])}
+    wbytes = 2 * E * F * d
+    return {"ms_per_step": ms, "tokens_per_s": T / (ms / 1000.0), "kernels_us_per_step": kern,
+            "weight_grad_bytes_fp32": 2 * wbytes, "note": "transpose_rows includes the two weight transposes"}
 
 
 def main():

@@ -492,6 +492,7 @@ static size_t layer_bwd_ws(int64_t T, int32_t d, int32_t d_ff, int32_t E, int32_
     n += up((size_t)T * E * sizeof(float));       // dz
     n += up((size_t)T * sizeof(float));           // dgate
     n += up((size_t)std::max(router_wgrad_slices(T, d, E), 1) * d * E * sizeof(float));   // dW_r slices
+    n += up((size_t)column_sum_slices(T) * E * sizeof(float));                              // db_r slices
     n += 3 * up((e + 1) * sizeof(int32_t));       // tile prefixes: token rows, d rows, d_ff rows
     n += up(ffn_tile_table_entries(E, C) * sizeof(int4)) + up(ffn_tile_table_entries(E, d) * sizeof(int4)) +
          up(ffn_tile_table_entries(E, d_ff) * sizeof(int4));
@@ -547,6 +548,7 @@ switch_status switch_layer_bwd(const switch_layer_bwd_args* ba, void* ws, size_t
     float* dz = c.take<float>((size_t)T * E);
     float* dgate = c.take<float>((size_t)T);
     float* part = c.take<float>((size_t)std::max(router_wgrad_slices(T, d, E), 1) * d * E);
+    float* dbs = c.take<float>((size_t)column_sum_slices(T) * E);
     int32_t* pre_c = c.take<int32_t>((size_t)E + 1);
     int32_t* pre_d = c.take<int32_t>((size_t)E + 1);
     int32_t* pre_f = c.take<int32_t>((size_t)E + 1);
@@ -563,7 +565,7 @@ switch_status switch_layer_bwd(const switch_layer_bwd_args* ba, void* ws, size_t
     if (tok)
         LAUNCH(K_ROUTER_DZ, "router_dz", s,
                launch_aux_grad(B.logits, B.lse, B.f, T, T, E, B.alpha, B.z_beta, B.expert, B.gate, dgate, 0, dz, s));
-    LAUNCH(K_ROUTER_DB, "router_db", s, launch_router_reduce(dz, (int)T, 1, E, B.db_r, s));
+    LAUNCH(K_ROUTER_DB, "router_db", s, launch_column_sum(dz, (int)T, E, dbs, B.db_r, s));
     LAUNCH(K_ROUTER_WGRAD, "router_wgrad", s, launch_router_wgrad(x, dz, T, d, E, part, B.dw_r, s));
     // experts: transposed operands, then the four grouped GEMMs
     LAUNCH(K_TRANSPOSE, "transpose_rows", s, launch_transpose_rows(B.w2, w2T, E, d, F, d, nullptr, s));

@@ -98,8 +98,8 @@ __global__ __launch_bounds__(256) void transpose_rows(const bf16_t* __restrict__
 constexpr int RW_CHUNK = 32;
 __global__ __launch_bounds__(256) void router_wgrad(const bf16_t* __restrict__ x, const float* __restrict__ dz,
                                                     int64_t T, int d, int E, int tps, float* __restrict__ part) {
-    __shared__ float xs[RW_CHUNK][64];
-    __shared__ float zs[RW_CHUNK][64 + 4];
+    __shared__ __attribute__((aligned(16))) float xs[RW_CHUNK][64];
+    __shared__ __attribute__((aligned(16))) float zs[RW_CHUNK][64];
     const int i0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
     const int64_t t0 = (int64_t)blockIdx.z * tps;
     const int64_t t1 = min(T, t0 + tps);
@@ -114,13 +114,10 @@ __global__ __launch_bounds__(256) void router_wgrad(const bf16_t* __restrict__ x
             zs[r][c] = (t < t1 && e0 + c < E) ? dz[t * E + e0 + c] : 0.f;
         }
         __syncthreads();
-#pragma unroll 4
+#pragma unroll 8
         for (int r = 0; r < RW_CHUNK; ++r) {
-            float xv[4], zv[4];
-#pragma unroll
-            for (int a = 0; a < 4; ++a) xv[a] = xs[r][ti * 4 + a];
-#pragma unroll
-            for (int b = 0; b < 4; ++b) zv[b] = zs[r][te * 4 + b];
+            const f32x4 xv = *(const f32x4*)&xs[r][ti * 4];
+            const f32x4 zv = *(const f32x4*)&zs[r][te * 4];
 #pragma unroll
             for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -146,57 +143,55 @@ __global__ __launch_bounds__(256) void router_wgrad_reduce(const float* __restri
     dw_r[i] = (float)s;
 }
 
-// dx: workgroup = 32 tokens x 64 columns of x; K = E in chunks of 64.
+// dx: workgroup = 64 tokens x 64 columns of x, 4 x 4 per thread; K = E in
+// chunks of 32.
 __global__ __launch_bounds__(256) void dx_assemble(const bf16_t* __restrict__ dout, const float* __restrict__ dbuf,
                                                    const int32_t* __restrict__ expert,
                                                    const int32_t* __restrict__ position,
                                                    const uint8_t* __restrict__ keep, const float* __restrict__ dz,
                                                    const float* __restrict__ w_r, int64_t T, int d, int E, int C,
                                                    bf16_t* __restrict__ dx) {
-    __shared__ float zs[32][64 + 1];
-    __shared__ float ws[64][64 + 1];   // [e][i]
-    const int64_t t0 = (int64_t)blockIdx.y * 32;
+    __shared__ __attribute__((aligned(16))) float zs[32][68];   // [e][token] (rows padded against bank conflicts)
+    __shared__ __attribute__((aligned(16))) float ws[32][68];   // [e][i]
+    const int64_t t0 = (int64_t)blockIdx.y * 64;
     const int i0 = blockIdx.x * 64;
-    const int tt = threadIdx.x >> 3, ic = (threadIdx.x & 7) * 8;   // token, 8 columns
-    float acc[8] = {};
-    for (int e0 = 0; e0 < E; e0 += 64) {
+    const int tq = threadIdx.x >> 4, iq = threadIdx.x & 15;     // tokens 4 tq.., columns 4 iq..
+    float acc[4][4] = {};
+    for (int e0 = 0; e0 < E; e0 += 32) {
         __syncthreads();
         for (int q = threadIdx.x; q < 32 * 64; q += 256) {
-            const int r = q >> 6, c = q & 63;
-            zs[r][c] = (t0 + r < T && e0 + c < E) ? dz[(t0 + r) * E + e0 + c] : 0.f;
-        }
-        for (int q = threadIdx.x; q < 64 * 64; q += 256) {
-            const int ii = q >> 6, ee = q & 63;   // w_r is [d, E]: consecutive threads read consecutive e
-            ws[ee][ii] = (e0 + ee < E) ? w_r[(size_t)(i0 + ii) * E + e0 + ee] : 0.f;
+            const int r = q >> 5, c = q & 31;    // token r, expert c: consecutive threads read consecutive e
+            zs[c][r] = (t0 + r < T && e0 + c < E) ? dz[(t0 + r) * E + e0 + c] : 0.f;
+            const int ii = q >> 5;               // column ii of x, expert c
+            ws[c][ii] = (e0 + c < E) ? w_r[(size_t)(i0 + ii) * E + e0 + c] : 0.f;
         }
         __syncthreads();
-        for (int ee = 0; ee < 64; ++ee) {
-            const float z = zs[tt][ee];
+#pragma unroll 8
+        for (int ee = 0; ee < 32; ++ee) {
+            const f32x4 zv = *(const f32x4*)&zs[ee][tq * 4];
+            const f32x4 wv = *(const f32x4*)&ws[ee][iq * 4];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) acc[j] = fmaf(z, ws[ee][ic + j], acc[j]);
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) acc[a][b] = fmaf(zv[a], wv[b], acc[a][b]);
         }
     }
-    const int64_t t = t0 + tt;
-    if (t >= T) return;
-    const uint4 dv = *(const uint4*)(dout + t * d + i0 + ic);
-    const uint32_t w[4] = {dv.x, dv.y, dv.z, dv.w};
-    float v[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        v[2 * j] = bf16_to_f32(w[j] & 0xffffu) + acc[2 * j];
-        v[2 * j + 1] = bf16_to_f32(w[j] >> 16) + acc[2 * j + 1];
+    for (int a = 0; a < 4; ++a) {
+        const int64_t t = t0 + tq * 4 + a;
+        if (t >= T) break;
+        const int i = i0 + iq * 4;
+        const uint2 dv = *(const uint2*)(dout + t * d + i);
+        float v[4] = {bf16_to_f32(dv.x & 0xffffu) + acc[a][0], bf16_to_f32(dv.x >> 16) + acc[a][1],
+                      bf16_to_f32(dv.y & 0xffffu) + acc[a][2], bf16_to_f32(dv.y >> 16) + acc[a][3]};
+        const int e = expert[t], pos = position[t];
+        if (keep[t] && e >= 0 && e < E && pos >= 0 && pos < C) {
+            const f32x4 b = *(const f32x4*)(dbuf + ((size_t)e * C + pos) * d + i);
+            v[0] += b[0]; v[1] += b[1]; v[2] += b[2]; v[3] += b[3];
+        }
+        *(uint2*)(dx + t * d + i) = make_uint2(bf16_rne(v[0]) | (bf16_rne(v[1]) << 16),
+                                               bf16_rne(v[2]) | (bf16_rne(v[3]) << 16));
     }
-    const int e = expert[t], pos = position[t];
-    if (keep[t] && e >= 0 && e < E && pos >= 0 && pos < C) {
-        const float* br = dbuf + ((size_t)e * C + pos) * d + i0 + ic;
-        const f32x4 b0 = *(const f32x4*)br, b1 = *(const f32x4*)(br + 4);
-        v[0] += b0[0]; v[1] += b0[1]; v[2] += b0[2]; v[3] += b0[3];
-        v[4] += b1[0]; v[5] += b1[1]; v[6] += b1[2]; v[7] += b1[3];
-    }
-    uint32_t o[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = bf16_rne(v[2 * j]) | (bf16_rne(v[2 * j + 1]) << 16);
-    *(uint4*)(dx + t * d + i0 + ic) = make_uint4(o[0], o[1], o[2], o[3]);
 }
 
 __global__ __launch_bounds__(256) void fill_zero(float* __restrict__ p, int64_t n) {
@@ -256,7 +251,7 @@ hipError_t launch_dx_assemble(const bf16_t* dout, const float* dbuf, const int32
                               const uint8_t* keep, const float* dz, const float* w_r, int64_t T, int d, int E, int C,
                               bf16_t* dx, hipStream_t s) {
     if (T == 0) return hipSuccess;
-    hipLaunchKernelGGL(dx_assemble, dim3(d / 64, (unsigned)((T + 31) / 32)), dim3(256), 0, s, dout, dbuf, expert,
+    hipLaunchKernelGGL(dx_assemble, dim3(d / 64, (unsigned)((T + 63) / 64)), dim3(256), 0, s, dout, dbuf, expert,
                        position, keep, dz, w_r, T, d, E, C, dx);
     return hipGetLastError();
 }

@@ -19,6 +19,8 @@ int router_softmax_blocks_grouped(int64_t T);   // one partial row per 64 tokens
 hipError_t launch_router_softmax(const float* logits, int T, int E, int k, bool rows_of_64, int32_t* expert,
                                  float* gate, float* lse, float* part, hipStream_t s);
 hipError_t launch_router_reduce(const float* part, int nblk, int ngroups, int E, float* prob_sum, hipStream_t s);
+int column_sum_slices(int64_t rows);
+hipError_t launch_column_sum(const float* a, int rows, int E, float* slices, float* out, hipStream_t s);
 constexpr int kRouterFusedMaxE = 256;
 int router_fused_blocks(int64_t T);     // one partial row per 64 tokens
 hipError_t launch_router_fused(const bf16_t* x, const bf16_t* wr3, const float* b_r, int T, int d, int E, int k,

@@ -207,13 +207,14 @@ __global__ __launch_bounds__(256) void router_softmax(const float* __restrict__ 
 // g*nblk .. g*nblk+nblk-1), in fp64, in a fixed order: a workgroup owns 64
 // experts of one group; its 16 row groups take every 16th partial row, then
 // the row groups are added in order.  One group: prob_sum[e] over all rows.
-__global__ __launch_bounds__(1024) void router_reduce(const float* __restrict__ part, int nblk, int E,
+__global__ __launch_bounds__(1024) void router_reduce(const float* __restrict__ part, int nblk, int total, int E,
                                                       float* __restrict__ prob_sum) {
     __shared__ double red[16][64];
     const int c = threadIdx.x & 63, rg = threadIdx.x >> 6;
     const int e = blockIdx.x * 64 + c;
     part += (size_t)blockIdx.y * nblk * E;
     prob_sum += (size_t)blockIdx.y * E;
+    nblk = min(nblk, total - (int)blockIdx.y * nblk);   // the last group may be short
     double s = 0.0;
     if (e < E) {
         int b = rg;
@@ -290,7 +291,23 @@ hipError_t launch_router_softmax(const float* logits, int T, int E, int k, bool 
 
 hipError_t launch_router_reduce(const float* part, int nblk, int ngroups, int E, float* prob_sum, hipStream_t s) {
     if (ngroups == 0) return hipSuccess;
-    hipLaunchKernelGGL(router_reduce, dim3((E + 63) / 64, ngroups), dim3(1024), 0, s, part, nblk, E, prob_sum);
+    hipLaunchKernelGGL(router_reduce, dim3((E + 63) / 64, ngroups), dim3(1024), 0, s, part, nblk, nblk * ngroups, E,
+                       prob_sum);
+    return hipGetLastError();
+}
+
+int column_sum_slices(int64_t rows) { return (int)std::max<int64_t>(1, (rows + 1023) / 1024); }
+
+// out[e] = sum over the rows of a [rows, E] array: slices of 1024 rows summed
+// in parallel (each in the fixed order above), then the slices in order.
+hipError_t launch_column_sum(const float* a, int rows, int E, float* slices, float* out, hipStream_t s) {
+    const int ns = column_sum_slices(rows);
+    if (ns == 1) {
+        hipLaunchKernelGGL(router_reduce, dim3((E + 63) / 64, 1), dim3(1024), 0, s, a, rows, rows, E, out);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(router_reduce, dim3((E + 63) / 64, ns), dim3(1024), 0, s, a, 1024, rows, E, slices);
+    hipLaunchKernelGGL(router_reduce, dim3((E + 63) / 64, 1), dim3(1024), 0, s, slices, ns, ns, E, out);
     return hipGetLastError();
 }
 
