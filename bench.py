@@ -182,7 +182,7 @@ def time_backward(sw, torch, cfg, x, w_r, b_r, w1, w2, stream, steps, warmup):
     kern = {k: round(1000.0 * v / steps, 2) for k, v in sorted(per.items(), key=lambda kv: -kv[1])}
     wbytes = 2 * E * F * d
     return {"ms_per_step": ms, "tokens_per_s": T / (ms / 1000.0), "kernels_us_per_step": kern,
-            "weight_grad_bytes_fp32": 2 * wbytes, "note": "transpose_rows includes the two weight transposes"}
+            "weight_grad_bytes_fp32": 2 * wbytes}
 
 
 def main():

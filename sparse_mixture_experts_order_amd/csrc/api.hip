@@ -487,7 +487,6 @@ static size_t layer_bwd_ws(int64_t T, int32_t d, int32_t d_ff, int32_t E, int32_
     n += up(e * C * d_ff * sizeof(bf16_t));       // dA
     n += up(e * d_ff * Cp * sizeof(bf16_t));      // dA^T
     n += up(e * d * Cp * sizeof(bf16_t));         // buf^T
-    n += 2 * up(e * d * d_ff * sizeof(bf16_t));   // W1^T, W2^T
     n += up(e * C * d * sizeof(float));           // dbuf
     n += up((size_t)T * E * sizeof(float));       // dz
     n += up((size_t)T * sizeof(float));           // dgate
@@ -542,8 +541,6 @@ switch_status switch_layer_bwd(const switch_layer_bwd_args* ba, void* ws, size_t
     bf16_t* dA = c.take<bf16_t>((size_t)E * C * F);
     bf16_t* dAT = c.take<bf16_t>((size_t)E * F * Cp);
     bf16_t* bufT = c.take<bf16_t>((size_t)E * d * Cp);
-    bf16_t* w1T = c.take<bf16_t>((size_t)E * d * F);
-    bf16_t* w2T = c.take<bf16_t>((size_t)E * d * F);
     float* dbuf = c.take<float>((size_t)E * C * d);
     float* dz = c.take<float>((size_t)T * E);
     float* dgate = c.take<float>((size_t)T);
@@ -567,18 +564,19 @@ switch_status switch_layer_bwd(const switch_layer_bwd_args* ba, void* ws, size_t
                launch_aux_grad(B.logits, B.lse, B.f, T, T, E, B.alpha, B.z_beta, B.expert, B.gate, dgate, 0, dz, s));
     LAUNCH(K_ROUTER_DB, "router_db", s, launch_column_sum(dz, (int)T, E, dbs, B.db_r, s));
     LAUNCH(K_ROUTER_WGRAD, "router_wgrad", s, launch_router_wgrad(x, dz, T, d, E, part, B.dw_r, s));
-    // experts: transposed operands, then the four grouped GEMMs
-    LAUNCH(K_TRANSPOSE, "transpose_rows", s, launch_transpose_rows(B.w2, w2T, E, d, F, d, nullptr, s));
-    LAUNCH(K_TRANSPOSE, "transpose_rows", s, launch_transpose_rows(B.w1, w1T, E, F, d, F, nullptr, s));
+    // experts: the two products with the weights read W1 and W2 as stored
+    // (K-major); the weight gradients take the token axis as K, transposed
     if (C > 0) {
         LAUNCH(K_TRANSPOSE, "transpose_rows", s, launch_transpose_rows(dy, dyT, E, C, d, Cp, B.accepted, s));
         LAUNCH(K_TRANSPOSE, "transpose_rows", s, launch_transpose_rows(B.h, hT, E, C, F, Cp, B.accepted, s));
         LAUNCH(K_TRANSPOSE, "transpose_rows", s, launch_transpose_rows(B.buf, bufT, E, C, d, Cp, B.accepted, s));
         LAUNCH(K_FFN_TILES, "ffn_tile_prefix", s, launch_ffn_tile_prefix(B.accepted, E, C, pre_c, tt_c, s));
-        // dA = (dy W2) * [H > 0]          rows: tokens, K = d, N = d_ff
-        LAUNCH(K_GEMM_DA, "gemm_dA", s, launch_grouped_gemm_masked(dy, w2T, pre_c, tt_c, dA, B.h, E, C, d, F, s));
-        // dbuf = dA W1                    rows: tokens, K = d_ff, N = d
-        LAUNCH(K_GEMM_DBUF, "gemm_dbuf", s, launch_grouped_gemm_f32(dA, w1T, pre_c, tt_c, dbuf, E, C, F, d, s));
+        // dA = (dy W2) * [H > 0]          rows: tokens, K = d, N = d_ff; W2[e] is [d][d_ff]
+        LAUNCH(K_GEMM_DA, "gemm_dA", s,
+               launch_grouped_gemm_kmajor_masked(dy, B.w2, pre_c, tt_c, dA, B.h, E, C, d, F, s));
+        // dbuf = dA W1                    rows: tokens, K = d_ff, N = d; W1[e] is [d_ff][d]
+        LAUNCH(K_GEMM_DBUF, "gemm_dbuf", s,
+               launch_grouped_gemm_kmajor_f32(dA, B.w1, pre_c, tt_c, dbuf, E, C, F, d, s));
         LAUNCH(K_TRANSPOSE, "transpose_rows", s, launch_transpose_rows(dA, dAT, E, C, F, Cp, B.accepted, s));
     }
     // weight gradients: K = the (zero-padded) token axis

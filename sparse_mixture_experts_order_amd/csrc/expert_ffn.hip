@@ -103,10 +103,14 @@ enum FfnOut { OUT_RELU_BF16 = 0, OUT_F32 = 1, OUT_MASK_BF16 = 2 };
 
 // TOKB: 32-row token blocks per tile; NBW: 32-row weight blocks per wave;
 // WAVES: waves per workgroup; R: depth of the register rings; PB: bytes of an
-// output row staged through LDS per pass; MODE: an FfnOut.
-template <int TOKB, int NBW, int WAVES, int R, int MODE, int PB>
+// output row staged through LDS per pass; MODE: an FfnOut; WKM: the weights
+// are stored K-major, W[e][k][n] (the backward's products with W1 and W2 as
+// stored), instead of W[e][n][k].  K-major weight chunks are read as 64 k-rows
+// of NWG contiguous columns, transposed 4 x 8 in registers and staged through
+// LDS like the token tile.
+template <int TOKB, int NBW, int WAVES, int R, int MODE, int PB, bool WKM = false>
 __global__ __launch_bounds__(64 * WAVES) void expert_gemm(const bf16_t* __restrict__ A,   // [E, C, K]
-                                                          const bf16_t* __restrict__ W,   // [E, N, K]
+                                                          const bf16_t* __restrict__ W,   // [E, N, K] or [E, K, N]
                                                           const int32_t* __restrict__ pre,
                                                           const int4* __restrict__ ttab,
                                                           void* __restrict__ out,         // [E, C, N]
@@ -128,9 +132,12 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm(const bf16_t* __restri
     constexpr int OSTRIDE = PASS_BYTES + 16;                          // bytes per staged row
     constexpr int A_BYTES = 2 * TOK * FFN_LDS_STRIDE * 2;
     constexpr int O_BYTES = TOK * OSTRIDE;
-    __shared__ __attribute__((aligned(16))) char lds_raw[A_BYTES + O_BYTES];
+    constexpr int W_BYTES = WKM ? 2 * NWG * FFN_LDS_STRIDE * 2 : 0;
+    __shared__ __attribute__((aligned(16))) char lds_raw[A_BYTES + O_BYTES + W_BYTES];
     bf16_t* const lds_a = reinterpret_cast<bf16_t*>(lds_raw);
     char* const lds_o = lds_raw + A_BYTES;
+    bf16_t* const lds_w = reinterpret_cast<bf16_t*>(lds_raw + A_BYTES + O_BYTES);   // [2][NWG][72] (WKM)
+    static_assert(!WKM || 2 * NWG == NBW * NTHR, "K-major weights: NBW groups of 4 k x 8 n per thread");
 
     const int total = pre[E] * n_tiles;
     const int G = gridDim.x;                                          // a multiple of 8
@@ -151,15 +158,42 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm(const bf16_t* __restri
     const char* wbase = nullptr;   // uniform: this wave's first weight row of the frontier tile
     const char* abase = nullptr;   // uniform: the frontier tile's first token row
     uint32_t woff[NBW];            // per lane: weight row nb*32 + l32, half-chunk `half`
+                                   // (K-major: group nb's k-row 4 kq and columns 8 nq ..)
     uint32_t aoffg[APT];           // per lane: token row and 16-byte column of piece j
+    int wcol[NBW];                 // K-major: first column 8 nq of group nb inside the tile
+    int wlds[NBW];                 // K-major: LDS element offset of group nb's (column 8 nq, k 4 kq)
 #pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) woff[nb] = ((uint32_t)(nb * 32 + l32) * K + half * 32) * 2;
+    for (int nb = 0; nb < NBW; ++nb) {
+        if constexpr (WKM) {
+            const int g = (int)threadIdx.x + nb * NTHR;
+            const int kq = g / (NWG / 8), nq = g - kq * (NWG / 8);
+            wcol[nb] = nq * 8;
+            wlds[nb] = nq * 8 * FFN_LDS_STRIDE + kq * 4;
+            woff[nb] = 0;
+        } else {
+            woff[nb] = ((uint32_t)(nb * 32 + l32) * K + half * 32) * 2;
+        }
+    }
     auto set_frontier = [&](int j) {
         f_tile = j;
         const FfnTile t = decode_tile(j * G + slot, ttab, n_tiles);
-        int wr0 = t.nt * NWG + wave * 32 * NBW;
-        if (wr0 >= N) wr0 = 0;     // waves past the last weight row read rows 0.. and store nothing
-        wbase = (const char*)W + ((size_t)t.e * N + wr0) * K * 2;
+        if constexpr (WKM) {
+            // columns past N read column group 0 and store nothing
+            const int c0 = t.nt * NWG;
+            wbase = (const char*)W + (size_t)t.e * K * N * 2;
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb) {
+                const int g = (int)threadIdx.x + nb * NTHR;
+                const int kq = g / (NWG / 8);
+                int col = c0 + wcol[nb];
+                if (col >= N) col = 0;
+                woff[nb] = ((uint32_t)(kq * 4) * N + col) * 2;
+            }
+        } else {
+            int wr0 = t.nt * NWG + wave * 32 * NBW;
+            if (wr0 >= N) wr0 = 0;     // waves past the last weight row read rows 0.. and store nothing
+            wbase = (const char*)W + ((size_t)t.e * N + wr0) * K * 2;
+        }
         abase = (const char*)A + ((size_t)t.e * C + t.tok_base) * K * 2;
 #pragma unroll
         for (int j2 = 0; j2 < APT; ++j2) {
@@ -190,19 +224,46 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm(const bf16_t* __restri
         const int jf = f / nk, kf = f - jf * nk;
         if (jf != f_tile) set_frontier(jf);
         const char* ak = abase + kf * 128;
-        const char* wk = wbase + kf * 128;
 #pragma unroll
         for (int j2 = 0; j2 < APT; ++j2) ar[j2] = *(const u32x4*)(ak + aoffg[j2]);
+        if constexpr (WKM) {
+            const char* wk = wbase + (size_t)kf * 64 * N * 2;   // k-rows 64 kf ..
 #pragma unroll
-        for (int nb = 0; nb < NBW; ++nb)
+            for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
-            for (int j2 = 0; j2 < 4; ++j2) wr[nb][j2] = *(const u32x4*)(wk + woff[nb] + j2 * 16);
+                for (int j2 = 0; j2 < 4; ++j2) wr[nb][j2] = *(const u32x4*)(wk + woff[nb] + (uint32_t)j2 * N * 2);
+        } else {
+            const char* wk = wbase + kf * 128;
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+                for (int j2 = 0; j2 < 4; ++j2) wr[nb][j2] = *(const u32x4*)(wk + woff[nb] + j2 * 16);
+        }
+    };
+
+    // K-major weights: group nb holds k-rows 4 kq .. 4 kq + 3 of columns 8 nq ..;
+    // column n of it goes to LDS row n as 4 consecutive k values
+    auto stage_w = [&](bf16_t* dstb, const u32x4 (&wr)[NBW][4]) {
+        if constexpr (WKM) {
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const uint32_t r0 = wr[nb][0][w], r1 = wr[nb][1][w], r2 = wr[nb][2][w], r3 = wr[nb][3][w];
+                    // columns 2w (low halves) and 2w + 1 (high halves)
+                    const uint2 lo = make_uint2((r0 & 0xffffu) | (r1 << 16), (r2 & 0xffffu) | (r3 << 16));
+                    const uint2 hi = make_uint2((r0 >> 16) | (r1 & 0xffff0000u), (r2 >> 16) | (r3 & 0xffff0000u));
+                    *(uint2*)(dstb + wlds[nb] + (2 * w) * FFN_LDS_STRIDE) = lo;
+                    *(uint2*)(dstb + wlds[nb] + (2 * w + 1) * FFN_LDS_STRIDE) = hi;
+                }
+        }
     };
 
 #pragma unroll
     for (int p = 0; p < R - 1; ++p) load_pos(p, areg[p], wreg[p]);
 #pragma unroll
     for (int j2 = 0; j2 < APT; ++j2) *(u32x4*)(lds_a + aoff[j2]) = areg[0][j2];
+    stage_w(lds_w, wreg[0]);
 
     for (int p0 = 0; p0 < P; p0 += R) {
 #pragma unroll
@@ -213,6 +274,7 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm(const bf16_t* __restri
                 load_pos(p + R - 1, areg[slot_n], wreg[slot_n]);
                 __syncthreads();
                 const bf16_t* lb = lds_a + (p & 1) * (TOK * FFN_LDS_STRIDE);
+                const bf16_t* lw = lds_w + (p & 1) * (NWG * FFN_LDS_STRIDE) + (wave * 32 * NBW + l32) * FFN_LDS_STRIDE;
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     bf16x8 bt[TOKB];
@@ -221,17 +283,22 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm(const bf16_t* __restri
                         bt[tb] = as_bf16x8(*(const u32x4*)(lb + (tb * 32 + l32) * FFN_LDS_STRIDE + half * 32 + s * 8));
 #pragma unroll
                     for (int nb = 0; nb < NBW; ++nb) {
-                        const bf16x8 wa = as_bf16x8(wreg[u][nb][s]);
+                        bf16x8 wa;
+                        if constexpr (WKM)
+                            wa = as_bf16x8(*(const u32x4*)(lw + nb * 32 * FFN_LDS_STRIDE + half * 32 + s * 8));
+                        else
+                            wa = as_bf16x8(wreg[u][nb][s]);
 #pragma unroll
                         for (int tb = 0; tb < TOKB; ++tb)
                             acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, bt[tb], acc[nb][tb], 0, 0, 0);
                     }
                 }
-                // token chunk of position p+1 into the other LDS buffer
+                // token chunk (and K-major weight chunk) of position p+1 into the other LDS buffer
                 const int slot_a = (u + 1) % R;
                 bf16_t* sb = lds_a + ((p + 1) & 1) * (TOK * FFN_LDS_STRIDE);
 #pragma unroll
                 for (int j2 = 0; j2 < APT; ++j2) *(u32x4*)(sb + aoff[j2]) = areg[slot_a][j2];
+                stage_w(lds_w + ((p + 1) & 1) * (NWG * FFN_LDS_STRIDE), wreg[slot_a]);
 
                 const int j = p / nk;
                 if (p - j * nk == nk - 1) {
@@ -322,7 +389,7 @@ static int device_cus() {
     return cus[dev];
 }
 
-template <int TOKB, int NBW, int WAVES, int R, int MODE, int PB>
+template <int TOKB, int NBW, int WAVES, int R, int MODE, int PB, bool WKM = false>
 hipError_t launch_expert_gemm_t(const bf16_t* A, const bf16_t* W, const int32_t* pre, const int4* ttab, void* out,
                                 const bf16_t* mask, int E, int C, int K, int N, hipStream_t s) {
     constexpr int NWG = WAVES * 32 * NBW;
@@ -330,7 +397,7 @@ hipError_t launch_expert_gemm_t(const bf16_t* A, const bf16_t* W, const int32_t*
     static int per_cu = 0;   // resident workgroups per CU for this kernel
     if (!per_cu) {
         int b = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, expert_gemm<TOKB, NBW, WAVES, R, MODE, PB>, 64 * WAVES, 0) !=
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, expert_gemm<TOKB, NBW, WAVES, R, MODE, PB, WKM>, 64 * WAVES, 0) !=
                 hipSuccess || b <= 0)
             b = 1;
         per_cu = b;
@@ -339,7 +406,7 @@ hipError_t launch_expert_gemm_t(const bf16_t* A, const bf16_t* W, const int32_t*
     const int64_t max_tiles = (int64_t)E * n_tiles * tok_tiles;
     int64_t grid = std::min<int64_t>((int64_t)device_cus() * per_cu, (max_tiles + 7) / 8 * 8);
     grid = std::max<int64_t>(8, grid / 8 * 8);
-    hipLaunchKernelGGL((expert_gemm<TOKB, NBW, WAVES, R, MODE, PB>), dim3((unsigned)grid), dim3(64 * WAVES), 0, s, A, W,
+    hipLaunchKernelGGL((expert_gemm<TOKB, NBW, WAVES, R, MODE, PB, WKM>), dim3((unsigned)grid), dim3(64 * WAVES), 0, s, A, W,
                        pre, ttab, out, mask, E, C, K, N, n_tiles);
     return hipGetLastError();
 }
@@ -394,6 +461,31 @@ hipError_t launch_expert_gemm1(const bf16_t* buf, const bf16_t* w1, const int32_
 hipError_t launch_expert_gemm2(const bf16_t* h, const bf16_t* w2, const int32_t* pre, const int4* ttab, float* y,
                                int E, int C, int d, int d_ff, hipStream_t s) {
     return launch_expert_gemm<OUT_F32>(h, w2, pre, ttab, y, nullptr, E, C, d_ff, d, s);
+}
+
+// K-major weights: one configuration per token-tile size; the staged weight
+// tile needs a 256-byte output pass to fit LDS next to it.
+template <int MODE>
+static hipError_t launch_expert_gemm_kmajor(const bf16_t* A, const bf16_t* W, const int32_t* pre, const int4* ttab,
+                                            void* out, const bf16_t* mask, int E, int C, int K, int N, hipStream_t s) {
+    if (C > 64) {
+        if (narrow_tiles(E, C, N))
+            return launch_expert_gemm_t<4, 1, 6, 3, MODE, 256, true>(A, W, pre, ttab, out, mask, E, C, K, N, s);
+        return launch_expert_gemm_t<4, 1, 8, 4, MODE, 256, true>(A, W, pre, ttab, out, mask, E, C, K, N, s);
+    }
+    if (C > 32) return launch_expert_gemm_t<2, 2, 4, 3, MODE, 512, true>(A, W, pre, ttab, out, mask, E, C, K, N, s);
+    return launch_expert_gemm_t<1, 2, 4, 4, MODE, 512, true>(A, W, pre, ttab, out, mask, E, C, K, N, s);
+}
+
+hipError_t launch_grouped_gemm_kmajor_f32(const bf16_t* A, const bf16_t* W, const int32_t* pre, const int4* ttab,
+                                          float* out, int E, int rows, int K, int N, hipStream_t s) {
+    return launch_expert_gemm_kmajor<OUT_F32>(A, W, pre, ttab, out, nullptr, E, rows, K, N, s);
+}
+
+hipError_t launch_grouped_gemm_kmajor_masked(const bf16_t* A, const bf16_t* W, const int32_t* pre, const int4* ttab,
+                                             bf16_t* out, const bf16_t* mask, int E, int rows, int K, int N,
+                                             hipStream_t s) {
+    return launch_expert_gemm_kmajor<OUT_MASK_BF16>(A, W, pre, ttab, out, mask, E, rows, K, N, s);
 }
 
 hipError_t launch_grouped_gemm_f32(const bf16_t* A, const bf16_t* W, const int32_t* pre, const int4* ttab, float* out,

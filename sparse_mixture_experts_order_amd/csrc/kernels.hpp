@@ -54,6 +54,12 @@ hipError_t launch_grouped_gemm_f32(const bf16_t* A, const bf16_t* W, const int32
                                    int E, int rows, int K, int N, hipStream_t s);
 hipError_t launch_grouped_gemm_masked(const bf16_t* A, const bf16_t* W, const int32_t* pre, const int4* ttab,
                                       bf16_t* out, const bf16_t* mask, int E, int rows, int K, int N, hipStream_t s);
+// the same with W stored K-major, W[e][k][n]
+hipError_t launch_grouped_gemm_kmajor_f32(const bf16_t* A, const bf16_t* W, const int32_t* pre, const int4* ttab,
+                                          float* out, int E, int rows, int K, int N, hipStream_t s);
+hipError_t launch_grouped_gemm_kmajor_masked(const bf16_t* A, const bf16_t* W, const int32_t* pre, const int4* ttab,
+                                             bf16_t* out, const bf16_t* mask, int E, int rows, int K, int N,
+                                             hipStream_t s);
 
 // combine.hip
 hipError_t launch_combine(const float* y, const int32_t* expert, const int32_t* slot, const uint8_t* keep,
