@@ -298,6 +298,8 @@ switch_status validate_ffn(const FfnArgs& a, const void* ws, size_t ws_bytes) {
     REQUIRE(a.d >= 1 && a.d_ff >= 1, "d and d_ff must be >= 1");
     SUPPORT(a.d % 64 == 0 && a.d_ff % 64 == 0, "d and d_ff must be multiples of 64 (got %d, %d)", a.d, a.d_ff);
     SUPPORT((int64_t)a.E * a.C * std::max(a.d, a.d_ff) < (int64_t(1) << 40), "E*C*max(d,d_ff) too large");
+    SUPPORT((int64_t)a.d * a.d_ff * 2 < (int64_t(1) << 31), "one expert's weights must be < 2 GiB (d*d_ff*2)");
+    SUPPORT((int64_t)a.C * std::max(a.d, a.d_ff) * 2 < (int64_t(1) << 31), "C*max(d,d_ff)*2 must be < 2 GiB");
     NONNULL(a.accepted); NONNULL(a.w1); NONNULL(a.w2);
     if (a.C > 0) { NONNULL(a.buf); NONNULL(a.y); }
     ALIGNED16(a.buf); ALIGNED16(a.w1); ALIGNED16(a.w2); ALIGNED16(a.y); ALIGNED4(a.accepted); ALIGNED16(a.h);
@@ -517,6 +519,8 @@ switch_status switch_layer_bwd(const switch_layer_bwd_args* ba, void* ws, size_t
     SUPPORT((int64_t)E * std::max<int64_t>(pad64(C), std::max(d, F)) * std::max(d, F) < (int64_t(1) << 40),
             "E*C*max(d,d_ff) too large");
     REQUIRE(std::isfinite(B.alpha) && std::isfinite(B.z_beta), "alpha and z_beta must be finite");
+    SUPPORT((int64_t)d * F * 2 < (int64_t(1) << 31), "one expert's weights must be < 2 GiB (d*d_ff*2)");
+    SUPPORT((int64_t)pad64(C) * std::max(d, F) * 2 < (int64_t(1) << 31), "C*max(d,d_ff)*2 must be < 2 GiB");
     const bool tok = T > 0;
     NONNULL_IF(tok, B.x); NONNULL(B.w_r); NONNULL(B.w1); NONNULL(B.w2);
     NONNULL_IF(tok, B.expert); NONNULL_IF(tok, B.gate); NONNULL_IF(tok, B.position); NONNULL_IF(tok, B.keep);

@@ -37,6 +37,10 @@
 namespace swmoe {
 
 constexpr int FFN_LDS_STRIDE = 72;  // bf16 elements per token row in LDS (64 + 8 pad)
+// Fourth word of a raw buffer descriptor: 32-bit data format (the format is
+// not used by 16-byte loads, but a zero format is invalid).  Reads at or past
+// the descriptor's byte count return zero.
+constexpr int kBufferWord3 = 0x00020000;
 
 // Token-tile list: pre[e] = number of valid TOK-row token tiles of experts < e
 // (pre[E] = total V), and ttab[v] = {expert, first row, valid rows, 0} for
@@ -101,6 +105,129 @@ __device__ __forceinline__ FfnTile decode_tile(int i, const int4* __restrict__ t
 // array (the backward of the ReLU: zero wherever the saved activation is 0).
 enum FfnOut { OUT_RELU_BF16 = 0, OUT_F32 = 1, OUT_MASK_BF16 = 2 };
 
+// Tile epilogue shared by the GEMM kernels.  Output rows go out through LDS in
+// passes of CPP columns: the waves owning a pass park their results (lane:
+// token column l32 of block tb, weight rows 8*(i/4) + 4*half + i%4), then the
+// workgroup writes whole row segments with 16-byte stores.  `bar` is the
+// workgroup barrier between the passes.
+template <int TOKB, int NBW, int WAVES, int MODE, int PB>
+struct FfnOutShape {
+    static constexpr int TOK = 32 * TOKB;
+    static constexpr int NWG = WAVES * 32 * NBW;
+    static constexpr int OUT_BYTES = MODE != OUT_F32 ? 2 : 4;
+    static constexpr int ROW_BYTES = NWG * OUT_BYTES;
+    static constexpr int PASS_BYTES = ROW_BYTES <= PB ? ROW_BYTES
+                                      : (ROW_BYTES % PB == 0 ? PB : (ROW_BYTES % (PB / 2) == 0 ? PB / 2 : PB / 4));
+    static_assert(ROW_BYTES % PASS_BYTES == 0 && PASS_BYTES % 16 == 0, "whole 16-byte passes");
+    static constexpr int NPASS = ROW_BYTES / PASS_BYTES;
+    static constexpr int CPP = PASS_BYTES / OUT_BYTES;    // columns per pass
+    static constexpr int OSTRIDE = PASS_BYTES + 16;       // bytes per staged row
+    static constexpr int O_BYTES = TOK * OSTRIDE;
+};
+
+// Tile epilogue without LDS: each lane stores its accumulator values straight
+// to memory, 4 consecutive output columns (8 bytes in bf16, 16 in fp32) of one
+// token row at a time; L2 merges the pieces into whole lines.
+template <int TOKB, int NBW, int WAVES, int MODE>
+__device__ __forceinline__ void ffn_store_tile_direct(f32x16 (&acc)[NBW][TOKB], const FfnTile& t, void* out,
+                                                      const bf16_t* mask, int C, int N, int wave, int l32, int half) {
+    constexpr int NWG = WAVES * 32 * NBW;
+#pragma unroll
+    for (int tb = 0; tb < TOKB; ++tb) {
+        const int r = tb * 32 + l32;
+        if (r >= t.nv) continue;
+        const size_t row = ((size_t)t.e * C + t.tok_base + r) * N;
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int n = t.nt * NWG + wave * 32 * NBW + nb * 32 + q * 8 + half * 4;
+                if (n >= N) continue;
+                const f32x16& a = acc[nb][tb];
+                if constexpr (MODE == OUT_F32) {
+                    *(f32x4*)((float*)out + row + n) = f32x4{a[4 * q + 0], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+                } else {
+                    float v0 = a[4 * q + 0], v1 = a[4 * q + 1], v2 = a[4 * q + 2], v3 = a[4 * q + 3];
+                    if constexpr (MODE == OUT_RELU_BF16) {
+                        v0 = fmaxf(v0, 0.f); v1 = fmaxf(v1, 0.f); v2 = fmaxf(v2, 0.f); v3 = fmaxf(v3, 0.f);
+                    }
+                    uint2 o = make_uint2(bf16_rne(v0) | (bf16_rne(v1) << 16), bf16_rne(v2) | (bf16_rne(v3) << 16));
+                    if constexpr (MODE == OUT_MASK_BF16) {
+                        // keep the elements whose saved activation is non-zero
+                        const uint2 m = *(const uint2*)(mask + row + n);
+                        o.x &= ((m.x & 0x7fffu) ? 0xffffu : 0u) | ((m.x & 0x7fff0000u) ? 0xffff0000u : 0u);
+                        o.y &= ((m.y & 0x7fffu) ? 0xffffu : 0u) | ((m.y & 0x7fff0000u) ? 0xffff0000u : 0u);
+                    }
+                    *(uint2*)((bf16_t*)out + row + n) = o;
+                }
+            }
+    }
+}
+
+template <int TOKB, int NBW, int WAVES, int MODE, int PB, class Bar>
+__device__ __forceinline__ void ffn_store_tile(f32x16 (&acc)[NBW][TOKB], char* lds_o, const FfnTile& t, void* out,
+                                               const bf16_t* mask, int C, int N, int wave, int l32, int half,
+                                               Bar bar) {
+    using Sh = FfnOutShape<TOKB, NBW, WAVES, MODE, PB>;
+    constexpr int TOK = Sh::TOK, NWG = Sh::NWG, OUT_BYTES = Sh::OUT_BYTES, PASS_BYTES = Sh::PASS_BYTES;
+    constexpr int NPASS = Sh::NPASS, CPP = Sh::CPP, OSTRIDE = Sh::OSTRIDE, NTHR = 64 * WAVES;
+    const int ncols = min(NWG, N - t.nt * NWG);
+#pragma unroll
+    for (int pass = 0; pass < NPASS; ++pass) {
+        if (pass > 0) bar();
+        const int c0 = wave * 32 * NBW - pass * CPP;
+        if (c0 >= 0 && c0 < CPP) {
+#pragma unroll
+            for (int tb = 0; tb < TOKB; ++tb)
+#pragma unroll
+                for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int c = c0 + nb * 32 + q * 8 + half * 4;
+                        const f32x16& a = acc[nb][tb];
+                        char* dst = lds_o + (tb * 32 + l32) * OSTRIDE + c * OUT_BYTES;
+                        if constexpr (MODE == OUT_RELU_BF16) {
+                            const uint32_t b0 = bf16_rne(fmaxf(a[4 * q + 0], 0.f));
+                            const uint32_t b1 = bf16_rne(fmaxf(a[4 * q + 1], 0.f));
+                            const uint32_t b2 = bf16_rne(fmaxf(a[4 * q + 2], 0.f));
+                            const uint32_t b3 = bf16_rne(fmaxf(a[4 * q + 3], 0.f));
+                            *(uint2*)dst = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+                        } else if constexpr (MODE == OUT_MASK_BF16) {
+                            const uint32_t b0 = bf16_rne(a[4 * q + 0]), b1 = bf16_rne(a[4 * q + 1]);
+                            const uint32_t b2 = bf16_rne(a[4 * q + 2]), b3 = bf16_rne(a[4 * q + 3]);
+                            *(uint2*)dst = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+                        } else {
+                            *(f32x4*)dst = f32x4{a[4 * q + 0], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+                        }
+                    }
+        }
+        bar();
+        constexpr int VPR = PASS_BYTES / 16;           // 16-byte vectors per staged row
+        const int vpr_valid = max(0, min(CPP, ncols - pass * CPP)) * OUT_BYTES / 16;
+        char* gout = (char*)out + (((size_t)t.e * C + t.tok_base) * N + (size_t)t.nt * NWG + pass * CPP) * OUT_BYTES;
+#pragma unroll
+        for (int it = 0; it < (TOK * VPR + NTHR - 1) / NTHR; ++it) {
+            const int i = threadIdx.x + it * NTHR;
+            const int r = i / VPR, v = i - r * VPR;
+            if (i < TOK * VPR && r < t.nv && v < vpr_valid) {
+                u32x4 val = *(const u32x4*)(lds_o + r * OSTRIDE + v * 16);
+                if constexpr (MODE == OUT_MASK_BF16) {
+                    // keep the elements whose saved activation is non-zero
+                    const size_t off = (size_t)(gout - (char*)out) + (size_t)r * N * OUT_BYTES + v * 16;
+                    const u32x4 m = *(const u32x4*)((const char*)mask + off);
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        const uint32_t keep_lo = (m[w] & 0x7fffu) ? 0xffffu : 0u;
+                        const uint32_t keep_hi = (m[w] & 0x7fff0000u) ? 0xffff0000u : 0u;
+                        val[w] &= keep_lo | keep_hi;
+                    }
+                }
+                *(u32x4*)(gout + (size_t)r * N * OUT_BYTES + v * 16) = val;
+            }
+        }
+    }
+}
+
 // TOKB: 32-row token blocks per tile; NBW: 32-row weight blocks per wave;
 // WAVES: waves per workgroup; R: depth of the register rings; PB: bytes of an
 // output row staged through LDS per pass; MODE: an FfnOut; WKM: the weights
@@ -116,22 +243,13 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm(const bf16_t* __restri
                                                           void* __restrict__ out,         // [E, C, N]
                                                           const bf16_t* __restrict__ mask, // [E, C, N] (OUT_MASK_BF16)
                                                           int E, int C, int K, int N, int n_tiles) {
-    constexpr bool BF16_OUT = MODE != OUT_F32;
     constexpr int TOK = 32 * TOKB;
     constexpr int NWG = WAVES * 32 * NBW;
     constexpr int NTHR = 64 * WAVES;
     constexpr int PIECES = TOK * 8;                       // 16-byte pieces of one token chunk
     constexpr int APT = (PIECES + NTHR - 1) / NTHR;       // pieces per thread
-    constexpr int OUT_BYTES = BF16_OUT ? 2 : 4;
-    constexpr int ROW_BYTES = NWG * OUT_BYTES;                        // output bytes per token row
-    constexpr int PASS_BYTES = ROW_BYTES <= PB ? ROW_BYTES
-                               : (ROW_BYTES % PB == 0 ? PB : (ROW_BYTES % (PB / 2) == 0 ? PB / 2 : PB / 4));
-    static_assert(ROW_BYTES % PASS_BYTES == 0 && PASS_BYTES % 16 == 0, "whole 16-byte passes");
-    constexpr int NPASS = ROW_BYTES / PASS_BYTES;
-    constexpr int CPP = PASS_BYTES / OUT_BYTES;                       // columns per pass
-    constexpr int OSTRIDE = PASS_BYTES + 16;                          // bytes per staged row
     constexpr int A_BYTES = 2 * TOK * FFN_LDS_STRIDE * 2;
-    constexpr int O_BYTES = TOK * OSTRIDE;
+    constexpr int O_BYTES = FfnOutShape<TOKB, NBW, WAVES, MODE, PB>::O_BYTES;
     constexpr int W_BYTES = WKM ? 2 * NWG * FFN_LDS_STRIDE * 2 : 0;
     __shared__ __attribute__((aligned(16))) char lds_raw[A_BYTES + O_BYTES + W_BYTES];
     bf16_t* const lds_a = reinterpret_cast<bf16_t*>(lds_raw);
@@ -151,12 +269,29 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm(const bf16_t* __restri
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int half = lane >> 5, l32 = lane & 31;
 
-    // Frontier tile (the one whose chunks are being loaded).  Load addresses
-    // are a uniform 64-bit base (scalar registers) plus a 32-bit per-lane
-    // offset, so the loop computes no per-lane 64-bit addresses.
+    // Frontier tile (the one whose chunks are being loaded).  Loads go through
+    // buffer descriptors (scalar registers) set once per tile: the per-lane
+    // offsets never change, the chunk step is the scalar offset, and the
+    // descriptor's byte count is the bound, so token rows past the tile's
+    // valid rows (and weight rows past N) read as zero with no per-lane
+    // clamping.  The loop therefore computes no per-lane addresses at all.
     int f_tile = -1;
-    const char* wbase = nullptr;   // uniform: this wave's first weight row of the frontier tile
-    const char* abase = nullptr;   // uniform: the frontier tile's first token row
+    // descriptor fields, kept as scalars (a descriptor carried across the loop
+    // would be taken for a per-lane value); the descriptors are rebuilt at use
+    uint32_t a_lo = 0, a_hi = 0, a_n = 0, w_lo = 0, w_hi = 0, w_n = 0;
+    // Every field comes from scalar arithmetic on uniform values, with no
+    // min/max pairs or 64-bit compares: those become vector instructions, and
+    // a vector temporary here would make the loop wait for the ring's loads.
+    auto set_rsrc = [](const char* base, uint32_t nbytes, uint32_t& lo, uint32_t& hi, uint32_t& n) {
+        const uint64_t b = (uint64_t)(uintptr_t)base;
+        lo = (uint32_t)b;
+        hi = (uint32_t)(b >> 32);
+        n = nbytes;
+    };
+    auto rsrc = [](uint32_t lo, uint32_t hi, uint32_t n) {
+        return __builtin_amdgcn_make_buffer_rsrc((void*)(uintptr_t)(((uint64_t)hi << 32) | lo), (short)0, (int)n,
+                                                 kBufferWord3);
+    };
     uint32_t woff[NBW];            // per lane: weight row nb*32 + l32, half-chunk `half`
                                    // (K-major: group nb's k-row 4 kq and columns 8 nq ..)
     uint32_t aoffg[APT];           // per lane: token row and 16-byte column of piece j
@@ -174,13 +309,20 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm(const bf16_t* __restri
             woff[nb] = ((uint32_t)(nb * 32 + l32) * K + half * 32) * 2;
         }
     }
+#pragma unroll
+    for (int j2 = 0; j2 < APT; ++j2) {
+        const int q = min((int)threadIdx.x + j2 * NTHR, PIECES - 1);
+        aoffg[j2] = ((uint32_t)(q >> 3) * K + (q & 7) * 8) * 2;
+    }
     auto set_frontier = [&](int j) {
         f_tile = j;
         const FfnTile t = decode_tile(j * G + slot, ttab, n_tiles);
+        const char* ab = (const char*)A + ((size_t)t.e * C + t.tok_base) * K * 2;
+        set_rsrc(ab, (uint32_t)(t.nv * K * 2), a_lo, a_hi, a_n);
         if constexpr (WKM) {
             // columns past N read column group 0 and store nothing
             const int c0 = t.nt * NWG;
-            wbase = (const char*)W + (size_t)t.e * K * N * 2;
+            set_rsrc((const char*)W + (size_t)t.e * K * N * 2, (uint32_t)(K * N * 2), w_lo, w_hi, w_n);
 #pragma unroll
             for (int nb = 0; nb < NBW; ++nb) {
                 const int g = (int)threadIdx.x + nb * NTHR;
@@ -190,15 +332,13 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm(const bf16_t* __restri
                 woff[nb] = ((uint32_t)(kq * 4) * N + col) * 2;
             }
         } else {
+            // rows past N read zeros (the byte count ends at the expert's last
+            // row); a wave whose first row is past N reads from row 0 and stores
+            // nothing
             int wr0 = t.nt * NWG + wave * 32 * NBW;
-            if (wr0 >= N) wr0 = 0;     // waves past the last weight row read rows 0.. and store nothing
-            wbase = (const char*)W + ((size_t)t.e * N + wr0) * K * 2;
-        }
-        abase = (const char*)A + ((size_t)t.e * C + t.tok_base) * K * 2;
-#pragma unroll
-        for (int j2 = 0; j2 < APT; ++j2) {
-            const int q = min((int)threadIdx.x + j2 * NTHR, PIECES - 1);
-            aoffg[j2] = ((uint32_t)min(q >> 3, t.nv - 1) * K + (q & 7) * 8) * 2;
+            wr0 = wr0 < N ? wr0 : 0;
+            set_rsrc((const char*)W + ((size_t)t.e * N + wr0) * K * 2, (uint32_t)((N - wr0) * K * 2), w_lo, w_hi,
+                     w_n);
         }
     };
     int aoff[APT];
@@ -223,21 +363,21 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm(const bf16_t* __restri
         f = min(f, P - 1);
         const int jf = f / nk, kf = f - jf * nk;
         if (jf != f_tile) set_frontier(jf);
-        const char* ak = abase + kf * 128;
+        const __amdgpu_buffer_rsrc_t rs_a = rsrc(a_lo, a_hi, a_n), rs_w = rsrc(w_lo, w_hi, w_n);
 #pragma unroll
-        for (int j2 = 0; j2 < APT; ++j2) ar[j2] = *(const u32x4*)(ak + aoffg[j2]);
+        for (int j2 = 0; j2 < APT; ++j2) ar[j2] = __builtin_amdgcn_raw_buffer_load_b128(rs_a, aoffg[j2], kf * 128, 0);
         if constexpr (WKM) {
-            const char* wk = wbase + (size_t)kf * 64 * N * 2;   // k-rows 64 kf ..
 #pragma unroll
             for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
-                for (int j2 = 0; j2 < 4; ++j2) wr[nb][j2] = *(const u32x4*)(wk + woff[nb] + (uint32_t)j2 * N * 2);
+                for (int j2 = 0; j2 < 4; ++j2)   // k-rows 64 kf + 4 kq + j2
+                    wr[nb][j2] = __builtin_amdgcn_raw_buffer_load_b128(rs_w, woff[nb], (kf * 64 + j2) * N * 2, 0);
         } else {
-            const char* wk = wbase + kf * 128;
 #pragma unroll
             for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
-                for (int j2 = 0; j2 < 4; ++j2) wr[nb][j2] = *(const u32x4*)(wk + woff[nb] + j2 * 16);
+                for (int j2 = 0; j2 < 4; ++j2)
+                    wr[nb][j2] = __builtin_amdgcn_raw_buffer_load_b128(rs_w, woff[nb] + j2 * 16, kf * 128, 0);
         }
     };
 
@@ -304,65 +444,189 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm(const bf16_t* __restri
                 if (p - j * nk == nk - 1) {
                     // ------------------------------------------------ tile epilogue
                     const FfnTile t = decode_tile(j * G + slot, ttab, n_tiles);
-                    // Output rows go out through LDS in passes of CPP columns:
-                    // the waves owning a pass park their results (lane: token
-                    // column l32 of block tb, weight rows 8*(i/4) + 4*half + i%4),
-                    // then the workgroup writes whole row segments with
-                    // 16-byte stores.
-                    const int ncols = min(NWG, N - t.nt * NWG);
+                    ffn_store_tile<TOKB, NBW, WAVES, MODE, PB>(acc, lds_o, t, out, mask, C, N, wave, l32, half,
+                                                               [] { __syncthreads(); });
 #pragma unroll
-                    for (int pass = 0; pass < NPASS; ++pass) {
-                        if (pass > 0) __syncthreads();
-                        const int c0 = wave * 32 * NBW - pass * CPP;
-                        if (c0 >= 0 && c0 < CPP) {
+                    for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
-                            for (int tb = 0; tb < TOKB; ++tb)
+                        for (int tb = 0; tb < TOKB; ++tb)
 #pragma unroll
-                                for (int nb = 0; nb < NBW; ++nb)
+                            for (int i = 0; i < 16; ++i) acc[nb][tb][i] = 0.f;
+                }
+            }
+        }
+    }
+}
+
+
+// ---------------------------------------------------------------------------
+// Direct-to-LDS variant for 128-row token tiles with weights stored [N][K].
+// Both operands of a 64-wide K chunk are copied from memory straight into an
+// LDS stage by buffer loads with an LDS destination, so no registers hold data
+// in flight and the copies run S - 1 chunks ahead of the MFMAs (the register
+// rings above are limited by the register file to about three chunks).  A
+// copy instruction moves 8 rows x 128 bytes; its lanes fetch 16-byte columns
+// XOR-swizzled by the row (column c of row r lands in slot c ^ (r & 7) of the
+// 128-byte LDS row), which keeps the MFMA fragment reads free of bank
+// conflicts.  Rows past a tile's valid tokens, or past N, read as zero through
+// the descriptors' byte counts.  Each wave waits for its own copies of a chunk
+// (vmcnt) before the workgroup barrier that publishes the chunk; the LDS-only
+// barriers avoid the full memory fence, which would wait for every copy in
+// flight.  The finished stage also holds the tile's output staging.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <int N_OUTSTANDING>
+__device__ __forceinline__ void wait_copies() {
+    static_assert(N_OUTSTANDING >= 0 && N_OUTSTANDING < 64, "vmcnt range");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((N_OUTSTANDING & 15) | ((N_OUTSTANDING >> 4) << 14) | 0x0F70);
+}
+
+// One 1 KiB copy: lane i's 16 bytes land at dst + 16 i.  (The LDS address
+// space exists only in the device pass.)
+__device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t rs, char* dst, uint32_t voff, uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0, 0);
+#endif
+}
+
+template <int TOKB, int NBW, int WAVES, int MODE, int PB, int S, bool DIRECT = false>
+__global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __restrict__ A,   // [E, C, K]
+                                                              const bf16_t* __restrict__ W,   // [E, N, K]
+                                                              const int32_t* __restrict__ pre,
+                                                              const int4* __restrict__ ttab,
+                                                              void* __restrict__ out,
+                                                              const bf16_t* __restrict__ mask,
+                                                              int E, int C, int K, int N, int n_tiles) {
+    using Sh = FfnOutShape<TOKB, NBW, WAVES, MODE, PB>;
+    constexpr int TOK = 32 * TOKB;
+    constexpr int NWG = WAVES * 32 * NBW;
+    constexpr int W_COPIES = NWG / 8;                       // 1 KiB copies per chunk
+    constexpr int A_COPIES = TOK / 8;
+    static_assert(W_COPIES % WAVES == 0, "whole weight copies per wave");
+    constexpr int WPW = W_COPIES / WAVES;
+    constexpr int APW = (A_COPIES + WAVES - 1) / WAVES;     // the last copies of some waves are spares
+    constexpr int W_STAGE = NWG * 128;
+    constexpr int A_STAGE = APW * WAVES * 1024;             // token rows, then the spares' landing area
+    constexpr int STAGE = W_STAGE + A_STAGE;
+    constexpr int PER_CHUNK = WPW + APW;                    // copies per wave per chunk
+    static_assert(DIRECT || Sh::O_BYTES <= STAGE, "output staging fits in a stage");
+    static_assert(PER_CHUNK * (S - 1) < 64, "outstanding copies fit the counter");
+    __shared__ __attribute__((aligned(16))) char lds[S * STAGE];
+
+    const int total = pre[E] * n_tiles;
+    const int G = gridDim.x;                                          // a multiple of 8
+    const int slot = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3); // XCD-major
+    if (slot >= total) return;
+    const int ntl = (total - slot + G - 1) / G;
+    const int nk = K >> 6;
+    const int P = ntl * nk;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int half = lane >> 5, l32 = lane & 31;
+
+    // lane offsets of the copies (row 8 q + lane / 8, swizzled 16-byte column)
+    uint32_t wvo[WPW], avo[APW];
 #pragma unroll
-                                    for (int q = 0; q < 4; ++q) {
-                                        const int c = c0 + nb * 32 + q * 8 + half * 4;
-                                        const f32x16& a = acc[nb][tb];
-                                        char* dst = lds_o + (tb * 32 + l32) * OSTRIDE + c * OUT_BYTES;
-                                        if constexpr (MODE == OUT_RELU_BF16) {
-                                            const uint32_t b0 = bf16_rne(fmaxf(a[4 * q + 0], 0.f));
-                                            const uint32_t b1 = bf16_rne(fmaxf(a[4 * q + 1], 0.f));
-                                            const uint32_t b2 = bf16_rne(fmaxf(a[4 * q + 2], 0.f));
-                                            const uint32_t b3 = bf16_rne(fmaxf(a[4 * q + 3], 0.f));
-                                            *(uint2*)dst = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
-                                        } else if constexpr (MODE == OUT_MASK_BF16) {
-                                            const uint32_t b0 = bf16_rne(a[4 * q + 0]), b1 = bf16_rne(a[4 * q + 1]);
-                                            const uint32_t b2 = bf16_rne(a[4 * q + 2]), b3 = bf16_rne(a[4 * q + 3]);
-                                            *(uint2*)dst = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
-                                        } else {
-                                            *(f32x4*)dst = f32x4{a[4 * q + 0], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
-                                        }
-                                    }
-                        }
-                        __syncthreads();
-                        constexpr int VPR = PASS_BYTES / 16;           // 16-byte vectors per staged row
-                        const int vpr_valid = max(0, min(CPP, ncols - pass * CPP)) * OUT_BYTES / 16;
-                        char* gout = (char*)out + (((size_t)t.e * C + t.tok_base) * N + (size_t)t.nt * NWG + pass * CPP) * OUT_BYTES;
+    for (int i = 0; i < WPW; ++i) {
+        const int r = 8 * (wave * WPW + i) + (lane >> 3);
+        wvo[i] = (uint32_t)r * K * 2 + (((lane & 7) ^ (r & 7)) << 4);
+    }
 #pragma unroll
-                        for (int it = 0; it < (TOK * VPR + NTHR - 1) / NTHR; ++it) {
-                            const int i = threadIdx.x + it * NTHR;
-                            const int r = i / VPR, v = i - r * VPR;
-                            if (i < TOK * VPR && r < t.nv && v < vpr_valid) {
-                                u32x4 val = *(const u32x4*)(lds_o + r * OSTRIDE + v * 16);
-                                if constexpr (MODE == OUT_MASK_BF16) {
-                                    // keep the elements whose saved activation is non-zero
-                                    const size_t off = (size_t)(gout - (char*)out) + (size_t)r * N * OUT_BYTES + v * 16;
-                                    const u32x4 m = *(const u32x4*)((const char*)mask + off);
+    for (int i = 0; i < APW; ++i) {
+        const int q = wave * APW + i;
+        const int r = 8 * (q < A_COPIES ? q : 0) + (lane >> 3);   // spares copy rows 0..7 again
+        avo[i] = (uint32_t)r * K * 2 + (((lane & 7) ^ (r & 7)) << 4);
+    }
+
+    int f_tile = -1;
+    uint32_t a_lo = 0, a_hi = 0, a_n = 0, w_lo = 0, w_hi = 0, w_n = 0;
+    auto rsrc = [](uint32_t lo, uint32_t hi, uint32_t n) {
+        return __builtin_amdgcn_make_buffer_rsrc((void*)(uintptr_t)(((uint64_t)hi << 32) | lo), (short)0, (int)n,
+                                                 kBufferWord3);
+    };
+    auto set_frontier = [&](int j) {
+        f_tile = j;
+        const FfnTile t = decode_tile(j * G + slot, ttab, n_tiles);
+        const uint64_t ab = (uint64_t)(uintptr_t)((const char*)A + ((size_t)t.e * C + t.tok_base) * K * 2);
+        a_lo = (uint32_t)ab;
+        a_hi = (uint32_t)(ab >> 32);
+        a_n = (uint32_t)(t.nv * K * 2);
+        const int r0 = t.nt * NWG;                                   // rows past N read zeros
+        const uint64_t wb = (uint64_t)(uintptr_t)((const char*)W + ((size_t)t.e * N + r0) * K * 2);
+        w_lo = (uint32_t)wb;
+        w_hi = (uint32_t)(wb >> 32);
+        w_n = (uint32_t)((N - r0) * K * 2);
+    };
+    // copies of chunk position f (clamped to the last one) into stage `stg`
+    auto issue = [&](int f, int stg) {
+        f = min(f, P - 1);
+        const int jf = f / nk, kf = f - jf * nk;
+        if (jf != f_tile) set_frontier(jf);
+        const __amdgpu_buffer_rsrc_t rs_a = rsrc(a_lo, a_hi, a_n), rs_w = rsrc(w_lo, w_hi, w_n);
+        char* sb = lds + stg * STAGE;
 #pragma unroll
-                                    for (int w = 0; w < 4; ++w) {
-                                        const uint32_t keep_lo = (m[w] & 0x7fffu) ? 0xffffu : 0u;
-                                        const uint32_t keep_hi = (m[w] & 0x7fff0000u) ? 0xffff0000u : 0u;
-                                        val[w] &= keep_lo | keep_hi;
-                                    }
-                                }
-                                *(u32x4*)(gout + (size_t)r * N * OUT_BYTES + v * 16) = val;
-                            }
-                        }
+        for (int i = 0; i < WPW; ++i) copy_to_lds(rs_w, sb + (wave * WPW + i) * 1024, wvo[i], kf * 128);
+#pragma unroll
+        for (int i = 0; i < APW; ++i) copy_to_lds(rs_a, sb + W_STAGE + (wave * APW + i) * 1024, avo[i], kf * 128);
+    };
+
+    f32x16 acc[NBW][TOKB];
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+        for (int tb = 0; tb < TOKB; ++tb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[nb][tb][i] = 0.f;
+
+#pragma unroll
+    for (int p = 0; p < S - 1; ++p) issue(p, p);
+
+    for (int p0 = 0; p0 < P; p0 += S) {
+#pragma unroll
+        for (int u = 0; u < S; ++u) {
+            const int p = p0 + u;
+            if (p < P) {
+                issue(p + S - 1, (u + S - 1) % S);      // the stage consumed at the previous position
+                wait_copies<PER_CHUNK * (S - 1)>();      // this wave's copies of position p are in LDS
+                lds_barrier();                           // and every wave's
+                const char* sw = lds + u * STAGE;
+                const char* sa = sw + W_STAGE;
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const int c = half * 4 + s;          // 16-byte column of the 128-byte row
+                    bf16x8 bt[TOKB];
+#pragma unroll
+                    for (int tb = 0; tb < TOKB; ++tb) {
+                        const int r = tb * 32 + l32;
+                        bt[tb] = as_bf16x8(*(const u32x4*)(sa + r * 128 + ((c ^ (r & 7)) << 4)));
+                    }
+#pragma unroll
+                    for (int nb = 0; nb < NBW; ++nb) {
+                        const int r = wave * 32 * NBW + nb * 32 + l32;
+                        const bf16x8 wa = as_bf16x8(*(const u32x4*)(sw + r * 128 + ((c ^ (r & 7)) << 4)));
+#pragma unroll
+                        for (int tb = 0; tb < TOKB; ++tb)
+                            acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, bt[tb], acc[nb][tb], 0, 0, 0);
+                    }
+                }
+                lds_barrier();                           // stage u is free for the next copies
+
+                const int j = p / nk;
+                if (p - j * nk == nk - 1) {
+                    const FfnTile t = decode_tile(j * G + slot, ttab, n_tiles);
+                    if constexpr (DIRECT) {
+                        ffn_store_tile_direct<TOKB, NBW, WAVES, MODE>(acc, t, out, mask, C, N, wave, l32, half);
+                    } else {
+                        ffn_store_tile<TOKB, NBW, WAVES, MODE, PB>(acc, lds + u * STAGE, t, out, mask, C, N, wave,
+                                                                   l32, half, [] { lds_barrier(); });
+                        lds_barrier();                   // the staging area is read out before stage u refills
                     }
 #pragma unroll
                     for (int nb = 0; nb < NBW; ++nb)
@@ -411,6 +675,20 @@ hipError_t launch_expert_gemm_t(const bf16_t* A, const bf16_t* W, const int32_t*
     return hipGetLastError();
 }
 
+template <int TOKB, int NBW, int WAVES, int MODE, int PB, int S, bool DIRECT = false>
+hipError_t launch_expert_gemm_dma_t(const bf16_t* A, const bf16_t* W, const int32_t* pre, const int4* ttab, void* out,
+                                    const bf16_t* mask, int E, int C, int K, int N, hipStream_t s) {
+    constexpr int NWG = WAVES * 32 * NBW;
+    const int n_tiles = (N + NWG - 1) / NWG;
+    const int tok_tiles = (C + 32 * TOKB - 1) / (32 * TOKB);
+    const int64_t max_tiles = (int64_t)E * n_tiles * tok_tiles;
+    int64_t grid = std::min<int64_t>((int64_t)device_cus(), (max_tiles + 7) / 8 * 8);   // one workgroup per CU
+    grid = std::max<int64_t>(8, grid / 8 * 8);
+    hipLaunchKernelGGL((expert_gemm_dma<TOKB, NBW, WAVES, MODE, PB, S, DIRECT>), dim3((unsigned)grid), dim3(64 * WAVES), 0,
+                       s, A, W, pre, ttab, out, mask, E, C, K, N, n_tiles);
+    return hipGetLastError();
+}
+
 int ffn_token_tile(int C) { return C > 64 ? 128 : (C > 32 ? 64 : 32); }
 
 size_t ffn_tile_table_entries(int E, int C) {
@@ -424,20 +702,24 @@ hipError_t launch_ffn_tile_prefix(const int32_t* accepted, int E, int C, int32_t
 }
 
 #ifndef SWMOE_FFN_CUSTOM_DISPATCH
-// Tile width for 128-row token tiles.  Every workgroup streams NWG weight rows
-// per tile, so a round of tiles over the persistent grid costs about NWG; the
-// kernel takes ceil(tiles / grid) rounds.  Choose the width with the smaller
-// rounds * NWG (the wider one on a tie), counting every expert's token tiles
-// as full: e.g. N = 768 at 128 experts gives 384 tiles of 256 columns (two
-// rounds, the second half empty) against 512 tiles of 192 (two full rounds).
-static bool narrow_tiles(int E, int C, int N) {
+// Tile width for 128-row token tiles (the direct-to-LDS kernel).  Every
+// workgroup streams NWG weight rows per tile, so a round of tiles over the
+// persistent grid (one workgroup per CU) costs about NWG, and the kernel takes
+// ceil(tiles / grid) rounds.  The width with the smallest rounds * NWG wins,
+// the wider one on a tie (fewer, longer weight streams per workgroup); every
+// expert's token tiles count as full.  E.g. at 128 experts, N = 768 takes 384
+// columns (two tiles per expert, one round); N = 3072 and N = 4096 take 512.
+static int dma_tile_width(int E, int C, int N) {
     const int64_t tok_tiles = (int64_t)E * ((C + 127) / 128);
-    const int64_t grid = device_cus();          // one 6- or 8-wave workgroup per CU
-    auto cost = [&](int nwg) {
+    const int64_t grid = device_cus();
+    int best = 0;
+    int64_t best_cost = 0;
+    for (const int nwg : {512, 384, 256, 192}) {
         const int64_t tiles = tok_tiles * ((N + nwg - 1) / nwg);
-        return (tiles + grid - 1) / grid * nwg;
-    };
-    return cost(192) < cost(256);
+        const int64_t cost = (tiles + grid - 1) / grid * nwg;
+        if (best == 0 || cost < best_cost) { best = nwg; best_cost = cost; }
+    }
+    return best;
 }
 
 template <int MODE>
@@ -445,26 +727,35 @@ static hipError_t launch_expert_gemm(const bf16_t* A, const bf16_t* W, const int
                                      const bf16_t* mask, int E, int C, int K, int N, hipStream_t s) {
     // the token tile must be ffn_token_tile(C) rows: the prefix kernel lists tiles of that size
     if (C > 64) {
-        if (narrow_tiles(E, C, N))
-            return launch_expert_gemm_t<4, 1, 6, 3, MODE, 256>(A, W, pre, ttab, out, mask, E, C, K, N, s);
-        return launch_expert_gemm_t<4, 1, 8, 4, MODE, 512>(A, W, pre, ttab, out, mask, E, C, K, N, s);
+        switch (dma_tile_width(E, C, N)) {
+            case 512:
+                return launch_expert_gemm_dma_t<4, 2, 8, MODE, 256, 2, true>(A, W, pre, ttab, out, mask, E, C, K, N, s);
+            case 384:
+                return launch_expert_gemm_dma_t<4, 2, 6, MODE, 256, 2, true>(A, W, pre, ttab, out, mask, E, C, K, N, s);
+            case 256:
+                return launch_expert_gemm_dma_t<4, 1, 8, MODE, 256, 2, true>(A, W, pre, ttab, out, mask, E, C, K, N, s);
+            default:
+                return launch_expert_gemm_dma_t<4, 1, 6, MODE, 256, 3, true>(A, W, pre, ttab, out, mask, E, C, K, N, s);
+        }
     }
     if (C > 32) return launch_expert_gemm_t<2, 2, 4, 3, MODE, 512>(A, W, pre, ttab, out, mask, E, C, K, N, s);
     return launch_expert_gemm_t<1, 2, 4, 4, MODE, 512>(A, W, pre, ttab, out, mask, E, C, K, N, s);
 }
 
-hipError_t launch_expert_gemm1(const bf16_t* buf, const bf16_t* w1, const int32_t* pre, const int4* ttab, bf16_t* h,
-                               int E, int C, int d, int d_ff, hipStream_t s) {
-    return launch_expert_gemm<OUT_RELU_BF16>(buf, w1, pre, ttab, h, nullptr, E, C, d, d_ff, s);
+// Register kernel with 128-row token tiles: 192 columns (6 waves) when that
+// takes fewer rounds x columns over the grid than 256 (8 waves).
+static bool narrow_tiles(int E, int C, int N) {
+    const int64_t tok_tiles = (int64_t)E * ((C + 127) / 128);
+    const int64_t grid = device_cus();
+    auto cost = [&](int nwg) {
+        const int64_t tiles = tok_tiles * ((N + nwg - 1) / nwg);
+        return (tiles + grid - 1) / grid * nwg;
+    };
+    return cost(192) < cost(256);
 }
 
-hipError_t launch_expert_gemm2(const bf16_t* h, const bf16_t* w2, const int32_t* pre, const int4* ttab, float* y,
-                               int E, int C, int d, int d_ff, hipStream_t s) {
-    return launch_expert_gemm<OUT_F32>(h, w2, pre, ttab, y, nullptr, E, C, d_ff, d, s);
-}
-
-// K-major weights: one configuration per token-tile size; the staged weight
-// tile needs a 256-byte output pass to fit LDS next to it.
+// K-major weights (the register kernel): one configuration per token-tile
+// size; the staged weight tile needs a 256-byte output pass to fit LDS next to it.
 template <int MODE>
 static hipError_t launch_expert_gemm_kmajor(const bf16_t* A, const bf16_t* W, const int32_t* pre, const int4* ttab,
                                             void* out, const bf16_t* mask, int E, int C, int K, int N, hipStream_t s) {
@@ -475,6 +766,16 @@ static hipError_t launch_expert_gemm_kmajor(const bf16_t* A, const bf16_t* W, co
     }
     if (C > 32) return launch_expert_gemm_t<2, 2, 4, 3, MODE, 512, true>(A, W, pre, ttab, out, mask, E, C, K, N, s);
     return launch_expert_gemm_t<1, 2, 4, 4, MODE, 512, true>(A, W, pre, ttab, out, mask, E, C, K, N, s);
+}
+
+hipError_t launch_expert_gemm1(const bf16_t* buf, const bf16_t* w1, const int32_t* pre, const int4* ttab, bf16_t* h,
+                               int E, int C, int d, int d_ff, hipStream_t s) {
+    return launch_expert_gemm<OUT_RELU_BF16>(buf, w1, pre, ttab, h, nullptr, E, C, d, d_ff, s);
+}
+
+hipError_t launch_expert_gemm2(const bf16_t* h, const bf16_t* w2, const int32_t* pre, const int4* ttab, float* y,
+                               int E, int C, int d, int d_ff, hipStream_t s) {
+    return launch_expert_gemm<OUT_F32>(h, w2, pre, ttab, y, nullptr, E, C, d_ff, d, s);
 }
 
 hipError_t launch_grouped_gemm_kmajor_f32(const bf16_t* A, const bf16_t* W, const int32_t* pre, const int4* ttab,
@@ -488,14 +789,17 @@ hipError_t launch_grouped_gemm_kmajor_masked(const bf16_t* A, const bf16_t* W, c
     return launch_expert_gemm_kmajor<OUT_MASK_BF16>(A, W, pre, ttab, out, mask, E, rows, K, N, s);
 }
 
+// Products whose output outweighs the weight stream (a short K, such as the
+// token axis of the weight gradients) keep the register kernel, whose tile
+// output leaves through LDS as whole 16-byte row segments.
 hipError_t launch_grouped_gemm_f32(const bf16_t* A, const bf16_t* W, const int32_t* pre, const int4* ttab, float* out,
                                    int E, int rows, int K, int N, hipStream_t s) {
+    if (rows > 64) {
+        if (narrow_tiles(E, rows, N))
+            return launch_expert_gemm_t<4, 1, 6, 3, OUT_F32, 256>(A, W, pre, ttab, out, nullptr, E, rows, K, N, s);
+        return launch_expert_gemm_t<4, 1, 8, 4, OUT_F32, 512>(A, W, pre, ttab, out, nullptr, E, rows, K, N, s);
+    }
     return launch_expert_gemm<OUT_F32>(A, W, pre, ttab, out, nullptr, E, rows, K, N, s);
-}
-
-hipError_t launch_grouped_gemm_masked(const bf16_t* A, const bf16_t* W, const int32_t* pre, const int4* ttab,
-                                      bf16_t* out, const bf16_t* mask, int E, int rows, int K, int N, hipStream_t s) {
-    return launch_expert_gemm<OUT_MASK_BF16>(A, W, pre, ttab, out, mask, E, rows, K, N, s);
 }
 #endif
 

@@ -49,11 +49,9 @@ hipError_t launch_expert_gemm1(const bf16_t* buf, const bf16_t* w1, const int32_
 hipError_t launch_expert_gemm2(const bf16_t* h, const bf16_t* w2, const int32_t* pre, const int4* ttab, float* y,
                                int E, int C, int d, int d_ff, hipStream_t s);
 // the same kernel on other operands: out[e, r, n] = sum_k A[e, r, k] W[e, n, k]
-// for the rows listed in (pre, ttab), fp32 out; or bf16 out zeroed where mask == 0
+// for the rows listed in (pre, ttab), fp32 out
 hipError_t launch_grouped_gemm_f32(const bf16_t* A, const bf16_t* W, const int32_t* pre, const int4* ttab, float* out,
                                    int E, int rows, int K, int N, hipStream_t s);
-hipError_t launch_grouped_gemm_masked(const bf16_t* A, const bf16_t* W, const int32_t* pre, const int4* ttab,
-                                      bf16_t* out, const bf16_t* mask, int E, int rows, int K, int N, hipStream_t s);
 // the same with W stored K-major, W[e][k][n]
 hipError_t launch_grouped_gemm_kmajor_f32(const bf16_t* A, const bf16_t* W, const int32_t* pre, const int4* ttab,
                                           float* out, int E, int rows, int K, int N, hipStream_t s);
