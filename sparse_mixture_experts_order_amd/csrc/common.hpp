@@ -64,4 +64,69 @@ __device__ __forceinline__ int xcd_swizzle(int bid, int grid_padded) {
     return (bid & 7) * per_xcd + (bid >> 3);
 }
 
+// Cross-lane moves that stay in the VALU (no LDS round trip).
+// lane ^ 16 and lane ^ 32: the gfx950 row swaps, applied to two copies of v,
+// return {v's even rows, v's odd rows} (or lower, upper halves) laid out so
+// that each lane picks its partner's value.
+__device__ __forceinline__ uint32_t lane_xor16(uint32_t v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return ((threadIdx.x >> 4) & 1) ? r[0] : r[1];
+}
+__device__ __forceinline__ uint32_t lane_xor32(uint32_t v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return ((threadIdx.x >> 5) & 1) ? r[0] : r[1];
+}
+__device__ __forceinline__ float lane_xor16(float v) { return __uint_as_float(lane_xor16(__float_as_uint(v))); }
+__device__ __forceinline__ float lane_xor32(float v) { return __uint_as_float(lane_xor32(__float_as_uint(v))); }
+__device__ __forceinline__ int lane_xor16(int v) { return (int)lane_xor16((uint32_t)v); }
+__device__ __forceinline__ int lane_xor32(int v) { return (int)lane_xor32((uint32_t)v); }
+
+// Sum over each row of 16 lanes, every lane of the row getting the sum: the
+// partners lane ^ 1, ^ 2 (quad permutations), then the mirrored quad and the
+// mirrored half row (DPP row_half_mirror, row_mirror), so the additions pair
+// the same values in the same order as a butterfly over lane ^ 1, 2, 4, 8.
+__device__ __forceinline__ float row16_sum(float v) {
+    v += __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), 0xB1, 0xF, 0xF, false));   // [1,0,3,2]
+    v += __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), 0x4E, 0xF, 0xF, false));   // [2,3,0,1]
+    v += __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), 0x141, 0xF, 0xF, false));  // half mirror
+    v += __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), 0x140, 0xF, 0xF, false));  // mirror
+    return v;
+}
+
+// Raw buffer descriptors.  The fourth word selects the 32-bit data format
+// (unused by 16-byte loads, but a zero format is invalid); reads at or past
+// the descriptor's byte count return zero.
+constexpr int kBufferWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t nbytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, kBufferWord3);
+}
+
+// Copies from memory straight into LDS.  A wave's copy instruction moves
+// 64 x 16 bytes (lane i's 16 bytes land at dst + 16 i) and counts in vmcnt
+// like any other load, so a wave waits for its own copies with wait_copies
+// and then meets the other waves at an LDS-only barrier (the full barrier's
+// memory fence would also wait for every copy still in flight).
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <int N_OUTSTANDING>
+__device__ __forceinline__ void wait_copies() {
+    static_assert(N_OUTSTANDING >= 0 && N_OUTSTANDING < 64, "vmcnt range");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((N_OUTSTANDING & 15) | ((N_OUTSTANDING >> 4) << 14) | 0x0F70);
+}
+
+// One 1 KiB copy: lane i's 16 bytes land at dst + 16 i.  (The LDS address
+// space exists only in the device pass.)
+__device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t rs, char* dst, uint32_t voff, uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0, 0);
+#endif
+}
+
 }  // namespace swmoe

@@ -37,10 +37,6 @@
 namespace swmoe {
 
 constexpr int FFN_LDS_STRIDE = 72;  // bf16 elements per token row in LDS (64 + 8 pad)
-// Fourth word of a raw buffer descriptor: 32-bit data format (the format is
-// not used by 16-byte loads, but a zero format is invalid).  Reads at or past
-// the descriptor's byte count return zero.
-constexpr int kBufferWord3 = 0x00020000;
 
 // Token-tile list: pre[e] = number of valid TOK-row token tiles of experts < e
 // (pre[E] = total V), and ttab[v] = {expert, first row, valid rows, 0} for
@@ -473,28 +469,6 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm(const bf16_t* __restri
 // (vmcnt) before the workgroup barrier that publishes the chunk; the LDS-only
 // barriers avoid the full memory fence, which would wait for every copy in
 // flight.  The finished stage also holds the tile's output staging.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-template <int N_OUTSTANDING>
-__device__ __forceinline__ void wait_copies() {
-    static_assert(N_OUTSTANDING >= 0 && N_OUTSTANDING < 64, "vmcnt range");
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt((N_OUTSTANDING & 15) | ((N_OUTSTANDING >> 4) << 14) | 0x0F70);
-}
-
-// One 1 KiB copy: lane i's 16 bytes land at dst + 16 i.  (The LDS address
-// space exists only in the device pass.)
-__device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t rs, char* dst, uint32_t voff, uint32_t soff) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0, 0);
-#endif
-}
-
 template <int TOKB, int NBW, int WAVES, int MODE, int PB, int S, bool DIRECT = false>
 __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __restrict__ A,   // [E, C, K]
                                                               const bf16_t* __restrict__ W,   // [E, N, K]
@@ -638,6 +612,7 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
             }
         }
     }
+    wait_copies<0>();   // the clamped copies past the last chunk land before the workgroup ends
 }
 
 // ------------------------------------------------------------------ launchers

@@ -17,10 +17,13 @@
 
 namespace swmoe {
 
-// w_r [d, E] fp32 -> wr3 [3][E][d] bf16 (expert-major so that an MFMA operand
-// row -- one expert, 8 consecutive k -- is 16 contiguous bytes).
+// w_r [d, E] fp32 -> the three bf16 terms, expert-major so that an MFMA
+// operand row (one expert, 8 consecutive k) is 16 contiguous bytes:
+//   plain   [3][E][d]                  (the two-pass router GEMM)
+//   chunked [d / 32][3][E][32]         (the fused router: the weight rows of
+//                                       one 32-wide K stage are one block)
 __global__ __launch_bounds__(256) void split_router_weights(const float* __restrict__ w_r,
-                                                            bf16_t* __restrict__ wr3, int d, int E) {
+                                                            bf16_t* __restrict__ wr3, int d, int E, int chunked) {
     __shared__ float tile[32][33];
     const int e0 = blockIdx.x * 32, k0 = blockIdx.y * 32;
     const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
@@ -39,10 +42,17 @@ __global__ __launch_bounds__(256) void split_router_weights(const float* __restr
             uint32_t mid = bf16_rne(r1);
             float r2 = r1 - bf16_to_f32(mid);
             uint32_t lo = bf16_rne(r2);
-            size_t o = (size_t)e * d + k;
-            wr3[o] = (bf16_t)hi;
-            wr3[plane + o] = (bf16_t)mid;
-            wr3[2 * plane + o] = (bf16_t)lo;
+            if (chunked) {   // d is a multiple of 32 here: the tile is one K stage
+                const size_t o = (size_t)blockIdx.y * 3 * E * 32 + (size_t)e * 32 + tx;
+                wr3[o] = (bf16_t)hi;
+                wr3[o + (size_t)E * 32] = (bf16_t)mid;
+                wr3[o + (size_t)2 * E * 32] = (bf16_t)lo;
+            } else {
+                const size_t o = (size_t)e * d + k;
+                wr3[o] = (bf16_t)hi;
+                wr3[plane + o] = (bf16_t)mid;
+                wr3[2 * plane + o] = (bf16_t)lo;
+            }
         }
     }
 }
@@ -238,9 +248,9 @@ __global__ __launch_bounds__(1024) void router_reduce(const float* __restrict__ 
 }
 
 // ------------------------------------------------------------------ launchers
-hipError_t launch_split_router_weights(const float* w_r, bf16_t* wr3, int d, int E, hipStream_t s) {
+hipError_t launch_split_router_weights(const float* w_r, bf16_t* wr3, int d, int E, bool chunked, hipStream_t s) {
     dim3 grid((E + 31) / 32, (d + 31) / 32);
-    hipLaunchKernelGGL(split_router_weights, grid, dim3(256), 0, s, w_r, wr3, d, E);
+    hipLaunchKernelGGL(split_router_weights, grid, dim3(256), 0, s, w_r, wr3, d, E, chunked ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -313,223 +323,255 @@ hipError_t launch_column_sum(const float* a, int rows, int E, float* slices, flo
 
 
 // ---------------------------------------------------------------------------
-// Fused router for E <= 256: logits, softmax statistics and top-1 in one pass.
-// A workgroup owns RF_TOK tokens and all experts; wave w owns 16*RF_TB of the
-// tokens (RF_TB 16-token MFMA blocks) against every expert, so a token's whole
-// logit row lives in one wave.  The three bf16 terms of W_r stream through LDS
-// (shared by the 4 waves) in 32-wide K stages; the token fragments stream
-// straight into registers.  Both go through register rings R stages deep.
-// Epilogue per token: bias, row max with the lowest index on ties, sum of
-// exp, lse, gate = 1/sum, optional logits store, and the workgroup's partial
-// sums of p_te over its tokens (shuffles over the 16 tokens of a block, the
-// two blocks in turn, then the waves in turn through LDS: a fixed order).
-constexpr int RF_TB = 1;                 // 16-token MFMA blocks per wave
-constexpr int RF_TOK = 4 * 16 * RF_TB;   // tokens per workgroup
-constexpr int RF_ROW = 40;     // bf16 per staged W row: 32 + 8 pad (80 bytes)
+// Fused router for E <= 256: logits, softmax statistics and top-k in one pass.
+// A workgroup (4 waves) owns RF_TOK = 64 tokens and all experts.  The waves
+// split the expert blocks of 16 (up to 4 ways) and, with fewer than 4 expert
+// blocks, the four 16-token blocks.  Per 32-wide K stage:
+//  - the 64 token rows (64 bytes each) are copied from memory straight into
+//    an LDS stage shared by the waves (one 1 KiB copy per wave), the four
+//    16-byte columns of a row XOR-swizzled by (row >> 1) & 3 so that the
+//    fragment reads are free of bank conflicts; token rows past T read as
+//    zero through the descriptor's byte count;
+//  - each wave loads its own weight fragments (hi, mid, lo terms of its
+//    expert blocks; the split weights are stored one K stage per block,
+//    [d / 32][3][E][32]) from memory straight into a register ring; rows
+//    past E repeat row E - 1 (they only feed outputs that are never used).
+// Both run S - 1 stages ahead of the MFMAs, with one workgroup barrier per
+// stage.  After the last stage the logits go through an LDS tile, and wave w
+// finishes tokens 16 w .. 16 w + 15: bias, row max with the lowest index on
+// ties, sum of exp, lse, gate = 1/sum, optional logits store, the top-k
+// choices, and the workgroup's partial sums of p_te over its tokens (DPP sums
+// over the 16 tokens of a wave, then the waves in turn through LDS: a fixed
+// order).
+constexpr int RF_TOK = 64;     // tokens per workgroup (one partial row)
+constexpr int RF_KC = 32;      // K per stage (one 16x16x32 MFMA step)
 
 // routing groups reduce whole 64-token partial rows (router_reduce)
 static_assert(RF_TOK == 64, "the fused router writes one partial row per 64 tokens");
 int router_fused_blocks(int64_t T) { return (int)((T + RF_TOK - 1) / RF_TOK); }
 
-template <int EB, int R, int KMAX>
+template <int EB, int S, int KMAX>
 __global__ __launch_bounds__(256) void router_fused(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wr3,
                                                     const float* __restrict__ b_r, int T, int d, int E, int k,
                                                     float* __restrict__ logits_out, int32_t* __restrict__ expert,
                                                     float* __restrict__ gate, float* __restrict__ lse,
                                                     float* __restrict__ part) {
-    constexpr int EP = EB * 16;                 // experts padded to whole 16-row blocks
-    constexpr int PIECES = 3 * EP * 4;          // 16-byte pieces of one stage (3 terms x EP rows x 64 B)
-    constexpr int PPT = (PIECES + 255) / 256;
-    __shared__ __attribute__((aligned(16))) bf16_t wl[2][3 * EP * RF_ROW];
-    __shared__ float red[EP];
+    constexpr int EP = EB * 16;
+    constexpr int STAGE = RF_TOK * 64;          // token rows of one stage
+    constexpr int WE = EB < 4 ? EB : 4;         // waves across expert blocks
+    constexpr int WT = 4 / WE;                  // waves across the four token blocks
+    constexpr int EBW = EB / WE, TBW = 4 / WT;  // blocks per wave
+    constexpr int NWF = 3 * EBW;                // weight fragments per wave per stage
+    constexpr int PER_STAGE = 1 + NWF;          // loads per wave per stage
+    constexpr int LROW = EP + 4;                // floats per token row of the logit tile
+    constexpr int TILE = RF_TOK * LROW * 4;
+    constexpr int LDS_BYTES = S * STAGE > TILE ? S * STAGE : TILE;
+    static_assert(EB == 1 || EB == 2 || EB % 4 == 0, "expert blocks split evenly over the waves");
+    static_assert(S >= 2 && PER_STAGE * (S - 1) < 64, "outstanding loads fit the counter");
+    // one LDS object: stages (later the logit tile), then the bias and the
+    // expert sums (with a second object the compiler could no longer tell that
+    // the fragment reads need only the waited-for copies, and would wait for
+    // all of them)
+    __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES + 2 * EP * 4];
+    float* bias = (float*)(lds + LDS_BYTES);
+    float* red = bias + EP;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int r16 = lane & 15, kq = (lane >> 4) * 8;
-    const int tbase = blockIdx.x * RF_TOK + wave * 16 * RF_TB;
-    const size_t plane = (size_t)E * d;
+    const int r16 = lane & 15, g = lane >> 4;
+    const int we = wave / WT, wt = wave - we * WT;
+    const int tbase = blockIdx.x * RF_TOK;
+    const int nk = d / RF_KC;
+    // the bias is fetched now and parked in LDS after the last stage
+    const float b_mine = (b_r && (int)threadIdx.x < E) ? b_r[threadIdx.x] : 0.f;
 
-    // token fragments: block tb, token tbase + 16 tb + r16 (clamped), k offset kq
-    uint32_t xoff[RF_TB];
+    // token copy: wave w covers rows 16 w .. 16 w + 15; lane -> row 16 w + lane / 4,
+    // LDS slot lane % 4, which holds 16-byte column slot ^ ((row >> 1) & 3)
+    const int ntok = min(RF_TOK, T - tbase);
+    const bf16_t* xw = x + (size_t)tbase * d;
+    const uint32_t x_bytes = (uint32_t)ntok * d * 2;
+    const int xr = wave * 16 + (lane >> 2);
+    const uint32_t xvo = (uint32_t)(xr * d * 2 + (((lane & 3) ^ ((xr >> 1) & 3)) << 4));
+    // weight fragment (term, eb): row r16 of expert block we * EBW + eb, 16-byte group g
+    const uint32_t w_bytes = (uint32_t)3 * E * d * 2;
+    const uint32_t w_stage = (uint32_t)3 * E * 64;        // bytes of one K stage of the split weights
+    uint32_t wvo[EBW];
 #pragma unroll
-    for (int tb = 0; tb < RF_TB; ++tb) xoff[tb] = ((uint32_t)min(tbase + tb * 16 + r16, T - 1) * d + kq) * 2;
-    // W pieces: q -> (row = q/4 in [3][EP], 16-byte column q%4); rows past E repeat row E-1
-    uint32_t woff[PPT];
-    int wlds[PPT];
-#pragma unroll
-    for (int j = 0; j < PPT; ++j) {
-        const int q = min((int)threadIdx.x + j * 256, PIECES - 1);
-        const int row = q >> 2, c = q & 3;
-        const int term = row / EP, e = min(row - term * EP, E - 1);
-        woff[j] = (uint32_t)(((size_t)term * plane + (size_t)e * d + c * 8) * 2);
-        wlds[j] = row * RF_ROW + c * 8;
+    for (int eb = 0; eb < EBW; ++eb) {
+        const int e = min((we * EBW + eb) * 16 + r16, E - 1);
+        wvo[eb] = (uint32_t)(e * 64 + g * 16);
     }
-    const char* xb8 = (const char*)x;
-    const char* wb8 = (const char*)wr3;
-
-    u32x4 wreg[R][PPT];
-    u32x4 xreg[R][RF_TB];
-    f32x4 acc[RF_TB][EB];
+    u32x4 wreg[S][NWF];
+    auto issue = [&](int kk, int stg, u32x4 (&wr)[NWF]) {
+        kk = min(kk, nk - 1);
+        copy_to_lds(buffer_rsrc(xw, x_bytes), lds + stg * STAGE + wave * 1024, xvo, kk * 64);
 #pragma unroll
-    for (int tb = 0; tb < RF_TB; ++tb)
+        for (int term = 0; term < 3; ++term)
 #pragma unroll
-        for (int eb = 0; eb < EB; ++eb) acc[tb][eb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const int nk = d >> 5;
-    auto load_stage = [&](int k, u32x4 (&wr)[PPT], u32x4 (&xr)[RF_TB]) {
-        k = min(k, nk - 1);
-        const char* wk = wb8 + k * 64;
-        const char* xk = xb8 + k * 64;
-#pragma unroll
-        for (int j = 0; j < PPT; ++j) wr[j] = *(const u32x4*)(wk + woff[j]);
-#pragma unroll
-        for (int tb = 0; tb < RF_TB; ++tb) xr[tb] = *(const u32x4*)(xk + xoff[tb]);
+            for (int eb = 0; eb < EBW; ++eb)
+                wr[term * EBW + eb] = __builtin_amdgcn_raw_buffer_load_b128(
+                    buffer_rsrc(wr3, w_bytes), wvo[eb] + (uint32_t)term * E * 64, kk * w_stage, 0);
+        // loads stay in step order (the waits count whole steps): neither the
+        // optimizer nor the scheduler may move them past this point
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
     };
-#pragma unroll
-    for (int p = 0; p < R - 1; ++p) load_stage(p, wreg[p], xreg[p]);
-#pragma unroll
-    for (int j = 0; j < PPT; ++j) *(u32x4*)(&wl[0][wlds[j]]) = wreg[0][j];
 
-    for (int k0 = 0; k0 < nk; k0 += R) {
+    f32x4 acc[TBW][EBW];
 #pragma unroll
-        for (int u = 0; u < R; ++u) {
-            const int k = k0 + u;
-            if (k < nk) {
-                const int slot_n = (u + R - 1) % R;
-                load_stage(k + R - 1, wreg[slot_n], xreg[slot_n]);
-                __syncthreads();
-                const bf16_t* lb = &wl[k & 1][0];
-                bf16x8 xb[RF_TB];
+    for (int tb = 0; tb < TBW; ++tb)
 #pragma unroll
-                for (int tb = 0; tb < RF_TB; ++tb) xb[tb] = as_bf16x8(xreg[u][tb]);
-                // small terms first: lo (plane 2), mid (1), hi (0)
+        for (int eb = 0; eb < EBW; ++eb) acc[tb][eb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+    for (int p = 0; p < S - 1; ++p) issue(p, p, wreg[p]);
+    // whole rounds of S steps keep every load and the register ring
+    // unconditional (steps past nk re-read the last stage and skip the MFMAs)
+    // (d >= 32, so there is at least one round: no guard for the loads to sink past)
+    const int nk_pad = (nk + S - 1) / S * S;
+    int k0 = 0;
+    do {
+#pragma unroll
+        for (int u = 0; u < S; ++u) {
+            const int kk = k0 + u;
+            wait_copies<PER_STAGE * (S - 2)>();        // this wave's loads of step kk are done
+            lds_barrier();                             // every wave's token copy too, and step kk - 1 is read out
+            issue(kk + S - 1, (u + S - 1) % S, wreg[(u + S - 1) % S]);   // into the slots of step kk - 1
+            if (kk < nk) {
+                const char* sb = lds + u * STAGE;
+                bf16x8 xb[TBW];
+#pragma unroll
+                for (int tb = 0; tb < TBW; ++tb) {
+                    const int r = (wt * TBW + tb) * 16 + r16;
+                    xb[tb] = as_bf16x8(*(const u32x4*)(sb + r * 64 + ((g ^ ((r >> 1) & 3)) << 4)));
+                }
+                // small terms first: lo (2), mid (1), hi (0)
 #pragma unroll
                 for (int jj = 0; jj < 3; ++jj) {
                     const int term = 2 - jj;
 #pragma unroll
-                    for (int eb = 0; eb < EB; ++eb) {
-                        const bf16x8 a = as_bf16x8(*(const u32x4*)(lb + (term * EP + eb * 16 + r16) * RF_ROW + kq));
+                    for (int eb = 0; eb < EBW; ++eb) {
+                        const bf16x8 a = as_bf16x8(wreg[u][term * EBW + eb]);
 #pragma unroll
-                        for (int tb = 0; tb < RF_TB; ++tb)
+                        for (int tb = 0; tb < TBW; ++tb)
                             acc[tb][eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xb[tb], acc[tb][eb], 0, 0, 0);
                     }
                 }
-                const int slot_a = (u + 1) % R;
-                bf16_t* sb = &wl[(k + 1) & 1][0];
-#pragma unroll
-                for (int j = 0; j < PPT; ++j) *(u32x4*)(sb + wlds[j]) = wreg[slot_a][j];
             }
         }
-    }
+        k0 += S;
+    } while (k0 < nk_pad);
+    wait_copies<0>();                                  // the clamped spare loads have landed
+    lds_barrier();
+
+    // logit tile: lane holds token 16 tb' + r16 and experts 16 eb' + 4 g + i
+    float* tile = (float*)lds;
+#pragma unroll
+    for (int tb = 0; tb < TBW; ++tb)
+#pragma unroll
+        for (int eb = 0; eb < EBW; ++eb)
+            *(f32x4*)&tile[((wt * TBW + tb) * 16 + r16) * LROW + (we * EBW + eb) * 16 + 4 * g] = acc[tb][eb];
+    if ((int)threadIdx.x < EP) bias[threadIdx.x] = b_mine;
+    lds_barrier();
 
     // ------------------------------------------------------------ epilogue
-    // lane holds token r16 of block tb and experts 16 eb + 4 (lane >> 4) + i
-    float psum[EB][4];
+    // wave w, lane (r16, g): token 16 w + r16, experts 16 eb + 4 g + i
+    const int t = tbase + wave * 16 + r16;
+    const float* trow = tile + (wave * 16 + r16) * LROW;
+    float v[EB][4];
+    float zc[KMAX > 1 ? EB : 1][4];
+    float m = -INFINITY;
+    int mi = 0x7fffffff;
 #pragma unroll
-    for (int eb = 0; eb < EB; ++eb)
+    for (int eb = 0; eb < EB; ++eb) {
+        const f32x4 z4 = *(const f32x4*)&trow[eb * 16 + 4 * g];
+        const f32x4 b4 = *(const f32x4*)&bias[eb * 16 + 4 * g];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) psum[eb][i] = 0.f;
-#pragma unroll
-    for (int tb = 0; tb < RF_TB; ++tb) {
-        const int t = tbase + tb * 16 + r16;
-        float v[EB][4];
-        float zc[KMAX > 1 ? EB : 1][4];
-        float m = -INFINITY;
-        int mi = 0x7fffffff;
-#pragma unroll
-        for (int eb = 0; eb < EB; ++eb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int e = eb * 16 + (lane >> 4) * 4 + i;
-                v[eb][i] = e < E ? acc[tb][eb][i] + (b_r ? b_r[e] : 0.f) : -INFINITY;
-                if constexpr (KMAX > 1) zc[eb][i] = v[eb][i];
-                if (v[eb][i] > m) { m = v[eb][i]; mi = e; }
-            }
-        // the 4 lane groups (lane >> 4) hold the other experts of the same token
-#pragma unroll
-        for (int off = 16; off <= 32; off <<= 1) {
-            const float om = __shfl_xor(m, off);
-            const int oi = __shfl_xor(mi, off);
-            if (om > m || (om == m && oi < mi)) { m = om; mi = oi; }
+        for (int i = 0; i < 4; ++i) {
+            const int e = eb * 16 + 4 * g + i;
+            v[eb][i] = e < E ? z4[i] + b4[i] : -INFINITY;
+            if constexpr (KMAX > 1) zc[eb][i] = v[eb][i];
+            if (v[eb][i] > m) { m = v[eb][i]; mi = e; }
         }
-        float ssum = 0.f;
-#pragma unroll
-        for (int eb = 0; eb < EB; ++eb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int e = eb * 16 + (lane >> 4) * 4 + i;
-                const float z = v[eb][i];
-                v[eb][i] = e < E ? expf(z - m) : 0.f;
-                ssum += v[eb][i];
-                if (logits_out && t < T && e < E) logits_out[(size_t)t * E + e] = z;
-            }
-        ssum += __shfl_xor(ssum, 16);
-        ssum += __shfl_xor(ssum, 32);
-        const float inv = 1.0f / ssum;
-        if (t < T && lane < 16) {
-            expert[(size_t)t * k] = mi;
-            gate[(size_t)t * k] = inv;
-            lse[t] = m + logf(ssum);
-        }
-        if constexpr (KMAX > 1) {
-            // choice r: the largest logit among the experts not yet chosen
-            // (zc keeps the logits; v now holds the exponentials)
-            int ch[KMAX];
-            ch[0] = mi;
-#pragma unroll
-            for (int r = 1; r < KMAX; ++r) {
-                if (r >= k) break;
-                float mr = -INFINITY;
-                int ir = 0x7fffffff;
-#pragma unroll
-                for (int eb = 0; eb < EB; ++eb)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int e = eb * 16 + (lane >> 4) * 4 + i;
-                        bool taken = e >= E;
-#pragma unroll
-                        for (int q = 0; q < r; ++q) taken |= e == ch[q];
-                        if (!taken && zc[eb][i] > mr) { mr = zc[eb][i]; ir = e; }
-                    }
-#pragma unroll
-                for (int off = 16; off <= 32; off <<= 1) {
-                    const float om = __shfl_xor(mr, off);
-                    const int oi = __shfl_xor(ir, off);
-                    if (om > mr || (om == mr && oi < ir)) { mr = om; ir = oi; }
-                }
-                ch[r] = ir;
-                if (t < T && lane < 16) {
-                    expert[(size_t)t * k + r] = ir;
-                    gate[(size_t)t * k + r] = expf(mr - m) * inv;
-                }
-            }
-        }
-        const float w = t < T ? inv : 0.f;
-#pragma unroll
-        for (int eb = 0; eb < EB; ++eb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) psum[eb][i] += v[eb][i] * w;
     }
-    // sum over the 16 tokens of a lane group, then waves in order
+    // the 4 lane groups (g) hold the other experts of the same token
+    {
+        float om = lane_xor16(m);
+        int oi = lane_xor16(mi);
+        if (om > m || (om == m && oi < mi)) { m = om; mi = oi; }
+        om = lane_xor32(m);
+        oi = lane_xor32(mi);
+        if (om > m || (om == m && oi < mi)) { m = om; mi = oi; }
+    }
+    float ssum = 0.f;
 #pragma unroll
     for (int eb = 0; eb < EB; ++eb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            float q = psum[eb][i];
-            q += __shfl_xor(q, 1);
-            q += __shfl_xor(q, 2);
-            q += __shfl_xor(q, 4);
-            q += __shfl_xor(q, 8);
-            psum[eb][i] = q;
+            const int e = eb * 16 + 4 * g + i;
+            const float z = v[eb][i];
+            v[eb][i] = e < E ? expf(z - m) : 0.f;
+            ssum += v[eb][i];
+            if (logits_out && t < T && e < E) logits_out[(size_t)t * E + e] = z;
         }
-    for (int w = 0; w < 4; ++w) {
-        if (wave == w && r16 == 0) {
+    ssum += lane_xor16(ssum);
+    ssum += lane_xor32(ssum);
+    const float inv = 1.0f / ssum;
+    if (t < T && lane < 16) {
+        expert[(size_t)t * k] = mi;
+        gate[(size_t)t * k] = inv;
+        lse[t] = m + logf(ssum);
+    }
+    if constexpr (KMAX > 1) {
+        // choice r: the largest logit among the experts not yet chosen
+        // (zc keeps the logits; v now holds the exponentials)
+        int ch[KMAX];
+        ch[0] = mi;
+#pragma unroll
+        for (int r = 1; r < KMAX; ++r) {
+            if (r >= k) break;
+            float mr = -INFINITY;
+            int ir = 0x7fffffff;
 #pragma unroll
             for (int eb = 0; eb < EB; ++eb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int e = eb * 16 + (lane >> 4) * 4 + i;
-                    red[e] = (w == 0) ? psum[eb][i] : red[e] + psum[eb][i];
+                    const int e = eb * 16 + 4 * g + i;
+                    bool taken = e >= E;
+#pragma unroll
+                    for (int q = 0; q < r; ++q) taken |= e == ch[q];
+                    if (!taken && zc[eb][i] > mr) { mr = zc[eb][i]; ir = e; }
+                }
+            {
+                float om = lane_xor16(mr);
+                int oi = lane_xor16(ir);
+                if (om > mr || (om == mr && oi < ir)) { mr = om; ir = oi; }
+                om = lane_xor32(mr);
+                oi = lane_xor32(ir);
+                if (om > mr || (om == mr && oi < ir)) { mr = om; ir = oi; }
+            }
+            ch[r] = ir;
+            if (t < T && lane < 16) {
+                expert[(size_t)t * k + r] = ir;
+                gate[(size_t)t * k + r] = expf(mr - m) * inv;
+            }
+        }
+    }
+    // p_te summed over the 16 tokens of a lane group, then the waves in order
+    const float w = t < T ? inv : 0.f;
+    float psum[EB][4];
+#pragma unroll
+    for (int eb = 0; eb < EB; ++eb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) psum[eb][i] = row16_sum(v[eb][i] * w);
+    for (int ww = 0; ww < 4; ++ww) {
+        if (wave == ww && r16 == 0) {
+#pragma unroll
+            for (int eb = 0; eb < EB; ++eb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int e = eb * 16 + 4 * g + i;
+                    red[e] = (ww == 0) ? psum[eb][i] : red[e] + psum[eb][i];
                 }
         }
         __syncthreads();
@@ -540,15 +582,14 @@ __global__ __launch_bounds__(256) void router_fused(const bf16_t* __restrict__ x
 template <int KMAX>
 static void fused_by_width(const bf16_t* x, const bf16_t* wr3, const float* b_r, int T, int d, int E, int k,
                            float* logits_out, int32_t* expert, float* gate, float* lse, float* part, hipStream_t s) {
-    const dim3 grid(router_fused_blocks(T));
-#define SWMOE_RF(EB, R)                                                                                    \
-    hipLaunchKernelGGL((router_fused<EB, R, KMAX>), grid, dim3(256), 0, s, x, wr3, b_r, T, d, E, k, logits_out, \
-                       expert, gate, lse, part)
+#define SWMOE_RF(EB, S)                                                                                     \
+    hipLaunchKernelGGL((router_fused<EB, S, KMAX>), dim3(router_fused_blocks(T)), dim3(256), 0, s, x, wr3, b_r, T, d, \
+                       E, k, logits_out, expert, gate, lse, part)
     if (E <= 16) SWMOE_RF(1, 4);
     else if (E <= 32) SWMOE_RF(2, 4);
     else if (E <= 64) SWMOE_RF(4, 4);
-    else if (E <= 128) SWMOE_RF(8, 4);
-    else SWMOE_RF(16, 2);
+    else if (E <= 128) SWMOE_RF(8, 3);
+    else SWMOE_RF(16, 3);
 #undef SWMOE_RF
 }
 
