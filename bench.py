@@ -248,12 +248,18 @@ def main():
     accepted = t["accepted"].cpu().numpy().astype(np.int64)
     A = int(accepted.sum())
     T, d, F, E = cfg.T, cfg.d, cfg.d_ff, cfg.E
-    # algorithmic bytes and flops per launch (padding rows excluded)
+    # algorithmic bytes and flops per launch (padding rows excluded).  Without a
+    # combine launch the second GEMM wrote the kept tokens' output rows itself
+    # (residual row read, bf16 row written, slot_token and gate read) and the
+    # gather copied the dropped tokens' residual rows.
+    fused = "combine" not in kern_us
     w_bytes = 2 * E * F * d
     alg = {
         "expert_gemm1": dict(bytes=w_bytes + 2 * A * d + 2 * A * F, flops=2 * A * d * F),
-        "expert_gemm2": dict(bytes=w_bytes + 2 * A * F + 4 * A * d, flops=2 * A * d * F),
-        "gather": dict(bytes=2 * A * d + 2 * E * C * d + 9 * T + 8 * E + 4 * E * C, flops=0),
+        "expert_gemm2": dict(bytes=w_bytes + 2 * A * F + (4 * A * d + 8 * A if fused else 4 * A * d),
+                             flops=2 * A * d * F),
+        "gather": dict(bytes=2 * A * d + 2 * E * C * d + 9 * T + 8 * E + 4 * E * C + (4 * (T - A) * d if fused else 0),
+                       flops=0),
         "combine": dict(bytes=4 * A * d + 2 * T * d + 2 * T * d + 13 * T, flops=0),
         "router_gemm": dict(bytes=2 * T * d + 6 * d * E + 4 * T * E, flops=2 * T * d * E),
         "router_fused": dict(bytes=2 * T * d + 6 * d * E + 12 * T + 4 * E * ((T + 63) // 64), flops=2 * T * d * E),
@@ -305,7 +311,8 @@ def main():
             "gather_GBps": alg["gather"]["bytes"] / (kern_us["gather"] * 1e-6) / 1e9,
             "us": dispatch_us,
         },
-        "combine_GBps": alg["combine"]["bytes"] / (kern_us["combine"] * 1e-6) / 1e9,
+        "combine": ({"fused": True, "into": "expert_gemm2 epilogue"} if fused else
+                    {"fused": False, "GBps": alg["combine"]["bytes"] / (kern_us["combine"] * 1e-6) / 1e9}),
         "kernels_us": {k: round(v, 2) for k, v in sorted(kern_us.items(), key=lambda kv: -kv[1])},
         "routing": {"accepted": A, "drop_rate": 1 - A / T,
                     "empty_slot_ratio": 1 - A / (E * C) if C else None},

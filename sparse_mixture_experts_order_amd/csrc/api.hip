@@ -233,6 +233,7 @@ struct DispatchArgs {
     int32_t* position; uint8_t* keep; int32_t* counts; int32_t* accepted; int32_t* slot_token; bf16_t* buf;
     int32_t k = 1; int64_t G = 0; int32_t priority = 0;   // C is the capacity of one group
     int32_t* slot = nullptr; int32_t* rows_total = nullptr;
+    bf16_t* out_pass = nullptr; bool pass_residual = false;   // k = 1: dropped tokens' output rows (fused combine)
 };
 
 switch_status validate_dispatch(const DispatchArgs& a, const void* ws, size_t ws_bytes) {
@@ -283,7 +284,8 @@ switch_status run_dispatch(const DispatchArgs& a, void* ws, hipStream_t s) {
                                s));
     LAUNCH(K_GATHER, "gather", s,
            launch_gather(a.x, a.expert, tile_counts, group_base, one ? a.accepted : rows_total, N, a.d, a.E, a.k, G,
-                         a.priority, tile, a.C, rows, a.position, a.keep, a.slot, a.slot_token, a.buf, s));
+                         a.priority, tile, a.C, rows, a.position, a.keep, a.slot, a.slot_token, a.buf, a.out_pass,
+                         a.pass_residual, s));
     return SWITCH_OK;
 }
 
@@ -291,6 +293,7 @@ struct FfnArgs {
     const bf16_t* buf; const int32_t* accepted; const bf16_t* w1; const bf16_t* w2;
     int32_t E, C, d, d_ff; float* y;
     bf16_t* h = nullptr;   // [E, C, d_ff] hidden activations; NULL: workspace only
+    const FfnCombine* cb = nullptr;   // the combine in the second GEMM's epilogue (y optional then)
 };
 
 switch_status validate_ffn(const FfnArgs& a, const void* ws, size_t ws_bytes) {
@@ -303,7 +306,8 @@ switch_status validate_ffn(const FfnArgs& a, const void* ws, size_t ws_bytes) {
     SUPPORT((int64_t)a.d * a.d_ff * 2 < (int64_t(1) << 31), "one expert's weights must be < 2 GiB (d*d_ff*2)");
     SUPPORT((int64_t)a.C * std::max(a.d, a.d_ff) * 2 < (int64_t(1) << 31), "C*max(d,d_ff)*2 must be < 2 GiB");
     NONNULL(a.accepted); NONNULL(a.w1); NONNULL(a.w2);
-    if (a.C > 0) { NONNULL(a.buf); NONNULL(a.y); }
+    if (a.C > 0) { NONNULL(a.buf); if (!a.cb) NONNULL(a.y); }
+    REQUIRE(!a.cb || ffn_combine_fusable(a.C), "the fused combine needs more than 64 buffer rows per expert");
     ALIGNED16(a.buf); ALIGNED16(a.w1); ALIGNED16(a.w2); ALIGNED16(a.y); ALIGNED4(a.accepted); ALIGNED16(a.h);
     const size_t need = ffn_ws(a.E, a.C, a.d_ff);
     if (ws_bytes < need) return fail(SWITCH_E_WORKSPACE, "expert_ffn needs %zu workspace bytes, got %zu", need, ws_bytes);
@@ -321,7 +325,11 @@ switch_status run_ffn(const FfnArgs& a, void* ws, hipStream_t s) {
     int4* ttab = c.take<int4>(ffn_tile_table_entries(a.E, a.C));
     LAUNCH(K_FFN_TILES, "ffn_tile_prefix", s, launch_ffn_tile_prefix(a.accepted, a.E, a.C, pre, ttab, s));
     LAUNCH(K_GEMM1, "expert_gemm1", s, launch_expert_gemm1(a.buf, a.w1, pre, ttab, h, a.E, a.C, a.d, a.d_ff, s));
-    LAUNCH(K_GEMM2, "expert_gemm2", s, launch_expert_gemm2(h, a.w2, pre, ttab, a.y, a.E, a.C, a.d, a.d_ff, s));
+    if (a.cb)
+        LAUNCH(K_GEMM2, "expert_gemm2", s,
+               launch_expert_gemm2_combine(h, a.w2, pre, ttab, *a.cb, a.E, a.C, a.d, a.d_ff, s));
+    else
+        LAUNCH(K_GEMM2, "expert_gemm2", s, launch_expert_gemm2(h, a.w2, pre, ttab, a.y, a.E, a.C, a.d, a.d_ff, s));
     return SWITCH_OK;
 }
 
@@ -472,6 +480,7 @@ static size_t layer_ws(int64_t T, int32_t d, int32_t d_ff, int32_t E, int32_t C,
     n += up((size_t)ng * E * sizeof(float));         // prob_sum
     n += up((size_t)E * rows * d * sizeof(bf16_t));  // buf
     n += up((size_t)E * rows * d * sizeof(float));   // y
+    n += up((size_t)E * rows * sizeof(int32_t));     // slot_token
     if (!one_group(T, G)) {
         n += up((size_t)T * k * sizeof(int32_t));    // slot
         n += up((size_t)E * sizeof(int32_t));        // accepted rows per expert
@@ -768,6 +777,7 @@ switch_status switch_layer_fwd(const switch_layer_args* la, void* ws, size_t ws_
     float* prob_sum = c.take<float>((size_t)group_count(L.T, G) * L.E);
     bf16_t* buf = c.take<bf16_t>((size_t)L.E * rows * L.d);
     float* y = c.take<float>((size_t)L.E * rows * L.d);
+    int32_t* slot_token = c.take<int32_t>((size_t)L.E * rows);
     int32_t* slot = nullptr;
     int32_t* acc_total = nullptr;
     if (!one) {
@@ -780,6 +790,7 @@ switch_status switch_layer_fwd(const switch_layer_args* la, void* ws, size_t ws_
     if (L.prob_sum) prob_sum = L.prob_sum;
     if (L.buf) buf = L.buf;
     if (L.y) y = L.y;
+    if (L.slot_token) slot_token = L.slot_token;
     if (L.slot) slot = L.slot;
     if (L.accepted_total) acc_total = L.accepted_total;
     // one group: the buffer row is the position, and accepted is per expert
@@ -787,9 +798,19 @@ switch_status switch_layer_fwd(const switch_layer_args* la, void* ws, size_t ws_
     const int32_t* filled = one ? L.accepted : acc_total;
 
     RouteArgs ra{L.x, L.w_r, L.b_r, nullptr, L.T, L.d, L.E, logits, L.expert, L.gate, lse, prob_sum, k, G};
-    DispatchArgs da{L.x, L.expert, L.T, L.d, L.E, L.C, L.position, L.keep, L.counts, L.accepted, L.slot_token, buf,
+    DispatchArgs da{L.x, L.expert, L.T, L.d, L.E, L.C, L.position, L.keep, L.counts, L.accepted, slot_token, buf,
                     k, G, L.priority, slot, acc_total};
     FfnArgs fa{buf, filled, L.w1, L.w2, L.E, rows, L.d, L.d_ff, y, L.h};
+    // k = 1 with 128-row token tiles: the second GEMM writes the kept tokens'
+    // output rows (and y only when asked for), gather the dropped ones, and
+    // there is no combine pass
+    const bool fused = k == 1 && L.T > 0 && ffn_combine_fusable(rows);
+    const FfnCombine cb{slot_token, L.gate, L.residual ? L.x : nullptr, L.out, L.y};
+    if (fused) {
+        da.out_pass = L.out;
+        da.pass_residual = L.residual != 0;
+        fa.cb = &cb;
+    }
     CombineArgs ca{y, L.expert, rows_of, L.keep, L.gate, L.residual ? L.x : nullptr, L.T, L.d, L.E, rows, L.out, k};
     AuxArgs xa{L.counts, prob_sum, logits, lse, L.T, L.E, L.alpha, L.f, L.P, L.loss, L.dlogits, L.z_beta, L.z_loss,
                k, G};
@@ -803,7 +824,7 @@ switch_status switch_layer_fwd(const switch_layer_args* la, void* ws, size_t ws_
     CHECK(run_route(ra, route_space, s));
     CHECK(run_dispatch(da, dispatch_space, s));
     CHECK(run_ffn(fa, ffn_space, s));
-    CHECK(run_combine(ca, s));
+    if (!fused) CHECK(run_combine(ca, s));
     CHECK(run_aux(xa, s));
     return SWITCH_OK;
 }

@@ -148,6 +148,9 @@ __global__ __launch_bounds__(256) void scan_offsets(int32_t* __restrict__ tile_c
 // Workgroups [0, ntok_blocks) handle GATHER_TOK assignments each (in [T, k]
 // order); the rest zero the empty rows, GATHER_ROWS rows each.  Buffer row of a
 // kept assignment: group_base[g][e] + position (position alone with one group).
+// With out_pass (k = 1, the combine done by the second expert GEMM) a dropped
+// token's output row is written here: its residual x row bit for bit, or zeros
+// without a residual.
 constexpr int GATHER_TOK = 16, GATHER_ROWS = 16;
 
 __global__ __launch_bounds__(256) void gather(const bf16_t* __restrict__ x, const int32_t* __restrict__ expert,
@@ -157,7 +160,8 @@ __global__ __launch_bounds__(256) void gather(const bf16_t* __restrict__ x, cons
                                               int G, int rank, int tile, int C, int rows, int ntok_blocks,
                                               int32_t* __restrict__ position, uint8_t* __restrict__ keep,
                                               int32_t* __restrict__ slot, int32_t* __restrict__ slot_token,
-                                              bf16_t* __restrict__ buf) {
+                                              bf16_t* __restrict__ buf, bf16_t* __restrict__ out_pass,
+                                              int pass_residual) {
     __shared__ int s_dst[GATHER_TOK];
     __shared__ int s_tok[GATHER_TOK];
     const int vpr = d >> 3;  // 16-byte vectors per row
@@ -188,14 +192,20 @@ __global__ __launch_bounds__(256) void gather(const bf16_t* __restrict__ x, cons
                     if (slot) slot[o] = row;
                 }
             }
-            s_dst[threadIdx.x] = dst;
+            // -1: nothing to copy; -2: a dropped token whose output row is written here
+            s_dst[threadIdx.x] = (dst < 0 && o < N && out_pass) ? -2 : dst;
             s_tok[threadIdx.x] = tok;
         }
         __syncthreads();
         for (int i = threadIdx.x; i < GATHER_TOK * vpr; i += 256) {
             const int r = i / vpr, v = i - r * vpr;
             const int dst = s_dst[r];
-            if (dst < 0) continue;
+            if (dst == -1) continue;
+            if (dst == -2) {
+                const uint4 val = pass_residual ? ((const uint4*)(x + (size_t)s_tok[r] * d))[v] : make_uint4(0, 0, 0, 0);
+                ((uint4*)(out_pass + (size_t)s_tok[r] * d))[v] = val;
+                continue;
+            }
             const uint4 val = ((const uint4*)(x + (size_t)s_tok[r] * d))[v];
             ((uint4*)(buf + (size_t)dst * d))[v] = val;
         }
@@ -249,13 +259,14 @@ hipError_t launch_scan_offsets(int32_t* tile_counts, int ntiles, int tiles_per_g
 hipError_t launch_gather(const bf16_t* x, const int32_t* expert, const int32_t* offsets, const int32_t* group_base,
                          const int32_t* rows_filled, int N, int d, int E, int k, int G, int rank, int tile, int C,
                          int rows, int32_t* position, uint8_t* keep, int32_t* slot, int32_t* slot_token, bf16_t* buf,
-                         hipStream_t s) {
+                         bf16_t* out_pass, bool pass_residual, hipStream_t s) {
     const int ntok = (N + GATHER_TOK - 1) / GATHER_TOK;
     const int64_t nrows = (int64_t)E * rows;
     const int nzero = (int)((nrows + GATHER_ROWS - 1) / GATHER_ROWS);
     if (ntok + nzero == 0) return hipSuccess;
     hipLaunchKernelGGL(gather, dim3(ntok + nzero), dim3(256), 0, s, x, expert, offsets, group_base, rows_filled, N, d,
-                       E, k, std::max(G, 1), rank, tile, C, rows, ntok, position, keep, slot, slot_token, buf);
+                       E, k, std::max(G, 1), rank, tile, C, rows, ntok, position, keep, slot, slot_token, buf,
+                       k == 1 ? out_pass : nullptr, pass_residual ? 1 : 0);
     return hipGetLastError();
 }
 

@@ -97,9 +97,10 @@ __device__ __forceinline__ FfnTile decode_tile(int i, const int4* __restrict__ t
 }
 
 // Output modes: bf16(ReLU(.)) (the first expert GEMM), fp32 (the second one,
-// and the gradients that reuse this kernel), and bf16 masked by a second
-// array (the backward of the ReLU: zero wherever the saved activation is 0).
-enum FfnOut { OUT_RELU_BF16 = 0, OUT_F32 = 1, OUT_MASK_BF16 = 2 };
+// and the gradients that reuse this kernel), bf16 masked by a second array
+// (the backward of the ReLU: zero wherever the saved activation is 0), and the
+// second GEMM with the gate-scaled combine into the token rows (FfnCombine).
+enum FfnOut { OUT_RELU_BF16 = 0, OUT_F32 = 1, OUT_MASK_BF16 = 2, OUT_COMBINE = 3 };
 
 // Tile epilogue shared by the GEMM kernels.  Output rows go out through LDS in
 // passes of CPP columns: the waves owning a pass park their results (lane:
@@ -122,41 +123,151 @@ struct FfnOutShape {
 };
 
 // Tile epilogue without LDS: each lane stores its accumulator values straight
-// to memory, 4 consecutive output columns (8 bytes in bf16, 16 in fp32) of one
-// token row at a time; L2 merges the pieces into whole lines.
+// to memory; L2 merges the pieces into whole lines.  In the MFMA layout a lane
+// holds, for one token, weight rows {0-3, 8-11, 16-19, 24-27} of a 32-row block
+// (half wave 0) or {4-7, 12-15, 20-23, 28-31} (half wave 1).
+//  - fp32 output: 4 consecutive columns (16 bytes) per store.
+//  - bf16 outputs: swapping rows 8-11 of half 0 with rows 4-7 of half 1 (and
+//    24-27 with 20-23; v_permlane32_swap) gives every lane two runs of 8
+//    consecutive columns, so each store (and each residual load of the
+//    combine mode) moves 16 bytes.  In the combine mode the row goes to its
+//    token's output row (and y, if kept, gets the fp32 values).
 template <int TOKB, int NBW, int WAVES, int MODE>
 __device__ __forceinline__ void ffn_store_tile_direct(f32x16 (&acc)[NBW][TOKB], const FfnTile& t, void* out,
-                                                      const bf16_t* mask, int C, int N, int wave, int l32, int half) {
+                                                      const bf16_t* mask, const FfnCombine& cb, int C, int N,
+                                                      int wave, int l32, int half) {
     constexpr int NWG = WAVES * 32 * NBW;
+    constexpr bool RUNS = MODE == OUT_RELU_BF16 || MODE == OUT_COMBINE;
+    if constexpr (RUNS) {
+        // lanes l and l ^ 32 hold the same token, so the swap is done by whole pairs
+#pragma unroll
+        for (int tb = 0; tb < TOKB; ++tb)
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int pr = 0; pr < 2; ++pr) {
+                        const auto sw = __builtin_amdgcn_permlane32_swap(
+                            __float_as_uint(acc[nb][tb][8 * pr + i]), __float_as_uint(acc[nb][tb][8 * pr + 4 + i]),
+                            false, false);
+                        acc[nb][tb][8 * pr + i] = __uint_as_float(sw[0]);
+                        acc[nb][tb][8 * pr + 4 + i] = __uint_as_float(sw[1]);
+                    }
+    }
+    const int n0 = t.nt * NWG + wave * 32 * NBW;   // first column of this wave
+    if constexpr (MODE == OUT_COMBINE) {
+        // every load of the epilogue is issued before its first store (two
+        // round trips: the token of each row, then its gate and residual runs)
+        int tok[TOKB];
+        float g[TOKB];
+        u32x4 rr[TOKB][NBW][2];
+#pragma unroll
+        for (int tb = 0; tb < TOKB; ++tb) {
+            const int r = tb * 32 + l32;
+            tok[tb] = r < t.nv ? cb.slot_token[(size_t)t.e * C + t.tok_base + r] : -1;
+        }
+#pragma unroll
+        for (int tb = 0; tb < TOKB; ++tb) {
+            g[tb] = tok[tb] >= 0 ? cb.gate[tok[tb]] : 0.f;
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+                for (int run = 0; run < 2; ++run) {
+                    const int n = n0 + nb * 32 + run * 16 + half * 8;
+                    rr[tb][nb][run] = (tok[tb] >= 0 && cb.residual && n < N)
+                                          ? *(const u32x4*)(cb.residual + (size_t)tok[tb] * N + n)
+                                          : u32x4{0u, 0u, 0u, 0u};
+                }
+        }
+        // all the arithmetic (one wait for the loads), then all the stores
+        u32x4 ov[TOKB][NBW][2];
+#pragma unroll
+        for (int tb = 0; tb < TOKB; ++tb)
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+                for (int run = 0; run < 2; ++run) {
+                    const f32x16& a = acc[nb][tb];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t res = rr[tb][nb][run][j];
+                        const float o0 = fmaf(g[tb], a[8 * run + 2 * j], bf16_to_f32(res & 0xffffu));
+                        const float o1 = fmaf(g[tb], a[8 * run + 2 * j + 1], bf16_to_f32(res >> 16));
+                        ov[tb][nb][run][j] = bf16_rne(o0) | (bf16_rne(o1) << 16);
+                    }
+                }
+#pragma unroll
+        for (int tb = 0; tb < TOKB; ++tb) {
+            if (tok[tb] < 0) continue;
+            const size_t orow = (size_t)tok[tb] * N;
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+                for (int run = 0; run < 2; ++run) {
+                    const int n = n0 + nb * 32 + run * 16 + half * 8;
+                    if (n < N) *(u32x4*)(cb.out + orow + n) = ov[tb][nb][run];
+                }
+        }
+        if (cb.y) {   // after every residual use: stores count in the same counter as the loads
+#pragma unroll
+            for (int tb = 0; tb < TOKB; ++tb) {
+                if (tok[tb] < 0) continue;
+                const size_t row = ((size_t)t.e * C + t.tok_base + tb * 32 + l32) * N;
+#pragma unroll
+                for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+                    for (int run = 0; run < 2; ++run) {
+                        const int n = n0 + nb * 32 + run * 16 + half * 8;
+                        if (n >= N) continue;
+                        const f32x16& a = acc[nb][tb];
+                        *(f32x4*)(cb.y + row + n) = f32x4{a[8 * run + 0], a[8 * run + 1], a[8 * run + 2], a[8 * run + 3]};
+                        *(f32x4*)(cb.y + row + n + 4) =
+                            f32x4{a[8 * run + 4], a[8 * run + 5], a[8 * run + 6], a[8 * run + 7]};
+                    }
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int tb = 0; tb < TOKB; ++tb) {
         const int r = tb * 32 + l32;
         if (r >= t.nv) continue;
         const size_t row = ((size_t)t.e * C + t.tok_base + r) * N;
 #pragma unroll
-        for (int nb = 0; nb < NBW; ++nb)
+        for (int nb = 0; nb < NBW; ++nb) {
+            const f32x16& a = acc[nb][tb];
+            if constexpr (MODE == OUT_RELU_BF16) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int n = t.nt * NWG + wave * 32 * NBW + nb * 32 + q * 8 + half * 4;
-                if (n >= N) continue;
-                const f32x16& a = acc[nb][tb];
-                if constexpr (MODE == OUT_F32) {
-                    *(f32x4*)((float*)out + row + n) = f32x4{a[4 * q + 0], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
-                } else {
-                    float v0 = a[4 * q + 0], v1 = a[4 * q + 1], v2 = a[4 * q + 2], v3 = a[4 * q + 3];
-                    if constexpr (MODE == OUT_RELU_BF16) {
-                        v0 = fmaxf(v0, 0.f); v1 = fmaxf(v1, 0.f); v2 = fmaxf(v2, 0.f); v3 = fmaxf(v3, 0.f);
-                    }
-                    uint2 o = make_uint2(bf16_rne(v0) | (bf16_rne(v1) << 16), bf16_rne(v2) | (bf16_rne(v3) << 16));
-                    if constexpr (MODE == OUT_MASK_BF16) {
-                        // keep the elements whose saved activation is non-zero
+                for (int run = 0; run < 2; ++run) {
+                    const int n = n0 + nb * 32 + run * 16 + half * 8;
+                    if (n >= N) continue;
+                    float v[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) v[j] = fmaxf(a[8 * run + j], 0.f);
+                    *(u32x4*)((bf16_t*)out + row + n) =
+                        u32x4{bf16_rne(v[0]) | (bf16_rne(v[1]) << 16), bf16_rne(v[2]) | (bf16_rne(v[3]) << 16),
+                              bf16_rne(v[4]) | (bf16_rne(v[5]) << 16), bf16_rne(v[6]) | (bf16_rne(v[7]) << 16)};
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int n = n0 + nb * 32 + q * 8 + half * 4;
+                    if (n >= N) continue;
+                    if constexpr (MODE == OUT_F32) {
+                        *(f32x4*)((float*)out + row + n) =
+                            f32x4{a[4 * q + 0], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+                    } else {   // OUT_MASK_BF16: keep the elements whose saved activation is non-zero
+                        uint2 o = make_uint2(bf16_rne(a[4 * q + 0]) | (bf16_rne(a[4 * q + 1]) << 16),
+                                             bf16_rne(a[4 * q + 2]) | (bf16_rne(a[4 * q + 3]) << 16));
                         const uint2 m = *(const uint2*)(mask + row + n);
                         o.x &= ((m.x & 0x7fffu) ? 0xffffu : 0u) | ((m.x & 0x7fff0000u) ? 0xffff0000u : 0u);
                         o.y &= ((m.y & 0x7fffu) ? 0xffffu : 0u) | ((m.y & 0x7fff0000u) ? 0xffff0000u : 0u);
+                        *(uint2*)((bf16_t*)out + row + n) = o;
                     }
-                    *(uint2*)((bf16_t*)out + row + n) = o;
                 }
             }
+        }
     }
 }
 
@@ -457,40 +568,53 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm(const bf16_t* __restri
 
 // ---------------------------------------------------------------------------
 // Direct-to-LDS variant for 128-row token tiles with weights stored [N][K].
-// Both operands of a 64-wide K chunk are copied from memory straight into an
-// LDS stage by buffer loads with an LDS destination, so no registers hold data
-// in flight and the copies run S - 1 chunks ahead of the MFMAs (the register
-// rings above are limited by the register file to about three chunks).  A
-// copy instruction moves 8 rows x 128 bytes; its lanes fetch 16-byte columns
-// XOR-swizzled by the row (column c of row r lands in slot c ^ (r & 7) of the
-// 128-byte LDS row), which keeps the MFMA fragment reads free of bank
-// conflicts.  Rows past a tile's valid tokens, or past N, read as zero through
-// the descriptors' byte counts.  Each wave waits for its own copies of a chunk
-// (vmcnt) before the workgroup barrier that publishes the chunk; the LDS-only
-// barriers avoid the full memory fence, which would wait for every copy in
-// flight.  The finished stage also holds the tile's output staging.
-template <int TOKB, int NBW, int WAVES, int MODE, int PB, int S, bool DIRECT = false>
+// Both operands of a KC-wide K chunk (KC = 64 or 32) are copied from memory
+// straight into an LDS stage by buffer loads with an LDS destination, so no
+// registers hold data in flight and the copies run S - 1 chunks ahead of the
+// MFMAs (the register rings above are limited by the register file to about
+// three chunks); the narrower chunk fits more stages, i.e. more bytes in
+// flight per CU, in the same LDS.  A copy instruction moves 1 KiB: 8 rows of
+// 128 bytes or 16 rows of 64 bytes.  Its lanes fetch 16-byte columns
+// XOR-swizzled by the row (column c of row r lands in slot c ^ (r & 7) of a
+// 128-byte row, c ^ ((r >> 1) & 3) of a 64-byte row), which keeps the MFMA
+// fragment reads (32 consecutive rows at one column) free of bank conflicts.
+// Rows past a tile's valid tokens, or past N, read as zero through the
+// descriptors' byte counts.  One workgroup barrier per chunk: each wave waits
+// for its own copies of chunk p (vmcnt), the LDS-only barrier then publishes
+// every wave's copies and also certifies that all waves are done with chunk
+// p - 1, whose stage the copies of chunk p + S - 1 refill right after.  (The
+// standard barrier's memory fence would wait for every copy in flight.)  The
+// tile's output goes straight from the accumulators to memory.
+template <int KC>
+__device__ __forceinline__ int dma_slot(int r, int c) {
+    return KC == 64 ? (c ^ (r & 7)) : (c ^ ((r >> 1) & 3));
+}
+
+template <int TOKB, int NBW, int WAVES, int MODE, int S, int KC>
 __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __restrict__ A,   // [E, C, K]
                                                               const bf16_t* __restrict__ W,   // [E, N, K]
                                                               const int32_t* __restrict__ pre,
                                                               const int4* __restrict__ ttab,
                                                               void* __restrict__ out,
                                                               const bf16_t* __restrict__ mask,
+                                                              const FfnCombine cb,
                                                               int E, int C, int K, int N, int n_tiles) {
-    using Sh = FfnOutShape<TOKB, NBW, WAVES, MODE, PB>;
+    static_assert(KC == 64 || KC == 32, "64- or 32-wide K chunks");
     constexpr int TOK = 32 * TOKB;
     constexpr int NWG = WAVES * 32 * NBW;
-    constexpr int W_COPIES = NWG / 8;                       // 1 KiB copies per chunk
-    constexpr int A_COPIES = TOK / 8;
+    constexpr int RB = KC * 2;                              // bytes per staged row
+    constexpr int RPC = 1024 / RB;                          // rows per 1 KiB copy
+    constexpr int NCOL = RB / 16;                           // 16-byte columns per row
+    constexpr int W_COPIES = NWG / RPC;                     // copies per chunk
+    constexpr int A_COPIES = TOK / RPC;
     static_assert(W_COPIES % WAVES == 0, "whole weight copies per wave");
     constexpr int WPW = W_COPIES / WAVES;
     constexpr int APW = (A_COPIES + WAVES - 1) / WAVES;     // the last copies of some waves are spares
-    constexpr int W_STAGE = NWG * 128;
+    constexpr int W_STAGE = NWG * RB;
     constexpr int A_STAGE = APW * WAVES * 1024;             // token rows, then the spares' landing area
     constexpr int STAGE = W_STAGE + A_STAGE;
     constexpr int PER_CHUNK = WPW + APW;                    // copies per wave per chunk
-    static_assert(DIRECT || Sh::O_BYTES <= STAGE, "output staging fits in a stage");
-    static_assert(PER_CHUNK * (S - 1) < 64, "outstanding copies fit the counter");
+    static_assert(S >= 2 && PER_CHUNK * (S - 1) < 64, "outstanding copies fit the counter");
     __shared__ __attribute__((aligned(16))) char lds[S * STAGE];
 
     const int total = pre[E] * n_tiles;
@@ -498,25 +622,25 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
     const int slot = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3); // XCD-major
     if (slot >= total) return;
     const int ntl = (total - slot + G - 1) / G;
-    const int nk = K >> 6;
+    const int nk = K / KC;
     const int P = ntl * nk;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int half = lane >> 5, l32 = lane & 31;
 
-    // lane offsets of the copies (row 8 q + lane / 8, swizzled 16-byte column)
+    // lane offsets of the copies (row RPC q + lane / NCOL, swizzled 16-byte column)
     uint32_t wvo[WPW], avo[APW];
 #pragma unroll
     for (int i = 0; i < WPW; ++i) {
-        const int r = 8 * (wave * WPW + i) + (lane >> 3);
-        wvo[i] = (uint32_t)r * K * 2 + (((lane & 7) ^ (r & 7)) << 4);
+        const int r = RPC * (wave * WPW + i) + lane / NCOL;
+        wvo[i] = (uint32_t)r * K * 2 + (dma_slot<KC>(r, lane % NCOL) << 4);
     }
 #pragma unroll
     for (int i = 0; i < APW; ++i) {
         const int q = wave * APW + i;
-        const int r = 8 * (q < A_COPIES ? q : 0) + (lane >> 3);   // spares copy rows 0..7 again
-        avo[i] = (uint32_t)r * K * 2 + (((lane & 7) ^ (r & 7)) << 4);
+        const int r = RPC * (q < A_COPIES ? q : 0) + lane / NCOL;   // spares copy the first rows again
+        avo[i] = (uint32_t)r * K * 2 + (dma_slot<KC>(r, lane % NCOL) << 4);
     }
 
     int f_tile = -1;
@@ -546,9 +670,9 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
         const __amdgpu_buffer_rsrc_t rs_a = rsrc(a_lo, a_hi, a_n), rs_w = rsrc(w_lo, w_hi, w_n);
         char* sb = lds + stg * STAGE;
 #pragma unroll
-        for (int i = 0; i < WPW; ++i) copy_to_lds(rs_w, sb + (wave * WPW + i) * 1024, wvo[i], kf * 128);
+        for (int i = 0; i < WPW; ++i) copy_to_lds(rs_w, sb + (wave * WPW + i) * 1024, wvo[i], kf * RB);
 #pragma unroll
-        for (int i = 0; i < APW; ++i) copy_to_lds(rs_a, sb + W_STAGE + (wave * APW + i) * 1024, avo[i], kf * 128);
+        for (int i = 0; i < APW; ++i) copy_to_lds(rs_a, sb + W_STAGE + (wave * APW + i) * 1024, avo[i], kf * RB);
     };
 
     f32x16 acc[NBW][TOKB];
@@ -567,41 +691,36 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
         for (int u = 0; u < S; ++u) {
             const int p = p0 + u;
             if (p < P) {
-                issue(p + S - 1, (u + S - 1) % S);      // the stage consumed at the previous position
-                wait_copies<PER_CHUNK * (S - 1)>();      // this wave's copies of position p are in LDS
-                lds_barrier();                           // and every wave's
+                wait_copies<PER_CHUNK * (S - 2)>();      // this wave's copies of position p are in LDS
+                lds_barrier();                           // every wave's too, and position p - 1 is read out
+                issue(p + S - 1, (u + S - 1) % S);      // into the stage of position p - 1
                 const char* sw = lds + u * STAGE;
                 const char* sa = sw + W_STAGE;
+                // K permuted identically for both operands: MFMA step s takes 16-byte
+                // columns s (half 0) and KC / 32 + s (half 1) of the chunk
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const int c = half * 4 + s;          // 16-byte column of the 128-byte row
+                for (int s = 0; s < KC / 16; ++s) {
+                    const int c = half * (KC / 16) + s;
                     bf16x8 bt[TOKB];
 #pragma unroll
                     for (int tb = 0; tb < TOKB; ++tb) {
                         const int r = tb * 32 + l32;
-                        bt[tb] = as_bf16x8(*(const u32x4*)(sa + r * 128 + ((c ^ (r & 7)) << 4)));
+                        bt[tb] = as_bf16x8(*(const u32x4*)(sa + r * RB + (dma_slot<KC>(r, c) << 4)));
                     }
 #pragma unroll
                     for (int nb = 0; nb < NBW; ++nb) {
                         const int r = wave * 32 * NBW + nb * 32 + l32;
-                        const bf16x8 wa = as_bf16x8(*(const u32x4*)(sw + r * 128 + ((c ^ (r & 7)) << 4)));
+                        const bf16x8 wa = as_bf16x8(*(const u32x4*)(sw + r * RB + (dma_slot<KC>(r, c) << 4)));
 #pragma unroll
                         for (int tb = 0; tb < TOKB; ++tb)
                             acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, bt[tb], acc[nb][tb], 0, 0, 0);
                     }
                 }
-                lds_barrier();                           // stage u is free for the next copies
 
                 const int j = p / nk;
                 if (p - j * nk == nk - 1) {
                     const FfnTile t = decode_tile(j * G + slot, ttab, n_tiles);
-                    if constexpr (DIRECT) {
-                        ffn_store_tile_direct<TOKB, NBW, WAVES, MODE>(acc, t, out, mask, C, N, wave, l32, half);
-                    } else {
-                        ffn_store_tile<TOKB, NBW, WAVES, MODE, PB>(acc, lds + u * STAGE, t, out, mask, C, N, wave,
-                                                                   l32, half, [] { lds_barrier(); });
-                        lds_barrier();                   // the staging area is read out before stage u refills
-                    }
+                    ffn_store_tile_direct<TOKB, NBW, WAVES, MODE>(acc, t, out, mask, cb, C, N, wave, l32, half);
 #pragma unroll
                     for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
@@ -650,17 +769,18 @@ hipError_t launch_expert_gemm_t(const bf16_t* A, const bf16_t* W, const int32_t*
     return hipGetLastError();
 }
 
-template <int TOKB, int NBW, int WAVES, int MODE, int PB, int S, bool DIRECT = false>
+template <int TOKB, int NBW, int WAVES, int MODE, int S, int KC>
 hipError_t launch_expert_gemm_dma_t(const bf16_t* A, const bf16_t* W, const int32_t* pre, const int4* ttab, void* out,
-                                    const bf16_t* mask, int E, int C, int K, int N, hipStream_t s) {
+                                    const bf16_t* mask, const FfnCombine& cb, int E, int C, int K, int N,
+                                    hipStream_t s) {
     constexpr int NWG = WAVES * 32 * NBW;
     const int n_tiles = (N + NWG - 1) / NWG;
     const int tok_tiles = (C + 32 * TOKB - 1) / (32 * TOKB);
     const int64_t max_tiles = (int64_t)E * n_tiles * tok_tiles;
     int64_t grid = std::min<int64_t>((int64_t)device_cus(), (max_tiles + 7) / 8 * 8);   // one workgroup per CU
     grid = std::max<int64_t>(8, grid / 8 * 8);
-    hipLaunchKernelGGL((expert_gemm_dma<TOKB, NBW, WAVES, MODE, PB, S, DIRECT>), dim3((unsigned)grid), dim3(64 * WAVES), 0,
-                       s, A, W, pre, ttab, out, mask, E, C, K, N, n_tiles);
+    hipLaunchKernelGGL((expert_gemm_dma<TOKB, NBW, WAVES, MODE, S, KC>), dim3((unsigned)grid), dim3(64 * WAVES), 0, s, A,
+                       W, pre, ttab, out, mask, cb, E, C, K, N, n_tiles);
     return hipGetLastError();
 }
 
@@ -684,12 +804,14 @@ hipError_t launch_ffn_tile_prefix(const int32_t* accepted, int E, int C, int32_t
 // the wider one on a tie (fewer, longer weight streams per workgroup); every
 // expert's token tiles count as full.  E.g. at 128 experts, N = 768 takes 384
 // columns (two tiles per expert, one round); N = 3072 and N = 4096 take 512.
-static int dma_tile_width(int E, int C, int N) {
+// `narrow` restricts the choice to one 32-row block per wave (256 or 192).
+static int dma_tile_width(int E, int C, int N, bool narrow = false) {
     const int64_t tok_tiles = (int64_t)E * ((C + 127) / 128);
     const int64_t grid = device_cus();
     int best = 0;
     int64_t best_cost = 0;
     for (const int nwg : {512, 384, 256, 192}) {
+        if (narrow && nwg > 256) continue;
         const int64_t tiles = tok_tiles * ((N + nwg - 1) / nwg);
         const int64_t cost = (tiles + grid - 1) / grid * nwg;
         if (best == 0 || cost < best_cost) { best = nwg; best_cost = cost; }
@@ -699,22 +821,35 @@ static int dma_tile_width(int E, int C, int N) {
 
 template <int MODE>
 static hipError_t launch_expert_gemm(const bf16_t* A, const bf16_t* W, const int32_t* pre, const int4* ttab, void* out,
-                                     const bf16_t* mask, int E, int C, int K, int N, hipStream_t s) {
+                                     const bf16_t* mask, int E, int C, int K, int N, hipStream_t s,
+                                     const FfnCombine& cb = FfnCombine{}) {
     // the token tile must be ffn_token_tile(C) rows: the prefix kernel lists tiles of that size
-    if (C > 64) {
-        switch (dma_tile_width(E, C, N)) {
-            case 512:
-                return launch_expert_gemm_dma_t<4, 2, 8, MODE, 256, 2, true>(A, W, pre, ttab, out, mask, E, C, K, N, s);
-            case 384:
-                return launch_expert_gemm_dma_t<4, 2, 6, MODE, 256, 2, true>(A, W, pre, ttab, out, mask, E, C, K, N, s);
-            case 256:
-                return launch_expert_gemm_dma_t<4, 1, 8, MODE, 256, 2, true>(A, W, pre, ttab, out, mask, E, C, K, N, s);
-            default:
-                return launch_expert_gemm_dma_t<4, 1, 6, MODE, 256, 3, true>(A, W, pre, ttab, out, mask, E, C, K, N, s);
+    if constexpr (MODE == OUT_COMBINE) {
+        // one 32-row block per wave: the epilogue's residual runs fit in registers
+        if (C <= 64) return hipErrorInvalidValue;   // the fused combine needs 128-row token tiles
+        if (dma_tile_width(E, C, N, true) == 256)
+            return launch_expert_gemm_dma_t<4, 1, 8, MODE, 3, 64>(A, W, pre, ttab, out, mask, cb, E, C, K, N, s);
+        return launch_expert_gemm_dma_t<4, 1, 6, MODE, 3, 64>(A, W, pre, ttab, out, mask, cb, E, C, K, N, s);
+    } else {
+        if (C > 64) {
+            switch (dma_tile_width(E, C, N)) {
+                case 512:
+                    return launch_expert_gemm_dma_t<4, 2, 8, MODE, 2, 64>(A, W, pre, ttab, out, mask, cb, E, C, K, N,
+                                                                          s);
+                case 384:
+                    return launch_expert_gemm_dma_t<4, 2, 6, MODE, 2, 64>(A, W, pre, ttab, out, mask, cb, E, C, K, N,
+                                                                          s);
+                case 256:
+                    return launch_expert_gemm_dma_t<4, 1, 8, MODE, 3, 64>(A, W, pre, ttab, out, mask, cb, E, C, K, N,
+                                                                          s);
+                default:
+                    return launch_expert_gemm_dma_t<4, 1, 6, MODE, 3, 64>(A, W, pre, ttab, out, mask, cb, E, C, K, N,
+                                                                          s);
+            }
         }
+        if (C > 32) return launch_expert_gemm_t<2, 2, 4, 3, MODE, 512>(A, W, pre, ttab, out, mask, E, C, K, N, s);
+        return launch_expert_gemm_t<1, 2, 4, 4, MODE, 512>(A, W, pre, ttab, out, mask, E, C, K, N, s);
     }
-    if (C > 32) return launch_expert_gemm_t<2, 2, 4, 3, MODE, 512>(A, W, pre, ttab, out, mask, E, C, K, N, s);
-    return launch_expert_gemm_t<1, 2, 4, 4, MODE, 512>(A, W, pre, ttab, out, mask, E, C, K, N, s);
 }
 
 // Register kernel with 128-row token tiles: 192 columns (6 waves) when that
@@ -751,6 +886,14 @@ hipError_t launch_expert_gemm1(const bf16_t* buf, const bf16_t* w1, const int32_
 hipError_t launch_expert_gemm2(const bf16_t* h, const bf16_t* w2, const int32_t* pre, const int4* ttab, float* y,
                                int E, int C, int d, int d_ff, hipStream_t s) {
     return launch_expert_gemm<OUT_F32>(h, w2, pre, ttab, y, nullptr, E, C, d_ff, d, s);
+}
+
+bool ffn_combine_fusable(int C) { return C > 64; }
+
+hipError_t launch_expert_gemm2_combine(const bf16_t* h, const bf16_t* w2, const int32_t* pre, const int4* ttab,
+                                       const FfnCombine& cb, int E, int C, int d, int d_ff, hipStream_t s) {
+    if (!ffn_combine_fusable(C)) return hipErrorInvalidValue;
+    return launch_expert_gemm<OUT_COMBINE>(h, w2, pre, ttab, nullptr, nullptr, E, C, d_ff, d, s, cb);
 }
 
 hipError_t launch_grouped_gemm_kmajor_f32(const bf16_t* A, const bf16_t* W, const int32_t* pre, const int4* ttab,

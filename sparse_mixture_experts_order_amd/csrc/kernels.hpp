@@ -39,7 +39,7 @@ hipError_t launch_scan_offsets(int32_t* tile_counts, int ntiles, int tiles_per_g
 hipError_t launch_gather(const bf16_t* x, const int32_t* expert, const int32_t* offsets, const int32_t* group_base,
                          const int32_t* rows_filled, int N, int d, int E, int k, int G, int rank, int tile, int C,
                          int rows, int32_t* position, uint8_t* keep, int32_t* slot, int32_t* slot_token, bf16_t* buf,
-                         hipStream_t s);
+                         bf16_t* out_pass, bool pass_residual, hipStream_t s);
 
 // expert_ffn.hip
 int ffn_token_tile(int C);
@@ -49,6 +49,21 @@ hipError_t launch_expert_gemm1(const bf16_t* buf, const bf16_t* w1, const int32_
                                int E, int C, int d, int d_ff, hipStream_t s);
 hipError_t launch_expert_gemm2(const bf16_t* h, const bf16_t* w2, const int32_t* pre, const int4* ttab, float* y,
                                int E, int C, int d, int d_ff, hipStream_t s);
+// The second expert GEMM with the combine (k = 1) in its epilogue: buffer row
+// s of expert e holds token slot_token[e * C + s], and
+//   out[token] = bf16(residual[token] + gate[token] * y[e, s])
+// (fp32, one rounding; no residual when it is NULL), plus y itself when y is
+// not NULL.  Only for 128-row token tiles (ffn_combine_fusable).
+struct FfnCombine {
+    const int32_t* slot_token;
+    const float* gate;
+    const bf16_t* residual;
+    bf16_t* out;
+    float* y;
+};
+bool ffn_combine_fusable(int C);
+hipError_t launch_expert_gemm2_combine(const bf16_t* h, const bf16_t* w2, const int32_t* pre, const int4* ttab,
+                                       const FfnCombine& cb, int E, int C, int d, int d_ff, hipStream_t s);
 // the same kernel on other operands: out[e, r, n] = sum_k A[e, r, k] W[e, n, k]
 // for the rows listed in (pre, ttab), fp32 out
 hipError_t launch_grouped_gemm_f32(const bf16_t* A, const bf16_t* W, const int32_t* pre, const int4* ttab, float* out,
