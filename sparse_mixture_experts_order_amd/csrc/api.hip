@@ -166,6 +166,9 @@ struct RouteArgs {
     int64_t T; int32_t d, E;
     float* logits_out; int32_t* expert; float* gate; float* lse; float* prob_sum;
     int32_t k = 1; int64_t G = 0;   // choices per token; tokens per routing group (0: one group)
+    // the layer forward: when the partial probability rows are few, leave their
+    // sum to the aux kernel (part_out / part_rows_out receive them; prob_sum unset)
+    bool defer_reduce = false; const float** part_out = nullptr; int* part_rows_out = nullptr;
 };
 
 switch_status validate_route(const RouteArgs& a, const void* ws, size_t ws_bytes) {
@@ -192,6 +195,17 @@ switch_status validate_route(const RouteArgs& a, const void* ws, size_t ws_bytes
     return SWITCH_OK;
 }
 
+// Sum the partial rows into prob_sum, or hand them to the aux step.
+switch_status finish_route(const RouteArgs& a, const float* part, int rows, int ng, hipStream_t s) {
+    if (a.defer_reduce && (int64_t)rows * ng * a.E <= kAuxPartsMax) {
+        *a.part_out = part;
+        *a.part_rows_out = rows;
+        return SWITCH_OK;
+    }
+    LAUNCH(K_RREDUCE, "router_reduce", s, launch_router_reduce(part, rows, ng, a.E, a.prob_sum, s));
+    return SWITCH_OK;
+}
+
 switch_status run_route(const RouteArgs& a, void* ws, hipStream_t s) {
     const int T = (int)a.T, E = a.E;
     // with routing groups the partial rows cover 64 tokens each and are summed per group
@@ -210,9 +224,7 @@ switch_status run_route(const RouteArgs& a, void* ws, hipStream_t s) {
                 LAUNCH(K_RFUSED, "router_fused", s,
                        launch_router_fused(a.x, wr3, a.b_r, T, a.d, E, a.k, a.logits_out, a.expert, a.gate, a.lse,
                                            part, s));
-            LAUNCH(K_RREDUCE, "router_reduce", s,
-                   launch_router_reduce(part, one ? nblk : rows_per_group, ng, E, a.prob_sum, s));
-            return SWITCH_OK;
+            return finish_route(a, part, one ? nblk : rows_per_group, ng, s);
         }
         float* z = a.logits_out ? a.logits_out : c.take<float>((size_t)T * E);
         if (T > 0) LAUNCH(K_RGEMM, "router_gemm", s, launch_router_gemm(a.x, wr3, a.b_r, z, T, a.d, E, s));
@@ -223,9 +235,7 @@ switch_status run_route(const RouteArgs& a, void* ws, hipStream_t s) {
     if (T > 0)
         LAUNCH(K_RSOFTMAX, "router_softmax", s,
                launch_router_softmax(logits, T, E, a.k, !one, a.expert, a.gate, a.lse, part, s));
-    LAUNCH(K_RREDUCE, "router_reduce", s,
-           launch_router_reduce(part, one ? nblk : rows_per_group, ng, E, a.prob_sum, s));
-    return SWITCH_OK;
+    return finish_route(a, part, one ? nblk : rows_per_group, ng, s);
 }
 
 struct DispatchArgs {
@@ -367,6 +377,8 @@ struct AuxArgs {
     int64_t T; int32_t E; float alpha; float* f; float* P; float* loss; float* dlogits;
     float beta; float* z_loss;   // router z-loss (optional, z_loss == NULL: not computed)
     int32_t k = 1; int64_t G = 0;   // counts, prob_sum, f, P are [groups, E]
+    // prob_sum still to be summed from the router's partial rows (rows per group)
+    const float* parts = nullptr; int parts_rows = 0; float* prob_sum_out = nullptr;
 };
 
 switch_status validate_aux(const AuxArgs& a) {
@@ -387,9 +399,14 @@ switch_status validate_aux(const AuxArgs& a) {
 
 switch_status run_aux(const AuxArgs& a, hipStream_t s) {
     const int64_t Gt = group_tokens(a.T, a.G);
-    LAUNCH(K_AUX_STATS, "aux_stats", s,
-           launch_aux_stats(a.counts, a.prob_sum, Gt, (int)group_count(a.T, a.G), a.E, a.k, a.alpha, a.f, a.P,
-                            a.loss, s));
+    if (a.parts)
+        LAUNCH(K_AUX_STATS, "aux_stats", s,
+               launch_aux_stats_parts(a.parts, a.parts_rows, (int)group_count(a.T, a.G), a.E, a.counts, Gt, a.k,
+                                      a.alpha, a.prob_sum_out, a.f, a.P, a.loss, s));
+    else
+        LAUNCH(K_AUX_STATS, "aux_stats", s,
+               launch_aux_stats(a.counts, a.prob_sum, Gt, (int)group_count(a.T, a.G), a.E, a.k, a.alpha, a.f, a.P,
+                                a.loss, s));
     if (a.z_loss) LAUNCH(K_Z_LOSS, "z_loss", s, launch_z_loss(a.lse, a.T, a.beta, a.z_loss, s));
     if (a.dlogits && a.T > 0)
         LAUNCH(K_AUX_GRAD, "aux_grad", s,
@@ -798,6 +815,11 @@ switch_status switch_layer_fwd(const switch_layer_args* la, void* ws, size_t ws_
     const int32_t* filled = one ? L.accepted : acc_total;
 
     RouteArgs ra{L.x, L.w_r, L.b_r, nullptr, L.T, L.d, L.E, logits, L.expert, L.gate, lse, prob_sum, k, G};
+    const float* parts = nullptr;   // partial probability rows left to the aux step
+    int parts_rows = 0;
+    ra.defer_reduce = true;
+    ra.part_out = &parts;
+    ra.part_rows_out = &parts_rows;
     DispatchArgs da{L.x, L.expert, L.T, L.d, L.E, L.C, L.position, L.keep, L.counts, L.accepted, slot_token, buf,
                     k, G, L.priority, slot, acc_total};
     FfnArgs fa{buf, filled, L.w1, L.w2, L.E, rows, L.d, L.d_ff, y, L.h};
@@ -822,6 +844,11 @@ switch_status switch_layer_fwd(const switch_layer_args* la, void* ws, size_t ws_
     CHECK(validate_combine(ca));
     CHECK(validate_aux(xa));
     CHECK(run_route(ra, route_space, s));
+    if (parts) {
+        xa.parts = parts;
+        xa.parts_rows = parts_rows;
+        xa.prob_sum_out = prob_sum;
+    }
     CHECK(run_dispatch(da, dispatch_space, s));
     CHECK(run_ffn(fa, ffn_space, s));
     if (!fused) CHECK(run_combine(ca, s));

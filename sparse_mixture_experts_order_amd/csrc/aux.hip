@@ -39,6 +39,70 @@ __global__ __launch_bounds__(1024) void aux_stats(const int32_t* __restrict__ co
     if (threadIdx.x == 0) loss[0] = ngroups > 0 ? (float)((double)alpha * (double)E * red[0] / (double)ngroups) : 0.f;
 }
 
+// The same with prob_sum taken from the router's partial rows (the layer
+// forward, when they are few): group g's column e is the sum of rows
+// [g rows, (g + 1) rows) of part[., E].  tpc threads share a column, each
+// summing every tpc-th row in row order (fp64; neighbouring lanes read
+// neighbouring columns of a row); the column's tpc sums are then added in
+// thread order.  prob_sum, f, P and the loss follow as in aux_stats.
+__global__ __launch_bounds__(1024) void aux_stats_parts(const float* __restrict__ part, int rows, int ngroups, int E,
+                                                        const int32_t* __restrict__ counts, int64_t G, int k,
+                                                        float alpha, float* __restrict__ prob_sum,
+                                                        float* __restrict__ f, float* __restrict__ P,
+                                                        float* __restrict__ loss) {
+    __shared__ double red[1024];
+    const int n = ngroups * E;
+    const int tpc = n >= 1024 ? 1 : min(16, 1024 / n);
+    const int cols = 1024 / tpc;                    // columns per pass; neighbouring lanes take neighbouring columns
+    const int j = (int)threadIdx.x / cols, cl = (int)threadIdx.x - j * cols;
+    double acc = 0.0;
+    for (int c0 = 0; c0 < n; c0 += cols) {
+        const int c = c0 + cl;
+        double sum = 0.0;
+        if (c < n) {
+            const int g = c / E, e = c - g * E;
+            const float* col = part + (size_t)g * rows * E + e;
+            int r = j;
+            for (; r + 31 * tpc < rows; r += 32 * tpc) {   // 32 loads in flight, added in row order
+                float v[32];
+#pragma unroll
+                for (int q = 0; q < 32; ++q) v[q] = col[(size_t)(r + q * tpc) * E];
+#pragma unroll
+                for (int q = 0; q < 32; ++q) sum += (double)v[q];
+            }
+            for (; r + 7 * tpc < rows; r += 8 * tpc) {
+                float v[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) v[q] = col[(size_t)(r + q * tpc) * E];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) sum += (double)v[q];
+            }
+            for (; r < rows; r += tpc) sum += (double)col[(size_t)r * E];
+        }
+        red[threadIdx.x] = sum;
+        __syncthreads();
+        if (j == 0 && c < n) {
+            double t = 0.0;
+            for (int q = 0; q < tpc; ++q) t += red[q * cols + cl];
+            const float ps = (float)t;
+            prob_sum[c] = ps;
+            const double fe = G > 0 ? (double)counts[c] / ((double)k * (double)G) : 0.0;
+            const double pe = G > 0 ? (double)ps / (double)G : 0.0;
+            f[c] = (float)fe;
+            P[c] = (float)pe;
+            acc += fe * pe;
+        }
+        __syncthreads();
+    }
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    for (int st = 512; st > 0; st >>= 1) {
+        if ((int)threadIdx.x < st) red[threadIdx.x] += red[threadIdx.x + st];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) loss[0] = ngroups > 0 ? (float)((double)alpha * (double)E * red[0] / (double)ngroups) : 0.f;
+}
+
 // Router z-loss (ST-MoE, as restated in "MoE routing load collapse",
 // zffjzz.top, "core idea and formulas"): L_z = beta (1/T) sum_t lse_t^2.
 // One workgroup, fp64, fixed tree order.
@@ -108,6 +172,14 @@ __global__ __launch_bounds__(256) void aux_grad(const float* __restrict__ logits
 hipError_t launch_aux_stats(const int32_t* counts, const float* prob_sum, int64_t G, int ngroups, int E, int k,
                             float alpha, float* f, float* P, float* loss, hipStream_t s) {
     hipLaunchKernelGGL(aux_stats, dim3(1), dim3(1024), 0, s, counts, prob_sum, G, ngroups, E, k, alpha, f, P, loss);
+    return hipGetLastError();
+}
+
+hipError_t launch_aux_stats_parts(const float* part, int rows, int ngroups, int E, const int32_t* counts, int64_t G,
+                                  int k, float alpha, float* prob_sum, float* f, float* P, float* loss,
+                                  hipStream_t s) {
+    hipLaunchKernelGGL(aux_stats_parts, dim3(1), dim3(1024), 0, s, part, rows, ngroups, E, counts, G, k, alpha,
+                       prob_sum, f, P, loss);
     return hipGetLastError();
 }
 

@@ -83,6 +83,11 @@ hipError_t launch_combine(const float* y, const int32_t* expert, const int32_t* 
 // aux.hip
 hipError_t launch_aux_stats(const int32_t* counts, const float* prob_sum, int64_t G, int ngroups, int E, int k,
                             float alpha, float* f, float* P, float* loss, hipStream_t s);
+// aux_stats with prob_sum summed from the router's partial rows [ngroups * rows, E]
+constexpr int64_t kAuxPartsMax = 262144;   // partial values one workgroup sums
+hipError_t launch_aux_stats_parts(const float* part, int rows, int ngroups, int E, const int32_t* counts, int64_t G,
+                                  int k, float alpha, float* prob_sum, float* f, float* P, float* loss,
+                                  hipStream_t s);
 hipError_t launch_z_loss(const float* lse, int64_t T, float beta, float* z_loss, hipStream_t s);
 hipError_t launch_aux_grad(const float* logits, const float* lse, const float* f, int64_t T, int64_t G, int E,
                            float alpha, float beta, const int32_t* expert, const float* gate, const float* dgate,
