@@ -244,6 +244,7 @@ struct DispatchArgs {
     int32_t k = 1; int64_t G = 0; int32_t priority = 0;   // C is the capacity of one group
     int32_t* slot = nullptr; int32_t* rows_total = nullptr;
     bf16_t* out_pass = nullptr; bool pass_residual = false;   // k = 1: dropped tokens' output rows (fused combine)
+    bool no_buf = false;   // the first expert GEMM gathers the token rows itself: buf is not written
 };
 
 switch_status validate_dispatch(const DispatchArgs& a, const void* ws, size_t ws_bytes) {
@@ -259,7 +260,7 @@ switch_status validate_dispatch(const DispatchArgs& a, const void* ws, size_t ws
     const bool tok = a.T > 0;
     NONNULL_IF(tok, a.x); NONNULL_IF(tok, a.expert); NONNULL_IF(tok, a.position); NONNULL_IF(tok, a.keep);
     NONNULL_IF(grouped, a.counts); NONNULL_IF(grouped, a.accepted);
-    NONNULL_IF(rows > 0, a.buf);
+    NONNULL_IF(rows > 0 && !a.no_buf, a.buf);
     ALIGNED16(a.x); ALIGNED16(a.buf); ALIGNED4(a.expert); ALIGNED4(a.position); ALIGNED4(a.counts);
     ALIGNED4(a.accepted); ALIGNED4(a.slot_token); ALIGNED4(a.slot); ALIGNED4(a.rows_total);
     const size_t need = dispatch_ws(a.T, a.E, a.k, a.G);
@@ -294,8 +295,8 @@ switch_status run_dispatch(const DispatchArgs& a, void* ws, hipStream_t s) {
                                s));
     LAUNCH(K_GATHER, "gather", s,
            launch_gather(a.x, a.expert, tile_counts, group_base, one ? a.accepted : rows_total, N, a.d, a.E, a.k, G,
-                         a.priority, tile, a.C, rows, a.position, a.keep, a.slot, a.slot_token, a.buf, a.out_pass,
-                         a.pass_residual, s));
+                         a.priority, tile, a.C, rows, a.position, a.keep, a.slot, a.slot_token,
+                         a.no_buf ? nullptr : a.buf, a.out_pass, a.pass_residual, s));
     return SWITCH_OK;
 }
 
@@ -304,6 +305,8 @@ struct FfnArgs {
     int32_t E, C, d, d_ff; float* y;
     bf16_t* h = nullptr;   // [E, C, d_ff] hidden activations; NULL: workspace only
     const FfnCombine* cb = nullptr;   // the combine in the second GEMM's epilogue (y optional then)
+    // token rows gathered by the first GEMM from x [x_tokens, d] through a_rows (= slot_token); buf unused
+    const bf16_t* x_src = nullptr; int64_t x_tokens = 0; const int32_t* a_rows = nullptr;
 };
 
 switch_status validate_ffn(const FfnArgs& a, const void* ws, size_t ws_bytes) {
@@ -316,8 +319,12 @@ switch_status validate_ffn(const FfnArgs& a, const void* ws, size_t ws_bytes) {
     SUPPORT((int64_t)a.d * a.d_ff * 2 < (int64_t(1) << 31), "one expert's weights must be < 2 GiB (d*d_ff*2)");
     SUPPORT((int64_t)a.C * std::max(a.d, a.d_ff) * 2 < (int64_t(1) << 31), "C*max(d,d_ff)*2 must be < 2 GiB");
     NONNULL(a.accepted); NONNULL(a.w1); NONNULL(a.w2);
-    if (a.C > 0) { NONNULL(a.buf); if (!a.cb) NONNULL(a.y); }
-    REQUIRE(!a.cb || ffn_combine_fusable(a.C), "the fused combine needs more than 64 buffer rows per expert");
+    if (a.C > 0) {
+        if (a.a_rows) NONNULL(a.x_src); else NONNULL(a.buf);
+        if (!a.cb) NONNULL(a.y);
+    }
+    REQUIRE(!a.a_rows || ffn_wide_tiles(a.C), "gathered token rows need more than 64 buffer rows per expert");
+    REQUIRE(!a.cb || ffn_wide_tiles(a.C), "the fused combine needs more than 64 buffer rows per expert");
     ALIGNED16(a.buf); ALIGNED16(a.w1); ALIGNED16(a.w2); ALIGNED16(a.y); ALIGNED4(a.accepted); ALIGNED16(a.h);
     const size_t need = ffn_ws(a.E, a.C, a.d_ff);
     if (ws_bytes < need) return fail(SWITCH_E_WORKSPACE, "expert_ffn needs %zu workspace bytes, got %zu", need, ws_bytes);
@@ -334,7 +341,12 @@ switch_status run_ffn(const FfnArgs& a, void* ws, hipStream_t s) {
     int32_t* pre = c.take<int32_t>((size_t)a.E + 1);
     int4* ttab = c.take<int4>(ffn_tile_table_entries(a.E, a.C));
     LAUNCH(K_FFN_TILES, "ffn_tile_prefix", s, launch_ffn_tile_prefix(a.accepted, a.E, a.C, pre, ttab, s));
-    LAUNCH(K_GEMM1, "expert_gemm1", s, launch_expert_gemm1(a.buf, a.w1, pre, ttab, h, a.E, a.C, a.d, a.d_ff, s));
+    if (a.a_rows)
+        LAUNCH(K_GEMM1, "expert_gemm1", s,
+               launch_expert_gemm1_gather(a.x_src, a.x_tokens, a.a_rows, a.w1, pre, ttab, h, a.E, a.C, a.d, a.d_ff,
+                                          s));
+    else
+        LAUNCH(K_GEMM1, "expert_gemm1", s, launch_expert_gemm1(a.buf, a.w1, pre, ttab, h, a.E, a.C, a.d, a.d_ff, s));
     if (a.cb)
         LAUNCH(K_GEMM2, "expert_gemm2", s,
                launch_expert_gemm2_combine(h, a.w2, pre, ttab, *a.cb, a.E, a.C, a.d, a.d_ff, s));
@@ -497,7 +509,7 @@ static size_t layer_ws(int64_t T, int32_t d, int32_t d_ff, int32_t E, int32_t C,
     n += up((size_t)ng * E * sizeof(float));         // prob_sum
     n += up((size_t)E * rows * d * sizeof(bf16_t));  // buf
     n += up((size_t)E * rows * d * sizeof(float));   // y
-    n += up((size_t)E * rows * sizeof(int32_t));     // slot_token
+    n += up(((size_t)E * rows + kRowMapPad) * sizeof(int32_t));   // slot_token (padded for the gathering GEMM)
     if (!one_group(T, G)) {
         n += up((size_t)T * k * sizeof(int32_t));    // slot
         n += up((size_t)E * sizeof(int32_t));        // accepted rows per expert
@@ -794,7 +806,7 @@ switch_status switch_layer_fwd(const switch_layer_args* la, void* ws, size_t ws_
     float* prob_sum = c.take<float>((size_t)group_count(L.T, G) * L.E);
     bf16_t* buf = c.take<bf16_t>((size_t)L.E * rows * L.d);
     float* y = c.take<float>((size_t)L.E * rows * L.d);
-    int32_t* slot_token = c.take<int32_t>((size_t)L.E * rows);
+    int32_t* slot_token = c.take<int32_t>((size_t)L.E * rows + kRowMapPad);
     int32_t* slot = nullptr;
     int32_t* acc_total = nullptr;
     if (!one) {
@@ -826,12 +838,20 @@ switch_status switch_layer_fwd(const switch_layer_args* la, void* ws, size_t ws_
     // k = 1 with 128-row token tiles: the second GEMM writes the kept tokens'
     // output rows (and y only when asked for), gather the dropped ones, and
     // there is no combine pass
-    const bool fused = k == 1 && L.T > 0 && ffn_combine_fusable(rows);
+    const bool fused = k == 1 && L.T > 0 && ffn_wide_tiles(rows);
     const FfnCombine cb{slot_token, L.gate, L.residual ? L.x : nullptr, L.out, L.y};
     if (fused) {
         da.out_pass = L.out;
         da.pass_residual = L.residual != 0;
         fa.cb = &cb;
+    }
+    // buf and slot_token not kept: the first GEMM reads the token rows from x
+    // through the (padded) workspace slot_token
+    if (!L.buf && !L.slot_token && L.T > 0 && ffn_wide_tiles(rows) && L.T * L.d * 2 + 2 * (int64_t)L.d + 256 < (int64_t(1) << 32)) {
+        da.no_buf = true;
+        fa.x_src = L.x;
+        fa.x_tokens = L.T;
+        fa.a_rows = slot_token;
     }
     CombineArgs ca{y, L.expert, rows_of, L.keep, L.gate, L.residual ? L.x : nullptr, L.T, L.d, L.E, rows, L.out, k};
     AuxArgs xa{L.counts, prob_sum, logits, lse, L.T, L.E, L.alpha, L.f, L.P, L.loss, L.dlogits, L.z_beta, L.z_loss,

@@ -150,7 +150,8 @@ __global__ __launch_bounds__(256) void scan_offsets(int32_t* __restrict__ tile_c
 // kept assignment: group_base[g][e] + position (position alone with one group).
 // With out_pass (k = 1, the combine done by the second expert GEMM) a dropped
 // token's output row is written here: its residual x row bit for bit, or zeros
-// without a residual.
+// without a residual.  With buf == NULL (the first expert GEMM gathers the
+// token rows from x itself) no rows are copied or zeroed.
 constexpr int GATHER_TOK = 16, GATHER_ROWS = 16;
 
 __global__ __launch_bounds__(256) void gather(const bf16_t* __restrict__ x, const int32_t* __restrict__ expert,
@@ -201,6 +202,7 @@ __global__ __launch_bounds__(256) void gather(const bf16_t* __restrict__ x, cons
             const int r = i / vpr, v = i - r * vpr;
             const int dst = s_dst[r];
             if (dst == -1) continue;
+            if (dst >= 0 && !buf) continue;
             if (dst == -2) {
                 const uint4 val = pass_residual ? ((const uint4*)(x + (size_t)s_tok[r] * d))[v] : make_uint4(0, 0, 0, 0);
                 ((uint4*)(out_pass + (size_t)s_tok[r] * d))[v] = val;
@@ -261,7 +263,7 @@ hipError_t launch_gather(const bf16_t* x, const int32_t* expert, const int32_t* 
                          int rows, int32_t* position, uint8_t* keep, int32_t* slot, int32_t* slot_token, bf16_t* buf,
                          bf16_t* out_pass, bool pass_residual, hipStream_t s) {
     const int ntok = (N + GATHER_TOK - 1) / GATHER_TOK;
-    const int64_t nrows = (int64_t)E * rows;
+    const int64_t nrows = buf ? (int64_t)E * rows : 0;
     const int nzero = (int)((nrows + GATHER_ROWS - 1) / GATHER_ROWS);
     if (ntok + nzero == 0) return hipSuccess;
     hipLaunchKernelGGL(gather, dim3(ntok + nzero), dim3(256), 0, s, x, expert, offsets, group_base, rows_filled, N, d,

@@ -590,14 +590,20 @@ __device__ __forceinline__ int dma_slot(int r, int c) {
     return KC == 64 ? (c ^ (r & 7)) : (c ^ ((r >> 1) & 3));
 }
 
+// With a_rows the token rows are gathered straight from A = x [T, K]: row s of
+// expert e is x[a_rows[e * C + s]] (a_bytes = T K 2, the descriptor's byte
+// count; a_rows has 128 entries of padding past E C).  The row map is read with uniform (scalar) loads when a tile starts,
+// so waiting for it never waits for the copies in flight; rows past the tile's
+// valid count point past the descriptor and read as zero.
 template <int TOKB, int NBW, int WAVES, int MODE, int S, int KC>
-__global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __restrict__ A,   // [E, C, K]
+__global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __restrict__ A,   // [E, C, K] or x
                                                               const bf16_t* __restrict__ W,   // [E, N, K]
                                                               const int32_t* __restrict__ pre,
                                                               const int4* __restrict__ ttab,
                                                               void* __restrict__ out,
                                                               const bf16_t* __restrict__ mask,
                                                               const FfnCombine cb,
+                                                              const int32_t* __restrict__ a_rows, uint32_t a_bytes,
                                                               int E, int C, int K, int N, int n_tiles) {
     static_assert(KC == 64 || KC == 32, "64- or 32-wide K chunks");
     constexpr int TOK = 32 * TOKB;
@@ -652,10 +658,45 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
     auto set_frontier = [&](int j) {
         f_tile = j;
         const FfnTile t = decode_tile(j * G + slot, ttab, n_tiles);
-        const uint64_t ab = (uint64_t)(uintptr_t)((const char*)A + ((size_t)t.e * C + t.tok_base) * K * 2);
-        a_lo = (uint32_t)ab;
-        a_hi = (uint32_t)(ab >> 32);
-        a_n = (uint32_t)(t.nv * K * 2);
+        if (a_rows) {
+            const uint64_t ab = (uint64_t)(uintptr_t)A;
+            a_lo = (uint32_t)ab;
+            a_hi = (uint32_t)(ab >> 32);
+            a_n = a_bytes;
+            const int32_t* rowp = a_rows + (size_t)t.e * C + t.tok_base;
+            const int rl = lane / NCOL;
+            // each copy's RPC row entries in one uniform load, all issued before any
+            // is used (the map is padded by 128 entries, so a short last tile
+            // reads past its rows harmlessly); readfirstlane keeps them scalar,
+            // or the per-lane pick below becomes a vector load, whose wait would
+            // also wait for the copies in flight
+            int tk[APW][RPC];
+#pragma unroll
+            for (int i = 0; i < APW; ++i) {
+                const int q = wave * APW + i;
+                const int r0 = RPC * (q < A_COPIES ? q : 0);
+#pragma unroll
+                for (int u = 0; u < RPC; ++u) tk[i][u] = __builtin_amdgcn_readfirstlane(rowp[r0 + u]);
+            }
+#pragma unroll
+            for (int i = 0; i < APW; ++i) {
+                const int q = wave * APW + i;
+                const int r0 = RPC * (q < A_COPIES ? q : 0);
+                int mine = tk[i][0];
+#pragma unroll
+                for (int u = 1; u < RPC; ++u) mine = rl == u ? tk[i][u] : mine;
+                // rows past the tile: past the end, zeros (a bitwise select, so no branch
+                // sinks the uniform loads into lane-dependent code)
+                const uint32_t valid = 0u - (uint32_t)(r0 + rl < t.nv);
+                const uint32_t off = (((uint32_t)mine * K * 2) & valid) | (a_bytes & ~valid);
+                avo[i] = off + (dma_slot<KC>(r0 + rl, lane % NCOL) << 4);
+            }
+        } else {
+            const uint64_t ab = (uint64_t)(uintptr_t)((const char*)A + ((size_t)t.e * C + t.tok_base) * K * 2);
+            a_lo = (uint32_t)ab;
+            a_hi = (uint32_t)(ab >> 32);
+            a_n = (uint32_t)(t.nv * K * 2);
+        }
         const int r0 = t.nt * NWG;                                   // rows past N read zeros
         const uint64_t wb = (uint64_t)(uintptr_t)((const char*)W + ((size_t)t.e * N + r0) * K * 2);
         w_lo = (uint32_t)wb;
@@ -772,7 +813,7 @@ hipError_t launch_expert_gemm_t(const bf16_t* A, const bf16_t* W, const int32_t*
 template <int TOKB, int NBW, int WAVES, int MODE, int S, int KC>
 hipError_t launch_expert_gemm_dma_t(const bf16_t* A, const bf16_t* W, const int32_t* pre, const int4* ttab, void* out,
                                     const bf16_t* mask, const FfnCombine& cb, int E, int C, int K, int N,
-                                    hipStream_t s) {
+                                    hipStream_t s, const int32_t* a_rows = nullptr, uint32_t a_bytes = 0) {
     constexpr int NWG = WAVES * 32 * NBW;
     const int n_tiles = (N + NWG - 1) / NWG;
     const int tok_tiles = (C + 32 * TOKB - 1) / (32 * TOKB);
@@ -780,7 +821,7 @@ hipError_t launch_expert_gemm_dma_t(const bf16_t* A, const bf16_t* W, const int3
     int64_t grid = std::min<int64_t>((int64_t)device_cus(), (max_tiles + 7) / 8 * 8);   // one workgroup per CU
     grid = std::max<int64_t>(8, grid / 8 * 8);
     hipLaunchKernelGGL((expert_gemm_dma<TOKB, NBW, WAVES, MODE, S, KC>), dim3((unsigned)grid), dim3(64 * WAVES), 0, s, A,
-                       W, pre, ttab, out, mask, cb, E, C, K, N, n_tiles);
+                       W, pre, ttab, out, mask, cb, a_rows, a_bytes, E, C, K, N, n_tiles);
     return hipGetLastError();
 }
 
@@ -822,29 +863,32 @@ static int dma_tile_width(int E, int C, int N, bool narrow = false) {
 template <int MODE>
 static hipError_t launch_expert_gemm(const bf16_t* A, const bf16_t* W, const int32_t* pre, const int4* ttab, void* out,
                                      const bf16_t* mask, int E, int C, int K, int N, hipStream_t s,
-                                     const FfnCombine& cb = FfnCombine{}) {
+                                     const FfnCombine& cb = FfnCombine{}, const int32_t* a_rows = nullptr,
+                                     uint32_t a_bytes = 0) {
+    // a_rows (token rows gathered from x) needs the direct-to-LDS kernel
+    if (a_rows && C <= 64) return hipErrorInvalidValue;
     // the token tile must be ffn_token_tile(C) rows: the prefix kernel lists tiles of that size
     if constexpr (MODE == OUT_COMBINE) {
         // one 32-row block per wave: the epilogue's residual runs fit in registers
         if (C <= 64) return hipErrorInvalidValue;   // the fused combine needs 128-row token tiles
         if (dma_tile_width(E, C, N, true) == 256)
-            return launch_expert_gemm_dma_t<4, 1, 8, MODE, 3, 64>(A, W, pre, ttab, out, mask, cb, E, C, K, N, s);
-        return launch_expert_gemm_dma_t<4, 1, 6, MODE, 3, 64>(A, W, pre, ttab, out, mask, cb, E, C, K, N, s);
+            return launch_expert_gemm_dma_t<4, 1, 8, MODE, 3, 64>(A, W, pre, ttab, out, mask, cb, E, C, K, N, s, a_rows, a_bytes);
+        return launch_expert_gemm_dma_t<4, 1, 6, MODE, 3, 64>(A, W, pre, ttab, out, mask, cb, E, C, K, N, s, a_rows, a_bytes);
     } else {
         if (C > 64) {
             switch (dma_tile_width(E, C, N)) {
                 case 512:
                     return launch_expert_gemm_dma_t<4, 2, 8, MODE, 2, 64>(A, W, pre, ttab, out, mask, cb, E, C, K, N,
-                                                                          s);
+                                                                          s, a_rows, a_bytes);
                 case 384:
                     return launch_expert_gemm_dma_t<4, 2, 6, MODE, 2, 64>(A, W, pre, ttab, out, mask, cb, E, C, K, N,
-                                                                          s);
+                                                                          s, a_rows, a_bytes);
                 case 256:
                     return launch_expert_gemm_dma_t<4, 1, 8, MODE, 3, 64>(A, W, pre, ttab, out, mask, cb, E, C, K, N,
-                                                                          s);
+                                                                          s, a_rows, a_bytes);
                 default:
                     return launch_expert_gemm_dma_t<4, 1, 6, MODE, 3, 64>(A, W, pre, ttab, out, mask, cb, E, C, K, N,
-                                                                          s);
+                                                                          s, a_rows, a_bytes);
             }
         }
         if (C > 32) return launch_expert_gemm_t<2, 2, 4, 3, MODE, 512>(A, W, pre, ttab, out, mask, E, C, K, N, s);
@@ -883,16 +927,24 @@ hipError_t launch_expert_gemm1(const bf16_t* buf, const bf16_t* w1, const int32_
     return launch_expert_gemm<OUT_RELU_BF16>(buf, w1, pre, ttab, h, nullptr, E, C, d, d_ff, s);
 }
 
+hipError_t launch_expert_gemm1_gather(const bf16_t* x, int64_t T, const int32_t* slot_token, const bf16_t* w1,
+                                      const int32_t* pre, const int4* ttab, bf16_t* h, int E, int C, int d, int d_ff,
+                                      hipStream_t s) {
+    if (!ffn_wide_tiles(C) || T * d * 2 + 2 * (int64_t)d + 256 >= (int64_t(1) << 32)) return hipErrorInvalidValue;
+    return launch_expert_gemm<OUT_RELU_BF16>(x, w1, pre, ttab, h, nullptr, E, C, d, d_ff, s, FfnCombine{}, slot_token,
+                                             (uint32_t)(T * d * 2));
+}
+
 hipError_t launch_expert_gemm2(const bf16_t* h, const bf16_t* w2, const int32_t* pre, const int4* ttab, float* y,
                                int E, int C, int d, int d_ff, hipStream_t s) {
     return launch_expert_gemm<OUT_F32>(h, w2, pre, ttab, y, nullptr, E, C, d_ff, d, s);
 }
 
-bool ffn_combine_fusable(int C) { return C > 64; }
+bool ffn_wide_tiles(int C) { return C > 64; }
 
 hipError_t launch_expert_gemm2_combine(const bf16_t* h, const bf16_t* w2, const int32_t* pre, const int4* ttab,
                                        const FfnCombine& cb, int E, int C, int d, int d_ff, hipStream_t s) {
-    if (!ffn_combine_fusable(C)) return hipErrorInvalidValue;
+    if (!ffn_wide_tiles(C)) return hipErrorInvalidValue;
     return launch_expert_gemm<OUT_COMBINE>(h, w2, pre, ttab, nullptr, nullptr, E, C, d_ff, d, s, cb);
 }
 
