@@ -245,6 +245,7 @@ struct DispatchArgs {
     int32_t* slot = nullptr; int32_t* rows_total = nullptr;
     bf16_t* out_pass = nullptr; bool pass_residual = false;   // k = 1: dropped tokens' output rows (fused combine)
     bool no_buf = false;   // the first expert GEMM gathers the token rows itself: buf is not written
+    int32_t* tl_pre = nullptr; int4* tl_tab = nullptr;   // also build the expert GEMMs' token-tile list
 };
 
 switch_status validate_dispatch(const DispatchArgs& a, const void* ws, size_t ws_bytes) {
@@ -296,7 +297,8 @@ switch_status run_dispatch(const DispatchArgs& a, void* ws, hipStream_t s) {
     LAUNCH(K_GATHER, "gather", s,
            launch_gather(a.x, a.expert, tile_counts, group_base, one ? a.accepted : rows_total, N, a.d, a.E, a.k, G,
                          a.priority, tile, a.C, rows, a.position, a.keep, a.slot, a.slot_token,
-                         a.no_buf ? nullptr : a.buf, a.out_pass, a.pass_residual, s));
+                         a.no_buf ? nullptr : a.buf, a.out_pass, a.pass_residual, a.tl_pre, a.tl_tab,
+                         ffn_token_tile(rows), s));
     return SWITCH_OK;
 }
 
@@ -307,6 +309,7 @@ struct FfnArgs {
     const FfnCombine* cb = nullptr;   // the combine in the second GEMM's epilogue (y optional then)
     // token rows gathered by the first GEMM from x [x_tokens, d] through a_rows (= slot_token); buf unused
     const bf16_t* x_src = nullptr; int64_t x_tokens = 0; const int32_t* a_rows = nullptr;
+    bool tiles_ready = false;   // the token-tile list in the workspace was built by the dispatch step
 };
 
 switch_status validate_ffn(const FfnArgs& a, const void* ws, size_t ws_bytes) {
@@ -340,7 +343,8 @@ switch_status run_ffn(const FfnArgs& a, void* ws, hipStream_t s) {
     if (a.h) h = a.h;
     int32_t* pre = c.take<int32_t>((size_t)a.E + 1);
     int4* ttab = c.take<int4>(ffn_tile_table_entries(a.E, a.C));
-    LAUNCH(K_FFN_TILES, "ffn_tile_prefix", s, launch_ffn_tile_prefix(a.accepted, a.E, a.C, pre, ttab, s));
+    if (!a.tiles_ready)
+        LAUNCH(K_FFN_TILES, "ffn_tile_prefix", s, launch_ffn_tile_prefix(a.accepted, a.E, a.C, pre, ttab, s));
     if (a.a_rows)
         LAUNCH(K_GEMM1, "expert_gemm1", s,
                launch_expert_gemm1_gather(a.x_src, a.x_tokens, a.a_rows, a.w1, pre, ttab, h, a.E, a.C, a.d, a.d_ff,
@@ -844,6 +848,15 @@ switch_status switch_layer_fwd(const switch_layer_args* la, void* ws, size_t ws_
         da.out_pass = L.out;
         da.pass_residual = L.residual != 0;
         fa.cb = &cb;
+    }
+    // the dispatch step's extra workgroup builds the expert GEMMs' token-tile
+    // list (same workspace carve as run_ffn), so no tile-prefix launch
+    if (rows > 0) {
+        Carver fc{ffn_space};
+        fc.take<bf16_t>((size_t)L.E * rows * L.d_ff);
+        da.tl_pre = fc.take<int32_t>((size_t)L.E + 1);
+        da.tl_tab = fc.take<int4>(ffn_tile_table_entries(L.E, rows));
+        fa.tiles_ready = true;
     }
     // buf and slot_token not kept: the first GEMM reads the token rows from x
     // through the (padded) workspace slot_token

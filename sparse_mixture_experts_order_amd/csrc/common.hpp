@@ -93,6 +93,47 @@ __device__ __forceinline__ float row16_sum(float v) {
     return v;
 }
 
+// Token-tile list of the expert GEMMs, built by one workgroup of NT threads:
+// pre[e] = number of valid TOK-row token tiles of experts < e (pre[E] = total
+// V), and ttab[v] = {expert, first row, valid rows, 0} for v = pre[e] + tt, the
+// token tiles of each expert in row order.  accepted == NULL means every
+// expert has all C rows.  The exclusive scan runs over the waves' prefix sums
+// in wave order.
+template <int NT>
+__device__ void ffn_tile_list(const int32_t* __restrict__ accepted, int E, int C, int TOK, int32_t* __restrict__ pre,
+                              int4* __restrict__ ttab) {
+    __shared__ int wsum[NT / 64];
+    const int per = (E + NT - 1) / NT;
+    const int e0 = threadIdx.x * per;
+    int local = 0;
+    for (int i = 0; i < per; ++i) {
+        const int e = e0 + i;
+        if (e < E) local += (min(max(accepted ? accepted[e] : C, 0), C) + TOK - 1) / TOK;
+    }
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int incl = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off);
+        if (lane >= off) incl += v;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int base = 0;
+    for (int w = 0; w < wave; ++w) base += wsum[w];
+    int run = base + incl - local;
+    for (int i = 0; i < per; ++i) {
+        const int e = e0 + i;
+        if (e < E) {
+            pre[e] = run;
+            const int a = min(max(accepted ? accepted[e] : C, 0), C);
+            for (int tt = 0; tt * TOK < a; ++tt) ttab[run + tt] = make_int4(e, tt * TOK, min(TOK, a - tt * TOK), 0);
+            run += (a + TOK - 1) / TOK;
+        }
+    }
+    if ((int)threadIdx.x == NT - 1) pre[E] = base + incl;
+}
+
 // Raw buffer descriptors.  The fourth word selects the 32-bit data format
 // (unused by 16-byte loads, but a zero format is invalid); reads at or past
 // the descriptor's byte count return zero.

@@ -151,7 +151,9 @@ __global__ __launch_bounds__(256) void scan_offsets(int32_t* __restrict__ tile_c
 // With out_pass (k = 1, the combine done by the second expert GEMM) a dropped
 // token's output row is written here: its residual x row bit for bit, or zeros
 // without a residual.  With buf == NULL (the first expert GEMM gathers the
-// token rows from x itself) no rows are copied or zeroed.
+// token rows from x itself) no rows are copied or zeroed.  With tl_pre one
+// extra (last) workgroup builds the expert GEMMs' token-tile list from the
+// filled rows per expert (ffn_tile_list, TOK = tl_tok).
 constexpr int GATHER_TOK = 16, GATHER_ROWS = 16;
 
 __global__ __launch_bounds__(256) void gather(const bf16_t* __restrict__ x, const int32_t* __restrict__ expert,
@@ -162,7 +164,12 @@ __global__ __launch_bounds__(256) void gather(const bf16_t* __restrict__ x, cons
                                               int32_t* __restrict__ position, uint8_t* __restrict__ keep,
                                               int32_t* __restrict__ slot, int32_t* __restrict__ slot_token,
                                               bf16_t* __restrict__ buf, bf16_t* __restrict__ out_pass,
-                                              int pass_residual) {
+                                              int pass_residual, int32_t* __restrict__ tl_pre,
+                                              int4* __restrict__ tl_tab, int tl_tok) {
+    if (tl_pre && blockIdx.x == gridDim.x - 1) {   // the expert GEMMs' token-tile list
+        ffn_tile_list<256>(rows_filled, E, rows, tl_tok, tl_pre, tl_tab);
+        return;
+    }
     __shared__ int s_dst[GATHER_TOK];
     __shared__ int s_tok[GATHER_TOK];
     const int vpr = d >> 3;  // 16-byte vectors per row
@@ -261,14 +268,16 @@ hipError_t launch_scan_offsets(int32_t* tile_counts, int ntiles, int tiles_per_g
 hipError_t launch_gather(const bf16_t* x, const int32_t* expert, const int32_t* offsets, const int32_t* group_base,
                          const int32_t* rows_filled, int N, int d, int E, int k, int G, int rank, int tile, int C,
                          int rows, int32_t* position, uint8_t* keep, int32_t* slot, int32_t* slot_token, bf16_t* buf,
-                         bf16_t* out_pass, bool pass_residual, hipStream_t s) {
+                         bf16_t* out_pass, bool pass_residual, int32_t* tl_pre, int4* tl_tab, int tl_tok,
+                         hipStream_t s) {
     const int ntok = (N + GATHER_TOK - 1) / GATHER_TOK;
     const int64_t nrows = buf ? (int64_t)E * rows : 0;
     const int nzero = (int)((nrows + GATHER_ROWS - 1) / GATHER_ROWS);
-    if (ntok + nzero == 0) return hipSuccess;
-    hipLaunchKernelGGL(gather, dim3(ntok + nzero), dim3(256), 0, s, x, expert, offsets, group_base, rows_filled, N, d,
+    const int nlist = tl_pre ? 1 : 0;
+    if (ntok + nzero + nlist == 0) return hipSuccess;
+    hipLaunchKernelGGL(gather, dim3(ntok + nzero + nlist), dim3(256), 0, s, x, expert, offsets, group_base, rows_filled, N, d,
                        E, k, std::max(G, 1), rank, tile, C, rows, ntok, position, keep, slot, slot_token, buf,
-                       k == 1 ? out_pass : nullptr, pass_residual ? 1 : 0);
+                       k == 1 ? out_pass : nullptr, pass_residual ? 1 : 0, tl_pre, tl_tab, tl_tok);
     return hipGetLastError();
 }
 

@@ -38,43 +38,10 @@ namespace swmoe {
 
 constexpr int FFN_LDS_STRIDE = 72;  // bf16 elements per token row in LDS (64 + 8 pad)
 
-// Token-tile list: pre[e] = number of valid TOK-row token tiles of experts < e
-// (pre[E] = total V), and ttab[v] = {expert, first row, valid rows, 0} for
-// v = pre[e] + tt, the token tiles of each expert in row order.  accepted ==
-// NULL means every expert has all C rows.
+// The token-tile list (ffn_tile_list) as a kernel of its own.
 __global__ __launch_bounds__(1024) void ffn_tile_prefix(const int32_t* __restrict__ accepted, int E, int C, int TOK,
                                                         int32_t* __restrict__ pre, int4* __restrict__ ttab) {
-    __shared__ int wsum[16];
-    const int per = (E + 1023) / 1024;
-    const int e0 = threadIdx.x * per;
-    int local = 0;
-    for (int i = 0; i < per; ++i) {
-        const int e = e0 + i;
-        if (e < E) local += (min(max(accepted ? accepted[e] : C, 0), C) + TOK - 1) / TOK;
-    }
-    // exclusive scan of `local` over the block: waves, then wave totals in order
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int incl = local;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int v = __shfl_up(incl, off);
-        if (lane >= off) incl += v;
-    }
-    if (lane == 63) wsum[wave] = incl;
-    __syncthreads();
-    int base = 0;
-    for (int w = 0; w < wave; ++w) base += wsum[w];
-    int run = base + incl - local;
-    for (int i = 0; i < per; ++i) {
-        const int e = e0 + i;
-        if (e < E) {
-            pre[e] = run;
-            const int a = min(max(accepted ? accepted[e] : C, 0), C);
-            for (int tt = 0; tt * TOK < a; ++tt) ttab[run + tt] = make_int4(e, tt * TOK, min(TOK, a - tt * TOK), 0);
-            run += (a + TOK - 1) / TOK;
-        }
-    }
-    if (threadIdx.x == 1023) pre[E] = base + incl;
+    ffn_tile_list<1024>(accepted, E, C, TOK, pre, ttab);
 }
 
 struct FfnTile {

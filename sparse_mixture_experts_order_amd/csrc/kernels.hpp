@@ -39,7 +39,8 @@ hipError_t launch_scan_offsets(int32_t* tile_counts, int ntiles, int tiles_per_g
 hipError_t launch_gather(const bf16_t* x, const int32_t* expert, const int32_t* offsets, const int32_t* group_base,
                          const int32_t* rows_filled, int N, int d, int E, int k, int G, int rank, int tile, int C,
                          int rows, int32_t* position, uint8_t* keep, int32_t* slot, int32_t* slot_token, bf16_t* buf,
-                         bf16_t* out_pass, bool pass_residual, hipStream_t s);
+                         bf16_t* out_pass, bool pass_residual, int32_t* tl_pre, int4* tl_tab, int tl_tok,
+                         hipStream_t s);
 
 // expert_ffn.hip
 int ffn_token_tile(int C);
