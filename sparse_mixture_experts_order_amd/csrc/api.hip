@@ -246,6 +246,9 @@ struct DispatchArgs {
     bf16_t* out_pass = nullptr; bool pass_residual = false;   // k = 1: dropped tokens' output rows (fused combine)
     bool no_buf = false;   // the first expert GEMM gathers the token rows itself: buf is not written
     int32_t* tl_pre = nullptr; int4* tl_tab = nullptr;   // also build the expert GEMMs' token-tile list
+    const AuxStatsArgs* aux = nullptr;                   // and the load-balancing statistics
+    // the router's partial probability rows (prows per group), summed into prob_sum by the scan
+    const float* parts = nullptr; int prows = 0; float* prob_sum = nullptr;
 };
 
 switch_status validate_dispatch(const DispatchArgs& a, const void* ws, size_t ws_bytes) {
@@ -293,12 +296,12 @@ switch_status run_dispatch(const DispatchArgs& a, void* ws, hipStream_t s) {
                launch_scan_local(a.expert, N, a.E, a.k, G, a.priority, tile, a.position, tile_counts, s));
     LAUNCH(K_SCAN_OFFSETS, "scan_offsets", s,
            launch_scan_offsets(tile_counts, ntiles, tpg, ng, a.E, a.C, a.counts, a.accepted, group_base, rows_total,
-                               s));
+                               a.parts, a.prows, a.prob_sum, s));
     LAUNCH(K_GATHER, "gather", s,
            launch_gather(a.x, a.expert, tile_counts, group_base, one ? a.accepted : rows_total, N, a.d, a.E, a.k, G,
                          a.priority, tile, a.C, rows, a.position, a.keep, a.slot, a.slot_token,
                          a.no_buf ? nullptr : a.buf, a.out_pass, a.pass_residual, a.tl_pre, a.tl_tab,
-                         ffn_token_tile(rows), s));
+                         ffn_token_tile(rows), a.aux, s));
     return SWITCH_OK;
 }
 
@@ -393,8 +396,7 @@ struct AuxArgs {
     int64_t T; int32_t E; float alpha; float* f; float* P; float* loss; float* dlogits;
     float beta; float* z_loss;   // router z-loss (optional, z_loss == NULL: not computed)
     int32_t k = 1; int64_t G = 0;   // counts, prob_sum, f, P are [groups, E]
-    // prob_sum still to be summed from the router's partial rows (rows per group)
-    const float* parts = nullptr; int parts_rows = 0; float* prob_sum_out = nullptr;
+    bool stats_done = false;   // prob_sum, f, P and the loss already computed by the dispatch step
 };
 
 switch_status validate_aux(const AuxArgs& a) {
@@ -415,11 +417,7 @@ switch_status validate_aux(const AuxArgs& a) {
 
 switch_status run_aux(const AuxArgs& a, hipStream_t s) {
     const int64_t Gt = group_tokens(a.T, a.G);
-    if (a.parts)
-        LAUNCH(K_AUX_STATS, "aux_stats", s,
-               launch_aux_stats_parts(a.parts, a.parts_rows, (int)group_count(a.T, a.G), a.E, a.counts, Gt, a.k,
-                                      a.alpha, a.prob_sum_out, a.f, a.P, a.loss, s));
-    else
+    if (!a.stats_done)
         LAUNCH(K_AUX_STATS, "aux_stats", s,
                launch_aux_stats(a.counts, a.prob_sum, Gt, (int)group_count(a.T, a.G), a.E, a.k, a.alpha, a.f, a.P,
                                 a.loss, s));
@@ -877,10 +875,15 @@ switch_status switch_layer_fwd(const switch_layer_args* la, void* ws, size_t ws_
     CHECK(validate_combine(ca));
     CHECK(validate_aux(xa));
     CHECK(run_route(ra, route_space, s));
-    if (parts) {
-        xa.parts = parts;
-        xa.parts_rows = parts_rows;
-        xa.prob_sum_out = prob_sum;
+    AuxStatsArgs aux_in_gather{};
+    if (parts) {   // the scan sums the partial rows into prob_sum; gather's extra workgroup does f, P, loss
+        da.parts = parts;
+        da.prows = parts_rows;
+        da.prob_sum = prob_sum;
+        aux_in_gather = AuxStatsArgs{L.counts, prob_sum, group_tokens(L.T, G), (int)group_count(L.T, G), L.E, k,
+                                     L.alpha, L.f, L.P, L.loss};
+        da.aux = &aux_in_gather;
+        xa.stats_done = true;
     }
     CHECK(run_dispatch(da, dispatch_space, s));
     CHECK(run_ffn(fa, ffn_space, s));

@@ -11,96 +11,12 @@
 
 namespace swmoe {
 
-// One workgroup: f, P and the loss, reduced in fp64 in a fixed tree order.
-// Routing groups: counts and prob_sum are [ngroups, E]; group g has G tokens
-// and k choices per token, f_ge = counts_ge / (k G), P_ge = prob_sum_ge / G and
-// the loss is alpha E times the mean over groups of sum_e f_ge P_ge.  One
-// group of T tokens with k = 1 is the Switch layer's loss.
+// The load-balancing statistics (aux_stats_block) as a kernel of its own.
 __global__ __launch_bounds__(1024) void aux_stats(const int32_t* __restrict__ counts,
                                                   const float* __restrict__ prob_sum, int64_t G, int ngroups, int E,
                                                   int k, float alpha, float* __restrict__ f, float* __restrict__ P,
                                                   float* __restrict__ loss) {
-    __shared__ double red[1024];
-    double acc = 0.0;
-    const int64_t n = (int64_t)ngroups * E;
-    for (int64_t i = threadIdx.x; i < n; i += 1024) {
-        const double fe = G > 0 ? (double)counts[i] / ((double)k * (double)G) : 0.0;
-        const double pe = G > 0 ? (double)prob_sum[i] / (double)G : 0.0;
-        f[i] = (float)fe;
-        P[i] = (float)pe;
-        acc += fe * pe;
-    }
-    red[threadIdx.x] = acc;
-    __syncthreads();
-    for (int s = 512; s > 0; s >>= 1) {
-        if ((int)threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
-        __syncthreads();
-    }
-    if (threadIdx.x == 0) loss[0] = ngroups > 0 ? (float)((double)alpha * (double)E * red[0] / (double)ngroups) : 0.f;
-}
-
-// The same with prob_sum taken from the router's partial rows (the layer
-// forward, when they are few): group g's column e is the sum of rows
-// [g rows, (g + 1) rows) of part[., E].  tpc threads share a column, each
-// summing every tpc-th row in row order (fp64; neighbouring lanes read
-// neighbouring columns of a row); the column's tpc sums are then added in
-// thread order.  prob_sum, f, P and the loss follow as in aux_stats.
-__global__ __launch_bounds__(1024) void aux_stats_parts(const float* __restrict__ part, int rows, int ngroups, int E,
-                                                        const int32_t* __restrict__ counts, int64_t G, int k,
-                                                        float alpha, float* __restrict__ prob_sum,
-                                                        float* __restrict__ f, float* __restrict__ P,
-                                                        float* __restrict__ loss) {
-    __shared__ double red[1024];
-    const int n = ngroups * E;
-    const int tpc = n >= 1024 ? 1 : min(16, 1024 / n);
-    const int cols = 1024 / tpc;                    // columns per pass; neighbouring lanes take neighbouring columns
-    const int j = (int)threadIdx.x / cols, cl = (int)threadIdx.x - j * cols;
-    double acc = 0.0;
-    for (int c0 = 0; c0 < n; c0 += cols) {
-        const int c = c0 + cl;
-        double sum = 0.0;
-        if (c < n) {
-            const int g = c / E, e = c - g * E;
-            const float* col = part + (size_t)g * rows * E + e;
-            int r = j;
-            for (; r + 31 * tpc < rows; r += 32 * tpc) {   // 32 loads in flight, added in row order
-                float v[32];
-#pragma unroll
-                for (int q = 0; q < 32; ++q) v[q] = col[(size_t)(r + q * tpc) * E];
-#pragma unroll
-                for (int q = 0; q < 32; ++q) sum += (double)v[q];
-            }
-            for (; r + 7 * tpc < rows; r += 8 * tpc) {
-                float v[8];
-#pragma unroll
-                for (int q = 0; q < 8; ++q) v[q] = col[(size_t)(r + q * tpc) * E];
-#pragma unroll
-                for (int q = 0; q < 8; ++q) sum += (double)v[q];
-            }
-            for (; r < rows; r += tpc) sum += (double)col[(size_t)r * E];
-        }
-        red[threadIdx.x] = sum;
-        __syncthreads();
-        if (j == 0 && c < n) {
-            double t = 0.0;
-            for (int q = 0; q < tpc; ++q) t += red[q * cols + cl];
-            const float ps = (float)t;
-            prob_sum[c] = ps;
-            const double fe = G > 0 ? (double)counts[c] / ((double)k * (double)G) : 0.0;
-            const double pe = G > 0 ? (double)ps / (double)G : 0.0;
-            f[c] = (float)fe;
-            P[c] = (float)pe;
-            acc += fe * pe;
-        }
-        __syncthreads();
-    }
-    red[threadIdx.x] = acc;
-    __syncthreads();
-    for (int st = 512; st > 0; st >>= 1) {
-        if ((int)threadIdx.x < st) red[threadIdx.x] += red[threadIdx.x + st];
-        __syncthreads();
-    }
-    if (threadIdx.x == 0) loss[0] = ngroups > 0 ? (float)((double)alpha * (double)E * red[0] / (double)ngroups) : 0.f;
+    aux_stats_block<1024>(AuxStatsArgs{counts, prob_sum, G, ngroups, E, k, alpha, f, P, loss});
 }
 
 // Router z-loss (ST-MoE, as restated in "MoE routing load collapse",
@@ -172,14 +88,6 @@ __global__ __launch_bounds__(256) void aux_grad(const float* __restrict__ logits
 hipError_t launch_aux_stats(const int32_t* counts, const float* prob_sum, int64_t G, int ngroups, int E, int k,
                             float alpha, float* f, float* P, float* loss, hipStream_t s) {
     hipLaunchKernelGGL(aux_stats, dim3(1), dim3(1024), 0, s, counts, prob_sum, G, ngroups, E, k, alpha, f, P, loss);
-    return hipGetLastError();
-}
-
-hipError_t launch_aux_stats_parts(const float* part, int rows, int ngroups, int E, const int32_t* counts, int64_t G,
-                                  int k, float alpha, float* prob_sum, float* f, float* P, float* loss,
-                                  hipStream_t s) {
-    hipLaunchKernelGGL(aux_stats_parts, dim3(1), dim3(1024), 0, s, part, rows, ngroups, E, counts, G, k, alpha,
-                       prob_sum, f, P, loss);
     return hipGetLastError();
 }
 

@@ -134,6 +134,39 @@ __device__ void ffn_tile_list(const int32_t* __restrict__ accepted, int E, int C
     if ((int)threadIdx.x == NT - 1) pre[E] = base + incl;
 }
 
+// Load-balancing statistics, one workgroup of NT threads, fp64 in a fixed
+// order.  Routing groups: counts and prob_sum are [ngroups, E]; group g has G
+// tokens and k choices per token, f_ge = counts_ge / (k G), P_ge = prob_sum_ge
+// / G and the loss is alpha E times the mean over groups of sum_e f_ge P_ge
+// (each thread adds the terms of columns i, i + NT, ... in order, then a fixed
+// tree).  One group of T tokens with k = 1 is the Switch layer's loss.
+struct AuxStatsArgs {
+    const int32_t* counts; const float* prob_sum; int64_t G; int ngroups, E, k; float alpha;
+    float* f; float* P; float* loss;
+};
+
+template <int NT>
+__device__ void aux_stats_block(const AuxStatsArgs a) {
+    __shared__ double red[NT];
+    double acc = 0.0;
+    const int64_t n = (int64_t)a.ngroups * a.E;
+    for (int64_t i = threadIdx.x; i < n; i += NT) {
+        const double fe = a.G > 0 ? (double)a.counts[i] / ((double)a.k * (double)a.G) : 0.0;
+        const double pe = a.G > 0 ? (double)a.prob_sum[i] / (double)a.G : 0.0;
+        a.f[i] = (float)fe;
+        a.P[i] = (float)pe;
+        acc += fe * pe;
+    }
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    for (int s = NT / 2; s > 0; s >>= 1) {
+        if ((int)threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0)
+        a.loss[0] = a.ngroups > 0 ? (float)((double)a.alpha * (double)a.E * red[0] / (double)a.ngroups) : 0.f;
+}
+
 // Raw buffer descriptors.  The fourth word selects the 32-bit data format
 // (unused by 16-byte loads, but a zero format is invalid); reads at or past
 // the descriptor's byte count return zero.

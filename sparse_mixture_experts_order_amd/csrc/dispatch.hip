@@ -90,26 +90,83 @@ __global__ __launch_bounds__(64 * W) void scan_local(const int32_t* __restrict__
 
 // tile_counts[b][e] becomes the exclusive prefix over the earlier tiles of
 // b's group (tpg tiles per group).  One wave per expert: lanes take 64 tiles
-// at a time; a segmented wave scan (shuffles, restarting at each group's
+// at a time (the counts of 4 such chunks are loaded together); a segmented wave scan (shuffles, restarting at each group's
 // first tile) ranks them and the open group's total carries into the next 64.
 // At each group's last tile: counts, accepted = min(counts, C) and, with
 // group_base, the group's first buffer row (a plain wave scan over the
 // accepted counts of the groups that end in these 64 tiles).  rows_total[e]
 // (optional) gets the accepted rows over all groups.
+// With parts (the layer forward) the wave also sums its expert's column of the
+// router's partial probability rows, prows rows per group, into prob_sum[g][e]
+// (fp64): with one group the lanes take every 64th row in row order and the
+// wave adds the lanes' sums in a fixed butterfly; with several groups lane l
+// takes a group and adds its rows in order.
+__device__ __forceinline__ void sum_prob_column(const float* __restrict__ parts, int prows, int ngroups, int E, int e,
+                                                int lane, float* __restrict__ prob_sum) {
+    if (ngroups == 1) {
+        double s = 0.0;
+        int r = lane;
+        for (; r + 192 < prows; r += 256) {   // four loads in flight, added in row order
+            const float v0 = parts[(size_t)r * E + e], v1 = parts[(size_t)(r + 64) * E + e];
+            const float v2 = parts[(size_t)(r + 128) * E + e], v3 = parts[(size_t)(r + 192) * E + e];
+            s += (double)v0;
+            s += (double)v1;
+            s += (double)v2;
+            s += (double)v3;
+        }
+        for (; r < prows; r += 64) s += (double)parts[(size_t)r * E + e];
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m);
+        if (lane == 0) prob_sum[e] = (float)s;
+        return;
+    }
+    for (int g0 = 0; g0 < ngroups; g0 += 64) {
+        const int g = g0 + lane;
+        if (g >= ngroups) break;
+        const float* col = parts + (size_t)g * prows * E + e;
+        double s = 0.0;
+        int r = 0;
+        for (; r + 3 < prows; r += 4) {
+            const float v0 = col[(size_t)r * E], v1 = col[(size_t)(r + 1) * E];
+            const float v2 = col[(size_t)(r + 2) * E], v3 = col[(size_t)(r + 3) * E];
+            s += (double)v0;
+            s += (double)v1;
+            s += (double)v2;
+            s += (double)v3;
+        }
+        for (; r < prows; ++r) s += (double)col[(size_t)r * E];
+        prob_sum[(size_t)g * E + e] = (float)s;
+    }
+}
+
 __global__ __launch_bounds__(256) void scan_offsets(int32_t* __restrict__ tile_counts, int ntiles, int tpg,
                                                     int ngroups, int E, int C, int32_t* __restrict__ counts,
                                                     int32_t* __restrict__ accepted, int32_t* __restrict__ group_base,
-                                                    int32_t* __restrict__ rows_total) {
+                                                    int32_t* __restrict__ rows_total, const float* __restrict__ parts,
+                                                    int prows, float* __restrict__ prob_sum) {
     const int lane = threadIdx.x & 63;
     const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (e >= E) return;
+    if (parts) sum_prob_column(parts, prows, ngroups, E, e, lane, prob_sum);
     int run = 0;    // count of the open group over the earlier chunks
     int rows = 0;   // accepted rows of the finished groups
+    constexpr int NB = 4;   // chunks of 64 tiles whose counts are loaded together
+    int cb[NB];
     for (int b0 = 0; b0 < ntiles; b0 += 64) {
+        const int q = (b0 >> 6) % NB;
+        if (q == 0) {
+#pragma unroll
+            for (int i = 0; i < NB; ++i) {
+                const int bi = b0 + 64 * i + lane;
+                cb[i] = bi < ntiles ? tile_counts[(size_t)bi * E + e] : 0;
+            }
+        }
         const int b = b0 + lane;
         const bool in = b < ntiles;
         const size_t o = (size_t)b * E + e;
-        const int c = in ? tile_counts[o] : 0;
+        int c = cb[0];
+#pragma unroll
+        for (int i = 1; i < NB; ++i) c = q == i ? cb[i] : c;
         const int gi = b / tpg;
         const int head = (b - gi * tpg) == 0;
         const bool tail = in && ((b - gi * tpg) == tpg - 1 || b == ntiles - 1);
@@ -153,7 +210,9 @@ __global__ __launch_bounds__(256) void scan_offsets(int32_t* __restrict__ tile_c
 // without a residual.  With buf == NULL (the first expert GEMM gathers the
 // token rows from x itself) no rows are copied or zeroed.  With tl_pre one
 // extra (last) workgroup builds the expert GEMMs' token-tile list from the
-// filled rows per expert (ffn_tile_list, TOK = tl_tok).
+// filled rows per expert (ffn_tile_list, TOK = tl_tok), and with aux.prob_sum
+// one more computes the load-balancing statistics (aux_stats_block; counts
+// and prob_sum are final once the scan has run).
 constexpr int GATHER_TOK = 16, GATHER_ROWS = 16;
 
 __global__ __launch_bounds__(256) void gather(const bf16_t* __restrict__ x, const int32_t* __restrict__ expert,
@@ -165,9 +224,13 @@ __global__ __launch_bounds__(256) void gather(const bf16_t* __restrict__ x, cons
                                               int32_t* __restrict__ slot, int32_t* __restrict__ slot_token,
                                               bf16_t* __restrict__ buf, bf16_t* __restrict__ out_pass,
                                               int pass_residual, int32_t* __restrict__ tl_pre,
-                                              int4* __restrict__ tl_tab, int tl_tok) {
+                                              int4* __restrict__ tl_tab, int tl_tok, const AuxStatsArgs aux) {
     if (tl_pre && blockIdx.x == gridDim.x - 1) {   // the expert GEMMs' token-tile list
         ffn_tile_list<256>(rows_filled, E, rows, tl_tok, tl_pre, tl_tab);
+        return;
+    }
+    if (aux.prob_sum && blockIdx.x == gridDim.x - 1 - (tl_pre ? 1 : 0)) {   // the load-balancing statistics
+        aux_stats_block<256>(aux);
         return;
     }
     __shared__ int s_dst[GATHER_TOK];
@@ -259,9 +322,10 @@ hipError_t launch_scan_local(const int32_t* expert, int N, int E, int k, int G, 
 
 hipError_t launch_scan_offsets(int32_t* tile_counts, int ntiles, int tiles_per_group, int ngroups, int E, int C,
                                int32_t* counts, int32_t* accepted, int32_t* group_base, int32_t* rows_total,
-                               hipStream_t s) {
+                               const float* parts, int prows, float* prob_sum, hipStream_t s) {
     hipLaunchKernelGGL(scan_offsets, dim3((E + 3) / 4), dim3(256), 0, s, tile_counts, ntiles,
-                       std::max(tiles_per_group, 1), ngroups, E, C, counts, accepted, group_base, rows_total);
+                       std::max(tiles_per_group, 1), ngroups, E, C, counts, accepted, group_base, rows_total, parts,
+                       prows, prob_sum);
     return hipGetLastError();
 }
 
@@ -269,15 +333,17 @@ hipError_t launch_gather(const bf16_t* x, const int32_t* expert, const int32_t* 
                          const int32_t* rows_filled, int N, int d, int E, int k, int G, int rank, int tile, int C,
                          int rows, int32_t* position, uint8_t* keep, int32_t* slot, int32_t* slot_token, bf16_t* buf,
                          bf16_t* out_pass, bool pass_residual, int32_t* tl_pre, int4* tl_tab, int tl_tok,
-                         hipStream_t s) {
+                         const AuxStatsArgs* aux, hipStream_t s) {
     const int ntok = (N + GATHER_TOK - 1) / GATHER_TOK;
     const int64_t nrows = buf ? (int64_t)E * rows : 0;
     const int nzero = (int)((nrows + GATHER_ROWS - 1) / GATHER_ROWS);
-    const int nlist = tl_pre ? 1 : 0;
+    const int nlist = (tl_pre ? 1 : 0) + (aux ? 1 : 0);
     if (ntok + nzero + nlist == 0) return hipSuccess;
+    const AuxStatsArgs no_aux{};
     hipLaunchKernelGGL(gather, dim3(ntok + nzero + nlist), dim3(256), 0, s, x, expert, offsets, group_base, rows_filled, N, d,
                        E, k, std::max(G, 1), rank, tile, C, rows, ntok, position, keep, slot, slot_token, buf,
-                       k == 1 ? out_pass : nullptr, pass_residual ? 1 : 0, tl_pre, tl_tab, tl_tok);
+                       k == 1 ? out_pass : nullptr, pass_residual ? 1 : 0, tl_pre, tl_tab, tl_tok,
+                       aux ? *aux : no_aux);
     return hipGetLastError();
 }
 

@@ -8,6 +8,7 @@
 
 namespace swmoe {
 typedef uint16_t bf16_t;
+struct AuxStatsArgs;   // common.hpp
 
 // route.hip
 hipError_t launch_split_router_weights(const float* w_r, bf16_t* wr3, int d, int E, bool chunked, hipStream_t s);
@@ -33,14 +34,16 @@ int scan_tile(int64_t group_assignments, bool one_group);   // 256, 128 or 64 as
 int scan_tiles(int64_t N, int tile);
 hipError_t launch_scan_local(const int32_t* expert, int N, int E, int k, int G, int rank, int tile,
                              int32_t* local_rank, int32_t* tile_counts, hipStream_t s);
+// parts (NULL: none): the router's partial probability rows, prows per group,
+// summed per expert into prob_sum [ngroups, E]
 hipError_t launch_scan_offsets(int32_t* tile_counts, int ntiles, int tiles_per_group, int ngroups, int E, int C,
                                int32_t* counts, int32_t* accepted, int32_t* group_base, int32_t* rows_total,
-                               hipStream_t s);
+                               const float* parts, int prows, float* prob_sum, hipStream_t s);
 hipError_t launch_gather(const bf16_t* x, const int32_t* expert, const int32_t* offsets, const int32_t* group_base,
                          const int32_t* rows_filled, int N, int d, int E, int k, int G, int rank, int tile, int C,
                          int rows, int32_t* position, uint8_t* keep, int32_t* slot, int32_t* slot_token, bf16_t* buf,
                          bf16_t* out_pass, bool pass_residual, int32_t* tl_pre, int4* tl_tab, int tl_tok,
-                         hipStream_t s);
+                         const AuxStatsArgs* aux, hipStream_t s);
 
 // expert_ffn.hip
 int ffn_token_tile(int C);
@@ -94,11 +97,10 @@ hipError_t launch_combine(const float* y, const int32_t* expert, const int32_t* 
 // aux.hip
 hipError_t launch_aux_stats(const int32_t* counts, const float* prob_sum, int64_t G, int ngroups, int E, int k,
                             float alpha, float* f, float* P, float* loss, hipStream_t s);
-// aux_stats with prob_sum summed from the router's partial rows [ngroups * rows, E]
-constexpr int64_t kAuxPartsMax = 262144;   // partial values one workgroup sums
-hipError_t launch_aux_stats_parts(const float* part, int rows, int ngroups, int E, const int32_t* counts, int64_t G,
-                                  int k, float alpha, float* prob_sum, float* f, float* P, float* loss,
-                                  hipStream_t s);
+// the layer forward hands the router's partial rows to the dispatch step's
+// scan (one wave per expert sums its column) when there are at most this
+// many values
+constexpr int64_t kAuxPartsMax = 262144;
 hipError_t launch_z_loss(const float* lse, int64_t T, float beta, float* z_loss, hipStream_t s);
 hipError_t launch_aux_grad(const float* logits, const float* lse, const float* f, int64_t T, int64_t G, int E,
                            float alpha, float beta, const int32_t* expert, const float* gate, const float* dgate,
