@@ -93,6 +93,25 @@ __device__ __forceinline__ float row16_sum(float v) {
     return v;
 }
 
+// row16_sum on each element of an array, one step over all elements before
+// the next (the same additions; independent instructions between dependent
+// DPP moves instead of wait states)
+template <int N>
+__device__ __forceinline__ void row16_sum_all(float (&v)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        v[i] += __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v[i]), 0xB1, 0xF, 0xF, false));
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        v[i] += __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v[i]), 0x4E, 0xF, 0xF, false));
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        v[i] += __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v[i]), 0x141, 0xF, 0xF, false));
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        v[i] += __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v[i]), 0x140, 0xF, 0xF, false));
+}
+
 // Token-tile list of the expert GEMMs, built by one workgroup of NT threads:
 // pre[e] = number of valid TOK-row token tiles of experts < e (pre[E] = total
 // V), and ttab[v] = {expert, first row, valid rows, 0} for v = pre[e] + tt, the

@@ -350,7 +350,12 @@ constexpr int RF_KC = 32;      // K per stage (one 16x16x32 MFMA step)
 static_assert(RF_TOK == 64, "the fused router writes one partial row per 64 tokens");
 int router_fused_blocks(int64_t T) { return (int)((T + RF_TOK - 1) / RF_TOK); }
 
-template <int EB, int S, int KMAX>
+// e^x for the softmax as 2^(x log2 e) on the hardware exp2 (v_exp_f32): the
+// rounding of the product adds a relative error of about |x| 2^-24 ln 2 to a
+// term, so the terms that matter (x near 0) stay within a few ulp.
+__device__ __forceinline__ float rf_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+
+template <int EB, int S, int KMAX, bool FULL>
 __global__ __launch_bounds__(256) void router_fused(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wr3,
                                                     const float* __restrict__ b_r, int T, int d, int E, int k,
                                                     float* __restrict__ logits_out, int32_t* __restrict__ expert,
@@ -489,7 +494,7 @@ __global__ __launch_bounds__(256) void router_fused(const bf16_t* __restrict__ x
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int e = eb * 16 + 4 * g + i;
-            v[eb][i] = e < E ? z4[i] + b4[i] : -INFINITY;
+            v[eb][i] = (FULL || e < E) ? z4[i] + b4[i] : -INFINITY;
             if constexpr (KMAX > 1) zc[eb][i] = v[eb][i];
             if (v[eb][i] > m) { m = v[eb][i]; mi = e; }
         }
@@ -503,16 +508,23 @@ __global__ __launch_bounds__(256) void router_fused(const bf16_t* __restrict__ x
         oi = lane_xor32(mi);
         if (om > m || (om == m && oi < mi)) { m = om; mi = oi; }
     }
+    if (logits_out && t < T) {
+#pragma unroll
+        for (int eb = 0; eb < EB; ++eb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int e = eb * 16 + 4 * g + i;
+                if (FULL || e < E) logits_out[(size_t)t * E + e] = v[eb][i];
+            }
+    }
     float ssum = 0.f;
 #pragma unroll
     for (int eb = 0; eb < EB; ++eb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int e = eb * 16 + 4 * g + i;
-            const float z = v[eb][i];
-            v[eb][i] = e < E ? expf(z - m) : 0.f;
+            v[eb][i] = (FULL || e < E) ? rf_exp(v[eb][i] - m) : 0.f;
             ssum += v[eb][i];
-            if (logits_out && t < T && e < E) logits_out[(size_t)t * E + e] = z;
         }
     ssum += lane_xor16(ssum);
     ssum += lane_xor32(ssum);
@@ -553,17 +565,18 @@ __global__ __launch_bounds__(256) void router_fused(const bf16_t* __restrict__ x
             ch[r] = ir;
             if (t < T && lane < 16) {
                 expert[(size_t)t * k + r] = ir;
-                gate[(size_t)t * k + r] = expf(mr - m) * inv;
+                gate[(size_t)t * k + r] = rf_exp(mr - m) * inv;
             }
         }
     }
     // p_te summed over the 16 tokens of a lane group, then the waves in order
     const float w = t < T ? inv : 0.f;
-    float psum[EB][4];
+    float psum[EB * 4];
 #pragma unroll
     for (int eb = 0; eb < EB; ++eb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) psum[eb][i] = row16_sum(v[eb][i] * w);
+        for (int i = 0; i < 4; ++i) psum[eb * 4 + i] = v[eb][i] * w;
+    row16_sum_all(psum);
     for (int ww = 0; ww < 4; ++ww) {
         if (wave == ww && r16 == 0) {
 #pragma unroll
@@ -571,7 +584,7 @@ __global__ __launch_bounds__(256) void router_fused(const bf16_t* __restrict__ x
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int e = eb * 16 + 4 * g + i;
-                    red[e] = (ww == 0) ? psum[eb][i] : red[e] + psum[eb][i];
+                    red[e] = (ww == 0) ? psum[eb * 4 + i] : red[e] + psum[eb * 4 + i];
                 }
         }
         __syncthreads();
@@ -582,9 +595,15 @@ __global__ __launch_bounds__(256) void router_fused(const bf16_t* __restrict__ x
 template <int KMAX>
 static void fused_by_width(const bf16_t* x, const bf16_t* wr3, const float* b_r, int T, int d, int E, int k,
                            float* logits_out, int32_t* expert, float* gate, float* lse, float* part, hipStream_t s) {
-#define SWMOE_RF(EB, S)                                                                                     \
-    hipLaunchKernelGGL((router_fused<EB, S, KMAX>), dim3(router_fused_blocks(T)), dim3(256), 0, s, x, wr3, b_r, T, d, \
-                       E, k, logits_out, expert, gate, lse, part)
+#define SWMOE_RF(EB, S)                                                                                         \
+    do {                                                                                                        \
+        if (E == 16 * (EB))                                                                                     \
+            hipLaunchKernelGGL((router_fused<EB, S, KMAX, true>), dim3(router_fused_blocks(T)), dim3(256), 0, s, x, \
+                               wr3, b_r, T, d, E, k, logits_out, expert, gate, lse, part);                      \
+        else                                                                                                    \
+            hipLaunchKernelGGL((router_fused<EB, S, KMAX, false>), dim3(router_fused_blocks(T)), dim3(256), 0, s,  \
+                               x, wr3, b_r, T, d, E, k, logits_out, expert, gate, lse, part);                   \
+    } while (0)
     if (E <= 16) SWMOE_RF(1, 4);
     else if (E <= 32) SWMOE_RF(2, 4);
     else if (E <= 64) SWMOE_RF(4, 4);
