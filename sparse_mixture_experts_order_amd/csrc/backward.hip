@@ -14,9 +14,10 @@
 //                   dgate_t = <dout_t, y[e, s]> (fp32), one wave per token
 //   transpose_rows  [E][R][S] -> [E][S][Rp] bf16 through 64x64 LDS tiles,
 //                   zero for rows >= valid[e] (the token axis of activations)
-//   router_wgrad    dW_r partial sums over token slices (fp32), then
+//   router_wgrad    dW_r partial sums over token slices (fp32 MFMA), then
 //   router_wgrad_reduce  the slices added in order in fp64
 //   dx_assemble     dx_t = bf16(dout_t + dbuf[e, s] + sum_e dz_te W_r[:, e])
+//                   (dx_assemble_mfma on the fp32 MFMA when E is a multiple of 8)
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -93,44 +94,103 @@ __global__ __launch_bounds__(256) void transpose_rows(const bf16_t* __restrict__
     }
 }
 
-// dW_r partial sums: workgroup (i block, e block, slice) adds
-// x[t, i] dz[t, e] over the slice's tokens, 64 x 64 outputs, 16 per thread.
+// dW_r partial sums on the fp32 MFMA (v_mfma_f32_32x32x2_f32, products and
+// sums in fp32 like the VALU): workgroup (128 rows i of W_r, 128 experts e,
+// one token slice); wave w takes rows 64 (w >> 1) and experts 64 (w & 1) of
+// it, as 2 x 2 blocks of 32.  Per 32-token chunk, x (converted to fp32) and dz
+// are staged in LDS as [token][128] rows (pitch 129 floats: the reads below
+// and the staging writes each hit every bank twice per wave).  MFMA step s (16
+// per chunk) gives the two half waves tokens s and 16 + s: lane l supplies
+// A = x[t][i + (l & 31)] and B = dz[t][e + (l & 31)], so D[i][e] = sum_t
+// x[t][i] dz[t][e].
 constexpr int RW_CHUNK = 32;
+constexpr int RW_TILE = 128;
 __global__ __launch_bounds__(256) void router_wgrad(const bf16_t* __restrict__ x, const float* __restrict__ dz,
                                                     int64_t T, int d, int E, int tps, float* __restrict__ part) {
-    __shared__ __attribute__((aligned(16))) float xs[RW_CHUNK][64];
-    __shared__ __attribute__((aligned(16))) float zs[RW_CHUNK][64];
-    const int i0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
+    __shared__ float xs[RW_CHUNK][RW_TILE + 1];
+    __shared__ float zs[RW_CHUNK][RW_TILE + 1];
+    const int i0 = blockIdx.x * RW_TILE, e0 = blockIdx.y * RW_TILE;
     const int64_t t0 = (int64_t)blockIdx.z * tps;
     const int64_t t1 = min(T, t0 + tps);
-    const int ti = threadIdx.x >> 4, te = threadIdx.x & 15;   // 4 i x 4 e per thread
-    float acc[4][4] = {};
-    for (int64_t tc = t0; tc < t1; tc += RW_CHUNK) {
-        __syncthreads();
-        for (int q = threadIdx.x; q < RW_CHUNK * 64; q += 256) {
-            const int r = q >> 6, c = q & 63;
-            const int64_t t = tc + r;
-            xs[r][c] = (t < t1 && i0 + c < d) ? bf16_to_f32(x[t * d + i0 + c]) : 0.f;
-            zs[r][c] = (t < t1 && e0 + c < E) ? dz[t * E + e0 + c] : 0.f;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l32 = lane & 31, h = lane >> 5;
+    const int wi = (wave >> 1) * 64, we = (wave & 1) * 64;
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
+    // the next chunk's rows are loaded into registers while the MFMAs run, by
+    // buffer loads without branches: x through a descriptor that ends with the
+    // slice (its rows past t1 read as zero, which also cancels whatever dz
+    // rows past t1 hold), dz through one over the whole array (columns past E
+    // only reach outputs that are not stored)
+    const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(x + t0 * d, (uint32_t)((t1 - t0) * d * 2));
+    const __amdgpu_buffer_rsrc_t rz = buffer_rsrc(dz, (uint32_t)(T * E * 4));
+    u32x4 xr[2];
+    u32x4 zr[4];
+    auto load_chunk = [&](int64_t tc) {
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {   // x: 32 rows x 128 columns, 2 x 8 per thread
+            const int q = threadIdx.x + 256 * jj;
+            const int r = q >> 4, c = (q & 15) * 8;
+            xr[jj] = __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)((r * d + i0 + c) * 2),
+                                                           (uint32_t)((tc - t0) * d * 2), 0);
         }
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {   // dz: 32 rows x 128 experts, 4 x 4 per thread
+            const int q = threadIdx.x + 256 * jj;
+            const int r = q >> 5, c = (q & 31) * 4;
+            zr[jj] = __builtin_amdgcn_raw_buffer_load_b128(rz, (uint32_t)((r * E + e0 + c) * 4), (uint32_t)(tc * E * 4),
+                                                           0);
+        }
+    };
+    if (t0 < t1) load_chunk(t0);
+    for (int64_t tc = t0; tc < t1; tc += RW_CHUNK) {
+        __syncthreads();   // the previous chunk's reads are done
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int q = threadIdx.x + 256 * jj;
+            const int r = q >> 4, c = (q & 15) * 8;
+            const uint32_t w4[4] = {xr[jj][0], xr[jj][1], xr[jj][2], xr[jj][3]};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                xs[r][c + 2 * j] = bf16_to_f32(w4[j] & 0xffffu);
+                xs[r][c + 2 * j + 1] = bf16_to_f32(w4[j] >> 16);
+            }
+        }
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int q = threadIdx.x + 256 * jj;
+            const int r = q >> 5, c = (q & 31) * 4;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) zs[r][c + j] = __uint_as_float(zr[jj][j]);
+        }
+        if (tc + RW_CHUNK < t1) load_chunk(tc + RW_CHUNK);
         __syncthreads();
-#pragma unroll 8
-        for (int r = 0; r < RW_CHUNK; ++r) {
-            const f32x4 xv = *(const f32x4*)&xs[r][ti * 4];
-            const f32x4 zv = *(const f32x4*)&zs[r][te * 4];
 #pragma unroll
-            for (int a = 0; a < 4; ++a)
-#pragma unroll
-                for (int b = 0; b < 4; ++b) acc[a][b] = fmaf(xv[a], zv[b], acc[a][b]);
+        for (int st = 0; st < RW_CHUNK / 2; ++st) {
+            const float a0 = xs[h * 16 + st][wi + l32], a1 = xs[h * 16 + st][wi + 32 + l32];
+            const float b0 = zs[h * 16 + st][we + l32], b1 = zs[h * 16 + st][we + 32 + l32];
+            acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
+            acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
+            acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
+            acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
         }
     }
     float* p = part + (size_t)blockIdx.z * d * E;
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int i = i0 + ti * 4 + a, e = e0 + te * 4 + b;
-            if (i < d && e < E) p[(size_t)i * E + e] = acc[a][b];
+        for (int b = 0; b < 2; ++b) {
+            const int e = e0 + we + 32 * b + l32;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int row = i0 + wi + 32 * a + 8 * (i >> 2) + 4 * h + (i & 3);
+                if (row < d && e < E) p[(size_t)row * E + e] = acc[a][b][i];
+            }
         }
 }
 
@@ -194,6 +254,126 @@ __global__ __launch_bounds__(256) void dx_assemble(const bf16_t* __restrict__ do
     }
 }
 
+// dx on the fp32 MFMA (E a multiple of 8, w_r and dz 16-byte aligned, d a
+// multiple of 128): workgroup = 128 columns i x 128 tokens, wave w = columns
+// 64 (w >> 1) x tokens 64 (w & 1) as 2 x 2 blocks of 32.  A = W_r rows (i,
+// K = e), B = dz^T (K = e, column = token): half wave h takes the experts
+// [h E/2, (h + 1) E/2), one per MFMA step, so a lane reads consecutive floats
+// of W_r and dz rows (16-byte loads, 16 experts at a time) and each loaded
+// value feeds two MFMAs.  In a result block lane l holds token l & 31 and
+// columns {0-3, 8-11, 16-19, 24-27} (+4 for h = 1); one v_permlane32_swap per
+// register pair turns these into two runs of 8 consecutive columns, so dout,
+// dbuf and dx move 16 or 32 bytes at a time.  dx = bf16(dout + sum_e dz W_r +
+// dbuf[e*, s]) as in dx_assemble.
+__global__ __launch_bounds__(256) void dx_assemble_mfma(const bf16_t* __restrict__ dout,
+                                                        const float* __restrict__ dbuf,
+                                                        const int32_t* __restrict__ expert,
+                                                        const int32_t* __restrict__ position,
+                                                        const uint8_t* __restrict__ keep,
+                                                        const float* __restrict__ dz, const float* __restrict__ w_r,
+                                                        int64_t T, int d, int E, int C, bf16_t* __restrict__ dx) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l32 = lane & 31, h = lane >> 5;
+    const int i0 = blockIdx.x * 128 + (wave >> 1) * 64;
+    const int64_t t0 = (int64_t)blockIdx.y * 128 + (wave & 1) * 64;
+    const int Eh = E / 2;
+    const float* arow[2];
+    const float* brow[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        arow[q] = w_r + (size_t)(i0 + 32 * q + l32) * E + h * Eh;
+        brow[q] = dz + min(t0 + 32 * q + l32, T - 1) * E + h * Eh;   // rows past T are not stored
+    }
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
+    // 16 experts per chunk, the next chunk's loads in flight during the MFMAs
+    float av[2][2][16], bv[2][2][16];
+    auto load_chunk = [&](int e0, float (&a)[2][16], float (&b)[2][16]) {
+        const int n = min(16, Eh - e0);   // a multiple of 4
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                f32x4 a4 = f32x4{0.f, 0.f, 0.f, 0.f}, b4 = a4;
+                if (4 * c < n) {
+                    a4 = *(const f32x4*)(arow[q] + e0 + 4 * c);
+                    b4 = *(const f32x4*)(brow[q] + e0 + 4 * c);
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    a[q][4 * c + j] = a4[j];
+                    b[q][4 * c + j] = b4[j];
+                }
+            }
+    };
+    auto mfma_chunk = [&](const float (&a)[2][16], const float (&b)[2][16]) {
+#pragma unroll
+        for (int st = 0; st < 16; ++st)
+#pragma unroll
+            for (int x0 = 0; x0 < 2; ++x0)
+#pragma unroll
+                for (int y0 = 0; y0 < 2; ++y0)
+                    acc[x0][y0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[x0][st], b[y0][st], acc[x0][y0], 0, 0, 0);
+    };
+    load_chunk(0, av[0], bv[0]);
+    for (int e0 = 0; e0 < Eh; e0 += 32) {
+        if (e0 + 16 < Eh) load_chunk(e0 + 16, av[1], bv[1]);
+        mfma_chunk(av[0], bv[0]);
+        if (e0 + 16 < Eh) {
+            if (e0 + 32 < Eh) load_chunk(e0 + 32, av[0], bv[0]);
+            mfma_chunk(av[1], bv[1]);
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        // runs of 8 columns: swap rows 8-11 of half 0 with rows 4-7 of half 1 (and 24-27 with 20-23)
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int pr = 0; pr < 2; ++pr) {
+                    const auto sw = __builtin_amdgcn_permlane32_swap(
+                        __float_as_uint(acc[a][b][8 * pr + i]), __float_as_uint(acc[a][b][8 * pr + 4 + i]), false,
+                        false);
+                    acc[a][b][8 * pr + i] = __uint_as_float(sw[0]);
+                    acc[a][b][8 * pr + 4 + i] = __uint_as_float(sw[1]);
+                }
+        const int64_t t = t0 + 32 * b + l32;
+        if (t >= T) continue;
+        const int e = expert[t], pos = position[t];
+        const bool kept = keep[t] && e >= 0 && e < E && pos >= 0 && pos < C;
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int run = 0; run < 2; ++run) {
+                const int i = i0 + 32 * a + 16 * run + 8 * h;
+                const uint4 dv = *(const uint4*)(dout + t * d + i);
+                f32x4 b0 = f32x4{0.f, 0.f, 0.f, 0.f}, b1 = b0;
+                if (kept) {
+                    const float* br = dbuf + ((size_t)e * C + pos) * d + i;
+                    b0 = *(const f32x4*)br;
+                    b1 = *(const f32x4*)(br + 4);
+                }
+                const uint32_t dw[4] = {dv.x, dv.y, dv.z, dv.w};
+                const float bb[8] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+                uint32_t o[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float v0 = (bf16_to_f32(dw[j] & 0xffffu) + acc[a][b][8 * run + 2 * j]) + bb[2 * j];
+                    const float v1 = (bf16_to_f32(dw[j] >> 16) + acc[a][b][8 * run + 2 * j + 1]) + bb[2 * j + 1];
+                    o[j] = bf16_rne(v0) | (bf16_rne(v1) << 16);
+                }
+                *(uint4*)(dx + t * d + i) = make_uint4(o[0], o[1], o[2], o[3]);
+            }
+    }
+}
+
 __global__ __launch_bounds__(256) void fill_zero(float* __restrict__ p, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i < n) p[i] = 0.f;
@@ -241,8 +421,8 @@ hipError_t launch_router_wgrad(const bf16_t* x, const float* dz, int64_t T, int 
     int tps = (int)((T + slices - 1) / slices);
     tps = (tps + RW_CHUNK - 1) / RW_CHUNK * RW_CHUNK;
     const int used = (int)((T + tps - 1) / tps);
-    hipLaunchKernelGGL(router_wgrad, dim3((d + 63) / 64, (E + 63) / 64, used), dim3(256), 0, s, x, dz, T, d, E, tps,
-                       part);
+    hipLaunchKernelGGL(router_wgrad, dim3((d + RW_TILE - 1) / RW_TILE, (E + RW_TILE - 1) / RW_TILE, used), dim3(256), 0,
+                       s, x, dz, T, d, E, tps, part);
     hipLaunchKernelGGL(router_wgrad_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part, used, n, dw_r);
     return hipGetLastError();
 }
@@ -251,8 +431,13 @@ hipError_t launch_dx_assemble(const bf16_t* dout, const float* dbuf, const int32
                               const uint8_t* keep, const float* dz, const float* w_r, int64_t T, int d, int E, int C,
                               bf16_t* dx, hipStream_t s) {
     if (T == 0) return hipSuccess;
-    hipLaunchKernelGGL(dx_assemble, dim3(d / 64, (unsigned)((T + 63) / 64)), dim3(256), 0, s, dout, dbuf, expert,
-                       position, keep, dz, w_r, T, d, E, C, dx);
+    // the MFMA kernel reads w_r and dz rows 16 bytes at a time
+    if (E % 8 == 0 && d % 128 == 0 && ((uintptr_t)w_r | (uintptr_t)dz) % 16 == 0)
+        hipLaunchKernelGGL(dx_assemble_mfma, dim3(d / 128, (unsigned)((T + 127) / 128)), dim3(256), 0, s, dout, dbuf,
+                           expert, position, keep, dz, w_r, T, d, E, C, dx);
+    else
+        hipLaunchKernelGGL(dx_assemble, dim3(d / 64, (unsigned)((T + 63) / 64)), dim3(256), 0, s, dout, dbuf, expert,
+                           position, keep, dz, w_r, T, d, E, C, dx);
     return hipGetLastError();
 }
 
