@@ -104,7 +104,7 @@ __device__ __forceinline__ void ffn_store_tile_direct(f32x16 (&acc)[NBW][TOKB], 
                                                       const bf16_t* mask, const FfnCombine& cb, int C, int N,
                                                       int wave, int l32, int half) {
     constexpr int NWG = WAVES * 32 * NBW;
-    constexpr bool RUNS = MODE == OUT_RELU_BF16 || MODE == OUT_COMBINE;
+    constexpr bool RUNS = MODE == OUT_RELU_BF16 || MODE == OUT_COMBINE || MODE == OUT_MASK_BF16;
     if constexpr (RUNS) {
         // lanes l and l ^ 32 hold the same token, so the swap is done by whole pairs
 #pragma unroll
@@ -196,6 +196,54 @@ __device__ __forceinline__ void ffn_store_tile_direct(f32x16 (&acc)[NBW][TOKB], 
         }
         return;
     }
+    if constexpr (MODE == OUT_MASK_BF16) {
+        // keep the elements whose saved activation is non-zero.  Every mask
+        // run is loaded before the first store (a load issued after a store
+        // waits for that store too), without branches: rows and columns past
+        // the tile read the last valid run, whose result is never stored.
+        u32x4 mk[NBW][TOKB][2];
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+            for (int tb = 0; tb < TOKB; ++tb)
+#pragma unroll
+                for (int run = 0; run < 2; ++run) {
+                    const int r = min(tb * 32 + l32, t.nv - 1);
+                    const int n = min(n0 + nb * 32 + run * 16 + half * 8, N - 8);
+                    mk[nb][tb][run] = *(const u32x4*)(mask + ((size_t)t.e * C + t.tok_base + r) * N + n);
+                }
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+            for (int tb = 0; tb < TOKB; ++tb)
+#pragma unroll
+                for (int run = 0; run < 2; ++run) {
+                    const f32x16& a = acc[nb][tb];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t m = mk[nb][tb][run][j];
+                        const uint32_t keep = ((m & 0x7fffu) ? 0xffffu : 0u) | ((m & 0x7fff0000u) ? 0xffff0000u : 0u);
+                        mk[nb][tb][run][j] =
+                            (bf16_rne(a[8 * run + 2 * j]) | (bf16_rne(a[8 * run + 2 * j + 1]) << 16)) & keep;
+                    }
+                    // computed here, not inside each store's branch (one wait for the loads)
+                    asm volatile("" : "+v"(mk[nb][tb][run]));
+                }
+#pragma unroll
+        for (int tb = 0; tb < TOKB; ++tb) {
+            const int r = tb * 32 + l32;
+            if (r >= t.nv) continue;
+            const size_t row = ((size_t)t.e * C + t.tok_base + r) * N;
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+                for (int run = 0; run < 2; ++run) {
+                    const int n = n0 + nb * 32 + run * 16 + half * 8;
+                    if (n < N) *(u32x4*)((bf16_t*)out + row + n) = mk[nb][tb][run];
+                }
+        }
+        return;
+    }
 #pragma unroll
     for (int tb = 0; tb < TOKB; ++tb) {
         const int r = tb * 32 + l32;
@@ -221,17 +269,7 @@ __device__ __forceinline__ void ffn_store_tile_direct(f32x16 (&acc)[NBW][TOKB], 
                 for (int q = 0; q < 4; ++q) {
                     const int n = n0 + nb * 32 + q * 8 + half * 4;
                     if (n >= N) continue;
-                    if constexpr (MODE == OUT_F32) {
-                        *(f32x4*)((float*)out + row + n) =
-                            f32x4{a[4 * q + 0], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
-                    } else {   // OUT_MASK_BF16: keep the elements whose saved activation is non-zero
-                        uint2 o = make_uint2(bf16_rne(a[4 * q + 0]) | (bf16_rne(a[4 * q + 1]) << 16),
-                                             bf16_rne(a[4 * q + 2]) | (bf16_rne(a[4 * q + 3]) << 16));
-                        const uint2 m = *(const uint2*)(mask + row + n);
-                        o.x &= ((m.x & 0x7fffu) ? 0xffffu : 0u) | ((m.x & 0x7fff0000u) ? 0xffff0000u : 0u);
-                        o.y &= ((m.y & 0x7fffu) ? 0xffffu : 0u) | ((m.y & 0x7fff0000u) ? 0xffff0000u : 0u);
-                        *(uint2*)((bf16_t*)out + row + n) = o;
-                    }
+                    *(f32x4*)((float*)out + row + n) = f32x4{a[4 * q + 0], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
                 }
             }
         }
@@ -557,14 +595,45 @@ __device__ __forceinline__ int dma_slot(int r, int c) {
     return KC == 64 ? (c ^ (r & 7)) : (c ^ ((r >> 1) & 3));
 }
 
+// Two transposed reads of a K-major stage (rows of rbw bytes): this lane's
+// piece is row k (the group's rows k0 + lane / 4 of 16) and 4 weights from
+// column col; the group's lanes get rows k0 .. k0 + 3 (first read) and
+// k0 + 4 .. k0 + 7 (second) of their own column.  Slot c of row k sits at
+// c ^ 2 (k & 3).
+__device__ __forceinline__ bf16x8 wkm_fragment(const char* st, int rbw, int k, int col) {
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    const int slot = col >> 3, half = (col >> 2) & 1;
+    const int k2 = k + 4;
+    const char* p1 = st + k * rbw + ((slot ^ (2 * (k & 3))) << 4) + half * 8;
+    const char* p2 = st + k2 * rbw + ((slot ^ (2 * (k2 & 3))) << 4) + half * 8;
+    v4s lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
+#if defined(__HIP_DEVICE_COMPILE__)
+    lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p1);
+    hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p2);
+#endif
+    const u32x4 w = u32x4{(uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
+                          (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
+                          (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
+                          (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)};
+    return as_bf16x8(w);
+}
+
 // With a_rows the token rows are gathered straight from A = x [T, K]: row s of
 // expert e is x[a_rows[e * C + s]] (a_bytes = T K 2, the descriptor's byte
 // count; a_rows has 128 entries of padding past E C).  The row map is read with uniform (scalar) loads when a tile starts,
 // so waiting for it never waits for the copies in flight; rows past the tile's
 // valid count point past the descriptor and read as zero.
-template <int TOKB, int NBW, int WAVES, int MODE, int S, int KC>
+// With WKM the weights are stored K-major, [E, K, N] (the backward reads W1
+// and W2 as stored): a chunk's stage holds KC rows k of NWG weights each, the
+// 16-byte slot c of row k at c ^ 2 (k & 3), and an MFMA fragment (8
+// consecutive k of one weight row n per lane) is two ds_read_b64_tr_b16: in
+// each 16-lane group, lane 4 j + a reads 4 weights of row k0 + j at columns
+// n0 + 4 a .. + 3, and lane i gets the 4 rows k0 .. k0 + 3 of column n0 + i.
+// The swizzle puts the 4 rows x 2 slots of a group's read on 8 different slots
+// (all 32 banks).
+template <int TOKB, int NBW, int WAVES, int MODE, int S, int KC, bool WKM = false>
 __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __restrict__ A,   // [E, C, K] or x
-                                                              const bf16_t* __restrict__ W,   // [E, N, K]
+                                                              const bf16_t* __restrict__ W,   // [E, N, K] or [E, K, N]
                                                               const int32_t* __restrict__ pre,
                                                               const int4* __restrict__ ttab,
                                                               void* __restrict__ out,
@@ -604,10 +673,18 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
 
     // lane offsets of the copies (row RPC q + lane / NCOL, swizzled 16-byte column)
     uint32_t wvo[WPW], avo[APW];
+    constexpr int RBW = NWG * 2;                            // bytes per K-major stage row
+    static_assert(!WKM || (KC == 64 && (NWG / 8) % 8 == 0), "K-major stages: 64-wide chunks, whole slot groups");
 #pragma unroll
     for (int i = 0; i < WPW; ++i) {
-        const int r = RPC * (wave * WPW + i) + lane / NCOL;
-        wvo[i] = (uint32_t)r * K * 2 + (dma_slot<KC>(r, lane % NCOL) << 4);
+        if constexpr (WKM) {
+            const int lin = (wave * WPW + i) * 1024 + lane * 16;   // this lane's 16 bytes of the stage
+            const int k = lin / RBW, slot = (lin - k * RBW) >> 4;
+            wvo[i] = (uint32_t)k * N * 2 + ((slot ^ (2 * (k & 3))) << 4);
+        } else {
+            const int r = RPC * (wave * WPW + i) + lane / NCOL;
+            wvo[i] = (uint32_t)r * K * 2 + (dma_slot<KC>(r, lane % NCOL) << 4);
+        }
     }
 #pragma unroll
     for (int i = 0; i < APW; ++i) {
@@ -665,10 +742,17 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
             a_n = (uint32_t)(t.nv * K * 2);
         }
         const int r0 = t.nt * NWG;                                   // rows past N read zeros
-        const uint64_t wb = (uint64_t)(uintptr_t)((const char*)W + ((size_t)t.e * N + r0) * K * 2);
-        w_lo = (uint32_t)wb;
-        w_hi = (uint32_t)(wb >> 32);
-        w_n = (uint32_t)((N - r0) * K * 2);
+        if constexpr (WKM) {   // columns past N read the next row: they only reach outputs past N, never stored
+            const uint64_t wb = (uint64_t)(uintptr_t)((const char*)W + ((size_t)t.e * K * N + r0) * 2);
+            w_lo = (uint32_t)wb;
+            w_hi = (uint32_t)(wb >> 32);
+            w_n = (uint32_t)(((size_t)K * N - r0) * 2);
+        } else {
+            const uint64_t wb = (uint64_t)(uintptr_t)((const char*)W + ((size_t)t.e * N + r0) * K * 2);
+            w_lo = (uint32_t)wb;
+            w_hi = (uint32_t)(wb >> 32);
+            w_n = (uint32_t)((N - r0) * K * 2);
+        }
     };
     // copies of chunk position f (clamped to the last one) into stage `stg`
     auto issue = [&](int f, int stg) {
@@ -678,7 +762,8 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
         const __amdgpu_buffer_rsrc_t rs_a = rsrc(a_lo, a_hi, a_n), rs_w = rsrc(w_lo, w_hi, w_n);
         char* sb = lds + stg * STAGE;
 #pragma unroll
-        for (int i = 0; i < WPW; ++i) copy_to_lds(rs_w, sb + (wave * WPW + i) * 1024, wvo[i], kf * RB);
+        for (int i = 0; i < WPW; ++i)
+            copy_to_lds(rs_w, sb + (wave * WPW + i) * 1024, wvo[i], WKM ? (uint32_t)kf * KC * N * 2 : kf * RB);
 #pragma unroll
         for (int i = 0; i < APW; ++i) copy_to_lds(rs_a, sb + W_STAGE + (wave * APW + i) * 1024, avo[i], kf * RB);
     };
@@ -717,8 +802,16 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
                     }
 #pragma unroll
                     for (int nb = 0; nb < NBW; ++nb) {
-                        const int r = wave * 32 * NBW + nb * 32 + l32;
-                        const bf16x8 wa = as_bf16x8(*(const u32x4*)(sw + r * RB + (dma_slot<KC>(r, c) << 4)));
+                        bf16x8 wa;
+                        if constexpr (WKM) {
+                            // rows k = 8 c .. 8 c + 7 of columns wave * 32 NBW + 32 nb + (l & 31)
+                            const int m = lane & 15;
+                            const int col = wave * 32 * NBW + nb * 32 + 16 * ((lane >> 4) & 1) + 4 * (m & 3);
+                            wa = wkm_fragment(sw, RBW, 8 * c + (m >> 2), col);
+                        } else {
+                            const int r = wave * 32 * NBW + nb * 32 + l32;
+                            wa = as_bf16x8(*(const u32x4*)(sw + r * RB + (dma_slot<KC>(r, c) << 4)));
+                        }
 #pragma unroll
                         for (int tb = 0; tb < TOKB; ++tb)
                             acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, bt[tb], acc[nb][tb], 0, 0, 0);
@@ -777,7 +870,7 @@ hipError_t launch_expert_gemm_t(const bf16_t* A, const bf16_t* W, const int32_t*
     return hipGetLastError();
 }
 
-template <int TOKB, int NBW, int WAVES, int MODE, int S, int KC>
+template <int TOKB, int NBW, int WAVES, int MODE, int S, int KC, bool WKM = false>
 hipError_t launch_expert_gemm_dma_t(const bf16_t* A, const bf16_t* W, const int32_t* pre, const int4* ttab, void* out,
                                     const bf16_t* mask, const FfnCombine& cb, int E, int C, int K, int N,
                                     hipStream_t s, const int32_t* a_rows = nullptr, uint32_t a_bytes = 0) {
@@ -787,7 +880,7 @@ hipError_t launch_expert_gemm_dma_t(const bf16_t* A, const bf16_t* W, const int3
     const int64_t max_tiles = (int64_t)E * n_tiles * tok_tiles;
     int64_t grid = std::min<int64_t>((int64_t)device_cus(), (max_tiles + 7) / 8 * 8);   // one workgroup per CU
     grid = std::max<int64_t>(8, grid / 8 * 8);
-    hipLaunchKernelGGL((expert_gemm_dma<TOKB, NBW, WAVES, MODE, S, KC>), dim3((unsigned)grid), dim3(64 * WAVES), 0, s, A,
+    hipLaunchKernelGGL((expert_gemm_dma<TOKB, NBW, WAVES, MODE, S, KC, WKM>), dim3((unsigned)grid), dim3(64 * WAVES), 0, s, A,
                        W, pre, ttab, out, mask, cb, a_rows, a_bytes, E, C, K, N, n_tiles);
     return hipGetLastError();
 }
@@ -880,10 +973,22 @@ static bool narrow_tiles(int E, int C, int N) {
 template <int MODE>
 static hipError_t launch_expert_gemm_kmajor(const bf16_t* A, const bf16_t* W, const int32_t* pre, const int4* ttab,
                                             void* out, const bf16_t* mask, int E, int C, int K, int N, hipStream_t s) {
-    if (C > 64) {
-        if (narrow_tiles(E, C, N))
-            return launch_expert_gemm_t<4, 1, 6, 3, MODE, 256, true>(A, W, pre, ttab, out, mask, E, C, K, N, s);
-        return launch_expert_gemm_t<4, 1, 8, 4, MODE, 256, true>(A, W, pre, ttab, out, mask, E, C, K, N, s);
+    if (C > 64) {   // the direct-to-LDS kernel with transposed fragment reads
+        const FfnCombine none{};
+        switch (dma_tile_width(E, C, N)) {
+            case 512:
+                return launch_expert_gemm_dma_t<4, 2, 8, MODE, 2, 64, true>(A, W, pre, ttab, out, mask, none, E, C, K, N,
+                                                                            s);
+            case 384:
+                return launch_expert_gemm_dma_t<4, 2, 6, MODE, 2, 64, true>(A, W, pre, ttab, out, mask, none, E, C, K, N,
+                                                                            s);
+            case 256:
+                return launch_expert_gemm_dma_t<4, 1, 8, MODE, 3, 64, true>(A, W, pre, ttab, out, mask, none, E, C, K, N,
+                                                                            s);
+            default:
+                return launch_expert_gemm_dma_t<4, 1, 6, MODE, 3, 64, true>(A, W, pre, ttab, out, mask, none, E, C, K, N,
+                                                                            s);
+        }
     }
     if (C > 32) return launch_expert_gemm_t<2, 2, 4, 3, MODE, 512, true>(A, W, pre, ttab, out, mask, E, C, K, N, s);
     return launch_expert_gemm_t<1, 2, 4, 4, MODE, 512, true>(A, W, pre, ttab, out, mask, E, C, K, N, s);
