@@ -184,8 +184,7 @@ switch_status validate_route(const RouteArgs& a, const void* ws, size_t ws_bytes
         ALIGNED16(a.x); ALIGNED4(a.w_r); ALIGNED4(a.b_r);
         REQUIRE(a.d >= 1, "d must be >= 1 (got %d)", a.d);
         SUPPORT(a.d % 32 == 0, "d must be a multiple of 32 for the router GEMM (got %d)", a.d);
-        SUPPORT(!route_fused(a.E) || (int64_t)6 * a.E * a.d < (int64_t(1) << 31),
-                "the split router weights (3*E*d bf16) must be < 2 GiB");
+        SUPPORT((int64_t)6 * a.E * a.d < (int64_t(1) << 31), "the split router weights (3*E*d bf16) must be < 2 GiB");
     }
     REQUIRE(a.logits_in != nullptr || !tok || a.x != nullptr, "x must not be NULL");
     const size_t need = a.logits_in ? route_ws(a.T, 0, a.E, true) : route_ws(a.T, a.d, a.E, a.logits_out != nullptr);
@@ -216,7 +215,7 @@ switch_status run_route(const RouteArgs& a, void* ws, hipStream_t s) {
     const float* logits = a.logits_in;
     if (!logits) {
         bf16_t* wr3 = c.take<bf16_t>((size_t)3 * a.d * E);
-        LAUNCH(K_SPLIT, "split_router_weights", s, launch_split_router_weights(a.w_r, wr3, a.d, E, route_fused(E), s));
+        LAUNCH(K_SPLIT, "split_router_weights", s, launch_split_router_weights(a.w_r, wr3, a.d, E, s));
         if (route_fused(E)) {
             float* part = c.take<float>(route_parts(T, E));
             const int nblk = T > 0 ? router_fused_blocks(T) : 0;

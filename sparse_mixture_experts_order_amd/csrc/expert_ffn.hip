@@ -124,65 +124,58 @@ __device__ __forceinline__ void ffn_store_tile_direct(f32x16 (&acc)[NBW][TOKB], 
     }
     const int n0 = t.nt * NWG + wave * 32 * NBW;   // first column of this wave
     if constexpr (MODE == OUT_COMBINE) {
-        // every load of the epilogue is issued before its first store (two
-        // round trips: the token of each row, then its gate and residual runs)
+        // per 32-column block, every load is issued before the block's first
+        // store (the token of each row and its gate once, then the block's
+        // residual runs); the output runs replace the residual runs in place
         int tok[TOKB];
         float g[TOKB];
-        u32x4 rr[TOKB][NBW][2];
 #pragma unroll
         for (int tb = 0; tb < TOKB; ++tb) {
             const int r = tb * 32 + l32;
             tok[tb] = r < t.nv ? cb.slot_token[(size_t)t.e * C + t.tok_base + r] : -1;
         }
 #pragma unroll
-        for (int tb = 0; tb < TOKB; ++tb) {
-            g[tb] = tok[tb] >= 0 ? cb.gate[tok[tb]] : 0.f;
+        for (int tb = 0; tb < TOKB; ++tb) g[tb] = tok[tb] >= 0 ? cb.gate[tok[tb]] : 0.f;
 #pragma unroll
-            for (int nb = 0; nb < NBW; ++nb)
+        for (int nb = 0; nb < NBW; ++nb) {
+            u32x4 rr[TOKB][2];
+#pragma unroll
+            for (int tb = 0; tb < TOKB; ++tb)
 #pragma unroll
                 for (int run = 0; run < 2; ++run) {
                     const int n = n0 + nb * 32 + run * 16 + half * 8;
-                    rr[tb][nb][run] = (tok[tb] >= 0 && cb.residual && n < N)
-                                          ? *(const u32x4*)(cb.residual + (size_t)tok[tb] * N + n)
-                                          : u32x4{0u, 0u, 0u, 0u};
+                    rr[tb][run] = (tok[tb] >= 0 && cb.residual && n < N)
+                                      ? *(const u32x4*)(cb.residual + (size_t)tok[tb] * N + n)
+                                      : u32x4{0u, 0u, 0u, 0u};
                 }
-        }
-        // all the arithmetic (one wait for the loads), then all the stores
-        u32x4 ov[TOKB][NBW][2];
 #pragma unroll
-        for (int tb = 0; tb < TOKB; ++tb)
-#pragma unroll
-            for (int nb = 0; nb < NBW; ++nb)
+            for (int tb = 0; tb < TOKB; ++tb)
 #pragma unroll
                 for (int run = 0; run < 2; ++run) {
                     const f32x16& a = acc[nb][tb];
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        const uint32_t res = rr[tb][nb][run][j];
+                        const uint32_t res = rr[tb][run][j];
                         const float o0 = fmaf(g[tb], a[8 * run + 2 * j], bf16_to_f32(res & 0xffffu));
                         const float o1 = fmaf(g[tb], a[8 * run + 2 * j + 1], bf16_to_f32(res >> 16));
-                        ov[tb][nb][run][j] = bf16_rne(o0) | (bf16_rne(o1) << 16);
+                        rr[tb][run][j] = bf16_rne(o0) | (bf16_rne(o1) << 16);
                     }
                 }
 #pragma unroll
-        for (int tb = 0; tb < TOKB; ++tb) {
-            if (tok[tb] < 0) continue;
-            const size_t orow = (size_t)tok[tb] * N;
-#pragma unroll
-            for (int nb = 0; nb < NBW; ++nb)
+            for (int tb = 0; tb < TOKB; ++tb) {
+                if (tok[tb] < 0) continue;
+                const size_t orow = (size_t)tok[tb] * N;
 #pragma unroll
                 for (int run = 0; run < 2; ++run) {
                     const int n = n0 + nb * 32 + run * 16 + half * 8;
-                    if (n < N) *(u32x4*)(cb.out + orow + n) = ov[tb][nb][run];
+                    if (n < N) *(u32x4*)(cb.out + orow + n) = rr[tb][run];
                 }
-        }
-        if (cb.y) {   // after every residual use: stores count in the same counter as the loads
+            }
+            if (cb.y) {   // after the block's residual use: stores count in the same counter as the loads
 #pragma unroll
-            for (int tb = 0; tb < TOKB; ++tb) {
-                if (tok[tb] < 0) continue;
-                const size_t row = ((size_t)t.e * C + t.tok_base + tb * 32 + l32) * N;
-#pragma unroll
-                for (int nb = 0; nb < NBW; ++nb)
+                for (int tb = 0; tb < TOKB; ++tb) {
+                    if (tok[tb] < 0) continue;
+                    const size_t row = ((size_t)t.e * C + t.tok_base + tb * 32 + l32) * N;
 #pragma unroll
                     for (int run = 0; run < 2; ++run) {
                         const int n = n0 + nb * 32 + run * 16 + half * 8;
@@ -192,6 +185,7 @@ __device__ __forceinline__ void ffn_store_tile_direct(f32x16 (&acc)[NBW][TOKB], 
                         *(f32x4*)(cb.y + row + n + 4) =
                             f32x4{a[8 * run + 4], a[8 * run + 5], a[8 * run + 6], a[8 * run + 7]};
                     }
+                }
             }
         }
         return;

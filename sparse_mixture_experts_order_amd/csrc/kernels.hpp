@@ -11,7 +11,7 @@ typedef uint16_t bf16_t;
 struct AuxStatsArgs;   // common.hpp
 
 // route.hip
-hipError_t launch_split_router_weights(const float* w_r, bf16_t* wr3, int d, int E, bool chunked, hipStream_t s);
+hipError_t launch_split_router_weights(const float* w_r, bf16_t* wr3, int d, int E, hipStream_t s);
 hipError_t launch_router_gemm(const bf16_t* x, const bf16_t* wr3, const float* b_r, float* logits, int T, int d,
                               int E, hipStream_t s);
 constexpr int kMaxTopK = 4;             // largest k the routers support
@@ -24,7 +24,7 @@ int column_sum_slices(int64_t rows);
 hipError_t launch_column_sum(const float* a, int rows, int E, float* slices, float* out, hipStream_t s);
 constexpr int kRouterFusedMaxE = 256;
 int router_fused_blocks(int64_t T);     // one partial row per 64 tokens
-// wr3 in the chunked layout [d / 32][3][E][32] (split_router_weights, chunked)
+// wr3 in the layout [d / 32][3][E][32] of split_router_weights
 hipError_t launch_router_fused(const bf16_t* x, const bf16_t* wr3, const float* b_r, int T, int d, int E, int k,
                                float* logits_out, int32_t* expert, float* gate, float* lse, float* part,
                                hipStream_t s);

@@ -17,13 +17,12 @@
 
 namespace swmoe {
 
-// w_r [d, E] fp32 -> the three bf16 terms, expert-major so that an MFMA
-// operand row (one expert, 8 consecutive k) is 16 contiguous bytes:
-//   plain   [3][E][d]                  (the two-pass router GEMM)
-//   chunked [d / 32][3][E][32]         (the fused router: the weight rows of
-//                                       one 32-wide K stage are one block)
+// w_r [d, E] fp32 -> the three bf16 terms, one K stage of 32 per block,
+// [d / 32][3][E][32], so that an MFMA operand row (one expert, 8 consecutive
+// k) is 16 contiguous bytes and the weight rows of one stage are one block
+// (d is a multiple of 32).
 __global__ __launch_bounds__(256) void split_router_weights(const float* __restrict__ w_r,
-                                                            bf16_t* __restrict__ wr3, int d, int E, int chunked) {
+                                                            bf16_t* __restrict__ wr3, int d, int E) {
     __shared__ float tile[32][33];
     const int e0 = blockIdx.x * 32, k0 = blockIdx.y * 32;
     const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
@@ -32,7 +31,6 @@ __global__ __launch_bounds__(256) void split_router_weights(const float* __restr
         tile[r][tx] = (k < d && e < E) ? w_r[(size_t)k * E + e] : 0.f;
     }
     __syncthreads();
-    const size_t plane = (size_t)E * d;
     for (int r = ty; r < 32; r += 8) {
         int e = e0 + r, k = k0 + tx;
         if (e < E && k < d) {
@@ -42,88 +40,139 @@ __global__ __launch_bounds__(256) void split_router_weights(const float* __restr
             uint32_t mid = bf16_rne(r1);
             float r2 = r1 - bf16_to_f32(mid);
             uint32_t lo = bf16_rne(r2);
-            if (chunked) {   // d is a multiple of 32 here: the tile is one K stage
-                const size_t o = (size_t)blockIdx.y * 3 * E * 32 + (size_t)e * 32 + tx;
-                wr3[o] = (bf16_t)hi;
-                wr3[o + (size_t)E * 32] = (bf16_t)mid;
-                wr3[o + (size_t)2 * E * 32] = (bf16_t)lo;
-            } else {
-                const size_t o = (size_t)e * d + k;
-                wr3[o] = (bf16_t)hi;
-                wr3[plane + o] = (bf16_t)mid;
-                wr3[2 * plane + o] = (bf16_t)lo;
-            }
+            const size_t o = (size_t)blockIdx.y * 3 * E * 32 + (size_t)e * 32 + tx;
+            wr3[o] = (bf16_t)hi;
+            wr3[o + (size_t)E * 32] = (bf16_t)mid;
+            wr3[o + (size_t)2 * E * 32] = (bf16_t)lo;
         }
     }
 }
 
-// logits[t, e] = sum_k x[t, k] (hi + mid + lo)[e, k] + b[e].
-// v_mfma_f32_16x16x32_bf16 with rows = experts (A operand, from wr3) and
-// columns = tokens (B operand, from x).  A wave owns RT_TB token blocks x
-// RT_EB expert blocks of 16; a workgroup of 4 waves covers 4*16*RT_TB tokens
-// and 16*RT_EB experts.  Operands are loaded straight from global memory
-// (x once per wave; the split weights are shared through L2).
-constexpr int RT_TB = 2, RT_EB = 4;
+// logits[t, e] = sum_k x[t, k] (hi + mid + lo)[e, k] + b[e] for E > 256.
+// A workgroup of 8 waves computes a tile of RG_T = 256 tokens x RG_E = 256
+// experts; wave (wt, we) = (w / 4, w % 4) owns tokens 128 wt .. + 127 and
+// experts 64 we .. + 63 as 4 x 2 blocks of v_mfma_f32_32x32x16_bf16 (A =
+// token rows, B = expert rows), each block taking the lo, mid and hi terms
+// in that order.  Per 32-wide K stage, the 256 token rows and the 3 x 256
+// weight rows (64 bytes each; in the chunked split layout each term's rows of
+// one stage are one contiguous block) go from memory straight into LDS, eight
+// 1 KiB copies per wave (waves 0-1 the token rows, 2-7 the weight terms), the
+// four 16-byte columns of row r at column ^ ((r >> 1) & 3), which makes the
+// 32-row fragment reads free of bank conflicts.  Two stages, one barrier per
+// stage.  Token rows past T read as zero; expert rows past E repeat row E - 1
+// and only reach logits that are never stored.  Tiles are numbered expert-tile-major and dealt XCD-major, so the
+// workgroups of an XCD share one expert tile's weight rows in its L2.
+constexpr int RG_T = 256, RG_E = 256;
+constexpr int RG_STAGE = (RG_T + 3 * RG_E) * 64;   // bytes of one K stage
 
-__global__ __launch_bounds__(256) void router_gemm(const bf16_t* __restrict__ x,
-                                                   const bf16_t* __restrict__ wr3,
-                                                   const float* __restrict__ b_r,
-                                                   float* __restrict__ logits, int T, int d, int E) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int t_base = (blockIdx.x * 4 + wave) * (16 * RT_TB);
-    const int e_base = blockIdx.y * (16 * RT_EB);
-    const int r16 = lane & 15, kq = (lane >> 4) * 8;
-    const size_t plane = (size_t)E * d;
+__global__ __launch_bounds__(512) void router_gemm(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wr3,
+                                                   const float* __restrict__ b_r, float* __restrict__ logits,
+                                                   int T, int d, int E, int n_tt, int n_tiles) {
+    __shared__ __attribute__((aligned(16))) char lds[2 * RG_STAGE];
+    const int tile = xcd_swizzle(blockIdx.x, gridDim.x);
+    if (tile >= n_tiles) return;
+    // (the division runs on the vector unit: readfirstlane keeps the tile, and
+    // so the copies' descriptors, scalar)
+    const int et = __builtin_amdgcn_readfirstlane(tile / n_tt), tt = tile - et * n_tt;
+    const int t0 = tt * RG_T, e0 = et * RG_E;
+    const int lane = threadIdx.x & 63, l32 = lane & 31, hl = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wt = wave >> 2, we = wave & 3;
+    const int nk = d / 32;
 
-    const bf16_t* xrow[RT_TB];
+    // this wave's eight copies: q = 8 wave + i lands at stage + 1 KiB q; lane ->
+    // row 16 (q % 16) + lane / 4 of its 256-row block, LDS column lane % 4
+    const bool tok_rows = wave < 2;
+    const char* base = tok_rows ? (const char*)(x + (size_t)t0 * d) : (const char*)wr3;
+    const uint32_t nbytes = tok_rows ? (uint32_t)min(RG_T, T - t0) * d * 2 : (uint32_t)3 * E * d * 2;
+    const uint32_t kstep = tok_rows ? 64u : (uint32_t)3 * E * 64;   // source bytes per K stage
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(base, nbytes);
+    uint32_t vo[8];
 #pragma unroll
-    for (int tb = 0; tb < RT_TB; ++tb) {
-        int t = min(t_base + tb * 16 + r16, T - 1);
-        xrow[tb] = x + (size_t)t * d + kq;
+    for (int i = 0; i < 8; ++i) {
+        const int q = 8 * wave + i;
+        const int row = 16 * (q & 15) + (lane >> 2);
+        const uint32_t col = (uint32_t)(((lane & 3) ^ ((row >> 1) & 3)) << 4);
+        const int term = (q >> 4) - 1;   // weight copies: q = 16 (1 + term) + row block
+        vo[i] = tok_rows ? (uint32_t)row * d * 2 + col : (uint32_t)(term * E + min(e0 + row, E - 1)) * 64 + col;
     }
-    const bf16_t* wrow[RT_EB];
+    auto issue = [&](int kk, int stg) {
+        char* dst = lds + stg * RG_STAGE + wave * 8 * 1024;
+        const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)kk * kstep);
 #pragma unroll
-    for (int eb = 0; eb < RT_EB; ++eb) {
-        int e = min(e_base + eb * 16 + r16, E - 1);
-        wrow[eb] = wr3 + (size_t)e * d + kq;
-    }
-    f32x4 acc[RT_TB][RT_EB];
-#pragma unroll
-    for (int tb = 0; tb < RT_TB; ++tb)
-#pragma unroll
-        for (int eb = 0; eb < RT_EB; ++eb) acc[tb][eb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < 8; ++i) copy_to_lds(rs, dst + i * 1024, vo[i], so);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
 
-    for (int k0 = 0; k0 < d; k0 += 32) {
-        bf16x8 xb[RT_TB];
+    f32x16 acc[4][2];
 #pragma unroll
-        for (int tb = 0; tb < RT_TB; ++tb) xb[tb] = as_bf16x8(*(const uint4*)(xrow[tb] + k0));
-        bf16x8 wa[3][RT_EB];
+    for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-        for (int j = 0; j < 3; ++j)
+        for (int eb = 0; eb < 2; ++eb)
 #pragma unroll
-            for (int eb = 0; eb < RT_EB; ++eb)
-                wa[j][eb] = as_bf16x8(*(const uint4*)(wrow[eb] + (2 - j) * plane + k0));
-        // small terms first: lo, mid, hi
+            for (int i = 0; i < 16; ++i) acc[tb][eb][i] = 0.f;
+
+    issue(0, 0);
+    int kk = 0;
+    do {   // d >= 32: at least one stage
+        wait_copies<0>();   // this wave's copies of stage kk
+        lds_barrier();      // every wave's, and stage kk - 1 is read out
+        issue(min(kk + 1, nk - 1), (kk + 1) & 1);   // the last stage is fetched twice, never read
+        const char* st = lds + (kk & 1) * RG_STAGE;
 #pragma unroll
-        for (int j = 0; j < 3; ++j)
+        for (int ks = 0; ks < 2; ++ks) {
+            const int c = 2 * ks + hl;   // this lane's 16-byte column of the 64-byte rows
+            bf16x8 a[4], b[3][2];
 #pragma unroll
-            for (int tb = 0; tb < RT_TB; ++tb)
+            for (int tb = 0; tb < 4; ++tb) {
+                const int r = wt * 128 + tb * 32 + l32;
+                a[tb] = as_bf16x8(*(const u32x4*)(st + r * 64 + ((c ^ ((r >> 1) & 3)) << 4)));
+            }
 #pragma unroll
-                for (int eb = 0; eb < RT_EB; ++eb)
-                    acc[tb][eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[j][eb], xb[tb], acc[tb][eb], 0, 0, 0);
-    }
-    // lane holds token column (lane & 15) and expert rows 4*(lane>>4) + 0..3
+            for (int term = 0; term < 3; ++term)
 #pragma unroll
-    for (int tb = 0; tb < RT_TB; ++tb) {
-        int t = t_base + tb * 16 + r16;
-        if (t >= T) continue;
+                for (int eb = 0; eb < 2; ++eb) {
+                    const int r = we * 64 + eb * 32 + l32;
+                    b[term][eb] = as_bf16x8(
+                        *(const u32x4*)(st + (1 + term) * RG_E * 64 + r * 64 + ((c ^ ((r >> 1) & 3)) << 4)));
+                }
 #pragma unroll
-        for (int eb = 0; eb < RT_EB; ++eb) {
-            int e = e_base + eb * 16 + (lane >> 4) * 4;
+            for (int jj = 0; jj < 3; ++jj)   // lo, mid, hi
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (e + i < E) logits[(size_t)t * E + e + i] = acc[tb][eb][i] + (b_r ? b_r[e + i] : 0.f);
+                for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+                    for (int eb = 0; eb < 2; ++eb)
+                        acc[tb][eb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[tb], b[2 - jj][eb], acc[tb][eb], 0, 0, 0);
         }
+    } while (++kk < nk);
+    wait_copies<0>();   // the spare copy of the last stage
+
+    // lane: expert column e0 + 64 we + 32 eb + l32, token rows 8 (i / 4) + 4 hl + i % 4 of
+    // block tb; stores past T (the descriptor's count) or past E (offset past it) are dropped
+    // The descriptor comes from readfirstlane'd words and the offset from a
+    // bitwise select, so the compiler sees no divergence to guard the stores
+    // with.  readfirstlane returns a signed int: each word goes through
+    // uint32_t, or the low word would be sign-extended into the high one.
+    const uint32_t out_bytes = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)min(RG_T, T - t0) * E * 4);
+    const uint64_t ob = (uint64_t)(uintptr_t)(logits + (size_t)t0 * E);
+    const uint32_t ob_lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)ob);
+    const uint32_t ob_hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(ob >> 32));
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(uintptr_t)(((uint64_t)ob_hi << 32) | (uint64_t)ob_lo), (short)0, (int)out_bytes, kBufferWord3);
+#pragma unroll
+    for (int eb = 0; eb < 2; ++eb) {
+        const int e = e0 + we * 64 + eb * 32 + l32;
+        const uint32_t in_e = 0u - (uint32_t)(e < E);
+        const float bias = b_r ? b_r[min(e, E - 1)] : 0.f;
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int row = wt * 128 + tb * 32 + 8 * (i >> 2) + 4 * hl + (i & 3);
+                const uint32_t off = ((((uint32_t)row * E + e) * 4) & in_e) | (out_bytes & ~in_e);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[tb][eb][i] + bias), ro, off, 0, 0);
+            }
     }
 }
 
@@ -248,16 +297,18 @@ __global__ __launch_bounds__(1024) void router_reduce(const float* __restrict__ 
 }
 
 // ------------------------------------------------------------------ launchers
-hipError_t launch_split_router_weights(const float* w_r, bf16_t* wr3, int d, int E, bool chunked, hipStream_t s) {
+hipError_t launch_split_router_weights(const float* w_r, bf16_t* wr3, int d, int E, hipStream_t s) {
     dim3 grid((E + 31) / 32, (d + 31) / 32);
-    hipLaunchKernelGGL(split_router_weights, grid, dim3(256), 0, s, w_r, wr3, d, E, chunked ? 1 : 0);
+    hipLaunchKernelGGL(split_router_weights, grid, dim3(256), 0, s, w_r, wr3, d, E);
     return hipGetLastError();
 }
 
 hipError_t launch_router_gemm(const bf16_t* x, const bf16_t* wr3, const float* b_r, float* logits,
                               int T, int d, int E, hipStream_t s) {
-    dim3 grid((T + 64 * RT_TB - 1) / (64 * RT_TB), (E + 16 * RT_EB - 1) / (16 * RT_EB));
-    hipLaunchKernelGGL(router_gemm, grid, dim3(256), 0, s, x, wr3, b_r, logits, T, d, E);
+    const int n_tt = (T + RG_T - 1) / RG_T, n_et = (E + RG_E - 1) / RG_E;
+    const int n_tiles = n_tt * n_et;
+    const int grid = (n_tiles + 7) / 8 * 8;
+    hipLaunchKernelGGL(router_gemm, dim3(grid), dim3(512), 0, s, x, wr3, b_r, logits, T, d, E, n_tt, n_tiles);
     return hipGetLastError();
 }
 

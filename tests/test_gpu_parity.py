@@ -155,6 +155,32 @@ def test_route_gemm(D):
     say(f"route gemm cfg{ci} ok: max logit err {err.max():.2e}, near ties {int((~safe).sum())}")
 
 
+@pytest.mark.parametrize("T,d,E,bias", [
+    (300, 96, 520, True),     # E > 256: expert tiles of 256, 256 and 8; a 44-token tail tile
+    (513, 32, 257, False),    # one K stage, one expert in the last tile, no bias
+    (256, 64, 768, True),     # whole tiles only
+])
+def test_route_gemm_ragged(T, d, E, bias):
+    """The tiled router GEMM (E > 256) on ragged token and expert tiles: every
+    logit against the fp64 oracle, and the routing on margin-safe tokens."""
+    say(f"route gemm ragged T={T} d={d} E={E} bias={bias}")
+    seed = 7000 + T + d + E
+    x_bits = workloads.random_bf16((T, d), seed)
+    w_r = (workloads.random_logits(d, E, seed) * np.float32(np.sqrt(0.5 / d))).astype(np.float32)
+    b_r = (workloads.random_logits(1, E, seed + 1)[0] * np.float32(0.1)) if bias else None
+    t = run_route(bits_to_dev(x_bits), f32_dev(w_r), f32_dev(b_r) if bias else None, None, T, d, E,
+                  want_logits=True)
+    z = so.router_logits(workloads.bf16_bits_to_f32(x_bits), w_r, b_r)
+    zg = t["logits"].cpu().numpy().astype(np.float64)
+    err = np.abs(zg - z)
+    assert err.max() <= 2e-5 * (1 + np.abs(z).max()), f"logit error {err.max():.3e}"
+    r = so.softmax_top1(z)
+    safe = top2_margin(z) > MARGIN
+    np.testing.assert_array_equal(t["expert"].cpu().numpy()[safe], r.expert[safe])
+    np.testing.assert_allclose(t["lse"].cpu().numpy(), r.lse, rtol=1e-5, atol=1e-5)
+    np.testing.assert_allclose(t["prob_sum"].cpu().numpy(), r.p.sum(axis=0), rtol=AUX_REL, atol=1e-3)
+
+
 # ------------------------------------------------------------ experts
 def test_expert_ffn(D):
     cfg = D.cfg
