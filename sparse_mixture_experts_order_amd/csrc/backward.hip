@@ -254,17 +254,23 @@ __global__ __launch_bounds__(256) void dx_assemble(const bf16_t* __restrict__ do
     }
 }
 
-// dx on the fp32 MFMA (E a multiple of 8, w_r and dz 16-byte aligned, d a
-// multiple of 128): workgroup = 128 columns i x 128 tokens, wave w = columns
+// dx on the fp32 MFMA (E a multiple of 32, d a multiple of 128, w_r and dz
+// 16-byte aligned): workgroup = 128 columns i x 128 tokens, wave w = columns
 // 64 (w >> 1) x tokens 64 (w & 1) as 2 x 2 blocks of 32.  A = W_r rows (i,
-// K = e), B = dz^T (K = e, column = token): half wave h takes the experts
-// [h E/2, (h + 1) E/2), one per MFMA step, so a lane reads consecutive floats
-// of W_r and dz rows (16-byte loads, 16 experts at a time) and each loaded
-// value feeds two MFMAs.  In a result block lane l holds token l & 31 and
-// columns {0-3, 8-11, 16-19, 24-27} (+4 for h = 1); one v_permlane32_swap per
-// register pair turns these into two runs of 8 consecutive columns, so dout,
-// dbuf and dx move 16 or 32 bytes at a time.  dx = bf16(dout + sum_e dz W_r +
+// K = e), B = dz^T (K = e, column = token).  Per chunk of 32 experts the
+// workgroup's 128 W_r rows and 128 dz rows (128 bytes each) go from memory
+// straight into LDS, eight 1 KiB copies per wave with the lanes along the
+// expert axis (16-byte column c of row r at c ^ (r & 7), which keeps the
+// 32-row fragment reads free of bank conflicts); two stages, one barrier per
+// chunk; dz rows past T read as zero.  MFMA step st of a chunk: half wave h
+// takes expert 16 h + st, so a lane's 16 values of a row are four
+// ds_read_b128.  In a result block lane l holds token l & 31 and columns
+// {0-3, 8-11, 16-19, 24-27} (+4 for h = 1); one v_permlane32_swap per register
+// pair turns these into two runs of 8 consecutive columns, so dout, dbuf and
+// dx move 16 or 32 bytes at a time.  dx = bf16(dout + sum_e dz W_r +
 // dbuf[e*, s]) as in dx_assemble.
+constexpr int DX_STAGE = 2 * 128 * 128;   // bytes: the W_r tile, then the dz tile
+
 __global__ __launch_bounds__(256) void dx_assemble_mfma(const bf16_t* __restrict__ dout,
                                                         const float* __restrict__ dbuf,
                                                         const int32_t* __restrict__ expert,
@@ -272,18 +278,37 @@ __global__ __launch_bounds__(256) void dx_assemble_mfma(const bf16_t* __restrict
                                                         const uint8_t* __restrict__ keep,
                                                         const float* __restrict__ dz, const float* __restrict__ w_r,
                                                         int64_t T, int d, int E, int C, bf16_t* __restrict__ dx) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __shared__ __attribute__((aligned(16))) char lds[2 * DX_STAGE];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l32 = lane & 31, h = lane >> 5;
-    const int i0 = blockIdx.x * 128 + (wave >> 1) * 64;
-    const int64_t t0 = (int64_t)blockIdx.y * 128 + (wave & 1) * 64;
-    const int Eh = E / 2;
-    const float* arow[2];
-    const float* brow[2];
+    const int ib = blockIdx.x * 128;
+    const int64_t tb = (int64_t)blockIdx.y * 128;
+    const int i0 = ib + (wave >> 1) * 64;
+    const int64_t t0 = tb + (wave & 1) * 64;
+    const int nk = E / 32;
+
+    // copy q = 8 wave + i lands at stage + 1 KiB q: W_r rows for q < 16, dz rows
+    // after; lane -> row 8 (q % 16) + lane / 8, LDS column lane % 8
+    const bool wrows = wave < 2;
+    const char* base = wrows ? (const char*)(w_r + (size_t)ib * E) : (const char*)(dz + tb * E);
+    const uint32_t nbytes = wrows ? (uint32_t)128 * E * 4 : (uint32_t)min<int64_t>(128, T - tb) * E * 4;
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(base, nbytes);
+    uint32_t vo[8];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        arow[q] = w_r + (size_t)(i0 + 32 * q + l32) * E + h * Eh;
-        brow[q] = dz + min(t0 + 32 * q + l32, T - 1) * E + h * Eh;   // rows past T are not stored
+    for (int i = 0; i < 8; ++i) {
+        const int row = 8 * ((8 * wave + i) & 15) + (lane >> 3);
+        vo[i] = (uint32_t)row * E * 4 + (((lane & 7) ^ (row & 7)) << 4);
     }
+    auto issue = [&](int kc, int stg) {
+        char* dst = lds + stg * DX_STAGE + wave * 8 * 1024;
+        const uint32_t so = (uint32_t)__builtin_amdgcn_readfirstlane(kc * 128);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) copy_to_lds(rs, dst + i * 1024, vo[i], so);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
     f32x16 acc[2][2];
 #pragma unroll
     for (int a = 0; a < 2; ++a)
@@ -291,47 +316,51 @@ __global__ __launch_bounds__(256) void dx_assemble_mfma(const bf16_t* __restrict
         for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
-    // 16 experts per chunk, the next chunk's loads in flight during the MFMAs
-    float av[2][2][16], bv[2][2][16];
-    auto load_chunk = [&](int e0, float (&a)[2][16], float (&b)[2][16]) {
-        const int n = min(16, Eh - e0);   // a multiple of 4
+
+    // the routing of this lane's two tokens, fetched now: the first chunk's wait covers it
+    int te[2], tp[2], tk[2];
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
+    for (int b = 0; b < 2; ++b) {
+        const int64_t tc = min<int64_t>(t0 + 32 * b + l32, T - 1);
+        te[b] = expert[tc];
+        tp[b] = position[tc];
+        tk[b] = keep[tc];
+    }
+    issue(0, 0);
+    int kc = 0;
+    do {   // E >= 32: at least one chunk
+        wait_copies<0>();   // this wave's copies of chunk kc
+        lds_barrier();      // every wave's, and chunk kc - 1 is read out
+        issue(min(kc + 1, nk - 1), (kc + 1) & 1);   // the last chunk is fetched twice, never read
+        const char* st = lds + (kc & 1) * DX_STAGE;
+        float av[2][16], bv[2][16];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int ra = (wave >> 1) * 64 + 32 * q + l32;   // W_r row in the tile
+            const int rb = (wave & 1) * 64 + 32 * q + l32;    // dz row in the tile
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                f32x4 a4 = f32x4{0.f, 0.f, 0.f, 0.f}, b4 = a4;
-                if (4 * c < n) {
-                    a4 = *(const f32x4*)(arow[q] + e0 + 4 * c);
-                    b4 = *(const f32x4*)(brow[q] + e0 + 4 * c);
-                }
+                const f32x4 a4 = *(const f32x4*)(st + ra * 128 + (((4 * h + c) ^ (ra & 7)) << 4));
+                const f32x4 b4 = *(const f32x4*)(st + 128 * 128 + rb * 128 + (((4 * h + c) ^ (rb & 7)) << 4));
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    a[q][4 * c + j] = a4[j];
-                    b[q][4 * c + j] = b4[j];
+                    av[q][4 * c + j] = a4[j];
+                    bv[q][4 * c + j] = b4[j];
                 }
             }
-    };
-    auto mfma_chunk = [&](const float (&a)[2][16], const float (&b)[2][16]) {
+        }
 #pragma unroll
-        for (int st = 0; st < 16; ++st)
+        for (int st16 = 0; st16 < 16; ++st16)
 #pragma unroll
             for (int x0 = 0; x0 < 2; ++x0)
 #pragma unroll
                 for (int y0 = 0; y0 < 2; ++y0)
-                    acc[x0][y0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[x0][st], b[y0][st], acc[x0][y0], 0, 0, 0);
-    };
-    load_chunk(0, av[0], bv[0]);
-    for (int e0 = 0; e0 < Eh; e0 += 32) {
-        if (e0 + 16 < Eh) load_chunk(e0 + 16, av[1], bv[1]);
-        mfma_chunk(av[0], bv[0]);
-        if (e0 + 16 < Eh) {
-            if (e0 + 32 < Eh) load_chunk(e0 + 32, av[0], bv[0]);
-            mfma_chunk(av[1], bv[1]);
-        }
-    }
+                    acc[x0][y0] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[x0][st16], bv[y0][st16], acc[x0][y0], 0, 0, 0);
+    } while (++kc < nk);
+    wait_copies<0>();   // the spare copy of the last chunk
+    // runs of 8 columns: swap rows 8-11 of half 0 with rows 4-7 of half 1 (and 24-27 with 20-23)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        // runs of 8 columns: swap rows 8-11 of half 0 with rows 4-7 of half 1 (and 24-27 with 20-23)
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -344,33 +373,55 @@ __global__ __launch_bounds__(256) void dx_assemble_mfma(const bf16_t* __restrict
                     acc[a][b][8 * pr + i] = __uint_as_float(sw[0]);
                     acc[a][b][8 * pr + 4 + i] = __uint_as_float(sw[1]);
                 }
-        const int64_t t = t0 + 32 * b + l32;
-        if (t >= T) continue;
-        const int e = expert[t], pos = position[t];
-        const bool kept = keep[t] && e >= 0 && e < E && pos >= 0 && pos < C;
+    // every load of the epilogue before its first store (a load issued after a
+    // store waits for that store too); rows past T read row T - 1 and are not stored
+    uint4 dv[2][2][2];
+    f32x4 bq[2][2][2][2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const int64_t tc = min<int64_t>(t0 + 32 * b + l32, T - 1);
+        const bool kept = tk[b] && te[b] >= 0 && te[b] < E && tp[b] >= 0 && tp[b] < C;
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
             for (int run = 0; run < 2; ++run) {
                 const int i = i0 + 32 * a + 16 * run + 8 * h;
-                const uint4 dv = *(const uint4*)(dout + t * d + i);
-                f32x4 b0 = f32x4{0.f, 0.f, 0.f, 0.f}, b1 = b0;
+                dv[b][a][run] = *(const uint4*)(dout + tc * d + i);
+                bq[b][a][run][0] = bq[b][a][run][1] = f32x4{0.f, 0.f, 0.f, 0.f};
                 if (kept) {
-                    const float* br = dbuf + ((size_t)e * C + pos) * d + i;
-                    b0 = *(const f32x4*)br;
-                    b1 = *(const f32x4*)(br + 4);
+                    const float* br = dbuf + ((size_t)te[b] * C + tp[b]) * d + i;
+                    bq[b][a][run][0] = *(const f32x4*)br;
+                    bq[b][a][run][1] = *(const f32x4*)(br + 4);
                 }
-                const uint32_t dw[4] = {dv.x, dv.y, dv.z, dv.w};
-                const float bb[8] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+            }
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int run = 0; run < 2; ++run) {
+                const uint4 v = dv[b][a][run];
+                const uint32_t dw[4] = {v.x, v.y, v.z, v.w};
                 uint32_t o[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const float v0 = (bf16_to_f32(dw[j] & 0xffffu) + acc[a][b][8 * run + 2 * j]) + bb[2 * j];
-                    const float v1 = (bf16_to_f32(dw[j] >> 16) + acc[a][b][8 * run + 2 * j + 1]) + bb[2 * j + 1];
+                    const f32x4& bb = bq[b][a][run][j >> 1];
+                    const float v0 = (bf16_to_f32(dw[j] & 0xffffu) + acc[a][b][8 * run + 2 * j]) + bb[2 * (j & 1)];
+                    const float v1 = (bf16_to_f32(dw[j] >> 16) + acc[a][b][8 * run + 2 * j + 1]) + bb[2 * (j & 1) + 1];
                     o[j] = bf16_rne(v0) | (bf16_rne(v1) << 16);
                 }
-                *(uint4*)(dx + t * d + i) = make_uint4(o[0], o[1], o[2], o[3]);
+                dv[b][a][run] = make_uint4(o[0], o[1], o[2], o[3]);
             }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const int64_t t = t0 + 32 * b + l32;
+        if (t >= T) continue;
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int run = 0; run < 2; ++run)
+                *(uint4*)(dx + t * d + i0 + 32 * a + 16 * run + 8 * h) = dv[b][a][run];
     }
 }
 
@@ -431,8 +482,8 @@ hipError_t launch_dx_assemble(const bf16_t* dout, const float* dbuf, const int32
                               const uint8_t* keep, const float* dz, const float* w_r, int64_t T, int d, int E, int C,
                               bf16_t* dx, hipStream_t s) {
     if (T == 0) return hipSuccess;
-    // the MFMA kernel reads w_r and dz rows 16 bytes at a time
-    if (E % 8 == 0 && d % 128 == 0 && ((uintptr_t)w_r | (uintptr_t)dz) % 16 == 0)
+    // the MFMA kernel copies 32-expert chunks of w_r and dz rows 16 bytes at a time
+    if (E % 32 == 0 && d % 128 == 0 && ((uintptr_t)w_r | (uintptr_t)dz) % 16 == 0)
         hipLaunchKernelGGL(dx_assemble_mfma, dim3(d / 128, (unsigned)((T + 127) / 128)), dim3(256), 0, s, dout, dbuf,
                            expert, position, keep, dz, w_r, T, d, E, C, dx);
     else
