@@ -610,28 +610,45 @@ switch_status switch_layer_bwd(const switch_layer_bwd_args* ba, void* ws, size_t
     LAUNCH(K_ROUTER_DB, "router_db", s, launch_column_sum(dz, (int)T, E, dbs, B.db_r, s));
     LAUNCH(K_ROUTER_WGRAD, "router_wgrad", s, launch_router_wgrad(x, dz, T, d, E, part, B.dw_r, s));
     // experts: the two products with the weights read W1 and W2 as stored
-    // (K-major); the weight gradients take the token axis as K, transposed
+    // (K-major).  The weight gradients take the token axis as K: with d, d_ff
+    // > 64 they read dy, H, dA and buf as stored (K-major operands, rows past
+    // accepted read as zero), else transposed copies of them
+    const bool tn = ffn_wide_tiles(d) && ffn_wide_tiles(F);
     if (C > 0) {
-        LAUNCH(K_TRANSPOSE, "transpose_rows", s, launch_transpose_rows(dy, dyT, E, C, d, Cp, B.accepted, s));
-        LAUNCH(K_TRANSPOSE, "transpose_rows", s, launch_transpose_rows(B.h, hT, E, C, F, Cp, B.accepted, s));
-        LAUNCH(K_TRANSPOSE, "transpose_rows", s, launch_transpose_rows(B.buf, bufT, E, C, d, Cp, B.accepted, s));
-        LAUNCH(K_FFN_TILES, "ffn_tile_prefix", s, launch_ffn_tile_prefix(B.accepted, E, C, pre_c, tt_c, s));
+        if (!tn) {
+            LAUNCH(K_TRANSPOSE, "transpose_rows", s, launch_transpose_rows(dy, dyT, E, C, d, Cp, B.accepted, s));
+            LAUNCH(K_TRANSPOSE, "transpose_rows", s, launch_transpose_rows(B.h, hT, E, C, F, Cp, B.accepted, s));
+            LAUNCH(K_TRANSPOSE, "transpose_rows", s, launch_transpose_rows(B.buf, bufT, E, C, d, Cp, B.accepted, s));
+        }
+        // the token tiles of the data products, and the d- and d_ff-row tiles of the
+        // weight gradients (carrying each expert's accepted count), in one launch
+        FfnTileLists tl{};
+        tl.E = E;
+        tl.list[0] = FfnTileListSpec{B.accepted, nullptr, C, pre_c, tt_c};
+        tl.list[1] = FfnTileListSpec{nullptr, B.accepted, d, pre_d, tt_d};
+        tl.list[2] = FfnTileListSpec{nullptr, B.accepted, F, pre_f, tt_f};
+        LAUNCH(K_FFN_TILES, "ffn_tile_prefix", s, launch_ffn_tile_lists(tl, 3, s));
         // dA = (dy W2) * [H > 0]          rows: tokens, K = d, N = d_ff; W2[e] is [d][d_ff]
         LAUNCH(K_GEMM_DA, "gemm_dA", s,
                launch_grouped_gemm_kmajor_masked(dy, B.w2, pre_c, tt_c, dA, B.h, E, C, d, F, s));
         // dbuf = dA W1                    rows: tokens, K = d_ff, N = d; W1[e] is [d_ff][d]
         LAUNCH(K_GEMM_DBUF, "gemm_dbuf", s,
                launch_grouped_gemm_kmajor_f32(dA, B.w1, pre_c, tt_c, dbuf, E, C, F, d, s));
-        LAUNCH(K_TRANSPOSE, "transpose_rows", s, launch_transpose_rows(dA, dAT, E, C, F, Cp, B.accepted, s));
+        if (!tn) LAUNCH(K_TRANSPOSE, "transpose_rows", s, launch_transpose_rows(dA, dAT, E, C, F, Cp, B.accepted, s));
     }
     // weight gradients: K = the (zero-padded) token axis
-    LAUNCH(K_FFN_TILES, "ffn_tile_prefix", s, launch_ffn_tile_prefix(nullptr, E, d, pre_d, tt_d, s));
-    LAUNCH(K_FFN_TILES, "ffn_tile_prefix", s, launch_ffn_tile_prefix(nullptr, E, F, pre_f, tt_f, s));
     if (C > 0) {
         // dW2[e] = dy^T H                 rows: d, K = tokens, N = d_ff
-        LAUNCH(K_GEMM_DW2, "gemm_dW2", s, launch_grouped_gemm_f32(dyT, hT, pre_d, tt_d, B.dw2, E, d, Cp, F, s));
         // dW1[e] = dA^T buf               rows: d_ff, K = tokens, N = d
-        LAUNCH(K_GEMM_DW1, "gemm_dW1", s, launch_grouped_gemm_f32(dAT, bufT, pre_f, tt_f, B.dw1, E, F, Cp, d, s));
+        if (tn) {
+            LAUNCH(K_GEMM_DW2, "gemm_dW2", s,
+                   launch_grouped_gemm_tn_f32(dy, B.h, pre_d, tt_d, B.dw2, E, d, C, F, s));
+            LAUNCH(K_GEMM_DW1, "gemm_dW1", s,
+                   launch_grouped_gemm_tn_f32(dA, B.buf, pre_f, tt_f, B.dw1, E, F, C, d, s));
+        } else {
+            LAUNCH(K_GEMM_DW2, "gemm_dW2", s, launch_grouped_gemm_f32(dyT, hT, pre_d, tt_d, B.dw2, E, d, Cp, F, s));
+            LAUNCH(K_GEMM_DW1, "gemm_dW1", s, launch_grouped_gemm_f32(dAT, bufT, pre_f, tt_f, B.dw1, E, F, Cp, d, s));
+        }
     } else {
         LAUNCH(K_GEMM_DW2, "zero", s, launch_fill_zero(B.dw2, (int64_t)E * d * F, s));
         LAUNCH(K_GEMM_DW1, "zero", s, launch_fill_zero(B.dw1, (int64_t)E * d * F, s));

@@ -114,13 +114,13 @@ __device__ __forceinline__ void row16_sum_all(float (&v)[N]) {
 
 // Token-tile list of the expert GEMMs, built by one workgroup of NT threads:
 // pre[e] = number of valid TOK-row token tiles of experts < e (pre[E] = total
-// V), and ttab[v] = {expert, first row, valid rows, 0} for v = pre[e] + tt, the
-// token tiles of each expert in row order.  accepted == NULL means every
-// expert has all C rows.  The exclusive scan runs over the waves' prefix sums
-// in wave order.
+// V), and ttab[v] = {expert, first row, valid rows, w[e] (0 without w)} for
+// v = pre[e] + tt, the token tiles of each expert in row order.  accepted ==
+// NULL means every expert has all C rows.  The exclusive scan runs over the
+// waves' prefix sums in wave order.
 template <int NT>
 __device__ void ffn_tile_list(const int32_t* __restrict__ accepted, int E, int C, int TOK, int32_t* __restrict__ pre,
-                              int4* __restrict__ ttab) {
+                              int4* __restrict__ ttab, const int32_t* __restrict__ w = nullptr) {
     __shared__ int wsum[NT / 64];
     const int per = (E + NT - 1) / NT;
     const int e0 = threadIdx.x * per;
@@ -146,7 +146,8 @@ __device__ void ffn_tile_list(const int32_t* __restrict__ accepted, int E, int C
         if (e < E) {
             pre[e] = run;
             const int a = min(max(accepted ? accepted[e] : C, 0), C);
-            for (int tt = 0; tt * TOK < a; ++tt) ttab[run + tt] = make_int4(e, tt * TOK, min(TOK, a - tt * TOK), 0);
+            const int we = w ? w[e] : 0;
+            for (int tt = 0; tt * TOK < a; ++tt) ttab[run + tt] = make_int4(e, tt * TOK, min(TOK, a - tt * TOK), we);
             run += (a + TOK - 1) / TOK;
         }
     }

@@ -38,14 +38,14 @@ namespace swmoe {
 
 constexpr int FFN_LDS_STRIDE = 72;  // bf16 elements per token row in LDS (64 + 8 pad)
 
-// The token-tile list (ffn_tile_list) as a kernel of its own.
-__global__ __launch_bounds__(1024) void ffn_tile_prefix(const int32_t* __restrict__ accepted, int E, int C, int TOK,
-                                                        int32_t* __restrict__ pre, int4* __restrict__ ttab) {
-    ffn_tile_list<1024>(accepted, E, C, TOK, pre, ttab);
+// Token-tile lists (ffn_tile_list) as a kernel of their own: block b builds list b.
+__global__ __launch_bounds__(1024) void ffn_tile_prefix(const FfnTileLists L) {
+    const FfnTileListSpec& t = L.list[blockIdx.x];
+    ffn_tile_list<1024>(t.accepted, L.E, t.C, t.tok, t.pre, t.ttab, t.w);
 }
 
 struct FfnTile {
-    int e, nt, tok_base, nv;
+    int e, nt, tok_base, nv, w;
 };
 
 // Tile i = v * n_tiles + nt: token tile v of the list, weight block nt.  The
@@ -59,6 +59,7 @@ __device__ __forceinline__ FfnTile decode_tile(int i, const int4* __restrict__ t
     t.e = __builtin_amdgcn_readfirstlane(m.x);
     t.tok_base = __builtin_amdgcn_readfirstlane(m.y);
     t.nv = __builtin_amdgcn_readfirstlane(m.z);
+    t.w = __builtin_amdgcn_readfirstlane(m.w);
     t.nt = i - v * n_tiles;
     return t;
 }
@@ -625,8 +626,8 @@ __device__ __forceinline__ bf16x8 wkm_fragment(const char* st, int rbw, int k, i
 // n0 + 4 a .. + 3, and lane i gets the 4 rows k0 .. k0 + 3 of column n0 + i.
 // The swizzle puts the 4 rows x 2 slots of a group's read on 8 different slots
 // (all 32 banks).
-template <int TOKB, int NBW, int WAVES, int MODE, int S, int KC, bool WKM = false>
-__global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __restrict__ A,   // [E, C, K] or x
+template <int TOKB, int NBW, int WAVES, int MODE, int S, int KC, bool WKM = false, bool AKM = false>
+__global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __restrict__ A,   // [E, C, K], x or [E, K, C]
                                                               const bf16_t* __restrict__ W,   // [E, N, K] or [E, K, N]
                                                               const int32_t* __restrict__ pre,
                                                               const int4* __restrict__ ttab,
@@ -634,8 +635,10 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
                                                               const bf16_t* __restrict__ mask,
                                                               const FfnCombine cb,
                                                               const int32_t* __restrict__ a_rows, uint32_t a_bytes,
-                                                              int E, int C, int K, int N, int n_tiles) {
+                                                              int E, int C, int K, int N, int n_tiles,
+                                                              int k_in_table, int kst) {
     static_assert(KC == 64 || KC == 32, "64- or 32-wide K chunks");
+    static_assert(!AKM || WKM, "K-major token rows come with K-major weights");
     constexpr int TOK = 32 * TOKB;
     constexpr int NWG = WAVES * 32 * NBW;
     constexpr int RB = KC * 2;                              // bytes per staged row
@@ -668,7 +671,9 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
     // lane offsets of the copies (row RPC q + lane / NCOL, swizzled 16-byte column)
     uint32_t wvo[WPW], avo[APW];
     constexpr int RBW = NWG * 2;                            // bytes per K-major stage row
+    constexpr int RBA = TOK * 2;
     static_assert(!WKM || (KC == 64 && (NWG / 8) % 8 == 0), "K-major stages: 64-wide chunks, whole slot groups");
+    static_assert(!AKM || (TOK / 8) % 8 == 0, "K-major token stages: whole slot groups");
 #pragma unroll
     for (int i = 0; i < WPW; ++i) {
         if constexpr (WKM) {
@@ -683,15 +688,37 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
 #pragma unroll
     for (int i = 0; i < APW; ++i) {
         const int q = wave * APW + i;
-        const int r = RPC * (q < A_COPIES ? q : 0) + lane / NCOL;   // spares copy the first rows again
-        avo[i] = (uint32_t)r * K * 2 + (dma_slot<KC>(r, lane % NCOL) << 4);
+        if constexpr (AKM) {
+            const int lin = (q < A_COPIES ? q : 0) * 1024 + lane * 16;   // spares copy the first bytes again
+            const int k = lin / RBA, sl = (lin - k * RBA) >> 4;
+            avo[i] = (uint32_t)k * C * 2 + ((sl ^ (2 * (k & 3))) << 4);
+        } else {
+            const int r = RPC * (q < A_COPIES ? q : 0) + lane / NCOL;   // spares copy the first rows again
+            avo[i] = (uint32_t)r * K * 2 + (dma_slot<KC>(r, lane % NCOL) << 4);
+        }
     }
 
     int f_tile = -1;
     uint32_t a_lo = 0, a_hi = 0, a_n = 0, w_lo = 0, w_hi = 0, w_n = 0;
+    // K-major operands: the tile's valid K rows and the byte offset of its first column in a K row
+    int kv = kst;
+    uint32_t a_col = 0, w_col = 0;
     auto rsrc = [](uint32_t lo, uint32_t hi, uint32_t n) {
         return __builtin_amdgcn_make_buffer_rsrc((void*)(uintptr_t)(((uint64_t)hi << 32) | lo), (short)0, (int)n,
                                                  kBufferWord3);
+    };
+    // the descriptor of one 64-row K chunk of a K-major operand (rows of `row_bytes`,
+    // tile base lo/hi): rows at or past kv, and the columns past the row's end in
+    // the last valid row, read as zero
+    // (the clamp and the byte count come out of vector instructions: readfirstlane
+    // keeps the descriptor scalar, each word through uint32_t)
+    auto kmajor_chunk = [&](uint32_t lo, uint32_t hi, int kf, uint32_t row_bytes, uint32_t col) {
+        const uint64_t b = ((((uint64_t)hi << 32) | lo) + (uint64_t)kf * KC * row_bytes);
+        const int vr = min(max(kv - kf * KC, 0), KC);
+        const int n = vr * (int)row_bytes - (int)col;
+        return rsrc((uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b),
+                    (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)),
+                    (uint32_t)__builtin_amdgcn_readfirstlane(n > 0 ? n : 0));
     };
     auto set_frontier = [&](int j) {
         f_tile = j;
@@ -729,6 +756,11 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
                 const uint32_t off = (((uint32_t)mine * K * 2) & valid) | (a_bytes & ~valid);
                 avo[i] = off + (dma_slot<KC>(r0 + rl, lane % NCOL) << 4);
             }
+        } else if constexpr (AKM) {   // columns past the tile only reach rows past C, never stored
+            const uint64_t ab = (uint64_t)(uintptr_t)((const char*)A + ((size_t)t.e * kst * C + t.tok_base) * 2);
+            a_lo = (uint32_t)ab;
+            a_hi = (uint32_t)(ab >> 32);
+            a_col = (uint32_t)t.tok_base * 2;
         } else {
             const uint64_t ab = (uint64_t)(uintptr_t)((const char*)A + ((size_t)t.e * C + t.tok_base) * K * 2);
             a_lo = (uint32_t)ab;
@@ -736,11 +768,12 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
             a_n = (uint32_t)(t.nv * K * 2);
         }
         const int r0 = t.nt * NWG;                                   // rows past N read zeros
-        if constexpr (WKM) {   // columns past N read the next row: they only reach outputs past N, never stored
-            const uint64_t wb = (uint64_t)(uintptr_t)((const char*)W + ((size_t)t.e * K * N + r0) * 2);
+        if constexpr (WKM) {   // columns past N only reach outputs past N, never stored
+            const uint64_t wb = (uint64_t)(uintptr_t)((const char*)W + ((size_t)t.e * kst * N + r0) * 2);
             w_lo = (uint32_t)wb;
             w_hi = (uint32_t)(wb >> 32);
-            w_n = (uint32_t)(((size_t)K * N - r0) * 2);
+            w_col = (uint32_t)r0 * 2;
+            kv = k_in_table ? min(max(t.w, 0), kst) : kst;
         } else {
             const uint64_t wb = (uint64_t)(uintptr_t)((const char*)W + ((size_t)t.e * N + r0) * K * 2);
             w_lo = (uint32_t)wb;
@@ -751,15 +784,20 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
     // copies of chunk position f (clamped to the last one) into stage `stg`
     auto issue = [&](int f, int stg) {
         f = min(f, P - 1);
-        const int jf = f / nk, kf = f - jf * nk;
+        // (the division runs on the vector unit: readfirstlane keeps the chunk, and
+        // the descriptors built from it, scalar)
+        const int jf = __builtin_amdgcn_readfirstlane(f / nk), kf = f - jf * nk;
         if (jf != f_tile) set_frontier(jf);
-        const __amdgpu_buffer_rsrc_t rs_a = rsrc(a_lo, a_hi, a_n), rs_w = rsrc(w_lo, w_hi, w_n);
+        const __amdgpu_buffer_rsrc_t rs_a = AKM ? kmajor_chunk(a_lo, a_hi, kf, (uint32_t)C * 2, a_col)
+                                                : rsrc(a_lo, a_hi, a_n);
+        const __amdgpu_buffer_rsrc_t rs_w = WKM ? kmajor_chunk(w_lo, w_hi, kf, (uint32_t)N * 2, w_col)
+                                                : rsrc(w_lo, w_hi, w_n);
         char* sb = lds + stg * STAGE;
 #pragma unroll
-        for (int i = 0; i < WPW; ++i)
-            copy_to_lds(rs_w, sb + (wave * WPW + i) * 1024, wvo[i], WKM ? (uint32_t)kf * KC * N * 2 : kf * RB);
+        for (int i = 0; i < WPW; ++i) copy_to_lds(rs_w, sb + (wave * WPW + i) * 1024, wvo[i], WKM ? 0u : kf * RB);
 #pragma unroll
-        for (int i = 0; i < APW; ++i) copy_to_lds(rs_a, sb + W_STAGE + (wave * APW + i) * 1024, avo[i], kf * RB);
+        for (int i = 0; i < APW; ++i)
+            copy_to_lds(rs_a, sb + W_STAGE + (wave * APW + i) * 1024, avo[i], AKM ? 0u : kf * RB);
     };
 
     f32x16 acc[NBW][TOKB];
@@ -791,8 +829,13 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
                     bf16x8 bt[TOKB];
 #pragma unroll
                     for (int tb = 0; tb < TOKB; ++tb) {
-                        const int r = tb * 32 + l32;
-                        bt[tb] = as_bf16x8(*(const u32x4*)(sa + r * RB + (dma_slot<KC>(r, c) << 4)));
+                        if constexpr (AKM) {   // rows k = 8 c .. 8 c + 7 of token column tb * 32 + (l & 31)
+                            const int m = lane & 15;
+                            bt[tb] = wkm_fragment(sa, RBA, 8 * c + (m >> 2), tb * 32 + 16 * ((lane >> 4) & 1) + 4 * (m & 3));
+                        } else {
+                            const int r = tb * 32 + l32;
+                            bt[tb] = as_bf16x8(*(const u32x4*)(sa + r * RB + (dma_slot<KC>(r, c) << 4)));
+                        }
                     }
 #pragma unroll
                     for (int nb = 0; nb < NBW; ++nb) {
@@ -864,18 +907,20 @@ hipError_t launch_expert_gemm_t(const bf16_t* A, const bf16_t* W, const int32_t*
     return hipGetLastError();
 }
 
-template <int TOKB, int NBW, int WAVES, int MODE, int S, int KC, bool WKM = false>
+template <int TOKB, int NBW, int WAVES, int MODE, int S, int KC, bool WKM = false, bool AKM = false>
 hipError_t launch_expert_gemm_dma_t(const bf16_t* A, const bf16_t* W, const int32_t* pre, const int4* ttab, void* out,
                                     const bf16_t* mask, const FfnCombine& cb, int E, int C, int K, int N,
-                                    hipStream_t s, const int32_t* a_rows = nullptr, uint32_t a_bytes = 0) {
+                                    hipStream_t s, const int32_t* a_rows = nullptr, uint32_t a_bytes = 0,
+                                    bool k_in_table = false, int kst = -1) {
     constexpr int NWG = WAVES * 32 * NBW;
     const int n_tiles = (N + NWG - 1) / NWG;
     const int tok_tiles = (C + 32 * TOKB - 1) / (32 * TOKB);
     const int64_t max_tiles = (int64_t)E * n_tiles * tok_tiles;
     int64_t grid = std::min<int64_t>((int64_t)device_cus(), (max_tiles + 7) / 8 * 8);   // one workgroup per CU
     grid = std::max<int64_t>(8, grid / 8 * 8);
-    hipLaunchKernelGGL((expert_gemm_dma<TOKB, NBW, WAVES, MODE, S, KC, WKM>), dim3((unsigned)grid), dim3(64 * WAVES), 0, s, A,
-                       W, pre, ttab, out, mask, cb, a_rows, a_bytes, E, C, K, N, n_tiles);
+    hipLaunchKernelGGL((expert_gemm_dma<TOKB, NBW, WAVES, MODE, S, KC, WKM, AKM>), dim3((unsigned)grid), dim3(64 * WAVES),
+                       0, s, A, W, pre, ttab, out, mask, cb, a_rows, a_bytes, E, C, K, N, n_tiles, k_in_table ? 1 : 0,
+                       kst < 0 ? K : kst);
     return hipGetLastError();
 }
 
@@ -887,7 +932,17 @@ size_t ffn_tile_table_entries(int E, int C) {
 }
 
 hipError_t launch_ffn_tile_prefix(const int32_t* accepted, int E, int C, int32_t* pre, int4* ttab, hipStream_t s) {
-    hipLaunchKernelGGL(ffn_tile_prefix, dim3(1), dim3(1024), 0, s, accepted, E, C, ffn_token_tile(C), pre, ttab);
+    FfnTileLists L{};
+    L.E = E;
+    L.list[0] = FfnTileListSpec{accepted, nullptr, C, pre, ttab};
+    return launch_ffn_tile_lists(L, 1, s);
+}
+
+hipError_t launch_ffn_tile_lists(const FfnTileLists& L, int n, hipStream_t s) {
+    if (n < 1 || n > kMaxTileLists) return hipErrorInvalidValue;
+    FfnTileLists Lt = L;
+    for (int i = 0; i < n; ++i) Lt.list[i].tok = ffn_token_tile(Lt.list[i].C);
+    hipLaunchKernelGGL(ffn_tile_prefix, dim3(n), dim3(1024), 0, s, Lt);
     return hipGetLastError();
 }
 
@@ -1023,6 +1078,32 @@ hipError_t launch_grouped_gemm_kmajor_masked(const bf16_t* A, const bf16_t* W, c
                                              bf16_t* out, const bf16_t* mask, int E, int rows, int K, int N,
                                              hipStream_t s) {
     return launch_expert_gemm_kmajor<OUT_MASK_BF16>(A, W, pre, ttab, out, mask, E, rows, K, N, s);
+}
+
+// out[e] = A[e]^T W[e] with the token axis as K, both operands as stored:
+// A [E, kst, M] and W [E, kst, N] bf16, out [E, M, N] fp32; rows k of expert
+// e at or past the valid count in the fourth word of its tile entries read as
+// zero.  The direct-to-LDS kernel with K-major stages for both operands
+// (128-row tiles over M, so M > 64).
+hipError_t launch_grouped_gemm_tn_f32(const bf16_t* A, const bf16_t* W, const int32_t* pre, const int4* ttab,
+                                      float* out, int E, int M, int kst, int N, hipStream_t s) {
+    if (!ffn_wide_tiles(M) || kst <= 0) return hipErrorInvalidValue;
+    const int K = (kst + 63) / 64 * 64;
+    const FfnCombine none{};
+    switch (dma_tile_width(E, M, N)) {
+        case 512:
+            return launch_expert_gemm_dma_t<4, 2, 8, OUT_F32, 2, 64, true, true>(A, W, pre, ttab, out, nullptr, none, E,
+                                                                              M, K, N, s, nullptr, 0, true, kst);
+        case 384:
+            return launch_expert_gemm_dma_t<4, 2, 6, OUT_F32, 2, 64, true, true>(A, W, pre, ttab, out, nullptr, none, E,
+                                                                              M, K, N, s, nullptr, 0, true, kst);
+        case 256:
+            return launch_expert_gemm_dma_t<4, 1, 8, OUT_F32, 3, 64, true, true>(A, W, pre, ttab, out, nullptr, none, E,
+                                                                              M, K, N, s, nullptr, 0, true, kst);
+        default:
+            return launch_expert_gemm_dma_t<4, 1, 6, OUT_F32, 3, 64, true, true>(A, W, pre, ttab, out, nullptr, none, E,
+                                                                              M, K, N, s, nullptr, 0, true, kst);
+    }
 }
 
 // Products whose output outweighs the weight stream (a short K, such as the

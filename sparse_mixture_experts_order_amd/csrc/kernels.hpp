@@ -49,6 +49,17 @@ hipError_t launch_gather(const bf16_t* x, const int32_t* expert, const int32_t* 
 int ffn_token_tile(int C);
 size_t ffn_tile_table_entries(int E, int C);
 hipError_t launch_ffn_tile_prefix(const int32_t* accepted, int E, int C, int32_t* pre, int4* ttab, hipStream_t s);
+// several token-tile lists over the same experts in one launch (block b builds list b);
+// w, if not NULL, goes into the fourth word of each tile entry of its expert
+constexpr int kMaxTileLists = 3;
+struct FfnTileListSpec {
+    const int32_t* accepted; const int32_t* w; int C; int32_t* pre; int4* ttab;
+    int tok;   // rows per tile: set by launch_ffn_tile_lists
+};
+struct FfnTileLists {
+    FfnTileListSpec list[kMaxTileLists]; int E;
+};
+hipError_t launch_ffn_tile_lists(const FfnTileLists& L, int n, hipStream_t s);
 hipError_t launch_expert_gemm1(const bf16_t* buf, const bf16_t* w1, const int32_t* pre, const int4* ttab, bf16_t* h,
                                int E, int C, int d, int d_ff, hipStream_t s);
 hipError_t launch_expert_gemm2(const bf16_t* h, const bf16_t* w2, const int32_t* pre, const int4* ttab, float* y,
@@ -88,6 +99,11 @@ hipError_t launch_grouped_gemm_kmajor_f32(const bf16_t* A, const bf16_t* W, cons
 hipError_t launch_grouped_gemm_kmajor_masked(const bf16_t* A, const bf16_t* W, const int32_t* pre, const int4* ttab,
                                              bf16_t* out, const bf16_t* mask, int E, int rows, int K, int N,
                                              hipStream_t s);
+// out[e, m, n] = sum_k A[e, k, m] W[e, k, n], both operands as stored (the token
+// axis k, kst rows per expert), for the M-row tiles listed in (pre, ttab), whose
+// fourth word holds the expert's valid k rows (the rest count as zero); M > 64
+hipError_t launch_grouped_gemm_tn_f32(const bf16_t* A, const bf16_t* W, const int32_t* pre, const int4* ttab,
+                                      float* out, int E, int M, int kst, int N, hipStream_t s);
 
 // combine.hip
 hipError_t launch_combine(const float* y, const int32_t* expert, const int32_t* slot, const uint8_t* keep,
