@@ -215,11 +215,17 @@ __device__ __forceinline__ void wait_copies() {
     __builtin_amdgcn_s_waitcnt((N_OUTSTANDING & 15) | ((N_OUTSTANDING >> 4) << 14) | 0x0F70);
 }
 
+// Cache policy of a load (the buffer instructions' auxiliary operand): kStream
+// marks data read once (the non-temporal hint, `nt`), so that streaming it
+// does not push out what is read again soon (L2 and the memory-side cache).
+constexpr int kCached = 0, kStream = 2;
+
 // One 1 KiB copy: lane i's 16 bytes land at dst + 16 i.  (The LDS address
 // space exists only in the device pass.)
+template <int AUX = kCached>
 __device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t rs, char* dst, uint32_t voff, uint32_t soff) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0, AUX);
 #endif
 }
 

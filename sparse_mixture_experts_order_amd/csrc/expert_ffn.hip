@@ -90,6 +90,44 @@ struct FfnOutShape {
     static constexpr int O_BYTES = TOK * OSTRIDE;
 };
 
+// What the combine epilogue reads besides the accumulators: the token of each
+// of the lane's rows (-1 past the tile), its gate, and the residual runs of
+// the lane's columns (two runs of 8 per 32-column block).
+template <int TOKB, int NBW>
+struct CombineInputs {
+    int tok[TOKB];
+    float g[TOKB];
+    u32x4 rr[TOKB][NBW][2];
+};
+
+template <int TOKB, int NBW>
+__device__ __forceinline__ void combine_load_tokens(CombineInputs<TOKB, NBW>& in, const FfnTile& t,
+                                                    const FfnCombine& cb, int C, int l32) {
+#pragma unroll
+    for (int tb = 0; tb < TOKB; ++tb) {
+        const int r = tb * 32 + l32;
+        in.tok[tb] = r < t.nv ? cb.slot_token[(size_t)t.e * C + t.tok_base + r] : -1;
+    }
+}
+
+template <int TOKB, int NBW>
+__device__ __forceinline__ void combine_load_rows(CombineInputs<TOKB, NBW>& in, const FfnCombine& cb, int N, int n0,
+                                                  int half) {
+#pragma unroll
+    for (int tb = 0; tb < TOKB; ++tb) {
+        in.g[tb] = in.tok[tb] >= 0 ? cb.gate[in.tok[tb]] : 0.f;
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+            for (int run = 0; run < 2; ++run) {
+                const int n = n0 + nb * 32 + run * 16 + half * 8;
+                in.rr[tb][nb][run] = (in.tok[tb] >= 0 && cb.residual && n < N)
+                                         ? *(const u32x4*)(cb.residual + (size_t)in.tok[tb] * N + n)
+                                         : u32x4{0u, 0u, 0u, 0u};
+            }
+    }
+}
+
 // Tile epilogue without LDS: each lane stores its accumulator values straight
 // to memory; L2 merges the pieces into whole lines.  In the MFMA layout a lane
 // holds, for one token, weight rows {0-3, 8-11, 16-19, 24-27} of a 32-row block
@@ -102,8 +140,9 @@ struct FfnOutShape {
 //    token's output row (and y, if kept, gets the fp32 values).
 template <int TOKB, int NBW, int WAVES, int MODE>
 __device__ __forceinline__ void ffn_store_tile_direct(f32x16 (&acc)[NBW][TOKB], const FfnTile& t, void* out,
-                                                      const bf16_t* mask, const FfnCombine& cb, int C, int N,
-                                                      int wave, int l32, int half) {
+                                                      const bf16_t* mask, const FfnCombine& cb,
+                                                      CombineInputs<TOKB, NBW>& in, int C, int N, int wave, int l32,
+                                                      int half) {
     constexpr int NWG = WAVES * 32 * NBW;
     constexpr bool RUNS = MODE == OUT_RELU_BF16 || MODE == OUT_COMBINE || MODE == OUT_MASK_BF16;
     if constexpr (RUNS) {
@@ -125,30 +164,11 @@ __device__ __forceinline__ void ffn_store_tile_direct(f32x16 (&acc)[NBW][TOKB], 
     }
     const int n0 = t.nt * NWG + wave * 32 * NBW;   // first column of this wave
     if constexpr (MODE == OUT_COMBINE) {
-        // per 32-column block, every load is issued before the block's first
-        // store (the token of each row and its gate once, then the block's
-        // residual runs); the output runs replace the residual runs in place
-        int tok[TOKB];
-        float g[TOKB];
-#pragma unroll
-        for (int tb = 0; tb < TOKB; ++tb) {
-            const int r = tb * 32 + l32;
-            tok[tb] = r < t.nv ? cb.slot_token[(size_t)t.e * C + t.tok_base + r] : -1;
-        }
-#pragma unroll
-        for (int tb = 0; tb < TOKB; ++tb) g[tb] = tok[tb] >= 0 ? cb.gate[tok[tb]] : 0.f;
+        // the token rows, gates and residual runs are in `in` (every load
+        // issued before the first store: a load issued after a store waits
+        // for that store too); each output run replaces its residual run
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb) {
-            u32x4 rr[TOKB][2];
-#pragma unroll
-            for (int tb = 0; tb < TOKB; ++tb)
-#pragma unroll
-                for (int run = 0; run < 2; ++run) {
-                    const int n = n0 + nb * 32 + run * 16 + half * 8;
-                    rr[tb][run] = (tok[tb] >= 0 && cb.residual && n < N)
-                                      ? *(const u32x4*)(cb.residual + (size_t)tok[tb] * N + n)
-                                      : u32x4{0u, 0u, 0u, 0u};
-                }
 #pragma unroll
             for (int tb = 0; tb < TOKB; ++tb)
 #pragma unroll
@@ -156,26 +176,26 @@ __device__ __forceinline__ void ffn_store_tile_direct(f32x16 (&acc)[NBW][TOKB], 
                     const f32x16& a = acc[nb][tb];
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        const uint32_t res = rr[tb][run][j];
-                        const float o0 = fmaf(g[tb], a[8 * run + 2 * j], bf16_to_f32(res & 0xffffu));
-                        const float o1 = fmaf(g[tb], a[8 * run + 2 * j + 1], bf16_to_f32(res >> 16));
-                        rr[tb][run][j] = bf16_rne(o0) | (bf16_rne(o1) << 16);
+                        const uint32_t res = in.rr[tb][nb][run][j];
+                        const float o0 = fmaf(in.g[tb], a[8 * run + 2 * j], bf16_to_f32(res & 0xffffu));
+                        const float o1 = fmaf(in.g[tb], a[8 * run + 2 * j + 1], bf16_to_f32(res >> 16));
+                        in.rr[tb][nb][run][j] = bf16_rne(o0) | (bf16_rne(o1) << 16);
                     }
                 }
 #pragma unroll
             for (int tb = 0; tb < TOKB; ++tb) {
-                if (tok[tb] < 0) continue;
-                const size_t orow = (size_t)tok[tb] * N;
+                if (in.tok[tb] < 0) continue;
+                const size_t orow = (size_t)in.tok[tb] * N;
 #pragma unroll
                 for (int run = 0; run < 2; ++run) {
                     const int n = n0 + nb * 32 + run * 16 + half * 8;
-                    if (n < N) *(u32x4*)(cb.out + orow + n) = rr[tb][run];
+                    if (n < N) *(u32x4*)(cb.out + orow + n) = in.rr[tb][nb][run];
                 }
             }
-            if (cb.y) {   // after the block's residual use: stores count in the same counter as the loads
+            if (cb.y) {
 #pragma unroll
                 for (int tb = 0; tb < TOKB; ++tb) {
-                    if (tok[tb] < 0) continue;
+                    if (in.tok[tb] < 0) continue;
                     const size_t row = ((size_t)t.e * C + t.tok_base + tb * 32 + l32) * N;
 #pragma unroll
                     for (int run = 0; run < 2; ++run) {
@@ -626,7 +646,8 @@ __device__ __forceinline__ bf16x8 wkm_fragment(const char* st, int rbw, int k, i
 // n0 + 4 a .. + 3, and lane i gets the 4 rows k0 .. k0 + 3 of column n0 + i.
 // The swizzle puts the 4 rows x 2 slots of a group's read on 8 different slots
 // (all 32 banks).
-template <int TOKB, int NBW, int WAVES, int MODE, int S, int KC, bool WKM = false, bool AKM = false>
+template <int TOKB, int NBW, int WAVES, int MODE, int S, int KC, bool WKM = false, bool AKM = false,
+          bool STREAM = false>
 __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __restrict__ A,   // [E, C, K], x or [E, K, C]
                                                               const bf16_t* __restrict__ W,   // [E, N, K] or [E, K, N]
                                                               const int32_t* __restrict__ pre,
@@ -794,7 +815,8 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
                                                 : rsrc(w_lo, w_hi, w_n);
         char* sb = lds + stg * STAGE;
 #pragma unroll
-        for (int i = 0; i < WPW; ++i) copy_to_lds(rs_w, sb + (wave * WPW + i) * 1024, wvo[i], WKM ? 0u : kf * RB);
+        for (int i = 0; i < WPW; ++i)
+            copy_to_lds<STREAM ? kStream : kCached>(rs_w, sb + (wave * WPW + i) * 1024, wvo[i], WKM ? 0u : kf * RB);
 #pragma unroll
         for (int i = 0; i < APW; ++i)
             copy_to_lds(rs_a, sb + W_STAGE + (wave * APW + i) * 1024, avo[i], AKM ? 0u : kf * RB);
@@ -811,6 +833,7 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
 #pragma unroll
     for (int p = 0; p < S - 1; ++p) issue(p, p);
 
+    CombineInputs<TOKB, NBW> cin;   // the combine epilogue's loads
     for (int p0 = 0; p0 < P; p0 += S) {
 #pragma unroll
         for (int u = 0; u < S; ++u) {
@@ -858,7 +881,11 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
                 const int j = p / nk;
                 if (p - j * nk == nk - 1) {
                     const FfnTile t = decode_tile(j * G + slot, ttab, n_tiles);
-                    ffn_store_tile_direct<TOKB, NBW, WAVES, MODE>(acc, t, out, mask, cb, C, N, wave, l32, half);
+                    if constexpr (MODE == OUT_COMBINE) {
+                        combine_load_tokens(cin, t, cb, C, l32);
+                        combine_load_rows(cin, cb, N, t.nt * NWG + wave * 32 * NBW, half);
+                    }
+                    ffn_store_tile_direct<TOKB, NBW, WAVES, MODE>(acc, t, out, mask, cb, cin, C, N, wave, l32, half);
 #pragma unroll
                     for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
@@ -918,6 +945,17 @@ hipError_t launch_expert_gemm_dma_t(const bf16_t* A, const bf16_t* W, const int3
     const int64_t max_tiles = (int64_t)E * n_tiles * tok_tiles;
     int64_t grid = std::min<int64_t>((int64_t)device_cus(), (max_tiles + 7) / 8 * 8);   // one workgroup per CU
     grid = std::max<int64_t>(8, grid / 8 * 8);
+    // expert weights read by a single token tile per expert are streamed (read
+    // once); with several token tiles they are read again and stay cached, and
+    // the K-major token-axis products' W operand is an activation, read again too
+    if constexpr (!AKM) {
+        if (tok_tiles == 1) {
+            hipLaunchKernelGGL((expert_gemm_dma<TOKB, NBW, WAVES, MODE, S, KC, WKM, AKM, true>), dim3((unsigned)grid),
+                               dim3(64 * WAVES), 0, s, A, W, pre, ttab, out, mask, cb, a_rows, a_bytes, E, C, K, N,
+                               n_tiles, k_in_table ? 1 : 0, kst < 0 ? K : kst);
+            return hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL((expert_gemm_dma<TOKB, NBW, WAVES, MODE, S, KC, WKM, AKM>), dim3((unsigned)grid), dim3(64 * WAVES),
                        0, s, A, W, pre, ttab, out, mask, cb, a_rows, a_bytes, E, C, K, N, n_tiles, k_in_table ? 1 : 0,
                        kst < 0 ? K : kst);
