@@ -625,8 +625,10 @@ switch_status switch_layer_bwd(const switch_layer_bwd_args* ba, void* ws, size_t
         FfnTileLists tl{};
         tl.E = E;
         tl.list[0] = FfnTileListSpec{B.accepted, nullptr, C, pre_c, tt_c};
-        tl.list[1] = FfnTileListSpec{nullptr, B.accepted, d, pre_d, tt_d};
-        tl.list[2] = FfnTileListSpec{nullptr, B.accepted, F, pre_f, tt_f};
+        // (the fourth word is the accepted count only for the K-major products;
+        // the transposed path's GEMM reads it as the tile count of the expert)
+        tl.list[1] = FfnTileListSpec{nullptr, tn ? B.accepted : nullptr, d, pre_d, tt_d};
+        tl.list[2] = FfnTileListSpec{nullptr, tn ? B.accepted : nullptr, F, pre_f, tt_f};
         LAUNCH(K_FFN_TILES, "ffn_tile_prefix", s, launch_ffn_tile_lists(tl, 3, s));
         // dA = (dy W2) * [H > 0]          rows: tokens, K = d, N = d_ff; W2[e] is [d][d_ff]
         LAUNCH(K_GEMM_DA, "gemm_dA", s,

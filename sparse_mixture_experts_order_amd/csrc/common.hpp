@@ -114,10 +114,11 @@ __device__ __forceinline__ void row16_sum_all(float (&v)[N]) {
 
 // Token-tile list of the expert GEMMs, built by one workgroup of NT threads:
 // pre[e] = number of valid TOK-row token tiles of experts < e (pre[E] = total
-// V), and ttab[v] = {expert, first row, valid rows, w[e] (0 without w)} for
-// v = pre[e] + tt, the token tiles of each expert in row order.  accepted ==
-// NULL means every expert has all C rows.  The exclusive scan runs over the
-// waves' prefix sums in wave order.
+// V), and ttab[v] = {expert, first row, valid rows, w[e]} for v = pre[e] + tt,
+// the token tiles of each expert in row order; without w the fourth word is
+// the expert's number of token tiles.  accepted == NULL means every expert
+// has all C rows.  The exclusive scan runs over the waves' prefix sums in wave
+// order.
 template <int NT>
 __device__ void ffn_tile_list(const int32_t* __restrict__ accepted, int E, int C, int TOK, int32_t* __restrict__ pre,
                               int4* __restrict__ ttab, const int32_t* __restrict__ w = nullptr) {
@@ -146,7 +147,7 @@ __device__ void ffn_tile_list(const int32_t* __restrict__ accepted, int E, int C
         if (e < E) {
             pre[e] = run;
             const int a = min(max(accepted ? accepted[e] : C, 0), C);
-            const int we = w ? w[e] : 0;
+            const int we = w ? w[e] : (a + TOK - 1) / TOK;
             for (int tt = 0; tt * TOK < a; ++tt) ttab[run + tt] = make_int4(e, tt * TOK, min(TOK, a - tt * TOK), we);
             run += (a + TOK - 1) / TOK;
         }

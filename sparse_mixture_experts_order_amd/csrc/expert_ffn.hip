@@ -48,19 +48,35 @@ struct FfnTile {
     int e, nt, tok_base, nv, w;
 };
 
-// Tile i = v * n_tiles + nt: token tile v of the list, weight block nt.  The
-// tiles of one token tile are neighbours (they share the token rows in L2).
-// The table read is uniform, so it goes through the scalar cache and uses no
-// vector registers.
-__device__ __forceinline__ FfnTile decode_tile(int i, const int4* __restrict__ ttab, int n_tiles) {
-    const int v = i / n_tiles;
-    const int4 m = ttab[v];
+// Tile i of a GEMM over the list: token tile v, weight block nt.  The n_tiles
+// * cnt tiles of an expert with cnt token tiles are consecutive, and inside
+// them the order is weight block major (EM, the fourth word of the list's
+// entries holding cnt): the token tiles that read one weight block are
+// neighbours, so they run together on one XCD and read it once from memory
+// (weight block minor, the tiles of one token tile share its token rows).
+// With one token tile per expert the two orders are the same.  The table
+// reads are uniform, so they go through the scalar cache and use no vector
+// registers.
+template <bool EM = false>
+__device__ __forceinline__ FfnTile decode_tile(int i, const int4* __restrict__ ttab, int n_tiles, int TOK = 1) {
+    const int v1 = __builtin_amdgcn_readfirstlane(i / n_tiles);
+    int4 m = ttab[v1];
+    int nt = i - v1 * n_tiles;
+    if constexpr (EM) {
+        const int cnt = __builtin_amdgcn_readfirstlane(m.w);
+        if (cnt > 1) {
+            const int p0 = v1 - __builtin_amdgcn_readfirstlane(m.y) / TOK;   // the expert's first token tile
+            const int local = i - p0 * n_tiles;
+            nt = __builtin_amdgcn_readfirstlane(local / cnt);
+            m = ttab[p0 + local - nt * cnt];
+        }
+    }
     FfnTile t;
     t.e = __builtin_amdgcn_readfirstlane(m.x);
     t.tok_base = __builtin_amdgcn_readfirstlane(m.y);
     t.nv = __builtin_amdgcn_readfirstlane(m.z);
     t.w = __builtin_amdgcn_readfirstlane(m.w);
-    t.nt = i - v * n_tiles;
+    t.nt = nt;
     return t;
 }
 
@@ -743,7 +759,7 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
     };
     auto set_frontier = [&](int j) {
         f_tile = j;
-        const FfnTile t = decode_tile(j * G + slot, ttab, n_tiles);
+        const FfnTile t = decode_tile<!AKM>(j * G + slot, ttab, n_tiles, TOK);
         if (a_rows) {
             const uint64_t ab = (uint64_t)(uintptr_t)A;
             a_lo = (uint32_t)ab;
@@ -880,7 +896,7 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
 
                 const int j = p / nk;
                 if (p - j * nk == nk - 1) {
-                    const FfnTile t = decode_tile(j * G + slot, ttab, n_tiles);
+                    const FfnTile t = decode_tile<!AKM>(j * G + slot, ttab, n_tiles, TOK);
                     if constexpr (MODE == OUT_COMBINE) {
                         combine_load_tokens(cin, t, cb, C, l32);
                         combine_load_rows(cin, cb, N, t.nt * NWG + wave * 32 * NBW, half);
