@@ -94,26 +94,32 @@ __global__ __launch_bounds__(256) void transpose_rows(const bf16_t* __restrict__
     }
 }
 
-// dW_r partial sums on the fp32 MFMA (v_mfma_f32_32x32x2_f32, products and
-// sums in fp32 like the VALU): workgroup (128 rows i of W_r, 128 experts e,
-// one token slice); wave w takes rows 64 (w >> 1) and experts 64 (w & 1) of
-// it, as 2 x 2 blocks of 32.  Per 32-token chunk, x (converted to fp32) and dz
-// are staged in LDS as [token][128] rows (pitch 129 floats: the reads below
-// and the staging writes each hit every bank twice per wave).  MFMA step s (16
-// per chunk) gives the two half waves tokens s and 16 + s: lane l supplies
-// A = x[t][i + (l & 31)] and B = dz[t][e + (l & 31)], so D[i][e] = sum_t
-// x[t][i] dz[t][e].
-constexpr int RW_CHUNK = 32;
+// dW_r partial sums on the bf16 MFMA: dz = hi + mid + lo exactly (three bf16
+// terms, as W_r in the router) and x is bf16, so every product is exact in
+// fp32 and v_mfma_f32_32x32x16_bf16 sums the three partial products in fp32.
+// Workgroup (128 rows i of W_r, 128 experts e, one token slice); wave w takes
+// rows 64 (w >> 1) and experts 64 (w & 1) as 2 x 2 blocks of 32 (A = x
+// columns, B = dz columns, K = tokens).  Per chunk of 64 tokens, x and the
+// three terms of dz are staged in LDS as K-major rows (token k: 128 bf16, the
+// 16-byte slot c at c ^ 2 (k & 3)) and the fragments (8 consecutive tokens
+// of one column) come from transposed reads.  The next chunk is loaded into
+// registers while the MFMAs run, through descriptors that end with the
+// chunk's last token of the slice (rows past it read as zero; the byte count,
+// not the scalar offset, decides).
+constexpr int RW_CHUNK = 64;
 constexpr int RW_TILE = 128;
+constexpr int RW_ROW = RW_TILE * 2;             // bytes per staged token row
+constexpr int RW_PLANE = RW_CHUNK * RW_ROW;     // one staged operand (16 KiB)
+constexpr int RW_PER = RW_CHUNK * 16 / 256;     // 16-byte x slots per thread per chunk
+
 __global__ __launch_bounds__(256) void router_wgrad(const bf16_t* __restrict__ x, const float* __restrict__ dz,
                                                     int64_t T, int d, int E, int tps, float* __restrict__ part) {
-    __shared__ float xs[RW_CHUNK][RW_TILE + 1];
-    __shared__ float zs[RW_CHUNK][RW_TILE + 1];
+    __shared__ __attribute__((aligned(16))) char lds[4 * RW_PLANE];   // x, then dz's hi, mid, lo
     const int i0 = blockIdx.x * RW_TILE, e0 = blockIdx.y * RW_TILE;
     const int64_t t0 = (int64_t)blockIdx.z * tps;
     const int64_t t1 = min(T, t0 + tps);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int l32 = lane & 31, h = lane >> 5;
+    const int h = lane >> 5, m = lane & 15, g1 = (lane >> 4) & 1;
     const int wi = (wave >> 1) * 64, we = (wave & 1) * 64;
     f32x16 acc[2][2];
 #pragma unroll
@@ -122,70 +128,84 @@ __global__ __launch_bounds__(256) void router_wgrad(const bf16_t* __restrict__ x
         for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
-    // the next chunk's rows are loaded into registers while the MFMAs run, by
-    // buffer loads without branches: x through a descriptor that ends with the
-    // slice (its rows past t1 read as zero, which also cancels whatever dz
-    // rows past t1 hold), dz through one over the whole array (columns past E
-    // only reach outputs that are not stored)
-    const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(x + t0 * d, (uint32_t)((t1 - t0) * d * 2));
-    const __amdgpu_buffer_rsrc_t rz = buffer_rsrc(dz, (uint32_t)(T * E * 4));
-    u32x4 xr[2];
-    u32x4 zr[4];
+    // thread q (of RW_PER x 256) loads row q >> 4, 16-byte slot q & 15 of x (8
+    // bf16) and the matching 8 floats of dz (two 16-byte loads)
+    u32x4 xr[RW_PER], zr[RW_PER][2];
     auto load_chunk = [&](int64_t tc) {
+        const uint32_t rows = (uint32_t)min<int64_t>(RW_CHUNK, t1 - tc);
+        const __amdgpu_buffer_rsrc_t rx = buffer_rsrc_uniform(x + tc * d, rows * d * 2);
+        const __amdgpu_buffer_rsrc_t rz = buffer_rsrc_uniform(dz + tc * E, rows * E * 4);
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {   // x: 32 rows x 128 columns, 2 x 8 per thread
+        for (int jj = 0; jj < RW_PER; ++jj) {
             const int q = threadIdx.x + 256 * jj;
-            const int r = q >> 4, c = (q & 15) * 8;
-            xr[jj] = __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)((r * d + i0 + c) * 2),
-                                                           (uint32_t)((tc - t0) * d * 2), 0);
-        }
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {   // dz: 32 rows x 128 experts, 4 x 4 per thread
-            const int q = threadIdx.x + 256 * jj;
-            const int r = q >> 5, c = (q & 31) * 4;
-            zr[jj] = __builtin_amdgcn_raw_buffer_load_b128(rz, (uint32_t)((r * E + e0 + c) * 4), (uint32_t)(tc * E * 4),
-                                                           0);
+            const int r = q >> 4, c = q & 15;
+            xr[jj] = __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)((r * d + i0 + 8 * c) * 2), 0, 0);
+            zr[jj][0] = __builtin_amdgcn_raw_buffer_load_b128(rz, (uint32_t)((r * E + e0 + 8 * c) * 4), 0, 0);
+            zr[jj][1] = __builtin_amdgcn_raw_buffer_load_b128(rz, (uint32_t)((r * E + e0 + 8 * c) * 4 + 16), 0, 0);
         }
     };
     if (t0 < t1) load_chunk(t0);
     for (int64_t tc = t0; tc < t1; tc += RW_CHUNK) {
-        __syncthreads();   // the previous chunk's reads are done
+        lds_barrier();   // the previous chunk's fragment reads are done
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
+        for (int jj = 0; jj < RW_PER; ++jj) {
             const int q = threadIdx.x + 256 * jj;
-            const int r = q >> 4, c = (q & 15) * 8;
-            const uint32_t w4[4] = {xr[jj][0], xr[jj][1], xr[jj][2], xr[jj][3]};
+            const int r = q >> 4, c = q & 15;
+            const int at = r * RW_ROW + ((c ^ (2 * (r & 3))) << 4);
+            *(u32x4*)(lds + at) = xr[jj];
+            u32x4 hi, mid, lo;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                xs[r][c + 2 * j] = bf16_to_f32(w4[j] & 0xffffu);
-                xs[r][c + 2 * j + 1] = bf16_to_f32(w4[j] >> 16);
+            for (int p2 = 0; p2 < 4; ++p2) {   // the three terms of floats 2 p2, 2 p2 + 1
+                uint32_t t3[3][2];
+#pragma unroll
+                for (int o = 0; o < 2; ++o) {
+                    const float w = __uint_as_float(zr[jj][p2 >> 1][2 * (p2 & 1) + o]);
+                    const uint32_t bh = bf16_rne(w);
+                    const float r1 = w - bf16_to_f32(bh);
+                    const uint32_t bm = bf16_rne(r1);
+                    const uint32_t bl = bf16_rne(r1 - bf16_to_f32(bm));
+                    t3[0][o] = bh;
+                    t3[1][o] = bm;
+                    t3[2][o] = bl;
+                }
+                hi[p2] = t3[0][0] | (t3[0][1] << 16);
+                mid[p2] = t3[1][0] | (t3[1][1] << 16);
+                lo[p2] = t3[2][0] | (t3[2][1] << 16);
             }
-        }
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int q = threadIdx.x + 256 * jj;
-            const int r = q >> 5, c = (q & 31) * 4;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) zs[r][c + j] = __uint_as_float(zr[jj][j]);
+            *(u32x4*)(lds + RW_PLANE + at) = hi;
+            *(u32x4*)(lds + 2 * RW_PLANE + at) = mid;
+            *(u32x4*)(lds + 3 * RW_PLANE + at) = lo;
         }
         if (tc + RW_CHUNK < t1) load_chunk(tc + RW_CHUNK);
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
-        for (int st = 0; st < RW_CHUNK / 2; ++st) {
-            const float a0 = xs[h * 16 + st][wi + l32], a1 = xs[h * 16 + st][wi + 32 + l32];
-            const float b0 = zs[h * 16 + st][we + l32], b1 = zs[h * 16 + st][we + 32 + l32];
-            acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
-            acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
-            acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
-            acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
+        for (int s = 0; s < RW_CHUNK / 16; ++s) {   // tokens 16 s .. 16 s + 15; this half wave's 8 are 8 (2 s + h) ..
+            const int k = 8 * (2 * s + h) + (m >> 2);
+            bf16x8 a[2], b[3][2];
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk) {
+                a[blk] = kmajor_fragment(lds, RW_ROW, k, wi + 32 * blk + 16 * g1 + 4 * (m & 3));
+#pragma unroll
+                for (int term = 0; term < 3; ++term)
+                    b[term][blk] = kmajor_fragment(lds + (1 + term) * RW_PLANE, RW_ROW, k,
+                                                   we + 32 * blk + 16 * g1 + 4 * (m & 3));
+            }
+#pragma unroll
+            for (int jj = 0; jj < 3; ++jj)   // lo, mid, hi
+#pragma unroll
+                for (int x0 = 0; x0 < 2; ++x0)
+#pragma unroll
+                    for (int y0 = 0; y0 < 2; ++y0)
+                        acc[x0][y0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[x0], b[2 - jj][y0], acc[x0][y0], 0, 0, 0);
         }
     }
+    // lane: expert column e0 + we + 32 b + (l & 31), rows 8 (i / 4) + 4 h + i % 4 of block a
     float* p = part + (size_t)blockIdx.z * d * E;
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
-            const int e = e0 + we + 32 * b + l32;
+            const int e = e0 + we + 32 * b + (lane & 31);
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int row = i0 + wi + 32 * a + 8 * (i >> 2) + 4 * h + (i & 3);
@@ -194,13 +214,38 @@ __global__ __launch_bounds__(256) void router_wgrad(const bf16_t* __restrict__ x
         }
 }
 
+// dW_r = the slices' partial sums added in slice order in fp64.  A thread
+// takes 4 consecutive outputs (one 16-byte load per slice) and issues the
+// loads of 8 slices before adding them, in order.
 __global__ __launch_bounds__(256) void router_wgrad_reduce(const float* __restrict__ part, int slices, int64_t n,
                                                            float* __restrict__ dw_r) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (i >= n) return;
-    double s = 0.0;
-    for (int k = 0; k < slices; ++k) s += (double)part[(size_t)k * n + i];
-    dw_r[i] = (float)s;
+    double s[4] = {0.0, 0.0, 0.0, 0.0};
+    if (i + 4 <= n && (n & 3) == 0 && ((uintptr_t)dw_r & 15) == 0) {   // part is 16-byte aligned (workspace)
+        int k = 0;
+        for (; k + 8 <= slices; k += 8) {
+            f32x4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = *(const f32x4*)(part + (size_t)(k + u) * n + i);
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) s[j] += (double)v[u][j];
+        }
+        for (; k < slices; ++k) {
+            const f32x4 v = *(const f32x4*)(part + (size_t)k * n + i);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) s[j] += (double)v[j];
+        }
+        *(f32x4*)(dw_r + i) = f32x4{(float)s[0], (float)s[1], (float)s[2], (float)s[3]};
+    } else {
+        for (int j = 0; j < 4 && i + j < n; ++j) {
+            double a = 0.0;
+            for (int k = 0; k < slices; ++k) a += (double)part[(size_t)k * n + i + j];
+            dw_r[i + j] = (float)a;
+        }
+    }
 }
 
 // dx: workgroup = 64 tokens x 64 columns of x, 4 x 4 per thread; K = E in
@@ -465,8 +510,9 @@ hipError_t launch_router_wgrad(const bf16_t* x, const float* dz, int64_t T, int 
                                hipStream_t s) {
     const int slices = router_wgrad_slices(T, d, E);
     const int64_t n = (int64_t)d * E;
+    const unsigned rblocks = (unsigned)((n + 1023) / 1024);   // 4 outputs per thread
     if (slices == 0) {   // no tokens: the gradient is zero
-        hipLaunchKernelGGL(router_wgrad_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part, 0, n, dw_r);
+        hipLaunchKernelGGL(router_wgrad_reduce, dim3(rblocks), dim3(256), 0, s, part, 0, n, dw_r);
         return hipGetLastError();
     }
     int tps = (int)((T + slices - 1) / slices);
@@ -474,7 +520,7 @@ hipError_t launch_router_wgrad(const bf16_t* x, const float* dz, int64_t T, int 
     const int used = (int)((T + tps - 1) / tps);
     hipLaunchKernelGGL(router_wgrad, dim3((d + RW_TILE - 1) / RW_TILE, (E + RW_TILE - 1) / RW_TILE, used), dim3(256), 0,
                        s, x, dz, T, d, E, tps, part);
-    hipLaunchKernelGGL(router_wgrad_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part, used, n, dw_r);
+    hipLaunchKernelGGL(router_wgrad_reduce, dim3(rblocks), dim3(256), 0, s, part, used, n, dw_r);
     return hipGetLastError();
 }
 

@@ -197,6 +197,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, kBufferWord3);
 }
 
+// The same from values the compiler may have computed on the vector unit but
+// that are uniform: each word goes through readfirstlane (as uint32_t: the
+// builtin returns a signed int), so the descriptor stays scalar and the loads
+// need no per-lane loop.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc_uniform(const void* base, uint32_t nbytes) {
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    const uint32_t n = (uint32_t)__builtin_amdgcn_readfirstlane(nbytes);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(uintptr_t)(((uint64_t)hi << 32) | lo), (short)0, (int)n,
+                                             kBufferWord3);
+}
+
 // Copies from memory straight into LDS.  A wave's copy instruction moves
 // 64 x 16 bytes (lane i's 16 bytes land at dst + 16 i) and counts in vmcnt
 // like any other load, so a wave waits for its own copies with wait_copies
@@ -214,6 +227,31 @@ __device__ __forceinline__ void wait_copies() {
     static_assert(N_OUTSTANDING >= 0 && N_OUTSTANDING < 64, "vmcnt range");
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt((N_OUTSTANDING & 15) | ((N_OUTSTANDING >> 4) << 14) | 0x0F70);
+}
+
+// An MFMA operand fragment (8 consecutive k of one column) from a K-major
+// LDS stage (rows k of rbw bytes, bf16), by two transposed reads
+// (ds_read_b64_tr_b16): this lane's piece is row k (the group's rows k0 +
+// lane / 4 of 16) and 4 elements from column col; the group's lanes get rows
+// k0 .. k0 + 3 (first read) and k0 + 4 .. k0 + 7 (second) of their own
+// column.  The 16-byte slot c of row k sits at c ^ 2 (k & 3), which puts a
+// group's 4 rows x 2 slots on 8 different slots (all 32 banks).
+__device__ __forceinline__ bf16x8 kmajor_fragment(const char* st, int rbw, int k, int col) {
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    const int slot = col >> 3, half = (col >> 2) & 1;
+    const int k2 = k + 4;
+    const char* p1 = st + k * rbw + ((slot ^ (2 * (k & 3))) << 4) + half * 8;
+    const char* p2 = st + k2 * rbw + ((slot ^ (2 * (k2 & 3))) << 4) + half * 8;
+    v4s lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
+#if defined(__HIP_DEVICE_COMPILE__)
+    lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p1);
+    hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p2);
+#endif
+    const u32x4 w = u32x4{(uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
+                          (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
+                          (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
+                          (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)};
+    return as_bf16x8(w);
 }
 
 // Cache policy of a load (the buffer instructions' auxiliary operand): kStream

@@ -626,29 +626,6 @@ __device__ __forceinline__ int dma_slot(int r, int c) {
     return KC == 64 ? (c ^ (r & 7)) : (c ^ ((r >> 1) & 3));
 }
 
-// Two transposed reads of a K-major stage (rows of rbw bytes): this lane's
-// piece is row k (the group's rows k0 + lane / 4 of 16) and 4 weights from
-// column col; the group's lanes get rows k0 .. k0 + 3 (first read) and
-// k0 + 4 .. k0 + 7 (second) of their own column.  Slot c of row k sits at
-// c ^ 2 (k & 3).
-__device__ __forceinline__ bf16x8 wkm_fragment(const char* st, int rbw, int k, int col) {
-    typedef short v4s __attribute__((ext_vector_type(4)));
-    const int slot = col >> 3, half = (col >> 2) & 1;
-    const int k2 = k + 4;
-    const char* p1 = st + k * rbw + ((slot ^ (2 * (k & 3))) << 4) + half * 8;
-    const char* p2 = st + k2 * rbw + ((slot ^ (2 * (k2 & 3))) << 4) + half * 8;
-    v4s lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
-#if defined(__HIP_DEVICE_COMPILE__)
-    lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p1);
-    hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p2);
-#endif
-    const u32x4 w = u32x4{(uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
-                          (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
-                          (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
-                          (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)};
-    return as_bf16x8(w);
-}
-
 // With a_rows the token rows are gathered straight from A = x [T, K]: row s of
 // expert e is x[a_rows[e * C + s]] (a_bytes = T K 2, the descriptor's byte
 // count; a_rows has 128 entries of padding past E C).  The row map is read with uniform (scalar) loads when a tile starts,
@@ -870,7 +847,7 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
                     for (int tb = 0; tb < TOKB; ++tb) {
                         if constexpr (AKM) {   // rows k = 8 c .. 8 c + 7 of token column tb * 32 + (l & 31)
                             const int m = lane & 15;
-                            bt[tb] = wkm_fragment(sa, RBA, 8 * c + (m >> 2), tb * 32 + 16 * ((lane >> 4) & 1) + 4 * (m & 3));
+                            bt[tb] = kmajor_fragment(sa, RBA, 8 * c + (m >> 2), tb * 32 + 16 * ((lane >> 4) & 1) + 4 * (m & 3));
                         } else {
                             const int r = tb * 32 + l32;
                             bt[tb] = as_bf16x8(*(const u32x4*)(sa + r * RB + (dma_slot<KC>(r, c) << 4)));
@@ -883,7 +860,7 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
                             // rows k = 8 c .. 8 c + 7 of columns wave * 32 NBW + 32 nb + (l & 31)
                             const int m = lane & 15;
                             const int col = wave * 32 * NBW + nb * 32 + 16 * ((lane >> 4) & 1) + 4 * (m & 3);
-                            wa = wkm_fragment(sw, RBW, 8 * c + (m >> 2), col);
+                            wa = kmajor_fragment(sw, RBW, 8 * c + (m >> 2), col);
                         } else {
                             const int r = wave * 32 * NBW + nb * 32 + l32;
                             wa = as_bf16x8(*(const u32x4*)(sw + r * RB + (dma_slot<KC>(r, c) << 4)));
