@@ -45,13 +45,16 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
-// Largest value, lowest index among equal values.
+// Largest value, lowest index among equal values.  (The test is bitwise, not
+// short-circuit: no branch per step, the values move by selects.)
 __device__ __forceinline__ void wave_argmax(float& v, int& i) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) {
-        float ov = __shfl_xor(v, m);
-        int oi = __shfl_xor(i, m);
-        if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
+        const float ov = __shfl_xor(v, m);
+        const int oi = __shfl_xor(i, m);
+        const bool take = (ov > v) | ((ov == v) & (oi < i));
+        v = take ? ov : v;
+        i = take ? oi : i;
     }
 }
 

@@ -176,6 +176,11 @@ __global__ __launch_bounds__(512) void router_gemm(const bf16_t* __restrict__ x,
     }
 }
 
+// e^x for the softmax as 2^(x log2 e) on the hardware exp2 (v_exp_f32): the
+// rounding of the product adds a relative error of about |x| 2^-24 ln 2 to a
+// term, so the terms that matter (x near 0) stay within a few ulp.
+__device__ __forceinline__ float rf_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+
 // Softmax statistics per token.  A workgroup (4 waves) owns `tpb` consecutive
 // tokens; a wave handles one token at a time with lane j holding experts
 // j, j+64, ...  Writes the k choices and their gates ([T, k], choices in
@@ -262,6 +267,125 @@ __global__ __launch_bounds__(256) void router_softmax(const float* __restrict__ 
     for (int e = threadIdx.x; e < E; e += 256) part[(size_t)blockIdx.x * E + e] = red[e];
 }
 
+// The same for E a multiple of 4 (and 16-byte aligned logits): lane j holds
+// experts 4 j + 256 i .. + 3 (one 16-byte load each), and a wave loads the
+// row of its next token while it works on the current one.  e^x is rf_exp,
+// as in the fused router.
+template <int NC4, int KMAX>
+__global__ __launch_bounds__(256) void router_softmax4(const float* __restrict__ logits, int T, int E, int k,
+                                                       int tpb, int32_t* __restrict__ expert,
+                                                       float* __restrict__ gate, float* __restrict__ lse,
+                                                       float* __restrict__ part) {
+    extern __shared__ float red[];  // [E]
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int t0 = blockIdx.x * tpb, t1 = min(T, t0 + tpb);
+    float acc[NC4][4];
+#pragma unroll
+    for (int i = 0; i < NC4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+    // every load unconditional (a load under a lane or token condition makes
+    // the compiler wait for all loads in flight, the prefetch included): the
+    // row's descriptor ends at E, and lanes past it read zero, taken as -inf
+    auto load = [&](int t, f32x4 (&v)[NC4]) {
+        const __amdgpu_buffer_rsrc_t rs = buffer_rsrc_uniform(logits + (size_t)t * E, (uint32_t)E * 4);
+#pragma unroll
+        for (int i = 0; i < NC4; ++i)
+            v[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)(4 * lane + 256 * i) * 4, 0, 0));
+        // issued here: the scheduler may not sink them below the waits for the other buffer
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // two row buffers: the row after next is always in flight while a row is
+    // processed (rows past the slice repeat its last row, unused)
+    auto process = [&](int t, f32x4 (&cur)[NC4]) {
+#pragma unroll
+        for (int i = 0; i < NC4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (4 * lane + 256 * i + j >= E) cur[i][j] = -INFINITY;
+        float m = -INFINITY;
+        int mi = 0x7fffffff;
+#pragma unroll
+        for (int i = 0; i < NC4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (cur[i][j] > m) { m = cur[i][j]; mi = 4 * lane + 256 * i + j; }   // strict: lowest index per lane
+        wave_argmax(m, mi);
+        float p[NC4][4];
+        float sum = 0.f;
+#pragma unroll
+        for (int i = 0; i < NC4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                p[i][j] = (4 * lane + 256 * i + j < E) ? rf_exp(cur[i][j] - m) : 0.f;
+                sum += p[i][j];
+            }
+        sum = wave_sum(sum);
+        const float inv = 1.0f / sum;
+#pragma unroll
+        for (int i = 0; i < NC4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] += p[i][j] * inv;
+        if (lane == 0) {
+            expert[(size_t)t * k] = mi;
+            gate[(size_t)t * k] = inv;    // p_{e*} = exp(z_e* - m) / s = 1 / s
+            lse[t] = m + logf(sum);
+        }
+        if constexpr (KMAX > 1) {
+            // choice r: the largest logit among the experts not yet chosen
+            int ch[KMAX];
+            ch[0] = mi;
+#pragma unroll
+            for (int r = 1; r < KMAX; ++r) {
+                if (r >= k) break;
+                float mr = -INFINITY;
+                int ir = 0x7fffffff;
+#pragma unroll
+                for (int i = 0; i < NC4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int e = 4 * lane + 256 * i + j;
+                        bool taken = e >= E;
+#pragma unroll
+                        for (int q = 0; q < r; ++q) taken |= e == ch[q];
+                        if (!taken && cur[i][j] > mr) { mr = cur[i][j]; ir = e; }
+                    }
+                wave_argmax(mr, ir);
+                ch[r] = ir;
+                if (lane == 0) {
+                    expert[(size_t)t * k + r] = ir;
+                    gate[(size_t)t * k + r] = rf_exp(mr - m) * inv;
+                }
+            }
+        }
+    };
+    f32x4 ra[NC4], rb[NC4];
+    const int tw = t0 + wave;
+    if (tw < t1) {
+        load(tw, ra);
+        for (int t = tw; t < t1; t += 8) {
+            load(min(t + 4, t1 - 1), rb);
+            process(t, ra);
+            load(min(t + 8, t1 - 1), ra);
+            if (t + 4 < t1) process(t + 4, rb);
+        }
+    }
+    for (int w = 0; w < 4; ++w) {
+        if (wave == w) {
+#pragma unroll
+            for (int i = 0; i < NC4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int e = 4 * lane + 256 * i + j;
+                    if (e < E) red[e] = (w == 0) ? acc[i][j] : red[e] + acc[i][j];
+                }
+        }
+        __syncthreads();
+    }
+    for (int e = threadIdx.x; e < E; e += 256) part[(size_t)blockIdx.x * E + e] = red[e];
+}
+
 // prob_sum[g][e] = sum over the partial rows of routing group g (rows
 // g*nblk .. g*nblk+nblk-1), in fp64, in a fixed order: a workgroup owns 64
 // experts of one group; its 16 row groups take every 16th partial row, then
@@ -326,6 +450,19 @@ template <int KMAX>
 static void softmax_by_width(int nblk, int tpb, const float* logits, int T, int E, int k, int32_t* expert,
                              float* gate, float* lse, float* part, hipStream_t s) {
     const size_t shm = (size_t)E * sizeof(float);
+    if (E % 4 == 0 && (uintptr_t)logits % 16 == 0) {   // 16-byte rows
+        const int nc4 = (E + 255) / 256;
+#define SWMOE_SOFTMAX4(N)                                                                                  \
+    hipLaunchKernelGGL((router_softmax4<N, KMAX>), dim3(nblk), dim3(256), shm, s, logits, T, E, k, tpb, expert, \
+                       gate, lse, part)
+        if (nc4 <= 1) SWMOE_SOFTMAX4(1);
+        else if (nc4 <= 2) SWMOE_SOFTMAX4(2);
+        else if (nc4 <= 4) SWMOE_SOFTMAX4(4);
+        else if (nc4 <= 8) SWMOE_SOFTMAX4(8);
+        else SWMOE_SOFTMAX4(16);
+#undef SWMOE_SOFTMAX4
+        return;
+    }
     const int nch = (E + 63) / 64;
 #define SWMOE_SOFTMAX(N)                                                                                  \
     hipLaunchKernelGGL((router_softmax<N, KMAX>), dim3(nblk), dim3(256), shm, s, logits, T, E, k, tpb, expert, \
@@ -401,10 +538,6 @@ constexpr int RF_KC = 32;      // K per stage (one 16x16x32 MFMA step)
 static_assert(RF_TOK == 64, "the fused router writes one partial row per 64 tokens");
 int router_fused_blocks(int64_t T) { return (int)((T + RF_TOK - 1) / RF_TOK); }
 
-// e^x for the softmax as 2^(x log2 e) on the hardware exp2 (v_exp_f32): the
-// rounding of the product adds a relative error of about |x| 2^-24 ln 2 to a
-// term, so the terms that matter (x near 0) stay within a few ulp.
-__device__ __forceinline__ float rf_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 
 template <int EB, int S, int KMAX, bool FULL>
 __global__ __launch_bounds__(256) void router_fused(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wr3,
