@@ -721,3 +721,101 @@ def layer_objective(x, w_r, b_r, w1, w2, c, alpha, dout, beta, expert, C):
     if beta:
         J += router_z_loss(L.z, beta).loss
     return J
+
+
+# ------------------------------- layer backward with routing groups and top-k
+#
+# The same objective J = sum_t <dout_t, out_t> + L_aux (+ L_z), now for the
+# layer of layer_forward_grouped: out_t = x_t + sum_i keep_ti g_ti y[e_ti, s_ti]
+# with g_ti = p_{t, e_ti} (raw, not renormalised), and L_aux the mean over the
+# groups of the per-group balance loss (f per group held fixed).  Every kept
+# assignment (t, i) is one buffer row s = slot_ti of expert e = e_ti and gets
+# the single-choice chain rule of layer_backward with its own gate; the
+# token's input gradient adds the contributions of all its kept choices:
+#   dgate_ti = <dout_t, y[e, s]>,  dy_s = g_ti dout_t,  da_s = (dy_s W2_e) * [a_s > 0]
+#   dW2_e = sum_s dy_s relu(a_s)^T,  dW1_e = sum_s da_s x_t^T,  dx_t = dout_t + sum_i da_s W1_e
+# and, since every gate is a softmax entry of the same row,
+#   dz_tj = sum_i dgate_ti g_ti (delta_{j e_ti} - p_tj) + dL_aux/dz_tj (+ dL_z/dz_tj).
+# Dropped choices contribute nothing (dgate_ti = 0).
+
+class LayerGradsG(NamedTuple):
+    dx: np.ndarray      # [T, d]
+    dw_r: np.ndarray    # [d, E]
+    db_r: np.ndarray    # [E]
+    dw1: np.ndarray     # [E, d_ff, d]
+    dw2: np.ndarray     # [E, d, d_ff]
+    dz: np.ndarray      # [T, E]
+    dgate: np.ndarray   # [T, k] <dout_t, y[e_ti, s_ti]> for kept choices, 0 for dropped ones
+
+
+def layer_backward_grouped(x, w_r, b_r, w1, w2, c: float, alpha: float, dout, k: int = 1,
+                           G: Optional[int] = None, priority: str = "token", beta: float = 0.0,
+                           Cg: Optional[int] = None, expert_override: Optional[np.ndarray] = None,
+                           forward: Optional[LayerResultG] = None, relu_active=None) -> LayerGradsG:
+    """Gradients of J for the layer with routing groups of G tokens and k
+    choices per token, in float64, expert by expert over its buffer rows
+    (rows 0 .. accepted_total[e]-1, token slot_token[e, row]).  relu_active(e,
+    a) may replace [a > 0] for expert e's filled rows, as in layer_backward."""
+    x = np.asarray(x, np.float64)
+    dout = np.asarray(dout, np.float64)
+    L = forward if forward is not None else layer_forward_grouped(
+        x, w_r, b_r, w1, w2, c, alpha, k=k, G=G, priority=priority, expert_override=expert_override, Cg=Cg)
+    T, d = x.shape
+    E = L.z.shape[1]
+    r, sl = L.routing, L.slots
+    kk = r.expert.shape[1]
+    w1e = (lambda e: np.asarray(w1(e) if callable(w1) else w1[e], np.float64))
+    w2e = (lambda e: np.asarray(w2(e) if callable(w2) else w2[e], np.float64))
+    F = w1e(0).shape[0]
+    dx = dout.copy()
+    dw1 = np.zeros((E, F, d))
+    dw2 = np.zeros((E, d, F))
+    dgate = np.zeros((T, kk))
+    # the assignment that owns each buffer row
+    owner = {}
+    for t in range(T):
+        for i in range(kk):
+            if sl.keep[t, i]:
+                owner[(int(r.expert[t, i]), int(sl.slot[t, i]))] = (t, i)
+    for e in range(E):
+        n = int(sl.accepted_total[e])
+        if n == 0:
+            continue
+        rows = [owner[(e, s)] for s in range(n)]
+        toks = np.array([t for t, _ in rows], np.int64)
+        ranks = np.array([i for _, i in rows], np.int64)
+        W1, W2 = w1e(e), w2e(e)
+        xe = x[toks]
+        acts = xe @ W1.T                    # pre-activations of the filled rows
+        hid = np.maximum(acts, 0.0)
+        yr = hid @ W2.T
+        gr = r.gate[toks, ranks]
+        dgate[toks, ranks] = np.sum(dout[toks] * yr, axis=1)
+        dyr = gr[:, None] * dout[toks]
+        dw2[e] = dyr.T @ hid
+        on = (acts > 0) if relu_active is None else relu_active(e, acts)
+        dar = (dyr @ W2) * on
+        dw1[e] = dar.T @ xe
+        np.add.at(dx, toks, dar @ W1)
+    dz = np.zeros((T, E))
+    for i in range(kk):
+        onehot = np.zeros((T, E))
+        onehot[np.arange(T), r.expert[:, i]] = 1.0
+        dz += (dgate[:, i] * r.gate[:, i])[:, None] * (onehot - r.p)
+    dz += L.aux.dlogits
+    if beta:
+        dz += router_z_loss(L.z, beta).dlogits
+    wr = np.asarray(w_r, np.float64)
+    dx += dz @ wr.T
+    return LayerGradsG(dx, x.T @ dz, dz.sum(axis=0), dw1, dw2, dz, dgate)
+
+
+def layer_objective_grouped(x, w_r, b_r, w1, w2, c, alpha, dout, beta, k, G, priority, expert, Cg):
+    """J = sum <dout, out> + L_aux (f fixed from `expert`) + L_z for the grouped
+    top-k layer at fixed choices and capacity; for the finite-difference pins."""
+    L = layer_forward_grouped(x, w_r, b_r, w1, w2, c, alpha, k=k, G=G, priority=priority,
+                              expert_override=expert, Cg=Cg)
+    J = float(np.sum(np.asarray(dout, np.float64) * L.out)) + L.aux.loss
+    if beta:
+        J += router_z_loss(L.z, beta).loss
+    return J

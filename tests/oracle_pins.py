@@ -627,3 +627,76 @@ def pin_backward_everything_dropped(so):
 BACKWARD_PINS = [pin_backward_finite_differences, pin_backward_single_expert_is_dense_mlp,
                  pin_backward_everything_dropped]
 ALL_PINS.extend(BACKWARD_PINS)
+
+
+# ------------------------- layer backward with routing groups and top-k choices
+def pin_backward_grouped_reduces_to_hot_path(so):
+    """One group of all T tokens and k = 1 is the hot-path layer: the grouped
+    backward equals layer_backward (its own finite-difference pins) field by
+    field, with and without z-loss, with some tokens dropped."""
+    x, w_r, b_r, w1, w2 = _fd_problem(51)
+    dout = _rng(52).standard_normal(x.shape)
+    for beta in (0.0, 0.07):
+        g1 = so.layer_backward(x, w_r, b_r, w1, w2, 1.0, 0.3, dout, beta=beta)
+        gk = so.layer_backward_grouped(x, w_r, b_r, w1, w2, 1.0, 0.3, dout, k=1, beta=beta)
+        assert (g1.dgate == 0).any() and (g1.dgate != 0).any()
+        for name in ("dx", "dw_r", "db_r", "dw1", "dw2", "dz"):
+            np.testing.assert_allclose(getattr(gk, name), getattr(g1, name), rtol=1e-12, atol=1e-14, err_msg=name)
+        np.testing.assert_allclose(gk.dgate[:, 0], g1.dgate, rtol=1e-12, atol=1e-14)
+
+
+def pin_backward_grouped_finite_differences(so):
+    """zffjzz 'troubleshooting' for the grouped top-2 layer: central finite
+    differences of J = sum <dout, out> + L_aux + L_z over every entry of x,
+    W_r, b_r, W1 and W2, with the choices, slots and masks held fixed; three
+    groups of 8 tokens, rank priority, some choices dropped."""
+    x, w_r, b_r, w1, w2 = _fd_problem(53, E=4)
+    T, d = x.shape
+    k, G, pr, c, alpha, beta = 2, 8, "rank", 0.75, 0.3, 0.05
+    dout = _rng(54).standard_normal((T, d))
+    L = so.layer_forward_grouped(x, w_r, b_r, w1, w2, c, alpha, k=k, G=G, priority=pr)
+    assert (~L.slots.keep).any() and L.slots.keep.any()
+    g = so.layer_backward_grouped(x, w_r, b_r, w1, w2, c, alpha, dout, k=k, G=G, priority=pr, beta=beta)
+    e_fix, Cg = L.routing.expert, L.Cg
+    h = 1e-6
+
+    def J(**kw):
+        a = dict(x=x, w_r=w_r, b_r=b_r, w1=w1, w2=w2)
+        a.update(kw)
+        return so.layer_objective_grouped(a["x"], a["w_r"], a["b_r"], a["w1"], a["w2"], c, alpha, dout, beta,
+                                          k, G, pr, e_fix, Cg)
+
+    for name, arr, grad in (("x", x, g.dx), ("w_r", w_r, g.dw_r), ("b_r", b_r, g.db_r),
+                            ("w1", w1, g.dw1), ("w2", w2, g.dw2)):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            p, m = arr.copy(), arr.copy()
+            p[idx] += h
+            m[idx] -= h
+            num[idx] = (J(**{name: p}) - J(**{name: m})) / (2 * h)
+        np.testing.assert_allclose(grad, num, rtol=1e-6, atol=2e-8, err_msg=f"d{name}")
+
+
+def pin_backward_soft_mixture_autograd(so):
+    """k = E with nothing dropped (c = 1, two groups): the layer is
+    x + sum_e p_te FFN_e(x_t) and the balance loss is the constant alpha
+    (f = 1/E in every group), so the gradients, z-loss included, are torch
+    autograd's of that dense formula."""
+    x, w_r, b_r, w1, w2 = _fd_problem(55, T=20, E=3)
+    beta, alpha = 0.04, 0.2
+    dout = _rng(56).standard_normal(x.shape)
+    g = so.layer_backward_grouped(x, w_r, b_r, w1, w2, 1.0, alpha, dout, k=3, G=10, beta=beta)
+    X, WR, BR, W1, W2 = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (x, w_r, b_r, w1, w2))
+    z = X @ WR + BR
+    H = torch.relu(torch.einsum("td,efd->tef", X, W1))
+    Y = torch.einsum("tef,edf->ted", H, W2)
+    out = X + torch.einsum("te,ted->td", torch.softmax(z, dim=1), Y)
+    J = (out * torch.tensor(dout)).sum() + beta * (torch.logsumexp(z, dim=1) ** 2).mean()
+    J.backward()
+    for name, t in (("dx", X), ("dw_r", WR), ("db_r", BR), ("dw1", W1), ("dw2", W2)):
+        np.testing.assert_allclose(getattr(g, name), t.grad.numpy(), rtol=1e-11, atol=1e-13, err_msg=name)
+
+
+GROUP_BACKWARD_PINS = [pin_backward_grouped_reduces_to_hot_path, pin_backward_grouped_finite_differences,
+                       pin_backward_soft_mixture_autograd]
+ALL_PINS.extend(GROUP_BACKWARD_PINS)

@@ -325,3 +325,31 @@ def test_backward_pins_catch_mutant(edit):
         except Exception:
             failed.append(pin.__name__)
     assert failed, f"no backward pin caught {new}"
+
+
+# ------------------- grouped / top-k backward: mistakes planted in the source text
+GROUP_BACKWARD_EDITS = [
+    ("gr = r.gate[toks, ranks]", "gr = r.gate[toks, 0]"),                               # first choice's gate
+    ("dgate[toks, ranks] = np.sum(", "dgate[toks, 0] = np.sum("),                       # dgate on rank 0
+    ("dz += (dgate[:, i] * r.gate[:, i])", "dz += (dgate[:, i] * r.gate[:, 0])"),       # wrong gate in dz
+    ("on = (acts > 0) if relu_active", "on = 1.0 if relu_active"),                      # no ReLU mask
+    ("np.add.at(dx, toks, dar @ W1)", "np.add.at(dx, toks, 0 * (dar @ W1))"),           # no expert path
+    ("dz += L.aux.dlogits", "dz += 0 * L.aux.dlogits"),                                 # aux gradient lost
+    ("dz += router_z_loss(L.z, beta).dlogits", "dz += 0 * router_z_loss(L.z, beta).dlogits"),   # z-loss lost
+    ("dx += dz @ wr.T", "dx += 0 * (dz @ wr.T)"),                                       # no router path
+]
+
+
+@pytest.mark.parametrize("edit", GROUP_BACKWARD_EDITS, ids=lambda e: e[1][:30])
+def test_group_backward_pins_catch_mutant(edit):
+    old, new = edit
+    assert SRC.count(old) == 1, old
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(SRC.replace(old, new), "oracle_mutant", "exec"), mod.__dict__)
+    failed = []
+    for pin in pins.GROUP_BACKWARD_PINS:
+        try:
+            pin(mod)
+        except Exception:
+            failed.append(pin.__name__)
+    assert failed, f"no grouped backward pin caught {new}"
