@@ -326,9 +326,9 @@ switch_status switch_aux_loss_ex(const int32_t *counts, const float *prob_sum, c
 /* ------------------------------------------------------------- backward
  *
  * Gradients of  J = sum_t <dout_t, out_t> + L_aux (+ L_z)  for the Switch
- * layer (one routing group, k = 1), with the choices and capacity masks of
- * the forward held fixed: argmax has no gradient and the router learns
- * through the selected gate.  Sources: wq-win note sec. 2 (the router stays
+ * layer, and for its routing-group / top-k form, with the choices and
+ * capacity masks of the forward held fixed: argmax has no gradient and the
+ * router learns through the selected gates.  Sources: wq-win note sec. 2 (the router stays
  * differentiable through p_e*; the balance loss is added to the training
  * loss); zffjzz.top note, "troubleshooting" (finite differences that keep the
  * discrete choices and masks).
@@ -339,6 +339,13 @@ switch_status switch_aux_loss_ex(const int32_t *counts, const float *prob_sum, c
  *   dz_tj = dgate_t g_t (delta_{j e} - p_tj) + dL_aux/dz_tj (+ dL_z/dz_tj)
  *   dW_r = x^T dz;  db_r = sum_t dz_t;  dx_t += W_r dz_t
  * Dropped tokens: dx_t = dout_t + W_r dz_t.
+ * With k choices every kept choice (t, i) is one buffer row and follows the
+ * rule above with its own gate g_ti = p_{t, e_ti}; dx_t adds the dA W1 terms
+ * of all kept choices and dz_tj = sum_i dgate_ti g_ti (delta_{j e_ti} - p_tj)
+ * + dL_aux/dz_tj (+ dL_z/dz_tj), the aux term with the f of the token's group.
+ * Sources for that form: "Mixture of experts" (world.lapla.si), "full means
+ * turned back" (top-k gates, no renormalisation); zffjzz.top note,
+ * "evaluation protocol" (per-group statistics).
  *
  * Precision: dy and dA are rounded to bf16 (the MFMA inputs), the GEMMs
  * accumulate in fp32, weight and router gradients are fp32, dx is rounded to
@@ -369,15 +376,31 @@ typedef struct switch_layer_bwd_args {
     float *dw1;                  /* [E, d_ff, d] */
     float *dw2;                  /* [E, d, d_ff] */
     float *dz;                   /*     [T, E] total gradient at the logits, or NULL */
-    float *dgate;                /*     [T] <dout_t, y_t> for kept tokens (0 if dropped), or NULL */
+    float *dgate;                /*     [T] (or [T, k]) <dout_t, y[e, s]> for kept choices (0 if
+                                  *     dropped), or NULL */
     /* sizes */
     int64_t T;
     int32_t d, d_ff, E, C;
     float alpha;                 /* aux-loss weight of the forward */
     float z_beta;                /* z-loss weight (0: no z-loss term) */
+    /* routing groups and top-k, as in switch_layer_args; zero selects the
+     * Switch layer (k = 0 means 1, group = 0 one group of T tokens).  With
+     * k > 1, expert/gate/position/keep/dgate are [T, k]; with several groups
+     * f is [T / group, E], C is the capacity of one group, buf/h/y have
+     * (T / group) * C rows per expert, and slot and accepted_total replace
+     * position and accepted (which are then not read). */
+    int32_t k;                   /* choices per token, 1 .. 4 */
+    int64_t group;               /* tokens per routing group */
+    const int32_t *slot;         /* [T, k] buffer row of each kept choice (several groups) */
+    const int32_t *accepted_total; /* [E] filled buffer rows per expert (several groups) */
 } switch_layer_bwd_args;
 
+/* Workspace of switch_layer_bwd: switch_layer_bwd_workspace_bytes_ex(T, d, d_ff,
+ * E, C, k, group) with C the capacity of one group; the plain query is its
+ * k = 1, one-group case.  Both return 0 for sizes the layer rejects. */
 size_t switch_layer_bwd_workspace_bytes(int64_t T, int32_t d, int32_t d_ff, int32_t E, int32_t C);
+size_t switch_layer_bwd_workspace_bytes_ex(int64_t T, int32_t d, int32_t d_ff, int32_t E, int32_t C, int32_t k,
+                                           int64_t group);
 switch_status switch_layer_bwd(const switch_layer_bwd_args *a, void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------- measurement */

@@ -28,6 +28,7 @@ EXPORTS = [
     "switch_profile_collect", "switch_kernel_name", "switch_router_z_loss",
     "switch_route_ex", "switch_dispatch_ex", "switch_dispatch_workspace_bytes_ex", "switch_combine_ex",
     "switch_aux_loss_ex", "switch_workspace_bytes_ex", "switch_layer_bwd", "switch_layer_bwd_workspace_bytes",
+    "switch_layer_bwd_workspace_bytes_ex",
 ]
 
 
@@ -54,7 +55,9 @@ class LayerBwdArgs(ctypes.Structure):
         "x", "w_r", "w1", "w2", "expert", "gate", "position", "keep", "accepted", "f", "logits", "lse", "buf", "h",
         "y", "dout", "dx", "dw_r", "db_r", "dw1", "dw2", "dz", "dgate")] + [
         ("T", ctypes.c_int64), ("d", ctypes.c_int32), ("d_ff", ctypes.c_int32), ("E", ctypes.c_int32),
-        ("C", ctypes.c_int32), ("alpha", ctypes.c_float), ("z_beta", ctypes.c_float)]
+        ("C", ctypes.c_int32), ("alpha", ctypes.c_float), ("z_beta", ctypes.c_float),
+        ("k", ctypes.c_int32), ("group", ctypes.c_int64), ("slot", ctypes.c_void_p),
+        ("accepted_total", ctypes.c_void_p)]
 
 
 def lib():
@@ -93,6 +96,7 @@ def lib():
             "switch_aux_loss_ex": (I32, [P, P, P, P, I64, I32, I32, I64, F32, P, P, P, P, P]),
             "switch_workspace_bytes_ex": (SZ, [I64, I32, I32, I32, I32, I32, I64]),
             "switch_layer_bwd_workspace_bytes": (SZ, [I64, I32, I32, I32, I32]),
+            "switch_layer_bwd_workspace_bytes_ex": (SZ, [I64, I32, I32, I32, I32, I32, I64]),
             "switch_layer_bwd": (I32, [ctypes.POINTER(LayerBwdArgs), P, SZ, P]),
         }
         for name, (res, args) in sig.items():
@@ -241,29 +245,37 @@ def switch_layer_bwd_workspace_bytes(T, d, d_ff, E, C):
     return lib().switch_layer_bwd_workspace_bytes(T, d, d_ff, E, C)
 
 
+def switch_layer_bwd_workspace_bytes_ex(T, d, d_ff, E, C, k, group):
+    return lib().switch_layer_bwd_workspace_bytes_ex(T, d, d_ff, E, C, k, group)
+
+
 def switch_layer_bwd(args: LayerBwdArgs, ws, stream=None):
     wp, wn = _ws(ws)
     _check(lib().switch_layer_bwd(ctypes.byref(args), wp, wn, _stream(stream)), "switch_layer_bwd")
 
 
 def make_layer_bwd_args(fwd: dict, x, w_r, w1, w2, dout, grads: dict, T, d, d_ff, E, C, alpha,
-                        z_beta=0.0) -> LayerBwdArgs:
+                        z_beta=0.0, k=1, group=0) -> LayerBwdArgs:
     """fwd: the forward's tensors (expert, gate, position, keep, accepted, f,
-    logits, lse, buf, h, y); grads: dx, dw_r, db_r, dw1, dw2 and optionally
-    dz, dgate."""
+    logits, lse, buf, h, y, and with several groups slot and accepted_total);
+    grads: dx, dw_r, db_r, dw1, dw2 and optionally dz, dgate.  C is the
+    capacity of one routing group."""
     a = LayerBwdArgs()
     for name, v in (("x", x), ("w_r", w_r), ("w1", w1), ("w2", w2), ("dout", dout)):
         setattr(a, name, _ptr(v))
-    for name in ("expert", "gate", "position", "keep", "accepted", "f", "logits", "lse", "buf", "h", "y"):
+    for name in ("expert", "gate", "position", "keep", "accepted", "f", "logits", "lse", "buf", "h", "y", "slot",
+                 "accepted_total"):
         setattr(a, name, _ptr(fwd.get(name)))
     for name in ("dx", "dw_r", "db_r", "dw1", "dw2", "dz", "dgate"):
         setattr(a, name, _ptr(grads.get(name)))
     a.T, a.d, a.d_ff, a.E, a.C, a.alpha, a.z_beta = T, d, d_ff, E, C, alpha, z_beta
+    a.k, a.group = k, group
     return a
 
 
-def layer_bwd_tensors(T, d, d_ff, E, C, device="cuda", inspect=False):
-    """Gradient tensors of switch_layer_bwd (plus its workspace)."""
+def layer_bwd_tensors(T, d, d_ff, E, C, device="cuda", inspect=False, k=1, group=0):
+    """Gradient tensors of switch_layer_bwd (plus its workspace); C is the
+    capacity of one routing group."""
     import torch
     dev = torch.device(device)
     g = {
@@ -275,9 +287,9 @@ def layer_bwd_tensors(T, d, d_ff, E, C, device="cuda", inspect=False):
     }
     if inspect:
         g["dz"] = torch.empty((T, E), dtype=torch.float32, device=dev)
-        g["dgate"] = torch.empty(T, dtype=torch.float32, device=dev)
-    g["ws"] = torch.empty(max(256, switch_layer_bwd_workspace_bytes(T, d, d_ff, E, C)), dtype=torch.uint8,
-                          device=dev)
+        g["dgate"] = torch.empty((T,) if k == 1 else (T, k), dtype=torch.float32, device=dev)
+    g["ws"] = torch.empty(max(256, switch_layer_bwd_workspace_bytes_ex(T, d, d_ff, E, C, k, group)),
+                          dtype=torch.uint8, device=dev)
     return g
 
 

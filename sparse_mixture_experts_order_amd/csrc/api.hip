@@ -424,7 +424,7 @@ switch_status run_aux(const AuxArgs& a, hipStream_t s) {
     if (a.dlogits && a.T > 0)
         LAUNCH(K_AUX_GRAD, "aux_grad", s,
                launch_aux_grad(a.logits, a.lse, a.f, a.T, Gt, a.E, a.alpha, a.z_loss ? a.beta : 0.f, nullptr, nullptr,
-                               nullptr, 0, a.dlogits,
+                               nullptr, 1, 0, a.dlogits,
                                s));
     return SWITCH_OK;
 }
@@ -521,7 +521,8 @@ static size_t layer_ws(int64_t T, int32_t d, int32_t d_ff, int32_t E, int32_t C,
 // ----------------------------------------------------------- layer backward
 static int64_t pad64(int64_t n) { return (n + 63) / 64 * 64; }
 
-static size_t layer_bwd_ws(int64_t T, int32_t d, int32_t d_ff, int32_t E, int32_t C) {
+// C: the buffer rows per expert (groups x the capacity of one group)
+static size_t layer_bwd_ws(int64_t T, int32_t d, int32_t d_ff, int32_t E, int32_t C, int32_t k) {
     const size_t Cp = (size_t)pad64(C), e = (size_t)E;
     size_t n = 0;
     n += up(e * C * d * sizeof(bf16_t));          // dy
@@ -532,7 +533,7 @@ static size_t layer_bwd_ws(int64_t T, int32_t d, int32_t d_ff, int32_t E, int32_
     n += up(e * d * Cp * sizeof(bf16_t));         // buf^T
     n += up(e * C * d * sizeof(float));           // dbuf
     n += up((size_t)T * E * sizeof(float));       // dz
-    n += up((size_t)T * sizeof(float));           // dgate
+    n += up((size_t)T * k * sizeof(float));       // dgate
     n += up((size_t)std::max(router_wgrad_slices(T, d, E), 1) * d * E * sizeof(float));   // dW_r slices
     n += up((size_t)column_sum_slices(T) * E * sizeof(float));                              // db_r slices
     n += 3 * up((e + 1) * sizeof(int32_t));       // tile prefixes: token rows, d rows, d_ff rows
@@ -543,7 +544,17 @@ static size_t layer_bwd_ws(int64_t T, int32_t d, int32_t d_ff, int32_t E, int32_
 
 size_t switch_layer_bwd_workspace_bytes(int64_t T, int32_t d, int32_t d_ff, int32_t E, int32_t C) {
     if (T < 0 || d < 1 || d_ff < 1 || E < 1 || E > 4096 || C < 0 || T >= (int64_t(1) << 31)) return 0;
-    return layer_bwd_ws(T, d, d_ff, E, C);
+    return layer_bwd_ws(T, d, d_ff, E, C, 1);
+}
+
+size_t switch_layer_bwd_workspace_bytes_ex(int64_t T, int32_t d, int32_t d_ff, int32_t E, int32_t C, int32_t k,
+                                           int64_t group) {
+    if (T < 0 || d < 1 || d_ff < 1 || E < 1 || E > 4096 || C < 0 || T >= (int64_t(1) << 31)) return 0;
+    if (k < 1 || k > kMaxTopK || group < 0 || T * k >= (int64_t(1) << 31)) return 0;
+    if (!one_group(T, group) && T % group != 0) return 0;
+    const int64_t rows = buffer_rows(T, group, C);
+    if ((int64_t)E * rows >= (int64_t(1) << 31)) return 0;
+    return layer_bwd_ws(T, d, d_ff, E, (int32_t)rows, k);
 }
 
 switch_status switch_layer_bwd(const switch_layer_bwd_args* ba, void* ws, size_t ws_bytes, void* stream) {
@@ -552,9 +563,17 @@ switch_status switch_layer_bwd(const switch_layer_bwd_args* ba, void* ws, size_t
     const switch_layer_bwd_args& B = *ba;
     hipStream_t s = (hipStream_t)stream;
     const int64_t T = B.T;
-    const int32_t d = B.d, F = B.d_ff, E = B.E, C = B.C;
+    const int32_t d = B.d, F = B.d_ff, E = B.E, Cg = B.C;
+    const int32_t k = B.k == 0 ? 1 : B.k;
+    const int64_t G = B.group;
     CHECK(check_TE(T, E));
-    CHECK(check_C(E, C));
+    CHECK(check_C(E, Cg));
+    CHECK(check_kG(T, E, k, G));
+    const bool one = one_group(T, G);
+    const int64_t rows64 = buffer_rows(T, G, Cg);
+    SUPPORT((int64_t)E * rows64 < (int64_t(1) << 31), "E * groups * C must be < 2^31");
+    // from here on C is the buffer rows per expert (groups x the capacity of one group)
+    const int32_t C = (int32_t)rows64;
     REQUIRE(d >= 1 && F >= 1, "d and d_ff must be >= 1");
     SUPPORT(d % 64 == 0 && F % 64 == 0, "d and d_ff must be multiples of 64 (got %d, %d)", d, F);
     SUPPORT((int64_t)E * std::max<int64_t>(pad64(C), std::max(d, F)) * std::max(d, F) < (int64_t(1) << 40),
@@ -562,18 +581,23 @@ switch_status switch_layer_bwd(const switch_layer_bwd_args* ba, void* ws, size_t
     REQUIRE(std::isfinite(B.alpha) && std::isfinite(B.z_beta), "alpha and z_beta must be finite");
     SUPPORT((int64_t)d * F * 2 < (int64_t(1) << 31), "one expert's weights must be < 2 GiB (d*d_ff*2)");
     SUPPORT((int64_t)pad64(C) * std::max(d, F) * 2 < (int64_t(1) << 31), "C*max(d,d_ff)*2 must be < 2 GiB");
+    // one group: the buffer row is the position and accepted counts the filled rows
+    const int32_t* slot = one ? B.position : B.slot;
+    const int32_t* filled = one ? B.accepted : B.accepted_total;
     const bool tok = T > 0;
     NONNULL_IF(tok, B.x); NONNULL(B.w_r); NONNULL(B.w1); NONNULL(B.w2);
-    NONNULL_IF(tok, B.expert); NONNULL_IF(tok, B.gate); NONNULL_IF(tok, B.position); NONNULL_IF(tok, B.keep);
-    NONNULL(B.accepted); NONNULL(B.f); NONNULL_IF(tok, B.logits); NONNULL_IF(tok, B.lse);
+    NONNULL_IF(tok, B.expert); NONNULL_IF(tok, B.gate); NONNULL_IF(tok, B.keep);
+    if (one) { NONNULL_IF(tok, B.position); NONNULL(B.accepted); }
+    else { NONNULL_IF(tok, B.slot); NONNULL(B.accepted_total); }
+    NONNULL(B.f); NONNULL_IF(tok, B.logits); NONNULL_IF(tok, B.lse);
     NONNULL_IF(C > 0, B.buf); NONNULL_IF(C > 0, B.h); NONNULL_IF(C > 0, B.y); NONNULL_IF(tok, B.dout);
     NONNULL_IF(tok, B.dx); NONNULL(B.dw_r); NONNULL(B.db_r); NONNULL(B.dw1); NONNULL(B.dw2);
     ALIGNED16(B.x); ALIGNED16(B.w1); ALIGNED16(B.w2); ALIGNED16(B.buf); ALIGNED16(B.h); ALIGNED16(B.y);
     ALIGNED16(B.dout); ALIGNED16(B.dx); ALIGNED16(B.dw1); ALIGNED16(B.dw2);
     ALIGNED4(B.w_r); ALIGNED4(B.expert); ALIGNED4(B.gate); ALIGNED4(B.position); ALIGNED4(B.accepted);
     ALIGNED4(B.f); ALIGNED4(B.logits); ALIGNED4(B.lse); ALIGNED4(B.dw_r); ALIGNED4(B.db_r); ALIGNED4(B.dz);
-    ALIGNED4(B.dgate);
-    const size_t need = layer_bwd_ws(T, d, F, E, C);
+    ALIGNED4(B.dgate); ALIGNED4(B.slot); ALIGNED4(B.accepted_total);
+    const size_t need = layer_bwd_ws(T, d, F, E, C, k);
     if (ws_bytes < need) return fail(SWITCH_E_WORKSPACE, "layer backward needs %zu workspace bytes, got %zu", need, ws_bytes);
     REQUIRE(ws != nullptr, "ws must not be NULL");
     REQUIRE(aligned(ws, kAlign), "ws must be %zu-byte aligned", kAlign);
@@ -588,7 +612,7 @@ switch_status switch_layer_bwd(const switch_layer_bwd_args* ba, void* ws, size_t
     bf16_t* bufT = c.take<bf16_t>((size_t)E * d * Cp);
     float* dbuf = c.take<float>((size_t)E * C * d);
     float* dz = c.take<float>((size_t)T * E);
-    float* dgate = c.take<float>((size_t)T);
+    float* dgate = c.take<float>((size_t)T * k);
     float* part = c.take<float>((size_t)std::max(router_wgrad_slices(T, d, E), 1) * d * E);
     float* dbs = c.take<float>((size_t)column_sum_slices(T) * E);
     int32_t* pre_c = c.take<int32_t>((size_t)E + 1);
@@ -603,32 +627,33 @@ switch_status switch_layer_bwd(const switch_layer_bwd_args* ba, void* ws, size_t
 
     // gate and router: dgate, then dz = task + aux (+ z) gradient, db_r, dW_r
     LAUNCH(K_COMBINE_BWD, "combine_bwd", s,
-           launch_combine_bwd(B.dout, B.y, B.expert, B.position, B.keep, B.gate, T, d, E, C, dy, dgate, s));
+           launch_combine_bwd(B.dout, B.y, B.expert, slot, B.keep, B.gate, T, k, d, E, C, dy, dgate, s));
     if (tok)
         LAUNCH(K_ROUTER_DZ, "router_dz", s,
-               launch_aux_grad(B.logits, B.lse, B.f, T, T, E, B.alpha, B.z_beta, B.expert, B.gate, dgate, 0, dz, s));
+               launch_aux_grad(B.logits, B.lse, B.f, T, group_tokens(T, G), E, B.alpha, B.z_beta, B.expert, B.gate,
+                               dgate, k, 0, dz, s));
     LAUNCH(K_ROUTER_DB, "router_db", s, launch_column_sum(dz, (int)T, E, dbs, B.db_r, s));
     LAUNCH(K_ROUTER_WGRAD, "router_wgrad", s, launch_router_wgrad(x, dz, T, d, E, part, B.dw_r, s));
     // experts: the two products with the weights read W1 and W2 as stored
     // (K-major).  The weight gradients take the token axis as K: with d, d_ff
     // > 64 they read dy, H, dA and buf as stored (K-major operands, rows past
-    // accepted read as zero), else transposed copies of them
+    // the filled ones read as zero), else transposed copies of them
     const bool tn = ffn_wide_tiles(d) && ffn_wide_tiles(F);
     if (C > 0) {
         if (!tn) {
-            LAUNCH(K_TRANSPOSE, "transpose_rows", s, launch_transpose_rows(dy, dyT, E, C, d, Cp, B.accepted, s));
-            LAUNCH(K_TRANSPOSE, "transpose_rows", s, launch_transpose_rows(B.h, hT, E, C, F, Cp, B.accepted, s));
-            LAUNCH(K_TRANSPOSE, "transpose_rows", s, launch_transpose_rows(B.buf, bufT, E, C, d, Cp, B.accepted, s));
+            LAUNCH(K_TRANSPOSE, "transpose_rows", s, launch_transpose_rows(dy, dyT, E, C, d, Cp, filled, s));
+            LAUNCH(K_TRANSPOSE, "transpose_rows", s, launch_transpose_rows(B.h, hT, E, C, F, Cp, filled, s));
+            LAUNCH(K_TRANSPOSE, "transpose_rows", s, launch_transpose_rows(B.buf, bufT, E, C, d, Cp, filled, s));
         }
         // the token tiles of the data products, and the d- and d_ff-row tiles of the
-        // weight gradients (carrying each expert's accepted count), in one launch
+        // weight gradients (carrying each expert's filled row count), in one launch
         FfnTileLists tl{};
         tl.E = E;
-        tl.list[0] = FfnTileListSpec{B.accepted, nullptr, C, pre_c, tt_c};
-        // (the fourth word is the accepted count only for the K-major products;
+        tl.list[0] = FfnTileListSpec{filled, nullptr, C, pre_c, tt_c};
+        // (the fourth word is the filled row count only for the K-major products;
         // the transposed path's GEMM reads it as the tile count of the expert)
-        tl.list[1] = FfnTileListSpec{nullptr, tn ? B.accepted : nullptr, d, pre_d, tt_d};
-        tl.list[2] = FfnTileListSpec{nullptr, tn ? B.accepted : nullptr, F, pre_f, tt_f};
+        tl.list[1] = FfnTileListSpec{nullptr, tn ? filled : nullptr, d, pre_d, tt_d};
+        tl.list[2] = FfnTileListSpec{nullptr, tn ? filled : nullptr, F, pre_f, tt_f};
         LAUNCH(K_FFN_TILES, "ffn_tile_prefix", s, launch_ffn_tile_lists(tl, 3, s));
         // dA = (dy W2) * [H > 0]          rows: tokens, K = d, N = d_ff; W2[e] is [d][d_ff]
         LAUNCH(K_GEMM_DA, "gemm_dA", s,
@@ -636,7 +661,7 @@ switch_status switch_layer_bwd(const switch_layer_bwd_args* ba, void* ws, size_t
         // dbuf = dA W1                    rows: tokens, K = d_ff, N = d; W1[e] is [d_ff][d]
         LAUNCH(K_GEMM_DBUF, "gemm_dbuf", s,
                launch_grouped_gemm_kmajor_f32(dA, B.w1, pre_c, tt_c, dbuf, E, C, F, d, s));
-        if (!tn) LAUNCH(K_TRANSPOSE, "transpose_rows", s, launch_transpose_rows(dA, dAT, E, C, F, Cp, B.accepted, s));
+        if (!tn) LAUNCH(K_TRANSPOSE, "transpose_rows", s, launch_transpose_rows(dA, dAT, E, C, F, Cp, filled, s));
     }
     // weight gradients: K = the (zero-padded) token axis
     if (C > 0) {
@@ -655,9 +680,9 @@ switch_status switch_layer_bwd(const switch_layer_bwd_args* ba, void* ws, size_t
         LAUNCH(K_GEMM_DW2, "zero", s, launch_fill_zero(B.dw2, (int64_t)E * d * F, s));
         LAUNCH(K_GEMM_DW1, "zero", s, launch_fill_zero(B.dw1, (int64_t)E * d * F, s));
     }
-    // dx = dout + dbuf (kept tokens) + dz W_r^T
+    // dx = dout + sum of the kept choices' dbuf rows + dz W_r^T
     LAUNCH(K_DX, "dx_assemble", s,
-           launch_dx_assemble(B.dout, dbuf, B.expert, B.position, B.keep, dz, B.w_r, T, d, E, C, B.dx, s));
+           launch_dx_assemble(B.dout, dbuf, B.expert, slot, B.keep, dz, B.w_r, T, d, E, k, C, B.dx, s));
     return SWITCH_OK;
 }
 
@@ -791,7 +816,7 @@ switch_status switch_router_z_loss(const float* lse, const float* logits, int64_
     LAUNCH(K_Z_LOSS, "z_loss", s, launch_z_loss(lse, T, beta, z_loss, s));
     if (dlogits && T > 0)
         LAUNCH(K_AUX_GRAD, "aux_grad", s,
-               launch_aux_grad(logits, lse, nullptr, T, T, E, 0.f, beta, nullptr, nullptr, nullptr, accumulate,
+               launch_aux_grad(logits, lse, nullptr, T, T, E, 0.f, beta, nullptr, nullptr, nullptr, 1, accumulate,
                                dlogits, s));
     return SWITCH_OK;
 }

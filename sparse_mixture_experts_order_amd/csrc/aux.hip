@@ -44,9 +44,10 @@ __global__ __launch_bounds__(1024) void z_loss_reduce(const float* __restrict__ 
 //   G_tj = p_tj * (c_aux (f_j - sum_e f_e p_te) + c_z lse_t)
 // c_aux = alpha E / T (aux, f held constant; f is the row of the token's
 // routing group of G tokens), c_z = 2 beta / T (z-loss).
-// With dgate (the layer backward) the task gradient through the selected gate
-// is added:  + dgate_t gate_t (delta_{j e*_t} - p_tj)  (d p_te / d z_tj =
-// p_te (delta_ej - p_tj)).
+// With dgate (the layer backward) the task gradient through the selected
+// gates is added:  + sum_i dgate_ti gate_ti (delta_{j e_ti} - p_tj) over the
+// token's k choices  (d p_te / d z_tj = p_te (delta_ej - p_tj)); expert, gate
+// and dgate are [T, k].
 // One wave per token row; lane j holds experts j, j+64, ...  With
 // `accumulate` the result is added to dlogits instead of stored.
 template <int NCH>
@@ -54,7 +55,7 @@ __global__ __launch_bounds__(256) void aux_grad(const float* __restrict__ logits
                                                 const float* __restrict__ f, int64_t T, int64_t G, int E, float c_aux,
                                                 float c_z, const int32_t* __restrict__ expert,
                                                 const float* __restrict__ gate, const float* __restrict__ dgate,
-                                                int accumulate, float* __restrict__ dlogits) {
+                                                int k, int accumulate, float* __restrict__ dlogits) {
     const int lane = threadIdx.x & 63;
     const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
@@ -72,14 +73,26 @@ __global__ __launch_bounds__(256) void aux_grad(const float* __restrict__ logits
     }
     s = wave_sum(s);
     const float zt = c_z * l;
-    const float dg = dgate ? dgate[t] * gate[t] : 0.f;
-    const int es = dgate ? expert[t] : -1;
+    // the gate terms: dg_i = dgate_ti gate_ti of choice i, and their sum
+    float dgi[kMaxTopK];
+    int es[kMaxTopK];
+    float dg = 0.f;
+#pragma unroll
+    for (int c = 0; c < kMaxTopK; ++c) {
+        const bool on = dgate && c < k;
+        dgi[c] = on ? dgate[t * k + c] * gate[t * k + c] : 0.f;
+        es[c] = on ? expert[t * k + c] : -1;
+        dg += dgi[c];
+    }
     float* g = dlogits + t * E;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
         const int e = lane + 64 * i;
         if (e < E) {
-            const float v = p[i] * (c_aux * (fr[i] - s) + zt - dg) + (e == es ? dg : 0.f);
+            float sel = 0.f;
+#pragma unroll
+            for (int c = 0; c < kMaxTopK; ++c) sel += e == es[c] ? dgi[c] : 0.f;
+            const float v = p[i] * (c_aux * (fr[i] - s) + zt - dg) + sel;
             g[e] = accumulate ? g[e] + v : v;
         }
     }
@@ -98,7 +111,7 @@ hipError_t launch_z_loss(const float* lse, int64_t T, float beta, float* z_loss,
 
 hipError_t launch_aux_grad(const float* logits, const float* lse, const float* f, int64_t T, int64_t G, int E,
                            float alpha, float beta, const int32_t* expert, const float* gate, const float* dgate,
-                           int accumulate, float* dlogits, hipStream_t s) {
+                           int k, int accumulate, float* dlogits, hipStream_t s) {
     if (T == 0) return hipSuccess;
     const float c_aux = f ? (float)((double)alpha * (double)E / (double)T) : 0.f;
     const float c_z = (float)(2.0 * (double)beta / (double)T);
@@ -106,7 +119,7 @@ hipError_t launch_aux_grad(const float* logits, const float* lse, const float* f
     const int nch = (E + 63) / 64;
 #define SWMOE_GRAD(N)                                                                                          \
     hipLaunchKernelGGL(aux_grad<N>, dim3(grid), dim3(256), 0, s, logits, lse, f, T, std::max<int64_t>(G, 1), E, \
-                       c_aux, c_z, expert, gate, dgate, accumulate, dlogits)
+                       c_aux, c_z, expert, gate, dgate, k, accumulate, dlogits)
     if (nch <= 1) SWMOE_GRAD(1);
     else if (nch <= 2) SWMOE_GRAD(2);
     else if (nch <= 4) SWMOE_GRAD(4);

@@ -1,7 +1,9 @@
 // Backward of the Switch layer: gradients of  sum_t <dout_t, out_t> + L_aux
 // (+ L_z)  with respect to x, W1, W2, W_r and b_r, the choices and capacity
 // masks held fixed (argmax has no gradient; the router learns through the
-// selected gate).
+// selected gate).  With routing groups and top-k choices every kept (token,
+// choice) is one buffer row of its expert and gets the single-choice chain
+// rule with its own gate; a token's input gradient adds all its choices.
 //
 // Sources: "042 Switch Transformer" (wq-win.github.io) sec. 2: the router stays
 // differentiable through the selected gate p_e*, and the balance loss is added
@@ -10,14 +12,16 @@
 // leave the discrete choices and masks unchanged.
 //
 // Kernels here (the expert GEMMs reuse expert_gemm):
-//   combine_bwd     dy[e, s] = bf16(gate_t dout_t) for kept tokens and
-//                   dgate_t = <dout_t, y[e, s]> (fp32), one wave per token
+//   combine_bwd     dy[e, s] = bf16(gate_ti dout_t) for kept choices (buffer
+//                   row s of expert e) and dgate_ti = <dout_t, y[e, s]> (fp32),
+//                   one wave per (token, choice)
 //   transpose_rows  [E][R][S] -> [E][S][Rp] bf16 through 64x64 LDS tiles,
 //                   zero for rows >= valid[e] (the token axis of activations)
 //   router_wgrad    dW_r partial sums over token slices (fp32 MFMA), then
 //   router_wgrad_reduce  the slices added in order in fp64
-//   dx_assemble     dx_t = bf16(dout_t + dbuf[e, s] + sum_e dz_te W_r[:, e])
-//                   (dx_assemble_mfma on the fp32 MFMA when E is a multiple of 8)
+//   dx_assemble     dx_t = bf16(dout_t + sum_e dz_te W_r[:, e] + sum_i dbuf[e_ti, s_ti])
+//                   over the token's kept choices (dx_assemble_mfma on the fp32
+//                   MFMA when E is a multiple of 32)
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -25,22 +29,23 @@ namespace swmoe {
 
 __global__ __launch_bounds__(256) void combine_bwd(const bf16_t* __restrict__ dout, const float* __restrict__ y,
                                                    const int32_t* __restrict__ expert,
-                                                   const int32_t* __restrict__ position,
+                                                   const int32_t* __restrict__ slot,
                                                    const uint8_t* __restrict__ keep, const float* __restrict__ gate,
-                                                   int64_t T, int d, int E, int C, bf16_t* __restrict__ dy,
+                                                   int N, int k, int d, int E, int R, bf16_t* __restrict__ dy,
                                                    float* __restrict__ dgate) {
     const int lane = threadIdx.x & 63;
-    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= T) return;
-    const int e = expert[t], pos = position[t];
-    if (!keep[t] || e < 0 || e >= E || pos < 0 || pos >= C) {
-        if (lane == 0) dgate[t] = 0.f;
+    const int n = blockIdx.x * 4 + (threadIdx.x >> 6);   // assignment (token n / k, choice n % k)
+    if (n >= N) return;
+    const int64_t t = k == 1 ? n : n / k;
+    const int e = expert[n], pos = slot[n];
+    if (!keep[n] || e < 0 || e >= E || pos < 0 || pos >= R) {
+        if (lane == 0) dgate[n] = 0.f;
         return;
     }
-    const float g = gate[t];
+    const float g = gate[n];
     const bf16_t* drow = dout + t * d;
-    const float* yrow = y + ((size_t)e * C + pos) * d;
-    bf16_t* dyrow = dy + ((size_t)e * C + pos) * d;
+    const float* yrow = y + ((size_t)e * R + pos) * d;
+    bf16_t* dyrow = dy + ((size_t)e * R + pos) * d;
     float acc = 0.f;
     for (int c = lane * 8; c < d; c += 64 * 8) {
         const uint4 dv = *(const uint4*)(drow + c);
@@ -58,7 +63,7 @@ __global__ __launch_bounds__(256) void combine_bwd(const bf16_t* __restrict__ do
         *(uint4*)(dyrow + c) = make_uint4(o[0], o[1], o[2], o[3]);
     }
     acc = wave_sum(acc);
-    if (lane == 0) dgate[t] = acc;
+    if (lane == 0) dgate[n] = acc;
 }
 
 // dst[e][c][r] = src[e][r][c] for r < valid (valid[e], or R), else 0; r < Rp.
@@ -252,10 +257,10 @@ __global__ __launch_bounds__(256) void router_wgrad_reduce(const float* __restri
 // chunks of 32.
 __global__ __launch_bounds__(256) void dx_assemble(const bf16_t* __restrict__ dout, const float* __restrict__ dbuf,
                                                    const int32_t* __restrict__ expert,
-                                                   const int32_t* __restrict__ position,
+                                                   const int32_t* __restrict__ slot,
                                                    const uint8_t* __restrict__ keep, const float* __restrict__ dz,
-                                                   const float* __restrict__ w_r, int64_t T, int d, int E, int C,
-                                                   bf16_t* __restrict__ dx) {
+                                                   const float* __restrict__ w_r, int64_t T, int d, int E, int k,
+                                                   int R, bf16_t* __restrict__ dx) {
     __shared__ __attribute__((aligned(16))) float zs[32][68];   // [e][token] (rows padded against bank conflicts)
     __shared__ __attribute__((aligned(16))) float ws[32][68];   // [e][i]
     const int64_t t0 = (int64_t)blockIdx.y * 64;
@@ -289,10 +294,13 @@ __global__ __launch_bounds__(256) void dx_assemble(const bf16_t* __restrict__ do
         const uint2 dv = *(const uint2*)(dout + t * d + i);
         float v[4] = {bf16_to_f32(dv.x & 0xffffu) + acc[a][0], bf16_to_f32(dv.x >> 16) + acc[a][1],
                       bf16_to_f32(dv.y & 0xffffu) + acc[a][2], bf16_to_f32(dv.y >> 16) + acc[a][3]};
-        const int e = expert[t], pos = position[t];
-        if (keep[t] && e >= 0 && e < E && pos >= 0 && pos < C) {
-            const f32x4 b = *(const f32x4*)(dbuf + ((size_t)e * C + pos) * d + i);
-            v[0] += b[0]; v[1] += b[1]; v[2] += b[2]; v[3] += b[3];
+        for (int c = 0; c < k; ++c) {   // the kept choices in rank order
+            const int64_t n = t * k + c;
+            const int e = expert[n], pos = slot[n];
+            if (keep[n] && e >= 0 && e < E && pos >= 0 && pos < R) {
+                const f32x4 b = *(const f32x4*)(dbuf + ((size_t)e * R + pos) * d + i);
+                v[0] += b[0]; v[1] += b[1]; v[2] += b[2]; v[3] += b[3];
+            }
         }
         *(uint2*)(dx + t * d + i) = make_uint2(bf16_rne(v[0]) | (bf16_rne(v[1]) << 16),
                                                bf16_rne(v[2]) | (bf16_rne(v[3]) << 16));
@@ -313,16 +321,17 @@ __global__ __launch_bounds__(256) void dx_assemble(const bf16_t* __restrict__ do
 // {0-3, 8-11, 16-19, 24-27} (+4 for h = 1); one v_permlane32_swap per register
 // pair turns these into two runs of 8 consecutive columns, so dout, dbuf and
 // dx move 16 or 32 bytes at a time.  dx = bf16(dout + sum_e dz W_r +
-// dbuf[e*, s]) as in dx_assemble.
+// the kept choices' dbuf rows) as in dx_assemble.
 constexpr int DX_STAGE = 2 * 128 * 128;   // bytes: the W_r tile, then the dz tile
 
+template <int K>
 __global__ __launch_bounds__(256) void dx_assemble_mfma(const bf16_t* __restrict__ dout,
                                                         const float* __restrict__ dbuf,
                                                         const int32_t* __restrict__ expert,
-                                                        const int32_t* __restrict__ position,
+                                                        const int32_t* __restrict__ slot,
                                                         const uint8_t* __restrict__ keep,
                                                         const float* __restrict__ dz, const float* __restrict__ w_r,
-                                                        int64_t T, int d, int E, int C, bf16_t* __restrict__ dx) {
+                                                        int64_t T, int d, int E, int R, bf16_t* __restrict__ dx) {
     __shared__ __attribute__((aligned(16))) char lds[2 * DX_STAGE];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -362,14 +371,18 @@ __global__ __launch_bounds__(256) void dx_assemble_mfma(const bf16_t* __restrict
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
 
-    // the routing of this lane's two tokens, fetched now: the first chunk's wait covers it
-    int te[2], tp[2], tk[2];
+    // the routing of this lane's two tokens, fetched now (the first chunk's
+    // wait covers it): the dbuf row e * R + slot of each kept choice, else -1
+    int te[2][K], tp[2][K], tk[2][K];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
         const int64_t tc = min<int64_t>(t0 + 32 * b + l32, T - 1);
-        te[b] = expert[tc];
-        tp[b] = position[tc];
-        tk[b] = keep[tc];
+#pragma unroll
+        for (int c = 0; c < K; ++c) {
+            te[b][c] = expert[tc * K + c];
+            tp[b][c] = slot[tc * K + c];
+            tk[b][c] = keep[tc * K + c];
+        }
     }
     issue(0, 0);
     int kc = 0;
@@ -421,24 +434,35 @@ __global__ __launch_bounds__(256) void dx_assemble_mfma(const bf16_t* __restrict
     // every load of the epilogue before its first store (a load issued after a
     // store waits for that store too); rows past T read row T - 1 and are not stored
     uint4 dv[2][2][2];
-    f32x4 bq[2][2][2][2];
+    f32x4 bq[2][2][2][2];   // the sum of the kept choices' dbuf rows
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        const int64_t tc = min<int64_t>(t0 + 32 * b + l32, T - 1);
-        const bool kept = tk[b] && te[b] >= 0 && te[b] < E && tp[b] >= 0 && tp[b] < C;
+    for (int c = 0; c < K; ++c) {
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
+        for (int b = 0; b < 2; ++b) {
+            const int64_t tc = min<int64_t>(t0 + 32 * b + l32, T - 1);
+            const bool kept = tk[b][c] && te[b][c] >= 0 && te[b][c] < E && tp[b][c] >= 0 && tp[b][c] < R;
 #pragma unroll
-            for (int run = 0; run < 2; ++run) {
-                const int i = i0 + 32 * a + 16 * run + 8 * h;
-                dv[b][a][run] = *(const uint4*)(dout + tc * d + i);
-                bq[b][a][run][0] = bq[b][a][run][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (kept) {
-                    const float* br = dbuf + ((size_t)te[b] * C + tp[b]) * d + i;
-                    bq[b][a][run][0] = *(const f32x4*)br;
-                    bq[b][a][run][1] = *(const f32x4*)(br + 4);
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int run = 0; run < 2; ++run) {
+                    const int i = i0 + 32 * a + 16 * run + 8 * h;
+                    if (c == 0) {
+                        dv[b][a][run] = *(const uint4*)(dout + tc * d + i);
+                        bq[b][a][run][0] = bq[b][a][run][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    }
+                    if (kept) {
+                        const float* br = dbuf + ((size_t)te[b][c] * R + tp[b][c]) * d + i;
+                        const f32x4 l0 = *(const f32x4*)br, l1 = *(const f32x4*)(br + 4);
+                        if (c == 0) {
+                            bq[b][a][run][0] = l0;
+                            bq[b][a][run][1] = l1;
+                        } else {
+                            bq[b][a][run][0] += l0;
+                            bq[b][a][run][1] += l1;
+                        }
+                    }
                 }
-            }
+        }
     }
 #pragma unroll
     for (int b = 0; b < 2; ++b)
@@ -482,12 +506,13 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_combine_bwd(const bf16_t* dout, const float* y, const int32_t* expert, const int32_t* position,
-                              const uint8_t* keep, const float* gate, int64_t T, int d, int E, int C, bf16_t* dy,
-                              float* dgate, hipStream_t s) {
+hipError_t launch_combine_bwd(const bf16_t* dout, const float* y, const int32_t* expert, const int32_t* slot,
+                              const uint8_t* keep, const float* gate, int64_t T, int k, int d, int E, int R,
+                              bf16_t* dy, float* dgate, hipStream_t s) {
     if (T == 0) return hipSuccess;
-    hipLaunchKernelGGL(combine_bwd, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, dout, y, expert, position, keep,
-                       gate, T, d, E, C, dy, dgate);
+    const int N = (int)(T * k);
+    hipLaunchKernelGGL(combine_bwd, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, s, dout, y, expert, slot, keep, gate,
+                       N, k, d, E, R, dy, dgate);
     return hipGetLastError();
 }
 
@@ -524,17 +549,27 @@ hipError_t launch_router_wgrad(const bf16_t* x, const float* dz, int64_t T, int 
     return hipGetLastError();
 }
 
-hipError_t launch_dx_assemble(const bf16_t* dout, const float* dbuf, const int32_t* expert, const int32_t* position,
-                              const uint8_t* keep, const float* dz, const float* w_r, int64_t T, int d, int E, int C,
-                              bf16_t* dx, hipStream_t s) {
+hipError_t launch_dx_assemble(const bf16_t* dout, const float* dbuf, const int32_t* expert, const int32_t* slot,
+                              const uint8_t* keep, const float* dz, const float* w_r, int64_t T, int d, int E, int k,
+                              int R, bf16_t* dx, hipStream_t s) {
     if (T == 0) return hipSuccess;
     // the MFMA kernel copies 32-expert chunks of w_r and dz rows 16 bytes at a time
-    if (E % 32 == 0 && d % 128 == 0 && ((uintptr_t)w_r | (uintptr_t)dz) % 16 == 0)
-        hipLaunchKernelGGL(dx_assemble_mfma, dim3(d / 128, (unsigned)((T + 127) / 128)), dim3(256), 0, s, dout, dbuf,
-                           expert, position, keep, dz, w_r, T, d, E, C, dx);
-    else
+    if (E % 32 == 0 && d % 128 == 0 && ((uintptr_t)w_r | (uintptr_t)dz) % 16 == 0) {
+        const dim3 grid(d / 128, (unsigned)((T + 127) / 128));
+#define SWMOE_DX(K)                                                                                            \
+    hipLaunchKernelGGL(dx_assemble_mfma<K>, grid, dim3(256), 0, s, dout, dbuf, expert, slot, keep, dz, w_r, T, d, \
+                       E, R, dx)
+        switch (k) {
+            case 1: SWMOE_DX(1); break;
+            case 2: SWMOE_DX(2); break;
+            case 3: SWMOE_DX(3); break;
+            default: SWMOE_DX(4); break;
+        }
+#undef SWMOE_DX
+    } else {
         hipLaunchKernelGGL(dx_assemble, dim3(d / 64, (unsigned)((T + 63) / 64)), dim3(256), 0, s, dout, dbuf, expert,
-                           position, keep, dz, w_r, T, d, E, C, dx);
+                           slot, keep, dz, w_r, T, d, E, k, R, dx);
+    }
     return hipGetLastError();
 }
 

@@ -120,21 +120,22 @@ constexpr int64_t kAuxPartsMax = 262144;
 hipError_t launch_z_loss(const float* lse, int64_t T, float beta, float* z_loss, hipStream_t s);
 hipError_t launch_aux_grad(const float* logits, const float* lse, const float* f, int64_t T, int64_t G, int E,
                            float alpha, float beta, const int32_t* expert, const float* gate, const float* dgate,
-                           int accumulate, float* dlogits, hipStream_t s);
+                           int k, int accumulate, float* dlogits, hipStream_t s);
 
 // backward.hip
-hipError_t launch_combine_bwd(const bf16_t* dout, const float* y, const int32_t* expert, const int32_t* position,
-                              const uint8_t* keep, const float* gate, int64_t T, int d, int E, int C, bf16_t* dy,
-                              float* dgate, hipStream_t s);
+// expert, slot, keep, gate, dgate [T, k]; R buffer rows per expert
+hipError_t launch_combine_bwd(const bf16_t* dout, const float* y, const int32_t* expert, const int32_t* slot,
+                              const uint8_t* keep, const float* gate, int64_t T, int k, int d, int E, int R,
+                              bf16_t* dy, float* dgate, hipStream_t s);
 hipError_t launch_transpose_rows(const bf16_t* src, bf16_t* dst, int E, int R, int S, int Rp, const int32_t* valid,
                                  hipStream_t s);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 int router_wgrad_slices(int64_t T, int d, int E);
 hipError_t launch_router_wgrad(const bf16_t* x, const float* dz, int64_t T, int d, int E, float* part, float* dw_r,
                                hipStream_t s);
-hipError_t launch_dx_assemble(const bf16_t* dout, const float* dbuf, const int32_t* expert, const int32_t* position,
-                              const uint8_t* keep, const float* dz, const float* w_r, int64_t T, int d, int E, int C,
-                              bf16_t* dx, hipStream_t s);
+hipError_t launch_dx_assemble(const bf16_t* dout, const float* dbuf, const int32_t* expert, const int32_t* slot,
+                              const uint8_t* keep, const float* dz, const float* w_r, int64_t T, int d, int E, int k,
+                              int R, bf16_t* dx, hipStream_t s);
 
 // api.hip
 hipError_t launch_stream_copy(void* dst, const void* src, size_t nbytes, hipStream_t s);
