@@ -23,29 +23,37 @@ namespace swmoe {
 // (d is a multiple of 32).
 __global__ __launch_bounds__(256) void split_router_weights(const float* __restrict__ w_r,
                                                             bf16_t* __restrict__ wr3, int d, int E) {
-    __shared__ float tile[32][33];
-    const int e0 = blockIdx.x * 32, k0 = blockIdx.y * 32;
-    const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
-    for (int r = ty; r < 32; r += 8) {
-        int k = k0 + r, e = e0 + tx;
-        tile[r][tx] = (k < d && e < E) ? w_r[(size_t)k * E + e] : 0.f;
-    }
-    __syncthreads();
-    for (int r = ty; r < 32; r += 8) {
-        int e = e0 + r, k = k0 + tx;
-        if (e < E && k < d) {
-            float w = tile[tx][r];
-            uint32_t hi = bf16_rne(w);
-            float r1 = w - bf16_to_f32(hi);
-            uint32_t mid = bf16_rne(r1);
-            float r2 = r1 - bf16_to_f32(mid);
-            uint32_t lo = bf16_rne(r2);
-            const size_t o = (size_t)blockIdx.y * 3 * E * 32 + (size_t)e * 32 + tx;
-            wr3[o] = (bf16_t)hi;
-            wr3[o + (size_t)E * 32] = (bf16_t)mid;
-            wr3[o + (size_t)2 * E * 32] = (bf16_t)lo;
+    // thread i: expert e = i % E and the 8 consecutive rows k = 8 (i / E) ..;
+    // a wave's eight loads (one per k) are each 64 consecutive experts, and
+    // each term's 8 values of one expert are one 16-byte store
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= (d / 8) * E) return;
+    const int kc = i / E, e = i - kc * E;
+    float w[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w[j] = w_r[(size_t)(8 * kc + j) * E + e];
+    uint32_t t3[3][4];
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+        uint32_t v[3][2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const float x = w[j + u];
+            const uint32_t hi = bf16_rne(x);
+            const float r1 = x - bf16_to_f32(hi);
+            const uint32_t mid = bf16_rne(r1);
+            const float r2 = r1 - bf16_to_f32(mid);
+            v[0][u] = hi;
+            v[1][u] = mid;
+            v[2][u] = bf16_rne(r2);
         }
+#pragma unroll
+        for (int q = 0; q < 3; ++q) t3[q][j / 2] = v[q][0] | (v[q][1] << 16);
     }
+    bf16_t* o = wr3 + (size_t)(kc / 4) * 3 * E * 32 + (size_t)e * 32 + 8 * (kc % 4);
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+        *(uint4*)(o + (size_t)q * E * 32) = make_uint4(t3[q][0], t3[q][1], t3[q][2], t3[q][3]);
 }
 
 // logits[t, e] = sum_k x[t, k] (hi + mid + lo)[e, k] + b[e] for E > 256.
@@ -422,8 +430,9 @@ __global__ __launch_bounds__(1024) void router_reduce(const float* __restrict__ 
 
 // ------------------------------------------------------------------ launchers
 hipError_t launch_split_router_weights(const float* w_r, bf16_t* wr3, int d, int E, hipStream_t s) {
-    dim3 grid((E + 31) / 32, (d + 31) / 32);
-    hipLaunchKernelGGL(split_router_weights, grid, dim3(256), 0, s, w_r, wr3, d, E);
+    const int64_t n = (int64_t)(d / 8) * E;   // d is a multiple of 32
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(split_router_weights, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, w_r, wr3, d, E);
     return hipGetLastError();
 }
 
