@@ -98,6 +98,74 @@ __global__ __launch_bounds__(256) void aux_grad(const float* __restrict__ logits
     }
 }
 
+// The same gradient for E a multiple of 4 with 16-byte aligned rows: L lanes
+// per token (E / 4 rounded up to a power of two, at most 64), so a wave
+// finishes 64 / L tokens; lane s of a token holds experts 4 (s + L i) .. + 3,
+// i < NV, and moves them with 16-byte loads and stores.  All of a token's
+// loads are issued before the first is used.
+template <int L, int NV>
+__global__ __launch_bounds__(256) void aux_grad4(const float* __restrict__ logits, const float* __restrict__ lse,
+                                                 const float* __restrict__ f, int64_t T, int64_t G, int E,
+                                                 float c_aux, float c_z, const int32_t* __restrict__ expert,
+                                                 const float* __restrict__ gate, const float* __restrict__ dgate,
+                                                 int k, int accumulate, float* __restrict__ dlogits) {
+    constexpr int TPW = 64 / L;
+    const int lane = threadIdx.x & 63, sub = lane % L;
+    const int64_t t = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * TPW + lane / L;
+    if (t >= T) return;   // whole groups of L lanes (one token) leave together
+    const float* row = logits + t * E;
+    const float* fr = f ? f + (t / G) * E : nullptr;
+    float* g = dlogits + t * E;
+    f32x4 z[NV], fv[NV], acc[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int e0 = 4 * (sub + L * i);
+        const bool in = e0 < E;
+        z[i] = in ? *(const f32x4*)(row + e0) : f32x4{0.f, 0.f, 0.f, 0.f};
+        fv[i] = (in && fr) ? *(const f32x4*)(fr + e0) : f32x4{0.f, 0.f, 0.f, 0.f};
+        acc[i] = (in && accumulate) ? *(const f32x4*)(g + e0) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    const float l = lse[t];
+    float dgi[kMaxTopK];
+    int es[kMaxTopK];
+    float dg = 0.f;
+#pragma unroll
+    for (int c = 0; c < kMaxTopK; ++c) {
+        const bool on = dgate && c < k;
+        dgi[c] = on ? dgate[t * k + c] * gate[t * k + c] : 0.f;
+        es[c] = on ? expert[t * k + c] : -1;
+        dg += dgi[c];
+    }
+    float p[NV][4];
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = 4 * (sub + L * i) + j;
+            p[i][j] = e < E ? expf(z[i][j] - l) : 0.f;
+            s = fmaf(fv[i][j], p[i][j], s);
+        }
+#pragma unroll
+    for (int m = L / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m);
+    const float zt = c_z * l;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int e0 = 4 * (sub + L * i);
+        if (e0 < E) {
+            f32x4 o;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float sel = 0.f;
+#pragma unroll
+                for (int c = 0; c < kMaxTopK; ++c) sel += e0 + j == es[c] ? dgi[c] : 0.f;
+                o[j] = p[i][j] * (c_aux * (fv[i][j] - s) + zt - dg) + sel;
+            }
+            *(f32x4*)(g + e0) = accumulate ? acc[i] + o : o;
+        }
+    }
+}
+
 hipError_t launch_aux_stats(const int32_t* counts, const float* prob_sum, int64_t G, int ngroups, int E, int k,
                             float alpha, float* f, float* P, float* loss, hipStream_t s) {
     hipLaunchKernelGGL(aux_stats, dim3(1), dim3(1024), 0, s, counts, prob_sum, G, ngroups, E, k, alpha, f, P, loss);
@@ -115,6 +183,35 @@ hipError_t launch_aux_grad(const float* logits, const float* lse, const float* f
     if (T == 0) return hipSuccess;
     const float c_aux = f ? (float)((double)alpha * (double)E / (double)T) : 0.f;
     const float c_z = (float)(2.0 * (double)beta / (double)T);
+    const int64_t Gc = std::max<int64_t>(G, 1);
+    if (E % 4 == 0 && ((uintptr_t)logits | (uintptr_t)dlogits | (uintptr_t)f) % 16 == 0) {
+        int lanes = 1;
+        while (lanes < 64 && 4 * lanes < E) lanes <<= 1;
+        const int64_t waves = (T + 64 / lanes - 1) / (64 / lanes);
+        const dim3 g4((unsigned)((waves + 3) / 4));
+#define SWMOE_GRAD4(L, NV)                                                                                     \
+    hipLaunchKernelGGL((aux_grad4<L, NV>), g4, dim3(256), 0, s, logits, lse, f, T, Gc, E, c_aux, c_z, expert, gate, \
+                       dgate, k, accumulate, dlogits)
+        if (lanes < 64) {
+            switch (lanes) {
+                case 1: SWMOE_GRAD4(1, 1); break;
+                case 2: SWMOE_GRAD4(2, 1); break;
+                case 4: SWMOE_GRAD4(4, 1); break;
+                case 8: SWMOE_GRAD4(8, 1); break;
+                case 16: SWMOE_GRAD4(16, 1); break;
+                default: SWMOE_GRAD4(32, 1); break;
+            }
+        } else {
+            const int nv = (E + 255) / 256;
+            if (nv <= 1) SWMOE_GRAD4(64, 1);
+            else if (nv <= 2) SWMOE_GRAD4(64, 2);
+            else if (nv <= 4) SWMOE_GRAD4(64, 4);
+            else if (nv <= 8) SWMOE_GRAD4(64, 8);
+            else SWMOE_GRAD4(64, 16);
+        }
+#undef SWMOE_GRAD4
+        return hipGetLastError();
+    }
     const unsigned grid = (unsigned)((T + 3) / 4);
     const int nch = (E + 63) / 64;
 #define SWMOE_GRAD(N)                                                                                          \
