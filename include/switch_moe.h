@@ -349,7 +349,8 @@ switch_status switch_aux_loss_ex(const int32_t *counts, const float *prob_sum, c
  *
  * Precision: dy and dA are rounded to bf16 (the MFMA inputs), the GEMMs
  * accumulate in fp32, weight and router gradients are fp32, dx is rounded to
- * bf16 once.  dz, dgate and the reductions over tokens (db_r, dW_r) are fp32
+ * bf16 once; its router term W_r dz_t is formed from two-term bf16 splits of
+ * W_r and dz (relative error about 2^-15, below that rounding).  dz, dgate and the reductions over tokens (db_r, dW_r) are fp32
  * with fp64 sums in a fixed order.  The aux gradient treats f as constant. */
 typedef struct switch_layer_bwd_args {
     /* saved by switch_layer_fwd (with logits and h requested) */

@@ -20,7 +20,7 @@
 //   router_wgrad    dW_r partial sums over token slices (fp32 MFMA), then
 //   router_wgrad_reduce  the slices added in order in fp64
 //   dx_assemble     dx_t = bf16(dout_t + sum_e dz_te W_r[:, e] + sum_i dbuf[e_ti, s_ti])
-//                   over the token's kept choices (dx_assemble_mfma on the fp32
+//                   over the token's kept choices (dx_assemble_mfma on the bf16
 //                   MFMA when E is a multiple of 32)
 #include "common.hpp"
 #include "kernels.hpp"
@@ -307,22 +307,47 @@ __global__ __launch_bounds__(256) void dx_assemble(const bf16_t* __restrict__ do
     }
 }
 
-// dx on the fp32 MFMA (E a multiple of 32, d a multiple of 128, w_r and dz
+// dx on the bf16 MFMA (E a multiple of 32, d a multiple of 128, w_r and dz
 // 16-byte aligned): workgroup = 128 columns i x 128 tokens, wave w = columns
 // 64 (w >> 1) x tokens 64 (w & 1) as 2 x 2 blocks of 32.  A = W_r rows (i,
-// K = e), B = dz^T (K = e, column = token).  Per chunk of 32 experts the
+// K = e), B = dz^T (K = e, column = token).  Both are fp32; each goes into
+// the MFMA as the first two terms of its bf16 split (hi + mid, a remainder
+// below 2^-16 of the value), and the products mid x hi, hi x mid and hi x hi
+// are accumulated in fp32, so the router term dz W_r^T carries a relative
+// error of about 2^-15 of sum_e |dz_te W_r[i, e]|, far below the bf16
+// rounding of dx.  Per chunk of 32 experts the
 // workgroup's 128 W_r rows and 128 dz rows (128 bytes each) go from memory
 // straight into LDS, eight 1 KiB copies per wave with the lanes along the
 // expert axis (16-byte column c of row r at c ^ (r & 7), which keeps the
 // 32-row fragment reads free of bank conflicts); two stages, one barrier per
-// chunk; dz rows past T read as zero.  MFMA step st of a chunk: half wave h
-// takes expert 16 h + st, so a lane's 16 values of a row are four
-// ds_read_b128.  In a result block lane l holds token l & 31 and columns
+// chunk; dz rows past T read as zero.  A chunk is two 16-expert MFMA steps
+// (v_mfma_f32_32x32x16_bf16): in step kq half wave h takes experts 16 kq +
+// 8 h .. + 7, two 16-byte columns of each of its rows, split in registers.
+// In a result block lane l holds token l & 31 and columns
 // {0-3, 8-11, 16-19, 24-27} (+4 for h = 1); one v_permlane32_swap per register
 // pair turns these into two runs of 8 consecutive columns, so dout, dbuf and
 // dx move 16 or 32 bytes at a time.  dx = bf16(dout + sum_e dz W_r +
 // the kept choices' dbuf rows) as in dx_assemble.
 constexpr int DX_STAGE = 2 * 128 * 128;   // bytes: the W_r tile, then the dz tile
+
+// v = hi + mid + (a remainder below 2^-16 |v|): the first two terms of the
+// exact three-term bf16 split, eight values at a time
+// (the hardware's round-to-nearest-even conversion, two values per instruction)
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void split2_bf16x8(const f32x4& v0, const f32x4& v1, bf16x8& hi, bf16x8& mid) {
+    const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    u32x4 ph, pm;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{v[2 * j], v[2 * j + 1]}, bf16x2));
+        const f32x2 r{v[2 * j] - __uint_as_float(h << 16), v[2 * j + 1] - __uint_as_float(h & 0xffff0000u)};
+        ph[j] = h;
+        pm[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
+    }
+    hi = as_bf16x8(ph);
+    mid = as_bf16x8(pm);
+}
 
 template <int K>
 __global__ __launch_bounds__(256) void dx_assemble_mfma(const bf16_t* __restrict__ dout,
@@ -391,29 +416,31 @@ __global__ __launch_bounds__(256) void dx_assemble_mfma(const bf16_t* __restrict
         lds_barrier();      // every wave's, and chunk kc - 1 is read out
         issue(min(kc + 1, nk - 1), (kc + 1) & 1);   // the last chunk is fetched twice, never read
         const char* st = lds + (kc & 1) * DX_STAGE;
-        float av[2][16], bv[2][16];
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int ra = (wave >> 1) * 64 + 32 * q + l32;   // W_r row in the tile
-            const int rb = (wave & 1) * 64 + 32 * q + l32;    // dz row in the tile
+        for (int kq = 0; kq < 2; ++kq) {   // experts 16 kq + 8 h .. + 7 of the chunk: 16-byte columns 4 kq + 2 h + {0, 1}
+            bf16x8 ah[2], am[2], bh[2], bm[2];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const f32x4 a4 = *(const f32x4*)(st + ra * 128 + (((4 * h + c) ^ (ra & 7)) << 4));
-                const f32x4 b4 = *(const f32x4*)(st + 128 * 128 + rb * 128 + (((4 * h + c) ^ (rb & 7)) << 4));
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    av[q][4 * c + j] = a4[j];
-                    bv[q][4 * c + j] = b4[j];
-                }
+            for (int q = 0; q < 2; ++q) {
+                const int ra = (wave >> 1) * 64 + 32 * q + l32;   // W_r row in the tile
+                const int rb = (wave & 1) * 64 + 32 * q + l32;    // dz row in the tile
+                const int c0 = 4 * kq + 2 * h;
+                const f32x4 a0 = *(const f32x4*)(st + ra * 128 + ((c0 ^ (ra & 7)) << 4));
+                const f32x4 a1 = *(const f32x4*)(st + ra * 128 + (((c0 + 1) ^ (ra & 7)) << 4));
+                const f32x4 b0 = *(const f32x4*)(st + 128 * 128 + rb * 128 + ((c0 ^ (rb & 7)) << 4));
+                const f32x4 b1 = *(const f32x4*)(st + 128 * 128 + rb * 128 + (((c0 + 1) ^ (rb & 7)) << 4));
+                split2_bf16x8(a0, a1, ah[q], am[q]);
+                split2_bf16x8(b0, b1, bh[q], bm[q]);
             }
-        }
-#pragma unroll
-        for (int st16 = 0; st16 < 16; ++st16)
+            // small products first: mid x hi, hi x mid, then hi x hi
 #pragma unroll
             for (int x0 = 0; x0 < 2; ++x0)
 #pragma unroll
-                for (int y0 = 0; y0 < 2; ++y0)
-                    acc[x0][y0] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[x0][st16], bv[y0][st16], acc[x0][y0], 0, 0, 0);
+                for (int y0 = 0; y0 < 2; ++y0) {
+                    acc[x0][y0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am[x0], bh[y0], acc[x0][y0], 0, 0, 0);
+                    acc[x0][y0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[x0], bm[y0], acc[x0][y0], 0, 0, 0);
+                    acc[x0][y0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[x0], bh[y0], acc[x0][y0], 0, 0, 0);
+                }
+        }
     } while (++kc < nk);
     wait_copies<0>();   // the spare copy of the last chunk
     // runs of 8 columns: swap rows 8-11 of half 0 with rows 4-7 of half 1 (and 24-27 with 20-23)
