@@ -503,17 +503,20 @@ hipError_t launch_router_reduce(const float* part, int nblk, int ngroups, int E,
     return hipGetLastError();
 }
 
-int column_sum_slices(int64_t rows) { return (int)std::max<int64_t>(1, (rows + 1023) / 1024); }
+// rows per slice of the column sum: 16 per thread of router_reduce, so each
+// thread's loads are few and the slices many
+constexpr int kColumnSlice = 256;
+int column_sum_slices(int64_t rows) { return (int)std::max<int64_t>(1, (rows + kColumnSlice - 1) / kColumnSlice); }
 
-// out[e] = sum over the rows of a [rows, E] array: slices of 1024 rows summed
-// in parallel (each in the fixed order above), then the slices in order.
+// out[e] = sum over the rows of a [rows, E] array: slices of kColumnSlice rows
+// summed in parallel (each in the fixed order above), then the slices in order.
 hipError_t launch_column_sum(const float* a, int rows, int E, float* slices, float* out, hipStream_t s) {
     const int ns = column_sum_slices(rows);
     if (ns == 1) {
         hipLaunchKernelGGL(router_reduce, dim3((E + 63) / 64, 1), dim3(1024), 0, s, a, rows, rows, E, out);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(router_reduce, dim3((E + 63) / 64, ns), dim3(1024), 0, s, a, 1024, rows, E, slices);
+    hipLaunchKernelGGL(router_reduce, dim3((E + 63) / 64, ns), dim3(1024), 0, s, a, kColumnSlice, rows, E, slices);
     hipLaunchKernelGGL(router_reduce, dim3((E + 63) / 64, 1), dim3(1024), 0, s, slices, ns, ns, E, out);
     return hipGetLastError();
 }
