@@ -161,21 +161,12 @@ __global__ __launch_bounds__(256) void router_wgrad(const bf16_t* __restrict__ x
             u32x4 hi, mid, lo;
 #pragma unroll
             for (int p2 = 0; p2 < 4; ++p2) {   // the three terms of floats 2 p2, 2 p2 + 1
-                uint32_t t3[3][2];
-#pragma unroll
-                for (int o = 0; o < 2; ++o) {
-                    const float w = __uint_as_float(zr[jj][p2 >> 1][2 * (p2 & 1) + o]);
-                    const uint32_t bh = bf16_rne(w);
-                    const float r1 = w - bf16_to_f32(bh);
-                    const uint32_t bm = bf16_rne(r1);
-                    const uint32_t bl = bf16_rne(r1 - bf16_to_f32(bm));
-                    t3[0][o] = bh;
-                    t3[1][o] = bm;
-                    t3[2][o] = bl;
-                }
-                hi[p2] = t3[0][0] | (t3[0][1] << 16);
-                mid[p2] = t3[1][0] | (t3[1][1] << 16);
-                lo[p2] = t3[2][0] | (t3[2][1] << 16);
+                uint32_t th, tm, tl;
+                split3_bf16x2(__uint_as_float(zr[jj][p2 >> 1][2 * (p2 & 1)]),
+                              __uint_as_float(zr[jj][p2 >> 1][2 * (p2 & 1) + 1]), th, tm, tl);
+                hi[p2] = th;
+                mid[p2] = tm;
+                lo[p2] = tl;
             }
             *(u32x4*)(lds + RW_PLANE + at) = hi;
             *(u32x4*)(lds + 2 * RW_PLANE + at) = mid;
@@ -333,17 +324,14 @@ constexpr int DX_STAGE = 2 * 128 * 128;   // bytes: the W_r tile, then the dz ti
 // v = hi + mid + (a remainder below 2^-16 |v|): the first two terms of the
 // exact three-term bf16 split, eight values at a time
 // (the hardware's round-to-nearest-even conversion, two values per instruction)
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void split2_bf16x8(const f32x4& v0, const f32x4& v1, bf16x8& hi, bf16x8& mid) {
     const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
     u32x4 ph, pm;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{v[2 * j], v[2 * j + 1]}, bf16x2));
-        const f32x2 r{v[2 * j] - __uint_as_float(h << 16), v[2 * j + 1] - __uint_as_float(h & 0xffff0000u)};
+        const uint32_t h = pack_bf16x2(v[2 * j], v[2 * j + 1]);
         ph[j] = h;
-        pm[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
+        pm[j] = pack_bf16x2(v[2 * j] - bf16_lo_f32(h), v[2 * j + 1] - bf16_hi_f32(h));
     }
     hi = as_bf16x8(ph);
     mid = as_bf16x8(pm);

@@ -23,6 +23,26 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
+// Two fp32 values rounded to bf16 (nearest, ties to even) by one hardware
+// conversion (v_cvt_pk_bf16_f32); a in the low half.  The same result as
+// bf16_rne for every finite value.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+__device__ __forceinline__ float bf16_lo_f32(uint32_t p) { return __uint_as_float(p << 16); }
+__device__ __forceinline__ float bf16_hi_f32(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }
+
+// The exact three-term bf16 split of two fp32 values (a = hi + mid + lo
+// exactly; Henry, Tang and Heinecke, ARITH 2019), each term a packed pair.
+__device__ __forceinline__ void split3_bf16x2(float a, float b, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+    hi = pack_bf16x2(a, b);
+    const float ra = a - bf16_lo_f32(hi), rb = b - bf16_hi_f32(hi);
+    mid = pack_bf16x2(ra, rb);
+    lo = pack_bf16x2(ra - bf16_lo_f32(mid), rb - bf16_hi_f32(mid));
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
     return __builtin_bit_cast(bf16x8, v);
 }

@@ -34,22 +34,7 @@ __global__ __launch_bounds__(256) void split_router_weights(const float* __restr
     for (int j = 0; j < 8; ++j) w[j] = w_r[(size_t)(8 * kc + j) * E + e];
     uint32_t t3[3][4];
 #pragma unroll
-    for (int j = 0; j < 8; j += 2) {
-        uint32_t v[3][2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const float x = w[j + u];
-            const uint32_t hi = bf16_rne(x);
-            const float r1 = x - bf16_to_f32(hi);
-            const uint32_t mid = bf16_rne(r1);
-            const float r2 = r1 - bf16_to_f32(mid);
-            v[0][u] = hi;
-            v[1][u] = mid;
-            v[2][u] = bf16_rne(r2);
-        }
-#pragma unroll
-        for (int q = 0; q < 3; ++q) t3[q][j / 2] = v[q][0] | (v[q][1] << 16);
-    }
+    for (int j = 0; j < 8; j += 2) split3_bf16x2(w[j], w[j + 1], t3[0][j / 2], t3[1][j / 2], t3[2][j / 2]);
     bf16_t* o = wr3 + (size_t)(kc / 4) * 3 * E * 32 + (size_t)e * 32 + 8 * (kc % 4);
 #pragma unroll
     for (int q = 0; q < 3; ++q)
