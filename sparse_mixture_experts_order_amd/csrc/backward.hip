@@ -58,7 +58,7 @@ __global__ __launch_bounds__(256) void combine_bwd(const bf16_t* __restrict__ do
             const float lo = bf16_to_f32(w[j] & 0xffffu), hi = bf16_to_f32(w[j] >> 16);
             acc = fmaf(lo, yv[2 * j], acc);
             acc = fmaf(hi, yv[2 * j + 1], acc);
-            o[j] = bf16_rne(g * lo) | (bf16_rne(g * hi) << 16);
+            o[j] = pack_bf16x2(g * lo, g * hi);
         }
         *(uint4*)(dyrow + c) = make_uint4(o[0], o[1], o[2], o[3]);
     }
@@ -293,8 +293,7 @@ __global__ __launch_bounds__(256) void dx_assemble(const bf16_t* __restrict__ do
                 v[0] += b[0]; v[1] += b[1]; v[2] += b[2]; v[3] += b[3];
             }
         }
-        *(uint2*)(dx + t * d + i) = make_uint2(bf16_rne(v[0]) | (bf16_rne(v[1]) << 16),
-                                               bf16_rne(v[2]) | (bf16_rne(v[3]) << 16));
+        *(uint2*)(dx + t * d + i) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
     }
 }
 
@@ -493,7 +492,7 @@ __global__ __launch_bounds__(256) void dx_assemble_mfma(const bf16_t* __restrict
                     const f32x4& bb = bq[b][a][run][j >> 1];
                     const float v0 = (bf16_to_f32(dw[j] & 0xffffu) + acc[a][b][8 * run + 2 * j]) + bb[2 * (j & 1)];
                     const float v1 = (bf16_to_f32(dw[j] >> 16) + acc[a][b][8 * run + 2 * j + 1]) + bb[2 * (j & 1) + 1];
-                    o[j] = bf16_rne(v0) | (bf16_rne(v1) << 16);
+                    o[j] = pack_bf16x2(v0, v1);
                 }
                 dv[b][a][run] = make_uint4(o[0], o[1], o[2], o[3]);
             }

@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256) void combine(const float* __restrict__ y, cons
     }
     uint32_t o[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = bf16_rne(acc[2 * j]) | (bf16_rne(acc[2 * j + 1]) << 16);
+    for (int j = 0; j < 4; ++j) o[j] = pack_bf16x2(acc[2 * j], acc[2 * j + 1]);
     ((uint4*)(out + t * d))[v] = make_uint4(o[0], o[1], o[2], o[3]);
 }
 

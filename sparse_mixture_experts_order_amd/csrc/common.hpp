@@ -13,19 +13,11 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kWave = 64;
 
-// Round-to-nearest-even float -> bf16 bits; NaN stays a quiet NaN.
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
-}
-
+// bf16 bits (low half) -> float, exactly
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// Two fp32 values rounded to bf16 (nearest, ties to even) by one hardware
-// conversion (v_cvt_pk_bf16_f32); a in the low half.  The same result as
-// bf16_rne for every finite value.
+// Two fp32 values rounded to bf16 (nearest, ties to even; NaN stays NaN) by
+// one hardware conversion (v_cvt_pk_bf16_f32); a in the low half.
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {

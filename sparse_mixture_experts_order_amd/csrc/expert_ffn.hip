@@ -195,7 +195,7 @@ __device__ __forceinline__ void ffn_store_tile_direct(f32x16 (&acc)[NBW][TOKB], 
                         const uint32_t res = in.rr[tb][nb][run][j];
                         const float o0 = fmaf(in.g[tb], a[8 * run + 2 * j], bf16_to_f32(res & 0xffffu));
                         const float o1 = fmaf(in.g[tb], a[8 * run + 2 * j + 1], bf16_to_f32(res >> 16));
-                        in.rr[tb][nb][run][j] = bf16_rne(o0) | (bf16_rne(o1) << 16);
+                        in.rr[tb][nb][run][j] = pack_bf16x2(o0, o1);
                     }
                 }
 #pragma unroll
@@ -255,7 +255,7 @@ __device__ __forceinline__ void ffn_store_tile_direct(f32x16 (&acc)[NBW][TOKB], 
                         const uint32_t m = mk[nb][tb][run][j];
                         const uint32_t keep = ((m & 0x7fffu) ? 0xffffu : 0u) | ((m & 0x7fff0000u) ? 0xffff0000u : 0u);
                         mk[nb][tb][run][j] =
-                            (bf16_rne(a[8 * run + 2 * j]) | (bf16_rne(a[8 * run + 2 * j + 1]) << 16)) & keep;
+                            pack_bf16x2(a[8 * run + 2 * j], a[8 * run + 2 * j + 1]) & keep;
                     }
                     // computed here, not inside each store's branch (one wait for the loads)
                     asm volatile("" : "+v"(mk[nb][tb][run]));
@@ -292,8 +292,8 @@ __device__ __forceinline__ void ffn_store_tile_direct(f32x16 (&acc)[NBW][TOKB], 
 #pragma unroll
                     for (int j = 0; j < 8; ++j) v[j] = fmaxf(a[8 * run + j], 0.f);
                     *(u32x4*)((bf16_t*)out + row + n) =
-                        u32x4{bf16_rne(v[0]) | (bf16_rne(v[1]) << 16), bf16_rne(v[2]) | (bf16_rne(v[3]) << 16),
-                              bf16_rne(v[4]) | (bf16_rne(v[5]) << 16), bf16_rne(v[6]) | (bf16_rne(v[7]) << 16)};
+                        u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                              pack_bf16x2(v[6], v[7])};
                 }
             } else {
 #pragma unroll
@@ -330,15 +330,11 @@ __device__ __forceinline__ void ffn_store_tile(f32x16 (&acc)[NBW][TOKB], char* l
                         const f32x16& a = acc[nb][tb];
                         char* dst = lds_o + (tb * 32 + l32) * OSTRIDE + c * OUT_BYTES;
                         if constexpr (MODE == OUT_RELU_BF16) {
-                            const uint32_t b0 = bf16_rne(fmaxf(a[4 * q + 0], 0.f));
-                            const uint32_t b1 = bf16_rne(fmaxf(a[4 * q + 1], 0.f));
-                            const uint32_t b2 = bf16_rne(fmaxf(a[4 * q + 2], 0.f));
-                            const uint32_t b3 = bf16_rne(fmaxf(a[4 * q + 3], 0.f));
-                            *(uint2*)dst = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+                            *(uint2*)dst = make_uint2(pack_bf16x2(fmaxf(a[4 * q + 0], 0.f), fmaxf(a[4 * q + 1], 0.f)),
+                                                      pack_bf16x2(fmaxf(a[4 * q + 2], 0.f), fmaxf(a[4 * q + 3], 0.f)));
                         } else if constexpr (MODE == OUT_MASK_BF16) {
-                            const uint32_t b0 = bf16_rne(a[4 * q + 0]), b1 = bf16_rne(a[4 * q + 1]);
-                            const uint32_t b2 = bf16_rne(a[4 * q + 2]), b3 = bf16_rne(a[4 * q + 3]);
-                            *(uint2*)dst = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+                            *(uint2*)dst = make_uint2(pack_bf16x2(a[4 * q + 0], a[4 * q + 1]),
+                                                      pack_bf16x2(a[4 * q + 2], a[4 * q + 3]));
                         } else {
                             *(f32x4*)dst = f32x4{a[4 * q + 0], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
                         }
