@@ -663,7 +663,8 @@ def layer_backward(x, w_r, b_r, w1, w2, c: float, alpha: float, dout, beta: floa
                    C: Optional[int] = None, expert_override: Optional[np.ndarray] = None,
                    forward: Optional[LayerResult] = None, relu_active=None) -> LayerGrads:
     """Gradients of J = sum_t <dout_t, out_t> + L_aux (+ L_z) for the Switch
-    layer (one routing group, k = 1), in float64, expert by expert.
+    layer (one routing group, k = 1; layer_backward_grouped below covers
+    routing groups and top-k), in float64, expert by expert.
 
     relu_active(e, a) may replace the ReLU derivative [a > 0] of expert e's
     kept rows (a: their pre-activations, tokens in order); tests use it to
