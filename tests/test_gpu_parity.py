@@ -502,3 +502,40 @@ def test_z_loss_shift_and_layer():
     g = tt["dlogits"].cpu().numpy()
     assert rel_fro(g, both) <= GRAD_REL
     assert np.abs(g - both).max() <= GRAD_REL * np.abs(both).max()
+
+
+@pytest.mark.parametrize("E", [300, 512, 1024, 2048, 4096, 12])
+def test_aux_and_z_gradient_widths(E):
+    """The gradient kernels at every row width they specialise: 16-byte rows
+    with E/4 lanes per token (E = 12), a whole wave and 2..16 vectors per
+    lane (E = 512 .. 4096), and the one-wave-per-token kernel (E = 300, and an
+    offset row base that breaks 16-byte alignment); aux + accumulated z-loss
+    against the oracle."""
+    T, beta, alpha = 1024, 1e-3, 0.01
+    rng = np.random.default_rng(100 + E)
+    z = (rng.standard_normal((T, E)) * 1.5).astype(np.float32)
+    r = so.softmax_top1(z)
+    counts = np.bincount(r.expert, minlength=E)
+    aux = so.aux_loss(counts, r.p, alpha)
+    zref = so.router_z_loss(z, beta)
+    both = aux.dlogits + zref.dlogits
+    lse = f32_dev(r.lse.astype(np.float32))
+    ps = f32_dev(r.p.sum(axis=0).astype(np.float32))
+    for offset in ((0, 1) if E == 12 else (0,)):
+        # logits and gradient at `offset` floats past a 16-byte boundary
+        zbuf = torch.zeros(T * E + 4, dtype=torch.float32, device="cuda")
+        zbuf[offset:offset + T * E] = f32_dev(z.reshape(-1))
+        gbuf = torch.full((T * E + 4,), float("nan"), dtype=torch.float32, device="cuda")
+        zd, G = zbuf[offset:offset + T * E], gbuf[offset:offset + T * E]
+        f = torch.empty(E, dtype=torch.float32, device="cuda")
+        P, loss = torch.empty_like(f), torch.empty(1, dtype=torch.float32, device="cuda")
+        zl = torch.empty(1, dtype=torch.float32, device="cuda")
+        sw.switch_aux_loss(i32_dev(counts), ps, zd, lse, T, E, alpha, f, P, loss, G)
+        g = G.cpu().numpy().reshape(T, E)
+        assert rel_fro(g, aux.dlogits) <= GRAD_REL, f"aux E={E} offset={offset}"
+        assert np.abs(g - aux.dlogits).max() <= GRAD_REL * np.abs(aux.dlogits).max()
+        sw.switch_router_z_loss(lse, zd, T, E, beta, zl, G, accumulate=True)
+        g = G.cpu().numpy().reshape(T, E)
+        assert rel_fro(g, both) <= GRAD_REL, f"aux + z E={E} offset={offset}"
+        assert np.abs(g - both).max() <= GRAD_REL * np.abs(both).max()
+        assert torch.isnan(gbuf[:offset]).all() and torch.isnan(gbuf[offset + T * E:]).all(), "wrote outside"
