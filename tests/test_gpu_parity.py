@@ -507,10 +507,10 @@ def test_z_loss_shift_and_layer():
 @pytest.mark.parametrize("E", [300, 512, 1024, 2048, 4096, 12])
 def test_aux_and_z_gradient_widths(E):
     """The gradient kernels at every row width they specialise: 16-byte rows
-    with E/4 lanes per token (E = 12), a whole wave and 2..16 vectors per
-    lane (E = 512 .. 4096), and the one-wave-per-token kernel (E = 300, and an
-    offset row base that breaks 16-byte alignment); aux + accumulated z-loss
-    against the oracle."""
+    with four lanes per token, one of them idle (E = 12), a whole wave and
+    2..16 vectors per lane (E = 512 .. 4096), and the one-wave-per-token
+    kernel (E = 300, and an offset row base that breaks 16-byte alignment);
+    aux + accumulated z-loss against the oracle."""
     T, beta, alpha = 1024, 1e-3, 0.01
     rng = np.random.default_rng(100 + E)
     z = (rng.standard_normal((T, E)) * 1.5).astype(np.float32)
