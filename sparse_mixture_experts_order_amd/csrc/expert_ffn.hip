@@ -116,30 +116,51 @@ struct CombineInputs {
     u32x4 rr[TOKB][NBW][2];
 };
 
+// Both loaders load unconditionally from clamped addresses and select after:
+// a load under a branch makes the next wait a full one (every memory operation
+// before it, the previous loads and stores included).
 template <int TOKB, int NBW>
 __device__ __forceinline__ void combine_load_tokens(CombineInputs<TOKB, NBW>& in, const FfnTile& t,
                                                     const FfnCombine& cb, int C, int l32) {
 #pragma unroll
     for (int tb = 0; tb < TOKB; ++tb) {
         const int r = tb * 32 + l32;
-        in.tok[tb] = r < t.nv ? cb.slot_token[(size_t)t.e * C + t.tok_base + r] : -1;
+        const int v = cb.slot_token[(size_t)t.e * C + min(t.tok_base + r, C - 1)];
+        in.tok[tb] = r < t.nv ? v : -1;
     }
 }
 
+// (without a residual the runs are read from `out`, which has the same shape,
+// and replaced by zeros)
 template <int TOKB, int NBW>
 __device__ __forceinline__ void combine_load_rows(CombineInputs<TOKB, NBW>& in, const FfnCombine& cb, int N, int n0,
                                                   int half) {
+    const bf16_t* res = cb.residual ? cb.residual : cb.out;
 #pragma unroll
     for (int tb = 0; tb < TOKB; ++tb) {
-        in.g[tb] = in.tok[tb] >= 0 ? cb.gate[in.tok[tb]] : 0.f;
+        const int tk = max(in.tok[tb], 0);
+        in.g[tb] = cb.gate[tk];
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
             for (int run = 0; run < 2; ++run) {
                 const int n = n0 + nb * 32 + run * 16 + half * 8;
-                in.rr[tb][nb][run] = (in.tok[tb] >= 0 && cb.residual && n < N)
-                                         ? *(const u32x4*)(cb.residual + (size_t)in.tok[tb] * N + n)
-                                         : u32x4{0u, 0u, 0u, 0u};
+                in.rr[tb][nb][run] = *(const u32x4*)(res + (size_t)tk * N + min(n, N - 8));
+            }
+    }
+    // every load is issued before the selects below use one (one wait for all)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int tb = 0; tb < TOKB; ++tb) {
+        const bool on = in.tok[tb] >= 0;
+        in.g[tb] = on ? in.g[tb] : 0.f;
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+            for (int run = 0; run < 2; ++run) {
+                const int n = n0 + nb * 32 + run * 16 + half * 8;
+                in.rr[tb][nb][run] = (on && cb.residual && n < N) ? in.rr[tb][nb][run] : u32x4{0u, 0u, 0u, 0u};
             }
     }
 }
@@ -197,6 +218,10 @@ __device__ __forceinline__ void ffn_store_tile_direct(f32x16 (&acc)[NBW][TOKB], 
                         const float o1 = fmaf(in.g[tb], a[8 * run + 2 * j + 1], bf16_to_f32(res >> 16));
                         in.rr[tb][nb][run][j] = pack_bf16x2(o0, o1);
                     }
+                    // the results are made here, in straight-line code: sunk into the
+                    // stores' branches, each branch would wait for every memory operation
+                    // before it, the previous stores included
+                    asm volatile("" : "+v"(in.rr[tb][nb][run]));
                 }
 #pragma unroll
             for (int tb = 0; tb < TOKB; ++tb) {
