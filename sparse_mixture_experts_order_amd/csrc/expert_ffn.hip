@@ -320,13 +320,38 @@ __device__ __forceinline__ void ffn_store_tile_direct(f32x16 (&acc)[NBW][TOKB], 
                         u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
                               pack_bf16x2(v[6], v[7])};
                 }
-            } else {
+            }
+        }
+    }
+}
+
+// fp32 output as buffer stores: the descriptor ends with the tile's valid rows
+// and columns past N get an offset past it, so every lane issues every store
+// and a wave always issues exactly ffn_f32_stores<TOKB, NBW> of them (the next
+// wait of the caller counts on that); out-of-range stores are dropped.
+template <int TOKB, int NBW>
+constexpr int ffn_f32_stores = TOKB * NBW * 4;
+
+template <int TOKB, int NBW, int WAVES>
+__device__ __forceinline__ void ffn_store_tile_f32(const f32x16 (&acc)[NBW][TOKB], const FfnTile& t, float* out,
+                                                   int C, int N, int wave, int l32, int half) {
+    constexpr int NWG = WAVES * 32 * NBW;
+    const int n0 = t.nt * NWG + wave * 32 * NBW;
+    const __amdgpu_buffer_rsrc_t rs =
+        buffer_rsrc_uniform(out + ((size_t)t.e * C + t.tok_base) * N, (uint32_t)max(t.nv, 0) * (uint32_t)N * 4u);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int n = n0 + nb * 32 + q * 8 + half * 4;
-                    if (n >= N) continue;
-                    *(f32x4*)((float*)out + row + n) = f32x4{a[4 * q + 0], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
-                }
+    for (int tb = 0; tb < TOKB; ++tb) {
+        const int r = tb * 32 + l32;
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb) {
+            const f32x16& a = acc[nb][tb];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int n = n0 + nb * 32 + q * 8 + half * 4;
+                const uint32_t off = (r < t.nv && n < N) ? (uint32_t)(r * N + n) * 4u : 0x80000000u;
+                const u32x4 v = u32x4{__float_as_uint(a[4 * q + 0]), __float_as_uint(a[4 * q + 1]),
+                                      __float_as_uint(a[4 * q + 2]), __float_as_uint(a[4 * q + 3])};
+                __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, 0);
             }
         }
     }
@@ -848,12 +873,19 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
     for (int p = 0; p < S - 1; ++p) issue(p, p);
 
     CombineInputs<TOKB, NBW> cin;   // the combine epilogue's loads
+    // fp32 output: right after a tile's stores, the wait for the next copies
+    // lets those stores (a fixed number, issued after the copies) stay in flight
+    constexpr int NST = MODE == OUT_F32 ? ffn_f32_stores<TOKB, NBW> : 0;
+    static_assert(PER_CHUNK * (S - 2) + NST < 64, "vmcnt range");
+    bool stored = false;
     for (int p0 = 0; p0 < P; p0 += S) {
 #pragma unroll
         for (int u = 0; u < S; ++u) {
             const int p = p0 + u;
             if (p < P) {
-                wait_copies<PER_CHUNK * (S - 2)>();      // this wave's copies of position p are in LDS
+                if (MODE == OUT_F32 && stored) wait_copies<PER_CHUNK * (S - 2) + NST>();
+                else wait_copies<PER_CHUNK * (S - 2)>();   // this wave's copies of position p are in LDS
+                stored = false;
                 lds_barrier();                           // every wave's too, and position p - 1 is read out
                 issue(p + S - 1, (u + S - 1) % S);      // into the stage of position p - 1
                 const char* sw = lds + u * STAGE;
@@ -899,7 +931,13 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
                         combine_load_tokens(cin, t, cb, C, l32);
                         combine_load_rows(cin, cb, N, t.nt * NWG + wave * 32 * NBW, half);
                     }
-                    ffn_store_tile_direct<TOKB, NBW, WAVES, MODE>(acc, t, out, mask, cb, cin, C, N, wave, l32, half);
+                    if constexpr (MODE == OUT_F32) {
+                        ffn_store_tile_f32<TOKB, NBW, WAVES>(acc, t, (float*)out, C, N, wave, l32, half);
+                        stored = true;
+                    } else {
+                        ffn_store_tile_direct<TOKB, NBW, WAVES, MODE>(acc, t, out, mask, cb, cin, C, N, wave, l32,
+                                                                      half);
+                    }
 #pragma unroll
                     for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
