@@ -661,7 +661,8 @@ class LayerGrads(NamedTuple):
 
 def layer_backward(x, w_r, b_r, w1, w2, c: float, alpha: float, dout, beta: float = 0.0,
                    C: Optional[int] = None, expert_override: Optional[np.ndarray] = None,
-                   forward: Optional[LayerResult] = None, relu_active=None) -> LayerGrads:
+                   forward: Optional[LayerResult] = None, relu_active=None,
+                   dw_experts: Optional[np.ndarray] = None) -> LayerGrads:
     """Gradients of J = sum_t <dout_t, out_t> + L_aux (+ L_z) for the Switch
     layer (one routing group, k = 1; layer_backward_grouped below covers
     routing groups and top-k), in float64, expert by expert.
@@ -669,7 +670,12 @@ def layer_backward(x, w_r, b_r, w1, w2, c: float, alpha: float, dout, beta: floa
     relu_active(e, a) may replace the ReLU derivative [a > 0] of expert e's
     kept rows (a: their pre-activations, tokens in order); tests use it to
     take the device's decision on pre-activations within rounding of zero,
-    as `expert_override` does for near-tie choices."""
+    as `expert_override` does for near-tie choices.
+
+    dw_experts, if given, lists the experts whose weight gradients are
+    returned: dw1 and dw2 then hold only those experts, in that order (every
+    other output is unchanged; this only bounds the memory of the result
+    when E * d * d_ff is large)."""
     x = np.asarray(x, np.float64)
     dout = np.asarray(dout, np.float64)
     L = forward if forward is not None else layer_forward(x, w_r, b_r, w1, w2, c, alpha, C=C,
@@ -681,8 +687,9 @@ def layer_backward(x, w_r, b_r, w1, w2, c: float, alpha: float, dout, beta: floa
     w2e = (lambda e: np.asarray(w2(e) if callable(w2) else w2[e], np.float64))
     F = w1e(0).shape[0]
     dx = dout.copy()
-    dw1 = np.zeros((E, F, d))
-    dw2 = np.zeros((E, d, F))
+    row_of = {e: e for e in range(E)} if dw_experts is None else {int(e): i for i, e in enumerate(dw_experts)}
+    dw1 = np.zeros((len(row_of), F, d))
+    dw2 = np.zeros((len(row_of), d, F))
     dgate = np.zeros(T)
     for e in range(E):
         toks = np.flatnonzero((r.expert == e) & sl.keep)
@@ -696,10 +703,13 @@ def layer_backward(x, w_r, b_r, w1, w2, c: float, alpha: float, dout, beta: floa
         g = r.gate[toks]
         dgate[toks] = np.sum(dout[toks] * y, axis=1)
         dy = g[:, None] * dout[toks]
-        dw2[e] = dy.T @ h
+        j = row_of.get(e)
+        if j is not None:
+            dw2[j] = dy.T @ h
         active = (a > 0) if relu_active is None else relu_active(e, a)
         da = (dy @ W2) * active
-        dw1[e] = da.T @ xe
+        if j is not None:
+            dw1[j] = da.T @ xe
         dx[toks] += da @ W1
     onehot = np.zeros((T, E))
     onehot[np.arange(T), r.expert] = 1.0

@@ -306,7 +306,7 @@ BACKWARD_EDITS = [
     ("dz = (dgate * r.gate)[:, None] * (onehot - r.p)",
      "dz = (dgate * r.gate)[:, None] * (r.p - onehot)"),                             # softmax sign
     ("dx = dx + dz @ w_r64.T", "dx = dx"),                                           # no router path
-    ("dw2[e] = dy.T @ h", "dw2[e] = dy.T @ a"),                                      # pre-activation
+    ("dw2[j] = dy.T @ h", "dw2[j] = dy.T @ a"),                                      # pre-activation
     ("dz = dz + L.aux.dlogits", "dz = dz"),                                          # aux gradient lost
     ("dgate[toks] = np.sum(dout[toks] * y, axis=1)", "dgate[toks] = np.sum(dout[toks] * h @ W2.T * g[:, None], axis=1)"),
 ]

@@ -29,3 +29,22 @@ def test_capacity_rejects_bad_arguments():
 def test_nonfinite_logits_rejected():
     with pytest.raises(ValueError):
         so.softmax_top1(np.array([[0.0, np.nan]]))
+
+
+def test_backward_weight_gradient_subset():
+    """dw_experts only selects which experts' weight gradients are returned:
+    the rows equal the full result's, every other output is identical."""
+    rng = np.random.default_rng(41)
+    T, d, F, E = 96, 8, 12, 5
+    x = rng.standard_normal((T, d))
+    w_r = rng.standard_normal((d, E)) * 0.3
+    w1 = rng.standard_normal((E, F, d)) * 0.2
+    w2 = rng.standard_normal((E, d, F)) * 0.2
+    dout = rng.standard_normal((T, d))
+    full = so.layer_backward(x, w_r, None, w1, w2, 1.0, 0.01, dout)
+    pick = np.array([3, 0])
+    part = so.layer_backward(x, w_r, None, w1, w2, 1.0, 0.01, dout, dw_experts=pick)
+    np.testing.assert_array_equal(part.dw1, full.dw1[pick])
+    np.testing.assert_array_equal(part.dw2, full.dw2[pick])
+    for name in ("dx", "dw_r", "db_r", "dz", "dgate"):
+        np.testing.assert_array_equal(getattr(part, name), getattr(full, name))
