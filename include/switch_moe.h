@@ -80,6 +80,10 @@ size_t switch_workspace_bytes(int64_t T, int32_t d, int32_t d_ff, int32_t E, int
 const char *switch_status_string(switch_status s);
 /* Detail of the last failing call on this host thread ("" if none). */
 const char *switch_last_error(void);
+/* Hash of the sources the library was built from (32 hex digits; "unknown"
+ * when built without it).  The Python binding compares it with the sources
+ * beside the library and refuses a stale build. */
+const char *switch_build_source_hash(void);
 
 /* ------------------------------------------------------- device entry points */
 
@@ -394,6 +398,11 @@ typedef struct switch_layer_bwd_args {
     int64_t group;               /* tokens per routing group */
     const int32_t *slot;         /* [T, k] buffer row of each kept choice (several groups) */
     const int32_t *accepted_total; /* [E] filled buffer rows per expert (several groups) */
+    /* 0: dx = dout + (expert and router terms), the layer's input gradient.
+     * 1: dx = the expert and router terms alone (sum of the kept choices'
+     *    dA W1 rows plus W_r dz_t), rounded to bf16 once; the identity path
+     *    of the residual is left to the caller.  Other values are rejected. */
+    int32_t dx_branch_only;
 } switch_layer_bwd_args;
 
 /* Workspace of switch_layer_bwd: switch_layer_bwd_workspace_bytes_ex(T, d, d_ff,

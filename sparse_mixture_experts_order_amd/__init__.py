@@ -28,7 +28,7 @@ EXPORTS = [
     "switch_profile_collect", "switch_kernel_name", "switch_router_z_loss",
     "switch_route_ex", "switch_dispatch_ex", "switch_dispatch_workspace_bytes_ex", "switch_combine_ex",
     "switch_aux_loss_ex", "switch_workspace_bytes_ex", "switch_layer_bwd", "switch_layer_bwd_workspace_bytes",
-    "switch_layer_bwd_workspace_bytes_ex",
+    "switch_layer_bwd_workspace_bytes_ex", "switch_build_source_hash",
 ]
 
 
@@ -57,16 +57,53 @@ class LayerBwdArgs(ctypes.Structure):
         ("T", ctypes.c_int64), ("d", ctypes.c_int32), ("d_ff", ctypes.c_int32), ("E", ctypes.c_int32),
         ("C", ctypes.c_int32), ("alpha", ctypes.c_float), ("z_beta", ctypes.c_float),
         ("k", ctypes.c_int32), ("group", ctypes.c_int64), ("slot", ctypes.c_void_p),
-        ("accepted_total", ctypes.c_void_p)]
+        ("accepted_total", ctypes.c_void_p), ("dx_branch_only", ctypes.c_int32)]
+
+
+class StaleLibraryError(RuntimeError):
+    """The built library does not match the sources beside it."""
+
+
+_HASH_TAG = b"switch-source-hash:"
+
+
+def library_hash(path: str = LIB_PATH) -> Optional[str]:
+    """The source hash embedded in a built library (read from the file, not
+    loaded, so a rebuild in the same process is seen), or None."""
+    if not os.path.exists(path):
+        return None
+    with open(path, "rb") as fh:
+        data = fh.read()
+    i = data.find(_HASH_TAG)
+    if i < 0:
+        return None
+    j = data.find(b"\0", i)
+    return data[i + len(_HASH_TAG):j].decode(errors="replace")
+
+
+def library_current(path: str = LIB_PATH) -> bool:
+    """True when the library exists and was built from the current sources."""
+    from .build import source_hash
+    return library_hash(path) == source_hash()
 
 
 def lib():
-    """Loads the library once; raises if it has not been built."""
+    """Loads the library once; raises if it has not been built, or if it was
+    built from sources other than the ones beside it (a stale build)."""
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with python -m sparse_mixture_experts_order_amd.build")
+        from .build import source_hash
+        built, want = library_hash(), source_hash()
+        if built != want:
+            raise StaleLibraryError(f"{LIB_PATH} was built from other sources (library {built}, sources {want}): "
+                                    "rebuild it with python -m sparse_mixture_experts_order_amd.build")
         L = ctypes.CDLL(LIB_PATH)
+        L.switch_build_source_hash.restype = ctypes.c_char_p
+        if L.switch_build_source_hash().decode() != want:   # the loader kept an older copy of this path
+            raise StaleLibraryError(f"{LIB_PATH}: the loaded copy predates a rebuild in this process; "
+                                    "start a new process")
         P, I64, I32, SZ, F32, F64 = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t,
                                       ctypes.c_float, ctypes.c_double)
         sig = {
@@ -98,6 +135,7 @@ def lib():
             "switch_layer_bwd_workspace_bytes": (SZ, [I64, I32, I32, I32, I32]),
             "switch_layer_bwd_workspace_bytes_ex": (SZ, [I64, I32, I32, I32, I32, I32, I64]),
             "switch_layer_bwd": (I32, [ctypes.POINTER(LayerBwdArgs), P, SZ, P]),
+            "switch_build_source_hash": (ctypes.c_char_p, []),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -255,7 +293,7 @@ def switch_layer_bwd(args: LayerBwdArgs, ws, stream=None):
 
 
 def make_layer_bwd_args(fwd: dict, x, w_r, w1, w2, dout, grads: dict, T, d, d_ff, E, C, alpha,
-                        z_beta=0.0, k=1, group=0) -> LayerBwdArgs:
+                        z_beta=0.0, k=1, group=0, dx_branch_only=False) -> LayerBwdArgs:
     """fwd: the forward's tensors (expert, gate, position, keep, accepted, f,
     logits, lse, buf, h, y, and with several groups slot and accepted_total);
     grads: dx, dw_r, db_r, dw1, dw2 and optionally dz, dgate.  C is the
@@ -270,6 +308,7 @@ def make_layer_bwd_args(fwd: dict, x, w_r, w1, w2, dout, grads: dict, T, d, d_ff
         setattr(a, name, _ptr(grads.get(name)))
     a.T, a.d, a.d_ff, a.E, a.C, a.alpha, a.z_beta = T, d, d_ff, E, C, alpha, z_beta
     a.k, a.group = k, group
+    a.dx_branch_only = 1 if dx_branch_only else 0
     return a
 
 

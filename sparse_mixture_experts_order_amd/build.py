@@ -4,6 +4,8 @@
 """
 from __future__ import annotations
 
+import glob
+import hashlib
 import os
 import subprocess
 import sys
@@ -16,6 +18,22 @@ LIB = os.path.join(PKG, "libswitch_moe.so")
 OBJ = os.path.join(PKG, "_build")
 SOURCES = ["route.hip", "dispatch.hip", "expert_ffn.hip", "combine.hip", "aux.hip", "backward.hip", "api.hip"]
 ARCH = os.environ.get("SWITCH_MOE_ARCH", "gfx950")
+
+
+def source_hash() -> str:
+    """SHA-256 (first 32 hex digits) over the library's sources: csrc/*.hip,
+    csrc/*.hpp and include/*.h, by file name, then content.  The build embeds
+    it in the library (switch_build_source_hash), and the binding refuses a
+    library whose embedded hash differs from the sources beside it."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.hpp")) +
+                   glob.glob(os.path.join(ROOT, "include", "*.h")))
+    for f in files:
+        h.update(os.path.relpath(f, ROOT).encode() + b"\0")
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+        h.update(b"\0")
+    return h.hexdigest()[:32]
 
 
 def hipcc() -> str:
@@ -45,9 +63,12 @@ def build(verbose: bool = False) -> str:
     """Compiles every source and links the shared library; returns its path."""
     os.makedirs(OBJ, exist_ok=True)
 
+    digest = source_hash()
+
     def compile_one(src):
         obj = os.path.join(OBJ, src.replace(".hip", ".o"))
-        out = _run([hipcc(), *flags(), "-c", os.path.join(CSRC, src), "-o", obj])
+        extra = [f'-DSWITCH_SOURCE_HASH="{digest}"'] if src == "api.hip" else []
+        out = _run([hipcc(), *flags(), *extra, "-c", os.path.join(CSRC, src), "-o", obj])
         if verbose and out.strip():
             print(out)
         return obj

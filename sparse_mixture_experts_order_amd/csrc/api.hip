@@ -579,6 +579,7 @@ switch_status switch_layer_bwd(const switch_layer_bwd_args* ba, void* ws, size_t
     SUPPORT((int64_t)E * std::max<int64_t>(pad64(C), std::max(d, F)) * std::max(d, F) < (int64_t(1) << 40),
             "E*C*max(d,d_ff) too large");
     REQUIRE(std::isfinite(B.alpha) && std::isfinite(B.z_beta), "alpha and z_beta must be finite");
+    REQUIRE(B.dx_branch_only == 0 || B.dx_branch_only == 1, "dx_branch_only must be 0 or 1");
     SUPPORT((int64_t)d * F * 2 < (int64_t(1) << 31), "one expert's weights must be < 2 GiB (d*d_ff*2)");
     SUPPORT((int64_t)pad64(C) * std::max(d, F) * 2 < (int64_t(1) << 31), "C*max(d,d_ff)*2 must be < 2 GiB");
     // one group: the buffer row is the position and accepted counts the filled rows
@@ -682,7 +683,8 @@ switch_status switch_layer_bwd(const switch_layer_bwd_args* ba, void* ws, size_t
     }
     // dx = dout + sum of the kept choices' dbuf rows + dz W_r^T
     LAUNCH(K_DX, "dx_assemble", s,
-           launch_dx_assemble(B.dout, dbuf, B.expert, slot, B.keep, dz, B.w_r, T, d, E, k, C, B.dx, s));
+           launch_dx_assemble(B.dx_branch_only ? nullptr : B.dout, dbuf, B.expert, slot, B.keep, dz, B.w_r, T, d,
+                              E, k, C, B.dx, s));
     return SWITCH_OK;
 }
 
@@ -712,6 +714,13 @@ const char* switch_status_string(switch_status s) {
 }
 
 const char* switch_last_error(void) { return g_err.c_str(); }
+
+#ifndef SWITCH_SOURCE_HASH
+#define SWITCH_SOURCE_HASH "unknown"
+#endif
+// the marker lets a reader find the hash in the file without loading it
+static const char kSourceHashTag[] = "switch-source-hash:" SWITCH_SOURCE_HASH;
+const char* switch_build_source_hash(void) { return kSourceHashTag + sizeof("switch-source-hash:") - 1; }
 
 switch_status switch_route(const switch_bf16* x, const float* w_r, const float* b_r, const float* logits_in,
                            int64_t T, int32_t d, int32_t E, float* logits_out, int32_t* expert, float* gate,

@@ -21,7 +21,8 @@
 //   router_wgrad_reduce  the slices added in order in fp64
 //   dx_assemble     dx_t = bf16(dout_t + sum_e dz_te W_r[:, e] + sum_i dbuf[e_ti, s_ti])
 //                   over the token's kept choices (dx_assemble_mfma on the bf16
-//                   MFMA when E is a multiple of 32)
+//                   MFMA when E is a multiple of 32); dout == NULL leaves the
+//                   identity term out (the branch of dx alone)
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -282,7 +283,7 @@ __global__ __launch_bounds__(256) void dx_assemble(const bf16_t* __restrict__ do
         const int64_t t = t0 + tq * 4 + a;
         if (t >= T) break;
         const int i = i0 + iq * 4;
-        const uint2 dv = *(const uint2*)(dout + t * d + i);
+        const uint2 dv = dout ? *(const uint2*)(dout + t * d + i) : make_uint2(0, 0);
         float v[4] = {bf16_to_f32(dv.x & 0xffffu) + acc[a][0], bf16_to_f32(dv.x >> 16) + acc[a][1],
                       bf16_to_f32(dv.y & 0xffffu) + acc[a][2], bf16_to_f32(dv.y >> 16) + acc[a][3]};
         for (int c = 0; c < k; ++c) {   // the kept choices in rank order
@@ -461,7 +462,7 @@ __global__ __launch_bounds__(256) void dx_assemble_mfma(const bf16_t* __restrict
                 for (int run = 0; run < 2; ++run) {
                     const int i = i0 + 32 * a + 16 * run + 8 * h;
                     if (c == 0) {
-                        dv[b][a][run] = *(const uint4*)(dout + tc * d + i);
+                        dv[b][a][run] = dout ? *(const uint4*)(dout + tc * d + i) : make_uint4(0, 0, 0, 0);
                         bq[b][a][run][0] = bq[b][a][run][1] = f32x4{0.f, 0.f, 0.f, 0.f};
                     }
                     if (kept) {

@@ -28,6 +28,21 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert sorted(sw.EXPORTS) == names
 
 
+def test_library_is_built_from_the_current_sources(tmp_path):
+    """The library carries the hash of the sources it was built from; a file
+    with another hash (or none) is not current, and lib() would refuse it."""
+    from sparse_mixture_experts_order_amd.build import source_hash
+    assert sw.library_hash() == source_hash()
+    assert sw.library_current()
+    other = tmp_path / "lib.so"
+    other.write_bytes(b"\x7fELF...switch-source-hash:" + b"0" * 32 + b"\0rest")
+    assert sw.library_hash(str(other)) == "0" * 32
+    assert not sw.library_current(str(other))
+    none = tmp_path / "none.so"
+    none.write_bytes(b"\x7fELF no tag")
+    assert sw.library_hash(str(none)) is None and not sw.library_current(str(none))
+
+
 def test_capacity_matches_oracle():
     cases = [(512, 4, 1.25), (16384, 128, 1.0), (16384, 64, 2.0), (32768, 128, 1.25), (65536, 2048, 1.0),
              (64, 4, 1.25), (100, 10, 1.0), (30, 3, 0.1), (0, 5, 3.0), (7, 7, 0.0), (1, 4096, 1e-300),

@@ -349,6 +349,47 @@ def test_layer_ex_end_to_end(ci, k, G, priority):
     assert_residual_close(ob2[toks], D.inp.x[toks], ref, f"layer_ex cfg{ci} residual out")
 
 
+# (config, k, group, priority) of the layer with no buf, slot_token or y kept
+NO_BUF_CASES = [(2, 2, 0, 0), (2, 1, 2048, 0), (3, 2, 0, 1), (4, 2, 8192, 0)]
+
+
+@pytest.mark.parametrize("ci,k,G,priority", NO_BUF_CASES)
+def test_layer_ex_no_buf_branch(ci, k, G, priority):
+    """The extended layer as a caller that keeps no intermediates runs it: the
+    first expert GEMM gathers its token rows from x through the workspace slot
+    table, and with k = 1 the second GEMM writes the combine.  Branch mode,
+    every token with a kept choice against the oracle at the stated
+    tolerance; tokens with every choice dropped carry exactly 0."""
+    D = inputs(ci)
+    cfg = D.cfg
+    T, E = cfg.T, cfg.E
+    C = so.group_capacity(G or T, E, cfg.c, k)
+    pr = "rank" if priority else "token"
+    say(f"layer_ex no-buf cfg{ci} k={k} G={G} C={C} {pr}: run")
+    t = run_layer_ex(D, k, G, C, priority, residual=False, inspect=False)
+    r = so.softmax_topk(D.z, k)
+    near = topk_near(D.z, k)
+    e_dev = t["expert"].cpu().numpy().reshape(T, k)
+    np.testing.assert_array_equal(e_dev[~near], r.expert[~near])
+    e_res = np.where(near[:, None], e_dev, r.expert)
+    gate_ref = np.take_along_axis(r.p, e_res, axis=1)
+    sl = so.slot_scan_grouped(e_res, E, G or T, C, pr)
+    shp = lambda a: a.cpu().numpy().reshape(T, k)
+    np.testing.assert_array_equal(shp(t["position"]), sl.position)
+    np.testing.assert_array_equal(shp(t["keep"]).astype(bool), sl.keep)
+    if "slot" in t:
+        np.testing.assert_array_equal(shp(t["slot"]), sl.slot)
+    np.testing.assert_array_equal(t["counts"].cpu().numpy().reshape(sl.counts.shape), sl.counts)
+    kept_any = sl.keep.any(axis=1)
+    ob = dev_bits(t["out"])
+    assert np.all(ob[~kept_any] == 0), "tokens with every choice dropped carry a zero branch"
+    toks = np.flatnonzero(kept_any)
+    say(f"layer_ex no-buf cfg{ci}: oracle branch on all {toks.size} tokens with a kept choice")
+    ref = oracle_branch_topk(D.inp, toks, e_res, gate_ref, sl.keep)
+    rf, mr = assert_branch_close(workloads.bf16_bits_to_f32(ob[toks]), ref, f"layer_ex no-buf cfg{ci} branch")
+    say(f"layer_ex no-buf cfg{ci}: rel fro {rf:.2e}, max/rms {mr:.2e}, kept choices {int(sl.keep.sum())}/{T * k}")
+
+
 @pytest.mark.parametrize("ci", [1, 2])
 def test_layer_ex_one_group_top1_is_the_switch_layer(ci):
     """k = 1 with group 0 or group T: the extended layer equals the Switch layer bit for bit."""
