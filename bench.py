@@ -6,12 +6,18 @@ loss) on one MI355X, with the fp64 oracle timed on the host beside it.
 Prints one JSON line.  A step is one switch_layer_fwd over the whole batch of
 seeded synthetic inputs (already in HBM when timing starts).  The default
 workload is the Switch-Base-shaped layer: T=16384 tokens, d=768, d_ff=3072,
-E=128 experts, capacity factor 1.0 (C=128).
+E=128 experts, capacity factor 1.0 (C=128).  The other layer shapes
+(congested 64 experts at c=2, Switch-Large-shaped, 2048 small experts) are
+measured after it under "per_config", each warm and with the caches flushed,
+with the standalone dispatch and combine entry points timed on their own.
+
+Bytes and flops are the method's algorithmic ones (no padded capacity slots,
+no round trip of the hidden activation); every roofline floor is
+max(flops / bf16 peak, bytes / HBM peak) with the MI355X spec peaks.
 """
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import platform
@@ -27,6 +33,11 @@ METRIC = "Switch FFN layer fwd tokens/s (E=128,d=768) + % bf16 MFMA peak + dispa
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 PROFILES = os.path.join(ROOT, "profiles")
+EVICT_BYTES = 512 << 20         # larger than the 256 MB memory-side cache
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
 
 
 def parse():
@@ -37,11 +48,27 @@ def parse():
     p.add_argument("--config", type=int, default=2, help="layer configuration 1..5 (2 = Switch-Base shape)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-variants", action="store_true",
-                   help="skip the timing of the layer variants (z-loss, routing groups, top-2)")
+                   help="skip the timing of the layer variants (z-loss, routing groups, top-2, backward)")
+    p.add_argument("--no-per-config", action="store_true", help="skip the other layer shapes")
+    p.add_argument("--per-config", type=str, default="3,4,5", help="other layer shapes to measure")
+    p.add_argument("--only-layer", action="store_true",
+                   help="time the main configuration's layer and nothing else (for profiler runs)")
     p.add_argument("--cpu-sample-tokens", type=int, default=0,
                    help="tokens in the oracle's timed sample (0 = the whole batch)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                    help="only run the plain copy kernel on BYTES bytes (hardware-counter calibration)")
+    p.add_argument("--standalone", action="store_true",
+                   help="only time the standalone dispatch and combine entry points (profiler runs)")
+    p.add_argument("--summarize-trace", metavar="DIR",
+                   help="write a kernel-time summary of a rocprofv3 --kernel-trace --stats output directory")
+    p.add_argument("--summarize-counters", metavar="DIR", nargs="+",
+                   help="write a per-kernel summary of rocprofv3 --pmc output directories")
+    p.add_argument("--calibration", metavar="DIR", nargs="*", default=[],
+                   help="--pmc output directories of the copy calibration run (FETCH_SIZE / WRITE_SIZE scales)")
+    p.add_argument("--copy-bytes", type=int, default=0, help="bytes of the calibration copy")
+    p.add_argument("--workload", default="", help="workload name written into a summary")
+    p.add_argument("--command", default="", help="the profiler command written into a summary")
+    p.add_argument("--out", default="", help="summary file to write")
     return p.parse_args()
 
 
@@ -65,16 +92,51 @@ def copy_calibration(nbytes: int, reps: int):
     print(json.dumps({"copy_bytes": nbytes, "reps": reps, "ms": ms, "GBps_read_plus_write": 2 * nbytes / ms / 1e6}))
 
 
-def kernel_source_sha() -> str:
-    src = os.path.join(ROOT, "sparse_mixture_experts_order_amd", "csrc", "expert_ffn.hip")
-    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+# ------------------------------------------------------------ algorithmic work
+def floors(T, d, F, E, C, A, want_grad):
+    """The method's algorithmic bytes and flops per step and their roofline
+    floors in microseconds (A = accepted tokens)."""
+    def fl(flops, nbytes):
+        return max(flops / (PEAK_BF16_TFLOPS * 1e12), nbytes / (PEAK_HBM_GBPS * 1e9)) * 1e6
+    w = 2 * E * F * d
+    work = {
+        "router": dict(flops=2 * T * d * E, bytes=2 * T * d + 4 * d * E + 12 * T),
+        "dispatch": dict(flops=0, bytes=2 * A * d + 2 * E * C * d + 9 * T + 4 * E * C),
+        "ffn": dict(flops=4 * A * d * F, bytes=2 * w + 2 * A * d + 4 * A * d),
+        "combine": dict(flops=0, bytes=4 * A * d + 2 * T * d + 2 * T * d + 13 * T),
+        "aux": dict(flops=0, bytes=(8 * T * E + 4 * T) if want_grad else 8 * E),
+    }
+    for v in work.values():
+        v["floor_us"] = fl(v["flops"], v["bytes"])
+    return work
 
 
+def kernel_bytes(T, d, F, E, C, A, fused, gathered):
+    """Algorithmic bytes per launch of the layer's kernels (the hidden
+    activation's write and read excluded, as in the step floors)."""
+    w = 2 * E * F * d
+    return {
+        "expert_gemm1": w + 2 * A * d,
+        "expert_gemm2": w + (2 * A * d + 2 * A * d + 8 * A if fused else 4 * A * d),
+        "expert_gemm2_with_h": w + 2 * A * F + (2 * A * d + 2 * A * d + 8 * A if fused else 4 * A * d),
+        # with the token rows gathered by the first GEMM no row is copied here:
+        # positions and masks, the slot table, and the dropped tokens' residual rows
+        "gather": (9 * T + 4 * A + (4 * (T - A) * d if fused else 0)) if gathered else
+                  (2 * A * d + 2 * E * C * d + 9 * T + 4 * E * C + (4 * (T - A) * d if fused else 0)),
+        "combine": 4 * A * d + 2 * T * d + 2 * T * d + 13 * T,
+        "router_fused": 2 * T * d + 6 * d * E + 12 * T,
+        "router_gemm": 2 * T * d + 6 * d * E + 4 * T * E,
+        "router_softmax": 4 * T * E + 12 * T,
+    }
+
+
+# ------------------------------------------------------------ counter summaries
 def read_traffic(kernel: str, workload: str):
     """HBM bytes per launch of `kernel` (FETCH_SIZE + WRITE_SIZE, each scaled by
     the same counter's reading on a plain copy of known size) from the committed
-    counter summary, or None when the summary is missing or was taken on a
-    different expert-kernel source."""
+    counter summary, or None when the summary is missing or was taken on other
+    library sources."""
+    from sparse_mixture_experts_order_amd.build import source_hash
     path = os.path.join(PROFILES, f"traffic_{workload}.txt")
     if not os.path.exists(path):
         return None
@@ -83,10 +145,378 @@ def read_traffic(kernel: str, workload: str):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("source_sha256_16") != kernel_source_sha():
+    if vals.get("library_source_hash") != source_hash():
         return None
     f, w = vals.get(f"{kernel}_fetch_bytes_per_launch"), vals.get(f"{kernel}_write_bytes_per_launch")
     return float(f) + float(w) if f and w else None
+
+
+# ------------------------------------------------------------ profiler summaries
+# The library's kernels under the names bench.py and the summaries use.  The
+# expert GEMM templates carry their output mode (0: ReLU to bf16 = the first
+# GEMM; 1: fp32 and 3: the combine epilogue = the second one; 2: the
+# backward's masked product) as the fourth (direct-to-LDS kernel) or fifth
+# (register kernel) template argument.
+def kernel_role(name: str) -> str:
+    import re
+    n = name.strip().strip('"')
+    m = re.search(r"(?:swmoe::)?(\w+)<([^>(]*)", n)
+    base = m.group(1) if m else re.sub(r"\(.*", "", n).split("::")[-1].strip()
+    args = [a.strip() for a in m.group(2).split(",")] if m else []
+    if base in ("expert_gemm_dma", "expert_gemm"):
+        mode = args[3] if base == "expert_gemm_dma" else (args[4] if len(args) > 4 else "")
+        return {"0": "expert_gemm1", "1": "expert_gemm2", "3": "expert_gemm2", "2": "gemm_masked"}.get(mode, base)
+    if base.startswith("router_softmax"):
+        return "router_softmax"
+    if base.startswith("scan_local"):
+        return "scan_local"
+    return base
+
+
+def _csv_rows(directory: str, suffix: str):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True)):
+        with open(f, newline="") as fh:
+            rows.extend(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit(f"no *{suffix} under {directory}")
+    return rows
+
+
+def summarize_trace(args):
+    rows = _csv_rows(args.summarize_trace, "kernel_trace.csv")
+    per = {}
+    for r in rows:
+        role = kernel_role(r["Kernel_Name"])
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+        per.setdefault(role, []).append(dur)
+    total = sum(sum(v) for v in per.values())
+    lines = [f"# rocprofv3 kernel trace, workload {args.workload} (one MI355X)",
+             f"# command: {args.command}",
+             "# averages over every call in the run (warm-up, timed steps and the per-launch event pass)",
+             "",
+             f"{'kernel':<28}{'calls':>8}{'avg_us':>10}{'min_us':>10}{'max_us':>10}{'pct':>8}"]
+    for role, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"{role:<28}{len(v):>8}{np.mean(v):>10.2f}{np.min(v):>10.2f}{np.max(v):>10.2f}"
+                     f"{100 * sum(v) / total:>8.2f}")
+    text = "\n".join(lines) + "\n"
+    open(args.out, "w").write(text) if args.out else None
+    print(text)
+
+
+def _counter_means(directory: str):
+    """{role: {counter: mean value per dispatch}} from a --pmc run."""
+    acc = {}
+    for r in _csv_rows(directory, "counter_collection.csv"):
+        role = kernel_role(r["Kernel_Name"])
+        key = (role, r["Counter_Name"])
+        acc.setdefault(key, {}).setdefault(r.get("Dispatch_Id", len(acc)), 0.0)
+        acc[key][r.get("Dispatch_Id", len(acc))] += float(r["Counter_Value"])
+    out = {}
+    for (role, cn), disp in acc.items():
+        out.setdefault(role, {})[cn] = float(np.mean(list(disp.values())))
+    return out
+
+
+def summarize_counters(args):
+    from sparse_mixture_experts_order_amd.build import source_hash
+    means = {}
+    for dr in args.summarize_counters:
+        for role, cs in _counter_means(dr).items():
+            means.setdefault(role, {}).update(cs)
+    scale = {}
+    for dr in args.calibration:
+        for role, cs in _counter_means(dr).items():
+            if role == "stream_copy_kernel":
+                for cn, v in cs.items():
+                    if cn in ("FETCH_SIZE", "WRITE_SIZE") and v > 0:
+                        scale[cn] = args.copy_bytes / (v * 1024.0)
+    lines = [f"# per-dispatch hardware counters, workload {args.workload} (one MI355X)",
+             f"# command: {args.command}",
+             f"# library_source_hash below: the sources the counters were taken on"]
+    if scale:
+        lines.append(f"# FETCH_SIZE / WRITE_SIZE (KiB) scaled by their reading on the library's plain copy kernel "
+                     f"of {args.copy_bytes} bytes")
+    lines.append(f"library_source_hash: {source_hash()}")
+    for cn, v in sorted(scale.items()):
+        lines.append(f"{cn.lower()}_scale: {v:.4f}")
+    for role, cs in sorted(means.items()):
+        for cn, v in sorted(cs.items()):
+            lines.append(f"{role}_{cn}: {v:.1f}")
+        if "FETCH_SIZE" in cs and "FETCH_SIZE" in scale:
+            lines.append(f"{role}_fetch_bytes_per_launch: {cs['FETCH_SIZE'] * 1024 * scale['FETCH_SIZE']:.0f}")
+        if "WRITE_SIZE" in cs and "WRITE_SIZE" in scale:
+            lines.append(f"{role}_write_bytes_per_launch: {cs['WRITE_SIZE'] * 1024 * scale['WRITE_SIZE']:.0f}")
+    text = "\n".join(lines) + "\n"
+    open(args.out, "w").write(text) if args.out else None
+    print(text)
+
+
+# ------------------------------------------------------------ device helpers
+def device_inputs(cfg, torch):
+    import workloads
+    inp = workloads.make_layer_inputs(cfg)
+    to_bf16 = lambda bits: torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to("cuda")
+    dev = dict(x=to_bf16(inp.x_bits), w1=to_bf16(inp.w1_bits), w2=to_bf16(inp.w2_bits),
+               w_r=torch.from_numpy(inp.w_r).to("cuda"), b_r=torch.from_numpy(inp.b_r).to("cuda"))
+    return inp, dev
+
+
+def timed_loop(torch, stream, fn, steps, warmup):
+    for _ in range(warmup):
+        fn()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(steps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def kernel_times(sw, torch, fn, steps):
+    """Per-kernel mean durations (us) from the library's per-launch events."""
+    sw.switch_profile_enable(True)
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    recs = sw.switch_profile_collect()
+    sw.switch_profile_enable(False)
+    per, count = {}, {}
+    for name, ms in recs:
+        per[name] = per.get(name, 0.0) + ms
+        count[name] = count.get(name, 0) + 1
+    # mean per launch, and the total per step
+    return ({k: 1000.0 * per[k] / count[k] for k in per}, {k: 1000.0 * per[k] / steps for k in per},
+            {k: count[k] / steps for k in per})
+
+
+def cold_times(torch, stream, fn, steps):
+    """Median step time (ms) with a 512 MiB buffer written before every step,
+    so no input, weight or workspace byte is still in the caches (the events
+    bracket the step only)."""
+    evict = torch.empty(EVICT_BYTES // 4, dtype=torch.float32, device="cuda")
+    fn()
+    ms = []
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        evict.fill_(float(i))
+        evs[i][0].record(stream)
+        fn()
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in evs]
+    del evict
+    return float(np.median(ms)), float(np.min(ms))
+
+
+# ------------------------------------------------------------ one configuration
+def measure_layer(sw, torch, cfg, dev, stream, steps, warmup, cold=True):
+    """The timed layer (no intermediates kept: the first expert GEMM gathers
+    its rows from x, the second writes the combine when k = 1 and C > 64)."""
+    T, d, F, E = cfg.T, cfg.d, cfg.d_ff, cfg.E
+    C = sw.switch_capacity(T, E, cfg.c)
+    t = sw.layer_tensors(T, d, F, E, C, dlogits=cfg.want_grad)
+    la = sw.make_layer_args(dev["x"], dev["w_r"], dev["b_r"], dev["w1"], dev["w2"], t, T, d, F, E, C, cfg.alpha,
+                            residual=True)
+
+    def step():
+        sw.switch_layer_fwd(la, t["ws"], stream)
+
+    wall0 = time.perf_counter()
+    ms = timed_loop(torch, stream, step, steps, warmup)
+    wall = time.perf_counter() - wall0
+    mean_us, per_step_us, launches = kernel_times(sw, torch, step, steps)
+    accepted = t["accepted"].cpu().numpy().astype(np.int64)
+    A = int(accepted.sum())
+    fused = "combine" not in mean_us
+    gathered = fused or ("gather" in mean_us and C > 64)
+    kb = kernel_bytes(T, d, F, E, C, A, fused, gathered)
+    wk = floors(T, d, F, E, C, A, cfg.want_grad)
+    gemms = [k for k in ("expert_gemm1", "expert_gemm2") if k in mean_us]
+    dominant = max(gemms, key=lambda k: mean_us[k])
+    ffn_us = sum(per_step_us[k] for k in gemms)
+    router_us = sum(per_step_us.get(k, 0.0) for k in ("split_router_weights", "router_fused", "router_gemm",
+                                                      "router_softmax", "router_reduce"))
+    layer_floor = sum(v["floor_us"] for v in wk.values())
+    res = {
+        "workload": cfg.name, "T": T, "d_model": d, "d_ff": F, "E": E, "capacity_factor": cfg.c, "C": C,
+        "ms_per_step": ms, "tokens_per_s": T / (ms / 1e3), "wall_s_timed": wall,
+        "layer_floor_us": layer_floor, "layer_roofline_frac": layer_floor / (ms * 1e3),
+        "routing": {"accepted": A, "drop_rate": 1 - A / T, "empty_slot_ratio": 1 - A / (E * C) if C else None},
+        "kernels_us": {k: round(v, 2) for k, v in sorted(per_step_us.items(), key=lambda kv: -kv[1])},
+        "ffn": {
+            "us": ffn_us, "floor_us": wk["ffn"]["floor_us"], "roofline_frac": wk["ffn"]["floor_us"] / ffn_us,
+            "mfma_pct_of_bf16_peak": 100.0 * wk["ffn"]["flops"] / (ffn_us * 1e-6) / (PEAK_BF16_TFLOPS * 1e12),
+            "hbm_GBps": wk["ffn"]["bytes"] / (ffn_us * 1e-6) / 1e9,
+            "algorithmic_flops": wk["ffn"]["flops"], "algorithmic_bytes": wk["ffn"]["bytes"],
+        },
+        "router": {"us": router_us, "floor_us": wk["router"]["floor_us"],
+                   "roofline_frac": wk["router"]["floor_us"] / router_us if router_us else None,
+                   "mfma_pct_of_bf16_peak": 100.0 * wk["router"]["flops"] / (router_us * 1e-6) /
+                   (PEAK_BF16_TFLOPS * 1e12) if router_us else None},
+        "dispatch_in_layer": ({"fused": True, "into": "expert_gemm1 (token rows gathered from x)",
+                               "gather_us": per_step_us.get("gather"), "gather_bytes": kb["gather"],
+                               "gather_GBps": kb["gather"] / (mean_us["gather"] * 1e-6) / 1e9}
+                              if gathered else
+                              {"fused": False, "gather_us": per_step_us.get("gather"),
+                               "GBps": kb["gather"] / (mean_us["gather"] * 1e-6) / 1e9}),
+        "combine_in_layer": ({"fused": True, "into": "expert_gemm2 epilogue"} if fused else
+                             {"fused": False, "us": per_step_us["combine"],
+                              "GBps": kb["combine"] / (mean_us["combine"] * 1e-6) / 1e9}),
+    }
+    achieved = kb[dominant] / (mean_us[dominant] * 1e-6) / 1e9
+    traffic = read_traffic(dominant, cfg.name)
+    res["roofline"] = {
+        "kernel": dominant, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+        "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
+        "traffic_over_algorithmic": traffic / kb[dominant] if traffic else None,
+        "algorithmic_bytes": kb[dominant], "avg_launch_us": mean_us[dominant],
+        "launches_per_step": launches[dominant],
+    }
+    if dominant == "expert_gemm2":
+        res["roofline"]["achieved_with_h_read"] = kb["expert_gemm2_with_h"] / (mean_us[dominant] * 1e-6) / 1e9
+    if cold:
+        med, mn = cold_times(torch, stream, step, min(steps, 20))
+        res["cold"] = {"ms_per_step_median": med, "ms_per_step_min": mn, "tokens_per_s": T / (med / 1e3),
+                       "flush": f"{EVICT_BYTES >> 20} MiB written before each step"}
+    return res, t, C, A
+
+
+def measure_standalone(sw, torch, cfg, dev, t_layer, C, A, stream, steps, warmup):
+    """switch_dispatch (scan + gather writing the [E, C, d] buffer, empty slots
+    zero-filled) and switch_combine (residual mode, fp32 y) on the layer's
+    own routing, each timed on its own."""
+    T, d, E = cfg.T, cfg.d, cfg.E
+    x = dev["x"]
+    expert = t_layer["expert"]
+    o = dict(position=torch.empty(T, dtype=torch.int32, device="cuda"),
+             keep=torch.empty(T, dtype=torch.uint8, device="cuda"),
+             counts=torch.empty(E, dtype=torch.int32, device="cuda"),
+             accepted=torch.empty(E, dtype=torch.int32, device="cuda"),
+             slot_token=torch.empty((E, C), dtype=torch.int32, device="cuda"),
+             buf=torch.empty((E, C, d), dtype=torch.bfloat16, device="cuda"))
+    ws = torch.empty(max(256, sw.switch_dispatch_workspace_bytes(T, E)), dtype=torch.uint8, device="cuda")
+
+    def disp():
+        sw.switch_dispatch(x, expert, T, d, E, C, o["position"], o["keep"], o["counts"], o["accepted"],
+                           o["slot_token"], o["buf"], ws, stream)
+
+    ms_d = timed_loop(torch, stream, disp, steps, warmup)
+    mean_d, step_d, _ = kernel_times(sw, torch, disp, steps)
+    wk = floors(T, d, cfg.d_ff, E, C, A, False)
+    y = torch.randn((E, C, d), dtype=torch.float32, device="cuda", generator=torch.Generator("cuda").manual_seed(3))
+    out = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+
+    def comb():
+        sw.switch_combine(y, expert, o["position"], o["keep"], t_layer["gate"], x, T, d, E, C, out, stream)
+
+    ms_c = timed_loop(torch, stream, comb, steps, warmup)
+    mean_c, _, _ = kernel_times(sw, torch, comb, steps)
+    db, cb = wk["dispatch"]["bytes"], wk["combine"]["bytes"]
+    res = {
+        "dispatch": {"us": ms_d * 1e3, "bytes": db, "GBps": db / (ms_d * 1e-3) / 1e9,
+                     "frac_of_hbm_peak": db / (ms_d * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                     "kernels_us": {k: round(v, 2) for k, v in step_d.items()},
+                     "gather_GBps": db / (mean_d["gather"] * 1e-6) / 1e9 if "gather" in mean_d else None},
+        "combine": {"us": ms_c * 1e3, "bytes": cb, "GBps": cb / (ms_c * 1e-3) / 1e9,
+                    "frac_of_hbm_peak": cb / (ms_c * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                    "kernel_us": round(mean_c.get("combine", 0.0), 2)},
+    }
+    del o, ws, y, out
+    return res
+
+
+# ------------------------------------------------------------ variants (main config)
+def time_variants(sw, torch, cfg, dev, stream, steps, warmup):
+    """The same layer with the rows beyond the Switch forward switched on: the
+    router z-loss, routing groups of 64 tokens (capacity per group), and top-2
+    choices in groups of 2048 tokens.  Each variant: warm-up, then `steps`
+    timed steps between events on the launch stream."""
+    out = {}
+    variants = [
+        ("z_loss", dict(k=1, group=0, z=True)),
+        ("groups_of_64", dict(k=1, group=64, z=False)),
+        ("top2_groups_of_2048", dict(k=2, group=2048, z=False)),
+        ("top2_one_group", dict(k=2, group=0, z=False)),
+    ]
+    x, w_r, b_r, w1, w2 = dev["x"], dev["w_r"], dev["b_r"], dev["w1"], dev["w2"]
+    for name, v in variants:
+        G = v["group"] or cfg.T
+        if cfg.T % G:
+            continue
+        C = sw.switch_capacity(v["k"] * G, cfg.E, cfg.c)
+        t = sw.layer_tensors(cfg.T, cfg.d, cfg.d_ff, cfg.E, C, dlogits=cfg.want_grad, z_loss=v["z"], k=v["k"],
+                             group=v["group"])
+        la = sw.make_layer_args(x, w_r, b_r, w1, w2, t, cfg.T, cfg.d, cfg.d_ff, cfg.E, C, cfg.alpha, residual=True,
+                                z_beta=1e-3 if v["z"] else 0.0, k=v["k"], group=v["group"])
+        ms = timed_loop(torch, stream, lambda: sw.switch_layer_fwd(la, t["ws"], stream), steps, warmup)
+        keep = t["keep"].cpu().numpy()
+        out[name] = {"k": v["k"], "group": G, "C_per_group": C, "ms_per_step": ms,
+                     "tokens_per_s": cfg.T / (ms / 1000.0), "kept_choices": float(keep.mean())}
+        del t, la
+    out["backward"] = time_backward(sw, torch, cfg, dev, stream, steps, warmup)
+    return out
+
+
+def time_backward(sw, torch, cfg, dev, stream, steps, warmup):
+    """The layer backward (switch_layer_bwd) after a forward that keeps what it
+    needs (logits, hidden activations, dispatch buffer, expert outputs); a
+    step is one backward.  Per-kernel times from the library's events."""
+    T, d, F, E = cfg.T, cfg.d, cfg.d_ff, cfg.E
+    x, w_r, b_r, w1, w2 = dev["x"], dev["w_r"], dev["b_r"], dev["w1"], dev["w2"]
+    C = sw.switch_capacity(T, E, cfg.c)
+    t = sw.layer_tensors(T, d, F, E, C, for_backward=True)
+    la = sw.make_layer_args(x, w_r, b_r, w1, w2, t, T, d, F, E, C, cfg.alpha, residual=True)
+    sw.switch_layer_fwd(la, t["ws"], stream)
+    dout = torch.randn((T, d), device=x.device, generator=torch.Generator(device=x.device).manual_seed(7)).to(
+        torch.bfloat16)
+    g = sw.layer_bwd_tensors(T, d, F, E, C)
+    ba = sw.make_layer_bwd_args(t, x, w_r, w1, w2, dout, g, T, d, F, E, C, cfg.alpha)
+    step = lambda: sw.switch_layer_bwd(ba, g["ws"], stream)
+    ms = timed_loop(torch, stream, step, steps, warmup)
+    _, per_step_us, _ = kernel_times(sw, torch, step, steps)
+    kern = {k: round(v, 2) for k, v in sorted(per_step_us.items(), key=lambda kv: -kv[1])}
+    return {"ms_per_step": ms, "tokens_per_s": T / (ms / 1000.0), "kernels_us_per_step": kern,
+            "weight_grad_bytes_fp32": 2 * 2 * E * F * d}
+
+
+def mfma_ceiling(torch, stream):
+    """A large bf16 GEMM through torch (the vendor BLAS), run only: the
+    measured dense-MFMA ceiling beside the spec peak."""
+    n = 8192
+    g = torch.Generator("cuda").manual_seed(1)
+    a = torch.randn((n, n), device="cuda", generator=g).to(torch.bfloat16)
+    b = torch.randn((n, n), device="cuda", generator=g).to(torch.bfloat16)
+    c = torch.empty((n, n), device="cuda", dtype=torch.bfloat16)
+    ms = timed_loop(torch, stream, lambda: torch.matmul(a, b, out=c), 10, 3)
+    del a, b, c
+    return {"gemm": f"bf16 {n}x{n}x{n} torch.matmul", "TFLOPs": 2 * n ** 3 / (ms * 1e-3) / 1e12,
+            "frac_of_spec_peak": 2 * n ** 3 / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+
+
+# ------------------------------------------------------------ CPU baseline
+def host_description():
+    model = platform.processor() or platform.machine()
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        cfg = np.show_config(mode="dicts")
+        bl = cfg.get("Build Dependencies", {}).get("blas", {})
+        blas = f"{bl.get('name', '?')} {bl.get('version', '')}".strip()
+    except Exception:
+        pass
+    return model, blas
 
 
 def cpu_baseline(inp, cfg, sample_tokens):
@@ -108,83 +538,6 @@ def cpu_baseline(inp, cfg, sample_tokens):
     return n / dt, dt, threads, n
 
 
-def time_variants(sw, torch, cfg, x, w_r, b_r, w1, w2, stream, steps, warmup):
-    """The same layer with the rows beyond the Switch forward switched on: the
-    router z-loss, routing groups of 64 tokens (capacity per group), and top-2
-    choices in groups of 2048 tokens.  Each variant: warm-up, then `steps`
-    timed steps between events on the launch stream."""
-    out = {}
-    variants = [
-        ("z_loss", dict(k=1, group=0, z=True)),
-        ("groups_of_64", dict(k=1, group=64, z=False)),
-        ("top2_groups_of_2048", dict(k=2, group=2048, z=False)),
-        ("top2_one_group", dict(k=2, group=0, z=False)),
-    ]
-    for name, v in variants:
-        G = v["group"] or cfg.T
-        if cfg.T % G:
-            continue
-        C = sw.switch_capacity(v["k"] * G, cfg.E, cfg.c)
-        t = sw.layer_tensors(cfg.T, cfg.d, cfg.d_ff, cfg.E, C, dlogits=cfg.want_grad, z_loss=v["z"], k=v["k"],
-                             group=v["group"])
-        la = sw.make_layer_args(x, w_r, b_r, w1, w2, t, cfg.T, cfg.d, cfg.d_ff, cfg.E, C, cfg.alpha, residual=True,
-                                z_beta=1e-3 if v["z"] else 0.0, k=v["k"], group=v["group"])
-        for _ in range(warmup):
-            sw.switch_layer_fwd(la, t["ws"], stream)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a.record(stream)
-        for _ in range(steps):
-            sw.switch_layer_fwd(la, t["ws"], stream)
-        b.record(stream)
-        torch.cuda.synchronize()
-        ms = a.elapsed_time(b) / steps
-        keep = t["keep"].cpu().numpy()
-        out[name] = {"k": v["k"], "group": G, "C_per_group": C, "ms_per_step": ms,
-                     "tokens_per_s": cfg.T / (ms / 1000.0), "kept_choices": float(keep.mean())}
-        del t, la
-    out["backward"] = time_backward(sw, torch, cfg, x, w_r, b_r, w1, w2, stream, steps, warmup)
-    return out
-
-
-def time_backward(sw, torch, cfg, x, w_r, b_r, w1, w2, stream, steps, warmup):
-    """The layer backward (switch_layer_bwd) after a forward that keeps what it
-    needs (logits, hidden activations, dispatch buffer, expert outputs); a
-    step is one backward.  Per-kernel times from the library's events."""
-    T, d, F, E = cfg.T, cfg.d, cfg.d_ff, cfg.E
-    C = sw.switch_capacity(T, E, cfg.c)
-    t = sw.layer_tensors(T, d, F, E, C, for_backward=True)
-    la = sw.make_layer_args(x, w_r, b_r, w1, w2, t, T, d, F, E, C, cfg.alpha, residual=True)
-    sw.switch_layer_fwd(la, t["ws"], stream)
-    dout = torch.randn((T, d), device=x.device, generator=torch.Generator(device=x.device).manual_seed(7)).to(
-        torch.bfloat16)
-    g = sw.layer_bwd_tensors(T, d, F, E, C)
-    ba = sw.make_layer_bwd_args(t, x, w_r, w1, w2, dout, g, T, d, F, E, C, cfg.alpha)
-    for _ in range(warmup):
-        sw.switch_layer_bwd(ba, g["ws"], stream)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    a.record(stream)
-    for _ in range(steps):
-        sw.switch_layer_bwd(ba, g["ws"], stream)
-    b.record(stream)
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / steps
-    sw.switch_profile_enable(True)
-    for _ in range(steps):
-        sw.switch_layer_bwd(ba, g["ws"], stream)
-    torch.cuda.synchronize()
-    recs = sw.switch_profile_collect()
-    sw.switch_profile_enable(False)
-    per = {}
-    for name, kms in recs:
-        per[name] = per.get(name, 0.0) + kms
-    kern = {k: round(1000.0 * v / steps, 2) for k, v in sorted(per.items(), key=lambda kv: -kv[1])}
-    wbytes = 2 * E * F * d
-    return {"ms_per_step": ms, "tokens_per_s": T / (ms / 1000.0), "kernels_us_per_step": kern,
-            "weight_grad_bytes_fp32": 2 * wbytes}
-
-
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -195,141 +548,98 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, max(1, args.steps))
         return
+    if args.summarize_trace:
+        summarize_trace(args)
+        return
+    if args.summarize_counters:
+        summarize_counters(args)
+        return
 
     import torch
 
     import sparse_mixture_experts_order_amd as sw
     import workloads
 
-    cfg = workloads.CONFIGS[args.config]
-    inp = workloads.make_layer_inputs(cfg)
-    dev = "cuda"
-    to_bf16 = lambda bits: torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
-    x, w1, w2 = to_bf16(inp.x_bits), to_bf16(inp.w1_bits), to_bf16(inp.w2_bits)
-    w_r, b_r = torch.from_numpy(inp.w_r).to(dev), torch.from_numpy(inp.b_r).to(dev)
-    C = sw.switch_capacity(cfg.T, cfg.E, cfg.c)
-    t = sw.layer_tensors(cfg.T, cfg.d, cfg.d_ff, cfg.E, C, device=dev, dlogits=cfg.want_grad)
-    la = sw.make_layer_args(x, w_r, b_r, w1, w2, t, cfg.T, cfg.d, cfg.d_ff, cfg.E, C, cfg.alpha, residual=True)
     stream = torch.cuda.current_stream()
+    cfg = workloads.CONFIGS[args.config]
+    log(f"inputs {cfg.name}")
+    inp, dev = device_inputs(cfg, torch)
 
-    def step():
-        sw.switch_layer_fwd(la, t["ws"], stream)
+    if args.standalone:
+        res, t, C, A = measure_layer(sw, torch, cfg, dev, stream, 2, 1, cold=False)
+        st = measure_standalone(sw, torch, cfg, dev, t, C, A, stream, args.steps, args.warmup)
+        print(json.dumps(st))
+        return
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # timed region: K whole-layer steps, events on the launch stream
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    stop.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_total = start.elapsed_time(stop)
-    ms_per_step = ms_total / args.steps
-
-    # per-kernel durations: the same K steps again with an event pair around
-    # every launch (recorded on the launch stream by the library)
-    sw.switch_profile_enable(True)
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    recs = sw.switch_profile_collect()
-    sw.switch_profile_enable(False)
-    per = {}
-    for name, ms in recs:
-        per.setdefault(name, []).append(ms)
-    kern_us = {k: 1000.0 * float(np.mean(v)) for k, v in per.items()}
-
-    accepted = t["accepted"].cpu().numpy().astype(np.int64)
-    A = int(accepted.sum())
-    T, d, F, E = cfg.T, cfg.d, cfg.d_ff, cfg.E
-    # algorithmic bytes and flops per launch (padding rows excluded).  Without a
-    # combine launch the second GEMM wrote the kept tokens' output rows itself
-    # (residual row read, bf16 row written, slot_token and gate read) and the
-    # gather copied the dropped tokens' residual rows.
-    fused = "combine" not in kern_us
-    w_bytes = 2 * E * F * d
-    alg = {
-        "expert_gemm1": dict(bytes=w_bytes + 2 * A * d + 2 * A * F, flops=2 * A * d * F),
-        "expert_gemm2": dict(bytes=w_bytes + 2 * A * F + (4 * A * d + 8 * A if fused else 4 * A * d),
-                             flops=2 * A * d * F),
-        "gather": dict(bytes=2 * A * d + 2 * E * C * d + 9 * T + 8 * E + 4 * E * C + (4 * (T - A) * d if fused else 0),
-                       flops=0),
-        "combine": dict(bytes=4 * A * d + 2 * T * d + 2 * T * d + 13 * T, flops=0),
-        "router_gemm": dict(bytes=2 * T * d + 6 * d * E + 4 * T * E, flops=2 * T * d * E),
-        "router_fused": dict(bytes=2 * T * d + 6 * d * E + 12 * T + 4 * E * ((T + 63) // 64), flops=2 * T * d * E),
-    }
-    dominant = max((k for k in kern_us if k in alg), key=lambda k: kern_us[k])
-    dur_s = kern_us[dominant] * 1e-6
-    achieved = alg[dominant]["bytes"] / dur_s / 1e9
-    ffn_us = kern_us.get("expert_gemm1", 0) + kern_us.get("expert_gemm2", 0)
-    ffn_flops = 4 * A * d * F
-    ffn_bytes = alg["expert_gemm1"]["bytes"] + alg["expert_gemm2"]["bytes"]
-    dispatch_us = sum(kern_us.get(k, 0) for k in ("scan_local", "scan_offsets", "gather"))
-    traffic = read_traffic(dominant, cfg.name)
+    log("layer")
+    main_res, t, C, A = measure_layer(sw, torch, cfg, dev, stream, args.steps, args.warmup,
+                                      cold=not args.only_layer)
+    if args.only_layer:
+        print(json.dumps(main_res))
+        return
+    log("standalone dispatch / combine")
+    main_res.update(measure_standalone(sw, torch, cfg, dev, t, C, A, stream, min(args.steps, 20),
+                                       min(args.warmup, 5)))
+    del t
 
     result = {
         "metric": METRIC,
-        "value": cfg.T * args.steps / (ms_total / 1000.0),
+        "value": main_res["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": main_res["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded: x ~ N(0,1) in bf16, router N(0, 0.1/d) fp32, experts truncated normal "
                 "0.1/sqrt(fan_in) in bf16)",
-        "config": {"workload": cfg.name, "T": T, "d_model": d, "d_ff": F, "E": E, "capacity_factor": cfg.c,
-                   "C": C, "alpha": cfg.alpha, "aux_grad": bool(cfg.want_grad), "parallelism": "none (1 GPU)"},
-        "roofline": {
-            "kernel": dominant,
-            "bound": "hbm",
-            "achieved": achieved,
-            "peak": PEAK_HBM_GBPS,
-            "unit": "GB/s",
-            "frac": achieved / PEAK_HBM_GBPS,
-            "traffic": traffic,
-            "algorithmic_bytes": alg[dominant]["bytes"],
-            "avg_launch_us": kern_us[dominant],
-        },
-        "ffn": {
-            "mfma_pct_of_bf16_peak": 100.0 * ffn_flops / (ffn_us * 1e-6) / (PEAK_BF16_TFLOPS * 1e12),
-            "hbm_GBps": ffn_bytes / (ffn_us * 1e-6) / 1e9,
-            "us": ffn_us,
-            "algorithmic_flops": ffn_flops,
-        },
-        "dispatch": {
-            "GBps": alg["gather"]["bytes"] / (dispatch_us * 1e-6) / 1e9 if dispatch_us else None,
-            "gather_GBps": alg["gather"]["bytes"] / (kern_us["gather"] * 1e-6) / 1e9,
-            "us": dispatch_us,
-        },
-        "combine": ({"fused": True, "into": "expert_gemm2 epilogue"} if fused else
-                    {"fused": False, "GBps": alg["combine"]["bytes"] / (kern_us["combine"] * 1e-6) / 1e9}),
-        "kernels_us": {k: round(v, 2) for k, v in sorted(kern_us.items(), key=lambda kv: -kv[1])},
-        "routing": {"accepted": A, "drop_rate": 1 - A / T,
-                    "empty_slot_ratio": 1 - A / (E * C) if C else None},
-        "wall_s_timed": wall,
+        "config": {"workload": cfg.name, "T": cfg.T, "d_model": cfg.d, "d_ff": cfg.d_ff, "E": cfg.E,
+                   "capacity_factor": cfg.c, "C": C, "alpha": cfg.alpha, "aux_grad": bool(cfg.want_grad),
+                   "parallelism": "none (1 GPU)"},
+        "roofline": main_res.pop("roofline"),
+        "ffn": main_res["ffn"],
+        "dispatch": main_res["dispatch"],
+        "combine": main_res["combine"],
+        "layer": main_res,
     }
 
     if not args.no_variants:
-        result["variants"] = time_variants(sw, torch, cfg, x, w_r, b_r, w1, w2, stream, min(args.steps, 20),
-                                           min(args.warmup, 5))
+        log("variants")
+        result["variants"] = time_variants(sw, torch, cfg, dev, stream, min(args.steps, 20), min(args.warmup, 5))
+    log("mfma ceiling")
+    result["measured_ceilings"] = {"bf16_gemm": mfma_ceiling(torch, stream)}
 
     if not args.no_cpu_baseline:
+        log("cpu baseline")
         rate, dt, threads, n = cpu_baseline(inp, cfg, args.cpu_sample_tokens)
+        model, blas = host_description()
         result["cpu_baseline"] = {
             "value": rate, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"whole fp64 oracle layer on {n} of {cfg.T} tokens, best of 3 ({dt:.1f} s each, "
-                      f"{platform.processor() or platform.machine()})",
+            "sample": f"whole fp64 oracle layer on {n} of {cfg.T} tokens, best of 3 ({dt:.2f} s each)",
+            "cpu": model, "blas": blas,
         }
+    del dev, inp
+    torch.cuda.empty_cache()
+
+    if not args.no_per_config:
+        per = {}
+        for ci in [int(c) for c in args.per_config.split(",") if c.strip()]:
+            if ci == args.config:
+                continue
+            c2 = workloads.CONFIGS[ci]
+            log(f"per-config inputs {c2.name}")
+            _, dv = device_inputs(c2, torch)
+            log(f"per-config layer {c2.name}")
+            r, tt, Cc, Ac = measure_layer(sw, torch, c2, dv, stream, min(args.steps, 20), min(args.warmup, 5))
+            r.update(measure_standalone(sw, torch, c2, dv, tt, Cc, Ac, stream, min(args.steps, 20),
+                                        min(args.warmup, 5)))
+            per[c2.name] = r
+            del tt, dv
+            torch.cuda.empty_cache()
+        result["per_config"] = per
     print(json.dumps(result))
 
 

