@@ -136,6 +136,25 @@ switch_status switch_dispatch(const switch_bf16 *x, const int32_t *expert, int64
                               int32_t *counts, int32_t *accepted, int32_t *slot_token,
                               switch_bf16 *buf, void *ws, size_t ws_bytes, void *stream);
 
+/* switch_dispatch for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments and results, without a workspace.  Its scratch (the
+ * per-tile expert counts of the slot scan, ceil(T / 256) * E * 4 bytes) is a
+ * fixed device array inside the library, one per GPU, of
+ * switch_dispatch_noalloc_max_scratch_bytes() = 4 MiB, held until the
+ * process ends; larger T * E return SWITCH_E_UNSUPPORTED with nothing
+ * enqueued.  The call makes no hipMalloc/hipFree or other allocating call.
+ * Every entry of the scratch is written before it is read, so nothing in it
+ * must start at zero; all calls on one GPU share it, so calls that overlap on
+ * one GPU (other streams, other host threads) race and must be serialised by
+ * the caller.  The first call on a device looks up that device's scratch
+ * address (hipGetSymbolAddress) on the current device. */
+size_t switch_dispatch_noalloc_max_scratch_bytes(void);
+switch_status switch_dispatch_noalloc(const switch_bf16 *x, const int32_t *expert, int64_t T, int32_t d,
+                                      int32_t E, int32_t C, int32_t *position, uint8_t *keep,
+                                      int32_t *counts, int32_t *accepted, int32_t *slot_token,
+                                      switch_bf16 *buf, void *stream);
+
 /* The experts: per expert e and row s < accepted[e],
  *   y[e, s] = ReLU(buf[e, s] W1_e^T) W2_e^T
  * Sources: dmxsf.com essay, "core structure" (experts replace the FFN

@@ -28,7 +28,8 @@ EXPORTS = [
     "switch_profile_collect", "switch_kernel_name", "switch_router_z_loss",
     "switch_route_ex", "switch_dispatch_ex", "switch_dispatch_workspace_bytes_ex", "switch_combine_ex",
     "switch_aux_loss_ex", "switch_workspace_bytes_ex", "switch_layer_bwd", "switch_layer_bwd_workspace_bytes",
-    "switch_layer_bwd_workspace_bytes_ex", "switch_build_source_hash",
+    "switch_layer_bwd_workspace_bytes_ex", "switch_build_source_hash", "switch_dispatch_noalloc",
+    "switch_dispatch_noalloc_max_scratch_bytes",
 ]
 
 
@@ -136,6 +137,8 @@ def lib():
             "switch_layer_bwd_workspace_bytes_ex": (SZ, [I64, I32, I32, I32, I32, I32, I64]),
             "switch_layer_bwd": (I32, [ctypes.POINTER(LayerBwdArgs), P, SZ, P]),
             "switch_build_source_hash": (ctypes.c_char_p, []),
+            "switch_dispatch_noalloc": (I32, [P, P, I64, I32, I32, I32, P, P, P, P, P, P, P]),
+            "switch_dispatch_noalloc_max_scratch_bytes": (SZ, []),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -223,6 +226,16 @@ def switch_dispatch(x, expert, T, d, E, C, position, keep, counts, accepted, slo
     _check(lib().switch_dispatch(_ptr(x), _ptr(expert), T, d, E, C, _ptr(position), _ptr(keep), _ptr(counts),
                                  _ptr(accepted), _ptr(slot_token), _ptr(buf), wp, wn, _stream(stream)),
            "switch_dispatch")
+
+
+def switch_dispatch_noalloc(x, expert, T, d, E, C, position, keep, counts, accepted, slot_token, buf, stream=None):
+    _check(lib().switch_dispatch_noalloc(_ptr(x), _ptr(expert), T, d, E, C, _ptr(position), _ptr(keep),
+                                         _ptr(counts), _ptr(accepted), _ptr(slot_token), _ptr(buf), _stream(stream)),
+           "switch_dispatch_noalloc")
+
+
+def switch_dispatch_noalloc_max_scratch_bytes():
+    return lib().switch_dispatch_noalloc_max_scratch_bytes()
 
 
 def switch_expert_ffn(buf, accepted, w1, w2, E, C, d, d_ff, y, ws, stream=None):

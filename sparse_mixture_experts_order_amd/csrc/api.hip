@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -447,6 +448,40 @@ hipError_t launch_stream_copy(void* dst, const void* src, size_t nbytes, hipStre
 }
 }  // namespace swmoe
 
+// ------------------------------------------------ allocation-free dispatch
+// The scratch of switch_dispatch_noalloc: the per-tile expert counts of the
+// slot scan (ceil(T / 256) * E int32).  A file-scope device array, so a call
+// allocates nothing; each GPU the library runs on holds its own copy until the
+// process ends.  In host code `scratch` names a host-side stand-in, never the
+// device memory: the device address comes from hipGetSymbolAddress, once per
+// device, and only that address is passed to kernels.
+constexpr size_t kNoAllocScratchBytes = size_t(4) << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of this device's scratch (looked up on the device's first call).
+switch_status scratch_address(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(SWITCH_E_UNSUPPORTED, "device index %d >= %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p || !aligned(p, kAlign)) return fail(SWITCH_E_HIP, "scratch has no aligned device address");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return SWITCH_OK;
+}
+}  // namespace
+
 // =================================================================== C ABI
 extern "C" {
 
@@ -780,6 +815,28 @@ switch_status switch_dispatch(const switch_bf16* x, const int32_t* expert, int64
     g_err.clear();
     DispatchArgs a{x, expert, T, d, E, C, position, keep, counts, accepted, slot_token, buf};
     CHECK(validate_dispatch(a, ws, ws_bytes));
+    return run_dispatch(a, ws, (hipStream_t)stream);
+}
+
+size_t switch_dispatch_noalloc_max_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+switch_status switch_dispatch_noalloc(const switch_bf16* x, const int32_t* expert, int64_t T, int32_t d, int32_t E,
+                                      int32_t C, int32_t* position, uint8_t* keep, int32_t* counts,
+                                      int32_t* accepted, int32_t* slot_token, switch_bf16* buf, void* stream) {
+    g_err.clear();
+    DispatchArgs a{x, expert, T, d, E, C, position, keep, counts, accepted, slot_token, buf};
+    CHECK(check_TE(T, E));
+    const size_t need = dispatch_ws(T, E, 1, 0);
+    if (need > kNoAllocScratchBytes)
+        return fail(SWITCH_E_UNSUPPORTED,
+                    "switch_dispatch_noalloc: T = %lld, E = %d need %zu scratch bytes, above its fixed %zu "
+                    "(ceil(T / 256) * E * 4 must be <= %zu); use switch_dispatch with a workspace",
+                    (long long)T, E, need, kNoAllocScratchBytes, kNoAllocScratchBytes);
+    // the same checks as switch_dispatch, with the scratch as the workspace (an
+    // aligned stand-in address: only its size and alignment are looked at)
+    CHECK(validate_dispatch(a, reinterpret_cast<void*>(kAlign), kNoAllocScratchBytes));
+    void* ws = nullptr;
+    CHECK(scratch_address(&ws));
     return run_dispatch(a, ws, (hipStream_t)stream);
 }
 

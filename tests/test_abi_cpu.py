@@ -43,6 +43,18 @@ def test_library_is_built_from_the_current_sources(tmp_path):
     assert sw.library_hash(str(none)) is None and not sw.library_current(str(none))
 
 
+def test_noalloc_dispatch_validates_before_any_hip_call():
+    """The allocation-free dispatch checks its arguments and its fixed scratch
+    size on the host: these return an error with nothing enqueued."""
+    L = sw.lib()
+    none = [None] * 6
+    # 1024 tiles x 4096 experts: 16 MiB of counts
+    assert L.switch_dispatch_noalloc(None, None, 1 << 18, 64, 4096, 1, *none, None) == sw.SWITCH_E_UNSUPPORTED
+    assert b"scratch" in L.switch_last_error()
+    assert L.switch_dispatch_noalloc(None, None, 100, 64, 4, 10, *none, None) == sw.SWITCH_E_INVALID
+    assert L.switch_dispatch_noalloc(None, None, 100, 64, 0, 10, *none, None) == sw.SWITCH_E_INVALID
+
+
 def test_capacity_matches_oracle():
     cases = [(512, 4, 1.25), (16384, 128, 1.0), (16384, 64, 2.0), (32768, 128, 1.25), (65536, 2048, 1.0),
              (64, 4, 1.25), (100, 10, 1.0), (30, 3, 0.1), (0, 5, 3.0), (7, 7, 0.0), (1, 4096, 1e-300),
