@@ -216,16 +216,16 @@ switch_status run_route(const RouteArgs& a, void* ws, hipStream_t s) {
     const float* logits = a.logits_in;
     if (!logits) {
         bf16_t* wr3 = c.take<bf16_t>((size_t)3 * a.d * E);
-        LAUNCH(K_SPLIT, "split_router_weights", s, launch_split_router_weights(a.w_r, wr3, a.d, E, s));
-        if (route_fused(E)) {
+        if (route_fused(E)) {   // splits W_r into its bf16 terms itself
             float* part = c.take<float>(route_parts(T, E));
             const int nblk = T > 0 ? router_fused_blocks(T) : 0;
             if (T > 0)
                 LAUNCH(K_RFUSED, "router_fused", s,
-                       launch_router_fused(a.x, wr3, a.b_r, T, a.d, E, a.k, a.logits_out, a.expert, a.gate, a.lse,
+                       launch_router_fused(a.x, a.w_r, a.b_r, T, a.d, E, a.k, a.logits_out, a.expert, a.gate, a.lse,
                                            part, s));
             return finish_route(a, part, one ? nblk : rows_per_group, ng, s);
         }
+        LAUNCH(K_SPLIT, "split_router_weights", s, launch_split_router_weights(a.w_r, wr3, a.d, E, s));
         float* z = a.logits_out ? a.logits_out : c.take<float>((size_t)T * E);
         if (T > 0) LAUNCH(K_RGEMM, "router_gemm", s, launch_router_gemm(a.x, wr3, a.b_r, z, T, a.d, E, s));
         logits = z;

@@ -108,6 +108,47 @@ __device__ __forceinline__ float row16_sum(float v) {
     return v;
 }
 
+// Largest value with the lowest index on ties over each row of 16 lanes, every
+// lane of the row getting the result: the same four DPP partners as
+// row16_sum.  The selection is a total order on (value desc, index asc), so
+// any pairing gives the same result.
+__device__ __forceinline__ void row16_argmax(float& v, int& i) {
+#define SWMOE_ARGMAX_DPP(ctrl)                                                                                   \
+    {                                                                                                           \
+        const float ov = __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), ctrl, 0xF, 0xF, false)); \
+        const int oi = __builtin_amdgcn_update_dpp(0, i, ctrl, 0xF, 0xF, false);                                 \
+        const bool take = (ov > v) | ((ov == v) & (oi < i));                                                    \
+        v = take ? ov : v;                                                                                      \
+        i = take ? oi : i;                                                                                      \
+    }
+    SWMOE_ARGMAX_DPP(0xB1)
+    SWMOE_ARGMAX_DPP(0x4E)
+    SWMOE_ARGMAX_DPP(0x141)
+    SWMOE_ARGMAX_DPP(0x140)
+#undef SWMOE_ARGMAX_DPP
+}
+
+// wave_sum and wave_argmax without the LDS path: rows of 16 by DPP, then the
+// row swaps (lane ^ 16, lane ^ 32).  Every lane gets the result.
+__device__ __forceinline__ float wave_sum_valu(float v) {
+    v = row16_sum(v);
+    v += lane_xor16(v);
+    v += lane_xor32(v);
+    return v;
+}
+
+__device__ __forceinline__ void wave_argmax_valu(float& v, int& i) {
+    row16_argmax(v, i);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const float ov = h ? lane_xor32(v) : lane_xor16(v);
+        const int oi = h ? lane_xor32(i) : lane_xor16(i);
+        const bool take = (ov > v) | ((ov == v) & (oi < i));
+        v = take ? ov : v;
+        i = take ? oi : i;
+    }
+}
+
 // row16_sum on each element of an array, one step over all elements before
 // the next (the same additions; independent instructions between dependent
 // DPP moves instead of wait states)
@@ -276,6 +317,63 @@ constexpr int kCached = 0, kStream = 2;
 
 // One 1 KiB copy: lane i's 16 bytes land at dst + 16 i.  (The LDS address
 // space exists only in the device pass.)
+// The two LDS byte addresses of a kmajor_fragment (rows k and k + 4).
+__device__ __forceinline__ void kmajor_addr(const char* st, int rbw, int k, int col, uint32_t& a1, uint32_t& a2) {
+    const int slot = col >> 3, half = (col >> 2) & 1;
+    const int k2 = k + 4;
+    const char* p1 = st + k * rbw + ((slot ^ (2 * (k & 3))) << 4) + half * 8;
+    const char* p2 = st + k2 * rbw + ((slot ^ (2 * (k2 & 3))) << 4) + half * 8;
+    a1 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p1;
+    a2 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p2;
+}
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// N transposed 64-bit LDS reads (N = 2, 4 or 8: one, two or four K-major
+// fragments) written out in asm, and their wait in the same block, so every
+// output is complete when the block ends.  The compiler's wait insertion
+// cannot tell a ds_read_b64_tr_b16 of the stage being read from the direct
+// copies still in flight into the other stages, and so waits for all of them
+// before the first such read; reads it does not see cost no such wait (the
+// pipeline's own wait and barrier already order them after their copies).
+// Outputs are early-clobber: a read's data may land before a later read of
+// the block has taken its address.
+template <int N>
+__device__ __forceinline__ void lds_read_tr_batch(const uint32_t (&a)[N], u32x2 (&r)[N]) {
+    static_assert(N == 2 || N == 4 || N == 8, "two, four or eight reads");
+#if defined(__HIP_DEVICE_COMPILE__)
+    if constexpr (N == 2) {
+        asm volatile("ds_read_b64_tr_b16 %0, %2\n\tds_read_b64_tr_b16 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                     : "=&v"(r[0]), "=&v"(r[1])
+                     : "v"(a[0]), "v"(a[1])
+                     : "memory");
+    } else if constexpr (N == 4) {
+        asm volatile("ds_read_b64_tr_b16 %0, %4\n\tds_read_b64_tr_b16 %1, %5\n\t"
+                     "ds_read_b64_tr_b16 %2, %6\n\tds_read_b64_tr_b16 %3, %7\n\ts_waitcnt lgkmcnt(0)"
+                     : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+                     : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+                     : "memory");
+    } else {
+        asm volatile("ds_read_b64_tr_b16 %0, %8\n\tds_read_b64_tr_b16 %1, %9\n\t"
+                     "ds_read_b64_tr_b16 %2, %10\n\tds_read_b64_tr_b16 %3, %11\n\t"
+                     "ds_read_b64_tr_b16 %4, %12\n\tds_read_b64_tr_b16 %5, %13\n\t"
+                     "ds_read_b64_tr_b16 %6, %14\n\tds_read_b64_tr_b16 %7, %15\n\ts_waitcnt lgkmcnt(0)"
+                     : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
+                       "=&v"(r[7])
+                     : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+                     : "memory");
+    }
+#else
+    for (int i = 0; i < N; ++i) r[i] = u32x2{a[i], 0u};
+#endif
+}
+
+// Fragment f of a batch: its rows k (read 2 f) and k + 4 (read 2 f + 1).
+template <int N>
+__device__ __forceinline__ bf16x8 batch_fragment(const u32x2 (&r)[N], int f) {
+    return as_bf16x8(u32x4{r[2 * f].x, r[2 * f].y, r[2 * f + 1].x, r[2 * f + 1].y});
+}
+
 template <int AUX = kCached>
 __device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t rs, char* dst, uint32_t voff, uint32_t soff) {
 #if defined(__HIP_DEVICE_COMPILE__)

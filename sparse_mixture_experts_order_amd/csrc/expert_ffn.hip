@@ -895,25 +895,48 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
 #pragma unroll
                 for (int s = 0; s < KC / 16; ++s) {
                     const int c = half * (KC / 16) + s;
+                    const int m = lane & 15;
                     bf16x8 bt[TOKB];
+                    if constexpr (AKM) {   // rows k = 8 c .. 8 c + 7 of token column tb * 32 + (l & 31)
+                        // two fragments per asm batch (fewer addresses live at once)
+                        static_assert(TOKB % 2 == 0, "token fragments in pairs");
 #pragma unroll
-                    for (int tb = 0; tb < TOKB; ++tb) {
-                        if constexpr (AKM) {   // rows k = 8 c .. 8 c + 7 of token column tb * 32 + (l & 31)
-                            const int m = lane & 15;
-                            bt[tb] = kmajor_fragment(sa, RBA, 8 * c + (m >> 2), tb * 32 + 16 * ((lane >> 4) & 1) + 4 * (m & 3));
-                        } else {
+                        for (int tp = 0; tp < TOKB; tp += 2) {
+                            uint32_t ta[4];
+                            u32x2 tr[4];
+#pragma unroll
+                            for (int q = 0; q < 2; ++q)
+                                kmajor_addr(sa, RBA, 8 * c + (m >> 2),
+                                            (tp + q) * 32 + 16 * ((lane >> 4) & 1) + 4 * (m & 3), ta[2 * q],
+                                            ta[2 * q + 1]);
+                            lds_read_tr_batch(ta, tr);
+                            bt[tp] = batch_fragment(tr, 0);
+                            bt[tp + 1] = batch_fragment(tr, 1);
+                        }
+                    } else {
+#pragma unroll
+                        for (int tb = 0; tb < TOKB; ++tb) {
                             const int r = tb * 32 + l32;
                             bt[tb] = as_bf16x8(*(const u32x4*)(sa + r * RB + (dma_slot<KC>(r, c) << 4)));
                         }
+                    }
+                    // K-major weights: rows k = 8 c .. 8 c + 7 of columns wave * 32 NBW + 32 nb + (l & 31)
+                    u32x2 wtr[WKM ? 2 * NBW : 2];
+                    if constexpr (WKM) {
+                        static_assert(NBW == 1 || NBW == 2, "one or two K-major weight fragments per asm batch");
+                        uint32_t wad[2 * NBW];
+#pragma unroll
+                        for (int nb = 0; nb < NBW; ++nb)
+                            kmajor_addr(sw, RBW, 8 * c + (m >> 2),
+                                        wave * 32 * NBW + nb * 32 + 16 * ((lane >> 4) & 1) + 4 * (m & 3), wad[2 * nb],
+                                        wad[2 * nb + 1]);
+                        lds_read_tr_batch(wad, wtr);
                     }
 #pragma unroll
                     for (int nb = 0; nb < NBW; ++nb) {
                         bf16x8 wa;
                         if constexpr (WKM) {
-                            // rows k = 8 c .. 8 c + 7 of columns wave * 32 NBW + 32 nb + (l & 31)
-                            const int m = lane & 15;
-                            const int col = wave * 32 * NBW + nb * 32 + 16 * ((lane >> 4) & 1) + 4 * (m & 3);
-                            wa = kmajor_fragment(sw, RBW, 8 * c + (m >> 2), col);
+                            wa = batch_fragment(wtr, nb);
                         } else {
                             const int r = wave * 32 * NBW + nb * 32 + l32;
                             wa = as_bf16x8(*(const u32x4*)(sw + r * RB + (dma_slot<KC>(r, c) << 4)));

@@ -24,8 +24,8 @@ int column_sum_slices(int64_t rows);
 hipError_t launch_column_sum(const float* a, int rows, int E, float* slices, float* out, hipStream_t s);
 constexpr int kRouterFusedMaxE = 256;
 int router_fused_blocks(int64_t T);     // one partial row per 64 tokens
-// wr3 in the layout [d / 32][3][E][32] of split_router_weights
-hipError_t launch_router_fused(const bf16_t* x, const bf16_t* wr3, const float* b_r, int T, int d, int E, int k,
+// E <= kRouterFusedMaxE; w_r as stored, [d, E] fp32 (split into bf16 terms inside)
+hipError_t launch_router_fused(const bf16_t* x, const float* w_r, const float* b_r, int T, int d, int E, int k,
                                float* logits_out, int32_t* expert, float* gate, float* lse, float* part,
                                hipStream_t s);
 

@@ -264,7 +264,7 @@ __global__ __launch_bounds__(256) void router_softmax(const float* __restrict__ 
 // experts 4 j + 256 i .. + 3 (one 16-byte load each), and a wave loads the
 // row of its next token while it works on the current one.  e^x is rf_exp,
 // as in the fused router.
-template <int NC4, int KMAX>
+template <int NC4, int KMAX, int R = 2>
 __global__ __launch_bounds__(256) void router_softmax4(const float* __restrict__ logits, int T, int E, int k,
                                                        int tpb, int32_t* __restrict__ expert,
                                                        float* __restrict__ gate, float* __restrict__ lse,
@@ -304,7 +304,7 @@ __global__ __launch_bounds__(256) void router_softmax4(const float* __restrict__
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 if (cur[i][j] > m) { m = cur[i][j]; mi = 4 * lane + 256 * i + j; }   // strict: lowest index per lane
-        wave_argmax(m, mi);
+        wave_argmax_valu(m, mi);
         float p[NC4][4];
         float sum = 0.f;
 #pragma unroll
@@ -314,7 +314,7 @@ __global__ __launch_bounds__(256) void router_softmax4(const float* __restrict__
                 p[i][j] = (4 * lane + 256 * i + j < E) ? rf_exp(cur[i][j] - m) : 0.f;
                 sum += p[i][j];
             }
-        sum = wave_sum(sum);
+        sum = wave_sum_valu(sum);
         const float inv = 1.0f / sum;
 #pragma unroll
         for (int i = 0; i < NC4; ++i)
@@ -344,7 +344,7 @@ __global__ __launch_bounds__(256) void router_softmax4(const float* __restrict__
                         for (int q = 0; q < r; ++q) taken |= e == ch[q];
                         if (!taken && cur[i][j] > mr) { mr = cur[i][j]; ir = e; }
                     }
-                wave_argmax(mr, ir);
+                wave_argmax_valu(mr, ir);
                 ch[r] = ir;
                 if (lane == 0) {
                     expert[(size_t)t * k + r] = ir;
@@ -353,15 +353,20 @@ __global__ __launch_bounds__(256) void router_softmax4(const float* __restrict__
             }
         }
     };
-    f32x4 ra[NC4], rb[NC4];
+    // a ring of R row buffers: while a row is processed the next R - 1 rows of
+    // the wave are in flight (rows past the slice repeat its last row, unused);
+    // the loop is unrolled by R so every buffer index is a constant
+    f32x4 ring[R][NC4];
     const int tw = t0 + wave;
     if (tw < t1) {
-        load(tw, ra);
-        for (int t = tw; t < t1; t += 8) {
-            load(min(t + 4, t1 - 1), rb);
-            process(t, ra);
-            load(min(t + 8, t1 - 1), ra);
-            if (t + 4 < t1) process(t + 4, rb);
+#pragma unroll
+        for (int i = 0; i < R - 1; ++i) load(min(tw + 4 * i, t1 - 1), ring[i]);
+        for (int t = tw; t < t1; t += 4 * R) {
+#pragma unroll
+            for (int u = 0; u < R; ++u) {
+                load(min(t + 4 * (u + R - 1), t1 - 1), ring[(u + R - 1) % R]);
+                if (t + 4 * u < t1) process(t + 4 * u, ring[u]);
+            }
         }
     }
     for (int w = 0; w < 4; ++w) {
@@ -440,6 +445,9 @@ int router_softmax_blocks(int64_t T, int E) {
 
 int router_softmax_blocks_grouped(int64_t T) { return (int)((T + 63) / 64); }
 
+// row buffers per wave of router_softmax4
+constexpr int kSoftmaxRing = 2;
+
 template <int KMAX>
 static void softmax_by_width(int nblk, int tpb, const float* logits, int T, int E, int k, int32_t* expert,
                              float* gate, float* lse, float* part, hipStream_t s) {
@@ -447,8 +455,8 @@ static void softmax_by_width(int nblk, int tpb, const float* logits, int T, int 
     if (E % 4 == 0 && (uintptr_t)logits % 16 == 0) {   // 16-byte rows
         const int nc4 = (E + 255) / 256;
 #define SWMOE_SOFTMAX4(N)                                                                                  \
-    hipLaunchKernelGGL((router_softmax4<N, KMAX>), dim3(nblk), dim3(256), shm, s, logits, T, E, k, tpb, expert, \
-                       gate, lse, part)
+    hipLaunchKernelGGL((router_softmax4<N, KMAX, kSoftmaxRing>), dim3(nblk), dim3(256), shm, s, logits, T, E, k, \
+                       tpb, expert, gate, lse, part)
         if (nc4 <= 1) SWMOE_SOFTMAX4(1);
         else if (nc4 <= 2) SWMOE_SOFTMAX4(2);
         else if (nc4 <= 4) SWMOE_SOFTMAX4(4);
@@ -517,10 +525,16 @@ hipError_t launch_column_sum(const float* a, int rows, int E, float* slices, flo
 //    16-byte columns of a row XOR-swizzled by (row >> 1) & 3 so that the
 //    fragment reads are free of bank conflicts; token rows past T read as
 //    zero through the descriptor's byte count;
-//  - each wave loads its own weight fragments (hi, mid, lo terms of its
-//    expert blocks; the split weights are stored one K stage per block,
-//    [d / 32][3][E][32]) from memory straight into a register ring; rows
-//    past E repeat row E - 1 (they only feed outputs that are never used).
+//  - each wave loads the fp32 router weights of its own fragments from W_r
+//    as stored ([d, E]: for lane (r16, g) of an expert block, the 8 values
+//    k = 8 g .. 8 g + 7 of expert r16, 8 dword loads whose lanes read 64
+//    contiguous bytes per k row) from memory straight into a register ring,
+//    and splits them into their hi, mid and lo bf16 terms right before the
+//    MFMAs (the hardware's round-to-nearest-even conversion, two values per
+//    instruction; the same exact split as split_router_weights, so no split
+//    pass runs and each weight crosses the caches as 4 bytes, not 6);
+//    experts past E repeat expert E - 1 (they only feed outputs that are
+//    never used).
 // Both run S - 1 stages ahead of the MFMAs, with one workgroup barrier per
 // stage.  After the last stage the logits go through an LDS tile, and wave w
 // finishes tokens 16 w .. 16 w + 15: bias, row max with the lowest index on
@@ -537,7 +551,7 @@ int router_fused_blocks(int64_t T) { return (int)((T + RF_TOK - 1) / RF_TOK); }
 
 
 template <int EB, int S, int KMAX, bool FULL>
-__global__ __launch_bounds__(256) void router_fused(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wr3,
+__global__ __launch_bounds__(256) void router_fused(const bf16_t* __restrict__ x, const float* __restrict__ w_r,
                                                     const float* __restrict__ b_r, int T, int d, int E, int k,
                                                     float* __restrict__ logits_out, int32_t* __restrict__ expert,
                                                     float* __restrict__ gate, float* __restrict__ lse,
@@ -547,8 +561,8 @@ __global__ __launch_bounds__(256) void router_fused(const bf16_t* __restrict__ x
     constexpr int WE = EB < 4 ? EB : 4;         // waves across expert blocks
     constexpr int WT = 4 / WE;                  // waves across the four token blocks
     constexpr int EBW = EB / WE, TBW = 4 / WT;  // blocks per wave
-    constexpr int NWF = 3 * EBW;                // weight fragments per wave per stage
-    constexpr int PER_STAGE = 1 + NWF;          // loads per wave per stage
+    constexpr int NWL = 8 * EBW;                // fp32 weight loads per wave per stage (8 k per fragment)
+    constexpr int PER_STAGE = 1 + NWL;          // loads per wave per stage
     constexpr int LROW = EP + 4;                // floats per token row of the logit tile
     constexpr int TILE = RF_TOK * LROW * 4;
     constexpr int LDS_BYTES = S * STAGE > TILE ? S * STAGE : TILE;
@@ -578,25 +592,25 @@ __global__ __launch_bounds__(256) void router_fused(const bf16_t* __restrict__ x
     const uint32_t x_bytes = (uint32_t)ntok * d * 2;
     const int xr = wave * 16 + (lane >> 2);
     const uint32_t xvo = (uint32_t)(xr * d * 2 + (((lane & 3) ^ ((xr >> 1) & 3)) << 4));
-    // weight fragment (term, eb): row r16 of expert block we * EBW + eb, 16-byte group g
-    const uint32_t w_bytes = (uint32_t)3 * E * d * 2;
-    const uint32_t w_stage = (uint32_t)3 * E * 64;        // bytes of one K stage of the split weights
+    // weight fragment eb: expert (we * EBW + eb) * 16 + r16, rows k = 32 kk + 8 g + j of W_r
+    const uint32_t w_bytes = (uint32_t)d * E * 4;
+    const uint32_t w_stage = (uint32_t)RF_KC * E * 4;     // bytes of one K stage of W_r
     uint32_t wvo[EBW];
 #pragma unroll
     for (int eb = 0; eb < EBW; ++eb) {
         const int e = min((we * EBW + eb) * 16 + r16, E - 1);
-        wvo[eb] = (uint32_t)(e * 64 + g * 16);
+        wvo[eb] = (uint32_t)((8 * g * E + e) * 4);
     }
-    u32x4 wreg[S][NWF];
-    auto issue = [&](int kk, int stg, u32x4 (&wr)[NWF]) {
+    float wreg[S][NWL];
+    auto issue = [&](int kk, int stg, float (&wr)[NWL]) {
         kk = min(kk, nk - 1);
         copy_to_lds(buffer_rsrc(xw, x_bytes), lds + stg * STAGE + wave * 1024, xvo, kk * 64);
 #pragma unroll
-        for (int term = 0; term < 3; ++term)
+        for (int eb = 0; eb < EBW; ++eb)
 #pragma unroll
-            for (int eb = 0; eb < EBW; ++eb)
-                wr[term * EBW + eb] = __builtin_amdgcn_raw_buffer_load_b128(
-                    buffer_rsrc(wr3, w_bytes), wvo[eb] + (uint32_t)term * E * 64, kk * w_stage, 0);
+            for (int j = 0; j < 8; ++j)
+                wr[eb * 8 + j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                    buffer_rsrc(w_r, w_bytes), wvo[eb] + (uint32_t)j * E * 4, kk * w_stage, 0));
         // loads stay in step order (the waits count whole steps): neither the
         // optimizer nor the scheduler may move them past this point
         asm volatile("" ::: "memory");
@@ -631,13 +645,22 @@ __global__ __launch_bounds__(256) void router_fused(const bf16_t* __restrict__ x
                     const int r = (wt * TBW + tb) * 16 + r16;
                     xb[tb] = as_bf16x8(*(const u32x4*)(sb + r * 64 + ((g ^ ((r >> 1) & 3)) << 4)));
                 }
-                // small terms first: lo (2), mid (1), hi (0)
+                // the three bf16 terms of each fragment, then the MFMAs with the
+                // small terms first: lo, mid, hi
+                uint32_t t3[3][EBW][4];
+#pragma unroll
+                for (int eb = 0; eb < EBW; ++eb)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        split3_bf16x2(wreg[u][eb * 8 + 2 * j], wreg[u][eb * 8 + 2 * j + 1], t3[0][eb][j], t3[1][eb][j],
+                                      t3[2][eb][j]);
 #pragma unroll
                 for (int jj = 0; jj < 3; ++jj) {
                     const int term = 2 - jj;
 #pragma unroll
                     for (int eb = 0; eb < EBW; ++eb) {
-                        const bf16x8 a = as_bf16x8(wreg[u][term * EBW + eb]);
+                        const bf16x8 a = as_bf16x8(
+                            u32x4{t3[term][eb][0], t3[term][eb][1], t3[term][eb][2], t3[term][eb][3]});
 #pragma unroll
                         for (int tb = 0; tb < TBW; ++tb)
                             acc[tb][eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xb[tb], acc[tb][eb], 0, 0, 0);
@@ -774,31 +797,31 @@ __global__ __launch_bounds__(256) void router_fused(const bf16_t* __restrict__ x
 }
 
 template <int KMAX>
-static void fused_by_width(const bf16_t* x, const bf16_t* wr3, const float* b_r, int T, int d, int E, int k,
+static void fused_by_width(const bf16_t* x, const float* w_r, const float* b_r, int T, int d, int E, int k,
                            float* logits_out, int32_t* expert, float* gate, float* lse, float* part, hipStream_t s) {
 #define SWMOE_RF(EB, S)                                                                                         \
     do {                                                                                                        \
         if (E == 16 * (EB))                                                                                     \
             hipLaunchKernelGGL((router_fused<EB, S, KMAX, true>), dim3(router_fused_blocks(T)), dim3(256), 0, s, x, \
-                               wr3, b_r, T, d, E, k, logits_out, expert, gate, lse, part);                      \
+                               w_r, b_r, T, d, E, k, logits_out, expert, gate, lse, part);                      \
         else                                                                                                    \
             hipLaunchKernelGGL((router_fused<EB, S, KMAX, false>), dim3(router_fused_blocks(T)), dim3(256), 0, s,  \
-                               x, wr3, b_r, T, d, E, k, logits_out, expert, gate, lse, part);                   \
+                               x, w_r, b_r, T, d, E, k, logits_out, expert, gate, lse, part);                   \
     } while (0)
     if (E <= 16) SWMOE_RF(1, 4);
     else if (E <= 32) SWMOE_RF(2, 4);
     else if (E <= 64) SWMOE_RF(4, 4);
     else if (E <= 128) SWMOE_RF(8, 3);
-    else SWMOE_RF(16, 3);
+    else SWMOE_RF(16, 2);   // 32 weight loads per wave per stage: one stage ahead
 #undef SWMOE_RF
 }
 
-hipError_t launch_router_fused(const bf16_t* x, const bf16_t* wr3, const float* b_r, int T, int d, int E, int k,
+hipError_t launch_router_fused(const bf16_t* x, const float* w_r, const float* b_r, int T, int d, int E, int k,
                                float* logits_out, int32_t* expert, float* gate, float* lse, float* part,
                                hipStream_t s) {
-    if (k <= 1) fused_by_width<1>(x, wr3, b_r, T, d, E, k, logits_out, expert, gate, lse, part, s);
-    else if (k <= 2) fused_by_width<2>(x, wr3, b_r, T, d, E, k, logits_out, expert, gate, lse, part, s);
-    else fused_by_width<kMaxTopK>(x, wr3, b_r, T, d, E, k, logits_out, expert, gate, lse, part, s);
+    if (k <= 1) fused_by_width<1>(x, w_r, b_r, T, d, E, k, logits_out, expert, gate, lse, part, s);
+    else if (k <= 2) fused_by_width<2>(x, w_r, b_r, T, d, E, k, logits_out, expert, gate, lse, part, s);
+    else fused_by_width<kMaxTopK>(x, w_r, b_r, T, d, E, k, logits_out, expert, gate, lse, part, s);
     return hipGetLastError();
 }
 
