@@ -160,9 +160,11 @@ def read_traffic(kernel: str, workload: str):
 def kernel_role(name: str) -> str:
     import re
     n = name.strip().strip('"')
-    m = re.search(r"(?:swmoe::)?(\w+)<([^>(]*)", n)
-    base = m.group(1) if m else re.sub(r"\(.*", "", n).split("::")[-1].strip()
-    args = [a.strip() for a in m.group(2).split(",")] if m else []
+    head = n.split("(", 1)[0]                      # the name with its template arguments, no parameters
+    head = re.sub(r"^(void|static|__global__)\s+", "", head).strip()
+    m = re.match(r"(?:\w+::)*(\w+)(?:<(.*))?$", head)
+    base = m.group(1) if m else head
+    args = [a.strip() for a in m.group(2).rstrip(">").split(",")] if m and m.group(2) else []
     if base in ("expert_gemm_dma", "expert_gemm"):
         mode = args[3] if base == "expert_gemm_dma" else (args[4] if len(args) > 4 else "")
         return {"0": "expert_gemm1", "1": "expert_gemm2", "3": "expert_gemm2", "2": "gemm_masked"}.get(mode, base)
