@@ -59,6 +59,8 @@ def parse():
                    help="only run the plain copy kernel on BYTES bytes (hardware-counter calibration)")
     p.add_argument("--standalone", action="store_true",
                    help="only time the standalone dispatch and combine entry points (profiler runs)")
+    p.add_argument("--only-backward", action="store_true",
+                   help="only time the layer backward of the main configuration (profiler runs)")
     p.add_argument("--summarize-trace", metavar="DIR",
                    help="write a kernel-time summary of a rocprofv3 --kernel-trace --stats output directory")
     p.add_argument("--summarize-counters", metavar="DIR", nargs="+",
@@ -131,12 +133,27 @@ def kernel_bytes(T, d, F, E, C, A, fused, gathered):
 
 
 # ------------------------------------------------------------ counter summaries
+# The sources of the expert GEMM kernels (the dominant ones): a counter summary
+# carries their hash, and its traffic figures stand only while it matches.
+GEMM_SOURCES = ["sparse_mixture_experts_order_amd/csrc/expert_ffn.hip",
+                "sparse_mixture_experts_order_amd/csrc/common.hpp",
+                "sparse_mixture_experts_order_amd/csrc/kernels.hpp"]
+
+
+def gemm_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        h.update(f.encode() + b"\0")
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
 def read_traffic(kernel: str, workload: str):
     """HBM bytes per launch of `kernel` (FETCH_SIZE + WRITE_SIZE, each scaled by
     the same counter's reading on a plain copy of known size) from the committed
     counter summary, or None when the summary is missing or was taken on other
-    library sources."""
-    from sparse_mixture_experts_order_amd.build import source_hash
+    expert-GEMM sources."""
     path = os.path.join(PROFILES, f"traffic_{workload}.txt")
     if not os.path.exists(path):
         return None
@@ -145,7 +162,7 @@ def read_traffic(kernel: str, workload: str):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("library_source_hash") != source_hash():
+    if vals.get("gemm_source_sha256_16") != gemm_source_hash():
         return None
     f, w = vals.get(f"{kernel}_fetch_bytes_per_launch"), vals.get(f"{kernel}_write_bytes_per_launch")
     return float(f) + float(w) if f and w else None
@@ -167,6 +184,12 @@ def kernel_role(name: str) -> str:
     args = [a.strip() for a in m.group(2).rstrip(">").split(",")] if m and m.group(2) else []
     if base in ("expert_gemm_dma", "expert_gemm"):
         mode = args[3] if base == "expert_gemm_dma" else (args[4] if len(args) > 4 else "")
+        wkm = base == "expert_gemm_dma" and len(args) > 6 and args[6] == "true"
+        akm = base == "expert_gemm_dma" and len(args) > 7 and args[7] == "true"
+        if akm:   # the backward's weight gradients: both operands K-major; named by tile width
+            return f"gemm_dW_{int(args[2]) * 32 * int(args[1])}cols"
+        if wkm:   # the backward's products with W1 and W2 as stored
+            return {"2": "gemm_dA", "1": "gemm_dbuf"}.get(mode, base)
         return {"0": "expert_gemm1", "1": "expert_gemm2", "3": "expert_gemm2", "2": "gemm_masked"}.get(mode, base)
     if base.startswith("router_softmax"):
         return "router_softmax"
@@ -209,21 +232,25 @@ def summarize_trace(args):
 
 
 def _counter_means(directory: str):
-    """{role: {counter: mean value per dispatch}} from a --pmc run."""
-    acc = {}
+    """{role: {counter: mean value per dispatch}} from a --pmc run, plus the
+    mean dispatch duration in ns under the counter run ("duration_ns")."""
+    acc, dur = {}, {}
     for r in _csv_rows(directory, "counter_collection.csv"):
         role = kernel_role(r["Kernel_Name"])
+        did = r.get("Dispatch_Id", "")
         key = (role, r["Counter_Name"])
-        acc.setdefault(key, {}).setdefault(r.get("Dispatch_Id", len(acc)), 0.0)
-        acc[key][r.get("Dispatch_Id", len(acc))] += float(r["Counter_Value"])
+        acc.setdefault(key, {}).setdefault(did, 0.0)
+        acc[key][did] += float(r["Counter_Value"])
+        dur.setdefault(role, {})[did] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
     out = {}
     for (role, cn), disp in acc.items():
         out.setdefault(role, {})[cn] = float(np.mean(list(disp.values())))
+    for role, d in dur.items():
+        out[role]["duration_ns"] = float(np.mean(list(d.values())))
     return out
 
 
 def summarize_counters(args):
-    from sparse_mixture_experts_order_amd.build import source_hash
     means = {}
     for dr in args.summarize_counters:
         for role, cs in _counter_means(dr).items():
@@ -237,16 +264,22 @@ def summarize_counters(args):
                         scale[cn] = args.copy_bytes / (v * 1024.0)
     lines = [f"# per-dispatch hardware counters, workload {args.workload} (one MI355X)",
              f"# command: {args.command}",
-             f"# library_source_hash below: the sources the counters were taken on"]
+             "# gemm_source_sha256_16: hash of the expert GEMM sources the counters were taken on "
+             f"({', '.join(GEMM_SOURCES)})"]
     if scale:
         lines.append(f"# FETCH_SIZE / WRITE_SIZE (KiB) scaled by their reading on the library's plain copy kernel "
                      f"of {args.copy_bytes} bytes")
-    lines.append(f"library_source_hash: {source_hash()}")
+    lines.append(f"gemm_source_sha256_16: {gemm_source_hash()}")
     for cn, v in sorted(scale.items()):
         lines.append(f"{cn.lower()}_scale: {v:.4f}")
     for role, cs in sorted(means.items()):
         for cn, v in sorted(cs.items()):
             lines.append(f"{role}_{cn}: {v:.1f}")
+        if cs.get("SQ_VALU_MFMA_BUSY_CYCLES", 0) > 0 and cs.get("duration_ns"):
+            # busy cycles summed over the 1024 SIMDs, against the dispatch's own
+            # duration in the counter run at the 2.4 GHz peak clock
+            pct = 100.0 * cs["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * cs["duration_ns"] * 2.4)
+            lines.append(f"{role}_mfma_busy_pct_of_duration: {pct:.1f}")
         if "FETCH_SIZE" in cs and "FETCH_SIZE" in scale:
             lines.append(f"{role}_fetch_bytes_per_launch: {cs['FETCH_SIZE'] * 1024 * scale['FETCH_SIZE']:.0f}")
         if "WRITE_SIZE" in cs and "WRITE_SIZE" in scale:
@@ -571,6 +604,9 @@ def main():
         res, t, C, A = measure_layer(sw, torch, cfg, dev, stream, 2, 1, cold=False)
         st = measure_standalone(sw, torch, cfg, dev, t, C, A, stream, args.steps, args.warmup)
         print(json.dumps(st))
+        return
+    if args.only_backward:
+        print(json.dumps(time_backward(sw, torch, cfg, dev, stream, args.steps, args.warmup)))
         return
 
     log("layer")
