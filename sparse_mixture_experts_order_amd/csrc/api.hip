@@ -329,8 +329,8 @@ switch_status validate_ffn(const FfnArgs& a, const void* ws, size_t ws_bytes) {
         if (a.a_rows) NONNULL(a.x_src); else NONNULL(a.buf);
         if (!a.cb) NONNULL(a.y);
     }
-    REQUIRE(!a.a_rows || ffn_wide_tiles(a.C), "gathered token rows need more than 64 buffer rows per expert");
-    REQUIRE(!a.cb || ffn_wide_tiles(a.C), "the fused combine needs more than 64 buffer rows per expert");
+    REQUIRE(!a.a_rows || ffn_rows_fused(a.C), "gathered token rows need at least one buffer row per expert");
+    REQUIRE(!a.cb || ffn_rows_fused(a.C), "the fused combine needs at least one buffer row per expert");
     ALIGNED16(a.buf); ALIGNED16(a.w1); ALIGNED16(a.w2); ALIGNED16(a.y); ALIGNED4(a.accepted); ALIGNED16(a.h);
     const size_t need = ffn_ws(a.E, a.C, a.d_ff);
     if (ws_bytes < need) return fail(SWITCH_E_WORKSPACE, "expert_ffn needs %zu workspace bytes, got %zu", need, ws_bytes);
@@ -949,7 +949,7 @@ switch_status switch_layer_fwd(const switch_layer_args* la, void* ws, size_t ws_
     // k = 1 with 128-row token tiles: the second GEMM writes the kept tokens'
     // output rows (and y only when asked for), gather the dropped ones, and
     // there is no combine pass
-    const bool fused = k == 1 && L.T > 0 && ffn_wide_tiles(rows);
+    const bool fused = k == 1 && L.T > 0 && ffn_rows_fused(rows);
     const FfnCombine cb{slot_token, L.gate, L.residual ? L.x : nullptr, L.out, L.y};
     if (fused) {
         da.out_pass = L.out;
@@ -967,7 +967,7 @@ switch_status switch_layer_fwd(const switch_layer_args* la, void* ws, size_t ws_
     }
     // buf and slot_token not kept: the first GEMM reads the token rows from x
     // through the (padded) workspace slot_token
-    if (!L.buf && !L.slot_token && L.T > 0 && ffn_wide_tiles(rows) && L.T * L.d * 2 + 2 * (int64_t)L.d + 256 < (int64_t(1) << 32)) {
+    if (!L.buf && !L.slot_token && L.T > 0 && ffn_rows_fused(rows) && L.T * L.d * 2 + 2 * (int64_t)L.d + 256 < (int64_t(1) << 32)) {
         da.no_buf = true;
         fa.x_src = L.x;
         fa.x_tokens = L.T;

@@ -1082,17 +1082,58 @@ static int dma_tile_width(int E, int C, int N, bool narrow = false) {
     return best;
 }
 
+// The direct-to-LDS kernel with 32- or 64-row token tiles (C <= 64: the
+// forward's expert GEMMs, whose weight stream bounds them at these sizes), the
+// column width chosen as for 128-row tiles.
+template <int TOKB, int MODE>
+static hipError_t launch_expert_gemm_dma_small(const bf16_t* A, const bf16_t* W, const int32_t* pre,
+                                               const int4* ttab, void* out, const bf16_t* mask, int E, int C, int K,
+                                               int N, hipStream_t s, const FfnCombine& cb, const int32_t* a_rows,
+                                               uint32_t a_bytes) {
+    if constexpr (MODE == OUT_COMBINE) {   // one 32-row block per wave, as with 128-row tiles
+        if (dma_tile_width(E, C, N, true) == 256)
+            return launch_expert_gemm_dma_t<TOKB, 1, 8, MODE, 3, 64>(A, W, pre, ttab, out, mask, cb, E, C, K, N, s,
+                                                                     a_rows, a_bytes);
+        return launch_expert_gemm_dma_t<TOKB, 1, 6, MODE, 3, 64>(A, W, pre, ttab, out, mask, cb, E, C, K, N, s, a_rows,
+                                                                 a_bytes);
+    } else {
+        switch (dma_tile_width(E, C, N)) {
+            case 512:
+                return launch_expert_gemm_dma_t<TOKB, 2, 8, MODE, 2, 64>(A, W, pre, ttab, out, mask, cb, E, C, K, N, s,
+                                                                         a_rows, a_bytes);
+            case 384:
+                return launch_expert_gemm_dma_t<TOKB, 2, 6, MODE, 2, 64>(A, W, pre, ttab, out, mask, cb, E, C, K, N, s,
+                                                                         a_rows, a_bytes);
+            case 256:
+                return launch_expert_gemm_dma_t<TOKB, 1, 8, MODE, 3, 64>(A, W, pre, ttab, out, mask, cb, E, C, K, N, s,
+                                                                         a_rows, a_bytes);
+            default:
+                return launch_expert_gemm_dma_t<TOKB, 1, 6, MODE, 3, 64>(A, W, pre, ttab, out, mask, cb, E, C, K, N, s,
+                                                                         a_rows, a_bytes);
+        }
+    }
+}
+
+// forward: the forward's expert GEMMs, which take the direct-to-LDS kernel at
+// every C (gathered token rows and the fused combine need it); otherwise
+// C <= 64 keeps the register kernel (the backward's small products).
 template <int MODE>
 static hipError_t launch_expert_gemm(const bf16_t* A, const bf16_t* W, const int32_t* pre, const int4* ttab, void* out,
                                      const bf16_t* mask, int E, int C, int K, int N, hipStream_t s,
                                      const FfnCombine& cb = FfnCombine{}, const int32_t* a_rows = nullptr,
-                                     uint32_t a_bytes = 0) {
+                                     uint32_t a_bytes = 0, bool forward = false) {
+    // the token tile must be ffn_token_tile(C) rows: the prefix kernel lists tiles of that size
+    if (C <= 64 && forward) {
+        if (C <= 32)
+            return launch_expert_gemm_dma_small<1, MODE>(A, W, pre, ttab, out, mask, E, C, K, N, s, cb, a_rows,
+                                                         a_bytes);
+        return launch_expert_gemm_dma_small<2, MODE>(A, W, pre, ttab, out, mask, E, C, K, N, s, cb, a_rows, a_bytes);
+    }
     // a_rows (token rows gathered from x) needs the direct-to-LDS kernel
     if (a_rows && C <= 64) return hipErrorInvalidValue;
-    // the token tile must be ffn_token_tile(C) rows: the prefix kernel lists tiles of that size
     if constexpr (MODE == OUT_COMBINE) {
         // one 32-row block per wave: the epilogue's residual runs fit in registers
-        if (C <= 64) return hipErrorInvalidValue;   // the fused combine needs 128-row token tiles
+        if (C <= 64) return hipErrorInvalidValue;   // the fused combine needs the direct-to-LDS kernel
         if (dma_tile_width(E, C, N, true) == 256)
             return launch_expert_gemm_dma_t<4, 1, 8, MODE, 3, 64>(A, W, pre, ttab, out, mask, cb, E, C, K, N, s, a_rows, a_bytes);
         return launch_expert_gemm_dma_t<4, 1, 6, MODE, 3, 64>(A, W, pre, ttab, out, mask, cb, E, C, K, N, s, a_rows, a_bytes);
@@ -1158,28 +1199,30 @@ static hipError_t launch_expert_gemm_kmajor(const bf16_t* A, const bf16_t* W, co
 
 hipError_t launch_expert_gemm1(const bf16_t* buf, const bf16_t* w1, const int32_t* pre, const int4* ttab, bf16_t* h,
                                int E, int C, int d, int d_ff, hipStream_t s) {
-    return launch_expert_gemm<OUT_RELU_BF16>(buf, w1, pre, ttab, h, nullptr, E, C, d, d_ff, s);
+    return launch_expert_gemm<OUT_RELU_BF16>(buf, w1, pre, ttab, h, nullptr, E, C, d, d_ff, s, FfnCombine{}, nullptr,
+                                             0, true);
 }
 
 hipError_t launch_expert_gemm1_gather(const bf16_t* x, int64_t T, const int32_t* slot_token, const bf16_t* w1,
                                       const int32_t* pre, const int4* ttab, bf16_t* h, int E, int C, int d, int d_ff,
                                       hipStream_t s) {
-    if (!ffn_wide_tiles(C) || T * d * 2 + 2 * (int64_t)d + 256 >= (int64_t(1) << 32)) return hipErrorInvalidValue;
+    if (!ffn_rows_fused(C) || T * d * 2 + 2 * (int64_t)d + 256 >= (int64_t(1) << 32)) return hipErrorInvalidValue;
     return launch_expert_gemm<OUT_RELU_BF16>(x, w1, pre, ttab, h, nullptr, E, C, d, d_ff, s, FfnCombine{}, slot_token,
-                                             (uint32_t)(T * d * 2));
+                                             (uint32_t)(T * d * 2), true);
 }
 
 hipError_t launch_expert_gemm2(const bf16_t* h, const bf16_t* w2, const int32_t* pre, const int4* ttab, float* y,
                                int E, int C, int d, int d_ff, hipStream_t s) {
-    return launch_expert_gemm<OUT_F32>(h, w2, pre, ttab, y, nullptr, E, C, d_ff, d, s);
+    return launch_expert_gemm<OUT_F32>(h, w2, pre, ttab, y, nullptr, E, C, d_ff, d, s, FfnCombine{}, nullptr, 0, true);
 }
 
 bool ffn_wide_tiles(int C) { return C > 64; }
+bool ffn_rows_fused(int C) { return C >= 1; }
 
 hipError_t launch_expert_gemm2_combine(const bf16_t* h, const bf16_t* w2, const int32_t* pre, const int4* ttab,
                                        const FfnCombine& cb, int E, int C, int d, int d_ff, hipStream_t s) {
-    if (!ffn_wide_tiles(C)) return hipErrorInvalidValue;
-    return launch_expert_gemm<OUT_COMBINE>(h, w2, pre, ttab, nullptr, nullptr, E, C, d_ff, d, s, cb);
+    if (!ffn_rows_fused(C)) return hipErrorInvalidValue;
+    return launch_expert_gemm<OUT_COMBINE>(h, w2, pre, ttab, nullptr, nullptr, E, C, d_ff, d, s, cb, nullptr, 0, true);
 }
 
 hipError_t launch_grouped_gemm_kmajor_f32(const bf16_t* A, const bf16_t* W, const int32_t* pre, const int4* ttab,

@@ -68,7 +68,7 @@ hipError_t launch_expert_gemm2(const bf16_t* h, const bf16_t* w2, const int32_t*
 // s of expert e holds token slot_token[e * C + s], and
 //   out[token] = bf16(residual[token] + gate[token] * y[e, s])
 // (fp32, one rounding; no residual when it is NULL), plus y itself when y is
-// not NULL.  Only for 128-row token tiles (ffn_wide_tiles).
+// not NULL.  Any C >= 1 (ffn_rows_fused).
 struct FfnCombine {
     const int32_t* slot_token;
     const float* gate;
@@ -76,13 +76,16 @@ struct FfnCombine {
     bf16_t* out;
     float* y;
 };
-// 128-row token tiles (C > 64: the direct-to-LDS kernel), which the fused
-// combine and the gathered token rows need
+// 128-row token tiles (C > 64: the direct-to-LDS kernel for every product,
+// the backward's included)
 bool ffn_wide_tiles(int C);
+// the forward's expert GEMMs run the direct-to-LDS kernel at every C >= 1 (32-,
+// 64- or 128-row token tiles), so they can gather token rows and fuse the combine
+bool ffn_rows_fused(int C);
 constexpr int kRowMapPad = 128;
 // The first expert GEMM reading its token rows straight from x [T, d]: buffer
 // row s of expert e is x[slot_token[e * C + s]] (no buf array).  Needs
-// ffn_wide_tiles(C), T * d * 2 well below 2^32, and kRowMapPad readable
+// ffn_rows_fused(C), T * d * 2 well below 2^32, and kRowMapPad readable
 // entries past slot_token[E * C - 1].
 hipError_t launch_expert_gemm1_gather(const bf16_t* x, int64_t T, const int32_t* slot_token, const bf16_t* w1,
                                       const int32_t* pre, const int4* ttab, bf16_t* h, int E, int C, int d, int d_ff,

@@ -416,7 +416,8 @@ def check_small_layer(D, t, residual=True):
     (777, 64, 128, 1, 1.0, 0.0),       # one expert: the dense FFN
     (333, 192, 320, 7, 7.0, 0.0),      # c >= E: nothing dropped
     (600, 64, 128, 6, 1.0, 3.0),       # hot expert 0, several empty experts
-    (5000, 128, 256, 300, 1.0, 0.0),   # many experts, C = 17
+    (5000, 128, 256, 300, 1.0, 0.0),   # many experts, C = 17: 32-row token tiles
+    (3000, 128, 192, 64, 1.3, 0.0),    # C = 61: 64-row token tiles
     (2000, 64, 128, 16, 4.5, 0.0),     # C = 563 > 512: three 256-row tiles
 ])
 def test_edge_shapes(shape):
