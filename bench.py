@@ -350,7 +350,7 @@ def cold_times(torch, stream, fn, steps):
 
 
 # ------------------------------------------------------------ one configuration
-def measure_layer(sw, torch, cfg, dev, stream, steps, warmup, cold=True):
+def measure_layer(sw, torch, cfg, dev, stream, steps, warmup, cold=True, library=True):
     """The timed layer (no intermediates kept: the first expert GEMM gathers
     its rows from x, the second writes the combine when k = 1 and C > 64)."""
     T, d, F, E = cfg.T, cfg.d, cfg.d_ff, cfg.E
@@ -415,6 +415,10 @@ def measure_layer(sw, torch, cfg, dev, stream, steps, warmup, cold=True):
     }
     if dominant == "expert_gemm2":
         res["roofline"]["achieved_with_h_read"] = kb["expert_gemm2_with_h"] / (mean_us[dominant] * 1e-6) / 1e9
+    lib = library_grouped_gemms(torch, stream, cfg, C) if library else None
+    if lib:
+        lib["layer_gemms_us"] = ffn_us
+        res["ffn"]["library_bmm_padded"] = lib
     if cold:
         med, mn = cold_times(torch, stream, step, min(steps, 20))
         res["cold"] = {"ms_per_step_median": med, "ms_per_step_min": mn, "tokens_per_s": T / (med / 1e3),
@@ -534,6 +538,31 @@ def mfma_ceiling(torch, stream):
             "frac_of_spec_peak": 2 * n ** 3 / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
 
+def library_grouped_gemms(torch, stream, cfg, C, steps=10, warmup=3):
+    """The two expert GEMMs of a configuration as the vendor BLAS runs them:
+    torch.bmm over the capacity-padded [E, C, d] x [E, d, d_ff] and
+    [E, C, d_ff] x [E, d_ff, d] products (bf16, contiguous operands), run only.
+    The vendor BLAS's rate on these shapes, beside the layer's own GEMMs."""
+    E, d, F = cfg.E, cfg.d, cfg.d_ff
+    if C <= 0:
+        return None
+    g = torch.Generator("cuda").manual_seed(5)
+    a1 = torch.randn((E, C, d), device="cuda", generator=g).to(torch.bfloat16)
+    b1 = torch.randn((E, d, F), device="cuda", generator=g).to(torch.bfloat16)
+    h = torch.empty((E, C, F), device="cuda", dtype=torch.bfloat16)
+    ms1 = timed_loop(torch, stream, lambda: torch.bmm(a1, b1, out=h), steps, warmup)
+    del a1, b1
+    b2 = torch.randn((E, F, d), device="cuda", generator=g).to(torch.bfloat16)
+    y = torch.empty((E, C, d), device="cuda", dtype=torch.bfloat16)
+    ms2 = timed_loop(torch, stream, lambda: torch.bmm(h, b2, out=y), steps, warmup)
+    del b2, h, y
+    torch.cuda.empty_cache()
+    flops = 2 * E * C * d * F
+    return {"shapes": f"torch.bmm [{E}, {C}, {d}] x [{E}, {d}, {F}] and [{E}, {C}, {F}] x [{E}, {F}, {d}], bf16",
+            "gemm1_us": ms1 * 1e3, "gemm2_us": ms2 * 1e3, "us": (ms1 + ms2) * 1e3,
+            "TFLOPs_padded": 2 * flops / ((ms1 + ms2) * 1e-3) / 1e12}
+
+
 # ------------------------------------------------------------ CPU baseline
 def host_description():
     model = platform.processor() or platform.machine()
@@ -601,7 +630,7 @@ def main():
     inp, dev = device_inputs(cfg, torch)
 
     if args.standalone:
-        res, t, C, A = measure_layer(sw, torch, cfg, dev, stream, 2, 1, cold=False)
+        res, t, C, A = measure_layer(sw, torch, cfg, dev, stream, 2, 1, cold=False, library=False)
         st = measure_standalone(sw, torch, cfg, dev, t, C, A, stream, args.steps, args.warmup)
         print(json.dumps(st))
         return
@@ -611,7 +640,7 @@ def main():
 
     log("layer")
     main_res, t, C, A = measure_layer(sw, torch, cfg, dev, stream, args.steps, args.warmup,
-                                      cold=not args.only_layer)
+                                      cold=not args.only_layer, library=not args.only_layer)
     if args.only_layer:
         print(json.dumps(main_res))
         return

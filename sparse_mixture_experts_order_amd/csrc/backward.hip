@@ -107,7 +107,7 @@ __global__ __launch_bounds__(256) void transpose_rows(const bf16_t* __restrict__
 // rows 64 (w >> 1) and experts 64 (w & 1) as 2 x 2 blocks of 32 (A = x
 // columns, B = dz columns, K = tokens).  Per chunk of 64 tokens, x and the
 // three terms of dz are staged in LDS as K-major rows (token k: 128 bf16, the
-// 16-byte slot c at c ^ 2 (k & 3)) and the fragments (8 consecutive tokens
+// 16-byte slot c at c ^ kmajor_swz(256, k)) and the fragments (8 consecutive tokens
 // of one column) come from transposed reads.  The next chunk is loaded into
 // registers while the MFMAs run, through descriptors that end with the
 // chunk's last token of the slice (rows past it read as zero; the byte count,
@@ -157,7 +157,7 @@ __global__ __launch_bounds__(256) void router_wgrad(const bf16_t* __restrict__ x
         for (int jj = 0; jj < RW_PER; ++jj) {
             const int q = threadIdx.x + 256 * jj;
             const int r = q >> 4, c = q & 15;
-            const int at = r * RW_ROW + ((c ^ (2 * (r & 3))) << 4);
+            const int at = r * RW_ROW + ((c ^ kmajor_swz(RW_ROW, r)) << 4);
             *(u32x4*)(lds + at) = xr[jj];
             u32x4 hi, mid, lo;
 #pragma unroll
@@ -309,8 +309,8 @@ __global__ __launch_bounds__(256) void dx_assemble(const bf16_t* __restrict__ do
 // rounding of dx.  Per chunk of 32 experts the
 // workgroup's 128 W_r rows and 128 dz rows (128 bytes each) go from memory
 // straight into LDS, eight 1 KiB copies per wave with the lanes along the
-// expert axis (16-byte column c of row r at c ^ (r & 7), which keeps the
-// 32-row fragment reads free of bank conflicts); two stages, one barrier per
+// expert axis (16-byte column c of row r at c ^ ((r >> 1) & 7): any 16
+// consecutive rows of a fragment read on all 64 LDS banks); two stages, one barrier per
 // chunk; dz rows past T read as zero.  A chunk is two 16-expert MFMA steps
 // (v_mfma_f32_32x32x16_bf16): in step kq half wave h takes experts 16 kq +
 // 8 h .. + 7, two 16-byte columns of each of its rows, split in registers.
@@ -365,7 +365,7 @@ __global__ __launch_bounds__(256) void dx_assemble_mfma(const bf16_t* __restrict
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int row = 8 * ((8 * wave + i) & 15) + (lane >> 3);
-        vo[i] = (uint32_t)row * E * 4 + (((lane & 7) ^ (row & 7)) << 4);
+        vo[i] = (uint32_t)row * E * 4 + (((lane & 7) ^ ((row >> 1) & 7)) << 4);
     }
     auto issue = [&](int kc, int stg) {
         char* dst = lds + stg * DX_STAGE + wave * 8 * 1024;
@@ -412,10 +412,10 @@ __global__ __launch_bounds__(256) void dx_assemble_mfma(const bf16_t* __restrict
                 const int ra = (wave >> 1) * 64 + 32 * q + l32;   // W_r row in the tile
                 const int rb = (wave & 1) * 64 + 32 * q + l32;    // dz row in the tile
                 const int c0 = 4 * kq + 2 * h;
-                const f32x4 a0 = *(const f32x4*)(st + ra * 128 + ((c0 ^ (ra & 7)) << 4));
-                const f32x4 a1 = *(const f32x4*)(st + ra * 128 + (((c0 + 1) ^ (ra & 7)) << 4));
-                const f32x4 b0 = *(const f32x4*)(st + 128 * 128 + rb * 128 + ((c0 ^ (rb & 7)) << 4));
-                const f32x4 b1 = *(const f32x4*)(st + 128 * 128 + rb * 128 + (((c0 + 1) ^ (rb & 7)) << 4));
+                const f32x4 a0 = *(const f32x4*)(st + ra * 128 + ((c0 ^ ((ra >> 1) & 7)) << 4));
+                const f32x4 a1 = *(const f32x4*)(st + ra * 128 + (((c0 + 1) ^ ((ra >> 1) & 7)) << 4));
+                const f32x4 b0 = *(const f32x4*)(st + 128 * 128 + rb * 128 + ((c0 ^ ((rb >> 1) & 7)) << 4));
+                const f32x4 b1 = *(const f32x4*)(st + 128 * 128 + rb * 128 + (((c0 + 1) ^ ((rb >> 1) & 7)) << 4));
                 split2_bf16x8(a0, a1, ah[q], am[q]);
                 split2_bf16x8(b0, b1, bh[q], bm[q]);
             }

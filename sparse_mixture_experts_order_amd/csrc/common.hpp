@@ -285,19 +285,29 @@ __device__ __forceinline__ void wait_copies() {
     __builtin_amdgcn_s_waitcnt((N_OUTSTANDING & 15) | ((N_OUTSTANDING >> 4) << 14) | 0x0F70);
 }
 
+// The XOR applied to the 16-byte slots of row k of a K-major LDS stage with
+// rows of rbw bytes (a multiple of 128).  A half wave's transposed reads take
+// 4 consecutive rows x 4 consecutive slots (the first a multiple of 4); the
+// swizzle spreads those 16 pieces over all 64 four-byte banks: rows of a
+// multiple of 256 bytes take XOR 4 (k & 3) (within 16-slot groups); rows of
+// 256 m + 128 bytes already alternate between the two bank halves and take
+// XOR 4 ((k >> 1) & 1) (within 8-slot groups).
+__device__ __forceinline__ int kmajor_swz(int rbw, int k) {
+    return (rbw & 255) ? 4 * ((k >> 1) & 1) : 4 * (k & 3);
+}
+
 // An MFMA operand fragment (8 consecutive k of one column) from a K-major
 // LDS stage (rows k of rbw bytes, bf16), by two transposed reads
 // (ds_read_b64_tr_b16): this lane's piece is row k (the group's rows k0 +
 // lane / 4 of 16) and 4 elements from column col; the group's lanes get rows
 // k0 .. k0 + 3 (first read) and k0 + 4 .. k0 + 7 (second) of their own
-// column.  The 16-byte slot c of row k sits at c ^ 2 (k & 3), which puts a
-// group's 4 rows x 2 slots on 8 different slots (all 32 banks).
+// column.  The 16-byte slot c of row k sits at c ^ kmajor_swz(rbw, k).
 __device__ __forceinline__ bf16x8 kmajor_fragment(const char* st, int rbw, int k, int col) {
     typedef short v4s __attribute__((ext_vector_type(4)));
     const int slot = col >> 3, half = (col >> 2) & 1;
     const int k2 = k + 4;
-    const char* p1 = st + k * rbw + ((slot ^ (2 * (k & 3))) << 4) + half * 8;
-    const char* p2 = st + k2 * rbw + ((slot ^ (2 * (k2 & 3))) << 4) + half * 8;
+    const char* p1 = st + k * rbw + ((slot ^ kmajor_swz(rbw, k)) << 4) + half * 8;
+    const char* p2 = st + k2 * rbw + ((slot ^ kmajor_swz(rbw, k2)) << 4) + half * 8;
     v4s lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
 #if defined(__HIP_DEVICE_COMPILE__)
     lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p1);
@@ -321,8 +331,8 @@ constexpr int kCached = 0, kStream = 2;
 __device__ __forceinline__ void kmajor_addr(const char* st, int rbw, int k, int col, uint32_t& a1, uint32_t& a2) {
     const int slot = col >> 3, half = (col >> 2) & 1;
     const int k2 = k + 4;
-    const char* p1 = st + k * rbw + ((slot ^ (2 * (k & 3))) << 4) + half * 8;
-    const char* p2 = st + k2 * rbw + ((slot ^ (2 * (k2 & 3))) << 4) + half * 8;
+    const char* p1 = st + k * rbw + ((slot ^ kmajor_swz(rbw, k)) << 4) + half * 8;
+    const char* p2 = st + k2 * rbw + ((slot ^ kmajor_swz(rbw, k2)) << 4) + half * 8;
     a1 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p1;
     a2 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p2;
 }

@@ -657,9 +657,12 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm(const bf16_t* __restri
 // three chunks); the narrower chunk fits more stages, i.e. more bytes in
 // flight per CU, in the same LDS.  A copy instruction moves 1 KiB: 8 rows of
 // 128 bytes or 16 rows of 64 bytes.  Its lanes fetch 16-byte columns
-// XOR-swizzled by the row (column c of row r lands in slot c ^ (r & 7) of a
-// 128-byte row, c ^ ((r >> 1) & 3) of a 64-byte row), which keeps the MFMA
-// fragment reads (32 consecutive rows at one column) free of bank conflicts.
+// XOR-swizzled by the row (column c of row r lands in slot c ^ ((r >> 1) & 7)
+// of a 128-byte row, c ^ ((r >> 2) & 3) of a 64-byte row): a fragment read
+// (32 consecutive rows at one column) serves 16 lanes at a time, and the
+// swizzle puts any 16 consecutive rows on 16 different 16-byte bank groups,
+// all 64 four-byte banks of gfx950's LDS (the row-only swizzles c ^ (r & 7)
+// and c ^ ((r >> 1) & 3) cover 32 banks and halve the read rate).
 // Rows past a tile's valid tokens, or past N, read as zero through the
 // descriptors' byte counts.  One workgroup barrier per chunk: each wave waits
 // for its own copies of chunk p (vmcnt), the LDS-only barrier then publishes
@@ -669,7 +672,7 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm(const bf16_t* __restri
 // tile's output goes straight from the accumulators to memory.
 template <int KC>
 __device__ __forceinline__ int dma_slot(int r, int c) {
-    return KC == 64 ? (c ^ (r & 7)) : (c ^ ((r >> 1) & 3));
+    return KC == 64 ? (c ^ ((r >> 1) & 7)) : (c ^ ((r >> 2) & 3));
 }
 
 // With a_rows the token rows are gathered straight from A = x [T, K]: row s of
@@ -679,12 +682,11 @@ __device__ __forceinline__ int dma_slot(int r, int c) {
 // valid count point past the descriptor and read as zero.
 // With WKM the weights are stored K-major, [E, K, N] (the backward reads W1
 // and W2 as stored): a chunk's stage holds KC rows k of NWG weights each, the
-// 16-byte slot c of row k at c ^ 2 (k & 3), and an MFMA fragment (8
-// consecutive k of one weight row n per lane) is two ds_read_b64_tr_b16: in
-// each 16-lane group, lane 4 j + a reads 4 weights of row k0 + j at columns
-// n0 + 4 a .. + 3, and lane i gets the 4 rows k0 .. k0 + 3 of column n0 + i.
-// The swizzle puts the 4 rows x 2 slots of a group's read on 8 different slots
-// (all 32 banks).
+// 16-byte slot c of row k at c ^ kmajor_swz(row bytes, k), and an MFMA
+// fragment (8 consecutive k of one weight row n per lane) is two
+// ds_read_b64_tr_b16: in each 16-lane group, lane 4 j + a reads 4 weights of
+// row k0 + j at columns n0 + 4 a .. + 3, and lane i gets the 4 rows k0 .. k0 +
+// 3 of column n0 + i.
 template <int TOKB, int NBW, int WAVES, int MODE, int S, int KC, bool WKM = false, bool AKM = false,
           bool STREAM = false>
 __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __restrict__ A,   // [E, C, K], x or [E, K, C]
@@ -732,14 +734,14 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
     uint32_t wvo[WPW], avo[APW];
     constexpr int RBW = NWG * 2;                            // bytes per K-major stage row
     constexpr int RBA = TOK * 2;
-    static_assert(!WKM || (KC == 64 && (NWG / 8) % 8 == 0), "K-major stages: 64-wide chunks, whole slot groups");
-    static_assert(!AKM || (TOK / 8) % 8 == 0, "K-major token stages: whole slot groups");
+    static_assert(!WKM || (KC == 64 && RBW % 128 == 0), "K-major stages: 64-wide chunks, whole swizzle groups");
+    static_assert(!AKM || RBA % 128 == 0, "K-major token stages: whole swizzle groups");
 #pragma unroll
     for (int i = 0; i < WPW; ++i) {
         if constexpr (WKM) {
             const int lin = (wave * WPW + i) * 1024 + lane * 16;   // this lane's 16 bytes of the stage
             const int k = lin / RBW, slot = (lin - k * RBW) >> 4;
-            wvo[i] = (uint32_t)k * N * 2 + ((slot ^ (2 * (k & 3))) << 4);
+            wvo[i] = (uint32_t)k * N * 2 + ((slot ^ kmajor_swz(RBW, k)) << 4);
         } else {
             const int r = RPC * (wave * WPW + i) + lane / NCOL;
             wvo[i] = (uint32_t)r * K * 2 + (dma_slot<KC>(r, lane % NCOL) << 4);
@@ -751,7 +753,7 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
         if constexpr (AKM) {
             const int lin = (q < A_COPIES ? q : 0) * 1024 + lane * 16;   // spares copy the first bytes again
             const int k = lin / RBA, sl = (lin - k * RBA) >> 4;
-            avo[i] = (uint32_t)k * C * 2 + ((sl ^ (2 * (k & 3))) << 4);
+            avo[i] = (uint32_t)k * C * 2 + ((sl ^ kmajor_swz(RBA, k)) << 4);
         } else {
             const int r = RPC * (q < A_COPIES ? q : 0) + lane / NCOL;   // spares copy the first rows again
             avo[i] = (uint32_t)r * K * 2 + (dma_slot<KC>(r, lane % NCOL) << 4);

@@ -50,8 +50,8 @@ __global__ __launch_bounds__(256) void split_router_weights(const float* __restr
 // weight rows (64 bytes each; in the chunked split layout each term's rows of
 // one stage are one contiguous block) go from memory straight into LDS, eight
 // 1 KiB copies per wave (waves 0-1 the token rows, 2-7 the weight terms), the
-// four 16-byte columns of row r at column ^ ((r >> 1) & 3), which makes the
-// 32-row fragment reads free of bank conflicts.  Two stages, one barrier per
+// four 16-byte columns of row r at column ^ ((r >> 2) & 3), which puts any
+// 16 consecutive rows of a fragment read on all 64 LDS banks.  Two stages, one barrier per
 // stage.  Token rows past T read as zero; expert rows past E repeat row E - 1
 // and only reach logits that are never stored.  Tiles are numbered expert-tile-major and dealt XCD-major, so the
 // workgroups of an XCD share one expert tile's weight rows in its L2.
@@ -85,7 +85,7 @@ __global__ __launch_bounds__(512) void router_gemm(const bf16_t* __restrict__ x,
     for (int i = 0; i < 8; ++i) {
         const int q = 8 * wave + i;
         const int row = 16 * (q & 15) + (lane >> 2);
-        const uint32_t col = (uint32_t)(((lane & 3) ^ ((row >> 1) & 3)) << 4);
+        const uint32_t col = (uint32_t)(((lane & 3) ^ ((row >> 2) & 3)) << 4);
         const int term = (q >> 4) - 1;   // weight copies: q = 16 (1 + term) + row block
         vo[i] = tok_rows ? (uint32_t)row * d * 2 + col : (uint32_t)(term * E + min(e0 + row, E - 1)) * 64 + col;
     }
@@ -120,7 +120,7 @@ __global__ __launch_bounds__(512) void router_gemm(const bf16_t* __restrict__ x,
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) {
                 const int r = wt * 128 + tb * 32 + l32;
-                a[tb] = as_bf16x8(*(const u32x4*)(st + r * 64 + ((c ^ ((r >> 1) & 3)) << 4)));
+                a[tb] = as_bf16x8(*(const u32x4*)(st + r * 64 + ((c ^ ((r >> 2) & 3)) << 4)));
             }
 #pragma unroll
             for (int term = 0; term < 3; ++term)
@@ -128,7 +128,7 @@ __global__ __launch_bounds__(512) void router_gemm(const bf16_t* __restrict__ x,
                 for (int eb = 0; eb < 2; ++eb) {
                     const int r = we * 64 + eb * 32 + l32;
                     b[term][eb] = as_bf16x8(
-                        *(const u32x4*)(st + (1 + term) * RG_E * 64 + r * 64 + ((c ^ ((r >> 1) & 3)) << 4)));
+                        *(const u32x4*)(st + (1 + term) * RG_E * 64 + r * 64 + ((c ^ ((r >> 2) & 3)) << 4)));
                 }
 #pragma unroll
             for (int jj = 0; jj < 3; ++jj)   // lo, mid, hi
@@ -522,8 +522,8 @@ hipError_t launch_column_sum(const float* a, int rows, int E, float* slices, flo
 // blocks, the four 16-token blocks.  Per 32-wide K stage:
 //  - the 64 token rows (64 bytes each) are copied from memory straight into
 //    an LDS stage shared by the waves (one 1 KiB copy per wave), the four
-//    16-byte columns of a row XOR-swizzled by (row >> 1) & 3 so that the
-//    fragment reads are free of bank conflicts; token rows past T read as
+//    16-byte columns of a row XOR-swizzled by (row >> 2) & 3 so that the
+//    16 rows of a fragment read fall on all 64 LDS banks; token rows past T read as
 //    zero through the descriptor's byte count;
 //  - each wave loads the fp32 router weights of its own fragments from W_r
 //    as stored ([d, E]: for lane (r16, g) of an expert block, the 8 values
@@ -586,12 +586,12 @@ __global__ __launch_bounds__(256) void router_fused(const bf16_t* __restrict__ x
     const float b_mine = (b_r && (int)threadIdx.x < E) ? b_r[threadIdx.x] : 0.f;
 
     // token copy: wave w covers rows 16 w .. 16 w + 15; lane -> row 16 w + lane / 4,
-    // LDS slot lane % 4, which holds 16-byte column slot ^ ((row >> 1) & 3)
+    // LDS slot lane % 4, which holds 16-byte column slot ^ ((row >> 2) & 3)
     const int ntok = min(RF_TOK, T - tbase);
     const bf16_t* xw = x + (size_t)tbase * d;
     const uint32_t x_bytes = (uint32_t)ntok * d * 2;
     const int xr = wave * 16 + (lane >> 2);
-    const uint32_t xvo = (uint32_t)(xr * d * 2 + (((lane & 3) ^ ((xr >> 1) & 3)) << 4));
+    const uint32_t xvo = (uint32_t)(xr * d * 2 + (((lane & 3) ^ ((xr >> 2) & 3)) << 4));
     // weight fragment eb: expert (we * EBW + eb) * 16 + r16, rows k = 32 kk + 8 g + j of W_r
     const uint32_t w_bytes = (uint32_t)d * E * 4;
     const uint32_t w_stage = (uint32_t)RF_KC * E * 4;     // bytes of one K stage of W_r
@@ -643,7 +643,7 @@ __global__ __launch_bounds__(256) void router_fused(const bf16_t* __restrict__ x
 #pragma unroll
                 for (int tb = 0; tb < TBW; ++tb) {
                     const int r = (wt * TBW + tb) * 16 + r16;
-                    xb[tb] = as_bf16x8(*(const u32x4*)(sb + r * 64 + ((g ^ ((r >> 1) & 3)) << 4)));
+                    xb[tb] = as_bf16x8(*(const u32x4*)(sb + r * 64 + ((g ^ ((r >> 2) & 3)) << 4)));
                 }
                 // the three bf16 terms of each fragment, then the MFMAs with the
                 // small terms first: lo, mid, hi
