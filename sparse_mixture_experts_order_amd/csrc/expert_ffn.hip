@@ -894,6 +894,39 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
                 const char* sa = sw + W_STAGE;
                 // K permuted identically for both operands: MFMA step s takes 16-byte
                 // columns s (half 0) and KC / 32 + s (half 1) of the chunk
+                if constexpr (!AKM && !WKM) {
+                    // row-major stages: the fragments of step s + 1 are read while
+                    // the MFMAs of step s run (two register sets), so only the first
+                    // step of a chunk waits for the LDS latency
+                    bf16x8 fb[2][TOKB], fw[2][NBW];
+                    auto read_step = [&](int s, bf16x8 (&bt)[TOKB], bf16x8 (&wv)[NBW]) {
+                        const int c = half * (KC / 16) + s;
+#pragma unroll
+                        for (int tb = 0; tb < TOKB; ++tb) {
+                            const int r = tb * 32 + l32;
+                            bt[tb] = as_bf16x8(*(const u32x4*)(sa + r * RB + (dma_slot<KC>(r, c) << 4)));
+                        }
+#pragma unroll
+                        for (int nb = 0; nb < NBW; ++nb) {
+                            const int r = wave * 32 * NBW + nb * 32 + l32;
+                            wv[nb] = as_bf16x8(*(const u32x4*)(sw + r * RB + (dma_slot<KC>(r, c) << 4)));
+                        }
+                    };
+                    read_step(0, fb[0], fw[0]);
+#pragma unroll
+                    for (int s = 0; s < KC / 16; ++s) {
+                        if (s + 1 < KC / 16) read_step(s + 1, fb[(s + 1) & 1], fw[(s + 1) & 1]);
+                        // the reads above are issued before these MFMAs
+                        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                        for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+                            for (int tb = 0; tb < TOKB; ++tb)
+                                acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[s & 1][nb], fb[s & 1][tb],
+                                                                                      acc[nb][tb], 0, 0, 0);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                } else {
 #pragma unroll
                 for (int s = 0; s < KC / 16; ++s) {
                     const int c = half * (KC / 16) + s;
@@ -947,6 +980,7 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
                         for (int tb = 0; tb < TOKB; ++tb)
                             acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, bt[tb], acc[nb][tb], 0, 0, 0);
                     }
+                }
                 }
 
                 const int j = p / nk;
