@@ -361,7 +361,7 @@ def test_layer_end_to_end(D):
 
 
 # ------------------------------------------------------------ edge cases
-def small_layer(T, d, F, E, c, seed, bias0=0.0, residual=True, want_grad=True):
+def small_layer(T, d, F, E, c, seed, bias0=0.0, residual=True, want_grad=True, inspect=True):
     cfg = workloads.custom_config(T, d, F, E, c, index=1000 + seed)
     inp = workloads.make_layer_inputs(cfg)
     inp.b_r = inp.b_r.copy()
@@ -374,7 +374,7 @@ def small_layer(T, d, F, E, c, seed, bias0=0.0, residual=True, want_grad=True):
     D.x, D.w_r, D.b_r = bits_to_dev(inp.x_bits), f32_dev(inp.w_r), f32_dev(inp.b_r)
     D.w1, D.w2 = bits_to_dev(inp.w1_bits), bits_to_dev(inp.w2_bits)
     D.C = so.capacity(T, E, c)
-    t = run_layer(D, residual=residual, want_grad=want_grad)
+    t = run_layer(D, residual=residual, want_grad=want_grad, inspect=inspect, logits=inspect)
     return D, t
 
 
@@ -418,13 +418,18 @@ def check_small_layer(D, t, residual=True):
     (600, 64, 128, 6, 1.0, 3.0),       # hot expert 0, several empty experts
     (5000, 128, 256, 300, 1.0, 0.0),   # many experts, C = 17: 32-row token tiles
     (3000, 128, 192, 64, 1.3, 0.0),    # C = 61: 64-row token tiles
-    (2000, 64, 128, 16, 4.5, 0.0),     # C = 563 > 512: three 256-row tiles
+    (2000, 64, 128, 16, 4.5, 0.0),     # C = 563 > 512: five 128-row tiles, the last short
+    (1500, 128, 256, 8, 1.2, 0.0),     # C = 225: two 128-row tiles per expert
+    (2100, 192, 320, 8, 1.1, 0.0),     # C = 289: three 128-row tiles, the last short
 ])
 def test_edge_shapes(shape):
     T, d, F, E, c, bias0 = shape
     say(f"edge shape {shape}")
-    for residual in (False, True):
-        D, t = small_layer(T, d, F, E, c, seed=hash(shape) % 1000, bias0=bias0, residual=residual)
+    # intermediates kept (the first GEMM reads buf) in both modes, then the
+    # timed path (token rows gathered from x, the combine in the second GEMM)
+    for residual, inspect in ((False, True), (True, True), (False, False)):
+        say(f"edge shape {shape} residual={residual} inspect={inspect}")
+        D, t = small_layer(T, d, F, E, c, seed=hash(shape) % 1000, bias0=bias0, residual=residual, inspect=inspect)
         check_small_layer(D, t, residual=residual)
 
 
