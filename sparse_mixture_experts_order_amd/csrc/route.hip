@@ -557,12 +557,20 @@ __global__ __launch_bounds__(256) void router_fused(const bf16_t* __restrict__ x
                                                     float* __restrict__ gate, float* __restrict__ lse,
                                                     float* __restrict__ part) {
     constexpr int EP = EB * 16;
-    constexpr int STAGE = RF_TOK * 64;          // token rows of one stage
+    // E a whole number of expert blocks: each K stage of W_r (32 rows of E
+    // floats, one contiguous block) is copied into LDS next to the token rows;
+    // otherwise each wave loads its fragments' weights into a register ring
+    constexpr bool LDSW = FULL;
+    constexpr int WSTAGE = LDSW ? RF_KC * EP * 4 : 0;   // W_r bytes of one stage
+    constexpr int NWC = WSTAGE / 1024;                  // its 1 KiB copies
+    constexpr int WCP = (NWC + 3) / 4;                  // per wave (past NWC: repeats)
+    constexpr int XSTAGE = RF_TOK * 64;                 // token rows of one stage
+    constexpr int STAGE = XSTAGE + WSTAGE;
     constexpr int WE = EB < 4 ? EB : 4;         // waves across expert blocks
     constexpr int WT = 4 / WE;                  // waves across the four token blocks
     constexpr int EBW = EB / WE, TBW = 4 / WT;  // blocks per wave
-    constexpr int NWL = 8 * EBW;                // fp32 weight loads per wave per stage (8 k per fragment)
-    constexpr int PER_STAGE = 1 + NWL;          // loads per wave per stage
+    constexpr int NWL = LDSW ? 0 : 8 * EBW;     // fp32 weight loads per wave per stage (8 k per fragment)
+    constexpr int PER_STAGE = 1 + (LDSW ? WCP : NWL);   // loads per wave per stage
     constexpr int LROW = EP + 4;                // floats per token row of the logit tile
     constexpr int TILE = RF_TOK * LROW * 4;
     constexpr int LDS_BYTES = S * STAGE > TILE ? S * STAGE : TILE;
@@ -595,22 +603,43 @@ __global__ __launch_bounds__(256) void router_fused(const bf16_t* __restrict__ x
     // weight fragment eb: expert (we * EBW + eb) * 16 + r16, rows k = 32 kk + 8 g + j of W_r
     const uint32_t w_bytes = (uint32_t)d * E * 4;
     const uint32_t w_stage = (uint32_t)RF_KC * E * 4;     // bytes of one K stage of W_r
-    uint32_t wvo[EBW];
+    // LDS stage of W_r: 32 rows of EP floats; the 16-byte chunk c of row k sits at
+    // c ^ wswz(k), so a fragment read (16 experts x rows 8 g + j, g = 0..3, one j)
+    // falls on all 64 banks
+    auto wswz = [](int k) { return (4 * ((k >> 3) & 3)) & (EP / 4 - 1); };
+    uint32_t wvo[LDSW ? WCP : EBW], wdst[LDSW ? WCP : 1];
+    if constexpr (LDSW) {
 #pragma unroll
-    for (int eb = 0; eb < EBW; ++eb) {
-        const int e = min((we * EBW + eb) * 16 + r16, E - 1);
-        wvo[eb] = (uint32_t)((8 * g * E + e) * 4);
+        for (int i = 0; i < WCP; ++i) {
+            const int q = (wave * WCP + i) % NWC;   // copies past NWC repeat one (same bytes, same place)
+            const int lin = q * 1024 + lane * 16;
+            const int k = lin / (EP * 4), c = (lin - k * EP * 4) >> 4;
+            wvo[i] = (uint32_t)(k * EP * 4 + ((c ^ wswz(k)) << 4));
+            wdst[i] = (uint32_t)(XSTAGE + q * 1024);
+        }
+    } else {
+#pragma unroll
+        for (int eb = 0; eb < EBW; ++eb) {
+            const int e = min((we * EBW + eb) * 16 + r16, E - 1);
+            wvo[eb] = (uint32_t)((8 * g * E + e) * 4);
+        }
     }
-    float wreg[S][NWL];
-    auto issue = [&](int kk, int stg, float (&wr)[NWL]) {
+    float wreg[LDSW ? 1 : S][LDSW ? 1 : NWL];
+    auto issue = [&](int kk, int stg, float (&wr)[LDSW ? 1 : NWL]) {
         kk = min(kk, nk - 1);
         copy_to_lds(buffer_rsrc(xw, x_bytes), lds + stg * STAGE + wave * 1024, xvo, kk * 64);
+        if constexpr (LDSW) {
 #pragma unroll
-        for (int eb = 0; eb < EBW; ++eb)
+            for (int i = 0; i < WCP; ++i)
+                copy_to_lds(buffer_rsrc(w_r, w_bytes), lds + stg * STAGE + wdst[i], wvo[i], kk * w_stage);
+        } else {
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                wr[eb * 8 + j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                    buffer_rsrc(w_r, w_bytes), wvo[eb] + (uint32_t)j * E * 4, kk * w_stage, 0));
+            for (int eb = 0; eb < EBW; ++eb)
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    wr[eb * 8 + j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                        buffer_rsrc(w_r, w_bytes), wvo[eb] + (uint32_t)j * E * 4, kk * w_stage, 0));
+        }
         // loads stay in step order (the waits count whole steps): neither the
         // optimizer nor the scheduler may move them past this point
         asm volatile("" ::: "memory");
@@ -624,7 +653,7 @@ __global__ __launch_bounds__(256) void router_fused(const bf16_t* __restrict__ x
         for (int eb = 0; eb < EBW; ++eb) acc[tb][eb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
-    for (int p = 0; p < S - 1; ++p) issue(p, p, wreg[p]);
+    for (int p = 0; p < S - 1; ++p) issue(p, p, wreg[LDSW ? 0 : p]);
     // whole rounds of S steps keep every load and the register ring
     // unconditional (steps past nk re-read the last stage and skip the MFMAs)
     // (d >= 32, so there is at least one round: no guard for the loads to sink past)
@@ -636,7 +665,7 @@ __global__ __launch_bounds__(256) void router_fused(const bf16_t* __restrict__ x
             const int kk = k0 + u;
             wait_copies<PER_STAGE * (S - 2)>();        // this wave's loads of step kk are done
             lds_barrier();                             // every wave's token copy too, and step kk - 1 is read out
-            issue(kk + S - 1, (u + S - 1) % S, wreg[(u + S - 1) % S]);   // into the slots of step kk - 1
+            issue(kk + S - 1, (u + S - 1) % S, wreg[LDSW ? 0 : (u + S - 1) % S]);   // into the slots of step kk - 1
             if (kk < nk) {
                 const char* sb = lds + u * STAGE;
                 bf16x8 xb[TBW];
@@ -647,13 +676,28 @@ __global__ __launch_bounds__(256) void router_fused(const bf16_t* __restrict__ x
                 }
                 // the three bf16 terms of each fragment, then the MFMAs with the
                 // small terms first: lo, mid, hi
+                float wv[EBW][8];
+                if constexpr (LDSW) {   // rows 8 g + j of expert (we EBW + eb) 16 + r16, from the stage
+                    const char* sw = sb + XSTAGE;
+#pragma unroll
+                    for (int eb = 0; eb < EBW; ++eb) {
+                        const int e = (we * EBW + eb) * 16 + r16;
+                        const char* base = sw + 8 * g * EP * 4 + ((((e >> 2) ^ wswz(8 * g)) << 2) + (e & 3)) * 4;
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) wv[eb][j] = *(const float*)(base + j * EP * 4);
+                    }
+                } else {
+#pragma unroll
+                    for (int eb = 0; eb < EBW; ++eb)
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) wv[eb][j] = wreg[LDSW ? 0 : u][eb * 8 + j];
+                }
                 uint32_t t3[3][EBW][4];
 #pragma unroll
                 for (int eb = 0; eb < EBW; ++eb)
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
-                        split3_bf16x2(wreg[u][eb * 8 + 2 * j], wreg[u][eb * 8 + 2 * j + 1], t3[0][eb][j], t3[1][eb][j],
-                                      t3[2][eb][j]);
+                        split3_bf16x2(wv[eb][2 * j], wv[eb][2 * j + 1], t3[0][eb][j], t3[1][eb][j], t3[2][eb][j]);
 #pragma unroll
                 for (int jj = 0; jj < 3; ++jj) {
                     const int term = 2 - jj;
@@ -799,20 +843,22 @@ __global__ __launch_bounds__(256) void router_fused(const bf16_t* __restrict__ x
 template <int KMAX>
 static void fused_by_width(const bf16_t* x, const float* w_r, const float* b_r, int T, int d, int E, int k,
                            float* logits_out, int32_t* expert, float* gate, float* lse, float* part, hipStream_t s) {
-#define SWMOE_RF(EB, S)                                                                                         \
+// SL: stages with W_r through LDS (E a multiple of 16), SR: with the register ring
+#define SWMOE_RF(EB, SL, SR)                                                                                    \
     do {                                                                                                        \
         if (E == 16 * (EB))                                                                                     \
-            hipLaunchKernelGGL((router_fused<EB, S, KMAX, true>), dim3(router_fused_blocks(T)), dim3(256), 0, s, x, \
-                               w_r, b_r, T, d, E, k, logits_out, expert, gate, lse, part);                      \
+            hipLaunchKernelGGL((router_fused<EB, SL, KMAX, true>), dim3(router_fused_blocks(T)), dim3(256), 0, s, \
+                               x, w_r, b_r, T, d, E, k, logits_out, expert, gate, lse, part);                   \
         else                                                                                                    \
-            hipLaunchKernelGGL((router_fused<EB, S, KMAX, false>), dim3(router_fused_blocks(T)), dim3(256), 0, s,  \
+            hipLaunchKernelGGL((router_fused<EB, SR, KMAX, false>), dim3(router_fused_blocks(T)), dim3(256), 0, s, \
                                x, w_r, b_r, T, d, E, k, logits_out, expert, gate, lse, part);                   \
     } while (0)
-    if (E <= 16) SWMOE_RF(1, 4);
-    else if (E <= 32) SWMOE_RF(2, 4);
-    else if (E <= 64) SWMOE_RF(4, 4);
-    else if (E <= 128) SWMOE_RF(8, 3);
-    else SWMOE_RF(16, 2);   // 32 weight loads per wave per stage: one stage ahead
+    // (LDS stages sized so that two workgroups fit a CU)
+    if (E <= 16) SWMOE_RF(1, 6, 4);
+    else if (E <= 32) SWMOE_RF(2, 6, 4);
+    else if (E <= 64) SWMOE_RF(4, 5, 4);
+    else if (E <= 128) SWMOE_RF(8, 3, 3);
+    else SWMOE_RF(16, 2, 2);   // register ring: 32 weight loads per wave per stage, one stage ahead
 #undef SWMOE_RF
 }
 
