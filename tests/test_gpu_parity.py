@@ -164,6 +164,29 @@ def test_route_gemm_ragged(T, d, E, bias):
     """The tiled router GEMM (E > 256) on ragged token and expert tiles: every
     logit against the fp64 oracle, and the routing on margin-safe tokens."""
     say(f"route gemm ragged T={T} d={d} E={E} bias={bias}")
+    check_route_shape(T, d, E, bias)
+
+
+@pytest.mark.parametrize("T,d,E,bias", [
+    (1000, 96, 16, True),     # one expert block, W_r through LDS, six stages
+    (777, 64, 32, False),     # two blocks; a 9-token last workgroup
+    (1000, 160, 48, True),    # 48 = 3 x 16 inside a 64-wide block: the register ring
+    (640, 96, 64, True),      # four blocks, five stages
+    (1000, 128, 96, False),   # 96 inside a 128-wide block: the register ring
+    (513, 224, 128, True),    # eight blocks, three stages; one token in the last workgroup
+    (700, 96, 200, True),     # 200 inside a 256-wide block: the register ring, two stages
+    (1024, 160, 256, True),   # sixteen blocks, two LDS stages of 36 KiB
+])
+def test_route_fused_widths(T, d, E, bias):
+    """The fused router (E <= 256) at every expert-block count it
+    specialises, with W_r staged through LDS (E a multiple of 16) and
+    through the register ring (other E), on ragged token counts: every logit
+    against the fp64 oracle, and the routing on margin-safe tokens."""
+    say(f"route fused T={T} d={d} E={E} bias={bias}")
+    check_route_shape(T, d, E, bias)
+
+
+def check_route_shape(T, d, E, bias):
     seed = 7000 + T + d + E
     x_bits = workloads.random_bf16((T, d), seed)
     w_r = (workloads.random_logits(d, E, seed) * np.float32(np.sqrt(0.5 / d))).astype(np.float32)
