@@ -11,26 +11,30 @@
 //
 // Design for one MI355X.  At Switch-Base shapes an expert sees ~120 rows, so
 // the layer is bound by streaming every expert's weights from HBM once, not
-// by MFMA.  The kernel is organised around that stream:
-//   - persistent workgroups (as many as fit on the chip) walk the tile list;
-//     a tile is (token block of TOK rows of one expert, weight-row block of
-//     NWG rows), ordered so the weight blocks of one token block are
-//     neighbours, and dealt XCD-major so neighbours share an L2;
-//   - each wave owns 32*NBW weight rows of the tile and computes them
-//     against all TOK token rows.  Weights never touch LDS: each lane loads
-//     64 contiguous bytes of its weight row per 64-wide K chunk straight into
-//     registers.  The K order inside a chunk is permuted identically for both
-//     operands (a reduction is order free), so a half wave reads whole
-//     64-byte runs;
-//   - weights and token tiles flow through rings of R register chunks, R-1
-//     of them in flight, and the ring runs across tile boundaries: the next
-//     tile's loads are in flight while a tile's results are written out, so
-//     the HBM stream never drains between tiles;
-//   - the token tile is shared by the waves through LDS, double buffered,
-//     rows padded to 144 bytes so the MFMA-layout reads are conflict free.
-//     Token loads are issued before weight loads of the same step: vector
-//     memory counters complete in issue order, so waiting for a token chunk
-//     never waits for a weight chunk still ahead of the MFMAs.
+// by MFMA.  Both kernels here are organised around that stream: persistent
+// workgroups (as many as fit on the chip) walk the tile list; a tile is (token
+// block of TOK rows of one expert, weight-row block of NWG rows), ordered so
+// the token tiles that read one weight block are neighbours, and dealt
+// XCD-major so neighbours share an L2.
+//   - expert_gemm_dma (every forward product, and the backward's products
+//     with 128-row token tiles): both operands of a 64-wide K chunk go from
+//     memory straight into LDS stages by buffer loads with an LDS
+//     destination, S - 1 chunks ahead of the MFMAs, one barrier per chunk;
+//     no register holds data in flight.  Its notes are at the kernel.
+//   - expert_gemm (the register kernel: the backward's products with 32- and
+//     64-row token tiles): each wave owns 32*NBW weight rows of the tile and
+//     computes them against all TOK token rows.  Weights never touch LDS:
+//     each lane loads 64 contiguous bytes of its weight row per 64-wide K
+//     chunk straight into registers.  The K order inside a chunk is permuted
+//     identically for both operands (a reduction is order free), so a half
+//     wave reads whole 64-byte runs.  Weights and token tiles flow through
+//     rings of R register chunks, R-1 of them in flight, and the ring runs
+//     across tile boundaries.  The token tile is shared by the waves through
+//     LDS, double buffered, rows padded to 144 bytes so the MFMA-layout reads
+//     are conflict free.  Token loads are issued before weight loads of the
+//     same step: vector memory counters complete in issue order, so waiting
+//     for a token chunk never waits for a weight chunk still ahead of the
+//     MFMAs.
 #include "common.hpp"
 #include "kernels.hpp"
 

@@ -76,8 +76,8 @@ struct FfnCombine {
     bf16_t* out;
     float* y;
 };
-// 128-row token tiles (C > 64: the direct-to-LDS kernel for every product,
-// the backward's included)
+// 128-row token tiles (C > 64), the direct-to-LDS kernel for every product
+// over them, the backward's included
 bool ffn_wide_tiles(int C);
 // the forward's expert GEMMs run the direct-to-LDS kernel at every C >= 1 (32-,
 // 64- or 128-row token tiles), so they can gather token rows and fuse the combine
