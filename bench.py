@@ -121,6 +121,9 @@ def kernel_bytes(T, d, F, E, C, A, fused, gathered):
         "expert_gemm1": w + 2 * A * d,
         "expert_gemm2": w + (2 * A * d + 2 * A * d + 8 * A if fused else 4 * A * d),
         "expert_gemm2_with_h": w + 2 * A * F + (2 * A * d + 2 * A * d + 8 * A if fused else 4 * A * d),
+        # both products in one kernel (small capacity): both weight sets, the
+        # gathered token rows, the residual rows, the output rows, gate and slot
+        "expert_ffn_fused": 2 * w + 2 * A * d + 2 * A * d + 2 * A * d + 8 * A,
         # with the token rows gathered by the first GEMM no row is copied here:
         # positions and masks, the slot table, and the dropped tokens' residual rows
         "gather": (9 * T + 4 * A + (4 * (T - A) * d if fused else 0)) if gathered else
@@ -372,7 +375,8 @@ def measure_layer(sw, torch, cfg, dev, stream, steps, warmup, cold=True, library
     gathered = fused or ("gather" in mean_us and C > 64)
     kb = kernel_bytes(T, d, F, E, C, A, fused, gathered)
     wk = floors(T, d, F, E, C, A, cfg.want_grad)
-    gemms = [k for k in ("expert_gemm1", "expert_gemm2") if k in mean_us]
+    gemms = [k for k in ("expert_gemm1", "expert_gemm2", "expert_ffn_fused") if k in mean_us]
+    one_kernel = "expert_ffn_fused" in mean_us
     dominant = max(gemms, key=lambda k: mean_us[k])
     ffn_us = sum(per_step_us[k] for k in gemms)
     router_us = sum(per_step_us.get(k, 0.0) for k in ("split_router_weights", "router_fused", "router_gemm",
@@ -394,13 +398,15 @@ def measure_layer(sw, torch, cfg, dev, stream, steps, warmup, cold=True, library
                    "roofline_frac": wk["router"]["floor_us"] / router_us if router_us else None,
                    "mfma_pct_of_bf16_peak": 100.0 * wk["router"]["flops"] / (router_us * 1e-6) /
                    (PEAK_BF16_TFLOPS * 1e12) if router_us else None},
-        "dispatch_in_layer": ({"fused": True, "into": "expert_gemm1 (token rows gathered from x)",
+        "dispatch_in_layer": ({"fused": True, "into": ("expert_ffn_fused" if one_kernel else "expert_gemm1") +
+                               " (token rows gathered from x)",
                                "gather_us": per_step_us.get("gather"), "gather_bytes": kb["gather"],
                                "gather_GBps": kb["gather"] / (mean_us["gather"] * 1e-6) / 1e9}
                               if gathered else
                               {"fused": False, "gather_us": per_step_us.get("gather"),
                                "GBps": kb["gather"] / (mean_us["gather"] * 1e-6) / 1e9}),
-        "combine_in_layer": ({"fused": True, "into": "expert_gemm2 epilogue"} if fused else
+        "combine_in_layer": ({"fused": True, "into": ("expert_ffn_fused" if one_kernel else "expert_gemm2") +
+                              " epilogue"} if fused else
                              {"fused": False, "us": per_step_us["combine"],
                               "GBps": kb["combine"] / (mean_us["combine"] * 1e-6) / 1e9}),
     }

@@ -37,13 +37,13 @@ enum KernelId {
     K_SPLIT = 0, K_RGEMM, K_RSOFTMAX, K_RREDUCE, K_SCAN_LOCAL, K_SCAN_OFFSETS, K_GATHER,
     K_GEMM1, K_GEMM2, K_COMBINE, K_AUX_STATS, K_AUX_GRAD, K_COPY, K_FFN_TILES, K_Z_LOSS, K_RFUSED,
     K_COMBINE_BWD, K_ROUTER_DZ, K_ROUTER_DB, K_ROUTER_WGRAD, K_TRANSPOSE, K_GEMM_DA, K_GEMM_DBUF, K_GEMM_DW2,
-    K_GEMM_DW1, K_DX, K_COUNT
+    K_GEMM_DW1, K_DX, K_FFN_FUSED, K_COUNT
 };
 const char* kKernelNames[K_COUNT] = {
     "split_router_weights", "router_gemm", "router_softmax", "router_reduce", "scan_local", "scan_offsets",
     "gather", "expert_gemm1", "expert_gemm2", "combine", "aux_stats", "aux_grad", "stream_copy", "ffn_tile_prefix", "z_loss", "router_fused",
     "combine_bwd", "router_dz", "router_db", "router_wgrad", "transpose_rows", "gemm_dA", "gemm_dbuf", "gemm_dW2",
-    "gemm_dW1", "dx_assemble"};
+    "gemm_dW1", "dx_assemble", "expert_ffn_fused"};
 
 struct ProfRec { int id; hipEvent_t a, b; };
 bool g_prof = false;
@@ -348,6 +348,14 @@ switch_status run_ffn(const FfnArgs& a, void* ws, hipStream_t s) {
     int4* ttab = c.take<int4>(ffn_tile_table_entries(a.E, a.C));
     if (!a.tiles_ready)
         LAUNCH(K_FFN_TILES, "ffn_tile_prefix", s, launch_ffn_tile_prefix(a.accepted, a.E, a.C, pre, ttab, s));
+    // gathered token rows, the fused combine and no H asked for: at small
+    // capacity both products run in one kernel with H on chip
+    if (a.a_rows && a.cb && !a.h && ffn_fused_small(a.C, a.d, a.d_ff)) {
+        LAUNCH(K_FFN_FUSED, "expert_ffn_fused", s,
+               launch_expert_ffn_fused(a.x_src, a.x_tokens, a.a_rows, a.w1, a.w2, pre, ttab, *a.cb, a.E, a.C, a.d,
+                                       a.d_ff, s));
+        return SWITCH_OK;
+    }
     if (a.a_rows)
         LAUNCH(K_GEMM1, "expert_gemm1", s,
                launch_expert_gemm1_gather(a.x_src, a.x_tokens, a.a_rows, a.w1, pre, ttab, h, a.E, a.C, a.d, a.d_ff,

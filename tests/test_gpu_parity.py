@@ -456,6 +456,36 @@ def test_edge_shapes(shape):
         check_small_layer(D, t, residual=residual)
 
 
+@pytest.mark.parametrize("shape", [
+    (3000, 256, 256, 128, 1.0, 0.0),    # C = 24, one 256-column block in each phase
+    (4096, 512, 1024, 128, 1.0, 0.0),   # C = 32, the largest H (64 KiB)
+    (1000, 256, 768, 200, 1.0, 3.0),    # C = 5, hot expert 0, many empty experts, 1536-byte H rows
+    (77, 768, 512, 64, 1.0, 0.0),       # C = 2, ragged T, most experts empty
+    (2003, 1024, 1024, 64, 0.5, 0.0),   # C = 16 at the many-small-experts widths, capacity factor 0.5
+    (1500, 512, 2048, 64, 1.0, 0.0),    # C = 24, d_ff = 2048: four pieces of H
+])
+def test_fused_small_capacity(shape):
+    """At most 32 buffer rows per expert (d a multiple of 256 up to 1024, d_ff
+    a multiple of 256): the timed path runs both expert products in one kernel
+    with the hidden activation on chip; branch and residual outputs against the
+    oracle, then the same layer with its intermediates kept (two kernels)."""
+    T, d, F, E, c, bias0 = shape
+    for residual in (False, True):
+        say(f"fused small capacity {shape} residual={residual}")
+        sw.switch_profile_enable(True)
+        try:
+            D, t = small_layer(T, d, F, E, c, seed=hash(shape) % 1000, bias0=bias0, residual=residual,
+                               inspect=False)
+        finally:
+            names = [n for n, _ in sw.switch_profile_collect()]
+            sw.switch_profile_enable(False)
+        assert D.C <= 32
+        assert "expert_ffn_fused" in names and "expert_gemm1" not in names, names
+        check_small_layer(D, t, residual=residual)
+    D2, t2 = small_layer(T, d, F, E, c, seed=hash(shape) % 1000, bias0=bias0, residual=True, inspect=True)
+    check_small_layer(D2, t2, residual=True)
+
+
 def test_zero_capacity_and_empty_batch():
     D, t = small_layer(256, 64, 128, 4, 0.0, seed=3)
     assert D.C == 0
