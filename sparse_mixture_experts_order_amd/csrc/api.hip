@@ -350,7 +350,7 @@ switch_status run_ffn(const FfnArgs& a, void* ws, hipStream_t s) {
         LAUNCH(K_FFN_TILES, "ffn_tile_prefix", s, launch_ffn_tile_prefix(a.accepted, a.E, a.C, pre, ttab, s));
     // gathered token rows, the fused combine and no H asked for: at small
     // capacity both products run in one kernel with H on chip
-    if (a.a_rows && a.cb && !a.h && ffn_fused_small(a.C, a.d, a.d_ff)) {
+    if (a.a_rows && a.cb && !a.h && ffn_fused_ok(a.C, a.d, a.d_ff)) {
         LAUNCH(K_FFN_FUSED, "expert_ffn_fused", s,
                launch_expert_ffn_fused(a.x_src, a.x_tokens, a.a_rows, a.w1, a.w2, pre, ttab, *a.cb, a.E, a.C, a.d,
                                        a.d_ff, s));

@@ -1015,30 +1015,31 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
 }
 
 // ------------------------------------------------------------------ fused FFN, small capacity
-// Both expert products in one kernel for experts of at most 32 buffer rows
-// (C <= 32; d a multiple of 256 up to 1024, d_ff a multiple of 256): the
-// hidden activation H never goes to memory.  (Stores inside the weight
-// stream cost far more than their bytes on this chip, and at these shapes H
-// is as large as the layer output.)  One workgroup of 8 waves per expert,
-// persistent over the expert list (one 32-row tile per non-empty expert).
-// d_ff is taken in pieces of HB blocks of 256 columns; per piece:
+// Both expert products in one kernel for experts of at most 64 buffer rows
+// (one token tile of 32 or 64 rows; d a multiple of 256 up to 1024, d_ff a
+// multiple of 256): the hidden activation H never goes to memory.  (Stores
+// inside the weight stream cost far more than their bytes on this chip, and
+// at these shapes H is as large as the layer output or larger.)  One
+// workgroup of 8 waves per expert, persistent over the tile list, each
+// expert's weights streamed once.  d_ff is taken in pieces of HB blocks of
+// 256 columns; per piece:
 //   phase 1, for each block of the piece: K = d in KC-wide chunks, a chunk
-//     holding 256 W1 rows and the 32 token rows (gathered from x through the
-//     slot table; rows past the expert's count read as zero); after the
+//     holding 256 W1 rows and the tile's TOK token rows (gathered from x
+//     through the slot table; rows past the tile read as zero); after the
 //     block's last chunk each wave writes bf16(ReLU(acc)) into the LDS piece
-//     of H (32 x 256 HB);
+//     of H (TOK x 256 HB);
 //   phase 2, for each block db of 256 output columns: K = the piece's
 //     columns of d_ff, a chunk holding 256 W2 rows; the token operand comes
-//     from H, and each wave adds into its accumulator of block db (the ND =
-//     d / 256 accumulators stay in registers over the pieces, so H is
-//     never needed whole).
+//     from H, and each wave adds into its accumulators of block db (the ND =
+//     d / 256 accumulators stay in registers over the pieces, so H is never
+//     needed whole).
 // After the last piece the combine epilogue writes the kept tokens' output
-// rows.  The copies run one pipeline over all chunks of all experts, S LDS
+// rows.  The copies run one pipeline over all chunks of all tiles, S LDS
 // stages, one barrier per chunk.  Wave w owns weight rows 32 w .. 32 w + 31
-// of each 256-row block against all 32 tokens.  In the H piece, within each
+// of each 256-row block against all TOK tokens.  In the H piece, within each
 // 256-byte window of a row, the 16-byte slot s of row r sits at s ^ (r & 15),
 // so the 16 rows of a fragment read cover all 64 banks.
-constexpr int FS_TOK = 32, FS_NWG = 256, FS_WAVES = 8, FS_MAXND = 4;
+constexpr int FS_NWG = 256, FS_WAVES = 8, FS_MAXND = 4;
 
 // byte offset in an H piece of rows of `rb` bytes of the 16-byte slot s
 // (columns 8 s .. 8 s + 7) of token row r
@@ -1057,7 +1058,7 @@ __device__ __forceinline__ void wait_copies_upto(int n) {
     }
 }
 
-template <int KC, int S, int HB, int ND>
+template <int KC, int S, int HB, int ND, int TOKB>
 __global__ __launch_bounds__(64 * FS_WAVES) void expert_ffn_fused(const bf16_t* __restrict__ x, uint32_t x_bytes,
                                                                   const int32_t* __restrict__ a_rows,
                                                                   const bf16_t* __restrict__ W1,
@@ -1067,22 +1068,25 @@ __global__ __launch_bounds__(64 * FS_WAVES) void expert_ffn_fused(const bf16_t* 
                                                                   int E, int C, int F) {
     static_assert(KC == 64 || KC == 32, "64- or 32-wide K chunks");
     static_assert(ND >= 1 && ND <= FS_MAXND, "d = 256 ND");
+    static_assert(TOKB == 1 || TOKB == 2, "32- or 64-row token tiles");
+    constexpr int TOK = 32 * TOKB;
     constexpr int d = ND * FS_NWG;
     constexpr int RB = KC * 2;                     // bytes per staged row
     constexpr int RPC = 1024 / RB;                 // rows per 1 KiB copy
     constexpr int NCOL = RB / 16;                  // 16-byte slots per row
     constexpr int KS = KC / 16;                    // MFMA steps per chunk
     constexpr int WPW = FS_NWG / RPC / FS_WAVES;   // weight copies per wave per chunk
-    constexpr int XCP = FS_TOK / RPC;              // token copies per chunk, one each by waves 0 .. XCP - 1
+    constexpr int XCP = TOK / RPC;                 // token copies per chunk, one each by waves 0 .. XCP - 1
+    static_assert(XCP <= FS_WAVES, "one token copy per wave at most");
     constexpr int W_STAGE = FS_NWG * RB;
-    constexpr int STAGE = W_STAGE + FS_TOK * RB;
+    constexpr int STAGE = W_STAGE + TOK * RB;
     constexpr int HRB = HB * FS_NWG * 2;           // bytes per row of the H piece
     constexpr int NKD = d / KC;                    // chunks of a phase-1 block
     constexpr int NKH = HB * FS_NWG / KC;          // chunks of a phase-2 block (one piece)
     constexpr int PH1 = HB * NKD;                  // phase-1 chunks of a piece
     constexpr int PP = PH1 + ND * NKH;             // chunks of a piece
     static_assert(S >= 2 && (WPW + 1) * (S - 1) < 64, "outstanding copies fit the counter");
-    __shared__ __attribute__((aligned(16))) char lds[S * STAGE + FS_TOK * HRB];
+    __shared__ __attribute__((aligned(16))) char lds[S * STAGE + TOK * HRB];
     char* const hl = lds + S * STAGE;
 
     const int total = pre[E];
@@ -1090,8 +1094,8 @@ __global__ __launch_bounds__(64 * FS_WAVES) void expert_ffn_fused(const bf16_t* 
     const int slot = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3); // XCD-major
     if (slot >= total) return;
     const int ntl = (total - slot + G - 1) / G;
-    const int npc = F / (HB * FS_NWG);   // pieces of an expert
-    const int PE = npc * PP;             // chunks of an expert
+    const int npc = F / (HB * FS_NWG);   // pieces of a tile
+    const int PE = npc * PP;             // chunks of a tile
     const int P = ntl * PE;
 
     const int lane = threadIdx.x & 63;
@@ -1107,29 +1111,29 @@ __global__ __launch_bounds__(64 * FS_WAVES) void expert_ffn_fused(const bf16_t* 
         wvo1[i] = (uint32_t)r * d * 2 + col;
         wvo2[i] = (uint32_t)r * F * 2 + col;
     }
-    // token copy (waves below XCP): rows RPC wave + lane / NCOL
+    // token copy (waves below XCP): tile rows RPC wave + lane / NCOL
     const bool has_x = wave < XCP;
     const int qt = has_x ? wave : 0;
     const int xr = RPC * qt + lane / NCOL;
     const uint32_t xcol = (uint32_t)(dma_slot<KC>(xr, lane % NCOL) << 4);
     const __amdgpu_buffer_rsrc_t rx = buffer_rsrc_uniform(x, x_bytes);
 
-    // the copies' expert (ahead of the compute's by up to S - 1 chunks)
-    int c_exp = -1, c_e = 0;
+    // the copies' tile (ahead of the compute's by up to S - 1 chunks)
+    int c_tile = -1, c_e = 0;
     uint32_t xo = 0;
     auto issue = [&](int f) {
         f = min(f, P - 1);   // past the end: the last chunk again (never read)
         const int j = __builtin_amdgcn_readfirstlane(f / PE);
         const int q = f - j * PE;
-        if (j != c_exp) {
-            c_exp = j;
-            const FfnTile t = decode_tile(j * G + slot, ttab, 1, FS_TOK);
+        if (j != c_tile) {
+            c_tile = j;
+            const FfnTile t = decode_tile(j * G + slot, ttab, 1, TOK);
             c_e = t.e;
             // this wave's RPC row-map entries, all issued as uniform loads before
             // any is used (the map is padded past its end), then the lane's own;
             // a per-lane load would be a vector load, whose wait would also wait
             // for the copies in flight
-            const int32_t* rowp = a_rows + (size_t)t.e * C + RPC * qt;
+            const int32_t* rowp = a_rows + (size_t)t.e * C + t.tok_base + RPC * qt;
             int tk[RPC];
 #pragma unroll
             for (int u = 0; u < RPC; ++u) tk[u] = __builtin_amdgcn_readfirstlane(rowp[u]);
@@ -1160,111 +1164,115 @@ __global__ __launch_bounds__(64 * FS_WAVES) void expert_ffn_fused(const bf16_t* 
         }
     };
 
-    f32x16 acc1;                 // phase 1: this wave's 32 H columns of the block
-    f32x16 acc2[ND];             // phase 2: acc2[0] is the block being added to (rotated after each)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc1[i] = 0.f;
+    f32x16 acc1[TOKB];       // phase 1: this wave's 32 H columns of the block, per 32 tokens
+    f32x16 acc2[ND][TOKB];   // phase 2: per output block, per 32 tokens
 #pragma unroll
     for (int b = 0; b < ND; ++b)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc2[b][i] = 0.f;
+        for (int tb = 0; tb < TOKB; ++tb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc2[b][tb][i] = 0.f;
     const int r = wave * 32 + l32;   // this lane's weight row in a stage
 
-#pragma unroll
-    for (int f = 0; f < S - 1; ++f) issue(f);
-    int j = 0, q = 0;   // chunk p is chunk q of the workgroup's expert j
-    for (int p = 0; p < P; ++p, q = q + 1 == PE ? 0 : q + 1, j += q == 0) {
+    // chunk f is a phase-1 one
+    auto phase1 = [&](int f) {
+        const int qf = f % PE;
+        return f < P && qf % PP < PH1;
+    };
+    // the next chunk p: wait for it, meet the other waves, send the copies
+    // S - 1 chunks ahead; returns its stage
+    int p = 0;
+    auto next_chunk = [&]() -> const char* {
         // this wave's copies of chunk p are in: the copies issued after them,
         // those of chunks p + 1 .. p + S - 2, may still be in flight (WPW per
         // chunk, one more for a phase-1 chunk in waves with a token copy; the
         // clamped ones past the end repeat the last chunk, a phase-2 one)
         int n1 = 0;
 #pragma unroll
-        for (int i = 1; i <= S - 2; ++i) {
-            const int qi = q + i < PE ? q + i : q + i - PE;
-            n1 += (p + i < P && qi % PP < PH1) ? 1 : 0;
-        }
-        wait_copies_upto<WPW * (S - 2), S - 2>(has_x ? n1 : 0);
+        for (int i = 1; i <= S - 2; ++i) n1 += phase1(p + i) ? 1 : 0;
+        wait_copies_upto<WPW * (S - 2), S - 2>(has_x ? __builtin_amdgcn_readfirstlane(n1) : 0);
         lds_barrier();   // every wave's; chunk p - 1 is read out, and the H writes before it are in
         issue(p + S - 1);
         const char* sw = lds + (p % S) * STAGE;
-        const int pc = q / PP, qq = q - pc * PP;
-        if (qq < PH1) {
-            const char* sx = sw + W_STAGE;
+        ++p;
+        return sw;
+    };
+
 #pragma unroll
-            for (int st = 0; st < KS; ++st) {
-                const int c = half * KS + st;
-                const bf16x8 wa = as_bf16x8(*(const u32x4*)(sw + r * RB + (dma_slot<KC>(r, c) << 4)));
-                const bf16x8 bt = as_bf16x8(*(const u32x4*)(sx + l32 * RB + (dma_slot<KC>(l32, c) << 4)));
-                acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, bt, acc1, 0, 0, 0);
-            }
-            const int fl = qq / NKD;
-            if (qq - fl * NKD == NKD - 1) {
-                // lane: token l32, piece columns 256 fl + 32 wave + 8 g + 4 half + (0..3) from acc1[4 g + (0..3)]
+    for (int f = 0; f < S - 1; ++f) issue(f);
+    for (int jt = 0; jt < ntl; ++jt) {
+        for (int pc = 0; pc < npc; ++pc) {
+            // phase 1: the piece's H blocks
+            for (int fl = 0; fl < HB; ++fl) {
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int f0 = fl * FS_NWG + wave * 32 + 8 * g + 4 * half;
-                    *(uint2*)(hl + fs_h_slot(l32, f0 >> 3, HRB) + (f0 & 7) * 2) =
-                        make_uint2(pack_bf16x2(fmaxf(acc1[4 * g + 0], 0.f), fmaxf(acc1[4 * g + 1], 0.f)),
-                                   pack_bf16x2(fmaxf(acc1[4 * g + 2], 0.f), fmaxf(acc1[4 * g + 3], 0.f)));
-                }
+                for (int tb = 0; tb < TOKB; ++tb)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) acc1[i] = 0.f;
-            }
-        } else {
-            const int q2 = qq - PH1;
-            const int db = q2 / NKH, kf = q2 - db * NKH;
+                    for (int i = 0; i < 16; ++i) acc1[tb][i] = 0.f;
+                for (int kf = 0; kf < NKD; ++kf) {
+                    const char* sw = next_chunk();
+                    const char* sx = sw + W_STAGE;
 #pragma unroll
-            for (int st = 0; st < KS; ++st) {
-                const int c = half * KS + st;
-                const bf16x8 wa = as_bf16x8(*(const u32x4*)(sw + r * RB + (dma_slot<KC>(r, c) << 4)));
-                const bf16x8 bt = as_bf16x8(*(const u32x4*)(hl + fs_h_slot(l32, kf * NCOL + c, HRB)));
-                acc2[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, bt, acc2[0], 0, 0, 0);
-            }
-            if (kf == NKH - 1) {
-                // block db done for this piece: the next block's accumulator to the front
-                const f32x16 t0 = acc2[0];
+                    for (int st = 0; st < KS; ++st) {
+                        const int c = half * KS + st;
+                        const bf16x8 wa = as_bf16x8(*(const u32x4*)(sw + r * RB + (dma_slot<KC>(r, c) << 4)));
 #pragma unroll
-                for (int b = 0; b + 1 < ND; ++b) acc2[b] = acc2[b + 1];
-                acc2[ND - 1] = t0;
-                if (q == PE - 1) {   // the expert's last chunk: the combine of every block
-                    FfnTile t = decode_tile(j * G + slot, ttab, 1, FS_TOK);
-                    CombineInputs<1, 1> cin[ND];
-                    combine_load_tokens(cin[0], t, cb, C, l32);
-#pragma unroll
-                    for (int b = 1; b < ND; ++b) cin[b].tok[0] = cin[0].tok[0];
-                    // every row load issued before any is used: one wait for all
-                    const bf16_t* res = cb.residual ? cb.residual : cb.out;
-                    const int tk = max(cin[0].tok[0], 0);
-                    const float gt = cb.gate[tk];
-#pragma unroll
-                    for (int b = 0; b < ND; ++b)
-#pragma unroll
-                        for (int run = 0; run < 2; ++run)
-                            cin[b].rr[0][0][run] =
-                                *(const u32x4*)(res + (size_t)tk * d + b * FS_NWG + wave * 32 + run * 16 + half * 8);
-                    asm volatile("" ::: "memory");
-                    __builtin_amdgcn_sched_barrier(0);
-                    const bool on = cin[0].tok[0] >= 0;
-#pragma unroll
-                    for (int b = 0; b < ND; ++b) {
-                        cin[b].g[0] = on ? gt : 0.f;
-#pragma unroll
-                        for (int run = 0; run < 2; ++run)
-                            cin[b].rr[0][0][run] =
-                                (on && cb.residual) ? cin[b].rr[0][0][run] : u32x4{0u, 0u, 0u, 0u};
+                        for (int tb = 0; tb < TOKB; ++tb) {
+                            const int xrow = tb * 32 + l32;
+                            const bf16x8 bt =
+                                as_bf16x8(*(const u32x4*)(sx + xrow * RB + (dma_slot<KC>(xrow, c) << 4)));
+                            acc1[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, bt, acc1[tb], 0, 0, 0);
+                        }
                     }
+                }
+                // lane: token 32 tb + l32, piece columns 256 fl + 32 wave + 8 g + 4 half + (0..3)
+                // from acc1[tb][4 g + (0..3)]
 #pragma unroll
-                    for (int b = 0; b < ND; ++b) {
-                        t.nt = b;
-                        f32x16 a1[1][1] = {{acc2[b]}};
-                        ffn_store_tile_direct<1, 1, FS_WAVES, OUT_COMBINE>(a1, t, nullptr, nullptr, cb, cin[b], C, d,
-                                                                           wave, l32, half);
+                for (int tb = 0; tb < TOKB; ++tb)
 #pragma unroll
-                        for (int i = 0; i < 16; ++i) acc2[b][i] = 0.f;
+                    for (int g = 0; g < 4; ++g) {
+                        const int f0 = fl * FS_NWG + wave * 32 + 8 * g + 4 * half;
+                        const f32x16& a = acc1[tb];
+                        *(uint2*)(hl + fs_h_slot(tb * 32 + l32, f0 >> 3, HRB) + (f0 & 7) * 2) =
+                            make_uint2(pack_bf16x2(fmaxf(a[4 * g + 0], 0.f), fmaxf(a[4 * g + 1], 0.f)),
+                                       pack_bf16x2(fmaxf(a[4 * g + 2], 0.f), fmaxf(a[4 * g + 3], 0.f)));
+                    }
+            }
+            // phase 2: every output block takes the piece's part of its sum
+#pragma unroll
+            for (int b = 0; b < ND; ++b) {
+                for (int kf = 0; kf < NKH; ++kf) {
+                    const char* sw = next_chunk();
+#pragma unroll
+                    for (int st = 0; st < KS; ++st) {
+                        const int c = half * KS + st;
+                        const bf16x8 wa = as_bf16x8(*(const u32x4*)(sw + r * RB + (dma_slot<KC>(r, c) << 4)));
+#pragma unroll
+                        for (int tb = 0; tb < TOKB; ++tb) {
+                            const bf16x8 bt =
+                                as_bf16x8(*(const u32x4*)(hl + fs_h_slot(tb * 32 + l32, kf * NCOL + c, HRB)));
+                            acc2[b][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, bt, acc2[b][tb], 0, 0, 0);
+                        }
                     }
                 }
             }
+        }
+        // the combine of every block
+        FfnTile t = decode_tile(jt * G + slot, ttab, 1, TOK);
+        CombineInputs<TOKB, 1> cin;
+        combine_load_tokens(cin, t, cb, C, l32);
+#pragma unroll
+        for (int b = 0; b < ND; ++b) {
+            t.nt = b;
+            combine_load_rows(cin, cb, d, b * FS_NWG + wave * 32, half);
+            f32x16 ab[1][TOKB];
+#pragma unroll
+            for (int tb = 0; tb < TOKB; ++tb) ab[0][tb] = acc2[b][tb];
+            ffn_store_tile_direct<TOKB, 1, FS_WAVES, OUT_COMBINE>(ab, t, nullptr, nullptr, cb, cin, C, d, wave, l32,
+                                                                  half);
+#pragma unroll
+            for (int tb = 0; tb < TOKB; ++tb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc2[b][tb][i] = 0.f;
         }
     }
     wait_copies<0>();   // the clamped copies past the last chunk land before the workgroup ends
@@ -1335,38 +1343,53 @@ hipError_t launch_expert_gemm_dma_t(const bf16_t* A, const bf16_t* W, const int3
 
 int ffn_token_tile(int C) { return C > 64 ? 128 : (C > 32 ? 64 : 32); }
 
-bool ffn_fused_small(int C, int d, int d_ff) {
-    return C >= 1 && C <= FS_TOK && d % FS_NWG == 0 && d <= FS_MAXND * FS_NWG && d_ff % FS_NWG == 0;
+bool ffn_fused_ok(int C, int d, int d_ff) {
+    return C >= 1 && C <= 64 && d % FS_NWG == 0 && d <= FS_MAXND * FS_NWG && d_ff % FS_NWG == 0;
 }
 
-template <int ND>
+template <int ND, int TOKB>
 static hipError_t launch_expert_ffn_fused_t(const bf16_t* x, uint32_t x_bytes, const int32_t* slot_token,
                                             const bf16_t* w1, const bf16_t* w2, const int32_t* pre, const int4* ttab,
                                             const FfnCombine& cb, int E, int C, int d_ff, hipStream_t s) {
     int64_t grid = std::min<int64_t>((int64_t)device_cus(), ((int64_t)E + 7) / 8 * 8);   // one workgroup per CU
     grid = std::max<int64_t>(8, grid / 8 * 8);
-    // pieces of two 256-column blocks of d_ff where they divide it (fewer token-row reads), else one
-    if ((d_ff / FS_NWG) % 2 == 0)
-        hipLaunchKernelGGL((expert_ffn_fused<64, 3, 2, ND>), dim3((unsigned)grid), dim3(64 * FS_WAVES), 0, s, x,
-                           x_bytes, slot_token, w1, w2, pre, ttab, cb, E, C, d_ff);
-    else
-        hipLaunchKernelGGL((expert_ffn_fused<64, 4, 1, ND>), dim3((unsigned)grid), dim3(64 * FS_WAVES), 0, s, x,
-                           x_bytes, slot_token, w1, w2, pre, ttab, cb, E, C, d_ff);
+    // 32-row tiles: pieces of two 256-column blocks of d_ff where they divide
+    // it (fewer token-row reads), else one with a stage more; 64-row tiles:
+    // pieces of one block, three stages
+    if constexpr (TOKB == 1) {
+        if ((d_ff / FS_NWG) % 2 == 0) {
+            hipLaunchKernelGGL((expert_ffn_fused<64, 3, 2, ND, TOKB>), dim3((unsigned)grid), dim3(64 * FS_WAVES), 0, s,
+                               x, x_bytes, slot_token, w1, w2, pre, ttab, cb, E, C, d_ff);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((expert_ffn_fused<64, TOKB == 1 ? 4 : 3, 1, ND, TOKB>), dim3((unsigned)grid),
+                       dim3(64 * FS_WAVES), 0, s, x, x_bytes, slot_token, w1, w2, pre, ttab, cb, E, C, d_ff);
     return hipGetLastError();
+}
+
+template <int TOKB>
+static hipError_t launch_expert_ffn_fused_nd(const bf16_t* x, uint32_t x_bytes, const int32_t* slot_token,
+                                             const bf16_t* w1, const bf16_t* w2, const int32_t* pre, const int4* ttab,
+                                             const FfnCombine& cb, int E, int C, int d, int d_ff, hipStream_t s) {
+    switch (d / FS_NWG) {
+        case 1: return launch_expert_ffn_fused_t<1, TOKB>(x, x_bytes, slot_token, w1, w2, pre, ttab, cb, E, C, d_ff, s);
+        case 2: return launch_expert_ffn_fused_t<2, TOKB>(x, x_bytes, slot_token, w1, w2, pre, ttab, cb, E, C, d_ff, s);
+        case 3: return launch_expert_ffn_fused_t<3, TOKB>(x, x_bytes, slot_token, w1, w2, pre, ttab, cb, E, C, d_ff, s);
+        default: return launch_expert_ffn_fused_t<4, TOKB>(x, x_bytes, slot_token, w1, w2, pre, ttab, cb, E, C, d_ff, s);
+    }
 }
 
 hipError_t launch_expert_ffn_fused(const bf16_t* x, int64_t T, const int32_t* slot_token, const bf16_t* w1,
                                    const bf16_t* w2, const int32_t* pre, const int4* ttab, const FfnCombine& cb,
                                    int E, int C, int d, int d_ff, hipStream_t s) {
-    if (!ffn_fused_small(C, d, d_ff) || T < 1) return hipErrorInvalidValue;
+    if (!ffn_fused_ok(C, d, d_ff) || T < 1) return hipErrorInvalidValue;
     const int64_t x_bytes = T * d * 2;
     if (x_bytes + 2 * (int64_t)d + 256 >= (int64_t(1) << 32)) return hipErrorInvalidValue;
-    switch (d / FS_NWG) {
-        case 1: return launch_expert_ffn_fused_t<1>(x, (uint32_t)x_bytes, slot_token, w1, w2, pre, ttab, cb, E, C, d_ff, s);
-        case 2: return launch_expert_ffn_fused_t<2>(x, (uint32_t)x_bytes, slot_token, w1, w2, pre, ttab, cb, E, C, d_ff, s);
-        case 3: return launch_expert_ffn_fused_t<3>(x, (uint32_t)x_bytes, slot_token, w1, w2, pre, ttab, cb, E, C, d_ff, s);
-        default: return launch_expert_ffn_fused_t<4>(x, (uint32_t)x_bytes, slot_token, w1, w2, pre, ttab, cb, E, C, d_ff, s);
-    }
+    // the tile list holds one ffn_token_tile(C)-row tile per non-empty expert
+    if (ffn_token_tile(C) == 32)
+        return launch_expert_ffn_fused_nd<1>(x, (uint32_t)x_bytes, slot_token, w1, w2, pre, ttab, cb, E, C, d, d_ff, s);
+    return launch_expert_ffn_fused_nd<2>(x, (uint32_t)x_bytes, slot_token, w1, w2, pre, ttab, cb, E, C, d, d_ff, s);
 }
 
 size_t ffn_tile_table_entries(int E, int C) {

@@ -93,9 +93,9 @@ hipError_t launch_expert_gemm1_gather(const bf16_t* x, int64_t T, const int32_t*
 // Both expert products and the combine (k = 1) in one kernel, the hidden
 // activation kept on chip: token rows gathered from x as in
 // launch_expert_gemm1_gather, output as in launch_expert_gemm2_combine, no H.
-// Needs ffn_fused_small(C, d, d_ff): C <= 32, d a multiple of 256 up to 1024,
-// d_ff a multiple of 256.
-bool ffn_fused_small(int C, int d, int d_ff);
+// Needs ffn_fused_ok(C, d, d_ff): C <= 64 (one token tile per expert), d a
+// multiple of 256 up to 1024, d_ff a multiple of 256.
+bool ffn_fused_ok(int C, int d, int d_ff);
 hipError_t launch_expert_ffn_fused(const bf16_t* x, int64_t T, const int32_t* slot_token, const bf16_t* w1,
                                    const bf16_t* w2, const int32_t* pre, const int4* ttab, const FfnCombine& cb,
                                    int E, int C, int d, int d_ff, hipStream_t s);

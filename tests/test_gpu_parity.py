@@ -463,12 +463,17 @@ def test_edge_shapes(shape):
     (77, 768, 512, 64, 1.0, 0.0),       # C = 2, ragged T, most experts empty
     (2003, 1024, 1024, 64, 0.5, 0.0),   # C = 16 at the many-small-experts widths, capacity factor 0.5
     (1500, 512, 2048, 64, 1.0, 0.0),    # C = 24, d_ff = 2048: four pieces of H
+    (4000, 256, 512, 64, 1.0, 0.0),     # C = 63: one 64-row tile per expert
+    (2100, 512, 512, 64, 1.0, 0.0),     # C = 33: 64-row tiles, at most 33 rows each
+    (3001, 768, 768, 64, 1.25, 2.0),    # C = 59, ragged T, hot expert 0, odd d_ff blocks
+    (4096, 1024, 256, 64, 1.0, 0.0),    # C = 64 at d = 1024: the most accumulators
 ])
 def test_fused_small_capacity(shape):
-    """At most 32 buffer rows per expert (d a multiple of 256 up to 1024, d_ff
-    a multiple of 256): the timed path runs both expert products in one kernel
-    with the hidden activation on chip; branch and residual outputs against the
-    oracle, then the same layer with its intermediates kept (two kernels)."""
+    """At most 64 buffer rows per expert (d a multiple of 256 up to 1024,
+    d_ff a multiple of 256): the timed path runs both expert products in one
+    kernel over one 32- or 64-row token tile per expert with the hidden
+    activation on chip; branch and residual outputs against the oracle, then
+    the same layer with its intermediates kept (two kernels)."""
     T, d, F, E, c, bias0 = shape
     for residual in (False, True):
         say(f"fused small capacity {shape} residual={residual}")
@@ -479,7 +484,7 @@ def test_fused_small_capacity(shape):
         finally:
             names = [n for n, _ in sw.switch_profile_collect()]
             sw.switch_profile_enable(False)
-        assert D.C <= 32
+        assert D.C <= 64
         assert "expert_ffn_fused" in names and "expert_gemm1" not in names, names
         check_small_layer(D, t, residual=residual)
     D2, t2 = small_layer(T, d, F, E, c, seed=hash(shape) % 1000, bias0=bias0, residual=True, inspect=True)
