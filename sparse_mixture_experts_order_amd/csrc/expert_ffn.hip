@@ -1420,14 +1420,15 @@ hipError_t launch_ffn_tile_lists(const FfnTileLists& L, int n, hipStream_t s) {
 // the wider one on a tie (fewer, longer weight streams per workgroup); every
 // expert's token tiles count as full.  E.g. at 128 experts, N = 768 takes 384
 // columns (two tiles per expert, one round); N = 3072 and N = 4096 take 512.
-// `narrow` restricts the choice to one 32-row block per wave (256 or 192).
-static int dma_tile_width(int E, int C, int N, bool narrow = false) {
+// `narrow` restricts the choice to one 32-row block per wave: 256 or 192
+// columns (8 or 6 waves), or 384 (12 waves) where `wide12`.
+static int dma_tile_width(int E, int C, int N, bool narrow = false, bool wide12 = false) {
     const int64_t tok_tiles = (int64_t)E * ((C + 127) / 128);
     const int64_t grid = device_cus();
     int best = 0;
     int64_t best_cost = 0;
     for (const int nwg : {512, 384, 256, 192}) {
-        if (narrow && nwg > 256) continue;
+        if (narrow && nwg > 256 && !(wide12 && nwg == 384)) continue;
         const int64_t tiles = tok_tiles * ((N + nwg - 1) / nwg);
         const int64_t cost = (tiles + grid - 1) / grid * nwg;
         if (best == 0 || cost < best_cost) { best = nwg; best_cost = cost; }
@@ -1487,6 +1488,13 @@ static hipError_t launch_expert_gemm(const bf16_t* A, const bf16_t* W, const int
     if constexpr (MODE == OUT_COMBINE) {
         // one 32-row block per wave: the epilogue's residual runs fit in registers
         if (C <= 64) return hipErrorInvalidValue;   // the fused combine needs the direct-to-LDS kernel
+        // 384 columns on 12 waves (three per SIMD, two stages) where experts
+        // hold several token tiles: each tile's H rows are read by half as
+        // many column tiles (measured faster there, slower with one token
+        // tile per expert)
+        if (dma_tile_width(E, C, N, true, C > 128) == 384)
+            return launch_expert_gemm_dma_t<4, 1, 12, MODE, 2, 64>(A, W, pre, ttab, out, mask, cb, E, C, K, N, s, a_rows,
+                                                                   a_bytes);
         if (dma_tile_width(E, C, N, true) == 256)
             return launch_expert_gemm_dma_t<4, 1, 8, MODE, 3, 64>(A, W, pre, ttab, out, mask, cb, E, C, K, N, s, a_rows, a_bytes);
         return launch_expert_gemm_dma_t<4, 1, 6, MODE, 3, 64>(A, W, pre, ttab, out, mask, cb, E, C, K, N, s, a_rows, a_bytes);

@@ -444,6 +444,7 @@ def check_small_layer(D, t, residual=True):
     (2000, 64, 128, 16, 4.5, 0.0),     # C = 563 > 512: five 128-row tiles, the last short
     (1500, 128, 256, 8, 1.2, 0.0),     # C = 225: two 128-row tiles per expert
     (2100, 192, 320, 8, 1.1, 0.0),     # C = 289: three 128-row tiles, the last short
+    (12800, 768, 256, 64, 1.0, 0.0),   # C = 200: two 128-row tiles, the second GEMM on 384 columns
 ])
 def test_edge_shapes(shape):
     T, d, F, E, c, bias0 = shape
