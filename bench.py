@@ -43,8 +43,10 @@ def log(*a):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    # the clocks take about 30 ms of this load to settle (0.327 ms per step
+    # after 10 warm-up steps, 0.310 after 100, at the Switch-Base shape)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--config", type=int, default=2, help="layer configuration 1..5 (2 = Switch-Base shape)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-variants", action="store_true",
@@ -651,8 +653,8 @@ def main():
         print(json.dumps(main_res))
         return
     log("standalone dispatch / combine")
-    main_res.update(measure_standalone(sw, torch, cfg, dev, t, C, A, stream, min(args.steps, 20),
-                                       min(args.warmup, 5)))
+    main_res.update(measure_standalone(sw, torch, cfg, dev, t, C, A, stream, min(args.steps, 50),
+                                       min(args.warmup, 50)))
     del t
 
     result = {
@@ -681,7 +683,7 @@ def main():
 
     if not args.no_variants:
         log("variants")
-        result["variants"] = time_variants(sw, torch, cfg, dev, stream, min(args.steps, 20), min(args.warmup, 5))
+        result["variants"] = time_variants(sw, torch, cfg, dev, stream, min(args.steps, 50), min(args.warmup, 50))
     log("mfma ceiling")
     result["measured_ceilings"] = {"bf16_gemm": mfma_ceiling(torch, stream)}
 
@@ -706,9 +708,9 @@ def main():
             log(f"per-config inputs {c2.name}")
             _, dv = device_inputs(c2, torch)
             log(f"per-config layer {c2.name}")
-            r, tt, Cc, Ac = measure_layer(sw, torch, c2, dv, stream, min(args.steps, 20), min(args.warmup, 5))
-            r.update(measure_standalone(sw, torch, c2, dv, tt, Cc, Ac, stream, min(args.steps, 20),
-                                        min(args.warmup, 5)))
+            r, tt, Cc, Ac = measure_layer(sw, torch, c2, dv, stream, min(args.steps, 50), min(args.warmup, 50))
+            r.update(measure_standalone(sw, torch, c2, dv, tt, Cc, Ac, stream, min(args.steps, 50),
+                                        min(args.warmup, 50)))
             per[c2.name] = r
             del tt, dv
             torch.cuda.empty_cache()

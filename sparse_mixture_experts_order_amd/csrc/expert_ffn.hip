@@ -1500,6 +1500,13 @@ static hipError_t launch_expert_gemm(const bf16_t* A, const bf16_t* W, const int
         return launch_expert_gemm_dma_t<4, 1, 6, MODE, 3, 64>(A, W, pre, ttab, out, mask, cb, E, C, K, N, s, a_rows, a_bytes);
     } else {
         if (C > 64) {
+            // the first GEMM with one 128-row token tile per expert: 256
+            // columns and three stages where the cost model allows them
+            // (measured faster there than 512 columns and two stages; slower
+            // with several token tiles per expert)
+            if (MODE == OUT_RELU_BF16 && C <= 128 && dma_tile_width(E, C, N, true) == 256)
+                return launch_expert_gemm_dma_t<4, 1, 8, MODE, 3, 64>(A, W, pre, ttab, out, mask, cb, E, C, K, N, s,
+                                                                      a_rows, a_bytes);
             switch (dma_tile_width(E, C, N)) {
                 case 512:
                     return launch_expert_gemm_dma_t<4, 2, 8, MODE, 2, 64>(A, W, pre, ttab, out, mask, cb, E, C, K, N,
