@@ -492,6 +492,53 @@ def test_fused_small_capacity(shape):
     check_small_layer(D2, t2, residual=True)
 
 
+@pytest.mark.parametrize("shape", [
+    (3000, 256, 512, 64, 1.0),    # C = 47: the fused FFN writes y from its epilogue
+    (4096, 256, 512, 16, 1.0),    # C = 256: the two expert GEMMs, y from the second
+])
+def test_layer_y_without_buf(shape):
+    """y [E, C, d] asked for with no buf or slot_token kept: the token rows are
+    still gathered from x and the combine fused, and y's kept rows hold each
+    token's expert output (ungated) against the oracle; out in branch mode."""
+    T, d, F, E, c = shape
+    cfg = workloads.custom_config(T, d, F, E, c, index=2000 + T)
+    inp = workloads.make_layer_inputs(cfg)
+    x, w_r, b_r = bits_to_dev(inp.x_bits), f32_dev(inp.w_r), f32_dev(inp.b_r)
+    w1, w2 = bits_to_dev(inp.w1_bits), bits_to_dev(inp.w2_bits)
+    C = so.capacity(T, E, c)
+    t = sw.layer_tensors(T, d, F, E, C)
+    t["y"] = torch.empty((E, C, d), dtype=torch.float32, device="cuda")
+    for k, v in t.items():
+        if k != "ws":
+            v.view(torch.uint8).fill_(0xFF)
+    args = sw.make_layer_args(x, w_r, b_r, w1, w2, t, T, d, F, E, C, cfg.alpha, residual=False)
+    say(f"y without buf {shape} C={C}")
+    sw.switch_profile_enable(True)
+    try:
+        sw.switch_layer_fwd(args, t["ws"])
+        torch.cuda.synchronize()
+    finally:
+        names = [n for n, _ in sw.switch_profile_collect()]
+        sw.switch_profile_enable(False)
+    assert ("expert_ffn_fused" in names) == (C <= 64), names
+    z = so.router_logits(inp.x, inp.w_r, inp.b_r)
+    r = so.softmax_top1(z)
+    e_dev = t["expert"].cpu().numpy()
+    near = top2_margin(z) <= MARGIN
+    np.testing.assert_array_equal(e_dev[~near], r.expert[~near])
+    e_res = np.where(near, e_dev, r.expert)
+    sl = so.slot_scan(e_res, E, C)
+    np.testing.assert_array_equal(t["position"].cpu().numpy(), sl.position)
+    kept = np.flatnonzero(sl.keep)
+    gate = r.p[np.arange(T), e_res]
+    ref_y = oracle_branch_rows(inp, kept, e_res, np.ones(T))
+    y = t["y"].cpu().numpy()
+    assert_branch_close(y[e_res[kept], sl.position[kept]], ref_y, f"y {shape}")
+    ob = dev_bits(t["out"])
+    assert np.all(ob[~sl.keep] == 0)
+    assert_branch_close(workloads.bf16_bits_to_f32(ob[kept]), gate[kept, None] * ref_y, f"out {shape}")
+
+
 def test_zero_capacity_and_empty_batch():
     D, t = small_layer(256, 64, 128, 4, 0.0, seed=3)
     assert D.C == 0
