@@ -60,11 +60,18 @@ def oracle_branch_topk(inp, tokens, expert, gate, keep):
 _CACHE = {}
 
 
+# extra layer shapes by name: (T, d, d_ff, E, c)
+CUSTOM = {"g64": (4096, 256, 512, 64, 1.0)}   # 4 groups of 1024 x 16 rows: 64 rows per expert, the fused FFN
+
+
 def inputs(ci):
     """A config's inputs, generated once per session (the 2048-expert config
     without its expert weights: only its routing and dispatch are tested here)."""
     if ci not in _CACHE:
-        _CACHE[ci] = DeviceInputs(workloads.CONFIGS[ci], with_experts=ci != 5)
+        if ci in CUSTOM:
+            _CACHE[ci] = DeviceInputs(workloads.custom_config(*CUSTOM[ci], index=3000))
+        else:
+            _CACHE[ci] = DeviceInputs(workloads.CONFIGS[ci], with_experts=ci != 5)
     return _CACHE[ci]
 
 
@@ -350,7 +357,7 @@ def test_layer_ex_end_to_end(ci, k, G, priority):
 
 
 # (config, k, group, priority) of the layer with no buf, slot_token or y kept
-NO_BUF_CASES = [(2, 2, 0, 0), (2, 1, 2048, 0), (3, 2, 0, 1), (4, 2, 8192, 0)]
+NO_BUF_CASES = [(2, 2, 0, 0), (2, 1, 2048, 0), (3, 2, 0, 1), (4, 2, 8192, 0), ("g64", 1, 1024, 0)]
 
 
 @pytest.mark.parametrize("ci,k,G,priority", NO_BUF_CASES)
@@ -366,7 +373,17 @@ def test_layer_ex_no_buf_branch(ci, k, G, priority):
     C = so.group_capacity(G or T, E, cfg.c, k)
     pr = "rank" if priority else "token"
     say(f"layer_ex no-buf cfg{ci} k={k} G={G} C={C} {pr}: run")
-    t = run_layer_ex(D, k, G, C, priority, residual=False, inspect=False)
+    sw.switch_profile_enable(True)
+    try:
+        t = run_layer_ex(D, k, G, C, priority, residual=False, inspect=False)
+    finally:
+        names = [n for n, _ in sw.switch_profile_collect()]
+        sw.switch_profile_enable(False)
+    # k = 1 with at most 64 buffer rows per expert (d, d_ff multiples of 256,
+    # d <= 1024): both expert products in one kernel
+    rows = ngroups(T, G) * C
+    fused = k == 1 and rows <= 64 and cfg.d % 256 == 0 and cfg.d <= 1024 and cfg.d_ff % 256 == 0
+    assert ("expert_ffn_fused" in names) == fused, names
     r = so.softmax_topk(D.z, k)
     near = topk_near(D.z, k)
     e_dev = t["expert"].cpu().numpy().reshape(T, k)
