@@ -313,6 +313,7 @@ struct FfnArgs {
     // token rows gathered by the first GEMM from x [x_tokens, d] through a_rows (= slot_token); buf unused
     const bf16_t* x_src = nullptr; int64_t x_tokens = 0; const int32_t* a_rows = nullptr;
     bool tiles_ready = false;   // the token-tile list in the workspace was built by the dispatch step
+    int64_t assignments = 0;    // T k of the layer (0: unknown): T k / E rows per expert expected
 };
 
 switch_status validate_ffn(const FfnArgs& a, const void* ws, size_t ws_bytes) {
@@ -356,15 +357,17 @@ switch_status run_ffn(const FfnArgs& a, void* ws, hipStream_t s) {
                                        a.d_ff, s));
         return SWITCH_OK;
     }
+    const int fill = a.assignments > 0 ? (int)std::min<int64_t>((a.assignments + a.E - 1) / a.E, a.C) : 0;
     if (a.a_rows)
         LAUNCH(K_GEMM1, "expert_gemm1", s,
                launch_expert_gemm1_gather(a.x_src, a.x_tokens, a.a_rows, a.w1, pre, ttab, h, a.E, a.C, a.d, a.d_ff,
-                                          s));
+                                          s, fill));
     else
-        LAUNCH(K_GEMM1, "expert_gemm1", s, launch_expert_gemm1(a.buf, a.w1, pre, ttab, h, a.E, a.C, a.d, a.d_ff, s));
+        LAUNCH(K_GEMM1, "expert_gemm1", s,
+               launch_expert_gemm1(a.buf, a.w1, pre, ttab, h, a.E, a.C, a.d, a.d_ff, s, fill));
     if (a.cb)
         LAUNCH(K_GEMM2, "expert_gemm2", s,
-               launch_expert_gemm2_combine(h, a.w2, pre, ttab, *a.cb, a.E, a.C, a.d, a.d_ff, s));
+               launch_expert_gemm2_combine(h, a.w2, pre, ttab, *a.cb, a.E, a.C, a.d, a.d_ff, s, fill));
     else
         LAUNCH(K_GEMM2, "expert_gemm2", s, launch_expert_gemm2(h, a.w2, pre, ttab, a.y, a.E, a.C, a.d, a.d_ff, s));
     return SWITCH_OK;
@@ -954,6 +957,7 @@ switch_status switch_layer_fwd(const switch_layer_args* la, void* ws, size_t ws_
     DispatchArgs da{L.x, L.expert, L.T, L.d, L.E, L.C, L.position, L.keep, L.counts, L.accepted, slot_token, buf,
                     k, G, L.priority, slot, acc_total};
     FfnArgs fa{buf, filled, L.w1, L.w2, L.E, rows, L.d, L.d_ff, y, L.h};
+    fa.assignments = L.T * k;
     // k = 1 with 128-row token tiles: the second GEMM writes the kept tokens'
     // output rows (and y only when asked for), gather the dropped ones, and
     // there is no combine pass

@@ -1475,7 +1475,11 @@ template <int MODE>
 static hipError_t launch_expert_gemm(const bf16_t* A, const bf16_t* W, const int32_t* pre, const int4* ttab, void* out,
                                      const bf16_t* mask, int E, int C, int K, int N, hipStream_t s,
                                      const FfnCombine& cb = FfnCombine{}, const int32_t* a_rows = nullptr,
-                                     uint32_t a_bytes = 0, bool forward = false) {
+                                     uint32_t a_bytes = 0, bool forward = false, int fill = 0) {
+    // rows an expert is expected to fill (the tile shapes below depend on how
+    // many 128-row token tiles it holds; the capacity alone overstates that
+    // when most slots stay empty)
+    const int rows = fill > 0 ? std::min(fill, C) : C;
     // the token tile must be ffn_token_tile(C) rows: the prefix kernel lists tiles of that size
     if (C <= 64 && forward) {
         if (C <= 32)
@@ -1492,7 +1496,7 @@ static hipError_t launch_expert_gemm(const bf16_t* A, const bf16_t* W, const int
         // hold several token tiles: each tile's H rows are read by half as
         // many column tiles (measured faster there, slower with one token
         // tile per expert)
-        if (dma_tile_width(E, C, N, true, C > 128) == 384)
+        if (dma_tile_width(E, C, N, true, rows > 128) == 384)
             return launch_expert_gemm_dma_t<4, 1, 12, MODE, 2, 64>(A, W, pre, ttab, out, mask, cb, E, C, K, N, s, a_rows,
                                                                    a_bytes);
         if (dma_tile_width(E, C, N, true) == 256)
@@ -1504,7 +1508,7 @@ static hipError_t launch_expert_gemm(const bf16_t* A, const bf16_t* W, const int
             // columns and three stages where the cost model allows them
             // (measured faster there than 512 columns and two stages; slower
             // with several token tiles per expert)
-            if (MODE == OUT_RELU_BF16 && C <= 128 && dma_tile_width(E, C, N, true) == 256)
+            if (MODE == OUT_RELU_BF16 && rows <= 128 && dma_tile_width(E, C, N, true) == 256)
                 return launch_expert_gemm_dma_t<4, 1, 8, MODE, 3, 64>(A, W, pre, ttab, out, mask, cb, E, C, K, N, s,
                                                                       a_rows, a_bytes);
             switch (dma_tile_width(E, C, N)) {
@@ -1566,17 +1570,17 @@ static hipError_t launch_expert_gemm_kmajor(const bf16_t* A, const bf16_t* W, co
 }
 
 hipError_t launch_expert_gemm1(const bf16_t* buf, const bf16_t* w1, const int32_t* pre, const int4* ttab, bf16_t* h,
-                               int E, int C, int d, int d_ff, hipStream_t s) {
+                               int E, int C, int d, int d_ff, hipStream_t s, int fill) {
     return launch_expert_gemm<OUT_RELU_BF16>(buf, w1, pre, ttab, h, nullptr, E, C, d, d_ff, s, FfnCombine{}, nullptr,
-                                             0, true);
+                                             0, true, fill);
 }
 
 hipError_t launch_expert_gemm1_gather(const bf16_t* x, int64_t T, const int32_t* slot_token, const bf16_t* w1,
                                       const int32_t* pre, const int4* ttab, bf16_t* h, int E, int C, int d, int d_ff,
-                                      hipStream_t s) {
+                                      hipStream_t s, int fill) {
     if (!ffn_rows_fused(C) || T * d * 2 + 2 * (int64_t)d + 256 >= (int64_t(1) << 32)) return hipErrorInvalidValue;
     return launch_expert_gemm<OUT_RELU_BF16>(x, w1, pre, ttab, h, nullptr, E, C, d, d_ff, s, FfnCombine{}, slot_token,
-                                             (uint32_t)(T * d * 2), true);
+                                             (uint32_t)(T * d * 2), true, fill);
 }
 
 hipError_t launch_expert_gemm2(const bf16_t* h, const bf16_t* w2, const int32_t* pre, const int4* ttab, float* y,
@@ -1588,9 +1592,10 @@ bool ffn_wide_tiles(int C) { return C > 64; }
 bool ffn_rows_fused(int C) { return C >= 1; }
 
 hipError_t launch_expert_gemm2_combine(const bf16_t* h, const bf16_t* w2, const int32_t* pre, const int4* ttab,
-                                       const FfnCombine& cb, int E, int C, int d, int d_ff, hipStream_t s) {
+                                       const FfnCombine& cb, int E, int C, int d, int d_ff, hipStream_t s, int fill) {
     if (!ffn_rows_fused(C)) return hipErrorInvalidValue;
-    return launch_expert_gemm<OUT_COMBINE>(h, w2, pre, ttab, nullptr, nullptr, E, C, d_ff, d, s, cb, nullptr, 0, true);
+    return launch_expert_gemm<OUT_COMBINE>(h, w2, pre, ttab, nullptr, nullptr, E, C, d_ff, d, s, cb, nullptr, 0, true,
+                                           fill);
 }
 
 hipError_t launch_grouped_gemm_kmajor_f32(const bf16_t* A, const bf16_t* W, const int32_t* pre, const int4* ttab,

@@ -60,8 +60,10 @@ struct FfnTileLists {
     FfnTileListSpec list[kMaxTileLists]; int E;
 };
 hipError_t launch_ffn_tile_lists(const FfnTileLists& L, int n, hipStream_t s);
+// fill (the forward's products): the rows each expert is expected to fill,
+// e.g. T k / E, which picks the tile shapes; 0: C
 hipError_t launch_expert_gemm1(const bf16_t* buf, const bf16_t* w1, const int32_t* pre, const int4* ttab, bf16_t* h,
-                               int E, int C, int d, int d_ff, hipStream_t s);
+                               int E, int C, int d, int d_ff, hipStream_t s, int fill = 0);
 hipError_t launch_expert_gemm2(const bf16_t* h, const bf16_t* w2, const int32_t* pre, const int4* ttab, float* y,
                                int E, int C, int d, int d_ff, hipStream_t s);
 // The second expert GEMM with the combine (k = 1) in its epilogue: buffer row
@@ -89,7 +91,7 @@ constexpr int kRowMapPad = 128;
 // entries past slot_token[E * C - 1].
 hipError_t launch_expert_gemm1_gather(const bf16_t* x, int64_t T, const int32_t* slot_token, const bf16_t* w1,
                                       const int32_t* pre, const int4* ttab, bf16_t* h, int E, int C, int d, int d_ff,
-                                      hipStream_t s);
+                                      hipStream_t s, int fill = 0);
 // Both expert products and the combine (k = 1) in one kernel, the hidden
 // activation kept on chip: token rows gathered from x as in
 // launch_expert_gemm1_gather, output as in launch_expert_gemm2_combine, no H.
@@ -100,7 +102,7 @@ hipError_t launch_expert_ffn_fused(const bf16_t* x, int64_t T, const int32_t* sl
                                    const bf16_t* w2, const int32_t* pre, const int4* ttab, const FfnCombine& cb,
                                    int E, int C, int d, int d_ff, hipStream_t s);
 hipError_t launch_expert_gemm2_combine(const bf16_t* h, const bf16_t* w2, const int32_t* pre, const int4* ttab,
-                                       const FfnCombine& cb, int E, int C, int d, int d_ff, hipStream_t s);
+                                       const FfnCombine& cb, int E, int C, int d, int d_ff, hipStream_t s, int fill = 0);
 // the same kernel on other operands: out[e, r, n] = sum_k A[e, r, k] W[e, n, k]
 // for the rows listed in (pre, ttab), fp32 out
 hipError_t launch_grouped_gemm_f32(const bf16_t* A, const bf16_t* W, const int32_t* pre, const int4* ttab, float* out,
