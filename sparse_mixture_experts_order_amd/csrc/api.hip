@@ -115,9 +115,30 @@ size_t dispatch_ws(int64_t T, int32_t E, int32_t k, int64_t G) {
     if (!one) n += up((size_t)group_count(T, G) * E * sizeof(int32_t)) + up((size_t)E * sizeof(int32_t));
     return n;
 }
+// the expert FFN's workspace: H, the second GEMM's token-tile list
+// (ffn_token_tile(C) rows per tile), and room for the first GEMM's own list
+// when it takes taller tiles (ffn_gemm1_token_tile; never more entries)
 size_t ffn_ws(int32_t E, int32_t C, int32_t d_ff) {
-    return up((size_t)E * C * d_ff * sizeof(bf16_t)) + up((size_t)(E + 1) * sizeof(int32_t)) +
-           up(ffn_tile_table_entries(E, C) * sizeof(int4));
+    return up((size_t)E * C * d_ff * sizeof(bf16_t)) +
+           2 * (up((size_t)(E + 1) * sizeof(int32_t)) + up(ffn_tile_table_entries(E, C) * sizeof(int4)));
+}
+struct FfnSpace {
+    bf16_t* h; TileListOut l2, l1;   // l1.pre NULL: the first GEMM reads l2 too
+};
+FfnSpace carve_ffn(void* ws, int32_t E, int32_t C, int32_t d_ff, int fill) {
+    Carver c{(char*)ws};
+    FfnSpace f{};
+    f.h = c.take<bf16_t>((size_t)E * C * d_ff);
+    f.l2.pre = c.take<int32_t>((size_t)E + 1);
+    f.l2.tab = c.take<int4>(ffn_tile_table_entries(E, C));
+    f.l2.tok = ffn_token_tile(C);
+    const int tok1 = ffn_gemm1_token_tile(E, C, fill, d_ff);
+    if (tok1 != f.l2.tok) {
+        f.l1.pre = c.take<int32_t>((size_t)E + 1);
+        f.l1.tab = c.take<int4>(ffn_tile_table_entries(E, C));
+        f.l1.tok = tok1;
+    }
+    return f;
 }
 
 // ----------------------------------------------------------- validation
@@ -245,7 +266,7 @@ struct DispatchArgs {
     int32_t* slot = nullptr; int32_t* rows_total = nullptr;
     bf16_t* out_pass = nullptr; bool pass_residual = false;   // k = 1: dropped tokens' output rows (fused combine)
     bool no_buf = false;   // the first expert GEMM gathers the token rows itself: buf is not written
-    int32_t* tl_pre = nullptr; int4* tl_tab = nullptr;   // also build the expert GEMMs' token-tile list
+    TileListOut tl0, tl1;   // also build the expert GEMMs' token-tile lists (those with pre set)
     const AuxStatsArgs* aux = nullptr;                   // and the load-balancing statistics
     // the router's partial probability rows (prows per group), summed into prob_sum by the scan
     const float* parts = nullptr; int prows = 0; float* prob_sum = nullptr;
@@ -300,8 +321,7 @@ switch_status run_dispatch(const DispatchArgs& a, void* ws, hipStream_t s) {
     LAUNCH(K_GATHER, "gather", s,
            launch_gather(a.x, a.expert, tile_counts, group_base, one ? a.accepted : rows_total, N, a.d, a.E, a.k, G,
                          a.priority, tile, a.C, rows, a.position, a.keep, a.slot, a.slot_token,
-                         a.no_buf ? nullptr : a.buf, a.out_pass, a.pass_residual, a.tl_pre, a.tl_tab,
-                         ffn_token_tile(rows), a.aux, s));
+                         a.no_buf ? nullptr : a.buf, a.out_pass, a.pass_residual, a.tl0, a.tl1, a.aux, s));
     return SWITCH_OK;
 }
 
@@ -342,13 +362,21 @@ switch_status validate_ffn(const FfnArgs& a, const void* ws, size_t ws_bytes) {
 
 switch_status run_ffn(const FfnArgs& a, void* ws, hipStream_t s) {
     if (a.C == 0) return SWITCH_OK;
-    Carver c{(char*)ws};
-    bf16_t* h = c.take<bf16_t>((size_t)a.E * a.C * a.d_ff);
-    if (a.h) h = a.h;
-    int32_t* pre = c.take<int32_t>((size_t)a.E + 1);
-    int4* ttab = c.take<int4>(ffn_tile_table_entries(a.E, a.C));
-    if (!a.tiles_ready)
-        LAUNCH(K_FFN_TILES, "ffn_tile_prefix", s, launch_ffn_tile_prefix(a.accepted, a.E, a.C, pre, ttab, s));
+    const int fill = ffn_expected_fill(a.assignments, a.E, a.C);
+    const FfnSpace f = carve_ffn(ws, a.E, a.C, a.d_ff, fill);
+    bf16_t* h = a.h ? a.h : f.h;
+    int32_t* pre = f.l2.pre;
+    int4* ttab = f.l2.tab;
+    // the first GEMM's list: its own when it takes taller token tiles
+    const int32_t* pre1 = f.l1.pre ? f.l1.pre : pre;
+    const int4* ttab1 = f.l1.pre ? f.l1.tab : ttab;
+    if (!a.tiles_ready) {
+        FfnTileLists tl{};
+        tl.E = a.E;
+        tl.list[0] = FfnTileListSpec{a.accepted, nullptr, a.C, pre, ttab, f.l2.tok};
+        if (f.l1.pre) tl.list[1] = FfnTileListSpec{a.accepted, nullptr, a.C, f.l1.pre, f.l1.tab, f.l1.tok};
+        LAUNCH(K_FFN_TILES, "ffn_tile_prefix", s, launch_ffn_tile_lists(tl, f.l1.pre ? 2 : 1, s));
+    }
     // gathered token rows, the fused combine and no H asked for: at small
     // capacity both products run in one kernel with H on chip
     if (a.a_rows && a.cb && !a.h && ffn_fused_ok(a.C, a.d, a.d_ff)) {
@@ -357,19 +385,19 @@ switch_status run_ffn(const FfnArgs& a, void* ws, hipStream_t s) {
                                        a.d_ff, s));
         return SWITCH_OK;
     }
-    const int fill = a.assignments > 0 ? (int)std::min<int64_t>((a.assignments + a.E - 1) / a.E, a.C) : 0;
     if (a.a_rows)
         LAUNCH(K_GEMM1, "expert_gemm1", s,
-               launch_expert_gemm1_gather(a.x_src, a.x_tokens, a.a_rows, a.w1, pre, ttab, h, a.E, a.C, a.d, a.d_ff,
+               launch_expert_gemm1_gather(a.x_src, a.x_tokens, a.a_rows, a.w1, pre1, ttab1, h, a.E, a.C, a.d, a.d_ff,
                                           s, fill));
     else
         LAUNCH(K_GEMM1, "expert_gemm1", s,
-               launch_expert_gemm1(a.buf, a.w1, pre, ttab, h, a.E, a.C, a.d, a.d_ff, s, fill));
+               launch_expert_gemm1(a.buf, a.w1, pre1, ttab1, h, a.E, a.C, a.d, a.d_ff, s, fill));
     if (a.cb)
         LAUNCH(K_GEMM2, "expert_gemm2", s,
                launch_expert_gemm2_combine(h, a.w2, pre, ttab, *a.cb, a.E, a.C, a.d, a.d_ff, s, fill));
     else
-        LAUNCH(K_GEMM2, "expert_gemm2", s, launch_expert_gemm2(h, a.w2, pre, ttab, a.y, a.E, a.C, a.d, a.d_ff, s));
+        LAUNCH(K_GEMM2, "expert_gemm2", s,
+               launch_expert_gemm2(h, a.w2, pre, ttab, a.y, a.E, a.C, a.d, a.d_ff, s, fill));
     return SWITCH_OK;
 }
 
@@ -971,10 +999,9 @@ switch_status switch_layer_fwd(const switch_layer_args* la, void* ws, size_t ws_
     // the dispatch step's extra workgroup builds the expert GEMMs' token-tile
     // list (same workspace carve as run_ffn), so no tile-prefix launch
     if (rows > 0) {
-        Carver fc{ffn_space};
-        fc.take<bf16_t>((size_t)L.E * rows * L.d_ff);
-        da.tl_pre = fc.take<int32_t>((size_t)L.E + 1);
-        da.tl_tab = fc.take<int4>(ffn_tile_table_entries(L.E, rows));
+        const FfnSpace f = carve_ffn(ffn_space, L.E, rows, L.d_ff, ffn_expected_fill(fa.assignments, L.E, rows));
+        da.tl0 = f.l2;
+        da.tl1 = f.l1;
         fa.tiles_ready = true;
     }
     // buf and slot_token not kept: the first GEMM reads the token rows from x

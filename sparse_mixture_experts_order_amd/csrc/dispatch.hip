@@ -208,11 +208,12 @@ __global__ __launch_bounds__(256) void scan_offsets(int32_t* __restrict__ tile_c
 // With out_pass (k = 1, the combine done by the second expert GEMM) a dropped
 // token's output row is written here: its residual x row bit for bit, or zeros
 // without a residual.  With buf == NULL (the first expert GEMM gathers the
-// token rows from x itself) no rows are copied or zeroed.  With tl_pre one
-// extra (last) workgroup builds the expert GEMMs' token-tile list from the
-// filled rows per expert (ffn_tile_list, TOK = tl_tok), and with aux.prob_sum
-// one more computes the load-balancing statistics (aux_stats_block; counts
-// and prob_sum are final once the scan has run).
+// token rows from x itself) no rows are copied or zeroed.  Each token-tile
+// list asked for (tl0, tl1: the expert GEMMs' lists, built from the filled
+// rows per expert by ffn_tile_list) takes one extra workgroup at the end of
+// the grid, and with aux.prob_sum one more computes the load-balancing
+// statistics (aux_stats_block; counts and prob_sum are final once the scan
+// has run).
 constexpr int GATHER_TOK = 16, GATHER_ROWS = 16;
 
 __global__ __launch_bounds__(256) void gather(const bf16_t* __restrict__ x, const int32_t* __restrict__ expert,
@@ -223,13 +224,15 @@ __global__ __launch_bounds__(256) void gather(const bf16_t* __restrict__ x, cons
                                               int32_t* __restrict__ position, uint8_t* __restrict__ keep,
                                               int32_t* __restrict__ slot, int32_t* __restrict__ slot_token,
                                               bf16_t* __restrict__ buf, bf16_t* __restrict__ out_pass,
-                                              int pass_residual, int32_t* __restrict__ tl_pre,
-                                              int4* __restrict__ tl_tab, int tl_tok, const AuxStatsArgs aux) {
-    if (tl_pre && blockIdx.x == gridDim.x - 1) {   // the expert GEMMs' token-tile list
-        ffn_tile_list<256>(rows_filled, E, rows, tl_tok, tl_pre, tl_tab);
+                                              int pass_residual, const TileListOut tl0, const TileListOut tl1,
+                                              const AuxStatsArgs aux) {
+    const int nl = (tl0.pre ? 1 : 0) + (tl1.pre ? 1 : 0);
+    if ((int)blockIdx.x >= (int)gridDim.x - nl) {   // the expert GEMMs' token-tile lists
+        const TileListOut& t = ((int)blockIdx.x == (int)gridDim.x - 1 && tl0.pre) ? tl0 : tl1;
+        ffn_tile_list<256>(rows_filled, E, rows, t.tok, t.pre, t.tab);
         return;
     }
-    if (aux.prob_sum && blockIdx.x == gridDim.x - 1 - (tl_pre ? 1 : 0)) {   // the load-balancing statistics
+    if (aux.prob_sum && (int)blockIdx.x == (int)gridDim.x - 1 - nl) {   // the load-balancing statistics
         aux_stats_block<256>(aux);
         return;
     }
@@ -332,18 +335,17 @@ hipError_t launch_scan_offsets(int32_t* tile_counts, int ntiles, int tiles_per_g
 hipError_t launch_gather(const bf16_t* x, const int32_t* expert, const int32_t* offsets, const int32_t* group_base,
                          const int32_t* rows_filled, int N, int d, int E, int k, int G, int rank, int tile, int C,
                          int rows, int32_t* position, uint8_t* keep, int32_t* slot, int32_t* slot_token, bf16_t* buf,
-                         bf16_t* out_pass, bool pass_residual, int32_t* tl_pre, int4* tl_tab, int tl_tok,
+                         bf16_t* out_pass, bool pass_residual, const TileListOut& tl0, const TileListOut& tl1,
                          const AuxStatsArgs* aux, hipStream_t s) {
     const int ntok = (N + GATHER_TOK - 1) / GATHER_TOK;
     const int64_t nrows = buf ? (int64_t)E * rows : 0;
     const int nzero = (int)((nrows + GATHER_ROWS - 1) / GATHER_ROWS);
-    const int nlist = (tl_pre ? 1 : 0) + (aux ? 1 : 0);
+    const int nlist = (tl0.pre ? 1 : 0) + (tl1.pre ? 1 : 0) + (aux ? 1 : 0);
     if (ntok + nzero + nlist == 0) return hipSuccess;
     const AuxStatsArgs no_aux{};
     hipLaunchKernelGGL(gather, dim3(ntok + nzero + nlist), dim3(256), 0, s, x, expert, offsets, group_base, rows_filled, N, d,
                        E, k, std::max(G, 1), rank, tile, C, rows, ntok, position, keep, slot, slot_token, buf,
-                       k == 1 ? out_pass : nullptr, pass_residual ? 1 : 0, tl_pre, tl_tab, tl_tok,
-                       aux ? *aux : no_aux);
+                       k == 1 ? out_pass : nullptr, pass_residual ? 1 : 0, tl0, tl1, aux ? *aux : no_aux);
     return hipGetLastError();
 }
 

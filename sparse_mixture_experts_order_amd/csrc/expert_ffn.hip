@@ -329,6 +329,196 @@ __device__ __forceinline__ void ffn_store_tile_direct(f32x16 (&acc)[NBW][TOKB], 
     }
 }
 
+// v_permlane32_swap of rows 8-11 of half 0 with rows 4-7 of half 1 (and 24-27
+// with 20-23) in one 32 x 32 accumulator block: each lane then holds two runs
+// of 8 consecutive columns of its token.  The block is first copied into
+// vector registers (the asm operand), so the accumulators themselves can stay
+// in the accumulation registers through the K loop.
+__device__ __forceinline__ f32x16 ffn_swapped_runs(const f32x16& acc) {
+    f32x16 a = acc;
+    asm volatile("" : "+v"(a));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(a[8 * pr + i]),
+                                                             __float_as_uint(a[8 * pr + 4 + i]), false, false);
+            a[8 * pr + i] = __uint_as_float(sw[0]);
+            a[8 * pr + 4 + i] = __uint_as_float(sw[1]);
+        }
+    return a;
+}
+
+// Tall token tiles (the forward's products where experts fill more than one
+// 128-row tile): the waves split the tile two ways, wave w taking the token
+// blocks 2 i + (w & 1) (interleaved, so both halves have about as many valid
+// blocks) against weight rows 32 NBW (w >> 1) .. + 32 NBW - 1; a tile is
+// 16 NBW WAVES weight rows wide.  Its epilogues below take the wave's TBW
+// token blocks, acc[nb][i] holding block 2 i + tg.
+template <int TOKB, int NBW, int WAVES>
+constexpr int dma_tile_cols() {
+    return TOKB > 4 ? WAVES * 32 * NBW / 2 : WAVES * 32 * NBW;
+}
+
+// bf16(ReLU) output of tall token tiles, one accumulator block at a time (the
+// swap needs the block in vector registers, and all blocks do not fit there).
+template <int TBW, int NBW>
+__device__ __forceinline__ void ffn_store_tile_relu_tall(f32x16 (&acc)[NBW][TBW], const FfnTile& t, bf16_t* out,
+                                                         int C, int N, int n0, int tg, int l32, int half) {
+#pragma unroll
+    for (int i = 0; i < TBW; ++i) {
+        const int r = (2 * i + tg) * 32 + l32;
+        const size_t row = ((size_t)t.e * C + t.tok_base + r) * N;
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb) {
+            const f32x16 a = ffn_swapped_runs(acc[nb][i]);
+#pragma unroll
+            for (int run = 0; run < 2; ++run) {
+                const int n = n0 + nb * 32 + run * 16 + half * 8;
+                float v[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) v[j] = fmaxf(a[8 * run + j], 0.f);
+                const u32x4 o = u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                                      pack_bf16x2(v[6], v[7])};
+                if (r < t.nv && n < N) *(u32x4*)(out + row + n) = o;
+            }
+        }
+    }
+}
+
+// fp32 output of tall token tiles: buffer stores whose descriptor ends with
+// the tile's valid rows (out-of-range ones are dropped), TBW NBW 4 per wave.
+template <int TBW, int NBW>
+__device__ __forceinline__ void ffn_store_tile_f32_tall(const f32x16 (&acc)[NBW][TBW], const FfnTile& t, float* out,
+                                                        int C, int N, int n0, int tg, int l32, int half) {
+    const __amdgpu_buffer_rsrc_t rs =
+        buffer_rsrc_uniform(out + ((size_t)t.e * C + t.tok_base) * N, (uint32_t)max(t.nv, 0) * (uint32_t)N * 4u);
+#pragma unroll
+    for (int i = 0; i < TBW; ++i) {
+        const int r = (2 * i + tg) * 32 + l32;
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb) {
+            const f32x16& a = acc[nb][i];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int n = n0 + nb * 32 + q * 8 + half * 4;
+                const uint32_t off = (r < t.nv && n < N) ? (uint32_t)(r * N + n) * 4u : 0x80000000u;
+                const u32x4 v = u32x4{__float_as_uint(a[4 * q + 0]), __float_as_uint(a[4 * q + 1]),
+                                      __float_as_uint(a[4 * q + 2]), __float_as_uint(a[4 * q + 3])};
+                __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, 0);
+            }
+        }
+    }
+}
+
+// The combine epilogue of tall token tiles.  With the accumulators of up to
+// ten token blocks live, the residual runs of every block do not fit in the
+// registers as well, so the blocks go in groups of TG: the token of each row
+// is loaded for all blocks first, then each group's gates and residual runs
+// are loaded before the previous group's results are stored (a load issued
+// after a store waits for that store too), so the groups' loads overlap the
+// stores.  Same arithmetic as ffn_store_tile_direct's combine mode: one fp32
+// fma and one rounding per element, the output run replacing the residual run.
+template <int TBW, int NBW, int TG>
+__device__ __forceinline__ void ffn_store_tile_combine_tall(f32x16 (&acc)[NBW][TBW], const FfnTile& t,
+                                                            const FfnCombine& cb, int C, int N, int n0, int tg,
+                                                            int l32, int half) {
+    static_assert(TBW % TG == 0, "whole groups of token blocks");
+    constexpr int NG = TBW / TG;
+    int tok[TBW];
+#pragma unroll
+    for (int i = 0; i < TBW; ++i) {   // clamped addresses, selected after (no load under a branch)
+        const int r = (2 * i + tg) * 32 + l32;
+        const int v = cb.slot_token[(size_t)t.e * C + min(t.tok_base + r, C - 1)];
+        tok[i] = r < t.nv ? v : -1;
+    }
+    const bf16_t* res = cb.residual ? cb.residual : cb.out;
+    float g[2][TG];
+    u32x4 rr[2][TG][NBW][2];
+    auto load_group = [&](int gi, float (&gd)[TG], u32x4 (&dst)[TG][NBW][2]) {
+#pragma unroll
+        for (int j = 0; j < TG; ++j) {
+            const int tk = max(tok[gi * TG + j], 0);
+            gd[j] = cb.gate[tk];
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+                for (int run = 0; run < 2; ++run) {
+                    const int n = n0 + nb * 32 + run * 16 + half * 8;
+                    dst[j][nb][run] = *(const u32x4*)(res + (size_t)tk * N + min(n, N - 8));
+                }
+        }
+    };
+    load_group(0, g[0], rr[0]);
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+        const int cur = gi & 1;
+        if (gi + 1 < NG) load_group(gi + 1, g[cur ^ 1], rr[cur ^ 1]);
+#pragma unroll
+        for (int j = 0; j < TG; ++j) {
+            const int i = gi * TG + j;
+            const bool on = tok[i] >= 0;
+            const float gg = on ? g[cur][j] : 0.f;
+            // the group's blocks only (the accumulators of all blocks do not fit
+            // the vector registers the swap works in): lanes l and l ^ 32 hold
+            // the same token, so after swapping by whole pairs every lane holds
+            // two runs of 8 consecutive columns per 32-column block
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb) {
+                const f32x16 a = ffn_swapped_runs(acc[nb][i]);
+#pragma unroll
+                for (int run = 0; run < 2; ++run) {
+                    const int n = n0 + nb * 32 + run * 16 + half * 8;
+                    u32x4 rv = (on && cb.residual && n < N) ? rr[cur][j][nb][run] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float o0 = fmaf(gg, a[8 * run + 2 * q], bf16_to_f32(rv[q] & 0xffffu));
+                        const float o1 = fmaf(gg, a[8 * run + 2 * q + 1], bf16_to_f32(rv[q] >> 16));
+                        rv[q] = pack_bf16x2(o0, o1);
+                    }
+                    // made here in straight-line code, not inside the stores' branches
+                    asm volatile("" : "+v"(rv));
+                    rr[cur][j][nb][run] = rv;
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < TG; ++j) {
+            const int i = gi * TG + j;
+            if (tok[i] < 0) continue;
+            const size_t orow = (size_t)tok[i] * N;
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+                for (int run = 0; run < 2; ++run) {
+                    const int n = n0 + nb * 32 + run * 16 + half * 8;
+                    if (n < N) *(u32x4*)(cb.out + orow + n) = rr[cur][j][nb][run];
+                }
+        }
+        if (cb.y) {
+#pragma unroll
+            for (int j = 0; j < TG; ++j) {
+                const int i = gi * TG + j;
+                if (tok[i] < 0) continue;
+                const size_t row = ((size_t)t.e * C + t.tok_base + (2 * i + tg) * 32 + l32) * N;
+#pragma unroll
+                for (int nb = 0; nb < NBW; ++nb) {
+                    const f32x16 a = ffn_swapped_runs(acc[nb][i]);   // the runs' layout again
+#pragma unroll
+                    for (int run = 0; run < 2; ++run) {
+                        const int n = n0 + nb * 32 + run * 16 + half * 8;
+                        if (n >= N) continue;
+                        *(f32x4*)(cb.y + row + n) =
+                            f32x4{a[8 * run + 0], a[8 * run + 1], a[8 * run + 2], a[8 * run + 3]};
+                        *(f32x4*)(cb.y + row + n + 4) =
+                            f32x4{a[8 * run + 4], a[8 * run + 5], a[8 * run + 6], a[8 * run + 7]};
+                    }
+                }
+            }
+        }
+    }
+}
+
 // fp32 output as buffer stores: the descriptor ends with the tile's valid rows
 // and columns past N get an offset past it, so every lane issues every store
 // and a wave always issues exactly ffn_f32_stores<TOKB, NBW> of them (the next
@@ -681,7 +871,7 @@ __device__ __forceinline__ int dma_slot(int r, int c) {
 
 // With a_rows the token rows are gathered straight from A = x [T, K]: row s of
 // expert e is x[a_rows[e * C + s]] (a_bytes = T K 2, the descriptor's byte
-// count; a_rows has 128 entries of padding past E C).  The row map is read with uniform (scalar) loads when a tile starts,
+// count; a_rows has kRowMapPad entries of padding past E C).  The row map is read with uniform (scalar) loads when a tile starts,
 // so waiting for it never waits for the copies in flight; rows past the tile's
 // valid count point past the descriptor and read as zero.
 // With WKM the weights are stored K-major, [E, K, N] (the backward reads W1
@@ -706,7 +896,7 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
     static_assert(KC == 64 || KC == 32, "64- or 32-wide K chunks");
     static_assert(!AKM || WKM, "K-major token rows come with K-major weights");
     constexpr int TOK = 32 * TOKB;
-    constexpr int NWG = WAVES * 32 * NBW;
+    constexpr int NWG = dma_tile_cols<TOKB, NBW, WAVES>();
     constexpr int RB = KC * 2;                              // bytes per staged row
     constexpr int RPC = 1024 / RB;                          // rows per 1 KiB copy
     constexpr int NCOL = RB / 16;                           // 16-byte columns per row
@@ -720,6 +910,12 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
     constexpr int STAGE = W_STAGE + A_STAGE;
     constexpr int PER_CHUNK = WPW + APW;                    // copies per wave per chunk
     static_assert(S >= 2 && PER_CHUNK * (S - 1) < 64, "outstanding copies fit the counter");
+    // tall token tiles (more than four 32-row blocks): the forward's products
+    // where experts fill several 128-row tiles, one tile of up to 32 TOKB rows
+    // per expert instead
+    constexpr bool TALL = TOKB > 4;
+    static_assert(!TALL || (!WKM && !AKM && TOKB % 2 == 0 && WAVES % 2 == 0), "tall token tiles: row-major operands");
+    constexpr int TBW = TALL ? TOKB / 2 : TOKB;   // token blocks per wave
     __shared__ __attribute__((aligned(16))) char lds[S * STAGE];
 
     const int total = pre[E] * n_tiles;
@@ -733,6 +929,7 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int half = lane >> 5, l32 = lane & 31;
+    const int tg = wave & 1, wn = wave >> 1;   // tall tiles: token half and weight slice of this wave
 
     // lane offsets of the copies (row RPC q + lane / NCOL, swizzled 16-byte column)
     uint32_t wvo[WPW], avo[APW];
@@ -765,6 +962,7 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
     }
 
     int f_tile = -1;
+    int c_tile = -1, c_nvb = TOKB;   // tall tiles: the computed tile and its valid token blocks
     uint32_t a_lo = 0, a_hi = 0, a_n = 0, w_lo = 0, w_hi = 0, w_n = 0;
     // K-major operands: the tile's valid K rows and the byte offset of its first column in a K row
     int kv = kst;
@@ -797,7 +995,7 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
             const int32_t* rowp = a_rows + (size_t)t.e * C + t.tok_base;
             const int rl = lane / NCOL;
             // each copy's RPC row entries in one uniform load, all issued before any
-            // is used (the map is padded by 128 entries, so a short last tile
+            // is used (the map is padded by kRowMapPad entries, so a short last tile
             // reads past its rows harmlessly); readfirstlane keeps them scalar,
             // or the per-lane pick below becomes a vector load, whose wait would
             // also wait for the copies in flight
@@ -867,11 +1065,11 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
             copy_to_lds(rs_a, sb + W_STAGE + (wave * APW + i) * 1024, avo[i], AKM ? 0u : kf * RB);
     };
 
-    f32x16 acc[NBW][TOKB];
+    f32x16 acc[NBW][TBW];
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
-        for (int tb = 0; tb < TOKB; ++tb)
+        for (int tb = 0; tb < TBW; ++tb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[nb][tb][i] = 0.f;
 
@@ -881,7 +1079,9 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
     CombineInputs<TOKB, NBW> cin;   // the combine epilogue's loads
     // fp32 output: right after a tile's stores, the wait for the next copies
     // lets those stores (a fixed number, issued after the copies) stay in flight
-    constexpr int NST = MODE == OUT_F32 ? ffn_f32_stores<TOKB, NBW> : 0;
+    // (more stores than the counter holds: the wait leaves the last ones in
+    // flight; operations retire in issue order, so the copies are still done)
+    constexpr int NST = MODE == OUT_F32 ? std::min(ffn_f32_stores<TBW, NBW>, 63 - PER_CHUNK * (S - 2)) : 0;
     static_assert(PER_CHUNK * (S - 2) + NST < 64, "vmcnt range");
     bool stored = false;
     for (int p0 = 0; p0 < P; p0 += S) {
@@ -898,7 +1098,52 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
                 const char* sa = sw + W_STAGE;
                 // K permuted identically for both operands: MFMA step s takes 16-byte
                 // columns s (half 0) and KC / 32 + s (half 1) of the chunk
-                if constexpr (!AKM && !WKM) {
+                if constexpr (TALL) {
+                    // the valid 32-row token blocks of the tile this chunk belongs to
+                    const int jc = __builtin_amdgcn_readfirstlane(p / nk);
+                    if (jc != c_tile) {
+                        c_tile = jc;
+                        const FfnTile tc = decode_tile<true>(jc * G + slot, ttab, n_tiles, TOK);
+                        c_nvb = __builtin_amdgcn_readfirstlane((tc.nv + 31) >> 5);
+                    }
+                    // one register set of token fragments, refilled as it is
+                    // consumed: block i's fragment for step s + 1 is read right
+                    // after the MFMAs of step s that use it (the weight fragments,
+                    // used by all of the wave's blocks, take two sets); blocks past
+                    // the valid rows hold zeros and get no MFMAs
+                    auto tok_frag = [&](int s, int i) {
+                        const int c = half * (KC / 16) + s;
+                        const int r = (2 * i + tg) * 32 + l32;
+                        return as_bf16x8(*(const u32x4*)(sa + r * RB + (dma_slot<KC>(r, c) << 4)));
+                    };
+                    auto w_frag = [&](int s, int nb) {
+                        const int c = half * (KC / 16) + s;
+                        const int r = wn * 32 * NBW + nb * 32 + l32;
+                        return as_bf16x8(*(const u32x4*)(sw + r * RB + (dma_slot<KC>(r, c) << 4)));
+                    };
+                    bf16x8 fb[TBW], fw[2][NBW];
+#pragma unroll
+                    for (int nb = 0; nb < NBW; ++nb) fw[0][nb] = w_frag(0, nb);
+#pragma unroll
+                    for (int i = 0; i < TBW; ++i) fb[i] = tok_frag(0, i);
+#pragma unroll
+                    for (int s = 0; s < KC / 16; ++s) {
+                        if (s + 1 < KC / 16) {
+#pragma unroll
+                            for (int nb = 0; nb < NBW; ++nb) fw[(s + 1) & 1][nb] = w_frag(s + 1, nb);
+                        }
+#pragma unroll
+                        for (int i = 0; i < TBW; ++i) {
+                            if (2 * i + tg < c_nvb) {
+#pragma unroll
+                                for (int nb = 0; nb < NBW; ++nb)
+                                    acc[nb][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[s & 1][nb], fb[i],
+                                                                                         acc[nb][i], 0, 0, 0);
+                            }
+                            if (s + 1 < KC / 16) fb[i] = tok_frag(s + 1, i);
+                        }
+                    }
+                } else if constexpr (!AKM && !WKM) {
                     // row-major stages: the fragments of step s + 1 are read while
                     // the MFMAs of step s run (two register sets), so only the first
                     // step of a chunk waits for the LDS latency
@@ -990,11 +1235,22 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
                 const int j = p / nk;
                 if (p - j * nk == nk - 1) {
                     const FfnTile t = decode_tile<!AKM>(j * G + slot, ttab, n_tiles, TOK);
-                    if constexpr (MODE == OUT_COMBINE) {
+                    if constexpr (MODE == OUT_COMBINE && !TALL) {
                         combine_load_tokens(cin, t, cb, C, l32);
                         combine_load_rows(cin, cb, N, t.nt * NWG + wave * 32 * NBW, half);
                     }
-                    if constexpr (MODE == OUT_F32) {
+                    if constexpr (TALL) {
+                        static_assert(MODE != OUT_MASK_BF16, "tall tiles: forward outputs");
+                        const int n0 = t.nt * NWG + wn * 32 * NBW;
+                        if constexpr (MODE == OUT_COMBINE) {
+                            ffn_store_tile_combine_tall<TBW, NBW, 1>(acc, t, cb, C, N, n0, tg, l32, half);
+                        } else if constexpr (MODE == OUT_RELU_BF16) {
+                            ffn_store_tile_relu_tall<TBW, NBW>(acc, t, (bf16_t*)out, C, N, n0, tg, l32, half);
+                        } else {
+                            ffn_store_tile_f32_tall<TBW, NBW>(acc, t, (float*)out, C, N, n0, tg, l32, half);
+                            stored = true;
+                        }
+                    } else if constexpr (MODE == OUT_F32) {
                         ffn_store_tile_f32<TOKB, NBW, WAVES>(acc, t, (float*)out, C, N, wave, l32, half);
                         stored = true;
                     } else {
@@ -1004,7 +1260,7 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
 #pragma unroll
                     for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
-                        for (int tb = 0; tb < TOKB; ++tb)
+                        for (int tb = 0; tb < TBW; ++tb)
 #pragma unroll
                             for (int i = 0; i < 16; ++i) acc[nb][tb][i] = 0.f;
                 }
@@ -1318,7 +1574,7 @@ hipError_t launch_expert_gemm_dma_t(const bf16_t* A, const bf16_t* W, const int3
                                     const bf16_t* mask, const FfnCombine& cb, int E, int C, int K, int N,
                                     hipStream_t s, const int32_t* a_rows = nullptr, uint32_t a_bytes = 0,
                                     bool k_in_table = false, int kst = -1) {
-    constexpr int NWG = WAVES * 32 * NBW;
+    constexpr int NWG = dma_tile_cols<TOKB, NBW, WAVES>();
     const int n_tiles = (N + NWG - 1) / NWG;
     const int tok_tiles = (C + 32 * TOKB - 1) / (32 * TOKB);
     const int64_t max_tiles = (int64_t)E * n_tiles * tok_tiles;
@@ -1342,6 +1598,30 @@ hipError_t launch_expert_gemm_dma_t(const bf16_t* A, const bf16_t* W, const int3
 }
 
 int ffn_token_tile(int C) { return C > 64 ? 128 : (C > 32 ? 64 : 32); }
+
+// Tall token tiles for the forward's first expert GEMM: when experts are
+// expected to fill more than one 128-row tile, a tile holds up to 32 kTallTokB
+// = 320 rows, so each (expert, weight block) is usually one tile.  Its
+// weights are then staged once for all of the expert's rows instead of once
+// per 128-row tile (whose copies of one weight block waited on a single HBM
+// stream), and a staged byte feeds M N / (M + N) flop, 142 at 320 x 256
+// against 102 at 128 x 512.  MFMAs of blocks past the valid rows are skipped.
+// A 320 x 256 tile's 72 KiB chunk leaves room for one chunk in flight, so the
+// copies bound it: where the token rows come from HBM (the second GEMM's H),
+// or where there are too few tiles to fill the chip a few times over, the
+// 128-row tiles stay (measured: Switch-Large shape, first GEMM 371 -> 307 us,
+// second 384 -> 420 us tall; congested 64-expert shape, both slower tall).
+int ffn_expected_fill(int64_t assignments, int E, int rows) {
+    if (assignments <= 0 || E <= 0) return 0;
+    return (int)std::min<int64_t>((assignments + E - 1) / E, rows);
+}
+
+int ffn_gemm1_token_tile(int E, int C, int fill, int d_ff) {
+    const int rows = fill > 0 ? std::min(fill, C) : C;
+    const int64_t tiles = (int64_t)E * ((d_ff + 255) / 256);
+    if (C > 128 && rows > 128 && tiles >= 4 * (int64_t)device_cus()) return 32 * kTallTokB;
+    return ffn_token_tile(C);
+}
 
 bool ffn_fused_ok(int C, int d, int d_ff) {
     return C >= 1 && C <= 64 && d % FS_NWG == 0 && d <= FS_MAXND * FS_NWG && d_ff % FS_NWG == 0;
@@ -1397,17 +1677,11 @@ size_t ffn_tile_table_entries(int E, int C) {
     return (size_t)E * ((C + tok - 1) / tok);
 }
 
-hipError_t launch_ffn_tile_prefix(const int32_t* accepted, int E, int C, int32_t* pre, int4* ttab, hipStream_t s) {
-    FfnTileLists L{};
-    L.E = E;
-    L.list[0] = FfnTileListSpec{accepted, nullptr, C, pre, ttab};
-    return launch_ffn_tile_lists(L, 1, s);
-}
-
 hipError_t launch_ffn_tile_lists(const FfnTileLists& L, int n, hipStream_t s) {
     if (n < 1 || n > kMaxTileLists) return hipErrorInvalidValue;
     FfnTileLists Lt = L;
-    for (int i = 0; i < n; ++i) Lt.list[i].tok = ffn_token_tile(Lt.list[i].C);
+    for (int i = 0; i < n; ++i)
+        if (Lt.list[i].tok <= 0) Lt.list[i].tok = ffn_token_tile(Lt.list[i].C);
     hipLaunchKernelGGL(ffn_tile_prefix, dim3(n), dim3(1024), 0, s, Lt);
     return hipGetLastError();
 }
@@ -1475,12 +1749,16 @@ template <int MODE>
 static hipError_t launch_expert_gemm(const bf16_t* A, const bf16_t* W, const int32_t* pre, const int4* ttab, void* out,
                                      const bf16_t* mask, int E, int C, int K, int N, hipStream_t s,
                                      const FfnCombine& cb = FfnCombine{}, const int32_t* a_rows = nullptr,
-                                     uint32_t a_bytes = 0, bool forward = false, int fill = 0) {
+                                     uint32_t a_bytes = 0, bool forward = false, int fill = 0, int tok = 0) {
     // rows an expert is expected to fill (the tile shapes below depend on how
     // many 128-row token tiles it holds; the capacity alone overstates that
     // when most slots stay empty)
     const int rows = fill > 0 ? std::min(fill, C) : C;
-    // the token tile must be ffn_token_tile(C) rows: the prefix kernel lists tiles of that size
+    // the token tile must be the list's: tok rows (the forward's first GEMM
+    // may take tall tiles), else ffn_token_tile(C)
+    if (forward && tok == 32 * kTallTokB)
+        return launch_expert_gemm_dma_t<kTallTokB, 2, 8, MODE, 2, 64>(A, W, pre, ttab, out, mask, cb, E, C, K, N, s,
+                                                                      a_rows, a_bytes);
     if (C <= 64 && forward) {
         if (C <= 32)
             return launch_expert_gemm_dma_small<1, MODE>(A, W, pre, ttab, out, mask, E, C, K, N, s, cb, a_rows,
@@ -1572,7 +1850,7 @@ static hipError_t launch_expert_gemm_kmajor(const bf16_t* A, const bf16_t* W, co
 hipError_t launch_expert_gemm1(const bf16_t* buf, const bf16_t* w1, const int32_t* pre, const int4* ttab, bf16_t* h,
                                int E, int C, int d, int d_ff, hipStream_t s, int fill) {
     return launch_expert_gemm<OUT_RELU_BF16>(buf, w1, pre, ttab, h, nullptr, E, C, d, d_ff, s, FfnCombine{}, nullptr,
-                                             0, true, fill);
+                                             0, true, fill, ffn_gemm1_token_tile(E, C, fill, d_ff));
 }
 
 hipError_t launch_expert_gemm1_gather(const bf16_t* x, int64_t T, const int32_t* slot_token, const bf16_t* w1,
@@ -1580,12 +1858,13 @@ hipError_t launch_expert_gemm1_gather(const bf16_t* x, int64_t T, const int32_t*
                                       hipStream_t s, int fill) {
     if (!ffn_rows_fused(C) || T * d * 2 + 2 * (int64_t)d + 256 >= (int64_t(1) << 32)) return hipErrorInvalidValue;
     return launch_expert_gemm<OUT_RELU_BF16>(x, w1, pre, ttab, h, nullptr, E, C, d, d_ff, s, FfnCombine{}, slot_token,
-                                             (uint32_t)(T * d * 2), true, fill);
+                                             (uint32_t)(T * d * 2), true, fill, ffn_gemm1_token_tile(E, C, fill, d_ff));
 }
 
 hipError_t launch_expert_gemm2(const bf16_t* h, const bf16_t* w2, const int32_t* pre, const int4* ttab, float* y,
-                               int E, int C, int d, int d_ff, hipStream_t s) {
-    return launch_expert_gemm<OUT_F32>(h, w2, pre, ttab, y, nullptr, E, C, d_ff, d, s, FfnCombine{}, nullptr, 0, true);
+                               int E, int C, int d, int d_ff, hipStream_t s, int fill) {
+    return launch_expert_gemm<OUT_F32>(h, w2, pre, ttab, y, nullptr, E, C, d_ff, d, s, FfnCombine{}, nullptr, 0, true,
+                                       fill);
 }
 
 bool ffn_wide_tiles(int C) { return C > 64; }

@@ -39,22 +39,31 @@ hipError_t launch_scan_local(const int32_t* expert, int N, int E, int k, int G, 
 hipError_t launch_scan_offsets(int32_t* tile_counts, int ntiles, int tiles_per_group, int ngroups, int E, int C,
                                int32_t* counts, int32_t* accepted, int32_t* group_base, int32_t* rows_total,
                                const float* parts, int prows, float* prob_sum, hipStream_t s);
+// a token-tile list for the expert GEMMs (ffn_tile_list): built when pre is not NULL
+struct TileListOut {
+    int32_t* pre = nullptr; int4* tab = nullptr; int tok = 0;
+};
 hipError_t launch_gather(const bf16_t* x, const int32_t* expert, const int32_t* offsets, const int32_t* group_base,
                          const int32_t* rows_filled, int N, int d, int E, int k, int G, int rank, int tile, int C,
                          int rows, int32_t* position, uint8_t* keep, int32_t* slot, int32_t* slot_token, bf16_t* buf,
-                         bf16_t* out_pass, bool pass_residual, int32_t* tl_pre, int4* tl_tab, int tl_tok,
+                         bf16_t* out_pass, bool pass_residual, const TileListOut& tl0, const TileListOut& tl1,
                          const AuxStatsArgs* aux, hipStream_t s);
 
 // expert_ffn.hip
 int ffn_token_tile(int C);
+// the forward's expert GEMMs: rows an expert is expected to fill (T k / E,
+// at most the buffer rows; 0 when unknown), and the token-tile height of the
+// first GEMM's list (ffn_token_tile(C), or taller; the second GEMM's list is
+// always ffn_token_tile(C), so ffn_tile_table_entries bounds both)
+int ffn_expected_fill(int64_t assignments, int E, int rows);
+int ffn_gemm1_token_tile(int E, int C, int fill, int d_ff);
 size_t ffn_tile_table_entries(int E, int C);
-hipError_t launch_ffn_tile_prefix(const int32_t* accepted, int E, int C, int32_t* pre, int4* ttab, hipStream_t s);
 // several token-tile lists over the same experts in one launch (block b builds list b);
 // w, if not NULL, goes into the fourth word of each tile entry of its expert
 constexpr int kMaxTileLists = 3;
 struct FfnTileListSpec {
     const int32_t* accepted; const int32_t* w; int C; int32_t* pre; int4* ttab;
-    int tok;   // rows per tile: set by launch_ffn_tile_lists
+    int tok;   // rows per tile (0: ffn_token_tile(C), set by launch_ffn_tile_lists)
 };
 struct FfnTileLists {
     FfnTileListSpec list[kMaxTileLists]; int E;
@@ -65,7 +74,7 @@ hipError_t launch_ffn_tile_lists(const FfnTileLists& L, int n, hipStream_t s);
 hipError_t launch_expert_gemm1(const bf16_t* buf, const bf16_t* w1, const int32_t* pre, const int4* ttab, bf16_t* h,
                                int E, int C, int d, int d_ff, hipStream_t s, int fill = 0);
 hipError_t launch_expert_gemm2(const bf16_t* h, const bf16_t* w2, const int32_t* pre, const int4* ttab, float* y,
-                               int E, int C, int d, int d_ff, hipStream_t s);
+                               int E, int C, int d, int d_ff, hipStream_t s, int fill = 0);
 // The second expert GEMM with the combine (k = 1) in its epilogue: buffer row
 // s of expert e holds token slot_token[e * C + s], and
 //   out[token] = bf16(residual[token] + gate[token] * y[e, s])
@@ -84,7 +93,9 @@ bool ffn_wide_tiles(int C);
 // the forward's expert GEMMs run the direct-to-LDS kernel at every C >= 1 (32-,
 // 64- or 128-row token tiles), so they can gather token rows and fuse the combine
 bool ffn_rows_fused(int C);
-constexpr int kRowMapPad = 128;
+// the tallest token tile of the forward's expert GEMMs, in 32-row blocks
+constexpr int kTallTokB = 10;
+constexpr int kRowMapPad = 32 * kTallTokB;   // a whole token tile past the last expert's rows
 // The first expert GEMM reading its token rows straight from x [T, d]: buffer
 // row s of expert e is x[slot_token[e * C + s]] (no buf array).  Needs
 // ffn_rows_fused(C), T * d * 2 well below 2^32, and kRowMapPad readable

@@ -445,6 +445,11 @@ def check_small_layer(D, t, residual=True):
     (1500, 128, 256, 8, 1.2, 0.0),     # C = 225: two 128-row tiles per expert
     (2100, 192, 320, 8, 1.1, 0.0),     # C = 289: three 128-row tiles, the last short
     (12800, 768, 256, 64, 1.0, 0.0),   # C = 200: two 128-row tiles, the second GEMM on 384 columns
+    # the first GEMM on tall (320-row) token tiles: experts expected to fill
+    # more than 128 rows, and at least four tiles per CU (E * d_ff / 256 >= 1024)
+    (12800, 64, 4096, 64, 1.0, 0.0),   # C = 200: one tall tile per expert
+    (16000, 128, 4096, 64, 2.0, 2.0),  # C = 500, hot expert 0: two tall tiles, the second short
+    (20800, 64, 4032, 64, 1.0, 0.0),   # C = 325: some experts just past one tall tile; d_ff not a multiple of 256
 ])
 def test_edge_shapes(shape):
     T, d, F, E, c, bias0 = shape
