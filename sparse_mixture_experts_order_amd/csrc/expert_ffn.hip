@@ -882,7 +882,7 @@ __device__ __forceinline__ int dma_slot(int r, int c) {
 // row k0 + j at columns n0 + 4 a .. + 3, and lane i gets the 4 rows k0 .. k0 +
 // 3 of column n0 + i.
 template <int TOKB, int NBW, int WAVES, int MODE, int S, int KC, bool WKM = false, bool AKM = false,
-          bool STREAM = false>
+          int STREAM = 0>
 __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __restrict__ A,   // [E, C, K], x or [E, K, C]
                                                               const bf16_t* __restrict__ W,   // [E, N, K] or [E, K, N]
                                                               const int32_t* __restrict__ pre,
@@ -962,6 +962,7 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
     }
 
     int f_tile = -1;
+    bool w_once = false;             // STREAM == 2: the frontier tile's expert has one token tile
     int c_tile = -1, c_nvb = TOKB;   // tall tiles: the computed tile and its valid token blocks
     uint32_t a_lo = 0, a_hi = 0, a_n = 0, w_lo = 0, w_hi = 0, w_n = 0;
     // K-major operands: the tile's valid K rows and the byte offset of its first column in a K row
@@ -987,6 +988,7 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
     auto set_frontier = [&](int j) {
         f_tile = j;
         const FfnTile t = decode_tile<!AKM>(j * G + slot, ttab, n_tiles, TOK);
+        if constexpr (STREAM == 2) w_once = t.w == 1;
         if (a_rows) {
             const uint64_t ab = (uint64_t)(uintptr_t)A;
             a_lo = (uint32_t)ab;
@@ -1059,7 +1061,10 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
         char* sb = lds + stg * STAGE;
 #pragma unroll
         for (int i = 0; i < WPW; ++i)
-            copy_to_lds<STREAM ? kStream : kCached>(rs_w, sb + (wave * WPW + i) * 1024, wvo[i], WKM ? 0u : kf * RB);
+            if (STREAM == 1 || (STREAM == 2 && w_once))
+                copy_to_lds<kStream>(rs_w, sb + (wave * WPW + i) * 1024, wvo[i], WKM ? 0u : kf * RB);
+            else
+                copy_to_lds<kCached>(rs_w, sb + (wave * WPW + i) * 1024, wvo[i], WKM ? 0u : kf * RB);
 #pragma unroll
         for (int i = 0; i < APW; ++i)
             copy_to_lds(rs_a, sb + W_STAGE + (wave * APW + i) * 1024, avo[i], AKM ? 0u : kf * RB);
@@ -1581,13 +1586,21 @@ hipError_t launch_expert_gemm_dma_t(const bf16_t* A, const bf16_t* W, const int3
     int64_t grid = std::min<int64_t>((int64_t)device_cus(), (max_tiles + 7) / 8 * 8);   // one workgroup per CU
     grid = std::max<int64_t>(8, grid / 8 * 8);
     // expert weights read by a single token tile per expert are streamed (read
-    // once); with several token tiles they are read again and stay cached, and
-    // the K-major token-axis products' W operand is an activation, read again too
+    // once); with several token tiles they are read again and stay cached, so
+    // where some experts may hold several, the policy follows each tile's
+    // expert (the list entry's tile count); the K-major token-axis products' W
+    // operand is an activation, read again too
     if constexpr (!AKM) {
         if (tok_tiles == 1) {
-            hipLaunchKernelGGL((expert_gemm_dma<TOKB, NBW, WAVES, MODE, S, KC, WKM, AKM, true>), dim3((unsigned)grid),
+            hipLaunchKernelGGL((expert_gemm_dma<TOKB, NBW, WAVES, MODE, S, KC, WKM, AKM, 1>), dim3((unsigned)grid),
                                dim3(64 * WAVES), 0, s, A, W, pre, ttab, out, mask, cb, a_rows, a_bytes, E, C, K, N,
                                n_tiles, k_in_table ? 1 : 0, kst < 0 ? K : kst);
+            return hipGetLastError();
+        }
+        if (!k_in_table) {
+            hipLaunchKernelGGL((expert_gemm_dma<TOKB, NBW, WAVES, MODE, S, KC, WKM, AKM, 2>), dim3((unsigned)grid),
+                               dim3(64 * WAVES), 0, s, A, W, pre, ttab, out, mask, cb, a_rows, a_bytes, E, C, K, N,
+                               n_tiles, 0, kst < 0 ? K : kst);
             return hipGetLastError();
         }
     }
