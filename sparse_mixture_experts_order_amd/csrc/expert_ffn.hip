@@ -349,11 +349,11 @@ __device__ __forceinline__ f32x16 ffn_swapped_runs(const f32x16& acc) {
     return a;
 }
 
-// Tall token tiles (the forward's products where experts fill more than one
+// Tall token tiles (the forward's first GEMM where experts fill more than one
 // 128-row tile): the waves split the tile two ways, wave w taking the token
 // blocks 2 i + (w & 1) (interleaved, so both halves have about as many valid
 // blocks) against weight rows 32 NBW (w >> 1) .. + 32 NBW - 1; a tile is
-// 16 NBW WAVES weight rows wide.  Its epilogues below take the wave's TBW
+// 16 NBW WAVES weight rows wide.  Its epilogue below takes the wave's TBW
 // token blocks, acc[nb][i] holding block 2 i + tg.
 template <int TOKB, int NBW, int WAVES>
 constexpr int dma_tile_cols() {
@@ -381,139 +381,6 @@ __device__ __forceinline__ void ffn_store_tile_relu_tall(f32x16 (&acc)[NBW][TBW]
                 const u32x4 o = u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
                                       pack_bf16x2(v[6], v[7])};
                 if (r < t.nv && n < N) *(u32x4*)(out + row + n) = o;
-            }
-        }
-    }
-}
-
-// fp32 output of tall token tiles: buffer stores whose descriptor ends with
-// the tile's valid rows (out-of-range ones are dropped), TBW NBW 4 per wave.
-template <int TBW, int NBW>
-__device__ __forceinline__ void ffn_store_tile_f32_tall(const f32x16 (&acc)[NBW][TBW], const FfnTile& t, float* out,
-                                                        int C, int N, int n0, int tg, int l32, int half) {
-    const __amdgpu_buffer_rsrc_t rs =
-        buffer_rsrc_uniform(out + ((size_t)t.e * C + t.tok_base) * N, (uint32_t)max(t.nv, 0) * (uint32_t)N * 4u);
-#pragma unroll
-    for (int i = 0; i < TBW; ++i) {
-        const int r = (2 * i + tg) * 32 + l32;
-#pragma unroll
-        for (int nb = 0; nb < NBW; ++nb) {
-            const f32x16& a = acc[nb][i];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int n = n0 + nb * 32 + q * 8 + half * 4;
-                const uint32_t off = (r < t.nv && n < N) ? (uint32_t)(r * N + n) * 4u : 0x80000000u;
-                const u32x4 v = u32x4{__float_as_uint(a[4 * q + 0]), __float_as_uint(a[4 * q + 1]),
-                                      __float_as_uint(a[4 * q + 2]), __float_as_uint(a[4 * q + 3])};
-                __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, 0);
-            }
-        }
-    }
-}
-
-// The combine epilogue of tall token tiles.  With the accumulators of up to
-// ten token blocks live, the residual runs of every block do not fit in the
-// registers as well, so the blocks go in groups of TG: the token of each row
-// is loaded for all blocks first, then each group's gates and residual runs
-// are loaded before the previous group's results are stored (a load issued
-// after a store waits for that store too), so the groups' loads overlap the
-// stores.  Same arithmetic as ffn_store_tile_direct's combine mode: one fp32
-// fma and one rounding per element, the output run replacing the residual run.
-template <int TBW, int NBW, int TG>
-__device__ __forceinline__ void ffn_store_tile_combine_tall(f32x16 (&acc)[NBW][TBW], const FfnTile& t,
-                                                            const FfnCombine& cb, int C, int N, int n0, int tg,
-                                                            int l32, int half) {
-    static_assert(TBW % TG == 0, "whole groups of token blocks");
-    constexpr int NG = TBW / TG;
-    int tok[TBW];
-#pragma unroll
-    for (int i = 0; i < TBW; ++i) {   // clamped addresses, selected after (no load under a branch)
-        const int r = (2 * i + tg) * 32 + l32;
-        const int v = cb.slot_token[(size_t)t.e * C + min(t.tok_base + r, C - 1)];
-        tok[i] = r < t.nv ? v : -1;
-    }
-    const bf16_t* res = cb.residual ? cb.residual : cb.out;
-    float g[2][TG];
-    u32x4 rr[2][TG][NBW][2];
-    auto load_group = [&](int gi, float (&gd)[TG], u32x4 (&dst)[TG][NBW][2]) {
-#pragma unroll
-        for (int j = 0; j < TG; ++j) {
-            const int tk = max(tok[gi * TG + j], 0);
-            gd[j] = cb.gate[tk];
-#pragma unroll
-            for (int nb = 0; nb < NBW; ++nb)
-#pragma unroll
-                for (int run = 0; run < 2; ++run) {
-                    const int n = n0 + nb * 32 + run * 16 + half * 8;
-                    dst[j][nb][run] = *(const u32x4*)(res + (size_t)tk * N + min(n, N - 8));
-                }
-        }
-    };
-    load_group(0, g[0], rr[0]);
-#pragma unroll
-    for (int gi = 0; gi < NG; ++gi) {
-        const int cur = gi & 1;
-        if (gi + 1 < NG) load_group(gi + 1, g[cur ^ 1], rr[cur ^ 1]);
-#pragma unroll
-        for (int j = 0; j < TG; ++j) {
-            const int i = gi * TG + j;
-            const bool on = tok[i] >= 0;
-            const float gg = on ? g[cur][j] : 0.f;
-            // the group's blocks only (the accumulators of all blocks do not fit
-            // the vector registers the swap works in): lanes l and l ^ 32 hold
-            // the same token, so after swapping by whole pairs every lane holds
-            // two runs of 8 consecutive columns per 32-column block
-#pragma unroll
-            for (int nb = 0; nb < NBW; ++nb) {
-                const f32x16 a = ffn_swapped_runs(acc[nb][i]);
-#pragma unroll
-                for (int run = 0; run < 2; ++run) {
-                    const int n = n0 + nb * 32 + run * 16 + half * 8;
-                    u32x4 rv = (on && cb.residual && n < N) ? rr[cur][j][nb][run] : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const float o0 = fmaf(gg, a[8 * run + 2 * q], bf16_to_f32(rv[q] & 0xffffu));
-                        const float o1 = fmaf(gg, a[8 * run + 2 * q + 1], bf16_to_f32(rv[q] >> 16));
-                        rv[q] = pack_bf16x2(o0, o1);
-                    }
-                    // made here in straight-line code, not inside the stores' branches
-                    asm volatile("" : "+v"(rv));
-                    rr[cur][j][nb][run] = rv;
-                }
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < TG; ++j) {
-            const int i = gi * TG + j;
-            if (tok[i] < 0) continue;
-            const size_t orow = (size_t)tok[i] * N;
-#pragma unroll
-            for (int nb = 0; nb < NBW; ++nb)
-#pragma unroll
-                for (int run = 0; run < 2; ++run) {
-                    const int n = n0 + nb * 32 + run * 16 + half * 8;
-                    if (n < N) *(u32x4*)(cb.out + orow + n) = rr[cur][j][nb][run];
-                }
-        }
-        if (cb.y) {
-#pragma unroll
-            for (int j = 0; j < TG; ++j) {
-                const int i = gi * TG + j;
-                if (tok[i] < 0) continue;
-                const size_t row = ((size_t)t.e * C + t.tok_base + (2 * i + tg) * 32 + l32) * N;
-#pragma unroll
-                for (int nb = 0; nb < NBW; ++nb) {
-                    const f32x16 a = ffn_swapped_runs(acc[nb][i]);   // the runs' layout again
-#pragma unroll
-                    for (int run = 0; run < 2; ++run) {
-                        const int n = n0 + nb * 32 + run * 16 + half * 8;
-                        if (n >= N) continue;
-                        *(f32x4*)(cb.y + row + n) =
-                            f32x4{a[8 * run + 0], a[8 * run + 1], a[8 * run + 2], a[8 * run + 3]};
-                        *(f32x4*)(cb.y + row + n + 4) =
-                            f32x4{a[8 * run + 4], a[8 * run + 5], a[8 * run + 6], a[8 * run + 7]};
-                    }
-                }
             }
         }
     }
@@ -914,7 +781,8 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
     // where experts fill several 128-row tiles, one tile of up to 32 TOKB rows
     // per expert instead
     constexpr bool TALL = TOKB > 4;
-    static_assert(!TALL || (!WKM && !AKM && TOKB % 2 == 0 && WAVES % 2 == 0), "tall token tiles: row-major operands");
+    static_assert(!TALL || (!WKM && !AKM && TOKB % 2 == 0 && WAVES % 2 == 0 && MODE == OUT_RELU_BF16),
+                  "tall token tiles: the first GEMM (row-major operands, bf16 ReLU output)");
     constexpr int TBW = TALL ? TOKB / 2 : TOKB;   // token blocks per wave
     __shared__ __attribute__((aligned(16))) char lds[S * STAGE];
 
@@ -1084,9 +952,7 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
     CombineInputs<TOKB, NBW> cin;   // the combine epilogue's loads
     // fp32 output: right after a tile's stores, the wait for the next copies
     // lets those stores (a fixed number, issued after the copies) stay in flight
-    // (more stores than the counter holds: the wait leaves the last ones in
-    // flight; operations retire in issue order, so the copies are still done)
-    constexpr int NST = MODE == OUT_F32 ? std::min(ffn_f32_stores<TBW, NBW>, 63 - PER_CHUNK * (S - 2)) : 0;
+    constexpr int NST = MODE == OUT_F32 ? ffn_f32_stores<TBW, NBW> : 0;
     static_assert(PER_CHUNK * (S - 2) + NST < 64, "vmcnt range");
     bool stored = false;
     for (int p0 = 0; p0 < P; p0 += S) {
@@ -1245,16 +1111,8 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm_dma(const bf16_t* __re
                         combine_load_rows(cin, cb, N, t.nt * NWG + wave * 32 * NBW, half);
                     }
                     if constexpr (TALL) {
-                        static_assert(MODE != OUT_MASK_BF16, "tall tiles: forward outputs");
-                        const int n0 = t.nt * NWG + wn * 32 * NBW;
-                        if constexpr (MODE == OUT_COMBINE) {
-                            ffn_store_tile_combine_tall<TBW, NBW, 1>(acc, t, cb, C, N, n0, tg, l32, half);
-                        } else if constexpr (MODE == OUT_RELU_BF16) {
-                            ffn_store_tile_relu_tall<TBW, NBW>(acc, t, (bf16_t*)out, C, N, n0, tg, l32, half);
-                        } else {
-                            ffn_store_tile_f32_tall<TBW, NBW>(acc, t, (float*)out, C, N, n0, tg, l32, half);
-                            stored = true;
-                        }
+                        ffn_store_tile_relu_tall<TBW, NBW>(acc, t, (bf16_t*)out, C, N,
+                                                           t.nt * NWG + wn * 32 * NBW, tg, l32, half);
                     } else if constexpr (MODE == OUT_F32) {
                         ffn_store_tile_f32<TOKB, NBW, WAVES>(acc, t, (float*)out, C, N, wave, l32, half);
                         stored = true;
@@ -1769,9 +1627,12 @@ static hipError_t launch_expert_gemm(const bf16_t* A, const bf16_t* W, const int
     const int rows = fill > 0 ? std::min(fill, C) : C;
     // the token tile must be the list's: tok rows (the forward's first GEMM
     // may take tall tiles), else ffn_token_tile(C)
-    if (forward && tok == 32 * kTallTokB)
-        return launch_expert_gemm_dma_t<kTallTokB, 2, 8, MODE, 2, 64>(A, W, pre, ttab, out, mask, cb, E, C, K, N, s,
-                                                                      a_rows, a_bytes);
+    if constexpr (MODE == OUT_RELU_BF16) {
+        if (forward && tok == 32 * kTallTokB)
+            return launch_expert_gemm_dma_t<kTallTokB, 2, 8, MODE, 2, 64>(A, W, pre, ttab, out, mask, cb, E, C, K, N,
+                                                                          s, a_rows, a_bytes);
+    }
+    if (tok == 32 * kTallTokB) return hipErrorInvalidValue;   // tall tiles: the first GEMM only
     if (C <= 64 && forward) {
         if (C <= 32)
             return launch_expert_gemm_dma_small<1, MODE>(A, W, pre, ttab, out, mask, E, C, K, N, s, cb, a_rows,
