@@ -439,6 +439,18 @@ switch_status switch_layer_bwd(const switch_layer_bwd_args *a, void *ws, size_t 
  * multiple of 16 and both pointers 16-byte aligned. */
 switch_status switch_stream_copy(void *dst, const void *src, size_t nbytes, void *stream);
 
+/* Rows per token tile of the first expert GEMM for an expert FFN over E
+ * experts with `rows` buffer rows each (the capacity, or groups x capacity
+ * with routing groups), `assignments` routed choices (T k in a layer; 0 when
+ * unknown, as in switch_expert_ffn) and hidden width d_ff, on the current
+ * device: 32, 64 or 128 rows by the buffer rows, or 320 ("tall" tiles, one per
+ * expert and weight block) when experts are expected to fill more than one
+ * 128-row tile and the grid holds at least four tiles per compute unit.
+ * Informational (no device work); switch_layer_fwd (any k and group) and
+ * switch_expert_ffn choose their tiles with this function.  Returns 0 for
+ * E, rows or d_ff <= 0. */
+int32_t switch_ffn_gemm1_token_tile(int32_t E, int32_t rows, int64_t assignments, int32_t d_ff);
+
 /* Per-launch timing.  While enabled, every kernel launch made by this library
  * is bracketed by two HIP events recorded on the launch's own stream.
  * switch_profile_collect waits for the recorded events, writes up to `max`

@@ -29,7 +29,7 @@ EXPORTS = [
     "switch_route_ex", "switch_dispatch_ex", "switch_dispatch_workspace_bytes_ex", "switch_combine_ex",
     "switch_aux_loss_ex", "switch_workspace_bytes_ex", "switch_layer_bwd", "switch_layer_bwd_workspace_bytes",
     "switch_layer_bwd_workspace_bytes_ex", "switch_build_source_hash", "switch_dispatch_noalloc",
-    "switch_dispatch_noalloc_max_scratch_bytes",
+    "switch_dispatch_noalloc_max_scratch_bytes", "switch_ffn_gemm1_token_tile",
 ]
 
 
@@ -126,6 +126,7 @@ def lib():
             "switch_profile_enable": (None, [I32]),
             "switch_profile_collect": (I32, [I32, P, P]),
             "switch_kernel_name": (ctypes.c_char_p, [I32]),
+            "switch_ffn_gemm1_token_tile": (I32, [I32, I32, I64, I32]),
             "switch_router_z_loss": (I32, [P, P, I64, I32, F32, P, P, I32, P]),
             "switch_route_ex": (I32, [P, P, P, P, I64, I32, I32, I32, I64, P, P, P, P, P, P, SZ, P]),
             "switch_dispatch_workspace_bytes_ex": (SZ, [I64, I32, I32, I64]),
@@ -181,6 +182,10 @@ def switch_capacity(T: int, E: int, c: float) -> int:
     out = ctypes.c_int32(0)
     _check(lib().switch_capacity(T, E, c, ctypes.byref(out)), "switch_capacity")
     return out.value
+
+
+def switch_ffn_gemm1_token_tile(E: int, rows: int, assignments: int, d_ff: int) -> int:
+    return lib().switch_ffn_gemm1_token_tile(E, rows, assignments, d_ff)
 
 
 def switch_route_workspace_bytes(T, d, E):

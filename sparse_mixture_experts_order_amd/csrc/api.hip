@@ -1073,4 +1073,9 @@ int switch_profile_collect(int max, int32_t* kernel_ids, float* ms) {
 
 const char* switch_kernel_name(int32_t id) { return (id >= 0 && id < K_COUNT) ? kKernelNames[id] : "?"; }
 
+int32_t switch_ffn_gemm1_token_tile(int32_t E, int32_t rows, int64_t assignments, int32_t d_ff) {
+    if (E <= 0 || rows <= 0 || d_ff <= 0) return 0;
+    return ffn_gemm1_token_tile(E, rows, ffn_expected_fill(assignments, E, rows), d_ff);
+}
+
 }  // extern "C"

@@ -87,6 +87,27 @@ def test_workspace_sizes():
     assert sw.switch_workspace_bytes(10, 64, 64, 5000, 1) == 0   # E above the limit
 
 
+def test_first_gemm_token_tile():
+    """The first expert GEMM's token-tile height (no device work; without a
+    GPU the library counts 256 compute units, the MI355X's): 32/64/128 rows by
+    the buffer rows, 320-row tall tiles where experts are expected to fill
+    more than 128 rows and E * ceil(d_ff / 256) >= 4 * 256 tiles."""
+    f = sw.switch_ffn_gemm1_token_tile
+    assert f(128, 128, 16384, 3072) == 128                # Switch-Base shape: 128 rows fill
+    assert f(128, 320, 32768, 4096) == 320                # Switch-Large shape: 256 rows fill, 2048 tiles
+    assert f(64, 512, 16384, 3072) == 128                 # congested: 768 tiles, under four per CU
+    assert f(2048, 32, 65536, 1024) == 32                 # many small experts
+    assert f(100, 61, 0, 512) == 64
+    assert f(128, 256, 16384 * 2, 3072) == 320            # top-2 at the Switch-Base shape
+    assert f(128, 16384 // 64 * 1, 16384, 3072) == 128    # routing groups: 256 rows, 128 filled
+    assert f(64, 200, 12800, 4096) == 320                 # the parity tests' tall edge shapes
+    assert f(64, 500, 16000, 4096) == 320
+    assert f(64, 325, 20800, 4032) == 320
+    assert f(64, 200, 12800, 4032 - 256 * 16) == 0        # d_ff <= 0
+    assert f(0, 128, 100, 256) == 0 and f(4, 0, 100, 256) == 0
+    assert f(64, 200, 0, 4096) == 320                     # fill unknown: the buffer rows count
+
+
 def _status(fn, *a):
     with pytest.raises(sw.SwitchError) as ei:
         fn(*a)

@@ -454,6 +454,8 @@ def check_small_layer(D, t, residual=True):
 def test_edge_shapes(shape):
     T, d, F, E, c, bias0 = shape
     say(f"edge shape {shape}")
+    if F == 4096 or F == 4032:   # the tall-tile shapes: the first GEMM must take 320-row tiles
+        assert sw.switch_ffn_gemm1_token_tile(E, so.capacity(T, E, c), T, F) == 320
     # intermediates kept (the first GEMM reads buf) in both modes, then the
     # timed path (token rows gathered from x, the combine in the second GEMM)
     for residual, inspect in ((False, True), (True, True), (False, False)):
