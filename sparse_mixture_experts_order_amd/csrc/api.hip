@@ -996,8 +996,8 @@ switch_status switch_layer_fwd(const switch_layer_args* la, void* ws, size_t ws_
         da.pass_residual = L.residual != 0;
         fa.cb = &cb;
     }
-    // the dispatch step's extra workgroup builds the expert GEMMs' token-tile
-    // list (same workspace carve as run_ffn), so no tile-prefix launch
+    // the dispatch step's extra workgroups build the expert GEMMs' token-tile
+    // lists (same workspace carve as run_ffn), so no tile-prefix launch
     if (rows > 0) {
         const FfnSpace f = carve_ffn(ffn_space, L.E, rows, L.d_ff, ffn_expected_fill(fa.assignments, L.E, rows));
         da.tl0 = f.l2;
