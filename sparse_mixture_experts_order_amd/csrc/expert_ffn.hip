@@ -16,8 +16,10 @@
 // block of TOK rows of one expert, weight-row block of NWG rows), ordered so
 // the token tiles that read one weight block are neighbours, and dealt
 // XCD-major so neighbours share an L2.
-//   - expert_gemm_dma (every forward product, and the backward's products
-//     with 128-row token tiles): both operands of a 64-wide K chunk go from
+//   - expert_gemm_dma (every forward product, the first one on 320-row
+//     "tall" token tiles where experts fill several 128-row tiles, and the
+//     backward's products with 128-row token tiles): both operands of a
+//     64-wide K chunk go from
 //     memory straight into LDS stages by buffer loads with an LDS
 //     destination, S - 1 chunks ahead of the MFMAs, one barrier per chunk;
 //     no register holds data in flight.  Its notes are at the kernel.
@@ -710,7 +712,8 @@ __global__ __launch_bounds__(64 * WAVES) void expert_gemm(const bf16_t* __restri
 
 
 // ---------------------------------------------------------------------------
-// Direct-to-LDS variant for 128-row token tiles with weights stored [N][K].
+// Direct-to-LDS variant for 32-, 64-, 128- or 320-row token tiles with
+// weights stored [N][K] (or [K][N], WKM).
 // Both operands of a KC-wide K chunk (KC = 64 or 32) are copied from memory
 // straight into an LDS stage by buffer loads with an LDS destination, so no
 // registers hold data in flight and the copies run S - 1 chunks ahead of the

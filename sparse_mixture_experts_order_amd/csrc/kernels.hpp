@@ -91,7 +91,8 @@ struct FfnCombine {
 // over them, the backward's included
 bool ffn_wide_tiles(int C);
 // the forward's expert GEMMs run the direct-to-LDS kernel at every C >= 1 (32-,
-// 64- or 128-row token tiles), so they can gather token rows and fuse the combine
+// 64- or 128-row token tiles, 320 for the first GEMM where ffn_gemm1_token_tile
+// picks them), so they can gather token rows and fuse the combine
 bool ffn_rows_fused(int C);
 // the tallest token tile of the forward's expert GEMMs, in 32-row blocks
 constexpr int kTallTokB = 10;
